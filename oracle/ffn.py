@@ -1,0 +1,172 @@
+"""FFN / MoE forward in W4A16 and W4A8 (oracle).
+
+TEST INFRASTRUCTURE ONLY -- see the package docstring.
+
+A quantised matrix is the tuple (q, s, z): integer codes q [N, K] (int64),
+binary16 scales s [N, K/128] and zero points z [N, K/128] (None for the
+symmetric format).  Its real value is w_hat = (q - z) * s (quant.dequantize).
+
+W4A16 (page "MoE推理优化实战：4bit存储+INT8计算的W4A8路线解析", §2.1: 4-bit
+storage, computation in 16-bit after dequantisation; this build fuses the
+dequantisation): every product is the exact real-number product with the
+dequantised weights, evaluated in float64.
+
+SwiGLU FFN (page "高效大语言模型推理实践：INT4量化与MoE架构的融合探索", 核心实现细节:
+LLaMA 3.2 with a SwiGLU FFN): out = down(silu(gate x) * up x), silu(v) = v / (1 + e^-v).
+
+MoE combine (page "大模型之Dense、MoE与量化", MoE section: expert outputs are
+combined in proportion to the router scores; a shared expert is used by every
+token): out[t] = sum_j w[t, j] * FFN_{ids[t, j]}(x[t]) (+ FFN_shared(x[t]) with
+weight 1).
+
+W4A8 (same W4A8 page, §2.3 three-step pipeline and §3.1 per-token activation
+quantisation):
+
+* activations are quantised per row: s = amax / 127 (float32 division),
+  q = clamp(rint(x / s), -128, 127) (float32 division, half-to-even), a zero row
+  gets s = 0 and q = 0;
+* the 4-bit weight is widened to an 8-bit integer without scaling:
+  w8 = q (symmetric) or q - z (asymmetric);
+* INT32 accumulation per group: acc[t, n, g] = sum_{k in g} qx[t, k] * w8[n, k];
+* rescale: y[t, n] = s_x[t] * sum_g s_w[n, g] * acc[t, n, g] (the pages'
+  single scale_w * scale_a rescale, applied per group because the weight
+  scales are per group);
+* x is quantised once per token before gate/up, h once per (token, choice)
+  row before down; the router stays in floating point.
+
+Pinned by (tests/test_oracle_ffn.py): brute-force dense evaluation of every
+expert on tiny inputs with an explicit per-token gather; the slice identity
+(k = E, unit weights, sliced dense weights -> the dense FFN); E = 1 reduces to
+the dense FFN; x = 0 -> 0; INT32 accumulators against element-by-element
+integer sums and their |acc| bound; every non-zero row has a +-127 code; the
+W4A8 special case (integer x with amax 127 -> s = 1 -> W4A8 gate/up equal
+W4A16 gate/up).
+"""
+import numpy as np
+
+from .quant import GROUP, dequantize
+
+
+def silu(v):
+    v = np.asarray(v, dtype=np.float64)
+    return v / (1.0 + np.exp(-v))
+
+
+# ---------------------------------------------------------------- W4A16
+def linear_w4a16(x, qm):
+    """y = x w_hat^T in float64."""
+    q, s, z = qm
+    return np.asarray(x, dtype=np.float64) @ dequantize(q, s, z).T
+
+
+def swiglu_w4a16(x, gate, up, down):
+    g = linear_w4a16(x, gate)
+    u = linear_w4a16(x, up)
+    return linear_w4a16(silu(g) * u, down)
+
+
+def moe_w4a16(x, expert, ids, weights, shared=None):
+    """``expert(e)`` returns (gate, up, down) quantised matrices of expert e;
+    ``shared`` is such a triple or None."""
+    x64 = np.asarray(x, dtype=np.float64)
+    ids = np.asarray(ids)
+    w = np.asarray(weights, dtype=np.float64)
+    t, k = ids.shape
+    out = np.zeros((t, x64.shape[1]), dtype=np.float64)
+    for e in np.unique(ids):
+        rows, cols = np.nonzero(ids == e)
+        y = swiglu_w4a16(x64[rows], *expert(int(e)))
+        for i, (r, c) in enumerate(zip(rows, cols)):
+            out[r] += w[r, c] * y[i]
+    if shared is not None:
+        out += swiglu_w4a16(x64, *shared)
+    return out
+
+
+# ---------------------------------------------------------------- W4A8
+def act_quant_int8(a):
+    """Per-row symmetric INT8 quantisation in float32 (W4A8 page, §3.1)."""
+    a32 = np.asarray(a, dtype=np.float32)
+    amax = np.max(np.abs(a32), axis=1)
+    s = amax / np.float32(127.0)                              # fp32 divide
+    q = np.zeros(a32.shape, dtype=np.float32)
+    nz = s > 0
+    q[nz] = np.clip(np.rint(a32[nz] / s[nz][:, None]), -128, 127)
+    return q.astype(np.int8), s.astype(np.float32)
+
+
+def widen_int8(qm):
+    """4-bit code -> 8-bit integer with the zero point removed, no scaling."""
+    q, s, z = qm
+    q = np.asarray(q, dtype=np.int64)
+    if z is None:
+        return q
+    zz = np.repeat(np.asarray(z, dtype=np.int64), GROUP, axis=1)
+    return q - zz
+
+
+def group_acc(qx, w8):
+    """acc[t, n, g] = sum_{k in group g} qx[t, k] * w8[n, k], exact in int64."""
+    qx = np.asarray(qx, dtype=np.int64)
+    w8 = np.asarray(w8, dtype=np.int64)
+    t, k = qx.shape
+    n = w8.shape[0]
+    g = k // GROUP
+    acc = np.empty((t, n, g), dtype=np.int64)
+    for gi in range(g):
+        sl = slice(gi * GROUP, (gi + 1) * GROUP)
+        acc[:, :, gi] = qx[:, sl] @ w8[:, sl].T               # integer matmul, exact
+    return acc
+
+
+def linear_w4a8(qx, sx, qm):
+    """y[t, n] = s_x[t] * sum_g s_w[n, g] * acc[t, n, g] in float64."""
+    _, s, _ = qm
+    acc = group_acc(qx, widen_int8(qm)).astype(np.float64)
+    sw = np.asarray(s, dtype=np.float16).astype(np.float64)
+    y = np.einsum("tng,ng->tn", acc, sw)
+    return np.asarray(sx, dtype=np.float64)[:, None] * y
+
+
+def swiglu_w4a8(x, gate, up, down, return_parts=False):
+    qx, sx = act_quant_int8(x)
+    g = linear_w4a8(qx, sx, gate)
+    u = linear_w4a8(qx, sx, up)
+    h = silu(g) * u
+    qh, sh = act_quant_int8(h.astype(np.float32))
+    y = linear_w4a8(qh, sh, down)
+    if return_parts:
+        return y, dict(qx=qx, sx=sx, g=g, u=u, h=h, qh=qh, sh=sh)
+    return y
+
+
+def moe_w4a8(x, expert, ids, weights, shared=None):
+    x32 = np.asarray(x, dtype=np.float32)
+    ids = np.asarray(ids)
+    w = np.asarray(weights, dtype=np.float64)
+    t, k = ids.shape
+    out = np.zeros((t, x32.shape[1]), dtype=np.float64)
+    for e in np.unique(ids):
+        rows, cols = np.nonzero(ids == e)
+        y = swiglu_w4a8(x32[rows], *expert(int(e)))
+        for i, (r, c) in enumerate(zip(rows, cols)):
+            out[r] += w[r, c] * y[i]
+    if shared is not None:
+        out += swiglu_w4a8(x32, *shared)
+    return out
+
+
+# ---------------------------------------------------------------- comparison
+def max_rel_l2(y, ref):
+    """max over rows of ||y - ref||_2 / ||ref||_2; a zero reference row needs a zero row."""
+    y = np.asarray(y, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    worst = 0.0
+    for a, b in zip(y, ref):
+        nb = np.linalg.norm(b)
+        if nb == 0.0:
+            if np.linalg.norm(a) != 0.0:
+                return np.inf
+            continue
+        worst = max(worst, np.linalg.norm(a - b) / nb)
+    return worst

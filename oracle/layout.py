@@ -1,0 +1,124 @@
+"""Device tile layout of one INT4 g128 matrix (oracle re-derivation of the spec).
+
+TEST INFRASTRUCTURE ONLY -- see the package docstring.
+
+The pages fix the canonical format (nibbles, per-group scales, optional zero
+points); the device layout is this library's own fixed permutation of those
+bytes, written out here from its specification and nothing else:
+
+Columns.  A matrix has N output columns (rows of the weight) and K reduction
+elements.  ``plain`` keeps column order.  ``gate_up`` takes a stacked
+[gate; up] matrix of 2I rows and interleaves 16-column blocks: device block
+2b holds gate rows [16b, 16b+16), device block 2b+1 holds up rows
+[I+16b, I+16b+16).
+
+Codes.  Every nibble holds an unsigned value d: d = q + 8 for the symmetric
+format (implied zero point 8), d = q for the asymmetric one.
+
+Weights.  One 1024-byte tile per (column block cb, group g), tiles ordered
+cb-major: byte offset 1024 * (cb * G + g).  Inside a tile, lane L in [0, 64)
+owns bytes [16 L, 16 L + 16): column c = L % 16 of the block and quarter
+kq = L // 16.  Its little-endian 32-bit word s in [0, 4) holds the elements
+k = 128 g + 32 s + 8 kq + e, e in [0, 8), element e at nibble position
+p(e) = [0, 4, 1, 5, 2, 6, 3, 7][e] (bits 4p .. 4p+3).
+
+Scales.  Binary16 bits, [N/16][G][16] (same column order), starting at byte
+align256(N K / 2).
+
+Zeros (asymmetric only).  One byte z per (column, group), [N/16][G][16],
+starting after the scales at align256(.) of their end.
+
+Total size: align256(N K/2) + align256(2 N G) (+ align256(N G)).
+
+Pinned by (tests/test_oracle_layout.py): unpack(layout(x)) == x on random
+canonical inputs (both column orders, both formats), and a hand-computed
+single-element placement.
+"""
+import numpy as np
+
+from .quant import GROUP, unpack_canonical
+
+NIBBLE_POS = np.array([0, 4, 1, 5, 2, 6, 3, 7])
+
+
+def _a256(x):
+    return (x + 255) // 256 * 256
+
+
+def device_bytes(n, k, asymmetric):
+    g = k // GROUP
+    total = _a256(n * k // 2) + _a256(2 * n * g)
+    if asymmetric:
+        total += _a256(n * g)
+    return total
+
+
+def column_source(n, gate_up):
+    """Device column j -> source row of the canonical matrix."""
+    j = np.arange(n)
+    if not gate_up:
+        return j
+    half = n // 2
+    cb, c = j // 16, j % 16
+    return np.where(cb % 2 == 0, 16 * (cb // 2) + c, half + 16 * (cb // 2) + c)
+
+
+def to_device(packed, scale_bits, zeros_packed, n, k, asymmetric, gate_up):
+    """Canonical bytes -> device bytes (uint8 array of device_bytes(n, k, asym))."""
+    if n % (32 if gate_up else 16) or k % GROUP:
+        raise ValueError("shape not supported by the device layout")
+    g = k // GROUP
+    q, s, z = unpack_canonical(packed, scale_bits, zeros_packed, k, asymmetric)
+    d = q + 8 if not asymmetric else q                       # unsigned nibble values
+    src = column_source(n, gate_up)
+    d = d[src]
+    s = s[src]
+    out = np.zeros(device_bytes(n, k, asymmetric), dtype=np.uint8)
+    # weights: element (col j, k) -> tile (j//16, k//128), lane, word, nibble
+    words = np.zeros(n * k // 8, dtype=np.uint64)
+    jj, kk = np.meshgrid(np.arange(n), np.arange(k), indexing="ij")
+    cb, c = jj // 16, jj % 16
+    gg, r = kk // GROUP, kk % GROUP
+    sidx, rem = r // 32, r % 32
+    kq, e = rem // 8, rem % 8
+    lane = kq * 16 + c
+    word_index = ((cb * g + gg) * 1024 + lane * 16 + sidx * 4) // 4
+    shift = 4 * NIBBLE_POS[e]
+    np.add.at(words, word_index.ravel(), (d.astype(np.uint64) << shift.astype(np.uint64)).ravel())
+    out[: n * k // 2] = words.astype("<u4").view(np.uint8)
+    # scales [N/16][G][16]
+    so = _a256(n * k // 2)
+    sc = s.view(np.uint16).reshape(n // 16, 16, g).transpose(0, 2, 1).reshape(-1)
+    out[so: so + 2 * n * g] = sc.astype("<u2").view(np.uint8)
+    if asymmetric:
+        zo = so + _a256(2 * n * g)
+        zz = z[src].reshape(n // 16, 16, g).transpose(0, 2, 1).reshape(-1)
+        out[zo: zo + n * g] = zz.astype(np.uint8)
+    return out
+
+
+def from_device(dev, n, k, asymmetric, gate_up):
+    """Device bytes -> (q int64 [N, K], scale bits uint16 [N, G], zeros int64 [N, G] or None),
+    in canonical row order."""
+    g = k // GROUP
+    dev = np.asarray(dev, dtype=np.uint8)
+    words = dev[: n * k // 2].view("<u4").astype(np.int64)
+    jj, kk = np.meshgrid(np.arange(n), np.arange(k), indexing="ij")
+    cb, c = jj // 16, jj % 16
+    gg, r = kk // GROUP, kk % GROUP
+    sidx, rem = r // 32, r % 32
+    kq, e = rem // 8, rem % 8
+    lane = kq * 16 + c
+    word_index = ((cb * g + gg) * 1024 + lane * 16 + sidx * 4) // 4
+    d = (words[word_index] >> (4 * NIBBLE_POS[e])) & 0xF
+    so = _a256(n * k // 2)
+    sc = dev[so: so + 2 * n * g].view("<u2").reshape(n // 16, g, 16).transpose(0, 2, 1).reshape(n, g)
+    zz = None
+    if asymmetric:
+        zo = so + _a256(2 * n * g)
+        zz = dev[zo: zo + n * g].reshape(n // 16, g, 16).transpose(0, 2, 1).reshape(n, g).astype(np.int64)
+    q = d if asymmetric else d - 8
+    src = column_source(n, gate_up)
+    inv = np.empty_like(src)
+    inv[src] = np.arange(n)
+    return q[inv], sc[inv].astype(np.uint16), (zz[inv] if zz is not None else None)

@@ -1,0 +1,172 @@
+"""INT4 group-128 weight quantisation and nibble packing (oracle).
+
+TEST INFRASTRUCTURE ONLY -- see the package docstring.
+
+Format (page "从FP32到INT4：大语言模型量化压缩实战指南", §1.3 分组量化技术解析:
+groups of 128 along the reduction dimension K, each group with its own scale
+from its own min/max, a zero point only in the asymmetric variant; page
+"高效大语言模型推理实践：INT4量化与MoE架构的融合探索", 核心实现细节 / INT4量化实现:
+4-bit integers plus an independent scale per group):
+
+* weight ``w`` of shape [N, K], K a multiple of 128, group g covers
+  k in [128 g, 128 g + 128) of every row;
+* one binary16 scale per (row, group), and in the asymmetric variant one
+  unsigned 4-bit zero point per (row, group);
+* two 4-bit codes per byte, the even k in the low nibble.
+
+Readings where the pages leave a step open (each listed in the design doc):
+
+* symmetric scale = amax / 7 computed as an IEEE float32 division, then
+  rounded to nearest-even binary16; codes are rint(w / s) with the *stored*
+  scale, clamped to [-8, 7], stored as two's-complement nibbles;
+* asymmetric range [min(min w, 0), max(max w, 0)], scale = (mx - mn) / 15 in
+  float32 rounded *upward* to binary16 (so the half-step bound holds at the
+  group maximum), z = clamp(rint(-mn / s), 0, 15),
+  q = clamp(rint(w / s) + z, 0, 15);
+* a group whose scale is zero gets s = 0, codes 0 (and z = 0).
+
+Pinned by (tests/test_oracle_quant.py): brute-force nearest-code search over
+all 16 codes for every element, the half-step error bound, constructed exact
+ties (half-to-even), the +-7 / code-0 invariants, exhaustive nibble
+round-trip of all 256 bytes, and the packed-size formula against the "about
+a quarter of fp16" statement.
+"""
+import numpy as np
+
+GROUP = 128
+
+
+def _groups(w):
+    w32 = np.asarray(w, dtype=np.float32)
+    if w32.ndim != 2:
+        raise ValueError("weight must be 2-D [N, K]")
+    n, k = w32.shape
+    if k % GROUP != 0:
+        raise ValueError("K must be a multiple of 128")
+    if not np.all(np.isfinite(w32)):
+        raise ValueError("non-finite weight")
+    return w32.reshape(n, k // GROUP, GROUP)
+
+
+def f32_to_f16_up(t):
+    """Round non-negative float32 values up (toward +inf) to binary16.
+
+    Definition: the smallest binary16 value that is >= t.  Built from the
+    library's round-to-nearest-even conversion plus one step of nextafter.
+    """
+    t = np.asarray(t, dtype=np.float32)
+    h = t.astype(np.float16)
+    low = h.astype(np.float32) < t
+    h = h.copy()
+    h[low] = np.nextafter(h[low], np.float16(np.inf))
+    return h
+
+
+def quantize_sym(w):
+    """Symmetric INT4 g128 quantisation.
+
+    Returns (q int8 [N, K] in [-8, 7], scales float16 [N, K/128]).
+    Follows §1.3 of the FP32->INT4 guide (per-group scale, no zero point for
+    the symmetric variant) with the amax / 7 reading of the scale.
+    """
+    wg = _groups(w)
+    amax = np.max(np.abs(wg), axis=2)                       # exact in fp32
+    s16 = (amax / np.float32(7.0)).astype(np.float16)       # fp32 divide, RNE to fp16
+    if not np.all(np.isfinite(s16)):
+        raise ValueError("scale overflows binary16")
+    s32 = s16.astype(np.float32)
+    q = np.zeros(wg.shape, dtype=np.float32)
+    nz = s32 > 0
+    # fp32 division by the stored scale, then round-half-to-even
+    q[nz] = np.rint(wg[nz] / s32[nz][:, None])
+    q = np.clip(q, -8, 7)
+    return q.reshape(np.asarray(w).shape).astype(np.int8), s16
+
+
+def quantize_asym(w):
+    """Asymmetric INT4 g128 quantisation with an unsigned 4-bit zero point.
+
+    Returns (q uint8 [N, K] in [0, 15], scales float16 [N, G], zeros uint8 [N, G]).
+    Follows §1.3 of the FP32->INT4 guide (each group computes its own min/max,
+    the asymmetric variant stores a zero point).
+    """
+    wg = _groups(w)
+    mn = np.minimum(np.min(wg, axis=2), np.float32(0))
+    mx = np.maximum(np.max(wg, axis=2), np.float32(0))
+    t = (mx - mn) / np.float32(15.0)                          # fp32 ops, RNE
+    s16 = f32_to_f16_up(t)
+    if not np.all(np.isfinite(s16)):
+        raise ValueError("scale overflows binary16")
+    s32 = s16.astype(np.float32)
+    n, g, _ = wg.shape
+    z = np.zeros((n, g), dtype=np.float32)
+    q = np.zeros(wg.shape, dtype=np.float32)
+    nz = s32 > 0
+    z[nz] = np.clip(np.rint(-mn[nz] / s32[nz]), 0, 15)
+    q[nz] = np.clip(np.rint(wg[nz] / s32[nz][:, None]) + z[nz][:, None], 0, 15)
+    return (q.reshape(np.asarray(w).shape).astype(np.uint8), s16, z.astype(np.uint8))
+
+
+def dequantize(q, scales, zeros=None):
+    """w_hat = (q - z) * s in float64 (exact: a 4-bit integer times a binary16)."""
+    q = np.asarray(q, dtype=np.int64)
+    n, k = q.shape
+    s = np.asarray(scales, dtype=np.float16).astype(np.float64)
+    z = np.zeros_like(s) if zeros is None else np.asarray(zeros, dtype=np.float64)
+    qg = q.reshape(n, k // GROUP, GROUP).astype(np.float64)
+    return ((qg - z[:, :, None]) * s[:, :, None]).reshape(n, k)
+
+
+def pack_nibbles(codes):
+    """Two 4-bit codes per byte along the last axis, the even index in the low nibble.
+
+    Signed codes are stored as two's complement (code & 0xF).
+    """
+    c = np.asarray(codes).astype(np.int64) & 0xF
+    if c.shape[-1] % 2:
+        pad = np.zeros(c.shape[:-1] + (1,), dtype=np.int64)
+        c = np.concatenate([c, pad], axis=-1)
+    lo = c[..., 0::2]
+    hi = c[..., 1::2]
+    return (lo | (hi << 4)).astype(np.uint8)
+
+
+def unpack_nibbles(packed, count, signed):
+    """Inverse of pack_nibbles: the first ``count`` codes along the last axis."""
+    p = np.asarray(packed, dtype=np.int64)
+    out = np.empty(p.shape[:-1] + (2 * p.shape[-1],), dtype=np.int64)
+    out[..., 0::2] = p & 0xF
+    out[..., 1::2] = (p >> 4) & 0xF
+    out = out[..., :count]
+    if signed:
+        out = np.where(out >= 8, out - 16, out)
+    return out
+
+
+def quantize_pack(w, asymmetric):
+    """Canonical byte layout of one matrix: (packed [N, K/2], scale bits [N, G] as
+    uint16, zeros [N, ceil(G/2)] or None)."""
+    if asymmetric:
+        q, s, z = quantize_asym(w)
+        return pack_nibbles(q), s.view(np.uint16), pack_nibbles(z)
+    q, s = quantize_sym(w)
+    return pack_nibbles(q), s.view(np.uint16), None
+
+
+def unpack_canonical(packed, scale_bits, zeros_packed, k, asymmetric):
+    """Canonical bytes -> (q int64 [N, K], scales float16 [N, G], zeros int64 [N, G] or None)."""
+    g = k // GROUP
+    q = unpack_nibbles(packed, k, signed=not asymmetric)
+    s = np.asarray(scale_bits, dtype=np.uint16).view(np.float16)
+    z = unpack_nibbles(zeros_packed, g, signed=False) if asymmetric else None
+    return q, s, z
+
+
+def packed_bytes(n, k, asymmetric):
+    """Bytes of the canonical format: N*K/2 nibble bytes + 2*N*G scale bytes
+    (+ N*ceil(G/2) zero-point bytes)."""
+    g = k // GROUP
+    b = n * k // 2 + 2 * n * g
+    if asymmetric:
+        b += n * ((g + 1) // 2)
+    return b
