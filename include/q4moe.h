@@ -1,0 +1,254 @@
+/*
+ * q4moe.h -- C ABI of the INT4 group-128 top-k MoE SwiGLU FFN forward for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Method (pages cited by title and section):
+ *  - "从FP32到INT4：大语言模型量化压缩实战指南" §1.3 (group-wise quantisation:
+ *    group 128 along K, a per-group scale from the group's min/max, a zero point
+ *    only in the asymmetric variant);
+ *  - "高效大语言模型推理实践：INT4量化与MoE架构的融合探索", INT4量化实现 and
+ *    MoE架构设计 (4-bit integers with an independent per-group scale; a MoE layer
+ *    of small FFN experts chosen per input by a router; slice mode);
+ *  - "MoE推理优化实战：4bit存储+INT8计算的W4A8路线解析" §2.3 (W4A8: 4-bit
+ *    storage widened to INT8, INT8 x INT8 -> INT32, rescale by
+ *    scale_w * scale_a), §3.1 (per-token activation scale amax / 127, round,
+ *    clamp to [-128, 127]), §3.2 (the router stays in floating point; the shared
+ *    expert sees every token);
+ *  - "大模型之Dense、MoE与量化", MoE section (a Linear router scores the
+ *    experts, a few are chosen, outputs combined in proportion to the scores).
+ *
+ * Conventions for every entry point:
+ *  - Pointers named *_dev or documented as device pointers point to device
+ *    memory of the current HIP device; the caller owns every buffer and the
+ *    stream.  The library allocates no device memory and keeps no pointer after
+ *    a call returns.  Work is enqueued on `stream` (may be NULL = default
+ *    stream); no call synchronises the device unless stated.
+ *  - Device pointers must be 16-byte aligned (128-bit loads), else
+ *    Q4_ERR_ALIGN.  All validation happens on the host before any launch; a
+ *    failed validation enqueues nothing.
+ *  - Return value: Q4_OK or one of the error codes below; q4_last_error()
+ *    gives a thread-local message for the last failing call.  No C++
+ *    exception crosses this boundary.
+ *  - Binary16 values travel as their uint16_t bit patterns, bf16 as uint16_t
+ *    bit patterns.
+ */
+#ifndef Q4MOE_H
+#define Q4MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* exported symbols (the library is built with hidden default visibility) */
+#if defined(__GNUC__)
+#define Q4_API __attribute__((visibility("default")))
+#else
+#define Q4_API
+#endif
+
+/* status codes */
+#define Q4_OK 0
+#define Q4_ERR_NULL 1        /* a required pointer is NULL                       */
+#define Q4_ERR_SHAPE 2       /* K % 128 != 0, k > E, t < 0, unsupported sizes... */
+#define Q4_ERR_ALIGN 3       /* a device pointer is not 16-byte aligned          */
+#define Q4_ERR_DTYPE 4       /* unsupported dtype / mode value                   */
+#define Q4_ERR_WORKSPACE 5   /* workspace or output buffer too small             */
+#define Q4_ERR_UNSUPPORTED 6 /* a case this build does not implement             */
+#define Q4_ERR_HIP 7         /* a HIP runtime / launch error                     */
+
+/* dtypes */
+#define Q4_F32 0
+#define Q4_F16 1
+#define Q4_BF16 2
+
+/* forward modes */
+#define Q4_W4A16 0 /* weights dequantised in-kernel, bf16 activations, fp32 accumulate */
+#define Q4_W4A8 1  /* per-token INT8 activations x INT4->INT8 weights, INT32 per group   */
+
+/* repack flags */
+#define Q4_REPACK_PLAIN 0
+#define Q4_REPACK_GATE_UP 1 /* input is [gate; up] stacked (2I rows); 16-column blocks interleaved */
+
+/* quantize_int4_g128 status flags written to *flags_dev (bitwise OR) */
+#define Q4_QFLAG_NONFINITE 1      /* a non-finite weight was seen (its group's codes are unspecified) */
+#define Q4_QFLAG_SCALE_OVERFLOW 2 /* a group scale exceeds binary16 range                           */
+
+/* Text of a status code; never NULL. */
+Q4_API const char* q4_status_string(int status);
+
+/* Thread-local message of the last failing call on this thread ("" if none). */
+Q4_API const char* q4_last_error(void);
+
+/* Library version, e.g. "q4moe 0.1 gfx950". */
+Q4_API const char* q4_version(void);
+
+/*
+ * quantize_int4_g128 -- A1: INT4 group-128 quantisation into the canonical layout.
+ * (FP32->INT4 guide §1.3; INT4量化实现 of the Efficient-LLM-Inference summary.)
+ *
+ *  w        device [n][k] weights of dtype w_dtype (Q4_F32, Q4_F16, Q4_BF16), row-major.
+ *  n, k     rows (output channels) and reduction length; k % 128 == 0, n >= 1.
+ *  asymmetric 0: scale s = fp16_rne(fp32(amax) / 7), q = clamp(rint(w / s), -8, 7),
+ *              two's-complement nibbles;
+ *             1: mn = min(min w, 0), mx = max(max w, 0), s = fp16 rounded up of
+ *              fp32(mx - mn) / 15, z = clamp(rint(-mn / s), 0, 15),
+ *              q = clamp(rint(w / s) + z, 0, 15).
+ *             Divisions are IEEE fp32 divisions by the stored scale; rint is
+ *             round-half-to-even; a zero scale gives codes (and zero point) 0.
+ *  packed   device [n][k/2] bytes; byte j of a row holds k = 2j (low nibble) and 2j + 1.
+ *  scales   device [n][k/128] binary16 bit patterns.
+ *  zeros    device [n][ceil((k/128)/2)] bytes, two zero points per byte, even group in
+ *           the low nibble, pad nibble 0; must be NULL iff asymmetric == 0.
+ *  flags_dev optional device int32 (may be NULL): Q4_QFLAG_* bits are OR-ed in; the
+ *           caller clears it beforehand.
+ */
+Q4_API int quantize_int4_g128(const void* w, int w_dtype, int64_t n, int64_t k, int asymmetric,
+                       uint8_t* packed, uint16_t* scales, uint8_t* zeros, int32_t* flags_dev,
+                       hipStream_t stream);
+
+/*
+ * q4_device_bytes / q4_repack_device -- A2: canonical layout -> device tile layout.
+ * The device layout is a fixed permutation of the canonical bytes (plus one
+ * byte per (column, group) for asymmetric zero points):
+ *  - columns: PLAIN keeps order; GATE_UP takes [gate; up] (n = 2I rows) and places
+ *    gate rows [16b, 16b+16) in device block 2b, up rows [I+16b, I+16b+16) in 2b+1;
+ *  - nibble value d = q + 8 (symmetric) or q (asymmetric);
+ *  - weights: one 1024-byte tile per (16-column block cb, group g), cb-major;
+ *    lane L in [0, 64) of a tile owns 16 bytes: column L % 16, quarter kq = L / 16;
+ *    its 32-bit little-endian word s in [0, 4) holds k = 128 g + 32 s + 8 kq + e,
+ *    e in [0, 8), element e at nibble position [0,4,1,5,2,6,3,7][e];
+ *  - scales: binary16 [n/16][k/128][16] at byte align256(n k / 2);
+ *  - zeros (asymmetric): one byte z per (column, group), [n/16][k/128][16], after the
+ *    scales at the next 256-byte boundary.
+ * Requirements: k % 128 == 0; n % 16 == 0 (PLAIN) or n % 32 == 0 (GATE_UP).
+ * q4_device_bytes returns 0 for an unsupported shape.
+ * dev_out: device buffer of at least q4_device_bytes(n, k, asymmetric) bytes
+ * (Q4_ERR_WORKSPACE otherwise).
+ */
+Q4_API size_t q4_device_bytes(int64_t n, int64_t k, int asymmetric);
+Q4_API int q4_repack_device(const uint8_t* packed, const uint16_t* scales, const uint8_t* zeros,
+                     int64_t n, int64_t k, int asymmetric, int flags, void* dev_out,
+                     size_t dev_bytes, hipStream_t stream);
+
+/*
+ * moe_route_topk -- A3 + A4: fp32 router logits, top-k and renormalised weights.
+ * (Dense/MoE page, MoE section: a Linear router; W4A8 page §3.2: router kept in float.)
+ *
+ *  x_bf16    device [t][h] bf16 tokens.
+ *  w_router  device [e][h] fp32 router weight; bias: device [e] fp32 or NULL.
+ *  logits_out device [t][e] fp32 (required): L = x W_r^T + b, fp32 arithmetic.
+ *  topk_ids  device [t][k] int32: experts by descending L, equal L -> lower index.
+ *  topk_w    device [t][k] fp32: exp(L_j - L_max) / sum over the selected k
+ *            (softmax over e, then renormalised over the selected k).
+ *  workspace device buffer of moe_route_workspace_bytes(t, h, e) bytes (may be 0).
+ *  Requires 1 <= k <= e <= 1024, h % 16 == 0, h >= 16; t == 0 is a no-op.
+ *  NaN logits give unspecified ids.
+ */
+Q4_API size_t moe_route_workspace_bytes(int64_t t, int64_t h, int32_t e);
+Q4_API int moe_route_topk(const uint16_t* x_bf16, const float* w_router, const float* bias, int64_t t,
+                   int64_t h, int32_t e, int32_t k, float* logits_out, int32_t* topk_ids,
+                   float* topk_w, void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * moe_permute -- A5: group the t*k routed slots (slot s = t_idx * k + j) by expert.
+ *  ids     device [t][k] int32 in [0, e).
+ *  counts  device [e] int32: slots per expert.
+ *  offsets device [e + 1] int32: exclusive prefix sum of counts.
+ *  perm    device [t*k] int32: position -> slot, sorted by expert, stable in slot order.
+ *  inv     device [t*k] int32: slot -> position.
+ *  Requires 1 <= k <= e <= 4096 and t*k < 2^31.  Ids outside [0, e) give unspecified
+ *  results.
+ */
+Q4_API int moe_permute(const int32_t* ids, int64_t t, int32_t k, int32_t e, int32_t* counts,
+                int32_t* offsets, int32_t* perm, int32_t* inv, hipStream_t stream);
+
+/*
+ * act_quant_int8 -- A6: per-row INT8 quantisation (W4A8 page §3.1).
+ *  x       device [rows][cols] of dtype x_dtype (Q4_BF16 or Q4_F32).
+ *  q       device [rows][cols] int8: clamp(rint(x / s), -128, 127).
+ *  s       device [rows] fp32: s = amax / 127 (IEEE fp32 divisions); a zero row
+ *          gets s = 0 and q = 0.
+ *  Requires cols % 128 == 0.
+ */
+Q4_API int act_quant_int8(const void* x, int x_dtype, int64_t rows, int64_t cols, int8_t* q, float* s,
+                   hipStream_t stream);
+
+/*
+ * Layer descriptor (host struct holding device pointers).
+ *  num_experts, hidden (H), inter (I), top_k, asymmetric as named.
+ *  gate_up: num_experts consecutive blocks of q4_device_bytes(2I, H, asymmetric) bytes,
+ *           each repacked with Q4_REPACK_GATE_UP from the expert's [gate; up] rows.
+ *  down:    num_experts consecutive blocks of q4_device_bytes(H, I, asymmetric) bytes
+ *           (Q4_REPACK_PLAIN).
+ *  shared_inter: 0 = no shared expert; else the shared expert's intermediate size,
+ *           which must equal inter in this build; shared_gate_up / shared_down are
+ *           one block each, laid out as above.
+ */
+typedef struct q4_moe_layer_t {
+  int32_t num_experts;
+  int32_t hidden;
+  int32_t inter;
+  int32_t top_k;
+  int32_t asymmetric;
+  int32_t shared_inter;
+  const void* gate_up;
+  const void* down;
+  const void* shared_gate_up;
+  const void* shared_down;
+} q4_moe_layer_t;
+
+/*
+ * moe_int4_ffn_forward -- A5..A11: the MoE SwiGLU FFN forward.
+ *   out[t] = sum_j topk_w[t, j] * FFN_{ids[t, j]}(x[t])  (+ FFN_shared(x[t]))
+ *   FFN(v) = down(silu(gate v) * up v)
+ * W4A16: weights dequantised in registers; products in bf16 MFMA with fp32
+ *   accumulation, one fp32 scale step per group; h rounded to bf16.
+ * W4A8: x quantised per token and h per (token, choice) row to INT8 (amax / 127);
+ *   INT32 accumulation per group of int8(x) * (q - z); y = s_x * sum_g s_w * acc.
+ * The combine adds the k routed outputs in ascending j in fp32, then the shared
+ * expert, then rounds to bf16.  A dense SwiGLU FFN is the case num_experts = 1,
+ * top_k = 1, topk_w = 1.
+ *
+ *  x_bf16   device [t][H] bf16; out_bf16 device [t][H] bf16 (may not alias x).
+ *  topk_ids device [t][top_k] int32 in [0, num_experts); topk_w device [t][top_k] fp32.
+ *  workspace device buffer of moe_int4_ffn_workspace_bytes(L, t, mode) bytes.
+ *  Requires H % 128 == 0, I % 128 == 0, 1 <= top_k <= num_experts <= 4096.
+ *  t == 0 is a no-op.  Ids outside range give unspecified results.
+ */
+Q4_API size_t moe_int4_ffn_workspace_bytes(const q4_moe_layer_t* layer, int64_t t, int mode);
+Q4_API int moe_int4_ffn_forward(const q4_moe_layer_t* layer, const uint16_t* x_bf16, int64_t t,
+                         const int32_t* topk_ids, const float* topk_w, int mode,
+                         uint16_t* out_bf16, void* workspace, size_t ws_bytes,
+                         hipStream_t stream);
+
+/*
+ * int4_linear_forward -- one INT4 g128 linear y = x W_hat^T (fp32 output), the
+ * W4A16 core on a plain token matrix.
+ *  x      device [t][k], dtype Q4_F16 or Q4_BF16.
+ *  w_dev  device layout (Q4_REPACK_PLAIN) of an [n][k] matrix.
+ *  y      device [t][n] fp32.
+ *  Requires k % 128 == 0, n % 64 == 0.
+ */
+Q4_API int int4_linear_forward(const void* x, int x_dtype, int64_t t, int64_t k, const void* w_dev,
+                        int64_t n, int asymmetric, float* y, hipStream_t stream);
+
+/*
+ * int4_w4a8_group_acc -- A11 debug view: the per-group INT32 accumulators of the
+ * W4A8 core, acc[r][c][g] = sum_{k in group g} q[r][k] * (code[c][k] - z[c][g]),
+ * computed by the same MFMA core as moe_int4_ffn_forward.
+ *  q      device [rows][k] int8 activation codes.
+ *  w_dev  device layout (Q4_REPACK_PLAIN) of an [n][k] matrix.
+ *  acc    device [rows][n][k/128] int32.
+ *  Requires k % 128 == 0, n % 64 == 0.
+ */
+Q4_API int int4_w4a8_group_acc(const int8_t* q, int64_t rows, int64_t k, const void* w_dev, int64_t n,
+                        int asymmetric, int32_t* acc, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* Q4MOE_H */

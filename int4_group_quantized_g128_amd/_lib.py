@@ -1,0 +1,286 @@
+"""ctypes binding of libq4moe.so (the HIP library); argument marshalling only.
+
+Every function here checks tensor devices, dtypes, shapes and contiguity, allocates
+outputs with PyTorch (device memory is PyTorch's job) and calls the C entry point of
+the same name on the current HIP stream.  All computation happens in the library's
+kernels; there is no fallback: if the library is missing, importing this module
+raises.
+"""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libq4moe.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build the HIP library first "
+        "(python -m int4_group_quantized_g128_amd.build, or __graft_entry__.build())")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+# status codes and enums (mirror include/q4moe.h)
+Q4_OK, Q4_ERR_NULL, Q4_ERR_SHAPE, Q4_ERR_ALIGN, Q4_ERR_DTYPE = 0, 1, 2, 3, 4
+Q4_ERR_WORKSPACE, Q4_ERR_UNSUPPORTED, Q4_ERR_HIP = 5, 6, 7
+Q4_F32, Q4_F16, Q4_BF16 = 0, 1, 2
+Q4_W4A16, Q4_W4A8 = 0, 1
+Q4_REPACK_PLAIN, Q4_REPACK_GATE_UP = 0, 1
+Q4_QFLAG_NONFINITE, Q4_QFLAG_SCALE_OVERFLOW = 1, 2
+
+_vp, _i64, _i32, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+_int = ctypes.c_int
+
+
+class Q4MoELayer(ctypes.Structure):
+    """Mirror of q4_moe_layer_t."""
+    _fields_ = [
+        ("num_experts", _i32), ("hidden", _i32), ("inter", _i32), ("top_k", _i32),
+        ("asymmetric", _i32), ("shared_inter", _i32),
+        ("gate_up", _vp), ("down", _vp), ("shared_gate_up", _vp), ("shared_down", _vp),
+    ]
+
+
+def _sig(name, res, args):
+    f = getattr(_lib, name)
+    f.restype = res
+    f.argtypes = args
+    return f
+
+
+_sig("q4_status_string", ctypes.c_char_p, [_int])
+_sig("q4_last_error", ctypes.c_char_p, [])
+_sig("q4_version", ctypes.c_char_p, [])
+_sig("quantize_int4_g128", _int, [_vp, _int, _i64, _i64, _int, _vp, _vp, _vp, _vp, _vp])
+_sig("q4_device_bytes", _sz, [_i64, _i64, _int])
+_sig("q4_repack_device", _int, [_vp, _vp, _vp, _i64, _i64, _int, _int, _vp, _sz, _vp])
+_sig("moe_route_workspace_bytes", _sz, [_i64, _i64, _i32])
+_sig("moe_route_topk", _int, [_vp, _vp, _vp, _i64, _i64, _i32, _i32, _vp, _vp, _vp, _vp, _sz, _vp])
+_sig("moe_permute", _int, [_vp, _i64, _i32, _i32, _vp, _vp, _vp, _vp, _vp])
+_sig("act_quant_int8", _int, [_vp, _int, _i64, _i64, _vp, _vp, _vp])
+_sig("moe_int4_ffn_workspace_bytes", _sz, [ctypes.POINTER(Q4MoELayer), _i64, _int])
+_sig("moe_int4_ffn_forward", _int, [ctypes.POINTER(Q4MoELayer), _vp, _i64, _vp, _vp, _int, _vp, _vp, _sz, _vp])
+_sig("int4_linear_forward", _int, [_vp, _int, _i64, _i64, _vp, _i64, _int, _vp, _vp])
+_sig("int4_w4a8_group_acc", _int, [_vp, _i64, _i64, _vp, _i64, _int, _vp, _vp])
+
+raw = _lib  # the C entry points, for tests of the ABI itself
+
+
+class Q4Error(RuntimeError):
+    def __init__(self, name, code):
+        msg = _lib.q4_last_error().decode()
+        super().__init__(f"{name}: {_lib.q4_status_string(code).decode()} ({code}): {msg}")
+        self.code = code
+
+
+def _check(name, code):
+    if code != Q4_OK:
+        raise Q4Error(name, code)
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _need(t, dtype, name, ndim=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions")
+    return t
+
+
+_DT = {torch.float32: Q4_F32, torch.float16: Q4_F16, torch.bfloat16: Q4_BF16}
+
+
+def version():
+    return _lib.q4_version().decode()
+
+
+# ------------------------------------------------------------------ A1 / A2
+def quantize_int4_g128(w, asymmetric=False, flags=None):
+    """Canonical INT4 g128 quantisation of w [n, k] -> (packed u8 [n, k/2],
+    scales int16 [n, k/128] (binary16 bits), zeros u8 [n, ceil(G/2)] or None)."""
+    _need(w, (torch.float32, torch.float16, torch.bfloat16), "w", 2)
+    n, k = w.shape
+    g = k // 128
+    packed = torch.empty((n, k // 2), dtype=torch.uint8, device=w.device)
+    scales = torch.empty((n, max(g, 1)), dtype=torch.int16, device=w.device)
+    zeros = torch.empty((n, (g + 1) // 2), dtype=torch.uint8, device=w.device) if asymmetric else None
+    _check("quantize_int4_g128", _lib.quantize_int4_g128(
+        _ptr(w), _DT[w.dtype], n, k, int(bool(asymmetric)), _ptr(packed), _ptr(scales), _ptr(zeros),
+        _ptr(flags), _stream()))
+    return packed, scales, zeros
+
+
+def q4_device_bytes(n, k, asymmetric=False):
+    return int(_lib.q4_device_bytes(n, k, int(bool(asymmetric))))
+
+
+def q4_repack_device(packed, scales, zeros, n, k, asymmetric=False, gate_up=False, out=None):
+    """Canonical bytes -> device tile layout (u8 tensor of q4_device_bytes bytes)."""
+    _need(packed, torch.uint8, "packed")
+    _need(scales, torch.int16, "scales")
+    if zeros is not None:
+        _need(zeros, torch.uint8, "zeros")
+    nbytes = q4_device_bytes(n, k, asymmetric)
+    if out is None:
+        out = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=packed.device)
+    _check("q4_repack_device", _lib.q4_repack_device(
+        _ptr(packed), _ptr(scales), _ptr(zeros), n, k, int(bool(asymmetric)),
+        Q4_REPACK_GATE_UP if gate_up else Q4_REPACK_PLAIN, _ptr(out), out.numel(), _stream()))
+    return out
+
+
+# ------------------------------------------------------------------ A3..A6
+def moe_route_topk(x, w_router, bias, k):
+    """-> (logits fp32 [t, e], ids int32 [t, k], weights fp32 [t, k])."""
+    _need(x, torch.bfloat16, "x", 2)
+    _need(w_router, torch.float32, "w_router", 2)
+    if bias is not None:
+        _need(bias, torch.float32, "bias", 1)
+    t, h = x.shape
+    e = w_router.shape[0]
+    logits = torch.empty((t, e), dtype=torch.float32, device=x.device)
+    ids = torch.empty((t, k), dtype=torch.int32, device=x.device)
+    w = torch.empty((t, k), dtype=torch.float32, device=x.device)
+    ws_bytes = int(_lib.moe_route_workspace_bytes(t, h, e))
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=x.device)
+    _check("moe_route_topk", _lib.moe_route_topk(
+        _ptr(x), _ptr(w_router), _ptr(bias), t, h, e, k, _ptr(logits), _ptr(ids), _ptr(w),
+        _ptr(ws), ws_bytes, _stream()))
+    return logits, ids, w
+
+
+def moe_permute(ids, num_experts):
+    """-> (counts [e], offsets [e + 1], perm [t k], inv [t k]) int32."""
+    _need(ids, torch.int32, "ids", 2)
+    t, k = ids.shape
+    dev = ids.device
+    counts = torch.empty(num_experts, dtype=torch.int32, device=dev)
+    offsets = torch.empty(num_experts + 1, dtype=torch.int32, device=dev)
+    perm = torch.empty(max(t * k, 1), dtype=torch.int32, device=dev)
+    inv = torch.empty(max(t * k, 1), dtype=torch.int32, device=dev)
+    _check("moe_permute", _lib.moe_permute(
+        _ptr(ids), t, k, num_experts, _ptr(counts), _ptr(offsets), _ptr(perm), _ptr(inv), _stream()))
+    return counts, offsets, perm[: t * k], inv[: t * k]
+
+
+def act_quant_int8(x):
+    """Per-row INT8 quantisation of x [rows, cols] (bf16 or fp32) -> (q int8, s fp32 [rows])."""
+    _need(x, (torch.bfloat16, torch.float32), "x", 2)
+    rows, cols = x.shape
+    q = torch.empty((rows, cols), dtype=torch.int8, device=x.device)
+    s = torch.empty(max(rows, 1), dtype=torch.float32, device=x.device)
+    _check("act_quant_int8", _lib.act_quant_int8(
+        _ptr(x), Q4_F32 if x.dtype == torch.float32 else Q4_BF16, rows, cols, _ptr(q), _ptr(s), _stream()))
+    return q, s[:rows]
+
+
+# ------------------------------------------------------------------ layer + forward
+class MoELayer:
+    """Device-resident INT4 MoE layer (stacked experts in the device tile layout)."""
+
+    def __init__(self, num_experts, hidden, inter, top_k, asymmetric=False, shared=False, device="cuda"):
+        self.num_experts, self.hidden, self.inter, self.top_k = num_experts, hidden, inter, top_k
+        self.asymmetric = bool(asymmetric)
+        self.shared = bool(shared)
+        self.gu_bytes = q4_device_bytes(2 * inter, hidden, asymmetric)
+        self.dn_bytes = q4_device_bytes(hidden, inter, asymmetric)
+        if self.gu_bytes == 0 or self.dn_bytes == 0:
+            raise ValueError("hidden and inter must be multiples of 128")
+        self.gate_up = torch.empty(num_experts * self.gu_bytes, dtype=torch.uint8, device=device)
+        self.down = torch.empty(num_experts * self.dn_bytes, dtype=torch.uint8, device=device)
+        self.shared_gate_up = torch.empty(self.gu_bytes, dtype=torch.uint8, device=device) if shared else None
+        self.shared_down = torch.empty(self.dn_bytes, dtype=torch.uint8, device=device) if shared else None
+        self.desc = Q4MoELayer(num_experts, hidden, inter, top_k, int(self.asymmetric),
+                               inter if shared else 0, self.gate_up.data_ptr(), self.down.data_ptr(),
+                               self.shared_gate_up.data_ptr() if shared else None,
+                               self.shared_down.data_ptr() if shared else None)
+
+    def weight_bytes(self):
+        """Device bytes of all expert weights."""
+        return self.gate_up.numel() + self.down.numel() + (self.gu_bytes + self.dn_bytes if self.shared else 0)
+
+    def set_expert(self, e, gate, up, down):
+        """Quantise (on the GPU) and place expert e; e == num_experts is the shared expert."""
+        I, H = self.inter, self.hidden
+        for name, t, shape in (("gate", gate, (I, H)), ("up", up, (I, H)), ("down", down, (H, I))):
+            _need(t, (torch.float32, torch.float16, torch.bfloat16), name, 2)
+            if tuple(t.shape) != shape:
+                raise ValueError(f"{name} must be {shape}, got {tuple(t.shape)}")
+        g = H // 128
+        dev = gate.device
+        packed = torch.empty((2 * I, H // 2), dtype=torch.uint8, device=dev)
+        scales = torch.empty((2 * I, g), dtype=torch.int16, device=dev)
+        zeros = torch.empty((2 * I, (g + 1) // 2), dtype=torch.uint8, device=dev) if self.asymmetric else None
+        for half, w in ((0, gate), (1, up)):
+            sl = slice(half * I, (half + 1) * I)
+            _check("quantize_int4_g128", _lib.quantize_int4_g128(
+                _ptr(w), _DT[w.dtype], I, H, int(self.asymmetric), _ptr(packed[sl]), _ptr(scales[sl]),
+                _ptr(zeros[sl]) if zeros is not None else ctypes.c_void_p(0), ctypes.c_void_p(0), _stream()))
+        if e == self.num_experts:
+            if not self.shared:
+                raise ValueError("layer has no shared expert")
+            gu_out, dn_out = self.shared_gate_up, self.shared_down
+        else:
+            gu_out = self.gate_up[e * self.gu_bytes:(e + 1) * self.gu_bytes]
+            dn_out = self.down[e * self.dn_bytes:(e + 1) * self.dn_bytes]
+        q4_repack_device(packed, scales, zeros, 2 * I, H, self.asymmetric, gate_up=True, out=gu_out)
+        dp, ds, dz = quantize_int4_g128(down, self.asymmetric)
+        q4_repack_device(dp, ds, dz, H, I, self.asymmetric, gate_up=False, out=dn_out)
+
+    def workspace_bytes(self, t, mode):
+        return int(_lib.moe_int4_ffn_workspace_bytes(ctypes.byref(self.desc), t, mode))
+
+
+def moe_int4_ffn_forward(layer, x, ids, weights, mode=Q4_W4A16, out=None, workspace=None):
+    """out [t, H] bf16 = sum_j w[t, j] FFN_{ids[t, j]}(x[t]) (+ shared)."""
+    _need(x, torch.bfloat16, "x", 2)
+    _need(ids, torch.int32, "ids", 2)
+    _need(weights, torch.float32, "weights", 2)
+    t = x.shape[0]
+    if x.shape[1] != layer.hidden or tuple(ids.shape) != (t, layer.top_k) or tuple(weights.shape) != (t, layer.top_k):
+        raise ValueError("shape mismatch between x, ids, weights and the layer")
+    if out is None:
+        out = torch.empty_like(x)
+    nbytes = layer.workspace_bytes(t, mode)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=x.device)
+    _check("moe_int4_ffn_forward", _lib.moe_int4_ffn_forward(
+        ctypes.byref(layer.desc), _ptr(x), t, _ptr(ids), _ptr(weights), mode, _ptr(out),
+        _ptr(workspace), workspace.numel(), _stream()))
+    return out
+
+
+def int4_linear_forward(x, w_dev, n, asymmetric=False):
+    """y [t, n] fp32 = x W_hat^T for x [t, k] fp16/bf16 and a PLAIN device-layout weight."""
+    _need(x, (torch.float16, torch.bfloat16), "x", 2)
+    _need(w_dev, torch.uint8, "w_dev")
+    t, k = x.shape
+    y = torch.empty((t, n), dtype=torch.float32, device=x.device)
+    _check("int4_linear_forward", _lib.int4_linear_forward(
+        _ptr(x), _DT[x.dtype], t, k, _ptr(w_dev), n, int(bool(asymmetric)), _ptr(y), _stream()))
+    return y
+
+
+def int4_w4a8_group_acc(q, w_dev, n, asymmetric=False):
+    """INT32 group accumulators acc [rows, n, k/128] of int8 codes q [rows, k]."""
+    _need(q, torch.int8, "q", 2)
+    _need(w_dev, torch.uint8, "w_dev")
+    rows, k = q.shape
+    acc = torch.empty((rows, n, k // 128), dtype=torch.int32, device=q.device)
+    _check("int4_w4a8_group_acc", _lib.int4_w4a8_group_acc(
+        _ptr(q), rows, k, _ptr(w_dev), n, int(bool(asymmetric)), _ptr(acc), _stream()))
+    return acc

@@ -1,0 +1,343 @@
+// C ABI of the q4moe library: host-side validation, workspace carving and the
+// launch sequence of each entry point.  Declarations and contracts: include/q4moe.h.
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/q4moe.h"
+#include "internal.h"
+
+using namespace q4;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int ok() { return Q4_OK; }
+
+bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+
+int check_hip(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(Q4_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+#define Q4_REQUIRE(cond, code, ...) \
+  do {                              \
+    if (!(cond)) return fail(code, __VA_ARGS__); \
+  } while (0)
+
+int64_t a256(int64_t x) { return align256(x); }
+
+// Carves the forward workspace; with base == nullptr only the size is computed.
+struct FwdWorkspace {
+  int32_t* counts = nullptr;
+  int32_t* offsets = nullptr;
+  int32_t* perm = nullptr;
+  int32_t* inv = nullptr;
+  TileDesc* tiles = nullptr;
+  int32_t* num_tiles = nullptr;
+  void* h = nullptr;
+  float* y = nullptr;
+  int8_t* qx = nullptr;
+  float* sx = nullptr;
+  int8_t* qh = nullptr;
+  float* sh = nullptr;
+  int64_t bytes = 0;
+  int32_t max_tiles = 0;
+  int tile_rows = 16;
+};
+
+int row_blocks_for(const q4_moe_layer_t* L, int64_t t) {
+  const double avg = double(t) * L->top_k / L->num_experts;
+  if (avg <= 16) return 1;
+  if (avg <= 32) return 2;
+  return 4;
+}
+
+FwdWorkspace carve(const q4_moe_layer_t* L, int64_t t, int mode, void* base) {
+  FwdWorkspace w;
+  const int shared = L->shared_inter > 0 ? 1 : 0;
+  const int64_t ee = int64_t(L->num_experts) + shared;
+  const int64_t S = L->top_k + shared;
+  const int64_t P = t * S;
+  const int64_t H = L->hidden, I = L->inter;
+  w.tile_rows = 16 * row_blocks_for(L, t);
+  w.max_tiles = int32_t(P / w.tile_rows + std::min<int64_t>(ee, P) + 1);
+  int64_t off = 0;
+  auto take = [&](int64_t bytes) {
+    const int64_t at = off;
+    off += a256(bytes);
+    return base ? static_cast<uint8_t*>(base) + at : nullptr;
+  };
+  w.counts = reinterpret_cast<int32_t*>(take((ee + 1) * 4));
+  w.offsets = reinterpret_cast<int32_t*>(take((ee + 2) * 4));
+  w.perm = reinterpret_cast<int32_t*>(take(P * 4));
+  w.inv = reinterpret_cast<int32_t*>(take(P * 4));
+  w.tiles = reinterpret_cast<TileDesc*>(take(int64_t(w.max_tiles) * sizeof(TileDesc)));
+  w.num_tiles = reinterpret_cast<int32_t*>(take(4));
+  w.h = take(P * I * (mode == Q4_W4A8 ? 4 : 2));
+  w.y = reinterpret_cast<float*>(take(P * H * 4));
+  if (mode == Q4_W4A8) {
+    w.qx = reinterpret_cast<int8_t*>(take(t * H));
+    w.sx = reinterpret_cast<float*>(take(t * 4));
+    w.qh = reinterpret_cast<int8_t*>(take(P * I));
+    w.sh = reinterpret_cast<float*>(take(P * 4));
+  }
+  w.bytes = off;
+  return w;
+}
+
+int validate_layer(const q4_moe_layer_t* L) {
+  Q4_REQUIRE(L, Q4_ERR_NULL, "layer descriptor is NULL");
+  Q4_REQUIRE(L->num_experts >= 1 && L->num_experts <= 4096, Q4_ERR_SHAPE, "num_experts %d not in [1, 4096]",
+             L->num_experts);
+  Q4_REQUIRE(L->top_k >= 1 && L->top_k <= L->num_experts, Q4_ERR_SHAPE, "top_k %d not in [1, num_experts]",
+             L->top_k);
+  Q4_REQUIRE(L->hidden > 0 && L->hidden % 128 == 0, Q4_ERR_SHAPE, "hidden %d must be a positive multiple of 128",
+             L->hidden);
+  Q4_REQUIRE(L->inter > 0 && L->inter % 128 == 0, Q4_ERR_SHAPE, "inter %d must be a positive multiple of 128",
+             L->inter);
+  Q4_REQUIRE(L->asymmetric == 0 || L->asymmetric == 1, Q4_ERR_SHAPE, "asymmetric must be 0 or 1");
+  Q4_REQUIRE(L->gate_up && L->down, Q4_ERR_NULL, "expert weight pointers are NULL");
+  Q4_REQUIRE(!misaligned(L->gate_up) && !misaligned(L->down), Q4_ERR_ALIGN, "expert weights not 16-byte aligned");
+  if (L->shared_inter != 0) {
+    Q4_REQUIRE(L->shared_inter == L->inter, Q4_ERR_UNSUPPORTED,
+               "shared_inter %d must equal inter %d in this build", L->shared_inter, L->inter);
+    Q4_REQUIRE(L->shared_gate_up && L->shared_down, Q4_ERR_NULL, "shared expert weight pointers are NULL");
+    Q4_REQUIRE(!misaligned(L->shared_gate_up) && !misaligned(L->shared_down), Q4_ERR_ALIGN,
+               "shared expert weights not 16-byte aligned");
+  }
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* q4_status_string(int s) {
+  switch (s) {
+    case Q4_OK: return "ok";
+    case Q4_ERR_NULL: return "null pointer";
+    case Q4_ERR_SHAPE: return "invalid shape";
+    case Q4_ERR_ALIGN: return "misaligned pointer";
+    case Q4_ERR_DTYPE: return "unsupported dtype or mode";
+    case Q4_ERR_WORKSPACE: return "workspace or buffer too small";
+    case Q4_ERR_UNSUPPORTED: return "unsupported case";
+    case Q4_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* q4_last_error(void) { return g_last_error.c_str(); }
+
+const char* q4_version(void) { return "q4moe 0.1 gfx950"; }
+
+int quantize_int4_g128(const void* w, int w_dtype, int64_t n, int64_t k, int asymmetric, uint8_t* packed,
+                       uint16_t* scales, uint8_t* zeros, int32_t* flags_dev, hipStream_t stream) {
+  g_last_error.clear();
+  Q4_REQUIRE(w_dtype == Q4_F32 || w_dtype == Q4_F16 || w_dtype == Q4_BF16, Q4_ERR_DTYPE, "w_dtype %d", w_dtype);
+  Q4_REQUIRE(asymmetric == 0 || asymmetric == 1, Q4_ERR_SHAPE, "asymmetric must be 0 or 1");
+  Q4_REQUIRE(n >= 1 && k >= 128 && k % 128 == 0, Q4_ERR_SHAPE, "need n >= 1 and k a positive multiple of 128");
+  Q4_REQUIRE(n * (k / 256 + 1) < (int64_t(1) << 31), Q4_ERR_SHAPE, "matrix too large");
+  Q4_REQUIRE(w && packed && scales, Q4_ERR_NULL, "w, packed and scales are required");
+  Q4_REQUIRE(asymmetric ? zeros != nullptr : zeros == nullptr, Q4_ERR_NULL,
+             "zeros must be given iff asymmetric");
+  Q4_REQUIRE(!misaligned(w) && !misaligned(packed) && !misaligned(scales) && !(zeros && misaligned(zeros)),
+             Q4_ERR_ALIGN, "device pointers must be 16-byte aligned");
+  return check_hip(launch_quantize(w, w_dtype, n, k, asymmetric, packed, scales, zeros, flags_dev, stream),
+                   "quantize launch");
+}
+
+size_t q4_device_bytes(int64_t n, int64_t k, int asymmetric) {
+  if (n < 16 || n % 16 || k < 128 || k % 128) return 0;
+  const int64_t g = k / 128;
+  int64_t b = a256(n * k / 2) + a256(2 * n * g);
+  if (asymmetric) b += a256(n * g);
+  return size_t(b);
+}
+
+int q4_repack_device(const uint8_t* packed, const uint16_t* scales, const uint8_t* zeros, int64_t n, int64_t k,
+                     int asymmetric, int flags, void* dev_out, size_t dev_bytes, hipStream_t stream) {
+  g_last_error.clear();
+  Q4_REQUIRE(flags == Q4_REPACK_PLAIN || flags == Q4_REPACK_GATE_UP, Q4_ERR_DTYPE, "flags %d", flags);
+  Q4_REQUIRE(asymmetric == 0 || asymmetric == 1, Q4_ERR_SHAPE, "asymmetric must be 0 or 1");
+  Q4_REQUIRE(k >= 128 && k % 128 == 0 && n >= 16 && n % (flags == Q4_REPACK_GATE_UP ? 32 : 16) == 0,
+             Q4_ERR_SHAPE, "need k %% 128 == 0 and n %% %d == 0", flags == Q4_REPACK_GATE_UP ? 32 : 16);
+  Q4_REQUIRE(packed && scales && dev_out, Q4_ERR_NULL, "packed, scales and dev_out are required");
+  Q4_REQUIRE(!asymmetric || zeros, Q4_ERR_NULL, "zeros required for the asymmetric format");
+  Q4_REQUIRE(!misaligned(packed) && !misaligned(dev_out), Q4_ERR_ALIGN, "device pointers must be 16-byte aligned");
+  Q4_REQUIRE(dev_bytes >= q4_device_bytes(n, k, asymmetric), Q4_ERR_WORKSPACE, "dev_out holds %zu bytes, need %zu",
+             dev_bytes, q4_device_bytes(n, k, asymmetric));
+  return check_hip(launch_repack(packed, scales, zeros, n, k, asymmetric, flags == Q4_REPACK_GATE_UP, dev_out, stream),
+                   "repack launch");
+}
+
+size_t moe_route_workspace_bytes(int64_t t, int64_t h, int32_t e) {
+  if (t <= 0 || h <= 0 || e <= 0) return 0;
+  return size_t(route_kslices(t, h, e)) * size_t(t) * size_t(e) * sizeof(float);
+}
+
+int moe_route_topk(const uint16_t* x_bf16, const float* w_router, const float* bias, int64_t t, int64_t h, int32_t e,
+                   int32_t k, float* logits_out, int32_t* topk_ids, float* topk_w, void* workspace, size_t ws_bytes,
+                   hipStream_t stream) {
+  g_last_error.clear();
+  Q4_REQUIRE(t >= 0, Q4_ERR_SHAPE, "t < 0");
+  Q4_REQUIRE(e >= 1 && e <= 1024 && k >= 1 && k <= e, Q4_ERR_SHAPE, "need 1 <= k <= e <= 1024 (k=%d, e=%d)", k, e);
+  Q4_REQUIRE(h >= 16 && h % 16 == 0, Q4_ERR_SHAPE, "h must be a positive multiple of 16");
+  if (t == 0) return ok();
+  Q4_REQUIRE(x_bf16 && w_router && logits_out && topk_ids && topk_w, Q4_ERR_NULL, "missing pointer");
+  Q4_REQUIRE(!misaligned(x_bf16) && !misaligned(w_router), Q4_ERR_ALIGN, "x and w_router must be 16-byte aligned");
+  const size_t need = moe_route_workspace_bytes(t, h, e);
+  Q4_REQUIRE(ws_bytes >= need && (need == 0 || workspace), Q4_ERR_WORKSPACE, "workspace %zu < %zu", ws_bytes, need);
+  return check_hip(launch_route(x_bf16, w_router, bias, t, h, e, k, logits_out, topk_ids, topk_w,
+                                static_cast<float*>(workspace), stream),
+                   "route launch");
+}
+
+int moe_permute(const int32_t* ids, int64_t t, int32_t k, int32_t e, int32_t* counts, int32_t* offsets, int32_t* perm,
+                int32_t* inv, hipStream_t stream) {
+  g_last_error.clear();
+  Q4_REQUIRE(t >= 0 && k >= 1 && k <= e && e <= 4096, Q4_ERR_SHAPE, "need 1 <= k <= e <= 4096, t >= 0");
+  Q4_REQUIRE(t * k < (int64_t(1) << 31), Q4_ERR_SHAPE, "t * k too large");
+  Q4_REQUIRE(counts && offsets, Q4_ERR_NULL, "counts and offsets are required");
+  Q4_REQUIRE(t == 0 || (ids && perm && inv), Q4_ERR_NULL, "ids, perm and inv are required");
+  return check_hip(launch_permute(ids, t, k, e, 0, counts, offsets, perm, inv, nullptr, nullptr, 16, stream),
+                   "permute launch");
+}
+
+int act_quant_int8(const void* x, int x_dtype, int64_t rows, int64_t cols, int8_t* q, float* s, hipStream_t stream) {
+  g_last_error.clear();
+  Q4_REQUIRE(x_dtype == Q4_BF16 || x_dtype == Q4_F32, Q4_ERR_DTYPE, "x_dtype must be Q4_BF16 or Q4_F32");
+  Q4_REQUIRE(rows >= 0 && cols >= 128 && cols % 128 == 0, Q4_ERR_SHAPE, "cols must be a positive multiple of 128");
+  if (rows == 0) return ok();
+  Q4_REQUIRE(x && q && s, Q4_ERR_NULL, "missing pointer");
+  Q4_REQUIRE(!misaligned(x) && !misaligned(q), Q4_ERR_ALIGN, "x and q must be 16-byte aligned");
+  return check_hip(launch_act_quant(x, x_dtype == Q4_F32, rows, cols, q, s, nullptr, stream), "act quant launch");
+}
+
+size_t moe_int4_ffn_workspace_bytes(const q4_moe_layer_t* layer, int64_t t, int mode) {
+  if (!layer || t < 0 || (mode != Q4_W4A16 && mode != Q4_W4A8) || validate_layer(layer) != Q4_OK) return 0;
+  return size_t(carve(layer, t, mode, nullptr).bytes);
+}
+
+int moe_int4_ffn_forward(const q4_moe_layer_t* L, const uint16_t* x_bf16, int64_t t, const int32_t* topk_ids,
+                         const float* topk_w, int mode, uint16_t* out_bf16, void* workspace, size_t ws_bytes,
+                         hipStream_t stream) {
+  g_last_error.clear();
+  if (int rc = validate_layer(L)) return rc;
+  Q4_REQUIRE(mode == Q4_W4A16 || mode == Q4_W4A8, Q4_ERR_DTYPE, "mode %d", mode);
+  Q4_REQUIRE(t >= 0, Q4_ERR_SHAPE, "t < 0");
+  if (t == 0) return ok();
+  const int shared = L->shared_inter > 0 ? 1 : 0;
+  const int64_t S = L->top_k + shared;
+  Q4_REQUIRE(t * S * std::max(L->hidden, L->inter) < (int64_t(1) << 40) && t * S < (int64_t(1) << 31), Q4_ERR_SHAPE,
+             "t too large");
+  Q4_REQUIRE(x_bf16 && topk_ids && topk_w && out_bf16 && workspace, Q4_ERR_NULL, "missing pointer");
+  Q4_REQUIRE(!misaligned(x_bf16) && !misaligned(out_bf16) && !misaligned(workspace), Q4_ERR_ALIGN,
+             "x, out and workspace must be 16-byte aligned");
+  FwdWorkspace w = carve(L, t, mode, workspace);
+  Q4_REQUIRE(ws_bytes >= size_t(w.bytes), Q4_ERR_WORKSPACE, "workspace %zu < %lld", ws_bytes, (long long)w.bytes);
+  const int64_t H = L->hidden, I = L->inter;
+  const int rb = w.tile_rows / 16;
+  int rc;
+  if ((rc = check_hip(launch_permute(topk_ids, t, L->top_k, L->num_experts, shared, w.counts, w.offsets, w.perm,
+                                     w.inv, w.tiles, w.num_tiles, w.tile_rows, stream),
+                      "permute")))
+    return rc;
+  GemmArgs gu{};
+  gu.perm = w.perm;
+  gu.slots_per_token = int32_t(S);
+  gu.w = static_cast<const uint8_t*>(L->gate_up);
+  gu.w_stride = int64_t(q4_device_bytes(2 * I, H, L->asymmetric));
+  gu.w_shared = static_cast<const uint8_t*>(L->shared_gate_up);
+  gu.num_experts = L->num_experts;
+  gu.asym = L->asymmetric;
+  gu.N = 2 * I;
+  gu.K = H;
+  gu.tiles = w.tiles;
+  gu.num_tiles = w.num_tiles;
+  gu.max_tiles = w.max_tiles;
+  gu.out = w.h;
+  GemmArgs dn = gu;
+  dn.perm = nullptr;
+  dn.w = static_cast<const uint8_t*>(L->down);
+  dn.w_stride = int64_t(q4_device_bytes(H, I, L->asymmetric));
+  dn.w_shared = static_cast<const uint8_t*>(L->shared_down);
+  dn.N = H;
+  dn.K = I;
+  dn.out = w.y;
+  if (mode == Q4_W4A16) {
+    gu.a = x_bf16;
+    dn.a = w.h;
+    if ((rc = check_hip(launch_gemm(gu, 0, GEMM_GATE_UP, rb, stream), "gate/up gemm"))) return rc;
+    if ((rc = check_hip(launch_gemm(dn, 0, GEMM_PLAIN, rb, stream), "down gemm"))) return rc;
+  } else {
+    if ((rc = check_hip(launch_act_quant(x_bf16, 0, t, H, w.qx, w.sx, nullptr, stream), "x quant"))) return rc;
+    gu.a = w.qx;
+    gu.a_scale = w.sx;
+    if ((rc = check_hip(launch_gemm(gu, 2, GEMM_GATE_UP, rb, stream), "gate/up gemm"))) return rc;
+    if ((rc = check_hip(launch_act_quant(w.h, 1, t * S, I, w.qh, w.sh, nullptr, stream), "h quant"))) return rc;
+    dn.a = w.qh;
+    dn.a_scale = w.sh;
+    if ((rc = check_hip(launch_gemm(dn, 2, GEMM_PLAIN, rb, stream), "down gemm"))) return rc;
+  }
+  return check_hip(launch_combine(w.y, w.inv, topk_w, t, L->top_k, shared, H, out_bf16, stream), "combine");
+}
+
+int int4_linear_forward(const void* x, int x_dtype, int64_t t, int64_t k, const void* w_dev, int64_t n, int asymmetric,
+                        float* y, hipStream_t stream) {
+  g_last_error.clear();
+  Q4_REQUIRE(x_dtype == Q4_F16 || x_dtype == Q4_BF16, Q4_ERR_DTYPE, "x_dtype must be Q4_F16 or Q4_BF16");
+  Q4_REQUIRE(t >= 0 && k >= 128 && k % 128 == 0 && n >= 64 && n % 64 == 0, Q4_ERR_SHAPE,
+             "need k %% 128 == 0 and n %% 64 == 0");
+  Q4_REQUIRE(asymmetric == 0 || asymmetric == 1, Q4_ERR_SHAPE, "asymmetric must be 0 or 1");
+  if (t == 0) return ok();
+  Q4_REQUIRE(x && w_dev && y, Q4_ERR_NULL, "missing pointer");
+  Q4_REQUIRE(!misaligned(x) && !misaligned(w_dev) && !misaligned(y), Q4_ERR_ALIGN, "pointers must be 16-byte aligned");
+  GemmArgs g{};
+  g.a = x;
+  g.w = static_cast<const uint8_t*>(w_dev);
+  g.num_experts = 1;
+  g.asym = asymmetric;
+  g.N = n;
+  g.K = k;
+  g.dense_rows = t;
+  g.out = y;
+  const int rb = t <= 16 ? 1 : (t <= 32 ? 2 : 4);
+  return check_hip(launch_gemm(g, x_dtype == Q4_F16 ? 1 : 0, GEMM_PLAIN, rb, stream), "linear gemm");
+}
+
+int int4_w4a8_group_acc(const int8_t* q, int64_t rows, int64_t k, const void* w_dev, int64_t n, int asymmetric,
+                        int32_t* acc, hipStream_t stream) {
+  g_last_error.clear();
+  Q4_REQUIRE(rows >= 0 && k >= 128 && k % 128 == 0 && n >= 64 && n % 64 == 0, Q4_ERR_SHAPE,
+             "need k %% 128 == 0 and n %% 64 == 0");
+  Q4_REQUIRE(asymmetric == 0 || asymmetric == 1, Q4_ERR_SHAPE, "asymmetric must be 0 or 1");
+  if (rows == 0) return ok();
+  Q4_REQUIRE(q && w_dev && acc, Q4_ERR_NULL, "missing pointer");
+  Q4_REQUIRE(!misaligned(q) && !misaligned(w_dev), Q4_ERR_ALIGN, "pointers must be 16-byte aligned");
+  GemmArgs g{};
+  g.a = q;
+  g.w = static_cast<const uint8_t*>(w_dev);
+  g.num_experts = 1;
+  g.asym = asymmetric;
+  g.N = n;
+  g.K = k;
+  g.dense_rows = rows;
+  g.acc_out = acc;
+  return check_hip(launch_gemm(g, 2, GEMM_GROUP_ACC, 1, stream), "group acc gemm");
+}
+
+}  // extern "C"

@@ -1,0 +1,135 @@
+// Shared device helpers of the q4moe HIP library (gfx950 / CDNA4 only).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+#include <stdint.h>
+
+#define Q4_DEVICE __device__ __forceinline__
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+namespace q4 {
+
+constexpr int kGroup = 128;
+constexpr int kWave = 64;
+constexpr int kTileBytes = 1024;  // one (16-column block, group) weight tile
+
+// Activation element types of the matrix core.
+enum class Act { BF16 = 0, F16 = 1, I8 = 2 };
+
+// ---------------------------------------------------------------- bit casts
+template <typename To, typename From>
+Q4_DEVICE To bitcast(const From& v) {
+  static_assert(sizeof(To) == sizeof(From), "size mismatch");
+  return __builtin_bit_cast(To, v);
+}
+
+Q4_DEVICE float bf16_to_f32(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
+
+// float -> bf16, round to nearest even (finite inputs; NaN kept quiet).
+Q4_DEVICE uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return uint16_t((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return uint16_t(u >> 16);
+}
+
+Q4_DEVICE float f16_bits_to_f32(uint16_t b) { return float(bitcast<_Float16>(b)); }
+
+// ---------------------------------------------------------------- wave reductions
+Q4_DEVICE float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+Q4_DEVICE float wave_min(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fminf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// ---------------------------------------------------------------- nibble widening
+// A 32-bit device word holds 8 unsigned nibbles d; nibble position r (bits 4r..4r+3)
+// is element 2r and position r + 4 is element 2r + 1 of the lane's 8 consecutive k.
+// OR-ing a nibble into the low mantissa bits of a magic constant yields the exact
+// value magic + d: bf16 0x4300 = 128 (step 1 up to 256), f16 0x6400 = 1024 (step 1
+// up to 2048).  Output register r holds elements (2r, 2r + 1) = (low, high half).
+template <Act A>
+Q4_DEVICE void widen_word_fp(uint32_t w, uint32_t out[4]) {
+  constexpr uint32_t magic = (A == Act::BF16) ? 0x43004300u : 0x64006400u;
+  out[0] = (w & 0x000F000Fu) | magic;
+  out[1] = ((w >> 4) & 0x000F000Fu) | magic;
+  out[2] = ((w >> 8) & 0x000F000Fu) | magic;
+  out[3] = ((w >> 12) & 0x000F000Fu) | magic;
+}
+
+// The magic offset of the widened value (value = offset + d).
+template <Act A>
+constexpr float magic_offset() { return A == Act::BF16 ? 128.0f : 1024.0f; }
+
+// INT8 widening: d - 8 as a two's-complement nibble, placed in the high half of a
+// byte (16 * (d - 8), exact in int8).  Returns two int8x4 registers holding the
+// lane's elements (0..3) and (4..7) in k order.
+Q4_DEVICE void widen_word_i8(uint32_t w, uint32_t& lo, uint32_t& hi) {
+  uint32_t t = w ^ 0x88888888u;                 // d -> d - 8 (two's complement nibble)
+  uint32_t ev = (t << 4) & 0xF0F0F0F0u;         // positions 0,2,4,6 = elements 0,4,1,5
+  uint32_t od = t & 0xF0F0F0F0u;                // positions 1,3,5,7 = elements 2,6,3,7
+  // elements 0..3 = ev.b0, ev.b2, od.b0, od.b2 ; elements 4..7 = ev.b1, ev.b3, od.b1, od.b3
+  lo = __builtin_amdgcn_perm(od, ev, 0x06040200u);
+  hi = __builtin_amdgcn_perm(od, ev, 0x07050301u);
+}
+
+// ---------------------------------------------------------------- MFMA wrappers
+template <Act A>
+Q4_DEVICE f32x4_t mfma16x16x32(const uint32_t a[4], const uint32_t b[4], f32x4_t c) {
+  u32x4_t av = {a[0], a[1], a[2], a[3]};
+  u32x4_t bv = {b[0], b[1], b[2], b[3]};
+  if constexpr (A == Act::BF16) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(bitcast<bf16x8_t>(av), bitcast<bf16x8_t>(bv), c, 0, 0, 0);
+  } else {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(bitcast<f16x8_t>(av), bitcast<f16x8_t>(bv), c, 0, 0, 0);
+  }
+}
+
+Q4_DEVICE i32x4_t mfma_i8_16x16x64(const uint32_t a[4], const uint32_t b[4], i32x4_t c) {
+  i32x4_t av = {int32_t(a[0]), int32_t(a[1]), int32_t(a[2]), int32_t(a[3])};
+  i32x4_t bv = {int32_t(b[0]), int32_t(b[1]), int32_t(b[2]), int32_t(b[3])};
+  return __builtin_amdgcn_mfma_i32_16x16x64_i8(av, bv, c, 0, 0, 0);
+}
+
+Q4_DEVICE f32x4_t mfma_f32_16x16x4(float a, float b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// Sum of the 8 activation elements held in one 16-byte fragment, fp32 accumulate.
+template <Act A>
+Q4_DEVICE float frag_sum(const uint32_t a[4], float acc) {
+  if constexpr (A == Act::BF16) {
+    const bf16x2_t one = bitcast<bf16x2_t>(0x3f803f80u);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc = __builtin_amdgcn_fdot2_f32_bf16(bitcast<bf16x2_t>(a[i]), one, acc, false);
+  } else {
+    const f16x2_t one = bitcast<f16x2_t>(0x3c003c00u);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc = __builtin_amdgcn_fdot2(bitcast<f16x2_t>(a[i]), one, acc, false);
+  }
+  return acc;
+}
+
+// ---------------------------------------------------------------- global loads
+Q4_DEVICE uint4 load16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+Q4_DEVICE uint2 load8(const void* p) { return *reinterpret_cast<const uint2*>(p); }
+
+// Non-temporal 16-byte load for streamed (read-once) weights.
+Q4_DEVICE uint4 load16_stream(const void* p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+}  // namespace q4

@@ -1,0 +1,74 @@
+// Internal launcher declarations of the q4moe HIP library.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <algorithm>
+
+namespace q4 {
+
+__host__ __device__ inline int64_t align256(int64_t x) { return (x + 255) / 256 * 256; }
+
+// Row tile of the grouped GEMM: one 16-row MFMA block per row block.
+struct TileDesc {
+  int32_t expert;
+  int32_t row_start;  // first position of the tile (index into perm / the row buffers)
+  int32_t rows;       // valid rows in the tile
+  int32_t pad;
+};
+
+hipError_t launch_quantize(const void* w, int dtype, int64_t n, int64_t k, int asym, uint8_t* packed,
+                           uint16_t* scales, uint8_t* zeros, int32_t* flags, hipStream_t st);
+hipError_t launch_repack(const uint8_t* packed, const uint16_t* scales, const uint8_t* zeros, int64_t n,
+                         int64_t k, int asym, int gate_up, void* out, hipStream_t st);
+
+// Router: fp32 logits split over kslices partial sums, then reduction + top-k.
+int route_kslices(int64_t t, int64_t h, int32_t e);
+hipError_t launch_route(const uint16_t* x, const float* wr, const float* bias, int64_t t, int64_t h,
+                        int32_t e, int32_t k, float* logits, int32_t* ids, float* w, float* partial,
+                        hipStream_t st);
+
+// Permutation.  Slots s = t * S + j with S = k + shared; expert(s) = ids[t][j] for
+// j < k, num_experts for the shared slot.  Optionally builds the row-tile list.
+hipError_t launch_permute(const int32_t* ids, int64_t t, int32_t k, int32_t e, int shared,
+                          int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv,
+                          TileDesc* tiles, int32_t* num_tiles, int tile_rows, hipStream_t st);
+
+// Per-row INT8 activation quantisation (x: bf16 or fp32 rows).
+hipError_t launch_act_quant(const void* x, int x_is_f32, int64_t rows, int64_t cols, int8_t* q, float* s,
+                            int32_t* qsum, hipStream_t st);
+
+// Grouped GEMM over INT4 device-layout weights.
+struct GemmArgs {
+  // activations
+  const void* a;          // bf16 / f16 [rows][K] or int8 [rows][K]
+  const float* a_scale;   // int8 mode: per-row scale
+  const int32_t* a_qsum;  // int8 asymmetric mode: per (row, group) code sums
+  const int32_t* perm;    // position -> slot (gather rows), or NULL = identity
+  int32_t slots_per_token;  // row = perm[p] / slots_per_token when perm != NULL
+  // weights
+  const uint8_t* w;       // routed experts: num_experts blocks of w_stride bytes
+  int64_t w_stride;
+  const uint8_t* w_shared;  // shared expert block (expert index == num_experts) or NULL
+  int32_t num_experts;
+  int32_t asym;
+  int64_t N;              // device columns (2I for gate/up)
+  int64_t K;
+  // tiles
+  const TileDesc* tiles;  // NULL = dense rows [0, dense_rows)
+  const int32_t* num_tiles;
+  int32_t max_tiles;
+  int64_t dense_rows;
+  // outputs
+  void* out;              // gate/up: h [rows][N/2] (bf16, or fp32 in int8 mode); else fp32 [rows][N]
+  int32_t* acc_out;       // debug: int32 [rows][N][G] group accumulators (int8 mode, plain)
+};
+
+enum GemmKind { GEMM_PLAIN = 0, GEMM_GATE_UP = 1, GEMM_GROUP_ACC = 2 };
+
+hipError_t launch_gemm(const GemmArgs& g, int act /*0 bf16, 1 f16, 2 i8*/, int kind, int row_blocks,
+                       hipStream_t st);
+
+hipError_t launch_combine(const float* y, const int32_t* inv, const float* w, int64_t t, int32_t k, int shared,
+                          int64_t h, uint16_t* out, hipStream_t st);
+
+}  // namespace q4

@@ -1,0 +1,171 @@
+// A5 group-by-expert permutation of the routed slots and the row-tile list.
+//
+// Page "MoE推理优化实战：4bit存储+INT8计算的W4A8路线解析" §1: dispatching tokens to
+// experts and combining the results are costs of their own; this is the dispatch step.
+//
+// One workgroup of up to 16 waves.  Wave w owns a contiguous range of slots.
+//   pass 1: per-wave expert counts in LDS;
+//   pass 2: counts, offsets (exclusive scan) and each wave's base per expert;
+//   pass 3: each wave walks its range 64 slots at a time in slot order; lanes with the
+//           same expert find their rank with ballots, so the scatter is stable.
+#include "common.h"
+#include "internal.h"
+
+namespace q4 {
+
+constexpr int kPermThreads = 1024;
+
+// Exclusive scan of n ints in LDS (in place); returns the total.  All threads call.
+__device__ int32_t block_exclusive_scan(int32_t* data, int n, int32_t* wave_tot) {
+  const int tid = threadIdx.x;
+  const int per = (n + kPermThreads - 1) / kPermThreads;
+  const int beg = tid * per, end = min(n, beg + per);
+  int32_t local = 0;
+  for (int i = beg; i < end; ++i) local += data[i];
+  // inclusive scan of 'local' across the block
+  const int lane = tid & 63, wid = tid >> 6;
+  int32_t v = local;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int32_t u = __shfl_up(v, o, 64);
+    if (lane >= o) v += u;
+  }
+  if (lane == 63) wave_tot[wid] = v;
+  __syncthreads();
+  if (tid == 0) {
+    int32_t run = 0;
+    for (int w = 0; w < kPermThreads / 64; ++w) {
+      const int32_t x = wave_tot[w];
+      wave_tot[w] = run;
+      run += x;
+    }
+    wave_tot[kPermThreads / 64] = run;
+  }
+  __syncthreads();
+  int32_t run = v - local + wave_tot[wid];
+  for (int i = beg; i < end; ++i) {
+    const int32_t x = data[i];
+    data[i] = run;
+    run += x;
+  }
+  const int32_t total = wave_tot[kPermThreads / 64];
+  __syncthreads();
+  return total;
+}
+
+__global__ void __launch_bounds__(kPermThreads) k_permute(const int32_t* __restrict__ ids, int64_t t, int32_t k,
+                                                          int32_t e, int shared, int nwaves,
+                                                          int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                                                          int32_t* __restrict__ perm, int32_t* __restrict__ inv,
+                                                          TileDesc* __restrict__ tiles, int32_t* __restrict__ num_tiles,
+                                                          int tile_rows) {
+  extern __shared__ int32_t lds[];
+  __shared__ int32_t wave_tot[kPermThreads / 64 + 1];
+  const int ee = e + shared;            // experts incl. the shared one
+  const int S = k + shared;             // slots per token
+  const int64_t P = t * S;
+  int32_t* cnt = lds;                   // [nwaves][ee]
+  int32_t* tot = lds + nwaves * ee;     // [ee + 1]
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  for (int i = tid; i < nwaves * ee + ee + 1; i += kPermThreads) lds[i] = 0;
+  __syncthreads();
+  const int64_t per = (P + nwaves - 1) / nwaves;
+  const int64_t beg = std::min<int64_t>(P, int64_t(wid) * per), end = std::min<int64_t>(P, beg + per);
+  auto expert_of = [&](int64_t s) -> int {
+    const int64_t tok = s / S;
+    const int j = int(s - tok * S);
+    if (j >= k) return e;               // the shared expert
+    int x = ids[tok * k + j];
+    return min(max(x, 0), e - 1);       // out-of-range ids are clamped
+  };
+  // pass 1
+  if (wid < nwaves) {
+    for (int64_t s = beg + lane; s < end; s += 64) atomicAdd(&cnt[wid * ee + expert_of(s)], 1);
+  }
+  __syncthreads();
+  // pass 2: totals, offsets, per-wave bases
+  for (int x = tid; x < ee; x += kPermThreads) {
+    int32_t run = 0;
+    for (int w = 0; w < nwaves; ++w) run += cnt[w * ee + x];
+    tot[x] = run;
+  }
+  __syncthreads();
+  for (int x = tid; x < ee; x += kPermThreads) counts[x] = tot[x];
+  __syncthreads();
+  const int32_t total = block_exclusive_scan(tot, ee, wave_tot);
+  for (int x = tid; x < ee; x += kPermThreads) {
+    offsets[x] = tot[x];
+    int32_t run = tot[x];
+    for (int w = 0; w < nwaves; ++w) {
+      const int32_t c = cnt[w * ee + x];
+      cnt[w * ee + x] = run;
+      run += c;
+    }
+  }
+  if (tid == 0) offsets[ee] = total;
+  __syncthreads();
+  // pass 3: stable scatter
+  int nbits = 1;
+  while ((1 << nbits) <= ee) ++nbits;
+  if (wid < nwaves) {
+    for (int64_t s0 = beg; s0 < end; s0 += 64) {
+      const int64_t s = s0 + lane;
+      const bool valid = s < end;
+      const int ex = valid ? expert_of(s) : 0;
+      unsigned long long peers = __ballot(valid);
+      for (int b = 0; b < nbits; ++b) {
+        const unsigned long long m = __ballot((ex >> b) & 1);
+        peers &= ((ex >> b) & 1) ? m : ~m;
+      }
+      const unsigned long long below = peers & ((1ull << lane) - 1ull);
+      const int rank = __popcll(below);
+      int32_t pos = 0;
+      if (valid) pos = cnt[wid * ee + ex] + rank;
+      // make sure every lane has read the base before the leader advances it
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      if (valid) {
+        perm[pos] = int32_t(s);
+        inv[s] = pos;
+        if (below == 0) cnt[wid * ee + ex] += __popcll(peers);
+      }
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+    }
+  }
+  // tile list: ceil(count / tile_rows) tiles per expert, in expert order
+  if (tiles) {
+    __syncthreads();
+    for (int x = tid; x < ee; x += kPermThreads) tot[x] = (counts[x] + tile_rows - 1) / tile_rows;
+    __syncthreads();
+    const int32_t ntiles = block_exclusive_scan(tot, ee, wave_tot);
+    for (int x = tid; x < ee; x += kPermThreads) {
+      const int32_t c = counts[x], o = offsets[x];
+      int32_t ti = tot[x];
+      for (int32_t r = 0; r < c; r += tile_rows, ++ti) {
+        TileDesc d;
+        d.expert = x;
+        d.row_start = o + r;
+        d.rows = min(tile_rows, c - r);
+        d.pad = 0;
+        tiles[ti] = d;
+      }
+    }
+    if (tid == 0) *num_tiles = ntiles;
+  }
+}
+
+hipError_t launch_permute(const int32_t* ids, int64_t t, int32_t k, int32_t e, int shared, int32_t* counts,
+                          int32_t* offsets, int32_t* perm, int32_t* inv, TileDesc* tiles, int32_t* num_tiles,
+                          int tile_rows, hipStream_t st) {
+  const int ee = e + shared;
+  const size_t budget = 96 * 1024;
+  int nwaves = int(std::min<size_t>(16, (budget / sizeof(int32_t) - (ee + 1)) / ee));
+  nwaves = std::max(1, nwaves);
+  const size_t lds = (size_t(nwaves) * ee + ee + 1) * sizeof(int32_t);
+  hipLaunchKernelGGL(k_permute, dim3(1), dim3(kPermThreads), lds, st, ids, t, k, e, shared, nwaves, counts,
+                     offsets, perm, inv, tiles, num_tiles, tile_rows);
+  return hipGetLastError();
+}
+
+}  // namespace q4

@@ -1,0 +1,202 @@
+// A1 quantise + pack and A2 device repack.
+//
+// Format: page "从FP32到INT4：大语言模型量化压缩实战指南" §1.3 (groups of 128 along
+// K, a scale per group from its own min/max, a zero point only when asymmetric);
+// page "高效大语言模型推理实践：INT4量化与MoE架构的融合探索", INT4量化实现 (4-bit
+// integers plus an independent per-group scale).
+#include "common.h"
+#include "internal.h"
+
+namespace q4 {
+
+// binary16 rounded toward +inf of a non-negative finite float: the smallest
+// binary16 value that is >= t.
+Q4_DEVICE uint16_t f32_to_f16_up(float t) {
+  __half h = __float2half_rn(t);
+  uint16_t b = __half_as_ushort(h);
+  if (__half2float(h) < t) b = uint16_t(b + 1);   // next binary16 up (t >= 0)
+  return b;
+}
+
+// One wave per (row, pair of groups).  Lane j covers k = 128 g + 2 j and 2 j + 1 and
+// writes byte j of the group's 64 packed bytes.
+template <int DT, bool ASYM>
+__global__ void __launch_bounds__(64) k_quantize_g128(const void* __restrict__ w, int64_t n, int64_t k,
+                                                     uint8_t* __restrict__ packed,
+                                                     uint16_t* __restrict__ scales,
+                                                     uint8_t* __restrict__ zeros,
+                                                     int32_t* __restrict__ flags) {
+  const int64_t G = k / kGroup;
+  const int64_t pairs = (G + 1) / 2;
+  const int64_t row = int64_t(blockIdx.x) / pairs;
+  const int64_t pair = int64_t(blockIdx.x) % pairs;
+  const int lane = threadIdx.x;
+  uint32_t zbyte = 0;
+  int flag = 0;
+  for (int h = 0; h < 2; ++h) {
+    const int64_t g = pair * 2 + h;
+    if (g >= G) break;
+    const int64_t base = row * k + g * kGroup + 2 * lane;
+    float v0, v1;
+    if constexpr (DT == 0) {
+      const float2 p = *reinterpret_cast<const float2*>(static_cast<const float*>(w) + base);
+      v0 = p.x;
+      v1 = p.y;
+    } else {
+      const uint32_t p = *reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(w) + base);
+      if constexpr (DT == 1) {
+        v0 = f16_bits_to_f32(uint16_t(p & 0xffff));
+        v1 = f16_bits_to_f32(uint16_t(p >> 16));
+      } else {
+        v0 = bf16_to_f32(uint16_t(p & 0xffff));
+        v1 = bf16_to_f32(uint16_t(p >> 16));
+      }
+    }
+    if (!__builtin_isfinite(v0) || !__builtin_isfinite(v1)) flag |= 1;
+    uint32_t c0, c1;
+    if constexpr (!ASYM) {
+      const float amax = wave_max(fmaxf(fabsf(v0), fabsf(v1)));
+      const float t = __fdiv_rn(amax, 7.0f);
+      const __half sh = __float2half_rn(t);
+      const uint16_t sb = __half_as_ushort(sh);
+      if ((sb & 0x7fff) >= 0x7c00) flag |= 2;
+      const float s = __half2float(sh);
+      float q0 = 0.f, q1 = 0.f;
+      if (s > 0.f) {
+        q0 = fminf(fmaxf(rintf(__fdiv_rn(v0, s)), -8.f), 7.f);
+        q1 = fminf(fmaxf(rintf(__fdiv_rn(v1, s)), -8.f), 7.f);
+      }
+      c0 = uint32_t(int(q0)) & 0xF;
+      c1 = uint32_t(int(q1)) & 0xF;
+      if (lane == 0) scales[row * G + g] = sb;
+    } else {
+      const float mn = fminf(wave_min(fminf(v0, v1)), 0.f);
+      const float mx = fmaxf(wave_max(fmaxf(v0, v1)), 0.f);
+      const float t = __fdiv_rn(__fsub_rn(mx, mn), 15.0f);
+      const uint16_t sb = f32_to_f16_up(t);
+      if ((sb & 0x7fff) >= 0x7c00) flag |= 2;
+      const float s = f16_bits_to_f32(sb);
+      float z = 0.f, q0 = 0.f, q1 = 0.f;
+      if (s > 0.f) {
+        z = fminf(fmaxf(rintf(__fdiv_rn(-mn, s)), 0.f), 15.f);
+        q0 = fminf(fmaxf(__fadd_rn(rintf(__fdiv_rn(v0, s)), z), 0.f), 15.f);
+        q1 = fminf(fmaxf(__fadd_rn(rintf(__fdiv_rn(v1, s)), z), 0.f), 15.f);
+      }
+      c0 = uint32_t(int(q0));
+      c1 = uint32_t(int(q1));
+      zbyte |= uint32_t(int(z)) << (4 * h);
+      if (lane == 0) scales[row * G + g] = sb;
+    }
+    packed[(row * k + g * kGroup) / 2 + lane] = uint8_t(c0 | (c1 << 4));
+  }
+  if constexpr (ASYM) {
+    if (lane == 0) zeros[row * ((G + 1) / 2) + pair] = uint8_t(zbyte);
+  }
+  if (flags) {
+    // any lane that saw a problem reports it
+    const unsigned long long any = __ballot(flag != 0);
+    if (any) {
+      int all = flag;
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) all |= __shfl_xor(all, o, 64);
+      if (lane == 0) atomicOr(flags, all);
+    }
+  }
+}
+
+// A2: one thread per 32-bit word of the device weights.  Word index
+// ((cb * G + g) * 64 + lane) * 4 + s; it gathers elements k = 128 g + 32 s + 8 kq + e,
+// e in [0, 8) (4 canonical bytes) of device column 16 cb + lane % 16.
+__global__ void k_repack_weights(const uint8_t* __restrict__ packed, int64_t n, int64_t k, int asym,
+                                 int gate_up, uint32_t* __restrict__ out) {
+  const int64_t G = k / kGroup;
+  const int64_t total = n * k / 8;
+  for (int64_t wi = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; wi < total;
+       wi += int64_t(gridDim.x) * blockDim.x) {
+    const int s = int(wi & 3);
+    const int lane = int((wi >> 2) & 63);
+    const int64_t tile = wi >> 8;
+    const int64_t g = tile % G;
+    const int64_t cb = tile / G;
+    const int c = lane & 15, kq = lane >> 4;
+    int64_t col = cb * 16 + c;
+    int64_t src = col;
+    if (gate_up) {
+      const int64_t half = n / 2;
+      src = (cb & 1) ? half + (cb >> 1) * 16 + c : (cb >> 1) * 16 + c;
+    }
+    const int64_t k0 = g * kGroup + 32 * s + 8 * kq;
+    const uint32_t in = *reinterpret_cast<const uint32_t*>(packed + (src * k + k0) / 2);
+    // in: nibble e (bits 4e..4e+3) is element e; out: element e at position p(e)
+    uint32_t o = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      uint32_t d = (in >> (4 * e)) & 0xF;
+      if (!asym) d ^= 0x8;                         // two's complement q -> q + 8
+      const int p = (e & 1) ? 4 + (e >> 1) : (e >> 1);
+      o |= d << (4 * p);
+    }
+    out[wi] = o;
+  }
+}
+
+// Scales (and zero points) into [n/16][G][16] with the device column order.
+__global__ void k_repack_meta(const uint16_t* __restrict__ scales, const uint8_t* __restrict__ zeros,
+                              int64_t n, int64_t k, int gate_up, uint16_t* __restrict__ sout,
+                              uint8_t* __restrict__ zout) {
+  const int64_t G = k / kGroup;
+  const int64_t total = n * G;
+  for (int64_t i = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; i < total;
+       i += int64_t(gridDim.x) * blockDim.x) {
+    const int c = int(i & 15);
+    const int64_t g = (i >> 4) % G;
+    const int64_t cb = (i >> 4) / G;
+    int64_t src = cb * 16 + c;
+    if (gate_up) {
+      const int64_t half = n / 2;
+      src = (cb & 1) ? half + (cb >> 1) * 16 + c : (cb >> 1) * 16 + c;
+    }
+    sout[i] = scales[src * G + g];
+    if (zout) {
+      const uint8_t zb = zeros[src * ((G + 1) / 2) + g / 2];
+      zout[i] = (g & 1) ? (zb >> 4) : (zb & 0xF);
+    }
+  }
+}
+
+hipError_t launch_quantize(const void* w, int dtype, int64_t n, int64_t k, int asym, uint8_t* packed,
+                           uint16_t* scales, uint8_t* zeros, int32_t* flags, hipStream_t st) {
+  const int64_t G = k / kGroup;
+  dim3 grid(unsigned(n * ((G + 1) / 2)));
+#define Q4_QLAUNCH(DT, AS) \
+  hipLaunchKernelGGL((k_quantize_g128<DT, AS>), grid, dim3(64), 0, st, w, n, k, packed, scales, zeros, flags)
+  if (asym) {
+    if (dtype == 0) Q4_QLAUNCH(0, true);
+    else if (dtype == 1) Q4_QLAUNCH(1, true);
+    else Q4_QLAUNCH(2, true);
+  } else {
+    if (dtype == 0) Q4_QLAUNCH(0, false);
+    else if (dtype == 1) Q4_QLAUNCH(1, false);
+    else Q4_QLAUNCH(2, false);
+  }
+#undef Q4_QLAUNCH
+  return hipGetLastError();
+}
+
+hipError_t launch_repack(const uint8_t* packed, const uint16_t* scales, const uint8_t* zeros, int64_t n,
+                         int64_t k, int asym, int gate_up, void* out, hipStream_t st) {
+  uint8_t* base = static_cast<uint8_t*>(out);
+  const int64_t G = k / kGroup;
+  const int64_t words = n * k / 8;
+  const int64_t sb = align256(n * k / 2);
+  const int64_t zb = sb + align256(2 * n * G);
+  unsigned blocks = unsigned(std::min<int64_t>((words + 255) / 256, 65536));
+  hipLaunchKernelGGL(k_repack_weights, dim3(blocks), dim3(256), 0, st, packed, n, k, asym, gate_up,
+                     reinterpret_cast<uint32_t*>(base));
+  unsigned mblocks = unsigned(std::min<int64_t>((n * G + 255) / 256, 65536));
+  hipLaunchKernelGGL(k_repack_meta, dim3(mblocks), dim3(256), 0, st, scales, asym ? zeros : nullptr, n, k,
+                     gate_up, reinterpret_cast<uint16_t*>(base + sb), asym ? base + zb : nullptr);
+  return hipGetLastError();
+}
+
+}  // namespace q4

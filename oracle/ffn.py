@@ -106,16 +106,24 @@ def widen_int8(qm):
 
 
 def group_acc(qx, w8):
-    """acc[t, n, g] = sum_{k in group g} qx[t, k] * w8[n, k], exact in int64."""
+    """acc[t, n, g] = sum_{k in group g} qx[t, k] * w8[n, k], exact.
+
+    The per-group products are evaluated by a float64 matrix product: every
+    operand is an integer with |qx| <= 128 and |w8| <= 15, so every partial sum is
+    an integer below 128 * 128 * 15 < 2^53 and float64 represents it exactly.
+    """
     qx = np.asarray(qx, dtype=np.int64)
     w8 = np.asarray(w8, dtype=np.int64)
+    assert np.all(np.abs(qx) <= 128) and np.all(np.abs(w8) <= 15)
     t, k = qx.shape
     n = w8.shape[0]
     g = k // GROUP
+    qf = qx.astype(np.float64)
+    wf = w8.astype(np.float64)
     acc = np.empty((t, n, g), dtype=np.int64)
     for gi in range(g):
         sl = slice(gi * GROUP, (gi + 1) * GROUP)
-        acc[:, :, gi] = qx[:, sl] @ w8[:, sl].T               # integer matmul, exact
+        acc[:, :, gi] = (qf[:, sl] @ wf[:, sl].T).astype(np.int64)
     return acc
 
 

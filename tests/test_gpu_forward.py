@@ -1,0 +1,178 @@
+"""GPU parity of the MoE / FFN forward (W4A16, W4A8) against the fp64 oracle."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import ffn, router
+from tests.helpers import OracleExperts, build_gpu_layer, random_expert_maker, require_gpu
+
+pytestmark = pytest.mark.gpu
+
+TOL_W4A16 = 5e-3
+TOL_W4A8 = 2e-2
+
+
+@pytest.fixture(scope="module")
+def lib():
+    require_gpu()
+    import int4_group_quantized_g128_amd as lib
+    return lib
+
+
+def _np(t):
+    return synth.to_numpy(t)
+
+
+def _forward(lib, layer, x, ids, w, mode):
+    out = lib.moe_int4_ffn_forward(layer, x.cuda(), torch.as_tensor(ids, dtype=torch.int32).cuda(),
+                                   torch.as_tensor(w, dtype=torch.float32).cuda(), mode=mode)
+    torch.cuda.synchronize()
+    return out
+
+
+def _oracle_route(x, name):
+    cfg = synth.CONFIGS[name]
+    w, b = synth.router_weights(name)
+    _, ids, wts = router.route(_np(x), _np(w), _np(b) if b is not None else None, cfg["top_k"])
+    return ids, wts
+
+
+# ------------------------------------------------------------------ small layer with a shared expert
+SMALL = dict(e=16, h=256, i=128, k=4)
+
+
+@pytest.fixture(scope="module", params=[False, True], ids=["sym", "asym"])
+def small(lib, request):
+    asym = request.param
+    make = random_expert_maker(11 + asym, SMALL["h"], SMALL["i"])
+    layer = build_gpu_layer(lib, make, SMALL["e"], SMALL["h"], SMALL["i"], SMALL["k"], asym=asym, shared=True)
+    return layer, OracleExperts(make, asym)
+
+
+@pytest.mark.parametrize("mode", [0, 1], ids=["w4a16", "w4a8"])
+@pytest.mark.parametrize("t", [1, 5, 33, 100])
+def test_small_shared_layer(lib, small, mode, t):
+    layer, oe = small
+    x = synth.normal(synth.stream_key(12, t), (t, SMALL["h"]), 1.0).to(torch.bfloat16)
+    rng = np.random.default_rng(t)
+    ids = np.stack([rng.permutation(SMALL["e"])[: SMALL["k"]] for _ in range(t)]).astype(np.int32)
+    L = rng.normal(size=(t, SMALL["e"]))
+    w = np.take_along_axis(np.exp(L), ids.astype(np.int64), axis=1)
+    w /= w.sum(axis=1, keepdims=True)
+    out = _forward(lib, layer, x, ids, w, mode)
+    fn = ffn.moe_w4a16 if mode == 0 else ffn.moe_w4a8
+    ref = fn(_np(x), oe, ids, w, shared=oe(SMALL["e"]))
+    assert ffn.max_rel_l2(_np(out), ref) <= (TOL_W4A16 if mode == 0 else TOL_W4A8)
+
+
+def test_zero_tokens_is_noop(lib, small):
+    layer, _ = small
+    x = torch.zeros((0, SMALL["h"]), dtype=torch.bfloat16)
+    out = _forward(lib, layer, x, np.zeros((0, SMALL["k"])), np.zeros((0, SMALL["k"])), 0)
+    assert out.shape == (0, SMALL["h"])
+
+
+def test_zero_input_gives_zero_output(lib, small):
+    layer, _ = small
+    x = torch.zeros((7, SMALL["h"]), dtype=torch.bfloat16)
+    ids = np.tile(np.arange(SMALL["k"], dtype=np.int32), (7, 1))
+    w = np.full((7, SMALL["k"]), 1.0 / SMALL["k"])
+    for mode in (0, 1):
+        assert torch.count_nonzero(_forward(lib, layer, x, ids, w, mode)) == 0
+
+
+def test_hot_expert_and_deterministic(lib, small):
+    layer, oe = small
+    t = 150
+    x = synth.normal(synth.stream_key(13, t), (t, SMALL["h"]), 1.0).to(torch.bfloat16)
+    ids = np.tile(np.array([3, 0, 9, 15], dtype=np.int32), (t, 1))   # every token on the same experts
+    w = np.tile(np.array([0.4, 0.3, 0.2, 0.1]), (t, 1))
+    a = _forward(lib, layer, x, ids, w, 0)
+    b = _forward(lib, layer, x, ids, w, 0)
+    assert torch.equal(a, b)
+    ref = ffn.moe_w4a16(_np(x), oe, ids, w, shared=oe(SMALL["e"]))
+    assert ffn.max_rel_l2(_np(a), ref) <= TOL_W4A16
+
+
+# ------------------------------------------------------------------ dense SwiGLU FFN (E = 1)
+@pytest.fixture(scope="module")
+def dense(lib):
+    cfg = synth.CONFIGS["dense"]
+    g, u, d = synth.dense_ffn_weights("dense")
+    layer = lib.MoELayer(1, cfg["hidden"], cfg["inter"], 1, asymmetric=True)
+    layer.set_expert(0, g.cuda(), u.cuda(), d.cuda())
+    torch.cuda.synchronize()
+    oe = OracleExperts(lambda e: (g, u, d), True)
+    return layer, oe
+
+
+@pytest.mark.parametrize("t", [1, 4, 16])
+def test_dense_ffn_asym_w4a16(lib, dense, t):
+    layer, oe = dense
+    x = synth.tokens("dense", t)
+    ids = np.zeros((t, 1), np.int32)
+    w = np.ones((t, 1))
+    out = _forward(lib, layer, x, ids, w, 0)
+    ref = ffn.swiglu_w4a16(_np(x), *oe(0))
+    assert ffn.max_rel_l2(_np(out), ref) <= TOL_W4A16
+
+
+def test_dense_ffn_asym_w4a8(lib, dense):
+    layer, oe = dense
+    x = synth.tokens("dense", 16)
+    out = _forward(lib, layer, x, np.zeros((16, 1), np.int32), np.ones((16, 1)), 1)
+    ref = ffn.swiglu_w4a8(_np(x), *oe(0))
+    assert ffn.max_rel_l2(_np(out), ref) <= TOL_W4A8
+
+
+# ------------------------------------------------------------------ 8 experts, top-2 (slice mode)
+@pytest.fixture(scope="module")
+def moe8(lib):
+    cfg = synth.CONFIGS["moe8"]
+    make = lambda e, device="cpu": synth.expert_weights("moe8", e, device)
+    layer = build_gpu_layer(lib, make, cfg["experts"], cfg["hidden"], cfg["inter"], cfg["top_k"])
+    return layer, OracleExperts(make, False)
+
+
+@pytest.mark.parametrize("t", [1, 2, 16, 64, 256])
+def test_moe8_w4a16(lib, moe8, t):
+    layer, oe = moe8
+    x = synth.tokens("moe8", t)
+    ids, w = _oracle_route(x, "moe8")
+    out = _forward(lib, layer, x, ids, w, 0)
+    ref = ffn.moe_w4a16(_np(x), oe, ids, w)
+    assert ffn.max_rel_l2(_np(out), ref) <= TOL_W4A16
+
+
+def test_moe8_slice_identity(lib, moe8):
+    """k = E with unit weights reproduces the dense FFN the experts were sliced from."""
+    layer, _ = moe8
+    cfg = synth.CONFIGS["moe8"]
+    t = 8
+    x = synth.tokens("moe8", t, salt=5)
+    ids = np.tile(np.arange(8, dtype=np.int32), (t, 1))
+    # a layer with top_k = 8 over the same weights
+    full = type(layer).__new__(type(layer))
+    full.__dict__.update(layer.__dict__)
+    full.top_k = 8
+    full.desc = type(layer.desc)(8, cfg["hidden"], cfg["inter"], 8, 0, 0, layer.gate_up.data_ptr(),
+                                 layer.down.data_ptr(), None, None)
+    out = _forward(lib, full, x, ids, np.ones((t, 8)), 0)
+    g, u, d = synth.dense_ffn_weights("moe8")
+    from tests.helpers import oracle_qmat
+    ref = ffn.swiglu_w4a16(_np(x), oracle_qmat(g, False), oracle_qmat(u, False), oracle_qmat(d, False))
+    assert ffn.max_rel_l2(_np(out), ref) <= TOL_W4A16
+
+
+@pytest.mark.parametrize("t", [40, 2048])
+def test_moe8_w4a8(lib, moe8, t):
+    """The W4A8 prefill workload (1 % hot channels x10); at T = 2048 the oracle checks a
+    seeded sample of tokens (tokens are independent given the routing)."""
+    layer, oe = moe8
+    x = synth.tokens("moe8_w4a8", t)
+    ids, w = _oracle_route(x, "moe8_w4a8")
+    out = _forward(lib, layer, x, ids, w, 1)
+    rows = np.arange(t) if t <= 64 else np.sort(np.random.default_rng(4).choice(t, 48, replace=False))
+    ref = ffn.moe_w4a8(_np(x)[rows], oe, ids[rows], w[rows])
+    assert ffn.max_rel_l2(_np(out)[rows], ref) <= TOL_W4A8
