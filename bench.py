@@ -1,0 +1,313 @@
+"""Benchmark of the INT4 g128 MoE SwiGLU FFN forward on one MI355X.
+
+A step is one pass of the hot path over one batch: fp32 router (logits, softmax,
+top-k) -> permutation -> fused gate/up + SwiGLU grouped GEMM -> down grouped GEMM ->
+weighted combine (+ the shared expert), all through the C ABI of libq4moe.so.
+
+Default workload: the large MoE layer on one GPU (hidden 7168, 256 routed experts of
+intermediate 2048 plus one shared expert, top-8, fp32 router with a Zipf-shaping
+bias, symmetric INT4 g128 weights, 5.84 GB packed), decode batch T = 64, W4A16.
+Weights and tokens are seeded synthetic data made on the GPU by the counter-based
+generator in ``synth`` (the oracle can regenerate any expert on the host).
+
+Prints one JSON line (see the keys below).  ``--gpus N`` with N > 1 exits: this
+build runs on one GPU.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0      # dense bf16 MFMA
+INT8_PEAK_TOPS = 5000.0        # dense int8 MFMA
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--tokens", type=int, default=64)
+    p.add_argument("--mode", choices=["w4a16", "w4a8"], default="w4a16")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-tokens", type=int, default=2, help="tokens in the oracle's timed sample")
+    p.add_argument("--no-extra", action="store_true", help="skip the secondary workloads")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="also run a plain 512 MiB device copy (HBM counter calibration)")
+    return p.parse_args()
+
+
+class Workload:
+    """Device-resident layer + router + tokens + preallocated buffers for one config."""
+
+    def __init__(self, lib, torch, synth, cfg_name, t, mode):
+        self.lib, self.torch = lib, torch
+        cfg = synth.CONFIGS[cfg_name]
+        self.cfg_name, self.cfg, self.t = cfg_name, cfg, t
+        self.mode = lib.Q4_W4A8 if mode == "w4a8" else lib.Q4_W4A16
+        e, h, i, k = cfg["experts"], cfg["hidden"], cfg["inter"], cfg["top_k"]
+        shared = bool(cfg.get("shared", False))
+        self.layer = lib.MoELayer(e, h, i, k, asymmetric=cfg["asymmetric"], shared=shared)
+        for j in range(e + (1 if shared else 0)):
+            g, u, d = synth.expert_weights(cfg_name, j, device="cuda")
+            self.layer.set_expert(j, g, u, d)
+            del g, u, d
+        self.wr, self.bias = synth.router_weights(cfg_name, device="cuda")
+        self.x = synth.tokens(cfg_name, t, device="cuda")
+        dev = "cuda"
+        self.logits = torch.empty((t, e), dtype=torch.float32, device=dev)
+        self.ids = torch.empty((t, k), dtype=torch.int32, device=dev)
+        self.w = torch.empty((t, k), dtype=torch.float32, device=dev)
+        self.rws_bytes = int(lib._lib.raw.moe_route_workspace_bytes(t, h, e))
+        self.rws = torch.empty(max(self.rws_bytes, 1), dtype=torch.uint8, device=dev)
+        self.out = torch.empty((t, h), dtype=torch.bfloat16, device=dev)
+        self.ws_bytes = self.layer.workspace_bytes(t, self.mode)
+        self.ws = torch.empty(max(self.ws_bytes, 1), dtype=torch.uint8, device=dev)
+        torch.cuda.synchronize()
+
+    def retoken(self, synth, t):
+        """Same layer and router, a new batch of t tokens with its own buffers."""
+        torch = self.torch
+        other = Workload.__new__(Workload)
+        other.__dict__.update(self.__dict__)
+        other.t = t
+        e, h, k = self.cfg["experts"], self.cfg["hidden"], self.cfg["top_k"]
+        other.x = synth.tokens(self.cfg_name, t, device="cuda")
+        other.logits = torch.empty((t, e), dtype=torch.float32, device="cuda")
+        other.ids = torch.empty((t, k), dtype=torch.int32, device="cuda")
+        other.w = torch.empty((t, k), dtype=torch.float32, device="cuda")
+        other.rws_bytes = int(self.lib._lib.raw.moe_route_workspace_bytes(t, h, e))
+        other.rws = torch.empty(max(other.rws_bytes, 1), dtype=torch.uint8, device="cuda")
+        other.out = torch.empty((t, h), dtype=torch.bfloat16, device="cuda")
+        other.ws_bytes = self.layer.workspace_bytes(t, self.mode)
+        other.ws = torch.empty(max(other.ws_bytes, 1), dtype=torch.uint8, device="cuda")
+        return other
+
+    def step(self):
+        L = self.lib._lib
+        raw, P, st = L.raw, L._ptr, L._stream()
+        e, h, k = self.cfg["experts"], self.cfg["hidden"], self.cfg["top_k"]
+        rc = raw.moe_route_topk(P(self.x), P(self.wr), P(self.bias), self.t, h, e, k, P(self.logits),
+                                P(self.ids), P(self.w), P(self.rws), self.rws_bytes, st)
+        if rc:
+            raise L.Q4Error("moe_route_topk", rc)
+        rc = raw.moe_int4_ffn_forward(L.ctypes.byref(self.layer.desc), P(self.x), self.t, P(self.ids), P(self.w),
+                                      self.mode, P(self.out), P(self.ws), self.ws_bytes, st)
+        if rc:
+            raise L.Q4Error("moe_int4_ffn_forward", rc)
+
+    def touched(self):
+        """Experts with at least one routed row (+ the shared expert)."""
+        ids = self.ids.cpu()
+        n = int(self.torch.unique(ids).numel())
+        return n + (1 if self.layer.shared else 0)
+
+    def expert_bytes(self):
+        """Canonical packed bytes of one expert: nibbles + fp16 scales (+ zero points)."""
+        h, i = self.cfg["hidden"], self.cfg["inter"]
+        gu = 2 * i * h // 2 + 2 * i * (h // 128) * 2
+        dn = h * i // 2 + h * (i // 128) * 2
+        if self.cfg["asymmetric"]:
+            gu += 2 * i * ((h // 128 + 1) // 2)
+            dn += h * ((i // 128 + 1) // 2)
+        return gu, dn
+
+    def flops(self):
+        """Algorithmic matrix flops of the expert GEMMs (routed slots + shared rows)."""
+        h, i, k = self.cfg["hidden"], self.cfg["inter"], self.cfg["top_k"]
+        rows = self.t * (k + (1 if self.layer.shared else 0))
+        return 2.0 * rows * 3 * h * i
+
+
+def time_steps(torch, wl, steps, warmup, stage_events):
+    lib = wl.lib
+    for _ in range(warmup):
+        wl.step()
+    torch.cuda.synchronize()
+    evs = []
+    if stage_events:
+        for _ in range(steps):
+            b = [torch.cuda.Event(enable_timing=True) for _ in lib._lib.STAGES]
+            e = [torch.cuda.Event(enable_timing=True) for _ in lib._lib.STAGES]
+            for ev in b + e:
+                ev.record()  # creates the underlying HIP event; the library re-records it
+            evs.append((b, e))
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(steps):
+        if stage_events:
+            lib._lib.set_stage_events(*evs[s])
+        wl.step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    lib._lib.set_stage_events(None, None)
+    stage_ms = {}
+    if stage_events:
+        used = ["permute", "gate_up", "down", "combine"] if wl.mode == lib.Q4_W4A16 else list(lib._lib.STAGES)
+        for name in used:
+            si = lib._lib.STAGES.index(name)
+            stage_ms[name] = sum(b[si].elapsed_time(e[si]) for b, e in evs) / steps
+    return (t1 - t0) / steps, stage_ms
+
+
+def summarize(wl, sec_per_step, stage_ms):
+    touched = wl.touched()
+    gu_b, dn_b = wl.expert_bytes()
+    h, i = wl.cfg["hidden"], wl.cfg["inter"]
+    rows = wl.t * (wl.cfg["top_k"] + (1 if wl.layer.shared else 0))
+    layer_bytes = touched * (gu_b + dn_b)
+    res = {
+        "tokens": wl.t,
+        "tokens_per_s": wl.t / sec_per_step,
+        "ms_per_step": sec_per_step * 1e3,
+        "experts_touched": touched,
+        "effective_weight_GBps": layer_bytes / sec_per_step / 1e9,
+        "hbm_frac": layer_bytes / sec_per_step / 1e9 / HBM_PEAK_GBS,
+        "stage_ms": {k: round(v, 5) for k, v in stage_ms.items()},
+    }
+    flops = wl.flops()
+    peak = INT8_PEAK_TOPS if wl.mode == wl.lib.Q4_W4A8 else BF16_PEAK_TFLOPS
+    res["mfma_frac"] = flops / sec_per_step / 1e12 / peak
+    if "gate_up" in stage_ms:
+        act = rows * h * (1 if wl.mode == wl.lib.Q4_W4A8 else 2) + rows * i * (4 if wl.mode == wl.lib.Q4_W4A8 else 2)
+        res["gate_up_bytes"] = touched * gu_b + act
+        res["gate_up_GBps"] = res["gate_up_bytes"] / (stage_ms["gate_up"] * 1e-3) / 1e9
+        res["gate_up_flops"] = 2.0 * rows * 2 * i * h
+    return res
+
+
+def cpu_baseline(synth, wl, ntok):
+    """The oracle (fp64 NumPy) on the first ``ntok`` tokens of the batch: router + MoE
+    forward with the shared expert; expert quantisation (offline) is not timed."""
+    import numpy as np
+    from oracle import ffn, quant, router
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        cores = len(os.sched_getaffinity(0))
+    x = synth.to_numpy(wl.x[:ntok])
+    wr, b = synth.to_numpy(wl.wr), synth.to_numpy(wl.bias) if wl.bias is not None else None
+    k = wl.cfg["top_k"]
+    # routing of the sample decides which experts the oracle needs (untimed preparation)
+    ids0 = router.select_topk(router.logits_fp64(x, wr, b), k)
+    need = sorted(set(int(v) for v in ids0.ravel()))
+    shared_e = wl.cfg["experts"] if wl.layer.shared else None
+    experts = {}
+    for e in need + ([shared_e] if shared_e is not None else []):
+        g, u, d = synth.expert_weights(wl.cfg_name, e)
+        experts[e] = tuple((lambda q: (q[0].astype(np.int64), q[1], None))(quant.quantize_sym(synth.to_numpy(m)))
+                           for m in (g, u, d))
+    # the timed sample is repeated until about 10 s of CPU work have been done
+    reps, dt = 0, 0.0
+    t0 = time.perf_counter()
+    while reps == 0 or (dt < 10.0 and reps < 64):
+        L = router.logits_fp64(x, wr, b)
+        ids = router.select_topk(L, k)
+        w = router.topk_weights(L, ids)
+        out = ffn.moe_w4a16(x, lambda e: experts[e], ids, w, shared=experts.get(shared_e))
+        reps += 1
+        dt = time.perf_counter() - t0
+    assert np.all(np.isfinite(out))
+    return {"value": ntok * reps / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"oracle router + W4A16 MoE forward (fp64 NumPy) on {ntok} of the {wl.t} tokens "
+                      f"({len(need)} routed experts + shared), repeated {reps}x: {dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1"}))
+        log("bench.py: only --gpus 1 is supported (single-GPU build)")
+        return 2
+    import torch
+    import int4_group_quantized_g128_amd as lib
+    import synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    log(f"[bench] building moe256 layer (T={args.tokens}, {args.mode})")
+    wl = Workload(lib, torch, synth, "moe256", args.tokens, args.mode)
+    log(f"[bench] layer weights {wl.layer.weight_bytes() / 1e9:.3f} GB; timing {args.steps} steps")
+    sec, stage_ms = time_steps(torch, wl, args.steps, args.warmup, stage_events=True)
+    main_res = summarize(wl, sec, stage_ms)
+    log(f"[bench] main: {json.dumps(main_res)}")
+
+    roof = None
+    if "gate_up_GBps" in main_res:
+        roof = {"kernel": "k_gemm gate/up + SwiGLU (W4A16, 16-row tiles)", "bound": "hbm",
+                "achieved": round(main_res["gate_up_GBps"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(main_res["gate_up_GBps"] / HBM_PEAK_GBS, 4), "traffic": None,
+                "algorithmic_bytes_per_launch": main_res["gate_up_bytes"],
+                "avg_launch_ms": main_res["stage_ms"]["gate_up"]}
+
+    extra = {}
+    if not args.no_extra:
+        for t in (1, 4096):
+            if t == args.tokens:
+                continue
+            log(f"[bench] extra moe256 T={t}")
+            wl2 = wl.retoken(synth, t)
+            steps = 10 if t > 1000 else 50
+            s2, st2 = time_steps(torch, wl2, steps, 3, stage_events=True)
+            extra[f"moe256_T{t}_w4a16"] = summarize(wl2, s2, st2)
+            del wl2
+            torch.cuda.empty_cache()
+        log("[bench] extra moe8 W4A8 prefill T=2048")
+        w8 = Workload(lib, torch, synth, "moe8_w4a8", 2048, "w4a8")
+        s3, st3 = time_steps(torch, w8, 20, 5, stage_events=True)
+        extra["moe8_T2048_w4a8"] = summarize(w8, s3, st3)
+        del w8
+
+    if args.copy_calibration:
+        n = 512 * 1024 * 1024
+        src = torch.empty(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        extra["copy_calibration_bytes"] = n
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log(f"[bench] cpu baseline: oracle on {args.cpu_tokens} tokens")
+        cpu = cpu_baseline(synth, wl, args.cpu_tokens)
+
+    res = {
+        "metric": "tokens/s per MoE layer forward (INT4 g128 experts, router to combine)",
+        "value": round(main_res["tokens_per_s"], 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(main_res["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if args.mode == "w4a16" else "int8",
+        "data": "synthetic",
+        "config": {"workload": f"moe256 decode: hidden 7168, 256 experts x inter 2048 + 1 shared, top-8, "
+                               f"INT4 g128 sym, T={args.tokens}, {args.mode}",
+                   "tokens": args.tokens, "experts_touched": main_res["experts_touched"],
+                   "effective_weight_GBps": round(main_res["effective_weight_GBps"], 1),
+                   "hbm_frac": round(main_res["hbm_frac"], 4)},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "stage_ms": main_res["stage_ms"],
+        "extra": extra,
+    }
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -248,6 +248,23 @@ Q4_API int int4_linear_forward(const void* x, int x_dtype, int64_t t, int64_t k,
 Q4_API int int4_w4a8_group_acc(const int8_t* q, int64_t rows, int64_t k, const void* w_dev, int64_t n,
                         int asymmetric, int32_t* acc, hipStream_t stream);
 
+/*
+ * q4_set_stage_events -- optional per-stage timing markers for profiling tools.
+ * When set (count >= Q4_NUM_STAGES, non-NULL arrays), every later
+ * moe_int4_ffn_forward call on this thread records begin[s] before and end[s] after
+ * the launches of stage s on its stream (hipEventRecord), for the stages it runs.
+ * The events (hipEvent_t handles) are owned by the caller and must outlive their
+ * use.  count == 0 or NULL arrays disable the markers.  Thread-local.
+ */
+#define Q4_STAGE_PERMUTE 0
+#define Q4_STAGE_X_QUANT 1
+#define Q4_STAGE_GATE_UP 2
+#define Q4_STAGE_H_QUANT 3
+#define Q4_STAGE_DOWN 4
+#define Q4_STAGE_COMBINE 5
+#define Q4_NUM_STAGES 6
+Q4_API int q4_set_stage_events(void* const* begin, void* const* end, int count);
+
 #ifdef __cplusplus
 }
 #endif

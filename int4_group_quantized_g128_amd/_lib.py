@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(_HERE, "libq4moe.so")
 if not os.path.exists(LIB_PATH):
     raise ImportError(
         f"{LIB_PATH} is missing: build the HIP library first "
-        "(python -m int4_group_quantized_g128_amd.build, or __graft_entry__.build())")
+        "(python int4_group_quantized_g128_amd/build.py, or __graft_entry__.build())")
 
 _lib = ctypes.CDLL(LIB_PATH)
 
@@ -64,7 +64,11 @@ _sig("moe_int4_ffn_forward", _int, [ctypes.POINTER(Q4MoELayer), _vp, _i64, _vp, 
 _sig("int4_linear_forward", _int, [_vp, _int, _i64, _i64, _vp, _i64, _int, _vp, _vp])
 _sig("int4_w4a8_group_acc", _int, [_vp, _i64, _i64, _vp, _i64, _int, _vp, _vp])
 
+_sig("q4_set_stage_events", _int, [ctypes.POINTER(_vp), ctypes.POINTER(_vp), _int])
+
 raw = _lib  # the C entry points, for tests of the ABI itself
+
+STAGES = ("permute", "x_quant", "gate_up", "h_quant", "down", "combine")
 
 
 class Q4Error(RuntimeError):
@@ -106,6 +110,19 @@ _DT = {torch.float32: Q4_F32, torch.float16: Q4_F16, torch.bfloat16: Q4_BF16}
 
 def version():
     return _lib.q4_version().decode()
+
+
+def set_stage_events(begin, end):
+    """Per-stage HIP event markers for moe_int4_ffn_forward on this thread: ``begin``
+    and ``end`` are lists of torch.cuda.Event (enable_timing=True), one per stage
+    (STAGES order); None disables."""
+    if begin is None:
+        _check("q4_set_stage_events", _lib.q4_set_stage_events(None, None, 0))
+        return
+    arr = ctypes.c_void_p * len(STAGES)
+    b = arr(*[ctypes.c_void_p(e.cuda_event) for e in begin])
+    e_ = arr(*[ctypes.c_void_p(e.cuda_event) for e in end])
+    _check("q4_set_stage_events", _lib.q4_set_stage_events(b, e_, len(STAGES)))
 
 
 # ------------------------------------------------------------------ A1 / A2

@@ -1,6 +1,7 @@
 """Builds libq4moe.so (gfx950) in-tree with hipcc.
 
-Usage: ``python -m int4_group_quantized_g128_amd.build`` or ``build()``.
+Usage: ``python int4_group_quantized_g128_amd/build.py`` (by path, so that a stale
+library is not loaded first) or ``__graft_entry__.build()``.
 """
 import os
 import subprocess

@@ -13,6 +13,16 @@ using namespace q4;
 namespace {
 
 thread_local std::string g_last_error;
+thread_local hipEvent_t g_stage_begin[Q4_NUM_STAGES];
+thread_local hipEvent_t g_stage_end[Q4_NUM_STAGES];
+thread_local bool g_stage_events = false;
+
+void stage_begin(int s, hipStream_t st) {
+  if (g_stage_events) (void)hipEventRecord(g_stage_begin[s], st);
+}
+void stage_end(int s, hipStream_t st) {
+  if (g_stage_events) (void)hipEventRecord(g_stage_end[s], st);
+}
 
 int fail(int code, const char* fmt, ...) {
   char buf[512];
@@ -144,6 +154,22 @@ const char* q4_last_error(void) { return g_last_error.c_str(); }
 
 const char* q4_version(void) { return "q4moe 0.1 gfx950"; }
 
+int q4_set_stage_events(void* const* begin, void* const* end, int count) {
+  g_last_error.clear();
+  if (count == 0 || !begin || !end) {
+    g_stage_events = false;
+    return ok();
+  }
+  Q4_REQUIRE(count >= Q4_NUM_STAGES, Q4_ERR_SHAPE, "need %d events per array", Q4_NUM_STAGES);
+  for (int i = 0; i < Q4_NUM_STAGES; ++i) {
+    Q4_REQUIRE(begin[i] && end[i], Q4_ERR_NULL, "event %d is NULL", i);
+    g_stage_begin[i] = static_cast<hipEvent_t>(begin[i]);
+    g_stage_end[i] = static_cast<hipEvent_t>(end[i]);
+  }
+  g_stage_events = true;
+  return ok();
+}
+
 int quantize_int4_g128(const void* w, int w_dtype, int64_t n, int64_t k, int asymmetric, uint8_t* packed,
                        uint16_t* scales, uint8_t* zeros, int32_t* flags_dev, hipStream_t stream) {
   g_last_error.clear();
@@ -252,10 +278,12 @@ int moe_int4_ffn_forward(const q4_moe_layer_t* L, const uint16_t* x_bf16, int64_
   const int64_t H = L->hidden, I = L->inter;
   const int rb = w.tile_rows / 16;
   int rc;
+  stage_begin(Q4_STAGE_PERMUTE, stream);
   if ((rc = check_hip(launch_permute(topk_ids, t, L->top_k, L->num_experts, shared, w.counts, w.offsets, w.perm,
                                      w.inv, w.tiles, w.num_tiles, w.tile_rows, stream),
                       "permute")))
     return rc;
+  stage_end(Q4_STAGE_PERMUTE, stream);
   GemmArgs gu{};
   gu.perm = w.perm;
   gu.slots_per_token = int32_t(S);
@@ -281,19 +309,34 @@ int moe_int4_ffn_forward(const q4_moe_layer_t* L, const uint16_t* x_bf16, int64_
   if (mode == Q4_W4A16) {
     gu.a = x_bf16;
     dn.a = w.h;
+    stage_begin(Q4_STAGE_GATE_UP, stream);
     if ((rc = check_hip(launch_gemm(gu, 0, GEMM_GATE_UP, rb, stream), "gate/up gemm"))) return rc;
+    stage_end(Q4_STAGE_GATE_UP, stream);
+    stage_begin(Q4_STAGE_DOWN, stream);
     if ((rc = check_hip(launch_gemm(dn, 0, GEMM_PLAIN, rb, stream), "down gemm"))) return rc;
+    stage_end(Q4_STAGE_DOWN, stream);
   } else {
+    stage_begin(Q4_STAGE_X_QUANT, stream);
     if ((rc = check_hip(launch_act_quant(x_bf16, 0, t, H, w.qx, w.sx, nullptr, stream), "x quant"))) return rc;
+    stage_end(Q4_STAGE_X_QUANT, stream);
     gu.a = w.qx;
     gu.a_scale = w.sx;
+    stage_begin(Q4_STAGE_GATE_UP, stream);
     if ((rc = check_hip(launch_gemm(gu, 2, GEMM_GATE_UP, rb, stream), "gate/up gemm"))) return rc;
+    stage_end(Q4_STAGE_GATE_UP, stream);
+    stage_begin(Q4_STAGE_H_QUANT, stream);
     if ((rc = check_hip(launch_act_quant(w.h, 1, t * S, I, w.qh, w.sh, nullptr, stream), "h quant"))) return rc;
+    stage_end(Q4_STAGE_H_QUANT, stream);
     dn.a = w.qh;
     dn.a_scale = w.sh;
+    stage_begin(Q4_STAGE_DOWN, stream);
     if ((rc = check_hip(launch_gemm(dn, 2, GEMM_PLAIN, rb, stream), "down gemm"))) return rc;
+    stage_end(Q4_STAGE_DOWN, stream);
   }
-  return check_hip(launch_combine(w.y, w.inv, topk_w, t, L->top_k, shared, H, out_bf16, stream), "combine");
+  stage_begin(Q4_STAGE_COMBINE, stream);
+  rc = check_hip(launch_combine(w.y, w.inv, topk_w, t, L->top_k, shared, H, out_bf16, stream), "combine");
+  stage_end(Q4_STAGE_COMBINE, stream);
+  return rc;
 }
 
 int int4_linear_forward(const void* x, int x_dtype, int64_t t, int64_t k, const void* w_dev, int64_t n, int asymmetric,

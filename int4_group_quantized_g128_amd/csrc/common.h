@@ -107,21 +107,6 @@ Q4_DEVICE f32x4_t mfma_f32_16x16x4(float a, float b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-// Sum of the 8 activation elements held in one 16-byte fragment, fp32 accumulate.
-template <Act A>
-Q4_DEVICE float frag_sum(const uint32_t a[4], float acc) {
-  if constexpr (A == Act::BF16) {
-    const bf16x2_t one = bitcast<bf16x2_t>(0x3f803f80u);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) acc = __builtin_amdgcn_fdot2_f32_bf16(bitcast<bf16x2_t>(a[i]), one, acc, false);
-  } else {
-    const f16x2_t one = bitcast<f16x2_t>(0x3c003c00u);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) acc = __builtin_amdgcn_fdot2(bitcast<f16x2_t>(a[i]), one, acc, false);
-  }
-  return acc;
-}
-
 // ---------------------------------------------------------------- global loads
 Q4_DEVICE uint4 load16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 Q4_DEVICE uint2 load8(const void* p) { return *reinterpret_cast<const uint2*>(p); }

@@ -14,9 +14,12 @@
 //    LDS at the end;
 //  - each lane streams its 16-byte share of each 1 KB weight tile (one column block x
 //    one group), widens the nibbles in registers and feeds the matrix core;
-//  - W4A16: the widened value is magic + d (exact in bf16/f16); per group
-//    gacc = sum x * (magic + d) over 4 MFMA 16x16x32, then acc += s * gacc and an fp32
-//    MFMA 16x16x4 adds -s * (magic + z) * sum_{k in g} x from the lanes' partial sums;
+//  - W4A16 (bf16): the widened value is magic + d (exact in bf16); per group
+//    gacc = sum x * (magic + d) over 4 MFMA 16x16x32 and the row sums xs = sum x over
+//    4 MFMA with B = 1.0, then acc += s * (gacc - (magic + z) * xs) in fp32;
+//  - fp16 activations: magic + d - (magic + z) = d - z is formed exactly with a packed
+//    fp16 add, so gacc = sum x * (d - z) directly and acc += s * gacc;
+//  - the loads of group g + 1 are issued before group g is computed (two stages);
 //  - W4A8: 16 * (d - 8) as int8, two MFMA i32 16x16x64 per group, the INT32 group
 //    accumulator is gacc / 16 (- (z - 8) * sum q_x for asymmetric weights), then
 //    acc += s_w * acc_g in fp32 and the row scale s_x at the end.
@@ -150,75 +153,109 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs args) {
 #pragma unroll
       for (int nb = 0; nb < kNB; ++nb) acc[mb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    for (int64_t g = g_beg; g < g_end; ++g) {
-      // weights: 16 bytes of each of the 4 tiles
+    // One group's operands: 16 bytes of each of the 4 weight tiles, the lane column's
+    // scale / zero point, and the A fragments of the MB row blocks.
+    struct Stage {
       uint32_t wv[kNB][4];
+      uint16_t sc[kNB];
+      uint8_t zp[kNB];
+      uint32_t av[MB][4][4];
+    };
+    auto load_stage = [&](Stage& st, int64_t g) {
 #pragma unroll
       for (int nb = 0; nb < kNB; ++nb) {
-        const uint4 v = load16(wbase + ((cb0 + nb) * G + g) * kTileBytes + lane * 16);
-        wv[nb][0] = v.x; wv[nb][1] = v.y; wv[nb][2] = v.z; wv[nb][3] = v.w;
-      }
-      float sc[kNB], zz[kNB];
-#pragma unroll
-      for (int nb = 0; nb < kNB; ++nb) {
+        const uint4 v = load16_stream(wbase + ((cb0 + nb) * G + g) * kTileBytes + lane * 16);
+        st.wv[nb][0] = v.x; st.wv[nb][1] = v.y; st.wv[nb][2] = v.z; st.wv[nb][3] = v.w;
         const int64_t mi = ((cb0 + nb) * G + g) * 16 + col;
-        sc[nb] = f16_bits_to_f32(wscale[mi]);
-        zz[nb] = args.asym ? float(wzero[mi]) : 8.0f;
+        st.sc[nb] = wscale[mi];
+        st.zp[nb] = args.asym ? wzero[mi] : uint8_t(8);
       }
-      if constexpr (A != Act::I8) {
-        const uint16_t* xa = static_cast<const uint16_t*>(args.a);
-        uint32_t av[MB][4][4];
-        float part[MB];
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-          part[mb] = 0.f;
+      for (int mb = 0; mb < MB; ++mb) {
+        if constexpr (A != Act::I8) {
+          const uint16_t* xa = static_cast<const uint16_t*>(args.a) + ri[mb].src * K + g * kGroup + 8 * kq;
 #pragma unroll
           for (int s = 0; s < 4; ++s) {
             uint4 v = make_uint4(0, 0, 0, 0);
-            if (ri[mb].valid) v = load16(xa + ri[mb].src * K + g * kGroup + 32 * s + 8 * kq);
-            av[mb][s][0] = v.x; av[mb][s][1] = v.y; av[mb][s][2] = v.z; av[mb][s][3] = v.w;
-            part[mb] = frag_sum<A>(av[mb][s], part[mb]);
+            if (ri[mb].valid) v = load16(xa + 32 * s);
+            st.av[mb][s][0] = v.x; st.av[mb][s][1] = v.y; st.av[mb][s][2] = v.z; st.av[mb][s][3] = v.w;
           }
+        } else {
+          const int8_t* qa = static_cast<const int8_t*>(args.a) + ri[mb].src * K + g * kGroup + 8 * kq;
+#pragma unroll
+          for (int i = 0; i < 2; ++i) {
+            uint2 lo = make_uint2(0, 0), hi = make_uint2(0, 0);
+            if (ri[mb].valid) {
+              lo = load8(qa + 64 * i);
+              hi = load8(qa + 64 * i + 32);
+            }
+            st.av[mb][i][0] = lo.x; st.av[mb][i][1] = lo.y; st.av[mb][i][2] = hi.x; st.av[mb][i][3] = hi.y;
+          }
+        }
+      }
+    };
+    auto compute_stage = [&](const Stage& st, int64_t g) {
+      float sc[kNB];
+#pragma unroll
+      for (int nb = 0; nb < kNB; ++nb) sc[nb] = f16_bits_to_f32(st.sc[nb]);
+      if constexpr (A == Act::BF16) {
+        // exact row sums of the group through the matrix core (B = 1.0)
+        const uint32_t ones[4] = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};
+        f32x4_t xs[MB];
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+          xs[mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int s = 0; s < 4; ++s) xs[mb] = mfma16x16x32<A>(st.av[mb][s], ones, xs[mb]);
         }
 #pragma unroll
         for (int nb = 0; nb < kNB; ++nb) {
           uint32_t b[4][4];
 #pragma unroll
-          for (int s = 0; s < 4; ++s) widen_word_fp<A>(wv[nb][s], b[s]);
-          const float negc = -sc[nb] * (magic_offset<A>() + zz[nb]);
+          for (int s = 0; s < 4; ++s) widen_word_fp<A>(st.wv[nb][s], b[s]);
+          const float negz = -(magic_offset<A>() + float(st.zp[nb]));
 #pragma unroll
           for (int mb = 0; mb < MB; ++mb) {
             f32x4_t gacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int s = 0; s < 4; ++s) gacc = mfma16x16x32<A>(av[mb][s], b[s], gacc);
+            for (int s = 0; s < 4; ++s) gacc = mfma16x16x32<A>(st.av[mb][s], b[s], gacc);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[mb][nb][i] = fmaf(sc[nb], fmaf(negz, xs[mb][i], gacc[i]), acc[mb][nb][i]);
+          }
+        }
+      } else if constexpr (A == Act::F16) {
+        // magic + d - (magic + z) = d - z, exact in fp16: no correction term
+#pragma unroll
+        for (int nb = 0; nb < kNB; ++nb) {
+          const _Float16 nz = _Float16(-(magic_offset<A>() + float(st.zp[nb])));
+          const f16x2_t negz = {nz, nz};
+          uint32_t b[4][4];
+#pragma unroll
+          for (int s = 0; s < 4; ++s) {
+            widen_word_fp<A>(st.wv[nb][s], b[s]);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) b[s][r] = bitcast<uint32_t>(bitcast<f16x2_t>(b[s][r]) + negz);
+          }
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb) {
+            f32x4_t gacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < 4; ++s) gacc = mfma16x16x32<A>(st.av[mb][s], b[s], gacc);
 #pragma unroll
             for (int i = 0; i < 4; ++i) acc[mb][nb][i] = fmaf(sc[nb], gacc[i], acc[mb][nb][i]);
-            acc[mb][nb] = mfma_f32_16x16x4(part[mb], negc, acc[mb][nb]);
           }
         }
       } else {
-        const int8_t* qa = static_cast<const int8_t*>(args.a);
-        uint32_t av[MB][2][4];
         int32_t qs[MB];
+        if (args.asym) {
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-          qs[mb] = 0;
+          for (int mb = 0; mb < MB; ++mb) {
+            qs[mb] = 0;
 #pragma unroll
-          for (int i = 0; i < 2; ++i) {
-            uint2 lo = make_uint2(0, 0), hi = make_uint2(0, 0);
-            if (ri[mb].valid) {
-              const int8_t* p = qa + ri[mb].src * K + g * kGroup + 64 * i + 8 * kq;
-              lo = load8(p);
-              hi = load8(p + 32);
-            }
-            av[mb][i][0] = lo.x; av[mb][i][1] = lo.y; av[mb][i][2] = hi.x; av[mb][i][3] = hi.y;
-            if (args.asym) {
+            for (int i = 0; i < 2; ++i)
 #pragma unroll
-              for (int j = 0; j < 4; ++j) qs[mb] = __builtin_amdgcn_sdot4(int32_t(av[mb][i][j]), 0x01010101, qs[mb], false);
-            }
-          }
-          if (args.asym) {
-            // row sum over the 4 quarters, then to the C layout (rows 4 kq + i)
+              for (int j = 0; j < 4; ++j) qs[mb] = __builtin_amdgcn_sdot4(int32_t(st.av[mb][i][j]), 0x01010101, qs[mb], false);
+            // row sum over the 4 quarters (every lane of a row then holds it)
             qs[mb] += __shfl_xor(qs[mb], 16, 64);
             qs[mb] += __shfl_xor(qs[mb], 32, 64);
           }
@@ -228,15 +265,15 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs args) {
           uint32_t b[2][4];
 #pragma unroll
           for (int i = 0; i < 2; ++i) {
-            widen_word_i8(wv[nb][2 * i], b[i][0], b[i][1]);
-            widen_word_i8(wv[nb][2 * i + 1], b[i][2], b[i][3]);
+            widen_word_i8(st.wv[nb][2 * i], b[i][0], b[i][1]);
+            widen_word_i8(st.wv[nb][2 * i + 1], b[i][2], b[i][3]);
           }
-          const int32_t zoff = int32_t(zz[nb]) - 8;
+          const int32_t zoff = int32_t(st.zp[nb]) - 8;
 #pragma unroll
           for (int mb = 0; mb < MB; ++mb) {
             i32x4_t gacc = {0, 0, 0, 0};
-            gacc = mfma_i8_16x16x64(av[mb][0], b[0], gacc);
-            gacc = mfma_i8_16x16x64(av[mb][1], b[1], gacc);
+            gacc = mfma_i8_16x16x64(st.av[mb][0], b[0], gacc);
+            gacc = mfma_i8_16x16x64(st.av[mb][1], b[1], gacc);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
               int32_t a32 = gacc[i] >> 4;                    // exact: gacc = 16 * sum q (d - 8)
@@ -251,6 +288,20 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs args) {
             }
           }
         }
+      }
+    };
+
+    // two-stage software pipeline over this wave's groups: the loads of group g + 1
+    // are in flight while group g is computed
+    if (g_beg < g_end) {
+      Stage s0, s1;
+      load_stage(s0, g_beg);
+      for (int64_t g = g_beg; g < g_end; g += 2) {
+        if (g + 1 < g_end) load_stage(s1, g + 1);
+        compute_stage(s0, g);
+        if (g + 1 >= g_end) break;
+        if (g + 2 < g_end) load_stage(s0, g + 2);
+        compute_stage(s1, g + 1);
       }
     }
     if constexpr (KIND == GEMM_GROUP_ACC) continue;

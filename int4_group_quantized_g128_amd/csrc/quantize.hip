@@ -164,6 +164,12 @@ __global__ void k_repack_meta(const uint16_t* __restrict__ scales, const uint8_t
   }
 }
 
+// Zero-fills alignment padding so the device image is fully defined.
+__global__ void k_zero_bytes(uint8_t* __restrict__ p, int64_t n) {
+  for (int64_t i = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; i < n; i += int64_t(gridDim.x) * blockDim.x)
+    p[i] = 0;
+}
+
 hipError_t launch_quantize(const void* w, int dtype, int64_t n, int64_t k, int asym, uint8_t* packed,
                            uint16_t* scales, uint8_t* zeros, int32_t* flags, hipStream_t st) {
   const int64_t G = k / kGroup;
@@ -196,6 +202,13 @@ hipError_t launch_repack(const uint8_t* packed, const uint16_t* scales, const ui
   unsigned mblocks = unsigned(std::min<int64_t>((n * G + 255) / 256, 65536));
   hipLaunchKernelGGL(k_repack_meta, dim3(mblocks), dim3(256), 0, st, scales, asym ? zeros : nullptr, n, k,
                      gate_up, reinterpret_cast<uint16_t*>(base + sb), asym ? base + zb : nullptr);
+  const int64_t scale_pad = zb - (sb + 2 * n * G);
+  if (scale_pad > 0)
+    hipLaunchKernelGGL(k_zero_bytes, dim3(1), dim3(256), 0, st, base + sb + 2 * n * G, scale_pad);
+  if (asym) {
+    const int64_t zero_pad = align256(n * G) - n * G;
+    if (zero_pad > 0) hipLaunchKernelGGL(k_zero_bytes, dim3(1), dim3(256), 0, st, base + zb + n * G, zero_pad);
+  }
   return hipGetLastError();
 }
 

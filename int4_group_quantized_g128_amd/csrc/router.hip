@@ -10,7 +10,10 @@ namespace q4 {
 
 // Partial logits over one K slice: a 16-token x 16-expert tile per wave, fp32 MFMA
 // 16x16x4.  Lane (m = lane % 16, kq = lane / 16) feeds x[t0 + m][k0 + 4 kq + j] and
-// W[e0 + m][k0 + 4 kq + j] to MFMA j of each 16-wide K step.
+// W[e0 + m][k0 + 4 kq + j] to MFMA j of each 16-wide K step; 8 steps of loads are
+// issued before their MFMAs.
+constexpr int kRouteUnroll = 8;
+
 __global__ void __launch_bounds__(64) k_router_partial(const uint16_t* __restrict__ x, const float* __restrict__ wr,
                                                        int64_t t, int64_t h, int32_t e, int64_t kslice,
                                                        float* __restrict__ partial) {
@@ -20,27 +23,26 @@ __global__ void __launch_bounds__(64) k_router_partial(const uint16_t* __restric
   const int64_t ks = blockIdx.z;
   const int64_t kb = ks * kslice, ke = std::min<int64_t>(h, kb + kslice);
   const bool tv = t0 + m < t, ev = e0 + m < e;
-  const uint16_t* xr = x + (t0 + m) * h;
-  const float* wrow = wr + (e0 + m) * h;
+  const uint16_t* xr = x + (tv ? t0 + m : 0) * h;
+  const float* wrow = wr + (ev ? e0 + m : 0) * h;
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-  for (int64_t k0 = kb; k0 < ke; k0 += 16) {
-    float xa[4] = {0.f, 0.f, 0.f, 0.f}, wb[4] = {0.f, 0.f, 0.f, 0.f};
-    if (tv) {
-      const uint2 v = load8(xr + k0 + 4 * kq);
-      xa[0] = bf16_to_f32(uint16_t(v.x & 0xffff));
-      xa[1] = bf16_to_f32(uint16_t(v.x >> 16));
-      xa[2] = bf16_to_f32(uint16_t(v.y & 0xffff));
-      xa[3] = bf16_to_f32(uint16_t(v.y >> 16));
-    }
-    if (ev) {
-      const float4 v = *reinterpret_cast<const float4*>(wrow + k0 + 4 * kq);
-      wb[0] = v.x;
-      wb[1] = v.y;
-      wb[2] = v.z;
-      wb[3] = v.w;
+  for (int64_t k0 = kb; k0 < ke; k0 += 16 * kRouteUnroll) {
+    uint2 xv[kRouteUnroll];
+    float4 wv[kRouteUnroll];
+#pragma unroll
+    for (int u = 0; u < kRouteUnroll; ++u) {
+      const int64_t k = k0 + 16 * u + 4 * kq;
+      const bool kv = k0 + 16 * u < ke;
+      xv[u] = (tv && kv) ? load8(xr + k) : make_uint2(0, 0);
+      wv[u] = (ev && kv) ? *reinterpret_cast<const float4*>(wrow + k) : make_float4(0.f, 0.f, 0.f, 0.f);
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc = mfma_f32_16x16x4(xa[j], wb[j], acc);
+    for (int u = 0; u < kRouteUnroll; ++u) {
+      acc = mfma_f32_16x16x4(bf16_to_f32(uint16_t(xv[u].x & 0xffff)), wv[u].x, acc);
+      acc = mfma_f32_16x16x4(bf16_to_f32(uint16_t(xv[u].x >> 16)), wv[u].y, acc);
+      acc = mfma_f32_16x16x4(bf16_to_f32(uint16_t(xv[u].y & 0xffff)), wv[u].z, acc);
+      acc = mfma_f32_16x16x4(bf16_to_f32(uint16_t(xv[u].y >> 16)), wv[u].w, acc);
+    }
   }
   // C layout: lane holds tokens t0 + 4 kq + i, expert e0 + m
 #pragma unroll
@@ -49,6 +51,8 @@ __global__ void __launch_bounds__(64) k_router_partial(const uint16_t* __restric
     if (tt < t && ev) partial[(ks * t + tt) * e + e0 + m] = acc[i];
   }
 }
+
+constexpr int kMaxSlices = 32;
 
 // One wave per token: logits = sum of the K-slice partials in slice order + bias, then
 // k rounds of a wave-wide arg-max with the key (larger logit, then lower index), then
@@ -67,8 +71,14 @@ __global__ void __launch_bounds__(64) k_topk(const float* __restrict__ partial, 
     const int ex = lane + 64 * i;
     float s = -__builtin_inff();
     if (ex < e) {
-      s = partial[tok * e + ex];
-      for (int ks = 1; ks < kslices; ++ks) s += partial[(int64_t(ks) * t + tok) * e + ex];
+      // all slice loads in flight, then summed in slice order
+      float pv[kMaxSlices];
+#pragma unroll
+      for (int ks = 0; ks < kMaxSlices; ++ks) pv[ks] = ks < kslices ? partial[(int64_t(ks) * t + tok) * e + ex] : 0.f;
+      s = pv[0];
+#pragma unroll
+      for (int ks = 1; ks < kMaxSlices; ++ks)
+        if (ks < kslices) s += pv[ks];
       if (bias) s += bias[ex];
       logits[tok * e + ex] = s;
       if (s != s) s = -__builtin_inff();  // NaN never wins; every id stays in range
@@ -116,7 +126,7 @@ __global__ void __launch_bounds__(64) k_topk(const float* __restrict__ partial, 
 int route_kslices(int64_t t, int64_t h, int32_t e) {
   const int64_t tiles = ((e + 15) / 16) * ((t + 15) / 16);
   int64_t ks = (1024 + tiles - 1) / tiles;
-  ks = std::max<int64_t>(1, std::min<int64_t>(ks, h / 256));
+  ks = std::max<int64_t>(1, std::min<int64_t>(std::min<int64_t>(ks, h / 256), kMaxSlices));
   return int(ks);
 }
 

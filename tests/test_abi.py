@@ -1,0 +1,146 @@
+"""The C ABI loads, exports every declared symbol and rejects bad arguments on the
+host before any launch (CPU only: no call here reaches a kernel)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "q4moe.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    from int4_group_quantized_g128_amd import _lib
+    return _lib
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return re.findall(r"Q4_API\s+[\w\s\*]+?\b(\w+)\s*\(", text)
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for required in ("quantize_int4_g128", "moe_route_topk", "moe_int4_ffn_forward"):
+        assert required in names
+    assert len(names) == len(set(names))
+
+
+def test_library_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert len(names) >= 14
+    for n in names:
+        assert hasattr(L.raw, n), n
+
+
+def test_status_strings_and_version(L):
+    assert L.raw.q4_status_string(0) == b"ok"
+    for c in range(1, 8):
+        assert L.raw.q4_status_string(c) not in (b"", b"unknown status")
+    assert L.raw.q4_status_string(99) == b"unknown status"
+    assert b"gfx950" in L.raw.q4_version()
+
+
+def _err(L):
+    return L.raw.q4_last_error().decode()
+
+
+def test_quantize_validation(L):
+    r = L.raw
+    fake = ctypes.c_void_p(4096)
+    assert r.quantize_int4_g128(fake, 9, 16, 128, 0, fake, fake, None, None, None) == L.Q4_ERR_DTYPE
+    assert r.quantize_int4_g128(fake, 0, 16, 100, 0, fake, fake, None, None, None) == L.Q4_ERR_SHAPE
+    assert "128" in _err(L)
+    assert r.quantize_int4_g128(fake, 0, 0, 128, 0, fake, fake, None, None, None) == L.Q4_ERR_SHAPE
+    assert r.quantize_int4_g128(None, 0, 16, 128, 0, fake, fake, None, None, None) == L.Q4_ERR_NULL
+    assert r.quantize_int4_g128(fake, 0, 16, 128, 1, fake, fake, None, None, None) == L.Q4_ERR_NULL
+    assert r.quantize_int4_g128(fake, 0, 16, 128, 0, fake, fake, fake, None, None) == L.Q4_ERR_NULL
+    assert r.quantize_int4_g128(ctypes.c_void_p(4100), 0, 16, 128, 0, fake, fake, None, None, None) == L.Q4_ERR_ALIGN
+
+
+def test_repack_validation(L):
+    r = L.raw
+    fake = ctypes.c_void_p(4096)
+    need = r.q4_device_bytes(64, 256, 0)
+    assert need == 64 * 128 + 2 * 64 * 2 + (256 - (2 * 64 * 2) % 256) % 256
+    assert r.q4_device_bytes(40, 256, 0) == 0 and r.q4_device_bytes(64, 200, 0) == 0
+    assert r.q4_device_bytes(64, 256, 1) == need + 256
+    assert r.q4_repack_device(fake, fake, None, 64, 256, 0, 0, fake, need - 1, None) == L.Q4_ERR_WORKSPACE
+    assert r.q4_repack_device(fake, fake, None, 48, 256, 0, 1, fake, need, None) == L.Q4_ERR_SHAPE
+    assert r.q4_repack_device(fake, fake, None, 64, 256, 1, 0, fake, need * 2, None) == L.Q4_ERR_NULL
+    assert r.q4_repack_device(fake, fake, None, 64, 256, 0, 7, fake, need, None) == L.Q4_ERR_DTYPE
+
+
+def test_route_validation(L):
+    r = L.raw
+    fake = ctypes.c_void_p(4096)
+    assert r.moe_route_topk(fake, fake, None, 4, 256, 8, 9, fake, fake, fake, fake, 1 << 30, None) == L.Q4_ERR_SHAPE
+    assert r.moe_route_topk(fake, fake, None, 4, 256, 2000, 2, fake, fake, fake, fake, 1 << 30, None) == L.Q4_ERR_SHAPE
+    assert r.moe_route_topk(fake, fake, None, 4, 250, 8, 2, fake, fake, fake, fake, 1 << 30, None) == L.Q4_ERR_SHAPE
+    assert r.moe_route_topk(fake, fake, None, 4, 256, 8, 2, None, fake, fake, fake, 1 << 30, None) == L.Q4_ERR_NULL
+    need = r.moe_route_workspace_bytes(4, 256, 8)
+    assert need > 0
+    assert r.moe_route_topk(fake, fake, None, 4, 256, 8, 2, fake, fake, fake, fake, need - 1, None) == L.Q4_ERR_WORKSPACE
+    # t == 0 is a successful no-op, even without buffers
+    assert r.moe_route_topk(None, None, None, 0, 256, 8, 2, None, None, None, None, 0, None) == L.Q4_OK
+
+
+def test_permute_and_act_quant_validation(L):
+    r = L.raw
+    fake = ctypes.c_void_p(4096)
+    assert r.moe_permute(fake, 4, 3, 2, fake, fake, fake, fake, None) == L.Q4_ERR_SHAPE
+    assert r.moe_permute(fake, 4, 1, 5000, fake, fake, fake, fake, None) == L.Q4_ERR_SHAPE
+    assert r.moe_permute(fake, 4, 1, 8, None, fake, fake, fake, None) == L.Q4_ERR_NULL
+    assert r.act_quant_int8(fake, L.Q4_F16, 4, 128, fake, fake, None) == L.Q4_ERR_DTYPE
+    assert r.act_quant_int8(fake, L.Q4_BF16, 4, 100, fake, fake, None) == L.Q4_ERR_SHAPE
+    assert r.act_quant_int8(None, L.Q4_BF16, 0, 128, None, None, None) == L.Q4_OK
+
+
+def _layer(L, **kw):
+    d = dict(num_experts=8, hidden=256, inter=128, top_k=2, asymmetric=0, shared_inter=0,
+             gate_up=4096, down=8192, shared_gate_up=None, shared_down=None)
+    d.update(kw)
+    return L.Q4MoELayer(**d)
+
+
+def test_forward_validation(L):
+    r = L.raw
+    fake = ctypes.c_void_p(4096)
+    ok = _layer(L)
+    need = r.moe_int4_ffn_workspace_bytes(ctypes.byref(ok), 10, 0)
+    assert need > 0
+    assert r.moe_int4_ffn_workspace_bytes(ctypes.byref(ok), 10, 1) > need
+    call = lambda lay, t=10, mode=0, ws=need, x=fake: r.moe_int4_ffn_forward(
+        ctypes.byref(lay), x, t, fake, fake, mode, fake, fake, ws, None)
+    assert call(ok, ws=need - 1) == L.Q4_ERR_WORKSPACE
+    assert call(ok, mode=5) == L.Q4_ERR_DTYPE
+    assert call(_layer(L, top_k=9)) == L.Q4_ERR_SHAPE
+    assert call(_layer(L, hidden=200)) == L.Q4_ERR_SHAPE
+    assert call(_layer(L, inter=100)) == L.Q4_ERR_SHAPE
+    assert call(_layer(L, gate_up=None)) == L.Q4_ERR_NULL
+    assert call(_layer(L, down=8200)) == L.Q4_ERR_ALIGN
+    assert call(_layer(L, shared_inter=256, shared_gate_up=4096, shared_down=4096)) == L.Q4_ERR_UNSUPPORTED
+    assert call(_layer(L, shared_inter=128)) == L.Q4_ERR_NULL
+    assert call(ok, x=ctypes.c_void_p(4098)) == L.Q4_ERR_ALIGN
+    assert call(ok, x=None) == L.Q4_ERR_NULL
+    assert call(ok, t=-1) == L.Q4_ERR_SHAPE
+    assert call(ok, t=0, x=None) == L.Q4_OK
+    assert r.moe_int4_ffn_workspace_bytes(None, 10, 0) == 0
+
+
+def test_linear_and_group_acc_validation(L):
+    r = L.raw
+    fake = ctypes.c_void_p(4096)
+    assert r.int4_linear_forward(fake, L.Q4_F32, 4, 128, fake, 64, 0, fake, None) == L.Q4_ERR_DTYPE
+    assert r.int4_linear_forward(fake, L.Q4_F16, 4, 128, fake, 48, 0, fake, None) == L.Q4_ERR_SHAPE
+    assert r.int4_linear_forward(fake, L.Q4_F16, 4, 128, None, 64, 0, fake, None) == L.Q4_ERR_NULL
+    assert r.int4_w4a8_group_acc(fake, 4, 130, fake, 64, 0, fake, None) == L.Q4_ERR_SHAPE
+    assert r.int4_w4a8_group_acc(fake, 0, 128, fake, 64, 0, fake, None) == L.Q4_OK
+
+
+def test_binding_refuses_cpu_tensors(L):
+    import torch
+    with pytest.raises(ValueError):
+        L.quantize_int4_g128(torch.zeros((16, 128)))
