@@ -12,7 +12,7 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libq4moe.so")
+LIB_PATH = os.environ.get("Q4MOE_LIB") or os.path.join(_HERE, "libq4moe.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(

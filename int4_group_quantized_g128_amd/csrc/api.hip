@@ -64,16 +64,27 @@ struct FwdWorkspace {
   float* sx = nullptr;
   int8_t* qh = nullptr;
   float* sh = nullptr;
+  void* rs_x = nullptr;   // prefill: per (token, group) sums of x (fp32) or of q_x (int32)
+  void* rs_h = nullptr;   // prefill: per (position, group) sums of h / q_h
+  bool prefill = false;
   int64_t bytes = 0;
   int32_t max_tiles = 0;
   int tile_rows = 16;
 };
 
+// Average routed rows per expert decides the GEMM shape: 16-row decode tiles, 32 / 64-row
+// mid tiles, or the 128-row prefill kernel.
+double avg_rows(const q4_moe_layer_t* L, int64_t t) { return double(t) * L->top_k / L->num_experts; }
+
 int row_blocks_for(const q4_moe_layer_t* L, int64_t t) {
-  const double avg = double(t) * L->top_k / L->num_experts;
+  const double avg = avg_rows(L, t);
   if (avg <= 16) return 1;
   if (avg <= 32) return 2;
   return 4;
+}
+
+bool use_prefill(const q4_moe_layer_t* L, int64_t t) {
+  return avg_rows(L, t) >= 64 && (2 * int64_t(L->inter)) % 128 == 0 && L->hidden % 128 == 0;
 }
 
 FwdWorkspace carve(const q4_moe_layer_t* L, int64_t t, int mode, void* base) {
@@ -83,7 +94,8 @@ FwdWorkspace carve(const q4_moe_layer_t* L, int64_t t, int mode, void* base) {
   const int64_t S = L->top_k + shared;
   const int64_t P = t * S;
   const int64_t H = L->hidden, I = L->inter;
-  w.tile_rows = 16 * row_blocks_for(L, t);
+  w.prefill = use_prefill(L, t);
+  w.tile_rows = w.prefill ? 128 : 16 * row_blocks_for(L, t);
   w.max_tiles = int32_t(P / w.tile_rows + std::min<int64_t>(ee, P) + 1);
   int64_t off = 0;
   auto take = [&](int64_t bytes) {
@@ -104,6 +116,10 @@ FwdWorkspace carve(const q4_moe_layer_t* L, int64_t t, int mode, void* base) {
     w.sx = reinterpret_cast<float*>(take(t * 4));
     w.qh = reinterpret_cast<int8_t*>(take(P * I));
     w.sh = reinterpret_cast<float*>(take(P * 4));
+  }
+  if (w.prefill && (mode == Q4_W4A16 || L->asymmetric)) {
+    w.rs_x = take(t * (H / 128) * 4);
+    w.rs_h = take(P * (I / 128) * 4);
   }
   w.bytes = off;
   return w;
@@ -306,31 +322,54 @@ int moe_int4_ffn_forward(const q4_moe_layer_t* L, const uint16_t* x_bf16, int64_
   dn.N = H;
   dn.K = I;
   dn.out = w.y;
+  auto gemm = [&](const GemmArgs& g, int act, int kind) {
+    return w.prefill ? launch_gemm_prefill(g, act, kind, stream) : launch_gemm(g, act, kind, rb, stream);
+  };
   if (mode == Q4_W4A16) {
     gu.a = x_bf16;
     dn.a = w.h;
+    if (w.prefill) {
+      stage_begin(Q4_STAGE_X_QUANT, stream);
+      if ((rc = check_hip(launch_rowsum(x_bf16, 0, t, H, w.rs_x, stream), "x row sums"))) return rc;
+      stage_end(Q4_STAGE_X_QUANT, stream);
+      gu.a_gsum = static_cast<const float*>(w.rs_x);
+      dn.a_gsum = static_cast<const float*>(w.rs_h);
+    }
     stage_begin(Q4_STAGE_GATE_UP, stream);
-    if ((rc = check_hip(launch_gemm(gu, 0, GEMM_GATE_UP, rb, stream), "gate/up gemm"))) return rc;
+    if ((rc = check_hip(gemm(gu, 0, GEMM_GATE_UP), "gate/up gemm"))) return rc;
     stage_end(Q4_STAGE_GATE_UP, stream);
+    if (w.prefill) {
+      stage_begin(Q4_STAGE_H_QUANT, stream);
+      if ((rc = check_hip(launch_rowsum(w.h, 0, t * S, I, w.rs_h, stream), "h row sums"))) return rc;
+      stage_end(Q4_STAGE_H_QUANT, stream);
+    }
     stage_begin(Q4_STAGE_DOWN, stream);
-    if ((rc = check_hip(launch_gemm(dn, 0, GEMM_PLAIN, rb, stream), "down gemm"))) return rc;
+    if ((rc = check_hip(gemm(dn, 0, GEMM_PLAIN), "down gemm"))) return rc;
     stage_end(Q4_STAGE_DOWN, stream);
   } else {
     stage_begin(Q4_STAGE_X_QUANT, stream);
     if ((rc = check_hip(launch_act_quant(x_bf16, 0, t, H, w.qx, w.sx, nullptr, stream), "x quant"))) return rc;
+    if (w.prefill && L->asymmetric &&
+        (rc = check_hip(launch_rowsum(w.qx, 1, t, H, w.rs_x, stream), "x code sums")))
+      return rc;
     stage_end(Q4_STAGE_X_QUANT, stream);
     gu.a = w.qx;
     gu.a_scale = w.sx;
+    gu.a_qsum = static_cast<const int32_t*>(w.rs_x);
     stage_begin(Q4_STAGE_GATE_UP, stream);
-    if ((rc = check_hip(launch_gemm(gu, 2, GEMM_GATE_UP, rb, stream), "gate/up gemm"))) return rc;
+    if ((rc = check_hip(gemm(gu, 2, GEMM_GATE_UP), "gate/up gemm"))) return rc;
     stage_end(Q4_STAGE_GATE_UP, stream);
     stage_begin(Q4_STAGE_H_QUANT, stream);
     if ((rc = check_hip(launch_act_quant(w.h, 1, t * S, I, w.qh, w.sh, nullptr, stream), "h quant"))) return rc;
+    if (w.prefill && L->asymmetric &&
+        (rc = check_hip(launch_rowsum(w.qh, 1, t * S, I, w.rs_h, stream), "h code sums")))
+      return rc;
     stage_end(Q4_STAGE_H_QUANT, stream);
     dn.a = w.qh;
     dn.a_scale = w.sh;
+    dn.a_qsum = static_cast<const int32_t*>(w.rs_h);
     stage_begin(Q4_STAGE_DOWN, stream);
-    if ((rc = check_hip(launch_gemm(dn, 2, GEMM_PLAIN, rb, stream), "down gemm"))) return rc;
+    if ((rc = check_hip(gemm(dn, 2, GEMM_PLAIN), "down gemm"))) return rc;
     stage_end(Q4_STAGE_DOWN, stream);
   }
   stage_begin(Q4_STAGE_COMBINE, stream);

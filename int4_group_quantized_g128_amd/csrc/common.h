@@ -57,16 +57,22 @@ Q4_DEVICE float wave_min(float v) {
 // ---------------------------------------------------------------- nibble widening
 // A 32-bit device word holds 8 unsigned nibbles d; nibble position r (bits 4r..4r+3)
 // is element 2r and position r + 4 is element 2r + 1 of the lane's 8 consecutive k.
-// OR-ing a nibble into the low mantissa bits of a magic constant yields the exact
-// value magic + d: bf16 0x4300 = 128 (step 1 up to 256), f16 0x6400 = 1024 (step 1
-// up to 2048).  Output register r holds elements (2r, 2r + 1) = (low, high half).
+// Placing a nibble in the low mantissa bits under a magic exponent byte yields the
+// exact value magic + d: bf16 0x43xx = 128 + d (step 1 up to 256), f16 0x64xx =
+// 1024 + d (step 1 up to 2048).  Output register r holds elements (2r, 2r + 1) =
+// (low, high half).
 template <Act A>
 Q4_DEVICE void widen_word_fp(uint32_t w, uint32_t out[4]) {
-  constexpr uint32_t magic = (A == Act::BF16) ? 0x43004300u : 0x64006400u;
-  out[0] = (w & 0x000F000Fu) | magic;
-  out[1] = ((w >> 4) & 0x000F000Fu) | magic;
-  out[2] = ((w >> 8) & 0x000F000Fu) | magic;
-  out[3] = ((w >> 12) & 0x000F000Fu) | magic;
+  // lo: nibble positions 0, 2, 4, 6 (one per byte, high halves cleared); hi: 1, 3, 5, 7.
+  // A byte permute then pairs two of them with the magic's high byte (0x43 / 0x64):
+  // positions (0, 4) = elements (0, 1), (1, 5) = (2, 3), (2, 6) = (4, 5), (3, 7) = (6, 7).
+  constexpr uint32_t magic_bytes = (A == Act::BF16) ? 0x43434343u : 0x64646464u;
+  const uint32_t lo = w & 0x0F0F0F0Fu;
+  const uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;
+  out[0] = __builtin_amdgcn_perm(magic_bytes, lo, 0x04020400u);
+  out[1] = __builtin_amdgcn_perm(magic_bytes, hi, 0x04020400u);
+  out[2] = __builtin_amdgcn_perm(magic_bytes, lo, 0x04030401u);
+  out[3] = __builtin_amdgcn_perm(magic_bytes, hi, 0x04030401u);
 }
 
 // The magic offset of the widened value (value = offset + d).
@@ -113,8 +119,12 @@ Q4_DEVICE uint2 load8(const void* p) { return *reinterpret_cast<const uint2*>(p)
 
 // Non-temporal 16-byte load for streamed (read-once) weights.
 Q4_DEVICE uint4 load16_stream(const void* p) {
+#ifdef Q4_NO_NT
+  return load16(p);
+#else
   const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
   return make_uint4(v[0], v[1], v[2], v[3]);
+#endif
 }
 
 }  // namespace q4

@@ -91,35 +91,45 @@ hipError_t launch_act_quant(const void* x, int x_is_f32, int64_t rows, int64_t c
 }
 
 // ------------------------------------------------------------------ grouped GEMM
-constexpr int kNB = 4;       // 16-column blocks per workgroup
-constexpr int kWaves = 4;    // K split across the waves of a workgroup
-
 struct RowInfo {
   int64_t src;   // activation row
   int64_t pos;   // output row
   bool valid;
 };
 
-template <Act A, int KIND, int MB>
+// Grouped INT4 GEMM.  Template parameters:
+//  MB  16-row blocks per tile (rows of one expert, gathered through perm),
+//  KW  waves of the workgroup that split the K groups (reduced through LDS),
+//  NBW 16-column blocks per wave (the workgroup covers (4 / KW) * NBW blocks),
+//  D   depth of the register pipeline (groups whose loads are in flight).
+// The workgroup's scales (and zero points) are staged in LDS once per work item.
+template <Act A, int KIND, bool ASYM, int MB, int KW, int NBW, int D>
 __global__ void __launch_bounds__(256) k_gemm(GemmArgs args) {
-  extern __shared__ float red_lds[];  // [kWaves][MB][kNB][64][4]
+  constexpr int kColGroups = 4 / KW;
+  constexpr int kCBWG = kColGroups * NBW;  // column blocks per workgroup
+  extern __shared__ __align__(16) uint8_t smem[];
   const int lane = threadIdx.x & 63;
   const int wid = threadIdx.x >> 6;
+  const int kw = wid % KW, cgrp = wid / KW;
   const int col = lane & 15, kq = lane >> 4;
   const int64_t N = args.N, K = args.K, G = K / kGroup;
-  const int64_t nblk = N / (16 * kNB);
+  const int64_t nblk = N / (16 * kCBWG);
   const int64_t tile_rows = 16 * MB;
   const int64_t ntiles = args.tiles ? int64_t(*args.num_tiles) : (args.dense_rows + tile_rows - 1) / tile_rows;
   const int64_t items = ntiles * nblk;
   const int64_t w_scale_off = align256(N * K / 2);
   const int64_t w_zero_off = w_scale_off + align256(2 * N * G);
-  // contiguous group range of this wave
-  const int64_t gper = (G + kWaves - 1) / kWaves;
-  const int64_t g_beg = std::min<int64_t>(G, wid * gper), g_end = std::min<int64_t>(G, g_beg + gper);
+  const int64_t gper = (G + KW - 1) / KW;
+  const int64_t g_beg = std::min<int64_t>(G, kw * gper), g_end = std::min<int64_t>(G, g_beg + gper);
+  // LDS: scales [kCBWG][G][16] fp16, zero points [kCBWG][G][16] u8, reduction buffer
+  uint16_t* s_scale = reinterpret_cast<uint16_t*>(smem);
+  uint8_t* s_zero = smem + align256(int64_t(kCBWG) * G * 32);
+  float* s_red = reinterpret_cast<float*>(smem + align256(int64_t(kCBWG) * G * 32) +
+                                          (ASYM ? align256(int64_t(kCBWG) * G * 16) : 0));
 
   for (int64_t item = blockIdx.x; item < items; item += gridDim.x) {
     const int64_t tile = item / nblk;
-    const int64_t cb0 = (item % nblk) * kNB;
+    const int64_t cb0 = (item % nblk) * kCBWG;     // first column block of the workgroup
     int32_t expert = 0;
     int64_t row_start, rows;
     if (args.tiles) {
@@ -132,102 +142,119 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs args) {
       rows = std::min<int64_t>(tile_rows, args.dense_rows - row_start);
     }
     const uint8_t* wbase = expert < args.num_experts ? args.w + int64_t(expert) * args.w_stride : args.w_shared;
-    const uint16_t* wscale = reinterpret_cast<const uint16_t*>(wbase + w_scale_off);
-    const uint8_t* wzero = wbase + w_zero_off;
 
-    // rows of the A fragments (lane row = col index in the A layout)
+    // stage the workgroup's scales / zero points (contiguous in the device layout)
+    {
+      const uint4* src = reinterpret_cast<const uint4*>(wbase + w_scale_off + cb0 * G * 32);
+      const int64_t n16 = int64_t(kCBWG) * G * 2;
+      for (int64_t i = threadIdx.x; i < n16; i += 256) reinterpret_cast<uint4*>(s_scale)[i] = src[i];
+      if constexpr (ASYM) {
+        const uint8_t* zsrc = wbase + w_zero_off + cb0 * G * 16;
+        for (int64_t i = threadIdx.x; i < int64_t(kCBWG) * G * 16; i += 256) s_zero[i] = zsrc[i];
+      }
+    }
+    __syncthreads();
+
+    // Rows past the tile end read the tile's first row: every MFMA output row depends on
+    // its own A row only, and those rows are never stored, so no zero fill is needed.
     RowInfo ri[MB];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
       const int64_t r = mb * 16 + col;
       ri[mb].valid = r < rows;
-      ri[mb].pos = row_start + r;
-      int64_t src = ri[mb].pos;
-      if (ri[mb].valid && args.perm) src = args.perm[ri[mb].pos] / args.slots_per_token;
-      ri[mb].src = ri[mb].valid ? src : 0;
+      ri[mb].pos = row_start + (ri[mb].valid ? r : 0);
+      ri[mb].src = args.perm ? args.perm[ri[mb].pos] / args.slots_per_token : ri[mb].pos;
     }
 
-    f32x4_t acc[MB][kNB];
+    const int lcb = cgrp * NBW;                       // wave's first block inside the workgroup
+    // per-item base pointers; each group then only adds a constant stride
+    const uint8_t* wp[NBW];
+#pragma unroll
+    for (int nb = 0; nb < NBW; ++nb) wp[nb] = wbase + ((cb0 + lcb + nb) * G) * kTileBytes + lane * 16;
+    const uint8_t* ap[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+      ap[mb] = static_cast<const uint8_t*>(args.a) + (ri[mb].src * K + 8 * kq) * (A == Act::I8 ? 1 : 2);
+    const int sbase = (lcb * int(G)) * 16 + col;
+
+    f32x4_t acc[MB][NBW];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-      for (int nb = 0; nb < kNB; ++nb) acc[mb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int nb = 0; nb < NBW; ++nb) acc[mb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    // One group's operands: 16 bytes of each of the 4 weight tiles, the lane column's
-    // scale / zero point, and the A fragments of the MB row blocks.
     struct Stage {
-      uint32_t wv[kNB][4];
-      uint16_t sc[kNB];
-      uint8_t zp[kNB];
+      uint32_t wv[NBW][4];
       uint32_t av[MB][4][4];
     };
-    auto load_stage = [&](Stage& st, int64_t g) {
+    auto load_stage = [&](Stage& st, int g) {
 #pragma unroll
-      for (int nb = 0; nb < kNB; ++nb) {
-        const uint4 v = load16_stream(wbase + ((cb0 + nb) * G + g) * kTileBytes + lane * 16);
+      for (int nb = 0; nb < NBW; ++nb) {
+        const uint4 v = load16_stream(wp[nb] + g * kTileBytes);
         st.wv[nb][0] = v.x; st.wv[nb][1] = v.y; st.wv[nb][2] = v.z; st.wv[nb][3] = v.w;
-        const int64_t mi = ((cb0 + nb) * G + g) * 16 + col;
-        st.sc[nb] = wscale[mi];
-        st.zp[nb] = args.asym ? wzero[mi] : uint8_t(8);
       }
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
         if constexpr (A != Act::I8) {
-          const uint16_t* xa = static_cast<const uint16_t*>(args.a) + ri[mb].src * K + g * kGroup + 8 * kq;
+          const uint8_t* xa = ap[mb] + g * (kGroup * 2);
 #pragma unroll
           for (int s = 0; s < 4; ++s) {
-            uint4 v = make_uint4(0, 0, 0, 0);
-            if (ri[mb].valid) v = load16(xa + 32 * s);
+            const uint4 v = load16(xa + 64 * s);
             st.av[mb][s][0] = v.x; st.av[mb][s][1] = v.y; st.av[mb][s][2] = v.z; st.av[mb][s][3] = v.w;
           }
         } else {
-          const int8_t* qa = static_cast<const int8_t*>(args.a) + ri[mb].src * K + g * kGroup + 8 * kq;
+          const uint8_t* qa = ap[mb] + g * kGroup;
 #pragma unroll
           for (int i = 0; i < 2; ++i) {
-            uint2 lo = make_uint2(0, 0), hi = make_uint2(0, 0);
-            if (ri[mb].valid) {
-              lo = load8(qa + 64 * i);
-              hi = load8(qa + 64 * i + 32);
-            }
+            const uint2 lo = load8(qa + 64 * i);
+            const uint2 hi = load8(qa + 64 * i + 32);
             st.av[mb][i][0] = lo.x; st.av[mb][i][1] = lo.y; st.av[mb][i][2] = hi.x; st.av[mb][i][3] = hi.y;
           }
         }
       }
     };
-    auto compute_stage = [&](const Stage& st, int64_t g) {
-      float sc[kNB];
+    auto compute_stage = [&](const Stage& st, int g) {
+      float sc[NBW], zp[NBW];
 #pragma unroll
-      for (int nb = 0; nb < kNB; ++nb) sc[nb] = f16_bits_to_f32(st.sc[nb]);
+      for (int nb = 0; nb < NBW; ++nb) {
+        const int li = sbase + (nb * int(G) + g) * 16;
+        sc[nb] = f16_bits_to_f32(s_scale[li]);
+        zp[nb] = ASYM ? float(s_zero[li]) : 8.0f;
+      }
       if constexpr (A == Act::BF16) {
-        // exact row sums of the group through the matrix core (B = 1.0)
-        const uint32_t ones[4] = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};
-        f32x4_t xs[MB];
+        // The correction -(magic + z) * sum x enters as the initial accumulator.  Its row
+        // sums come from the matrix core: B = -(128 + 8) for symmetric weights (one
+        // product serves every column), B = 1 then a per-column multiply otherwise.
+        f32x4_t ini[MB];
+        const uint32_t cb = ASYM ? 0x3f803f80u : 0xc308c308u;   // bf16 1.0 / -136.0
+        const uint32_t cvec[4] = {cb, cb, cb, cb};
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
-          xs[mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+          ini[mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int s = 0; s < 4; ++s) xs[mb] = mfma16x16x32<A>(st.av[mb][s], ones, xs[mb]);
+          for (int s = 0; s < 4; ++s) ini[mb] = mfma16x16x32<A>(st.av[mb][s], cvec, ini[mb]);
         }
 #pragma unroll
-        for (int nb = 0; nb < kNB; ++nb) {
+        for (int nb = 0; nb < NBW; ++nb) {
           uint32_t b[4][4];
 #pragma unroll
           for (int s = 0; s < 4; ++s) widen_word_fp<A>(st.wv[nb][s], b[s]);
-          const float negz = -(magic_offset<A>() + float(st.zp[nb]));
+          const float negz = -(magic_offset<A>() + zp[nb]);
 #pragma unroll
           for (int mb = 0; mb < MB; ++mb) {
-            f32x4_t gacc = {0.f, 0.f, 0.f, 0.f};
+            f32x4_t gacc = ini[mb];
+            if constexpr (ASYM) gacc *= negz;
 #pragma unroll
             for (int s = 0; s < 4; ++s) gacc = mfma16x16x32<A>(st.av[mb][s], b[s], gacc);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) acc[mb][nb][i] = fmaf(sc[nb], fmaf(negz, xs[mb][i], gacc[i]), acc[mb][nb][i]);
+            for (int i = 0; i < 4; ++i) acc[mb][nb][i] = fmaf(sc[nb], gacc[i], acc[mb][nb][i]);
           }
         }
       } else if constexpr (A == Act::F16) {
         // magic + d - (magic + z) = d - z, exact in fp16: no correction term
 #pragma unroll
-        for (int nb = 0; nb < kNB; ++nb) {
-          const _Float16 nz = _Float16(-(magic_offset<A>() + float(st.zp[nb])));
+        for (int nb = 0; nb < NBW; ++nb) {
+          const _Float16 nz = _Float16(-(magic_offset<A>() + zp[nb]));
           const f16x2_t negz = {nz, nz};
           uint32_t b[4][4];
 #pragma unroll
@@ -247,7 +274,7 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs args) {
         }
       } else {
         int32_t qs[MB];
-        if (args.asym) {
+        if constexpr (ASYM) {
 #pragma unroll
           for (int mb = 0; mb < MB; ++mb) {
             qs[mb] = 0;
@@ -261,14 +288,14 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs args) {
           }
         }
 #pragma unroll
-        for (int nb = 0; nb < kNB; ++nb) {
+        for (int nb = 0; nb < NBW; ++nb) {
           uint32_t b[2][4];
 #pragma unroll
           for (int i = 0; i < 2; ++i) {
             widen_word_i8(st.wv[nb][2 * i], b[i][0], b[i][1]);
             widen_word_i8(st.wv[nb][2 * i + 1], b[i][2], b[i][3]);
           }
-          const int32_t zoff = int32_t(st.zp[nb]) - 8;
+          const int32_t zoff = int32_t(zp[nb]) - 8;
 #pragma unroll
           for (int mb = 0; mb < MB; ++mb) {
             i32x4_t gacc = {0, 0, 0, 0};
@@ -277,11 +304,11 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs args) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
               int32_t a32 = gacc[i] >> 4;                    // exact: gacc = 16 * sum q (d - 8)
-              if (args.asym) a32 -= zoff * __shfl(qs[mb], 4 * kq + i, 64);
+              if constexpr (ASYM) a32 -= zoff * __shfl(qs[mb], 4 * kq + i, 64);
               if constexpr (KIND == GEMM_GROUP_ACC) {
                 const int64_t r = mb * 16 + 4 * kq + i;
                 if (r < rows)
-                  args.acc_out[((row_start + r) * N + (cb0 + nb) * 16 + col) * G + g] = a32;
+                  args.acc_out[((row_start + r) * N + (cb0 + lcb + nb) * 16 + col) * G + g] = a32;
               } else {
                 acc[mb][nb][i] = fmaf(sc[nb], float(a32), acc[mb][nb][i]);
               }
@@ -291,75 +318,73 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs args) {
       }
     };
 
-    // two-stage software pipeline over this wave's groups: the loads of group g + 1
-    // are in flight while group g is computed
+    // D-stage register pipeline over this wave's groups: while group g is computed the
+    // loads of groups g + 1 .. g + D - 1 are in flight
     if (g_beg < g_end) {
-      Stage s0, s1;
-      load_stage(s0, g_beg);
-      for (int64_t g = g_beg; g < g_end; g += 2) {
-        if (g + 1 < g_end) load_stage(s1, g + 1);
-        compute_stage(s0, g);
-        if (g + 1 >= g_end) break;
-        if (g + 2 < g_end) load_stage(s0, g + 2);
-        compute_stage(s1, g + 1);
-      }
-    }
-    if constexpr (KIND == GEMM_GROUP_ACC) continue;
-
-    // ---------------- cross-wave reduction and epilogue
-    float* mine = red_lds + wid * (MB * kNB * 64 * 4);
+      Stage st[D];
+      const int gb = int(g_beg), ge = int(g_end);
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
+      for (int j = 0; j < D - 1; ++j)
+        if (gb + j < ge) load_stage(st[j], gb + j);
+      for (int g = gb; g < ge; g += D) {
 #pragma unroll
-      for (int nb = 0; nb < kNB; ++nb)
-        *reinterpret_cast<f32x4_t*>(mine + ((mb * kNB + nb) * 64 + lane) * 4) = acc[mb][nb];
-    __syncthreads();
-    auto reduced = [&](int mb, int nb) {
-      f32x4_t s = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w)
-        s += *reinterpret_cast<const f32x4_t*>(red_lds + w * (MB * kNB * 64 * 4) + ((mb * kNB + nb) * 64 + lane) * 4);
-      return s;
-    };
-    if constexpr (KIND == GEMM_PLAIN) {
-      const int nb = wid;
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        const f32x4_t v = reduced(mb, nb);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int64_t r = mb * 16 + 4 * kq + i;
-          if (r < rows) {
-            const int64_t pos = row_start + r;
-            float y = v[i];
-            if constexpr (A == Act::I8) y *= args.a_scale[args.perm ? args.perm[pos] / args.slots_per_token : pos];
-            static_cast<float*>(args.out)[pos * N + (cb0 + nb) * 16 + col] = y;
-          }
+        for (int j = 0; j < D; ++j) {
+          if (g + j >= ge) break;
+          if (g + j + D - 1 < ge) load_stage(st[(j + D - 1) % D], g + j + D - 1);
+          compute_stage(st[j], g + j);
         }
       }
-    } else if (wid < 2) {
-      // device blocks cb0.. = gate_j, up_j, gate_j+1, up_j+1 ; pair wid -> h columns
-      const int64_t I = N / 2;
-      const int64_t hcol = (cb0 / 2 + wid) * 16 + col;
+    }
+
+    if constexpr (KIND != GEMM_GROUP_ACC) {
+      // ---------------- reduction over the KW waves of a column group, then epilogue
+      if constexpr (KW > 1) {
+        float* mine = s_red + wid * (MB * NBW * 64 * 4);
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        const f32x4_t gv = reduced(mb, 2 * wid), uv = reduced(mb, 2 * wid + 1);
+        for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int64_t r = mb * 16 + 4 * kq + i;
-          if (r < rows) {
+          for (int nb = 0; nb < NBW; ++nb)
+            *reinterpret_cast<f32x4_t*>(mine + ((mb * NBW + nb) * 64 + lane) * 4) = acc[mb][nb];
+        __syncthreads();
+        if (kw == 0) {
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+              for (int w = 1; w < KW; ++w)
+                acc[mb][nb] += *reinterpret_cast<const f32x4_t*>(s_red + (wid + w) * (MB * NBW * 64 * 4) +
+                                                                 ((mb * NBW + nb) * 64 + lane) * 4);
+        }
+      }
+      if (kw == 0) {
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int64_t r = mb * 16 + 4 * kq + i;
+            if (r >= rows) continue;
             const int64_t pos = row_start + r;
-            float gg = gv[i], uu = uv[i];
-            if constexpr (A == Act::I8) {
-              const float sa = args.a_scale[args.perm ? args.perm[pos] / args.slots_per_token : pos];
-              gg *= sa;
-              uu *= sa;
+            float sa = 1.0f;
+            if constexpr (A == Act::I8) sa = args.a_scale[args.perm ? args.perm[pos] / args.slots_per_token : pos];
+            if constexpr (KIND == GEMM_PLAIN) {
+#pragma unroll
+              for (int nb = 0; nb < NBW; ++nb)
+                static_cast<float*>(args.out)[pos * N + (cb0 + lcb + nb) * 16 + col] = acc[mb][nb][i] * sa;
+            } else {
+              // device blocks alternate gate_j, up_j: pair p -> h columns of block (cb0 + lcb) / 2 + p
+              const int64_t I = N / 2;
+#pragma unroll
+              for (int p = 0; p < NBW / 2; ++p) {
+                const float gg = acc[mb][2 * p][i] * sa, uu = acc[mb][2 * p + 1][i] * sa;
+                const float hv = gg / (1.0f + expf(-gg)) * uu;
+                const int64_t hcol = ((cb0 + lcb) / 2 + p) * 16 + col;
+                if constexpr (A == Act::I8)
+                  static_cast<float*>(args.out)[pos * I + hcol] = hv;
+                else
+                  static_cast<uint16_t*>(args.out)[pos * I + hcol] = f32_to_bf16(hv);
+              }
             }
-            const float hv = gg / (1.0f + expf(-gg)) * uu;
-            if constexpr (A == Act::I8)
-              static_cast<float*>(args.out)[pos * I + hcol] = hv;
-            else
-              static_cast<uint16_t*>(args.out)[pos * I + hcol] = f32_to_bf16(hv);
           }
         }
       }
@@ -368,33 +393,73 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs args) {
   }
 }
 
-template <Act A, int KIND>
-static hipError_t launch_gemm_mb(const GemmArgs& g, int mb, hipStream_t st) {
-  const int64_t nblk = g.N / (16 * kNB);
-  const int64_t trows = 16 * mb;
+// LDS bytes of one configuration (scales, zero points, reduction buffer).
+static size_t gemm_lds_bytes(int64_t K, int asym, int mb, int kw, int nbw) {
+  const int64_t G = K / kGroup;
+  const int64_t cbwg = (4 / kw) * nbw;
+  size_t b = size_t(align256(cbwg * G * 32));
+  if (asym) b += size_t(align256(cbwg * G * 16));
+  if (kw > 1) b += size_t(4) * mb * nbw * 64 * 4 * sizeof(float);
+  return b;
+}
+
+template <Act A, int KIND, int MB, int KW, int NBW, int D>
+static hipError_t launch_cfg(const GemmArgs& g, hipStream_t st) {
+  constexpr int cbwg = (4 / KW) * NBW;
+  const int64_t nblk = g.N / (16 * cbwg);
+  const int64_t trows = 16 * MB;
   const int64_t max_tiles = g.tiles ? g.max_tiles : (g.dense_rows + trows - 1) / trows;
   const int64_t items = max_tiles * nblk;
   if (items == 0) return hipSuccess;
-  const unsigned grid = unsigned(std::min<int64_t>(items, 256 * 16));
-  const size_t lds = KIND == GEMM_GROUP_ACC ? 0 : size_t(kWaves) * mb * kNB * 64 * 4 * sizeof(float);
-  switch (mb) {
-    case 1: hipLaunchKernelGGL((k_gemm<A, KIND, 1>), dim3(grid), dim3(256), lds, st, g); break;
-    case 2: hipLaunchKernelGGL((k_gemm<A, KIND, 2>), dim3(grid), dim3(256), lds, st, g); break;
-    default: hipLaunchKernelGGL((k_gemm<A, KIND, 4>), dim3(grid), dim3(256), lds, st, g); break;
-  }
+#ifndef Q4_GRID_CAP
+#define Q4_GRID_CAP (256 * 16)
+#endif
+  const unsigned grid = unsigned(std::min<int64_t>(items, Q4_GRID_CAP));
+  const size_t lds = gemm_lds_bytes(g.K, g.asym, MB, KW, NBW);
+  if (lds > 160 * 1024) return hipErrorInvalidValue;  // K too large for the staged scales
+  if (g.asym)
+    hipLaunchKernelGGL((k_gemm<A, KIND, true, MB, KW, NBW, D>), dim3(grid), dim3(256), lds, st, g);
+  else
+    hipLaunchKernelGGL((k_gemm<A, KIND, false, MB, KW, NBW, D>), dim3(grid), dim3(256), lds, st, g);
   return hipGetLastError();
 }
 
-hipError_t launch_gemm(const GemmArgs& g, int act, int kind, int row_blocks, hipStream_t st) {
-  const int mb = row_blocks <= 1 ? 1 : (row_blocks <= 2 ? 2 : 4);
-  if (act == 0) {
-    if (kind == GEMM_GATE_UP) return launch_gemm_mb<Act::BF16, GEMM_GATE_UP>(g, mb, st);
-    return launch_gemm_mb<Act::BF16, GEMM_PLAIN>(g, mb, st);
+// Decode configuration (16-row tiles, many tiles); overridable at build time.
+#ifndef Q4_DEC_KW
+#define Q4_DEC_KW 1
+#endif
+#ifndef Q4_DEC_NBW
+#define Q4_DEC_NBW 4
+#endif
+#ifndef Q4_DEC_D
+#define Q4_DEC_D 2
+#endif
+
+// Configuration table: (MB, KW, NBW, D) by row blocks and the column count.
+template <Act A, int KIND>
+static hipError_t launch_kind(const GemmArgs& g, int rb, int split, hipStream_t st) {
+  if (rb <= 1) {
+    constexpr int dec_cb = (4 / Q4_DEC_KW) * Q4_DEC_NBW;
+    if (split && g.N % (16 * 2) == 0) return launch_cfg<A, KIND, 1, 4, 2, 2>(g, st);
+    if (g.N % (16 * dec_cb) == 0) return launch_cfg<A, KIND, 1, Q4_DEC_KW, Q4_DEC_NBW, Q4_DEC_D>(g, st);
+    return launch_cfg<A, KIND, 1, 4, 2, 2>(g, st);
   }
-  if (act == 1) return launch_gemm_mb<Act::F16, GEMM_PLAIN>(g, mb, st);
-  if (kind == GEMM_GATE_UP) return launch_gemm_mb<Act::I8, GEMM_GATE_UP>(g, mb, st);
-  if (kind == GEMM_GROUP_ACC) return launch_gemm_mb<Act::I8, GEMM_GROUP_ACC>(g, mb, st);
-  return launch_gemm_mb<Act::I8, GEMM_PLAIN>(g, mb, st);
+  if (rb <= 2) return launch_cfg<A, KIND, 2, 4, 4, 2>(g, st);
+  return launch_cfg<A, KIND, 4, 4, 4, 2>(g, st);
+}
+
+hipError_t launch_gemm(const GemmArgs& g, int act, int kind, int row_blocks, hipStream_t st) {
+  // few tiles (small batches): split K over the 4 waves for more waves in flight
+  const int64_t est_items = (g.tiles ? std::min<int64_t>(g.max_tiles, 64) : 1) * (g.N / 128);
+  const int split = est_items < 1024 ? 1 : 0;
+  if (act == 0) {
+    if (kind == GEMM_GATE_UP) return launch_kind<Act::BF16, GEMM_GATE_UP>(g, row_blocks, split, st);
+    return launch_kind<Act::BF16, GEMM_PLAIN>(g, row_blocks, split, st);
+  }
+  if (act == 1) return launch_kind<Act::F16, GEMM_PLAIN>(g, row_blocks, split, st);
+  if (kind == GEMM_GATE_UP) return launch_kind<Act::I8, GEMM_GATE_UP>(g, row_blocks, split, st);
+  if (kind == GEMM_GROUP_ACC) return launch_cfg<Act::I8, GEMM_GROUP_ACC, 1, 4, 1, 2>(g, st);
+  return launch_kind<Act::I8, GEMM_PLAIN>(g, row_blocks, split, st);
 }
 
 // ------------------------------------------------------------------ A9 combine

@@ -42,7 +42,8 @@ struct GemmArgs {
   // activations
   const void* a;          // bf16 / f16 [rows][K] or int8 [rows][K]
   const float* a_scale;   // int8 mode: per-row scale
-  const int32_t* a_qsum;  // int8 asymmetric mode: per (row, group) code sums
+  const int32_t* a_qsum;  // int8 asymmetric prefill: per (row, group) code sums [rows][G]
+  const float* a_gsum;    // bf16 prefill: per (row, group) activation sums [rows][G]
   const int32_t* perm;    // position -> slot (gather rows), or NULL = identity
   int32_t slots_per_token;  // row = perm[p] / slots_per_token when perm != NULL
   // weights
@@ -67,6 +68,11 @@ enum GemmKind { GEMM_PLAIN = 0, GEMM_GATE_UP = 1, GEMM_GROUP_ACC = 2 };
 
 hipError_t launch_gemm(const GemmArgs& g, int act /*0 bf16, 1 f16, 2 i8*/, int kind, int row_blocks,
                        hipStream_t st);
+
+// Prefill (128-row tiles, LDS-staged activations); tiles must be built with 128 rows.
+hipError_t launch_gemm_prefill(const GemmArgs& g, int act /*0 bf16, 2 i8*/, int kind, hipStream_t st);
+// Per-(row, group of 128) sums: bf16 -> fp32, or int8 -> int32.
+hipError_t launch_rowsum(const void* a, int is_i8, int64_t rows, int64_t K, void* out, hipStream_t st);
 
 hipError_t launch_combine(const float* y, const int32_t* inv, const float* w, int64_t t, int32_t k, int shared,
                           int64_t h, uint16_t* out, hipStream_t st);

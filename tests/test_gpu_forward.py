@@ -51,7 +51,7 @@ def small(lib, request):
 
 
 @pytest.mark.parametrize("mode", [0, 1], ids=["w4a16", "w4a8"])
-@pytest.mark.parametrize("t", [1, 5, 33, 100])
+@pytest.mark.parametrize("t", [1, 5, 33, 100, 300])
 def test_small_shared_layer(lib, small, mode, t):
     layer, oe = small
     x = synth.normal(synth.stream_key(12, t), (t, SMALL["h"]), 1.0).to(torch.bfloat16)
