@@ -17,6 +17,8 @@
 //    registers during group g and widens them there (the same nibble layout as decode);
 //  - bf16: acc += s * (sum_k x (magic + d) - (magic + z) * sum_k x), the row sums coming
 //    precomputed per (row, group); INT8: acc += s * (acc_i32 / 16 [- (z - 8) sum q]).
+#include <type_traits>
+
 #include "common.h"
 #include "internal.h"
 
@@ -79,17 +81,45 @@ hipError_t launch_rowsum(const void* a, int is_i8, int64_t rows, int64_t K, void
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
+// s_waitcnt that waits until at most n vector-memory operations are outstanding
+// (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] in [15:14]).
+template <int N>
+Q4_DEVICE void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// Per-stage LDS image of one group (K = 128) of one work item:
+//   A tile  [128 rows][ROWB]  (16-byte chunks XOR-swizzled by row)
+//   W tiles [8 column blocks][64 lanes][16 B]  (the device tiles as stored)
+//   scales  [8][16] fp16, zero points [8][16] u8 (asymmetric)
+//   rsum    [128] fp32 row sums (bf16) / int32 code sums (int8, asymmetric)
+template <Act A>
+struct PfStage {
+  static constexpr int ESZ = (A == Act::I8) ? 1 : 2;
+  static constexpr int ROWB = kGroup * ESZ;
+  static constexpr int A_BYTES = kPfRows * ROWB;
+  static constexpr int W_OFF = A_BYTES;
+  static constexpr int S_OFF = W_OFF + kPfCB * kTileBytes;
+  static constexpr int Z_OFF = S_OFF + kPfCB * 32;
+  static constexpr int R_OFF = S_OFF + 512;
+  static constexpr int BYTES = R_OFF + kPfRows * 4;
+};
+constexpr int kPfStages = 3;
+
 template <Act A, int KIND, bool ASYM>
-__global__ void __launch_bounds__(256, 2) k_gemm_pf(GemmArgs args) {
-  constexpr int ESZ = (A == Act::I8) ? 1 : 2;
-  constexpr int ROWB = kGroup * ESZ;                 // bytes of one tile row
+__global__ void __launch_bounds__(256, 1) k_gemm_pf(GemmArgs args) {
+  using St = PfStage<A>;
+  constexpr int ROWB = St::ROWB;
   constexpr int CHUNKS = ROWB / 16;                   // 16-byte chunks per row
   constexpr int ROWS_PER_INST = 64 / CHUNKS;          // rows one direct-to-LDS load covers
-  constexpr int INSTS = 32 / ROWS_PER_INST;           // loads per wave per group (32 rows)
-  constexpr int TILE_BYTES = kPfRows * ROWB;
-  extern __shared__ __align__(16) uint8_t smem[];
-  uint8_t* a_lds = smem;                                                   // [2][128][ROWB]
-  float* xs_lds = reinterpret_cast<float*>(smem + 2 * TILE_BYTES);         // [2][128]
+  constexpr int A_INSTS = 32 / ROWS_PER_INST;         // A loads per wave per stage (32 rows)
+  constexpr bool RSUM = (A != Act::I8) || ASYM;
+  // three distinct LDS objects, so the compiler can tell which in-flight copies a read
+  // depends on (the loop below is unrolled by three to keep each slot compile-time)
+  __shared__ __align__(16) uint8_t slot0[St::BYTES];
+  __shared__ __align__(16) uint8_t slot1[St::BYTES];
+  __shared__ __align__(16) uint8_t slot2[St::BYTES];
 
   const int lane = threadIdx.x & 63;
   const int wid = threadIdx.x >> 6;
@@ -113,59 +143,52 @@ __global__ void __launch_bounds__(256, 2) k_gemm_pf(GemmArgs args) {
       const int64_t pos = row_start + (r < rows ? r : 0);
       return args.perm ? args.perm[pos] / args.slots_per_token : pos;
     };
-    // rows this lane copies into LDS: wave rows [32 wid, 32 wid + 32)
-    const uint8_t* arow[INSTS];
+    // global sources of this lane's direct-to-LDS copies
+    const uint8_t* arow[A_INSTS];
 #pragma unroll
-    for (int j = 0; j < INSTS; ++j) {
+    for (int j = 0; j < A_INSTS; ++j) {
       const int r = 32 * wid + ROWS_PER_INST * j + lane / CHUNKS;
-      const int slot = lane % CHUNKS;
-      const int c = slot ^ (r % CHUNKS);               // global chunk that lands in this slot
-      arow[j] = static_cast<const uint8_t*>(args.a) + src_of(r) * K * ESZ + c * 16;
+      const int c = (lane % CHUNKS) ^ (r % CHUNKS);   // global chunk that lands in this slot
+      arow[j] = static_cast<const uint8_t*>(args.a) + src_of(r) * K * St::ESZ + c * 16;
     }
-    // row sums (bf16) / code sums (int8, asymmetric) of tile row threadIdx.x
-    int64_t my_src = 0;
-    if (threadIdx.x < kPfRows) my_src = src_of(threadIdx.x);
-    // this wave's 4 weight column blocks
-    const uint8_t* wp[4];
-    int sidx[4];
+    const uint8_t* wsrc[2];
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-      const int64_t cb = cb0 + wn * 4 + nb;
-      wp[nb] = wbase + cb * G * kTileBytes + lane * 16;
-      sidx[nb] = int(cb * G) * 16 + col;
+    for (int j = 0; j < 2; ++j) wsrc[j] = wbase + (cb0 + 2 * wid + j) * G * kTileBytes + lane * 16;
+    // wave 0: scales (lanes 0..15) and zero points (lanes 16..23) of the 8 blocks
+    const uint8_t* msrc = nullptr;
+    if (lane < 16) msrc = wbase + w_scale_off + ((cb0 + lane / 2) * G) * 32 + (lane & 1) * 16;
+    else if (lane < 24) msrc = wbase + w_zero_off + ((cb0 + lane - 16) * G) * 16;
+    // waves 1 and 2: the row sums of rows (wid - 1) * 64 + lane
+    const void* rsrc = nullptr;
+    if constexpr (RSUM) {
+      if (wid == 1 || wid == 2) {
+        const int64_t sr = src_of((wid - 1) * 64 + lane);
+        if constexpr (A == Act::I8) rsrc = args.a_qsum + sr * G;
+        else rsrc = args.a_gsum + sr * G;
+      }
     }
-    const uint16_t* wscale = reinterpret_cast<const uint16_t*>(wbase + w_scale_off);
-    const uint8_t* wzero = wbase + w_zero_off;
-
-    auto issue_a = [&](int g, int buf) {
+    auto slot_of = [&](auto sl) -> uint8_t* {
+      if constexpr (decltype(sl)::value == 0) return slot0;
+      else if constexpr (decltype(sl)::value == 1) return slot1;
+      else return slot2;
+    };
+    auto issue = [&](int g, auto sl) {
+      uint8_t* base = slot_of(sl);
 #pragma unroll
-      for (int j = 0; j < INSTS; ++j) {
-        uint8_t* dst = a_lds + buf * TILE_BYTES + (32 * wid + ROWS_PER_INST * j) * ROWB;
+      for (int j = 0; j < A_INSTS; ++j)
         __builtin_amdgcn_global_load_lds(static_cast<const void*>(arow[j] + int64_t(g) * ROWB),
-                                         (lds_ptr_t)(dst), 16, 0, 0);
-      }
-    };
-    auto load_rowsum = [&](int g) -> float {
-      if (threadIdx.x >= kPfRows) return 0.f;
-      if constexpr (A == Act::I8) {
-        if constexpr (ASYM) return __int_as_float(args.a_qsum[my_src * G + g]);
-        return 0.f;
-      } else {
-        return args.a_gsum[my_src * G + g];
-      }
-    };
-    struct WStage {
-      uint32_t wv[4][4];
-      uint16_t sc[4];
-      uint8_t zp[4];
-    };
-    auto load_w = [&](WStage& ws, int g) {
+                                         (lds_ptr_t)(base + (32 * wid + ROWS_PER_INST * j) * ROWB), 16, 0, 0);
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
-        const uint4 v = load16_stream(wp[nb] + int64_t(g) * kTileBytes);
-        ws.wv[nb][0] = v.x; ws.wv[nb][1] = v.y; ws.wv[nb][2] = v.z; ws.wv[nb][3] = v.w;
-        ws.sc[nb] = wscale[sidx[nb] + g * 16];
-        ws.zp[nb] = ASYM ? wzero[sidx[nb] + g * 16] : uint8_t(8);
+      for (int j = 0; j < 2; ++j)
+        __builtin_amdgcn_global_load_lds(static_cast<const void*>(wsrc[j] + int64_t(g) * kTileBytes),
+                                         (lds_ptr_t)(base + St::W_OFF + (2 * wid + j) * kTileBytes), 16, 0, 0);
+      if (wid == 0 && (lane < 16 || (ASYM && lane < 24)))
+        __builtin_amdgcn_global_load_lds(static_cast<const void*>(msrc + (lane < 16 ? g * 32 : g * 16)),
+                                         (lds_ptr_t)(base + St::S_OFF), 16, 0, 0);
+      if constexpr (RSUM) {
+        if (wid == 1 || wid == 2)
+          __builtin_amdgcn_global_load_lds(static_cast<const void*>(static_cast<const int32_t*>(rsrc) + g),
+                                           (lds_ptr_t)(base + St::R_OFF + (wid - 1) * 256), 4, 0, 0);
       }
     };
 
@@ -175,12 +198,23 @@ __global__ void __launch_bounds__(256, 2) k_gemm_pf(GemmArgs args) {
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    auto compute = [&](const WStage& ws, int buf) {
-      const uint8_t* at = a_lds + buf * TILE_BYTES;
-      const float* xsb = xs_lds + buf * kPfRows;
-      float sc[4];
+    // compute(sl, after_reads): after the LDS fragments of the stage are in registers,
+    // after_reads() issues the copies of a later stage, then the math runs.
+    auto compute = [&](auto sl, auto&& after_reads) {
+      const uint8_t* base = slot_of(sl);
+      const uint16_t* s_sc = reinterpret_cast<const uint16_t*>(base + St::S_OFF);
+      const uint8_t* s_z = base + St::Z_OFF;
+      const float* s_rs = reinterpret_cast<const float*>(base + St::R_OFF);
+      float sc[4], zp[4];
+      uint32_t wv[4][4];
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) sc[nb] = f16_bits_to_f32(ws.sc[nb]);
+      for (int nb = 0; nb < 4; ++nb) {
+        const int cbl = wn * 4 + nb;
+        sc[nb] = f16_bits_to_f32(s_sc[cbl * 16 + col]);
+        zp[nb] = ASYM ? float(s_z[cbl * 16 + col]) : 8.0f;
+        const uint4 v = *reinterpret_cast<const uint4*>(base + St::W_OFF + cbl * kTileBytes + lane * 16);
+        wv[nb][0] = v.x; wv[nb][1] = v.y; wv[nb][2] = v.z; wv[nb][3] = v.w;
+      }
       if constexpr (A == Act::BF16) {
         uint32_t af[4][4][4];
         f32x4_t xv[4];
@@ -190,17 +224,18 @@ __global__ void __launch_bounds__(256, 2) k_gemm_pf(GemmArgs args) {
 #pragma unroll
           for (int s = 0; s < 4; ++s) {
             const int c = (4 * s + kq) ^ col;          // r % 16 == col
-            const uint4 v = *reinterpret_cast<const uint4*>(at + r * ROWB + c * 16);
+            const uint4 v = *reinterpret_cast<const uint4*>(base + r * ROWB + c * 16);
             af[mb][s][0] = v.x; af[mb][s][1] = v.y; af[mb][s][2] = v.z; af[mb][s][3] = v.w;
           }
-          xv[mb] = *reinterpret_cast<const f32x4_t*>(xsb + wm * 64 + mb * 16 + 4 * kq);
+          xv[mb] = *reinterpret_cast<const f32x4_t*>(s_rs + wm * 64 + mb * 16 + 4 * kq);
         }
+        after_reads();
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb) {
           uint32_t b[4][4];
 #pragma unroll
-          for (int s = 0; s < 4; ++s) widen_word_fp<A>(ws.wv[nb][s], b[s]);
-          const float negz = -(magic_offset<A>() + float(ws.zp[nb]));
+          for (int s = 0; s < 4; ++s) widen_word_fp<A>(wv[nb][s], b[s]);
+          const float negz = -(magic_offset<A>() + zp[nb]);
 #pragma unroll
           for (int mb = 0; mb < 4; ++mb) {
             f32x4_t gacc = xv[mb] * negz;
@@ -219,25 +254,26 @@ __global__ void __launch_bounds__(256, 2) k_gemm_pf(GemmArgs args) {
 #pragma unroll
           for (int i = 0; i < 2; ++i) {
             const int c1 = (4 * i + (kq >> 1)) ^ (col & 7), c2 = (4 * i + 2 + (kq >> 1)) ^ (col & 7);
-            const uint2 lo = *reinterpret_cast<const uint2*>(at + r * ROWB + c1 * 16 + 8 * (kq & 1));
-            const uint2 hi = *reinterpret_cast<const uint2*>(at + r * ROWB + c2 * 16 + 8 * (kq & 1));
+            const uint2 lo = *reinterpret_cast<const uint2*>(base + r * ROWB + c1 * 16 + 8 * (kq & 1));
+            const uint2 hi = *reinterpret_cast<const uint2*>(base + r * ROWB + c2 * 16 + 8 * (kq & 1));
             af[mb][i][0] = lo.x; af[mb][i][1] = lo.y; af[mb][i][2] = hi.x; af[mb][i][3] = hi.y;
           }
           if constexpr (ASYM) {
-            const f32x4_t q4 = *reinterpret_cast<const f32x4_t*>(xsb + wm * 64 + mb * 16 + 4 * kq);
+            const i32x4_t q4 = *reinterpret_cast<const i32x4_t*>(s_rs + wm * 64 + mb * 16 + 4 * kq);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) qv[mb][i] = __float_as_int(q4[i]);
+            for (int i = 0; i < 4; ++i) qv[mb][i] = q4[i];
           }
         }
+        after_reads();
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb) {
           uint32_t b[2][4];
 #pragma unroll
           for (int i = 0; i < 2; ++i) {
-            widen_word_i8(ws.wv[nb][2 * i], b[i][0], b[i][1]);
-            widen_word_i8(ws.wv[nb][2 * i + 1], b[i][2], b[i][3]);
+            widen_word_i8(wv[nb][2 * i], b[i][0], b[i][1]);
+            widen_word_i8(wv[nb][2 * i + 1], b[i][2], b[i][3]);
           }
-          const int32_t zoff = int32_t(ws.zp[nb]) - 8;
+          const int32_t zoff = int32_t(zp[nb]) - 8;
 #pragma unroll
           for (int mb = 0; mb < 4; ++mb) {
             i32x4_t gacc = {0, 0, 0, 0};
@@ -254,33 +290,33 @@ __global__ void __launch_bounds__(256, 2) k_gemm_pf(GemmArgs args) {
       }
     };
 
-    // prologue: group 0 into buffer 0
-    WStage w0, w1;
-    issue_a(0, 0);
-    load_w(w0, 0);
-    {
-      const float rs = load_rowsum(0);
-      if (threadIdx.x < kPfRows) xs_lds[threadIdx.x] = rs;
-    }
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    auto step = [&](int g, WStage& cur, WStage& nxt) {
-      const int buf = g & 1;
-      float rs = 0.f;
-      const bool more = g + 1 < G;
-      if (more) {
-        issue_a(g + 1, buf ^ 1);
-        load_w(nxt, g + 1);
-        rs = load_rowsum(g + 1);
-      }
-      compute(cur, buf);
-      if (more && threadIdx.x < kPfRows) xs_lds[(buf ^ 1) * kPfRows + threadIdx.x] = rs;
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
+    // 3-slot ring: stages g + 1 and g + 2 are in flight while stage g is computed.  Each
+    // wave issues at least A_INSTS + 2 copies per stage, so waiting until that many are
+    // outstanding leaves only the newest stage in flight; then a barrier publishes every
+    // wave's completed copies.  (The raw barrier carries no wait of its own; the empty
+    // asm statements keep the compiler from moving memory accesses across it.)
+    auto sync = [&](bool newest_in_flight) {
+      if (newest_in_flight) wait_vmcnt<A_INSTS + 2>();
+      else wait_vmcnt<0>();
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
     };
-    for (int g = 0; g < G; g += 2) {
-      step(g, w0, w1);
-      if (g + 1 < G) step(g + 1, w1, w0);
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    using S2 = std::integral_constant<int, 2>;
+    issue(0, S0{});
+    if (G > 1) issue(1, S1{});
+    sync(G > 1);
+    for (int g = 0; g < G; g += 3) {
+      compute(S0{}, [&] { if (g + 2 < G) issue(g + 2, S2{}); });
+      sync(g + 2 < G);
+      if (g + 1 >= G) break;
+      compute(S1{}, [&] { if (g + 3 < G) issue(g + 3, S0{}); });
+      sync(g + 3 < G);
+      if (g + 2 >= G) break;
+      compute(S2{}, [&] { if (g + 4 < G) issue(g + 4, S1{}); });
+      sync(g + 4 < G);
     }
 
     // epilogue
@@ -316,21 +352,20 @@ __global__ void __launch_bounds__(256, 2) k_gemm_pf(GemmArgs args) {
 }
 
 size_t prefill_lds_bytes(int act) {
-  const int esz = act == 2 ? 1 : 2;
-  return size_t(2) * kPfRows * kGroup * esz + 2 * kPfRows * sizeof(float);
+  return size_t(kPfStages) * (act == 2 ? PfStage<Act::I8>::BYTES : PfStage<Act::BF16>::BYTES);
 }
+
 
 template <Act A, int KIND>
 static hipError_t launch_pf_kind(const GemmArgs& g, hipStream_t st) {
   const int64_t nblk = g.N / (16 * kPfCB);
   const int64_t items = int64_t(g.max_tiles) * nblk;
   if (items == 0) return hipSuccess;
-  const unsigned grid = unsigned(std::min<int64_t>(items, 256 * 2));
-  const size_t lds = prefill_lds_bytes(int(A));
+  const unsigned grid = unsigned(std::min<int64_t>(items, 256));
   if (g.asym)
-    hipLaunchKernelGGL((k_gemm_pf<A, KIND, true>), dim3(grid), dim3(256), lds, st, g);
+    hipLaunchKernelGGL((k_gemm_pf<A, KIND, true>), dim3(grid), dim3(256), 0, st, g);
   else
-    hipLaunchKernelGGL((k_gemm_pf<A, KIND, false>), dim3(grid), dim3(256), lds, st, g);
+    hipLaunchKernelGGL((k_gemm_pf<A, KIND, false>), dim3(grid), dim3(256), 0, st, g);
   return hipGetLastError();
 }
 
