@@ -24,6 +24,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+# HBM counter summary (rocprofv3 FETCH_SIZE / WRITE_SIZE, copy-calibrated) of the default workload's
+# gate/up kernel; used as roofline traffic only while the GEMM sources still hash the same
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "k_gemm_gate_up_moe256_T64_w4a16.txt")
 BF16_PEAK_TFLOPS = 2500.0      # dense bf16 MFMA
 INT8_PEAK_TOPS = 5000.0        # dense int8 MFMA
 
@@ -249,6 +252,12 @@ def main():
                 "frac": round(main_res["gate_up_GBps"] / HBM_PEAK_GBS, 4), "traffic": None,
                 "algorithmic_bytes_per_launch": main_res["gate_up_bytes"],
                 "avg_launch_ms": main_res["stage_ms"]["gate_up"]}
+        if args.tokens == 64 and args.mode == "w4a16":
+            from int4_group_quantized_g128_amd import profiling
+            kv = profiling.read_kv(TRAFFIC_PROFILE)
+            if kv.get("source_hash") == profiling.source_hash() and "traffic_bytes[gate_up]" in kv:
+                roof["traffic"] = int(kv["traffic_bytes[gate_up]"])
+                roof["traffic_source"] = os.path.relpath(TRAFFIC_PROFILE, ROOT)
 
     extra = {}
     if not args.no_extra:

@@ -1,0 +1,148 @@
+"""Summaries of rocprofv3 runs of the benchmark (kernel statistics and HBM counters).
+
+Usage, after the three rocprofv3 runs (``--kernel-trace --stats``, ``--pmc FETCH_SIZE``,
+``--pmc WRITE_SIZE``, each with ``-f csv -d DIR``) of the same bench.py command::
+
+    python -m int4_group_quantized_g128_amd.profiling \\
+        --stats DIR_STATS --fetch DIR_FETCH --write DIR_WRITE \\
+        --role 'gate_up=k_gemm<\\(q4::Act\\)0, 1, false, 1, 1, 4, 2>' \\
+        --workload "..." --commands "..." --out profiles/NAME
+
+Each ``--role NAME=REGEX`` names one kernel instantiation (a regular expression searched
+in the demangled kernel name).  The summary ``NAME.md`` keeps every library kernel's
+average duration and, per role, the FETCH_SIZE / WRITE_SIZE counters per dispatch scaled
+by what the same counters read for a plain device copy of known size (the bench's
+``--copy-calibration`` copy of 512 MiB, ``__amd_rocclr_copyBuffer``), plus a hash of the
+GEMM kernel sources the counters were taken with.  ``NAME.txt`` repeats the derived
+figures as ``key=value`` lines; bench.py reports them as the roofline traffic only while
+the hash still matches the sources.
+"""
+import argparse
+import collections
+import csv
+import glob
+import hashlib
+import os
+import re
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+KERNEL_SOURCES = ("csrc/common.h", "csrc/internal.h", "csrc/gemm.hip", "csrc/gemm_prefill.hip")
+COPY_BYTES = 512 * 1024 * 1024
+COPY_KERNEL = "__amd_rocclr_copyBuffer"
+
+
+def source_hash():
+    """Hash of the GEMM kernel sources (counters are stale once these change)."""
+    h = hashlib.sha1()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(HERE, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_kv(path):
+    """The key=value figures of a summary (empty dict when the file is missing)."""
+    out = {}
+    if not os.path.exists(path):
+        return out
+    with open(path) as f:
+        for line in f:
+            if "=" in line:
+                k, v = line.rstrip("\n").split("=", 1)
+                out[k] = v
+    return out
+
+
+def _csv(d, suffix):
+    files = sorted(glob.glob(os.path.join(d, "**", f"*{suffix}"), recursive=True))
+    if not files:
+        raise FileNotFoundError(f"no *{suffix} under {d}")
+    rows = []
+    for fn in files:
+        with open(fn) as f:
+            rows += list(csv.DictReader(f))
+    return rows
+
+
+def kernel_stats(d):
+    """kernel name -> (calls, average ns)"""
+    return {r["Name"]: (int(r["Calls"]), float(r["AverageNs"])) for r in _csv(d, "kernel_stats.csv")}
+
+
+def counter_values(d, counter):
+    """kernel name -> per-dispatch counter values (KiB for the *_SIZE counters)."""
+    agg = collections.defaultdict(list)
+    for r in _csv(d, "counter_collection.csv"):
+        if r.get("Counter_Name") == counter:
+            agg[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+    return agg
+
+
+def _match(names, rx):
+    hits = [n for n in names if re.search(rx, n)]
+    if len(hits) != 1:
+        raise SystemExit(f"role regex {rx!r} matches {len(hits)} kernels: {hits}")
+    return hits[0]
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--stats", required=True)
+    ap.add_argument("--fetch", required=True)
+    ap.add_argument("--write", required=True)
+    ap.add_argument("--role", action="append", default=[], help="NAME=REGEX")
+    ap.add_argument("--workload", required=True)
+    ap.add_argument("--commands", default="")
+    ap.add_argument("--out", required=True)
+    a = ap.parse_args()
+
+    stats = kernel_stats(a.stats)
+    fetch = counter_values(a.fetch, "FETCH_SIZE")
+    write = counter_values(a.write, "WRITE_SIZE")
+    kib = COPY_BYTES / 1024.0
+    cf = max(fetch.get(COPY_KERNEL, [0.0]))
+    cw = max(write.get(COPY_KERNEL, [0.0]))
+    if not (cf and cw):
+        raise SystemExit("the counter runs hold no copy-calibration dispatch")
+    f_scale, w_scale = kib / cf, kib / cw
+    sh = source_hash()
+    lines = [f"# rocprofv3 summary: {a.workload}", "",
+             f"GEMM kernel source hash `{sh}` (csrc/common.h, internal.h, gemm.hip, gemm_prefill.hip).", "",
+             "Commands (on an MI355X; $R is the repository root):", "", "```", a.commands.strip(), "```", "",
+             "## Kernel statistics (--kernel-trace --stats)", "",
+             "| kernel | calls | average µs |", "|---|---|---|"]
+    for name, (calls, avg) in sorted(stats.items(), key=lambda kv: -kv[1][0] * kv[1][1]):
+        if "q4::" in name:
+            lines.append(f"| `{name.split('(q4::GemmArgs)')[0][:120]}` | {calls} | {avg / 1e3:.2f} |")
+    lines += ["", "## HBM counters per dispatch (--pmc FETCH_SIZE; --pmc WRITE_SIZE)", "",
+              f"Calibration: the {COPY_BYTES}-byte device copy reads FETCH_SIZE {cf:.0f} KiB and WRITE_SIZE "
+              f"{cw:.0f} KiB, so one counted KiB stands for {f_scale:.4f} KiB read and {w_scale:.4f} KiB written.",
+              "", "| role | kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | read bytes | written bytes | "
+              "average µs (trace) |", "|---|---|---|---|---|---|---|---|"]
+    kv = {"source_hash": sh, "fetch_scale": f"{f_scale:.6f}", "write_scale": f"{w_scale:.6f}"}
+    for role in a.role:
+        rname, rx = role.split("=", 1)
+        kn = _match(set(fetch) | set(write) | set(stats), rx)
+        fv, wv = fetch.get(kn, []), write.get(kn, [])
+        fm = sum(fv) / max(len(fv), 1)
+        wm = sum(wv) / max(len(wv), 1)
+        rb, wb = fm * 1024 * f_scale, wm * 1024 * w_scale
+        avg = stats.get(kn, (0, 0.0))[1] / 1e3
+        lines.append(f"| {rname} | `{kn.split('(q4::GemmArgs)')[0]}` | {len(fv)} | {fm:.0f} | {wm:.0f} | "
+                     f"{rb:.4g} | {wb:.4g} | {avg:.2f} |")
+        kv[f"kernel[{rname}]"] = kn
+        kv[f"read_bytes[{rname}]"] = f"{rb:.0f}"
+        kv[f"write_bytes[{rname}]"] = f"{wb:.0f}"
+        kv[f"traffic_bytes[{rname}]"] = f"{rb + wb:.0f}"
+        kv[f"avg_us[{rname}]"] = f"{avg:.3f}"
+    os.makedirs(os.path.dirname(os.path.abspath(a.out)), exist_ok=True)
+    with open(a.out + ".md", "w") as f:
+        f.write("\n".join(lines) + "\n")
+    with open(a.out + ".txt", "w") as f:
+        for k, v in kv.items():
+            f.write(f"{k}={v}\n")
+    print("\n".join(lines))
+
+
+if __name__ == "__main__":
+    main()
