@@ -23,6 +23,8 @@ FLAGS = [
     "-Wno-unused-function",
     # packed fp32 arithmetic off in device code (v_pk_* fp32 forms are avoided)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results in VGPRs (the per-group scaling reads them with VALU right away)
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-fvisibility=hidden",
 ]
 

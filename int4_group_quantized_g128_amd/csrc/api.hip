@@ -83,8 +83,12 @@ int row_blocks_for(const q4_moe_layer_t* L, int64_t t) {
   return 4;
 }
 
-bool use_prefill(const q4_moe_layer_t* L, int64_t t) {
-  return avg_rows(L, t) >= 64 && (2 * int64_t(L->inter)) % 128 == 0 && L->hidden % 128 == 0;
+bool use_prefill(const q4_moe_layer_t* L, int64_t t, int mode) {
+  const int act = mode == Q4_W4A8 ? 2 : 0;
+  const int64_t S = L->top_k + (L->shared_inter > 0 ? 1 : 0);
+  return avg_rows(L, t) >= 64 && (2 * int64_t(L->inter)) % 128 == 0 && L->hidden % 128 == 0 &&
+         prefill_fits(t, L->hidden, act, int64_t(q4_device_bytes(2 * L->inter, L->hidden, L->asymmetric))) &&
+         prefill_fits(t * S, L->inter, act, int64_t(q4_device_bytes(L->hidden, L->inter, L->asymmetric)));
 }
 
 FwdWorkspace carve(const q4_moe_layer_t* L, int64_t t, int mode, void* base) {
@@ -94,7 +98,7 @@ FwdWorkspace carve(const q4_moe_layer_t* L, int64_t t, int mode, void* base) {
   const int64_t S = L->top_k + shared;
   const int64_t P = t * S;
   const int64_t H = L->hidden, I = L->inter;
-  w.prefill = use_prefill(L, t);
+  w.prefill = use_prefill(L, t, mode);
   w.tile_rows = w.prefill ? 128 : 16 * row_blocks_for(L, t);
   w.max_tiles = int32_t(P / w.tile_rows + std::min<int64_t>(ee, P) + 1);
   int64_t off = 0;
@@ -314,7 +318,9 @@ int moe_int4_ffn_forward(const q4_moe_layer_t* L, const uint16_t* x_bf16, int64_
   gu.num_tiles = w.num_tiles;
   gu.max_tiles = w.max_tiles;
   gu.out = w.h;
+  gu.a_rows = t;
   GemmArgs dn = gu;
+  dn.a_rows = t * S;
   dn.perm = nullptr;
   dn.w = static_cast<const uint8_t*>(L->down);
   dn.w_stride = int64_t(q4_device_bytes(H, I, L->asymmetric));
@@ -396,6 +402,7 @@ int int4_linear_forward(const void* x, int x_dtype, int64_t t, int64_t k, const 
   g.N = n;
   g.K = k;
   g.dense_rows = t;
+  g.a_rows = t;
   g.out = y;
   const int rb = t <= 16 ? 1 : (t <= 32 ? 2 : 4);
   return check_hip(launch_gemm(g, x_dtype == Q4_F16 ? 1 : 0, GEMM_PLAIN, rb, stream), "linear gemm");
@@ -418,6 +425,7 @@ int int4_w4a8_group_acc(const int8_t* q, int64_t rows, int64_t k, const void* w_
   g.N = n;
   g.K = k;
   g.dense_rows = rows;
+  g.a_rows = rows;
   g.acc_out = acc;
   return check_hip(launch_gemm(g, 2, GEMM_GROUP_ACC, 1, stream), "group acc gemm");
 }

@@ -30,6 +30,13 @@ Q4_DEVICE To bitcast(const From& v) {
   return __builtin_bit_cast(To, v);
 }
 
+// SwiGLU of one element: silu(g) * u = g / (1 + e^-g) * u, with the hardware exp2 and
+// reciprocal (about 1 ulp each; -g large gives e^-g = inf and a zero result).
+Q4_DEVICE float swiglu(float g, float u) {
+  const float e = __expf(-g);
+  return g * __builtin_amdgcn_rcpf(1.0f + e) * u;
+}
+
 Q4_DEVICE float bf16_to_f32(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
 
 // float -> bf16, round to nearest even (finite inputs; NaN kept quiet).

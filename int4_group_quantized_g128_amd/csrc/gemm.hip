@@ -377,7 +377,7 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs args) {
 #pragma unroll
               for (int p = 0; p < NBW / 2; ++p) {
                 const float gg = acc[mb][2 * p][i] * sa, uu = acc[mb][2 * p + 1][i] * sa;
-                const float hv = gg / (1.0f + expf(-gg)) * uu;
+                const float hv = swiglu(gg, uu);
                 const int64_t hcol = ((cb0 + lcb) / 2 + p) * 16 + col;
                 if constexpr (A == Act::I8)
                   static_cast<float*>(args.out)[pos * I + hcol] = hv;

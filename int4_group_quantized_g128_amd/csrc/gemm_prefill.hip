@@ -89,6 +89,48 @@ Q4_DEVICE void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
+// Raw buffer resource (V#) over [base, base + bytes), bytes < 2^31: copies address it with
+// a per-lane 32-bit offset plus a wave-uniform scalar offset, so advancing K costs no VALU.
+Q4_DEVICE u32x4_t buffer_rsrc(const void* base, int64_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  return u32x4_t{uint32_t(a), uint32_t(a >> 32) & 0xffffu, uint32_t(bytes), 0x00020000u};
+}
+
+Q4_DEVICE uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_ptr_t)(const_cast<void*>(p))));
+}
+
+// Direct-to-LDS copy of SIZE (16 or 4) bytes per lane: lane L's bytes land at
+// lds + L * SIZE.  Written as inline asm with no register outputs other than a scratch
+// SGPR: the compiler then does not see an LDS write whose target it cannot tell apart
+// from the ring slot being read, and would otherwise wait for every copy in flight
+// before each LDS read.  The kernel orders copies and reads itself (vmcnt waits +
+// barriers).  M0 (the LDS base of the copy) is saved and restored around it; the
+// leading s_nop covers the wait states between SGPR/M0 writes and their use.
+template <int SIZE>
+Q4_DEVICE void copy_to_lds(const u32x4_t& rsrc, uint32_t lds_in, uint32_t voff, uint32_t soff_in) {
+  static_assert(SIZE == 16 || SIZE == 4, "copy size");
+  // wave-uniform by construction; readfirstlane makes that visible (scalar operands)
+  const uint32_t lds = __builtin_amdgcn_readfirstlane(lds_in);
+  const uint32_t soff = __builtin_amdgcn_readfirstlane(soff_in);
+  uint32_t saved;
+  if constexpr (SIZE == 16)
+    asm volatile(
+        "s_mov_b32 %0, m0\n\ts_nop 4\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
+        "buffer_load_dwordx4 %2, %3, %4 offen lds\n\ts_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(lds), "v"(voff), "s"(rsrc), "s"(soff)
+        : "memory");
+  else
+    asm volatile(
+        "s_mov_b32 %0, m0\n\ts_nop 4\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
+        "buffer_load_dword %2, %3, %4 offen lds\n\ts_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(lds), "v"(voff), "s"(rsrc), "s"(soff)
+        : "memory");
+  (void)saved;
+}
+
 // Per-stage LDS image of one group (K = 128) of one work item:
 //   A tile  [128 rows][ROWB]  (16-byte chunks XOR-swizzled by row)
 //   W tiles [8 column blocks][64 lanes][16 B]  (the device tiles as stored)
@@ -105,16 +147,35 @@ struct PfStage {
   static constexpr int R_OFF = S_OFF + 512;
   static constexpr int BYTES = R_OFF + kPfRows * 4;
 };
-constexpr int kPfStages = 3;
+
+// Work items (row tile, 128-column block) in tile-major order.  Workgroups are dispatched
+// round-robin over the 8 XCDs (workgroup x runs on XCD x % 8); with a grid that is a
+// multiple of 8, each XCD walks one contiguous range of items, so the column blocks that
+// share an activation tile are computed under the same L2.
+struct ItemRange {
+  int64_t first, last, step;
+};
+Q4_DEVICE ItemRange item_range(int64_t items) {
+  const int64_t nwg = gridDim.x;
+  if (nwg % 8 != 0) return {int64_t(blockIdx.x), items, nwg};
+  const int64_t chunk = (items + 7) / 8, xcd = blockIdx.x % 8;
+  const int64_t last = std::min<int64_t>(items, (xcd + 1) * chunk);
+  return {xcd * chunk + blockIdx.x / 8, last, nwg / 8};
+}
 
 template <Act A, int KIND, bool ASYM>
 __global__ void __launch_bounds__(256, 1) k_gemm_pf(GemmArgs args) {
   using St = PfStage<A>;
   constexpr int ROWB = St::ROWB;
   constexpr int CHUNKS = ROWB / 16;                   // 16-byte chunks per row
-  constexpr int ROWS_PER_INST = 64 / CHUNKS;          // rows one direct-to-LDS load covers
-  constexpr int A_INSTS = 32 / ROWS_PER_INST;         // A loads per wave per stage (32 rows)
+  constexpr int ROWS_PER_INST = 64 / CHUNKS;          // rows one copy instruction covers
+  constexpr int A_INSTS = 32 / ROWS_PER_INST;         // A copies per wave per stage (32 rows)
   constexpr bool RSUM = (A != Act::I8) || ASYM;
+  // LDS slot of 16-byte chunk c of tile row r: c ^ swz(r).  A fragment read touches 16
+  // rows (r % 16 = 0..15) at one chunk index: bf16 rows are 256 B (one bank period), so
+  // XOR by r % 16 spreads them; int8 rows are 128 B, two rows per period, so rows of
+  // equal parity are spread by (r / 2) % 8.
+  auto swz = [](int r) -> int { return CHUNKS == 16 ? (r & 15) : ((r >> 1) & 7); };
   // three distinct LDS objects, so the compiler can tell which in-flight copies a read
   // depends on (the loop below is unrolled by three to keep each slot compile-time)
   __shared__ __align__(16) uint8_t slot0[St::BYTES];
@@ -122,73 +183,77 @@ __global__ void __launch_bounds__(256, 1) k_gemm_pf(GemmArgs args) {
   __shared__ __align__(16) uint8_t slot2[St::BYTES];
 
   const int lane = threadIdx.x & 63;
-  const int wid = threadIdx.x >> 6;
+  const int wid = __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6));
+  // wave (wm, wn): row blocks {wm, wm + 2, wm + 4, wm + 6} (interleaved, so that a short
+  // tile leaves both wave rows with work) and column blocks 4 wn .. 4 wn + 3
   const int wm = wid & 1, wn = wid >> 1;
   const int col = lane & 15, kq = lane >> 4;
   const int64_t N = args.N, K = args.K;
   const int G = int(K / kGroup);
   const int64_t nblk = N / (16 * kPfCB);
-  const int64_t ntiles = *args.num_tiles;
-  const int64_t items = ntiles * nblk;
+  const int64_t items = *args.num_tiles * nblk;
   const int64_t w_scale_off = align256(N * K / 2);
   const int64_t w_zero_off = w_scale_off + align256(2 * N * int64_t(G));
+  const auto a_rsrc = buffer_rsrc(args.a, args.a_rows * K * St::ESZ);
+  const void* rs_base = (A == Act::I8) ? static_cast<const void*>(args.a_qsum) : static_cast<const void*>(args.a_gsum);
+  const auto r_rsrc = buffer_rsrc(rs_base, RSUM ? args.a_rows * G * 4 : 0);
 
-  for (int64_t item = blockIdx.x; item < items; item += gridDim.x) {
+  const ItemRange ir = item_range(items);
+  for (int64_t item = ir.first; item < ir.last; item += ir.step) {
     const int64_t tile = item / nblk;
     const int64_t cb0 = (item % nblk) * kPfCB;
     const TileDesc d = args.tiles[tile];
-    const int64_t row_start = d.row_start, rows = d.rows;
+    const int64_t row_start = d.row_start;
+    const int rows = d.rows;
     const uint8_t* wbase = d.expert < args.num_experts ? args.w + int64_t(d.expert) * args.w_stride : args.w_shared;
-    auto src_of = [&](int64_t r) -> int64_t {   // activation row of tile row r (clamped)
+    const auto w_rsrc = buffer_rsrc(wbase, args.w_stride);
+    auto src_of = [&](int r) -> int64_t {   // activation row of tile row r (clamped)
       const int64_t pos = row_start + (r < rows ? r : 0);
       return args.perm ? args.perm[pos] / args.slots_per_token : pos;
     };
-    // global sources of this lane's direct-to-LDS copies
-    const uint8_t* arow[A_INSTS];
+    // per-lane byte offsets of this lane's copies (the stage adds a scalar offset)
+    uint32_t a_off[A_INSTS];
 #pragma unroll
     for (int j = 0; j < A_INSTS; ++j) {
       const int r = 32 * wid + ROWS_PER_INST * j + lane / CHUNKS;
-      const int c = (lane % CHUNKS) ^ (r % CHUNKS);   // global chunk that lands in this slot
-      arow[j] = static_cast<const uint8_t*>(args.a) + src_of(r) * K * St::ESZ + c * 16;
+      const int c = (lane % CHUNKS) ^ swz(r);         // global chunk that lands in this slot
+      a_off[j] = uint32_t(src_of(r) * K * St::ESZ + c * 16);
     }
-    const uint8_t* wsrc[2];
+    uint32_t w_off[2];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) wsrc[j] = wbase + (cb0 + 2 * wid + j) * G * kTileBytes + lane * 16;
-    // wave 0: scales (lanes 0..15) and zero points (lanes 16..23) of the 8 blocks
-    const uint8_t* msrc = nullptr;
-    if (lane < 16) msrc = wbase + w_scale_off + ((cb0 + lane / 2) * G) * 32 + (lane & 1) * 16;
-    else if (lane < 24) msrc = wbase + w_zero_off + ((cb0 + lane - 16) * G) * 16;
-    // waves 1 and 2: the row sums of rows (wid - 1) * 64 + lane
-    const void* rsrc = nullptr;
-    if constexpr (RSUM) {
-      if (wid == 1 || wid == 2) {
-        const int64_t sr = src_of((wid - 1) * 64 + lane);
-        if constexpr (A == Act::I8) rsrc = args.a_qsum + sr * G;
-        else rsrc = args.a_gsum + sr * G;
-      }
+    for (int j = 0; j < 2; ++j) w_off[j] = uint32_t((cb0 + 2 * wid + j) * G * kTileBytes + lane * 16);
+    // wave 0: scales of the 8 blocks (lanes 0..15, 32 B per block and group) and zero
+    // points (lanes 16..23, 16 B per block and group)
+    uint32_t m_off = 0, m_step = 0;
+    if (lane < 16) {
+      m_off = uint32_t(w_scale_off + (cb0 + lane / 2) * G * 32 + (lane & 1) * 16);
+      m_step = 32;
+    } else if (lane < 24) {
+      m_off = uint32_t(w_zero_off + (cb0 + lane - 16) * G * 16);
+      m_step = 16;
     }
+    // waves 1 and 2: the row sums of tile rows (wid - 1) * 64 + lane
+    uint32_t r_off = 0;
+    if (RSUM && (wid == 1 || wid == 2)) r_off = uint32_t(src_of((wid - 1) * 64 + lane) * G * 4);
+
     auto slot_of = [&](auto sl) -> uint8_t* {
       if constexpr (decltype(sl)::value == 0) return slot0;
       else if constexpr (decltype(sl)::value == 1) return slot1;
       else return slot2;
     };
     auto issue = [&](int g, auto sl) {
-      uint8_t* base = slot_of(sl);
+      const uint32_t base = lds_addr(slot_of(sl));
 #pragma unroll
       for (int j = 0; j < A_INSTS; ++j)
-        __builtin_amdgcn_global_load_lds(static_cast<const void*>(arow[j] + int64_t(g) * ROWB),
-                                         (lds_ptr_t)(base + (32 * wid + ROWS_PER_INST * j) * ROWB), 16, 0, 0);
+        copy_to_lds<16>(a_rsrc, base + (32 * wid + ROWS_PER_INST * j) * ROWB, a_off[j], uint32_t(g * ROWB));
 #pragma unroll
       for (int j = 0; j < 2; ++j)
-        __builtin_amdgcn_global_load_lds(static_cast<const void*>(wsrc[j] + int64_t(g) * kTileBytes),
-                                         (lds_ptr_t)(base + St::W_OFF + (2 * wid + j) * kTileBytes), 16, 0, 0);
+        copy_to_lds<16>(w_rsrc, base + St::W_OFF + (2 * wid + j) * kTileBytes, w_off[j], uint32_t(g * kTileBytes));
       if (wid == 0 && (lane < 16 || (ASYM && lane < 24)))
-        __builtin_amdgcn_global_load_lds(static_cast<const void*>(msrc + (lane < 16 ? g * 32 : g * 16)),
-                                         (lds_ptr_t)(base + St::S_OFF), 16, 0, 0);
+        copy_to_lds<16>(w_rsrc, base + St::S_OFF, m_off + uint32_t(g) * m_step, 0u);
       if constexpr (RSUM) {
         if (wid == 1 || wid == 2)
-          __builtin_amdgcn_global_load_lds(static_cast<const void*>(static_cast<const int32_t*>(rsrc) + g),
-                                           (lds_ptr_t)(base + St::R_OFF + (wid - 1) * 256), 4, 0, 0);
+          copy_to_lds<4>(r_rsrc, base + St::R_OFF + (wid - 1) * 256, r_off, uint32_t(g * 4));
       }
     };
 
@@ -198,103 +263,106 @@ __global__ void __launch_bounds__(256, 1) k_gemm_pf(GemmArgs args) {
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    // compute(sl, after_reads): after the LDS fragments of the stage are in registers,
-    // after_reads() issues the copies of a later stage, then the math runs.
-    auto compute = [&](auto sl, auto&& after_reads) {
+    // One group of one stage: the widened weight fragments of the wave's 4 column blocks
+    // stay in registers; the activation fragments are read per row block.  Only the
+    // wave's first NMB row blocks hold valid rows (NMB is fixed per work item, so the
+    // step has no branches and the MFMAs of one row block overlap the scaling of another).
+    auto compute = [&](auto sl, auto nmb_c) {
+      constexpr int NMB = decltype(nmb_c)::value;
       const uint8_t* base = slot_of(sl);
       const uint16_t* s_sc = reinterpret_cast<const uint16_t*>(base + St::S_OFF);
       const uint8_t* s_z = base + St::Z_OFF;
-      const float* s_rs = reinterpret_cast<const float*>(base + St::R_OFF);
-      float sc[4], zp[4];
-      uint32_t wv[4][4];
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
-        const int cbl = wn * 4 + nb;
-        sc[nb] = f16_bits_to_f32(s_sc[cbl * 16 + col]);
-        zp[nb] = ASYM ? float(s_z[cbl * 16 + col]) : 8.0f;
-        const uint4 v = *reinterpret_cast<const uint4*>(base + St::W_OFF + cbl * kTileBytes + lane * 16);
-        wv[nb][0] = v.x; wv[nb][1] = v.y; wv[nb][2] = v.z; wv[nb][3] = v.w;
-      }
       if constexpr (A == Act::BF16) {
-        uint32_t af[4][4][4];
-        f32x4_t xv[4];
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb) {
-          const int r = wm * 64 + mb * 16 + col;
-#pragma unroll
-          for (int s = 0; s < 4; ++s) {
-            const int c = (4 * s + kq) ^ col;          // r % 16 == col
-            const uint4 v = *reinterpret_cast<const uint4*>(base + r * ROWB + c * 16);
-            af[mb][s][0] = v.x; af[mb][s][1] = v.y; af[mb][s][2] = v.z; af[mb][s][3] = v.w;
-          }
-          xv[mb] = *reinterpret_cast<const f32x4_t*>(s_rs + wm * 64 + mb * 16 + 4 * kq);
-        }
-        after_reads();
+        float sc[4], negz[4];
+        uint32_t b[4][4][4];
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb) {
-          uint32_t b[4][4];
+          const int cbl = wn * 4 + nb;
+          sc[nb] = f16_bits_to_f32(s_sc[cbl * 16 + col]);
+          negz[nb] = -(magic_offset<A>() + (ASYM ? float(s_z[cbl * 16 + col]) : 8.0f));
+          const uint4 v = *reinterpret_cast<const uint4*>(base + St::W_OFF + cbl * kTileBytes + lane * 16);
+          widen_word_fp<A>(v.x, b[nb][0]);
+          widen_word_fp<A>(v.y, b[nb][1]);
+          widen_word_fp<A>(v.z, b[nb][2]);
+          widen_word_fp<A>(v.w, b[nb][3]);
+        }
+        const float* s_rs = reinterpret_cast<const float*>(base + St::R_OFF);
 #pragma unroll
-          for (int s = 0; s < 4; ++s) widen_word_fp<A>(wv[nb][s], b[s]);
-          const float negz = -(magic_offset<A>() + zp[nb]);
+        for (int mb = 0; mb < NMB; ++mb) {
+          const int rb = 2 * mb + wm;
+          const int r = rb * 16 + col;
+          uint32_t af[4][4];
 #pragma unroll
-          for (int mb = 0; mb < 4; ++mb) {
-            f32x4_t gacc = xv[mb] * negz;
+          for (int s = 0; s < 4; ++s) {
+            const int c = (4 * s + kq) ^ swz(r);
+            const uint4 v = *reinterpret_cast<const uint4*>(base + r * ROWB + c * 16);
+            af[s][0] = v.x; af[s][1] = v.y; af[s][2] = v.z; af[s][3] = v.w;
+          }
+          const f32x4_t xv = *reinterpret_cast<const f32x4_t*>(s_rs + rb * 16 + 4 * kq);
 #pragma unroll
-            for (int s = 0; s < 4; ++s) gacc = mfma16x16x32<A>(af[mb][s], b[s], gacc);
+          for (int nb = 0; nb < 4; ++nb) {
+            f32x4_t gacc = xv * negz[nb];
+#pragma unroll
+            for (int s = 0; s < 4; ++s) gacc = mfma16x16x32<A>(af[s], b[nb][s], gacc);
 #pragma unroll
             for (int i = 0; i < 4; ++i) acc[mb][nb][i] = fmaf(sc[nb], gacc[i], acc[mb][nb][i]);
           }
         }
       } else {
-        uint32_t af[4][2][4];
-        int32_t qv[4][4];
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb) {
-          const int r = wm * 64 + mb * 16 + col;
-#pragma unroll
-          for (int i = 0; i < 2; ++i) {
-            const int c1 = (4 * i + (kq >> 1)) ^ (col & 7), c2 = (4 * i + 2 + (kq >> 1)) ^ (col & 7);
-            const uint2 lo = *reinterpret_cast<const uint2*>(base + r * ROWB + c1 * 16 + 8 * (kq & 1));
-            const uint2 hi = *reinterpret_cast<const uint2*>(base + r * ROWB + c2 * 16 + 8 * (kq & 1));
-            af[mb][i][0] = lo.x; af[mb][i][1] = lo.y; af[mb][i][2] = hi.x; af[mb][i][3] = hi.y;
-          }
-          if constexpr (ASYM) {
-            const i32x4_t q4 = *reinterpret_cast<const i32x4_t*>(s_rs + wm * 64 + mb * 16 + 4 * kq);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) qv[mb][i] = q4[i];
-          }
-        }
-        after_reads();
+        // widened codes are 16 (d - 8); s / 16 is exact in fp32, so scaling the raw
+        // accumulator by s / 16 equals scaling the group sum by s
+        float sc16[4];
+        int32_t zoff16[4];
+        uint32_t b[4][2][4];
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb) {
-          uint32_t b[2][4];
+          const int cbl = wn * 4 + nb;
+          sc16[nb] = f16_bits_to_f32(s_sc[cbl * 16 + col]) * 0.0625f;
+          zoff16[nb] = ASYM ? 16 * (int32_t(s_z[cbl * 16 + col]) - 8) : 0;
+          const uint4 v = *reinterpret_cast<const uint4*>(base + St::W_OFF + cbl * kTileBytes + lane * 16);
+          widen_word_i8(v.x, b[nb][0][0], b[nb][0][1]);
+          widen_word_i8(v.y, b[nb][0][2], b[nb][0][3]);
+          widen_word_i8(v.z, b[nb][1][0], b[nb][1][1]);
+          widen_word_i8(v.w, b[nb][1][2], b[nb][1][3]);
+        }
+        const int32_t* s_qs = reinterpret_cast<const int32_t*>(base + St::R_OFF);
+#pragma unroll
+        for (int mb = 0; mb < NMB; ++mb) {
+          const int rb = 2 * mb + wm;
+          const int r = rb * 16 + col;
+          uint32_t af[2][4];
 #pragma unroll
           for (int i = 0; i < 2; ++i) {
-            widen_word_i8(wv[nb][2 * i], b[i][0], b[i][1]);
-            widen_word_i8(wv[nb][2 * i + 1], b[i][2], b[i][3]);
+            const int c1 = (4 * i + (kq >> 1)) ^ swz(r), c2 = (4 * i + 2 + (kq >> 1)) ^ swz(r);
+            const uint2 lo = *reinterpret_cast<const uint2*>(base + r * ROWB + c1 * 16 + 8 * (kq & 1));
+            const uint2 hi = *reinterpret_cast<const uint2*>(base + r * ROWB + c2 * 16 + 8 * (kq & 1));
+            af[i][0] = lo.x; af[i][1] = lo.y; af[i][2] = hi.x; af[i][3] = hi.y;
           }
-          const int32_t zoff = int32_t(zp[nb]) - 8;
+          i32x4_t qv = {0, 0, 0, 0};
+          if constexpr (ASYM) qv = *reinterpret_cast<const i32x4_t*>(s_qs + rb * 16 + 4 * kq);
 #pragma unroll
-          for (int mb = 0; mb < 4; ++mb) {
+          for (int nb = 0; nb < 4; ++nb) {
             i32x4_t gacc = {0, 0, 0, 0};
-            gacc = mfma_i8_16x16x64(af[mb][0], b[0], gacc);
-            gacc = mfma_i8_16x16x64(af[mb][1], b[1], gacc);
+            gacc = mfma_i8_16x16x64(af[0], b[nb][0], gacc);
+            gacc = mfma_i8_16x16x64(af[1], b[nb][1], gacc);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              int32_t a32 = gacc[i] >> 4;
-              if constexpr (ASYM) a32 -= zoff * qv[mb][i];
-              acc[mb][nb][i] = fmaf(sc[nb], float(a32), acc[mb][nb][i]);
+              int32_t a32 = gacc[i];
+              if constexpr (ASYM) a32 -= zoff16[nb] * qv[i];
+              acc[mb][nb][i] = fmaf(sc16[nb], float(a32), acc[mb][nb][i]);
             }
           }
         }
       }
     };
 
-    // 3-slot ring: stages g + 1 and g + 2 are in flight while stage g is computed.  Each
-    // wave issues at least A_INSTS + 2 copies per stage, so waiting until that many are
-    // outstanding leaves only the newest stage in flight; then a barrier publishes every
-    // wave's completed copies.  (The raw barrier carries no wait of its own; the empty
-    // asm statements keep the compiler from moving memory accesses across it.)
+    // 3-slot ring: while stage g is computed, stages g + 1 and g + 2 are in flight.  The
+    // copies of stage g + 2 go to the slot that stage g - 1 used, which every wave has
+    // finished reading (barrier at the end of the previous step).  Each wave issues at
+    // least A_INSTS + 2 copies per stage, so waiting until that many are outstanding
+    // leaves only the newest stage in flight; the barrier then publishes every wave's
+    // completed copies.  (The raw barrier carries no wait of its own; the empty asm
+    // statements keep the compiler from moving memory accesses across it.)
     auto sync = [&](bool newest_in_flight) {
       if (newest_in_flight) wait_vmcnt<A_INSTS + 2>();
       else wait_vmcnt<0>();
@@ -305,26 +373,41 @@ __global__ void __launch_bounds__(256, 1) k_gemm_pf(GemmArgs args) {
     using S0 = std::integral_constant<int, 0>;
     using S1 = std::integral_constant<int, 1>;
     using S2 = std::integral_constant<int, 2>;
-    issue(0, S0{});
-    if (G > 1) issue(1, S1{});
-    sync(G > 1);
-    for (int g = 0; g < G; g += 3) {
-      compute(S0{}, [&] { if (g + 2 < G) issue(g + 2, S2{}); });
-      sync(g + 2 < G);
-      if (g + 1 >= G) break;
-      compute(S1{}, [&] { if (g + 3 < G) issue(g + 3, S0{}); });
-      sync(g + 3 < G);
-      if (g + 2 >= G) break;
-      compute(S2{}, [&] { if (g + 4 < G) issue(g + 4, S1{}); });
-      sync(g + 4 < G);
+    auto kloop = [&](auto nmb_c) {
+      issue(0, S0{});
+      if (G > 1) issue(1, S1{});
+      sync(G > 1);
+      for (int g = 0; g < G; g += 3) {
+        if (g + 2 < G) issue(g + 2, S2{});
+        compute(S0{}, nmb_c);
+        sync(g + 2 < G);
+        if (g + 1 >= G) break;
+        if (g + 3 < G) issue(g + 3, S0{});
+        compute(S1{}, nmb_c);
+        sync(g + 3 < G);
+        if (g + 2 >= G) break;
+        if (g + 4 < G) issue(g + 4, S1{});
+        compute(S2{}, nmb_c);
+        sync(g + 4 < G);
+      }
+    };
+    // row blocks 2 mb + wm (mb < nmb) hold valid rows; nmb is uniform within the wave
+    const int nrb = (rows + 15) / 16;
+    const int nmb = std::min(4, std::max(0, (nrb - wm + 1) / 2));
+    switch (nmb) {
+      case 4: kloop(std::integral_constant<int, 4>{}); break;
+      case 3: kloop(std::integral_constant<int, 3>{}); break;
+      case 2: kloop(std::integral_constant<int, 2>{}); break;
+      case 1: kloop(std::integral_constant<int, 1>{}); break;
+      default: kloop(std::integral_constant<int, 0>{}); break;
     }
 
-    // epilogue
+    // epilogue: row (2 mb + wm) * 16 + 4 kq + i, columns of blocks 4 wn + nb
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int64_t r = wm * 64 + mb * 16 + 4 * kq + i;
+        const int r = (2 * mb + wm) * 16 + 4 * kq + i;
         if (r >= rows) continue;
         const int64_t pos = row_start + r;
         float sa = 1.0f;
@@ -338,7 +421,7 @@ __global__ void __launch_bounds__(256, 1) k_gemm_pf(GemmArgs args) {
 #pragma unroll
           for (int p = 0; p < 2; ++p) {
             const float gg = acc[mb][2 * p][i] * sa, uu = acc[mb][2 * p + 1][i] * sa;
-            const float hv = gg / (1.0f + expf(-gg)) * uu;
+            const float hv = swiglu(gg, uu);
             const int64_t hcol = ((cb0 + wn * 4) / 2 + p) * 16 + col;
             if constexpr (A == Act::I8)
               static_cast<float*>(args.out)[pos * I + hcol] = hv;
@@ -350,11 +433,6 @@ __global__ void __launch_bounds__(256, 1) k_gemm_pf(GemmArgs args) {
     }
   }
 }
-
-size_t prefill_lds_bytes(int act) {
-  return size_t(kPfStages) * (act == 2 ? PfStage<Act::I8>::BYTES : PfStage<Act::BF16>::BYTES);
-}
-
 
 template <Act A, int KIND>
 static hipError_t launch_pf_kind(const GemmArgs& g, hipStream_t st) {
@@ -369,8 +447,15 @@ static hipError_t launch_pf_kind(const GemmArgs& g, hipStream_t st) {
   return hipGetLastError();
 }
 
+bool prefill_fits(int64_t a_rows, int64_t K, int act, int64_t w_stride) {
+  const int64_t esz = act == 2 ? 1 : 2;
+  const int64_t lim = int64_t(1) << 31;
+  return a_rows * K * esz < lim && a_rows * (K / kGroup) * 4 < lim && w_stride < lim;
+}
+
 hipError_t launch_gemm_prefill(const GemmArgs& g, int act, int kind, hipStream_t st) {
-  if (g.N % (16 * kPfCB) != 0 || !g.tiles) return hipErrorInvalidValue;
+  if (g.N % (16 * kPfCB) != 0 || !g.tiles || !prefill_fits(g.a_rows, g.K, act, g.w_stride))
+    return hipErrorInvalidValue;
   if (act == 0) {
     if (kind == GEMM_GATE_UP) return launch_pf_kind<Act::BF16, GEMM_GATE_UP>(g, st);
     return launch_pf_kind<Act::BF16, GEMM_PLAIN>(g, st);

@@ -44,6 +44,7 @@ struct GemmArgs {
   const float* a_scale;   // int8 mode: per-row scale
   const int32_t* a_qsum;  // int8 asymmetric prefill: per (row, group) code sums [rows][G]
   const float* a_gsum;    // bf16 prefill: per (row, group) activation sums [rows][G]
+  int64_t a_rows;         // rows of the activation buffer(s) a / a_scale / a_qsum / a_gsum
   const int32_t* perm;    // position -> slot (gather rows), or NULL = identity
   int32_t slots_per_token;  // row = perm[p] / slots_per_token when perm != NULL
   // weights
@@ -70,6 +71,8 @@ hipError_t launch_gemm(const GemmArgs& g, int act /*0 bf16, 1 f16, 2 i8*/, int k
                        hipStream_t st);
 
 // Prefill (128-row tiles, LDS-staged activations); tiles must be built with 128 rows.
+// prefill_fits: the buffers stay within the kernel's 32-bit buffer offsets.
+bool prefill_fits(int64_t a_rows, int64_t K, int act, int64_t w_stride);
 hipError_t launch_gemm_prefill(const GemmArgs& g, int act /*0 bf16, 2 i8*/, int kind, hipStream_t st);
 // Per-(row, group of 128) sums: bf16 -> fp32, or int8 -> int32.
 hipError_t launch_rowsum(const void* a, int is_i8, int64_t rows, int64_t K, void* out, hipStream_t st);
