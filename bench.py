@@ -45,6 +45,7 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-tokens", type=int, default=2, help="tokens in the oracle's timed sample")
     p.add_argument("--no-extra", action="store_true", help="skip the secondary workloads")
+    p.add_argument("--no-graph", action="store_true", help="time eager launches instead of graph replays")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a plain 512 MiB device copy (HBM counter calibration)")
     return p.parse_args()
@@ -78,12 +79,15 @@ class Workload:
         self.ws = torch.empty(max(self.ws_bytes, 1), dtype=torch.uint8, device=dev)
         torch.cuda.synchronize()
 
-    def retoken(self, synth, t):
-        """Same layer and router, a new batch of t tokens with its own buffers."""
+    def retoken(self, synth, t, mode=None):
+        """Same layer and router, a new batch of t tokens with its own buffers (and
+        optionally the other arithmetic mode)."""
         torch = self.torch
         other = Workload.__new__(Workload)
         other.__dict__.update(self.__dict__)
         other.t = t
+        if mode is not None:
+            other.mode = self.lib.Q4_W4A8 if mode == "w4a8" else self.lib.Q4_W4A16
         e, h, k = self.cfg["experts"], self.cfg["hidden"], self.cfg["top_k"]
         other.x = synth.tokens(self.cfg_name, t, device="cuda")
         other.logits = torch.empty((t, e), dtype=torch.float32, device="cuda")
@@ -92,7 +96,7 @@ class Workload:
         other.rws_bytes = int(self.lib._lib.raw.moe_route_workspace_bytes(t, h, e))
         other.rws = torch.empty(max(other.rws_bytes, 1), dtype=torch.uint8, device="cuda")
         other.out = torch.empty((t, h), dtype=torch.bfloat16, device="cuda")
-        other.ws_bytes = self.layer.workspace_bytes(t, self.mode)
+        other.ws_bytes = self.layer.workspace_bytes(t, other.mode)
         other.ws = torch.empty(max(other.ws_bytes, 1), dtype=torch.uint8, device="cuda")
         return other
 
@@ -132,34 +136,52 @@ class Workload:
         return 2.0 * rows * 3 * h * i
 
 
-def time_steps(torch, wl, steps, warmup, stage_events):
+def time_steps(torch, wl, steps, warmup, stage_events, graph=True):
+    """Wall-clock per step over ``steps`` replays of a HIP graph holding one whole step
+    (router + forward; the CPU launch cost of the ~10 kernels is then off the clock),
+    bracketed by device synchronisation.  ``stage_events``: a second, eager pass of the
+    same number of steps with HIP events around each stage (recorded by the library on
+    its stream), for the per-kernel averages."""
     lib = wl.lib
     for _ in range(warmup):
         wl.step()
     torch.cuda.synchronize()
-    evs = []
+    g = None
+    if graph:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            wl.step()
+        for _ in range(max(warmup, 1)):
+            g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        if g is not None:
+            g.replay()
+        else:
+            wl.step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    stage_ms = {}
     if stage_events:
+        evs = []
         for _ in range(steps):
             b = [torch.cuda.Event(enable_timing=True) for _ in lib._lib.STAGES]
             e = [torch.cuda.Event(enable_timing=True) for _ in lib._lib.STAGES]
             for ev in b + e:
                 ev.record()  # creates the underlying HIP event; the library re-records it
             evs.append((b, e))
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s in range(steps):
-        if stage_events:
+        torch.cuda.synchronize()
+        for s in range(steps):
             lib._lib.set_stage_events(*evs[s])
-        wl.step()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    lib._lib.set_stage_events(None, None)
-    stage_ms = {}
-    if stage_events:
+            wl.step()
+        torch.cuda.synchronize()
+        lib._lib.set_stage_events(None, None)
         used = ["permute", "gate_up", "down", "combine"] if wl.mode == lib.Q4_W4A16 else list(lib._lib.STAGES)
         for name in used:
             si = lib._lib.STAGES.index(name)
             stage_ms[name] = sum(b[si].elapsed_time(e[si]) for b, e in evs) / steps
+    del g
     return (t1 - t0) / steps, stage_ms
 
 
@@ -241,7 +263,7 @@ def main():
     log(f"[bench] building moe256 layer (T={args.tokens}, {args.mode})")
     wl = Workload(lib, torch, synth, "moe256", args.tokens, args.mode)
     log(f"[bench] layer weights {wl.layer.weight_bytes() / 1e9:.3f} GB; timing {args.steps} steps")
-    sec, stage_ms = time_steps(torch, wl, args.steps, args.warmup, stage_events=True)
+    sec, stage_ms = time_steps(torch, wl, args.steps, args.warmup, stage_events=True, graph=not args.no_graph)
     main_res = summarize(wl, sec, stage_ms)
     log(f"[bench] main: {json.dumps(main_res)}")
 
@@ -261,19 +283,20 @@ def main():
 
     extra = {}
     if not args.no_extra:
-        for t in (1, 4096):
-            if t == args.tokens:
+        other = "w4a8" if args.mode == "w4a16" else "w4a16"
+        for t, mode in ((1, args.mode), (4096, args.mode), (1, other), (args.tokens, other)):
+            if t == args.tokens and mode == args.mode:
                 continue
-            log(f"[bench] extra moe256 T={t}")
-            wl2 = wl.retoken(synth, t)
+            log(f"[bench] extra moe256 T={t} {mode}")
+            wl2 = wl.retoken(synth, t, mode)
             steps = 10 if t > 1000 else 50
-            s2, st2 = time_steps(torch, wl2, steps, 3, stage_events=True)
-            extra[f"moe256_T{t}_w4a16"] = summarize(wl2, s2, st2)
+            s2, st2 = time_steps(torch, wl2, steps, 3, stage_events=True, graph=not args.no_graph)
+            extra[f"moe256_T{t}_{mode}"] = summarize(wl2, s2, st2)
             del wl2
             torch.cuda.empty_cache()
         log("[bench] extra moe8 W4A8 prefill T=2048")
         w8 = Workload(lib, torch, synth, "moe8_w4a8", 2048, "w4a8")
-        s3, st3 = time_steps(torch, w8, 20, 5, stage_events=True)
+        s3, st3 = time_steps(torch, w8, 20, 5, stage_events=True, graph=not args.no_graph)
         extra["moe8_T2048_w4a8"] = summarize(w8, s3, st3)
         del w8
 

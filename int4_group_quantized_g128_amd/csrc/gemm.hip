@@ -474,14 +474,31 @@ __global__ void __launch_bounds__(256) k_combine(const float* __restrict__ y, co
   const int64_t c = (i - tok * per_tok) * 4;
   const int S = k + shared;
   float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-  for (int j = 0; j < k; ++j) {
-    const int64_t pos = inv[tok * S + j];
-    const float wj = w[tok * k + j];
-    const float4 v = *reinterpret_cast<const float4*>(y + pos * h + c);
-    a0 = fmaf(wj, v.x, a0);
-    a1 = fmaf(wj, v.y, a1);
-    a2 = fmaf(wj, v.z, a2);
-    a3 = fmaf(wj, v.w, a3);
+  // eight slots at a time: all index / weight loads, then all row loads, then the sums
+  // in slot order
+  constexpr int U = 8;
+  for (int j0 = 0; j0 < k; j0 += U) {
+    int64_t pos[U];
+    float wj[U];
+    float4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const bool ok = j0 + u < k;
+      pos[u] = ok ? inv[tok * S + j0 + u] : 0;
+      wj[u] = ok ? w[tok * k + j0 + u] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      v[u] = j0 + u < k ? *reinterpret_cast<const float4*>(y + pos[u] * h + c) : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (j0 + u < k) {
+        a0 = fmaf(wj[u], v[u].x, a0);
+        a1 = fmaf(wj[u], v[u].y, a1);
+        a2 = fmaf(wj[u], v[u].z, a2);
+        a3 = fmaf(wj[u], v[u].w, a3);
+      }
+    }
   }
   if (shared) {
     const int64_t pos = inv[tok * S + k];

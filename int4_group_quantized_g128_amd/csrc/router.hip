@@ -12,7 +12,7 @@ namespace q4 {
 // 16x16x4.  Lane (m = lane % 16, kq = lane / 16) feeds x[t0 + m][k0 + 4 kq + j] and
 // W[e0 + m][k0 + 4 kq + j] to MFMA j of each 16-wide K step; 8 steps of loads are
 // issued before their MFMAs.
-constexpr int kRouteUnroll = 8;
+constexpr int kRouteUnroll = 16;
 
 __global__ void __launch_bounds__(64) k_router_partial(const uint16_t* __restrict__ x, const float* __restrict__ wr,
                                                        int64_t t, int64_t h, int32_t e, int64_t kslice,
@@ -54,78 +54,133 @@ __global__ void __launch_bounds__(64) k_router_partial(const uint16_t* __restric
 
 constexpr int kMaxSlices = 32;
 
+// Unsigned image of a float that orders like the float (non-NaN inputs).
+Q4_DEVICE uint32_t ordered_bits(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+Q4_DEVICE float ordered_to_float(uint32_t o) {
+  return __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
+}
+
+// 64-bit maximum over the wave, in every lane: DPP exchanges inside each 16-lane row
+// (lane ^ 1, lane ^ 2, then the 8- and 16-lane mirrors), then the four row results.
+template <int CTRL>
+Q4_DEVICE uint64_t dpp_u64(uint64_t x) {
+  const uint32_t lo = uint32_t(__builtin_amdgcn_update_dpp(0, int(uint32_t(x)), CTRL, 0xf, 0xf, false));
+  const uint32_t hi = uint32_t(__builtin_amdgcn_update_dpp(0, int(uint32_t(x >> 32)), CTRL, 0xf, 0xf, false));
+  return (uint64_t(hi) << 32) | lo;
+}
+Q4_DEVICE uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+Q4_DEVICE uint64_t wave_max_u64(uint64_t x) {
+  x = max_u64(x, dpp_u64<0xb1>(x));    // quad_perm [1,0,3,2]
+  x = max_u64(x, dpp_u64<0x4e>(x));    // quad_perm [2,3,0,1]
+  x = max_u64(x, dpp_u64<0x141>(x));   // row_half_mirror
+  x = max_u64(x, dpp_u64<0x140>(x));   // row_mirror
+  uint64_t m = 0;
+#pragma unroll
+  for (int row = 0; row < 4; ++row) {
+    const uint32_t lo = __builtin_amdgcn_readlane(uint32_t(x), 16 * row);
+    const uint32_t hi = __builtin_amdgcn_readlane(uint32_t(x >> 32), 16 * row);
+    m = max_u64(m, (uint64_t(hi) << 32) | lo);
+  }
+  return m;
+}
+
 // One wave per token: logits = sum of the K-slice partials in slice order + bias, then
-// k rounds of a wave-wide arg-max with the key (larger logit, then lower index), then
-// the renormalised softmax weights of the selected experts.
+// k rounds of a wave-wide arg-max of the key (larger logit, then lower index), then
+// the renormalised softmax weights of the selected experts.  Lane l holds experts
+// l + 64 i (i < NI, NI = ceil(e / 64)); the round winners go through LDS so that ids
+// and weights are written once, coalesced.
+template <int NI>
 __global__ void __launch_bounds__(64) k_topk(const float* __restrict__ partial, int32_t kslices,
                                              const float* __restrict__ bias, int64_t t, int32_t e,
                                              int32_t k, float* __restrict__ logits, int32_t* __restrict__ ids,
                                              float* __restrict__ weights) {
-  constexpr int kMaxPerLane = 16;  // e <= 1024
+  __shared__ int32_t s_id[64 * NI];
+  __shared__ float s_w[64 * NI];
   const int lane = threadIdx.x;
   const int64_t tok = blockIdx.x;
-  float v[kMaxPerLane];
-  uint32_t taken = 0;
+  float v[NI];
 #pragma unroll
-  for (int i = 0; i < kMaxPerLane; ++i) {
+  for (int i = 0; i < NI; ++i) v[i] = 0.f;
+  // slice sums in slice order (0 + p0 = p0 exactly); addresses clamped into range
+  int ks = 0;
+  if constexpr (NI <= 4) {
+    // every partial load in flight at once (clamped slice index; unused slices add 0)
+    float p[kMaxSlices][NI];
+#pragma unroll
+    for (int u = 0; u < kMaxSlices; ++u)
+#pragma unroll
+      for (int i = 0; i < NI; ++i)
+        p[u][i] = partial[(int64_t(min(u, kslices - 1)) * t + tok) * e + min(lane + 64 * i, e - 1)];
+#pragma unroll
+    for (int u = 0; u < kMaxSlices; ++u)
+#pragma unroll
+      for (int i = 0; i < NI; ++i) v[i] += u < kslices ? p[u][i] : 0.f;
+    ks = kslices;
+  }
+  for (; ks + 4 <= kslices; ks += 4) {
+    float p[4][NI];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int i = 0; i < NI; ++i)
+        p[u][i] = partial[(int64_t(ks + u) * t + tok) * e + min(lane + 64 * i, e - 1)];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int i = 0; i < NI; ++i) v[i] += p[u][i];
+  }
+  for (; ks < kslices; ++ks)
+#pragma unroll
+    for (int i = 0; i < NI; ++i) v[i] += partial[(int64_t(ks) * t + tok) * e + min(lane + 64 * i, e - 1)];
+  // selection key: larger logit first, then lower expert index (0 = taken / absent)
+  uint64_t key[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
     const int ex = lane + 64 * i;
-    float s = -__builtin_inff();
     if (ex < e) {
-      // all slice loads in flight, then summed in slice order
-      float pv[kMaxSlices];
-#pragma unroll
-      for (int ks = 0; ks < kMaxSlices; ++ks) pv[ks] = ks < kslices ? partial[(int64_t(ks) * t + tok) * e + ex] : 0.f;
-      s = pv[0];
-#pragma unroll
-      for (int ks = 1; ks < kMaxSlices; ++ks)
-        if (ks < kslices) s += pv[ks];
-      if (bias) s += bias[ex];
-      logits[tok * e + ex] = s;
-      if (s != s) s = -__builtin_inff();  // NaN never wins; every id stays in range
+      if (bias) v[i] += bias[ex];
+      logits[tok * e + ex] = v[i];
+      if (v[i] != v[i]) v[i] = -__builtin_inff();  // NaN never wins; every id stays in range
+      // -0 keyed as +0: equal logits tie on the index alone
+      key[i] = (uint64_t(ordered_bits(v[i] == 0.f ? 0.f : v[i])) << 32) | uint32_t(~uint32_t(ex));
     } else {
-      taken |= 1u << i;
+      key[i] = 0;
     }
-    v[i] = s;
   }
   float lmax = 0.f, denom = 0.f;
   for (int r = 0; r < k; ++r) {
-    // local best among not-taken entries
-    float bv = -__builtin_inff();
-    int bi = 0x7fffffff;
+    uint64_t best = key[0];
 #pragma unroll
-    for (int i = 0; i < kMaxPerLane; ++i) {
-      const int ex = lane + 64 * i;
-      if (!(taken & (1u << i)) && (v[i] > bv || (v[i] == bv && ex < bi))) {
-        bv = v[i];
-        bi = ex;
-      }
-    }
+    for (int i = 1; i < NI; ++i) best = key[i] > best ? key[i] : best;
+    best = wave_max_u64(best);
+    const int bi = int(~uint32_t(best));
+    const float bv = ordered_to_float(uint32_t(best >> 32));
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-      const float ov = __shfl_xor(bv, o, 64);
-      const int oi = __shfl_xor(bi, o, 64);
-      if (ov > bv || (ov == bv && oi < bi)) {
-        bv = ov;
-        bi = oi;
-      }
-    }
-    if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
+    for (int i = 0; i < NI; ++i)
+      if (bi == lane + 64 * i) key[i] = 0;
+    if (r == 0) lmax = bv;
+    const float ex = expf(bv - lmax);   // the same in every lane
+    denom += ex;
     if (lane == 0) {
-      ids[tok * k + r] = bi;
-      if (r == 0) lmax = bv;
-      const float ex = expf(bv - lmax);
-      denom += ex;
-      weights[tok * k + r] = ex;  // normalised below
+      s_id[r] = bi;
+      s_w[r] = ex;
     }
   }
-  if (lane == 0) {
-    for (int r = 0; r < k; ++r) weights[tok * k + r] = __fdiv_rn(weights[tok * k + r], denom);
+  __syncthreads();
+  for (int r = lane; r < k; r += 64) {
+    ids[tok * k + r] = s_id[r];
+    weights[tok * k + r] = __fdiv_rn(s_w[r], denom);
   }
 }
 
+// K slices: enough waves to cover the chip (about 2048), at least 256 of K per slice
+// (one iteration of the unrolled load loop), at most kMaxSlices partial sums.
 int route_kslices(int64_t t, int64_t h, int32_t e) {
   const int64_t tiles = ((e + 15) / 16) * ((t + 15) / 16);
-  int64_t ks = (1024 + tiles - 1) / tiles;
+  int64_t ks = (2048 + tiles - 1) / tiles;
   ks = std::max<int64_t>(1, std::min<int64_t>(std::min<int64_t>(ks, h / 256), kMaxSlices));
   return int(ks);
 }
@@ -139,7 +194,17 @@ hipError_t launch_route(const uint16_t* x, const float* wr, const float* bias, i
   const int kused = int((h + kslice - 1) / kslice);
   dim3 grid(unsigned((e + 15) / 16), unsigned((t + 15) / 16), unsigned(kused));
   hipLaunchKernelGGL(k_router_partial, grid, dim3(64), 0, st, x, wr, t, h, e, kslice, partial);
-  hipLaunchKernelGGL(k_topk, dim3(unsigned(t)), dim3(64), 0, st, partial, kused, bias, t, e, k, logits, ids, w);
+  const dim3 g = dim3(unsigned(t)), b = dim3(64);
+  if (e <= 64)
+    hipLaunchKernelGGL(k_topk<1>, g, b, 0, st, partial, kused, bias, t, e, k, logits, ids, w);
+  else if (e <= 128)
+    hipLaunchKernelGGL(k_topk<2>, g, b, 0, st, partial, kused, bias, t, e, k, logits, ids, w);
+  else if (e <= 256)
+    hipLaunchKernelGGL(k_topk<4>, g, b, 0, st, partial, kused, bias, t, e, k, logits, ids, w);
+  else if (e <= 512)
+    hipLaunchKernelGGL(k_topk<8>, g, b, 0, st, partial, kused, bias, t, e, k, logits, ids, w);
+  else
+    hipLaunchKernelGGL(k_topk<16>, g, b, 0, st, partial, kused, bias, t, e, k, logits, ids, w);
   return hipGetLastError();
 }
 

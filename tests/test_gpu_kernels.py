@@ -103,6 +103,23 @@ def test_router_parity(lib, name, t):
     assert np.allclose(_np(wts).sum(axis=1), 1.0, atol=2e-6)
 
 
+@pytest.mark.parametrize("t,h,e,k", [(17, 512, 100, 3), (9, 256, 1000, 70), (3, 768, 64, 64), (40, 256, 300, 8)])
+def test_router_parity_shapes(lib, t, h, e, k):
+    """Expert counts across the one-, two-, four-, eight- and sixteen-slot variants of
+    the selection kernel, k up to e and beyond one wave's width."""
+    x = synth.normal(synth.stream_key(70, t, e), (t, h), 1.0).to(torch.bfloat16)
+    w = synth.normal(synth.stream_key(71, h, e), (e, h), 0.05)
+    b = synth.normal(synth.stream_key(72, e), (e,), 0.3)
+    logits, ids, wts = lib.moe_route_topk(x.cuda(), w.cuda(), b.cuda(), k)
+    Lg = _np(logits)
+    L64 = router.logits_fp64(_np(x), _np(w), _np(b))
+    mag = np.abs(_np(x)).astype(np.float64) @ np.abs(_np(w)).astype(np.float64).T
+    assert np.all(np.abs(Lg - L64) <= 2e-6 * mag + 1e-6)
+    ref_ids = router.select_topk(Lg, k)
+    assert np.array_equal(_np(ids), ref_ids)
+    assert np.allclose(_np(wts), router.topk_weights(Lg, ref_ids), rtol=2e-6, atol=1e-7)
+
+
 def test_router_ties_pick_lower_index(lib):
     # x = 0 -> logits equal the bias; equal bias values tie
     e, h, k = 32, 256, 6
