@@ -120,7 +120,8 @@ Q4_API int quantize_int4_g128(const void* w, int w_dtype, int64_t n, int64_t k, 
  *  - weights: one 1024-byte tile per (16-column block cb, group g), cb-major;
  *    lane L in [0, 64) of a tile owns 16 bytes: column L % 16, quarter kq = L / 16;
  *    its 32-bit little-endian word s in [0, 4) holds k = 128 g + 32 s + 8 kq + e,
- *    e in [0, 8), element e at nibble position [0,4,1,5,2,6,3,7][e];
+ *    e in [0, 8), element e at nibble position [0,2,4,6,1,3,5,7][e] (byte j of the
+ *    word: element j in the low nibble, element j + 4 in the high nibble);
  *  - scales: binary16 [n/16][k/128][16] at byte align256(n k / 2);
  *  - zeros (asymmetric): one byte z per (column, group), [n/16][k/128][16], after the
  *    scales at the next 256-byte boundary.

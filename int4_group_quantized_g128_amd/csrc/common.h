@@ -62,24 +62,23 @@ Q4_DEVICE float wave_min(float v) {
 }
 
 // ---------------------------------------------------------------- nibble widening
-// A 32-bit device word holds 8 unsigned nibbles d; nibble position r (bits 4r..4r+3)
-// is element 2r and position r + 4 is element 2r + 1 of the lane's 8 consecutive k.
+// A 32-bit device word holds 8 unsigned nibbles d of the lane's 8 consecutive k:
+// byte j holds element j in its low nibble and element j + 4 in its high nibble.
 // Placing a nibble in the low mantissa bits under a magic exponent byte yields the
 // exact value magic + d: bf16 0x43xx = 128 + d (step 1 up to 256), f16 0x64xx =
 // 1024 + d (step 1 up to 2048).  Output register r holds elements (2r, 2r + 1) =
 // (low, high half).
 template <Act A>
 Q4_DEVICE void widen_word_fp(uint32_t w, uint32_t out[4]) {
-  // lo: nibble positions 0, 2, 4, 6 (one per byte, high halves cleared); hi: 1, 3, 5, 7.
-  // A byte permute then pairs two of them with the magic's high byte (0x43 / 0x64):
-  // positions (0, 4) = elements (0, 1), (1, 5) = (2, 3), (2, 6) = (4, 5), (3, 7) = (6, 7).
+  // lo: elements 0..3 (one per byte, high halves cleared); hi: elements 4..7.  A byte
+  // permute pairs two of them with the magic's high byte (0x43 / 0x64).
   constexpr uint32_t magic_bytes = (A == Act::BF16) ? 0x43434343u : 0x64646464u;
   const uint32_t lo = w & 0x0F0F0F0Fu;
   const uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;
-  out[0] = __builtin_amdgcn_perm(magic_bytes, lo, 0x04020400u);
-  out[1] = __builtin_amdgcn_perm(magic_bytes, hi, 0x04020400u);
-  out[2] = __builtin_amdgcn_perm(magic_bytes, lo, 0x04030401u);
-  out[3] = __builtin_amdgcn_perm(magic_bytes, hi, 0x04030401u);
+  out[0] = __builtin_amdgcn_perm(magic_bytes, lo, 0x04010400u);
+  out[1] = __builtin_amdgcn_perm(magic_bytes, lo, 0x04030402u);
+  out[2] = __builtin_amdgcn_perm(magic_bytes, hi, 0x04010400u);
+  out[3] = __builtin_amdgcn_perm(magic_bytes, hi, 0x04030402u);
 }
 
 // The magic offset of the widened value (value = offset + d).
@@ -88,14 +87,12 @@ constexpr float magic_offset() { return A == Act::BF16 ? 128.0f : 1024.0f; }
 
 // INT8 widening: d - 8 as a two's-complement nibble, placed in the high half of a
 // byte (16 * (d - 8), exact in int8).  Returns two int8x4 registers holding the
-// lane's elements (0..3) and (4..7) in k order.
+// lane's elements (0..3) and (4..7) in k order: the low nibbles shifted up, and the
+// high nibbles in place.
 Q4_DEVICE void widen_word_i8(uint32_t w, uint32_t& lo, uint32_t& hi) {
-  uint32_t t = w ^ 0x88888888u;                 // d -> d - 8 (two's complement nibble)
-  uint32_t ev = (t << 4) & 0xF0F0F0F0u;         // positions 0,2,4,6 = elements 0,4,1,5
-  uint32_t od = t & 0xF0F0F0F0u;                // positions 1,3,5,7 = elements 2,6,3,7
-  // elements 0..3 = ev.b0, ev.b2, od.b0, od.b2 ; elements 4..7 = ev.b1, ev.b3, od.b1, od.b3
-  lo = __builtin_amdgcn_perm(od, ev, 0x06040200u);
-  hi = __builtin_amdgcn_perm(od, ev, 0x07050301u);
+  const uint32_t t = w ^ 0x88888888u;           // d -> d - 8 (two's complement nibble)
+  lo = (t << 4) & 0xF0F0F0F0u;
+  hi = t & 0xF0F0F0F0u;
 }
 
 // ---------------------------------------------------------------- MFMA wrappers

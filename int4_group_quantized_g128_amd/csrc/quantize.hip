@@ -133,7 +133,7 @@ __global__ void k_repack_weights(const uint8_t* __restrict__ packed, int64_t n, 
     for (int e = 0; e < 8; ++e) {
       uint32_t d = (in >> (4 * e)) & 0xF;
       if (!asym) d ^= 0x8;                         // two's complement q -> q + 8
-      const int p = (e & 1) ? 4 + (e >> 1) : (e >> 1);
+      const int p = 2 * (e & 3) + (e >> 2);       // byte e % 4, high nibble for e >= 4
       o |= d << (4 * p);
     }
     out[wi] = o;

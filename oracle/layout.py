@@ -20,7 +20,8 @@ cb-major: byte offset 1024 * (cb * G + g).  Inside a tile, lane L in [0, 64)
 owns bytes [16 L, 16 L + 16): column c = L % 16 of the block and quarter
 kq = L // 16.  Its little-endian 32-bit word s in [0, 4) holds the elements
 k = 128 g + 32 s + 8 kq + e, e in [0, 8), element e at nibble position
-p(e) = [0, 4, 1, 5, 2, 6, 3, 7][e] (bits 4p .. 4p+3).
+p(e) = [0, 2, 4, 6, 1, 3, 5, 7][e] (bits 4p .. 4p+3): byte j of the word holds
+element j in its low nibble and element j + 4 in its high nibble.
 
 Scales.  Binary16 bits, [N/16][G][16] (same column order), starting at byte
 align256(N K / 2).
@@ -38,7 +39,7 @@ import numpy as np
 
 from .quant import GROUP, unpack_canonical
 
-NIBBLE_POS = np.array([0, 4, 1, 5, 2, 6, 3, 7])
+NIBBLE_POS = np.array([0, 2, 4, 6, 1, 3, 5, 7])
 
 
 def _a256(x):

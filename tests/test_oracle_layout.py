@@ -25,7 +25,7 @@ def test_roundtrip(asym, gate_up):
 def test_single_element_placement_by_hand():
     # one non-zero code: row 17 (block 1, column 1), k = 128 + 32*2 + 8*3 + 5
     # -> tile (1, 1) of a 2-group matrix = tile index 3, lane 3*16 + 1 = 49, word 2,
-    #    element 5 at nibble position 6
+    #    element 5 at nibble position 3 (byte 1, high nibble)
     n, k = 32, 256
     q = np.zeros((n, k), dtype=np.int64)
     kk = 128 + 64 + 24 + 5
@@ -34,7 +34,7 @@ def test_single_element_placement_by_hand():
     sb = np.full((n, 2), np.float16(1.0).view(np.uint16), dtype=np.uint16)
     dev = layout.to_device(packed, sb, None, n, k, False, False)
     word = dev[3 * 1024 + 49 * 16 + 2 * 4: 3 * 1024 + 49 * 16 + 3 * 4].view("<u4")[0]
-    assert (int(word) >> 24) & 0xF == 11
+    assert (int(word) >> 12) & 0xF == 11
     # every other nibble of the weights holds 8 (code 0)
     w = dev[: n * k // 2].view("<u4").astype(np.int64)
     nib = np.stack([(w >> (4 * p)) & 0xF for p in range(8)], axis=1)
