@@ -227,6 +227,41 @@ Q4_API int moe_int4_ffn_forward(const q4_moe_layer_t* layer, const uint16_t* x_b
                          hipStream_t stream);
 
 /*
+ * moe_int4_ffn_debug -- moe_int4_ffn_forward (same arguments, same results) that
+ * also returns views of its intermediates, for stage-by-stage parity checks: the
+ * INT8 codes and scales of x and h (page "MoE推理优化实战：4bit存储+INT8计算的W4A8路线解析"
+ * §3, per-token activation quantisation) and the per-position expert outputs before
+ * the weighted combine (page "大模型之Dense、MoE与量化", MoE section).
+ * On success `views` points into `workspace` (valid once the stream has executed the
+ * call, until the workspace is reused); P = t * slots_per_token positions, position
+ * p holds slot perm[p] = token * slots_per_token + j (j == top_k: the shared expert):
+ *   counts [E + shared] int32, offsets [E + shared + 1] int32, perm / inv [P] int32;
+ *   h   [P][I]: silu(gate) * up per position, bf16 (W4A16) or fp32 (W4A8);
+ *   y   [P][H] fp32: the down projection per position;
+ *   q_x [t][H] int8, s_x [t] fp32, q_h [P][I] int8, s_h [P] fp32 (W4A8; NULL in W4A16).
+ * views == NULL -> Q4_ERR_NULL; on any error *views is zeroed.
+ */
+typedef struct q4_ffn_views_t {
+  const int32_t* counts;
+  const int32_t* offsets;
+  const int32_t* perm;
+  const int32_t* inv;
+  const void* h;
+  int32_t h_is_f32;
+  int32_t slots_per_token;
+  int64_t positions;
+  const float* y;
+  const int8_t* q_x;
+  const float* s_x;
+  const int8_t* q_h;
+  const float* s_h;
+} q4_ffn_views_t;
+Q4_API int moe_int4_ffn_debug(const q4_moe_layer_t* layer, const uint16_t* x_bf16, int64_t t,
+                       const int32_t* topk_ids, const float* topk_w, int mode,
+                       uint16_t* out_bf16, void* workspace, size_t ws_bytes,
+                       q4_ffn_views_t* views, hipStream_t stream);
+
+/*
  * int4_linear_forward -- one INT4 g128 linear y = x W_hat^T (fp32 output), the
  * W4A16 core on a plain token matrix.
  *  x      device [t][k], dtype Q4_F16 or Q4_BF16.

@@ -42,6 +42,15 @@ class Q4MoELayer(ctypes.Structure):
     ]
 
 
+class Q4FfnViews(ctypes.Structure):
+    """Mirror of q4_ffn_views_t."""
+    _fields_ = [
+        ("counts", _vp), ("offsets", _vp), ("perm", _vp), ("inv", _vp), ("h", _vp),
+        ("h_is_f32", _i32), ("slots_per_token", _i32), ("positions", _i64),
+        ("y", _vp), ("q_x", _vp), ("s_x", _vp), ("q_h", _vp), ("s_h", _vp),
+    ]
+
+
 def _sig(name, res, args):
     f = getattr(_lib, name)
     f.restype = res
@@ -61,6 +70,8 @@ _sig("moe_permute", _int, [_vp, _i64, _i32, _i32, _vp, _vp, _vp, _vp, _vp])
 _sig("act_quant_int8", _int, [_vp, _int, _i64, _i64, _vp, _vp, _vp])
 _sig("moe_int4_ffn_workspace_bytes", _sz, [ctypes.POINTER(Q4MoELayer), _i64, _int])
 _sig("moe_int4_ffn_forward", _int, [ctypes.POINTER(Q4MoELayer), _vp, _i64, _vp, _vp, _int, _vp, _vp, _sz, _vp])
+_sig("moe_int4_ffn_debug", _int, [ctypes.POINTER(Q4MoELayer), _vp, _i64, _vp, _vp, _int, _vp, _vp, _sz,
+                                  ctypes.POINTER(Q4FfnViews), _vp])
 _sig("int4_linear_forward", _int, [_vp, _int, _i64, _i64, _vp, _i64, _int, _vp, _vp])
 _sig("int4_w4a8_group_acc", _int, [_vp, _i64, _i64, _vp, _i64, _int, _vp, _vp])
 
@@ -279,6 +290,53 @@ def moe_int4_ffn_forward(layer, x, ids, weights, mode=Q4_W4A16, out=None, worksp
         ctypes.byref(layer.desc), _ptr(x), t, _ptr(ids), _ptr(weights), mode, _ptr(out),
         _ptr(workspace), workspace.numel(), _stream()))
     return out
+
+
+def moe_int4_ffn_debug(layer, x, ids, weights, mode=Q4_W4A16):
+    """moe_int4_ffn_forward plus its intermediates: returns (out, views) where views
+    maps counts, offsets, perm, inv, h, y (and q_x, s_x, q_h, s_h in W4A8) to tensors
+    that are views into the call's workspace (shapes as in q4_ffn_views_t)."""
+    _need(x, torch.bfloat16, "x", 2)
+    _need(ids, torch.int32, "ids", 2)
+    _need(weights, torch.float32, "weights", 2)
+    t = x.shape[0]
+    if x.shape[1] != layer.hidden or tuple(ids.shape) != (t, layer.top_k) or tuple(weights.shape) != (t, layer.top_k):
+        raise ValueError("shape mismatch between x, ids, weights and the layer")
+    out = torch.empty_like(x)
+    ws = torch.empty(max(layer.workspace_bytes(t, mode), 1), dtype=torch.uint8, device=x.device)
+    v = Q4FfnViews()
+    _check("moe_int4_ffn_debug", _lib.moe_int4_ffn_debug(
+        ctypes.byref(layer.desc), _ptr(x), t, _ptr(ids), _ptr(weights), mode, _ptr(out),
+        _ptr(ws), ws.numel(), ctypes.byref(v), _stream()))
+    base = ws.data_ptr()
+    P, S, E = int(v.positions), int(v.slots_per_token), layer.num_experts + (1 if layer.shared else 0)
+    H, I = layer.hidden, layer.inter
+
+    def view(ptr, dtype, shape):
+        if not ptr:
+            return None
+        n = 1
+        for d in shape:
+            n *= d
+        off = ptr - base
+        esz = torch.empty((), dtype=dtype).element_size()
+        return ws[off:off + n * esz].view(dtype).view(shape)
+
+    views = {
+        "slots_per_token": S,
+        "counts": view(v.counts, torch.int32, (E,)),
+        "offsets": view(v.offsets, torch.int32, (E + 1,)),
+        "perm": view(v.perm, torch.int32, (P,)),
+        "inv": view(v.inv, torch.int32, (P,)),
+        "h": view(v.h, torch.float32 if v.h_is_f32 else torch.bfloat16, (P, I)),
+        "y": view(v.y, torch.float32, (P, H)),
+        "q_x": view(v.q_x, torch.int8, (t, H)),
+        "s_x": view(v.s_x, torch.float32, (t,)),
+        "q_h": view(v.q_h, torch.int8, (P, I)),
+        "s_h": view(v.s_h, torch.float32, (P,)),
+        "workspace": ws,
+    }
+    return out, views
 
 
 def int4_linear_forward(x, w_dev, n, asymmetric=False):

@@ -278,10 +278,13 @@ size_t moe_int4_ffn_workspace_bytes(const q4_moe_layer_t* layer, int64_t t, int 
   return size_t(carve(layer, t, mode, nullptr).bytes);
 }
 
-int moe_int4_ffn_forward(const q4_moe_layer_t* L, const uint16_t* x_bf16, int64_t t, const int32_t* topk_ids,
-                         const float* topk_w, int mode, uint16_t* out_bf16, void* workspace, size_t ws_bytes,
-                         hipStream_t stream) {
+namespace {
+
+int ffn_forward(const q4_moe_layer_t* L, const uint16_t* x_bf16, int64_t t, const int32_t* topk_ids,
+                const float* topk_w, int mode, uint16_t* out_bf16, void* workspace, size_t ws_bytes,
+                hipStream_t stream, q4_ffn_views_t* views) {
   g_last_error.clear();
+  if (views) *views = q4_ffn_views_t{};
   if (int rc = validate_layer(L)) return rc;
   Q4_REQUIRE(mode == Q4_W4A16 || mode == Q4_W4A8, Q4_ERR_DTYPE, "mode %d", mode);
   Q4_REQUIRE(t >= 0, Q4_ERR_SHAPE, "t < 0");
@@ -295,6 +298,21 @@ int moe_int4_ffn_forward(const q4_moe_layer_t* L, const uint16_t* x_bf16, int64_
              "x, out and workspace must be 16-byte aligned");
   FwdWorkspace w = carve(L, t, mode, workspace);
   Q4_REQUIRE(ws_bytes >= size_t(w.bytes), Q4_ERR_WORKSPACE, "workspace %zu < %lld", ws_bytes, (long long)w.bytes);
+  if (views) {
+    views->counts = w.counts;
+    views->offsets = w.offsets;
+    views->perm = w.perm;
+    views->inv = w.inv;
+    views->h = w.h;
+    views->h_is_f32 = mode == Q4_W4A8 ? 1 : 0;
+    views->slots_per_token = int32_t(S);
+    views->positions = t * S;
+    views->y = w.y;
+    views->q_x = w.qx;
+    views->s_x = w.sx;
+    views->q_h = w.qh;
+    views->s_h = w.sh;
+  }
   const int64_t H = L->hidden, I = L->inter;
   const int rb = w.tile_rows / 16;
   int rc;
@@ -382,6 +400,24 @@ int moe_int4_ffn_forward(const q4_moe_layer_t* L, const uint16_t* x_bf16, int64_
   rc = check_hip(launch_combine(w.y, w.inv, topk_w, t, L->top_k, shared, H, out_bf16, stream), "combine");
   stage_end(Q4_STAGE_COMBINE, stream);
   return rc;
+}
+
+}  // namespace
+
+int moe_int4_ffn_forward(const q4_moe_layer_t* L, const uint16_t* x_bf16, int64_t t, const int32_t* topk_ids,
+                         const float* topk_w, int mode, uint16_t* out_bf16, void* workspace, size_t ws_bytes,
+                         hipStream_t stream) {
+  return ffn_forward(L, x_bf16, t, topk_ids, topk_w, mode, out_bf16, workspace, ws_bytes, stream, nullptr);
+}
+
+int moe_int4_ffn_debug(const q4_moe_layer_t* L, const uint16_t* x_bf16, int64_t t, const int32_t* topk_ids,
+                       const float* topk_w, int mode, uint16_t* out_bf16, void* workspace, size_t ws_bytes,
+                       q4_ffn_views_t* views, hipStream_t stream) {
+  if (!views) {
+    g_last_error = "views is NULL";
+    return Q4_ERR_NULL;
+  }
+  return ffn_forward(L, x_bf16, t, topk_ids, topk_w, mode, out_bf16, workspace, ws_bytes, stream, views);
 }
 
 int int4_linear_forward(const void* x, int x_dtype, int64_t t, int64_t k, const void* w_dev, int64_t n, int asymmetric,
