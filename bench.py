@@ -38,8 +38,8 @@ def log(*a):
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--steps", type=int, default=100)
+    p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--tokens", type=int, default=64)
     p.add_argument("--mode", choices=["w4a16", "w4a8"], default="w4a16")
     p.add_argument("--no-cpu-baseline", action="store_true")
