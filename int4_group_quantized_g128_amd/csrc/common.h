@@ -113,6 +113,19 @@ Q4_DEVICE i32x4_t mfma_i8_16x16x64(const uint32_t a[4], const uint32_t b[4], i32
   return __builtin_amdgcn_mfma_i32_16x16x64_i8(av, bv, c, 0, 0, 0);
 }
 
+template <Act A>
+Q4_DEVICE f32x4_t mfma16x16x32(u32x4_t av, u32x4_t bv, f32x4_t c) {
+  if constexpr (A == Act::BF16) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(bitcast<bf16x8_t>(av), bitcast<bf16x8_t>(bv), c, 0, 0, 0);
+  } else {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(bitcast<f16x8_t>(av), bitcast<f16x8_t>(bv), c, 0, 0, 0);
+  }
+}
+
+Q4_DEVICE i32x4_t mfma_i8_16x16x64(u32x4_t a, u32x4_t b, i32x4_t c) {
+  return __builtin_amdgcn_mfma_i32_16x16x64_i8(bitcast<i32x4_t>(a), bitcast<i32x4_t>(b), c, 0, 0, 0);
+}
+
 Q4_DEVICE f32x4_t mfma_f32_16x16x4(float a, float b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }

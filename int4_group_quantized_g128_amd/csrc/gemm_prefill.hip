@@ -181,6 +181,7 @@ __global__ void __launch_bounds__(256, 1) k_gemm_pf(GemmArgs args) {
   __shared__ __align__(16) uint8_t slot0[St::BYTES];
   __shared__ __align__(16) uint8_t slot1[St::BYTES];
   __shared__ __align__(16) uint8_t slot2[St::BYTES];
+  __shared__ float s_sa[kPfRows];   // int8: per-row activation scales of the item
 
   const int lane = threadIdx.x & 63;
   const int wid = __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6));
@@ -202,6 +203,7 @@ __global__ void __launch_bounds__(256, 1) k_gemm_pf(GemmArgs args) {
   for (int64_t item = ir.first; item < ir.last; item += ir.step) {
     const int64_t tile = item / nblk;
     const int64_t cb0 = (item % nblk) * kPfCB;
+    if constexpr (A == Act::I8) __syncthreads();   // previous item's epilogue is done with s_sa
     const TileDesc d = args.tiles[tile];
     const int64_t row_start = d.row_start;
     const int rows = d.rows;
@@ -272,86 +274,162 @@ __global__ void __launch_bounds__(256, 1) k_gemm_pf(GemmArgs args) {
       const uint8_t* base = slot_of(sl);
       const uint16_t* s_sc = reinterpret_cast<const uint16_t*>(base + St::S_OFF);
       const uint8_t* s_z = base + St::Z_OFF;
+      // Software pipeline over the (row block, column block) tiles of the stage: chunk
+      // (mb, nb) issues the MFMAs of its tile, then the VALU work of the previous tile
+      // (its rescale into the fp32 accumulators) and widens the next column block's
+      // weights, so the matrix core and the VALU work at the same time.  A scheduling
+      // fence closes every chunk (the compiler would otherwise hoist all MFMAs first).
+      // pin(v): v is computed before this point; pass(x): x is (re)defined here, so
+      // users of x cannot move above it.  Empty asm statements, no instructions.
+      auto pin = [](const f32x4_t& v) { asm volatile("" ::"v"(v[0]), "v"(v[1]), "v"(v[2]), "v"(v[3])); };
+      auto pass = [](u32x4_t& x) { asm volatile("" : "+v"(x)); };
+      auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
+      uint4 wraw[4];
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+        wraw[nb] = *reinterpret_cast<const uint4*>(base + St::W_OFF + (wn * 4 + nb) * kTileBytes + lane * 16);
       if constexpr (A == Act::BF16) {
         float sc[4], negz[4];
-        uint32_t b[4][4][4];
+        u32x4_t b[4][4];
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb) {
           const int cbl = wn * 4 + nb;
           sc[nb] = f16_bits_to_f32(s_sc[cbl * 16 + col]);
           negz[nb] = -(magic_offset<A>() + (ASYM ? float(s_z[cbl * 16 + col]) : 8.0f));
-          const uint4 v = *reinterpret_cast<const uint4*>(base + St::W_OFF + cbl * kTileBytes + lane * 16);
-          widen_word_fp<A>(v.x, b[nb][0]);
-          widen_word_fp<A>(v.y, b[nb][1]);
-          widen_word_fp<A>(v.z, b[nb][2]);
-          widen_word_fp<A>(v.w, b[nb][3]);
         }
-        const float* s_rs = reinterpret_cast<const float*>(base + St::R_OFF);
+        auto widen = [&](int nb) {
+          const uint32_t w4[4] = {wraw[nb].x, wraw[nb].y, wraw[nb].z, wraw[nb].w};
 #pragma unroll
-        for (int mb = 0; mb < NMB; ++mb) {
+          for (int s = 0; s < 4; ++s) {
+            uint32_t o[4];
+            widen_word_fp<A>(w4[s], o);
+            b[nb][s] = u32x4_t{o[0], o[1], o[2], o[3]};
+          }
+        };
+        const float* s_rs = reinterpret_cast<const float*>(base + St::R_OFF);
+        auto read_a = [&](int mb, u32x4_t (&af)[4], f32x4_t& xv) {
           const int rb = 2 * mb + wm;
           const int r = rb * 16 + col;
-          uint32_t af[4][4];
 #pragma unroll
           for (int s = 0; s < 4; ++s) {
             const int c = (4 * s + kq) ^ swz(r);
-            const uint4 v = *reinterpret_cast<const uint4*>(base + r * ROWB + c * 16);
-            af[s][0] = v.x; af[s][1] = v.y; af[s][2] = v.z; af[s][3] = v.w;
+            af[s] = *reinterpret_cast<const u32x4_t*>(base + r * ROWB + c * 16);
           }
-          const f32x4_t xv = *reinterpret_cast<const f32x4_t*>(s_rs + rb * 16 + 4 * kq);
+          xv = *reinterpret_cast<const f32x4_t*>(s_rs + rb * 16 + 4 * kq);
+        };
+        if constexpr (NMB > 0) {
+          u32x4_t afc[4], afn[4];
+          f32x4_t xvc, xvn;
+          read_a(0, afc, xvc);
+          widen(0);
+          f32x4_t gt[4], gl;
 #pragma unroll
-          for (int nb = 0; nb < 4; ++nb) {
-            f32x4_t gacc = xv * negz[nb];
+          for (int mb = 0; mb < NMB; ++mb) {
 #pragma unroll
-            for (int s = 0; s < 4; ++s) gacc = mfma16x16x32<A>(af[s], b[nb][s], gacc);
+            for (int nb = 0; nb < 4; ++nb) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) acc[mb][nb][i] = fmaf(sc[nb], gacc[i], acc[mb][nb][i]);
+              for (int s = 0; s < 4; ++s) pass(b[nb][s]);
+              f32x4_t g = xvc * negz[nb];
+#pragma unroll
+              for (int s = 0; s < 4; ++s) g = mfma16x16x32<A>(afc[s], b[nb][s], g);
+              gt[nb] = g;
+              if (mb == 0 && nb < 3) widen(nb + 1);
+              if (nb == 0 && mb + 1 < NMB) read_a(mb + 1, afn, xvn);
+              if (nb > 0) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[mb][nb - 1][i] = fmaf(sc[nb - 1], gt[nb - 1][i], acc[mb][nb - 1][i]);
+                pin(acc[mb][nb - 1]);
+              } else if (mb > 0) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[mb - 1][3][i] = fmaf(sc[3], gl[i], acc[mb - 1][3][i]);
+                pin(acc[mb - 1][3]);
+              }
+              fence();
+            }
+            gl = gt[3];
+#pragma unroll
+            for (int s = 0; s < 4; ++s) afc[s] = afn[s];
+            xvc = xvn;
           }
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[NMB - 1][3][i] = fmaf(sc[3], gl[i], acc[NMB - 1][3][i]);
         }
       } else {
         // widened codes are 16 (d - 8); s / 16 is exact in fp32, so scaling the raw
         // accumulator by s / 16 equals scaling the group sum by s
         float sc16[4];
         int32_t zoff16[4];
-        uint32_t b[4][2][4];
+        u32x4_t b[4][2];
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb) {
           const int cbl = wn * 4 + nb;
           sc16[nb] = f16_bits_to_f32(s_sc[cbl * 16 + col]) * 0.0625f;
           zoff16[nb] = ASYM ? 16 * (int32_t(s_z[cbl * 16 + col]) - 8) : 0;
-          const uint4 v = *reinterpret_cast<const uint4*>(base + St::W_OFF + cbl * kTileBytes + lane * 16);
-          widen_word_i8(v.x, b[nb][0][0], b[nb][0][1]);
-          widen_word_i8(v.y, b[nb][0][2], b[nb][0][3]);
-          widen_word_i8(v.z, b[nb][1][0], b[nb][1][1]);
-          widen_word_i8(v.w, b[nb][1][2], b[nb][1][3]);
         }
+        auto widen = [&](int nb) {
+          uint32_t o[8];
+          widen_word_i8(wraw[nb].x, o[0], o[1]);
+          widen_word_i8(wraw[nb].y, o[2], o[3]);
+          widen_word_i8(wraw[nb].z, o[4], o[5]);
+          widen_word_i8(wraw[nb].w, o[6], o[7]);
+          b[nb][0] = u32x4_t{o[0], o[1], o[2], o[3]};
+          b[nb][1] = u32x4_t{o[4], o[5], o[6], o[7]};
+        };
         const int32_t* s_qs = reinterpret_cast<const int32_t*>(base + St::R_OFF);
-#pragma unroll
-        for (int mb = 0; mb < NMB; ++mb) {
+        auto read_a = [&](int mb, u32x4_t (&af)[2], i32x4_t& qv) {
           const int rb = 2 * mb + wm;
           const int r = rb * 16 + col;
-          uint32_t af[2][4];
 #pragma unroll
           for (int i = 0; i < 2; ++i) {
             const int c1 = (4 * i + (kq >> 1)) ^ swz(r), c2 = (4 * i + 2 + (kq >> 1)) ^ swz(r);
             const uint2 lo = *reinterpret_cast<const uint2*>(base + r * ROWB + c1 * 16 + 8 * (kq & 1));
             const uint2 hi = *reinterpret_cast<const uint2*>(base + r * ROWB + c2 * 16 + 8 * (kq & 1));
-            af[i][0] = lo.x; af[i][1] = lo.y; af[i][2] = hi.x; af[i][3] = hi.y;
+            af[i] = u32x4_t{lo.x, lo.y, hi.x, hi.y};
           }
-          i32x4_t qv = {0, 0, 0, 0};
           if constexpr (ASYM) qv = *reinterpret_cast<const i32x4_t*>(s_qs + rb * 16 + 4 * kq);
+        };
+        auto rescale = [&](int mb, int nb, const i32x4_t& g, const i32x4_t& qv) {
 #pragma unroll
-          for (int nb = 0; nb < 4; ++nb) {
-            i32x4_t gacc = {0, 0, 0, 0};
-            gacc = mfma_i8_16x16x64(af[0], b[nb][0], gacc);
-            gacc = mfma_i8_16x16x64(af[1], b[nb][1], gacc);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              int32_t a32 = gacc[i];
-              if constexpr (ASYM) a32 -= zoff16[nb] * qv[i];
-              acc[mb][nb][i] = fmaf(sc16[nb], float(a32), acc[mb][nb][i]);
-            }
+          for (int i = 0; i < 4; ++i) {
+            int32_t a32 = g[i];
+            if constexpr (ASYM) a32 -= zoff16[nb] * qv[i];
+            acc[mb][nb][i] = fmaf(sc16[nb], float(a32), acc[mb][nb][i]);
           }
+        };
+        if constexpr (NMB > 0) {
+          u32x4_t afc[2], afn[2];
+          i32x4_t qvc = {0, 0, 0, 0}, qvn = {0, 0, 0, 0}, qvl = {0, 0, 0, 0};
+          read_a(0, afc, qvc);
+          widen(0);
+          i32x4_t gt[4], gl;
+#pragma unroll
+          for (int mb = 0; mb < NMB; ++mb) {
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb) {
+              pass(b[nb][0]);
+              pass(b[nb][1]);
+              i32x4_t g = {0, 0, 0, 0};
+              g = mfma_i8_16x16x64(afc[0], b[nb][0], g);
+              g = mfma_i8_16x16x64(afc[1], b[nb][1], g);
+              gt[nb] = g;
+              if (mb == 0 && nb < 3) widen(nb + 1);
+              if (nb == 0 && mb + 1 < NMB) read_a(mb + 1, afn, qvn);
+              if (nb > 0) {
+                rescale(mb, nb - 1, gt[nb - 1], qvc);
+                pin(acc[mb][nb - 1]);
+              } else if (mb > 0) {
+                rescale(mb - 1, 3, gl, qvl);
+                pin(acc[mb - 1][3]);
+              }
+              fence();
+            }
+            gl = gt[3];
+            qvl = qvc;
+            afc[0] = afn[0];
+            afc[1] = afn[1];
+            qvc = qvn;
+          }
+          rescale(NMB - 1, 3, gl, qvl);
         }
       }
     };
@@ -376,6 +454,13 @@ __global__ void __launch_bounds__(256, 1) k_gemm_pf(GemmArgs args) {
     auto kloop = [&](auto nmb_c) {
       issue(0, S0{});
       if (G > 1) issue(1, S1{});
+      if constexpr (A == Act::I8) {
+        // row scales for the epilogue (published by the barrier of the first sync)
+        if (threadIdx.x < kPfRows) {
+          const int r = int(threadIdx.x);
+          s_sa[r] = r < rows ? args.a_scale[src_of(r)] : 0.f;
+        }
+      }
       sync(G > 1);
       for (int g = 0; g < G; g += 3) {
         if (g + 2 < G) issue(g + 2, S2{});
@@ -411,7 +496,7 @@ __global__ void __launch_bounds__(256, 1) k_gemm_pf(GemmArgs args) {
         if (r >= rows) continue;
         const int64_t pos = row_start + r;
         float sa = 1.0f;
-        if constexpr (A == Act::I8) sa = args.a_scale[args.perm ? args.perm[pos] / args.slots_per_token : pos];
+        if constexpr (A == Act::I8) sa = s_sa[r];
         if constexpr (KIND == GEMM_PLAIN) {
 #pragma unroll
           for (int nb = 0; nb < 4; ++nb)
