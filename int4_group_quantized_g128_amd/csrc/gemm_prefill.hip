@@ -18,6 +18,7 @@
 //  - bf16: acc += s * (sum_k x (magic + d) - (magic + z) * sum_k x), the row sums coming
 //    precomputed per (row, group); INT8: acc += s * (acc_i32 / 16 [- (z - 8) sum q]).
 #include <type_traits>
+#include <utility>
 
 #include "common.h"
 #include "internal.h"
@@ -146,7 +147,19 @@ struct PfStage {
   static constexpr int Z_OFF = S_OFF + kPfCB * 32;
   static constexpr int R_OFF = S_OFF + 512;
   static constexpr int BYTES = R_OFF + kPfRows * 4;
+  // LDS ring depth (3 x 41 KB bf16, 3 x 25.6 KB int8)
+  static constexpr int SLOTS = 3;
 };
+
+// f(integral_constant<int, i>) for i = 0 .. N - 1, in order.
+template <typename F, int... I>
+Q4_DEVICE void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+Q4_DEVICE void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 
 // Work items (row tile, 128-column block) in tile-major order.  Workgroups are dispatched
 // round-robin over the 8 XCDs (workgroup x runs on XCD x % 8); with a grid that is a
@@ -176,11 +189,10 @@ __global__ void __launch_bounds__(256, 1) k_gemm_pf(GemmArgs args) {
   // XOR by r % 16 spreads them; int8 rows are 128 B, two rows per period, so rows of
   // equal parity are spread by (r / 2) % 8.
   auto swz = [](int r) -> int { return CHUNKS == 16 ? (r & 15) : ((r >> 1) & 7); };
-  // three distinct LDS objects, so the compiler can tell which in-flight copies a read
-  // depends on (the loop below is unrolled by three to keep each slot compile-time)
-  __shared__ __align__(16) uint8_t slot0[St::BYTES];
-  __shared__ __align__(16) uint8_t slot1[St::BYTES];
-  __shared__ __align__(16) uint8_t slot2[St::BYTES];
+  // ring of NS stage slots (the loop below is unrolled by NS so every slot offset is a
+  // compile-time constant)
+  constexpr int NS = PfStage<A>::SLOTS;
+  __shared__ __align__(16) uint8_t ring[NS * St::BYTES];
   __shared__ float s_sa[kPfRows];   // int8: per-row activation scales of the item
 
   const int lane = threadIdx.x & 63;
@@ -238,11 +250,7 @@ __global__ void __launch_bounds__(256, 1) k_gemm_pf(GemmArgs args) {
     uint32_t r_off = 0;
     if (RSUM && (wid == 1 || wid == 2)) r_off = uint32_t(src_of((wid - 1) * 64 + lane) * G * 4);
 
-    auto slot_of = [&](auto sl) -> uint8_t* {
-      if constexpr (decltype(sl)::value == 0) return slot0;
-      else if constexpr (decltype(sl)::value == 1) return slot1;
-      else return slot2;
-    };
+    auto slot_of = [&](auto sl) -> uint8_t* { return ring + decltype(sl)::value * St::BYTES; };
     auto issue = [&](int g, auto sl) {
       const uint32_t base = lds_addr(slot_of(sl));
 #pragma unroll
@@ -434,26 +442,28 @@ __global__ void __launch_bounds__(256, 1) k_gemm_pf(GemmArgs args) {
       }
     };
 
-    // 3-slot ring: while stage g is computed, stages g + 1 and g + 2 are in flight.  The
-    // copies of stage g + 2 go to the slot that stage g - 1 used, which every wave has
-    // finished reading (barrier at the end of the previous step).  Each wave issues at
-    // least A_INSTS + 2 copies per stage, so waiting until that many are outstanding
-    // leaves only the newest stage in flight; the barrier then publishes every wave's
-    // completed copies.  (The raw barrier carries no wait of its own; the empty asm
-    // statements keep the compiler from moving memory accesses across it.)
-    auto sync = [&](bool newest_in_flight) {
-      if (newest_in_flight) wait_vmcnt<A_INSTS + 2>();
+    // NS-slot ring: while stage g is computed, stages g + 1 .. g + NS - 1 are in flight.
+    // The copies of stage g + NS - 1 go to the slot that stage g - 1 used, which every
+    // wave has finished reading (barrier at the end of the previous step).  Each wave
+    // issues at least PER = A_INSTS + 2 copies per stage and copies complete in order,
+    // so after step g waiting until n * PER are outstanding (n = stages issued after
+    // stage g + 1) leaves stage g + 1 complete; the barrier then publishes every wave's
+    // copies.  (The raw barrier carries no wait of its own; the empty asm statements
+    // keep the compiler from moving memory accesses across it.)
+    constexpr int PER = A_INSTS + 2;
+    auto sync = [&](int newer) {
+      static_assert((NS - 2) * PER < 64, "vmcnt range");
+      if (newer >= 2 && NS > 3) wait_vmcnt<(NS > 3 ? 2 * PER : 0)>();
+      else if (newer >= 1) wait_vmcnt<PER>();
       else wait_vmcnt<0>();
       asm volatile("" ::: "memory");
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
     };
-    using S0 = std::integral_constant<int, 0>;
-    using S1 = std::integral_constant<int, 1>;
-    using S2 = std::integral_constant<int, 2>;
     auto kloop = [&](auto nmb_c) {
-      issue(0, S0{});
-      if (G > 1) issue(1, S1{});
+      static_for<NS - 1>([&](auto u) {
+        if (decltype(u)::value < G) issue(decltype(u)::value, u);
+      });
       if constexpr (A == Act::I8) {
         // row scales for the epilogue (published by the barrier of the first sync)
         if (threadIdx.x < kPfRows) {
@@ -461,19 +471,20 @@ __global__ void __launch_bounds__(256, 1) k_gemm_pf(GemmArgs args) {
           s_sa[r] = r < rows ? args.a_scale[src_of(r)] : 0.f;
         }
       }
-      sync(G > 1);
-      for (int g = 0; g < G; g += 3) {
-        if (g + 2 < G) issue(g + 2, S2{});
-        compute(S0{}, nmb_c);
-        sync(g + 2 < G);
-        if (g + 1 >= G) break;
-        if (g + 3 < G) issue(g + 3, S0{});
-        compute(S1{}, nmb_c);
-        sync(g + 3 < G);
-        if (g + 2 >= G) break;
-        if (g + 4 < G) issue(g + 4, S1{});
-        compute(S2{}, nmb_c);
-        sync(g + 4 < G);
+      sync(std::min(NS - 2, G - 1));
+      for (int g0 = 0; g0 < G; g0 += NS) {
+        bool done = false;
+        static_for<NS>([&](auto u) {
+          constexpr int U = decltype(u)::value;
+          const int g = g0 + U;
+          if (done || g >= G) {
+            done = true;
+            return;
+          }
+          if (g + NS - 1 < G) issue(g + NS - 1, std::integral_constant<int, (U + NS - 1) % NS>{});
+          compute(u, nmb_c);
+          sync(std::max(0, std::min(NS - 2, G - 2 - g)));
+        });
       }
     };
     // row blocks 2 mb + wm (mb < nmb) hold valid rows; nmb is uniform within the wave
