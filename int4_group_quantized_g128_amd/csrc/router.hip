@@ -8,48 +8,84 @@
 
 namespace q4 {
 
-// Partial logits over one K slice: a 16-token x 16-expert tile per wave, fp32 MFMA
-// 16x16x4.  Lane (m = lane % 16, kq = lane / 16) feeds x[t0 + m][k0 + 4 kq + j] and
-// W[e0 + m][k0 + 4 kq + j] to MFMA j of each 16-wide K step; 8 steps of loads are
-// issued before their MFMAs.
-constexpr int kRouteUnroll = 16;
-
+// Partial logits over one K slice: a (16 TB)-token x (16 EB)-expert tile per wave,
+// fp32 MFMA 16x16x4.  Lane (m = lane % 16, kq = lane / 16) feeds x[t0 + 16 i + m][k]
+// and W[e0 + 16 j + m][k] for k = k0 + 4 kq + s to MFMA s of each 16-wide K step; U
+// steps of loads are issued before their MFMAs.  Small batches use 16 x 16 tiles and
+// many K slices; large batches use 32 x 64 or 64 x 64 tiles (each loaded x value
+// feeds four expert blocks, each W value two or four token blocks).
+template <int TB, int EB, int U>
 __global__ void __launch_bounds__(64) k_router_partial(const uint16_t* __restrict__ x, const float* __restrict__ wr,
                                                        int64_t t, int64_t h, int32_t e, int64_t kslice,
                                                        float* __restrict__ partial) {
   const int lane = threadIdx.x;
   const int m = lane & 15, kq = lane >> 4;
-  const int64_t e0 = int64_t(blockIdx.x) * 16, t0 = int64_t(blockIdx.y) * 16;
+  const int64_t e0 = int64_t(blockIdx.x) * 16 * EB, t0 = int64_t(blockIdx.y) * 16 * TB;
   const int64_t ks = blockIdx.z;
   const int64_t kb = ks * kslice, ke = std::min<int64_t>(h, kb + kslice);
-  const bool tv = t0 + m < t, ev = e0 + m < e;
-  const uint16_t* xr = x + (tv ? t0 + m : 0) * h;
-  const float* wrow = wr + (ev ? e0 + m : 0) * h;
-  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-  for (int64_t k0 = kb; k0 < ke; k0 += 16 * kRouteUnroll) {
-    uint2 xv[kRouteUnroll];
-    float4 wv[kRouteUnroll];
+  const uint16_t* xr[TB];
+  const float* wrow[EB];
+  bool tv[TB], ev[EB];
 #pragma unroll
-    for (int u = 0; u < kRouteUnroll; ++u) {
+  for (int i = 0; i < TB; ++i) {
+    tv[i] = t0 + 16 * i + m < t;
+    xr[i] = x + (tv[i] ? t0 + 16 * i + m : 0) * h;
+  }
+#pragma unroll
+  for (int j = 0; j < EB; ++j) {
+    ev[j] = e0 + 16 * j + m < e;
+    wrow[j] = wr + (ev[j] ? e0 + 16 * j + m : 0) * h;
+  }
+  f32x4_t acc[TB][EB];
+#pragma unroll
+  for (int i = 0; i < TB; ++i)
+#pragma unroll
+    for (int j = 0; j < EB; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int64_t k0 = kb; k0 < ke; k0 += 16 * U) {
+    uint2 xv[U][TB];
+    float4 wv[U][EB];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
       const int64_t k = k0 + 16 * u + 4 * kq;
       const bool kv = k0 + 16 * u < ke;
-      xv[u] = (tv && kv) ? load8(xr + k) : make_uint2(0, 0);
-      wv[u] = (ev && kv) ? *reinterpret_cast<const float4*>(wrow + k) : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int i = 0; i < TB; ++i) xv[u][i] = (tv[i] && kv) ? load8(xr[i] + k) : make_uint2(0, 0);
+#pragma unroll
+      for (int j = 0; j < EB; ++j)
+        wv[u][j] = (ev[j] && kv) ? *reinterpret_cast<const float4*>(wrow[j] + k) : make_float4(0.f, 0.f, 0.f, 0.f);
     }
 #pragma unroll
-    for (int u = 0; u < kRouteUnroll; ++u) {
-      acc = mfma_f32_16x16x4(bf16_to_f32(uint16_t(xv[u].x & 0xffff)), wv[u].x, acc);
-      acc = mfma_f32_16x16x4(bf16_to_f32(uint16_t(xv[u].x >> 16)), wv[u].y, acc);
-      acc = mfma_f32_16x16x4(bf16_to_f32(uint16_t(xv[u].y & 0xffff)), wv[u].z, acc);
-      acc = mfma_f32_16x16x4(bf16_to_f32(uint16_t(xv[u].y >> 16)), wv[u].w, acc);
+    for (int u = 0; u < U; ++u) {
+      float xa[TB][4];
+#pragma unroll
+      for (int i = 0; i < TB; ++i) {
+        xa[i][0] = bf16_to_f32(uint16_t(xv[u][i].x & 0xffff));
+        xa[i][1] = bf16_to_f32(uint16_t(xv[u][i].x >> 16));
+        xa[i][2] = bf16_to_f32(uint16_t(xv[u][i].y & 0xffff));
+        xa[i][3] = bf16_to_f32(uint16_t(xv[u][i].y >> 16));
+      }
+      // consecutive MFMAs go to different accumulators (no back-to-back dependency)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int i = 0; i < TB; ++i)
+#pragma unroll
+          for (int j = 0; j < EB; ++j) {
+            const float wq = q == 0 ? wv[u][j].x : q == 1 ? wv[u][j].y : q == 2 ? wv[u][j].z : wv[u][j].w;
+            acc[i][j] = mfma_f32_16x16x4(xa[i][q], wq, acc[i][j]);
+          }
     }
   }
-  // C layout: lane holds tokens t0 + 4 kq + i, expert e0 + m
+  // C layout: lane holds tokens t0 + 16 i + 4 kq + r, expert e0 + 16 j + m
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int64_t tt = t0 + 4 * kq + i;
-    if (tt < t && ev) partial[(ks * t + tt) * e + e0 + m] = acc[i];
-  }
+  for (int i = 0; i < TB; ++i)
+#pragma unroll
+    for (int j = 0; j < EB; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t tt = t0 + 16 * i + 4 * kq + r;
+        if (tt < t && ev[j]) partial[(ks * t + tt) * e + e0 + 16 * j + m] = acc[i][j][r];
+      }
 }
 
 constexpr int kMaxSlices = 32;
@@ -176,10 +212,17 @@ __global__ void __launch_bounds__(64) k_topk(const float* __restrict__ partial, 
   }
 }
 
-// K slices: enough waves to cover the chip (about 2048), at least 256 of K per slice
-// (one iteration of the unrolled load loop), at most kMaxSlices partial sums.
+// Wave tile of the partial-logit kernel: 16 x 16 for small batches, 32 tokens x 64
+// experts once there are enough tiles to fill the chip without splitting K much.
+static bool route_big_tiles(int64_t t, int32_t e) { return t >= 512 && e >= 64; }
+static bool route_huge_tiles(int64_t t, int32_t e) { return t >= 2048 && e >= 64; }
+
+// K slices: enough waves to cover the chip (about 2048), at least 256 of K per slice,
+// at most kMaxSlices partial sums.
 int route_kslices(int64_t t, int64_t h, int32_t e) {
-  const int64_t tiles = ((e + 15) / 16) * ((t + 15) / 16);
+  const int64_t tiles = route_huge_tiles(t, e) ? ((e + 63) / 64) * ((t + 63) / 64)
+                       : route_big_tiles(t, e) ? ((e + 63) / 64) * ((t + 31) / 32)
+                                               : ((e + 15) / 16) * ((t + 15) / 16);
   int64_t ks = (2048 + tiles - 1) / tiles;
   ks = std::max<int64_t>(1, std::min<int64_t>(std::min<int64_t>(ks, h / 256), kMaxSlices));
   return int(ks);
@@ -192,8 +235,16 @@ hipError_t launch_route(const uint16_t* x, const float* wr, const float* bias, i
   int64_t kslice = (h + ks - 1) / ks;
   kslice = (kslice + 15) / 16 * 16;
   const int kused = int((h + kslice - 1) / kslice);
-  dim3 grid(unsigned((e + 15) / 16), unsigned((t + 15) / 16), unsigned(kused));
-  hipLaunchKernelGGL(k_router_partial, grid, dim3(64), 0, st, x, wr, t, h, e, kslice, partial);
+  if (route_huge_tiles(t, e)) {
+    dim3 grid(unsigned((e + 63) / 64), unsigned((t + 63) / 64), unsigned(kused));
+    hipLaunchKernelGGL((k_router_partial<4, 4, 2>), grid, dim3(64), 0, st, x, wr, t, h, e, kslice, partial);
+  } else if (route_big_tiles(t, e)) {
+    dim3 grid(unsigned((e + 63) / 64), unsigned((t + 31) / 32), unsigned(kused));
+    hipLaunchKernelGGL((k_router_partial<2, 4, 4>), grid, dim3(64), 0, st, x, wr, t, h, e, kslice, partial);
+  } else {
+    dim3 grid(unsigned((e + 15) / 16), unsigned((t + 15) / 16), unsigned(kused));
+    hipLaunchKernelGGL((k_router_partial<1, 1, 16>), grid, dim3(64), 0, st, x, wr, t, h, e, kslice, partial);
+  }
   const dim3 g = dim3(unsigned(t)), b = dim3(64);
   if (e <= 64)
     hipLaunchKernelGGL(k_topk<1>, g, b, 0, st, partial, kused, bias, t, e, k, logits, ids, w);

@@ -103,10 +103,13 @@ def test_router_parity(lib, name, t):
     assert np.allclose(_np(wts).sum(axis=1), 1.0, atol=2e-6)
 
 
-@pytest.mark.parametrize("t,h,e,k", [(17, 512, 100, 3), (9, 256, 1000, 70), (3, 768, 64, 64), (40, 256, 300, 8)])
+@pytest.mark.parametrize("t,h,e,k", [(17, 512, 100, 3), (9, 256, 1000, 70), (3, 768, 64, 64), (40, 256, 300, 8),
+                                     (600, 512, 256, 8), (517, 256, 100, 5), (2100, 256, 130, 4)])
 def test_router_parity_shapes(lib, t, h, e, k):
     """Expert counts across the one-, two-, four-, eight- and sixteen-slot variants of
-    the selection kernel, k up to e and beyond one wave's width."""
+    the selection kernel, k up to e and beyond one wave's width; batches of 512 and 2048
+    tokens and more take the 32 x 64- and 64 x 64-tile logit kernels (ragged in tokens
+    and experts here)."""
     x = synth.normal(synth.stream_key(70, t, e), (t, h), 1.0).to(torch.bfloat16)
     w = synth.normal(synth.stream_key(71, h, e), (e, h), 0.05)
     b = synth.normal(synth.stream_key(72, e), (e,), 0.3)
