@@ -37,6 +37,7 @@ Modules:
 * ``permute`` -- group-by-expert permutation (counts, offsets, perm, inv).
 * ``ffn``     -- fp64 W4A16 and W4A8 FFN / MoE forward, per-token INT8
   activation quantisation, the INT32 group accumulators.
+* ``lora``    -- LoRA-mode experts: low-rank adapters on the frozen INT4 dense FFN.
 
 Parity status of each function is listed in its docstring ("pinned by" /
 "parity unpinned").

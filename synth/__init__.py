@@ -114,10 +114,17 @@ CONFIGS = {
     "moe256": dict(seed=505, hidden=7168, inter=2048, experts=256, top_k=8, shared=True,
                    sigma=0.02, router_sigma=0.02, asymmetric=False, zipf_s=1.1,
                    tokens=(1, 64, 4096)),
+    # LoRA mode: 8 experts = low-rank adapters (rank 16) on the frozen dense 2048/8192
+    # FFN that the 8-expert slice-mode layers are cut from; adapter delta ~ 20 % of the
+    # base output.
+    "lora8": dict(seed=606, hidden=2048, inter=8192, experts=8, top_k=2, rank=16,
+                  sigma=0.02, lora_sigma_a=0.02, lora_sigma_b=0.05, router_sigma=0.02,
+                  asymmetric=False, tokens=(1, 64, 2048)),
 }
 
 # Tensor tags of the stream keys.
 TAG_X, TAG_W, TAG_ROUTER, TAG_GATE, TAG_UP, TAG_DOWN = 1, 2, 3, 4, 5, 6
+TAG_LORA_A, TAG_LORA_B = 7, 8
 
 # Zipf shaping of the 256-expert router: bias b_e = -zipf_s * KAPPA * ln(rank_e).
 # KAPPA is fitted by oracle/fit_zipf_kappa.py (see that script) so that the
@@ -204,6 +211,39 @@ def expert_weights(cfg_name, e, device="cpu"):
     up = normal(stream_key(seed, TAG_UP, e), (i, h), cfg["sigma"], device)
     down = normal(stream_key(seed, TAG_DOWN, e), (h, i), cfg["sigma"], device)
     return gate, up, down
+
+
+def lora_base(cfg_name, device="cpu"):
+    """The frozen dense FFN of a LoRA-mode layer: (gate [I, H], up [I, H], down [H, I])
+    float32 -- the same dense weights the 8-expert slice-mode layers are cut from."""
+    cfg = CONFIGS[cfg_name]
+    seed = CONFIGS["moe8"]["seed"]
+    h, i = cfg["hidden"], cfg["inter"]
+    gate = normal(stream_key(seed, TAG_GATE), (i, h), cfg["sigma"], device)
+    up = normal(stream_key(seed, TAG_UP), (i, h), cfg["sigma"], device)
+    down = normal(stream_key(seed, TAG_DOWN), (h, i), cfg["sigma"], device)
+    return gate, up, down
+
+
+LORA_MATS = (("gate", "hidden", "inter"), ("up", "hidden", "inter"), ("down", "inter", "hidden"))
+
+
+def lora_adapters(cfg_name, e, device="cpu", rank=None, dims=None):
+    """Adapters of expert e: {"A_gate": [r, H], "B_gate": [I, r], "A_up": [r, H],
+    "B_up": [I, r], "A_down": [r, I], "B_down": [H, r]} as bfloat16 tensors
+    (~N(0, sigma_a) and ~N(0, sigma_b) before the bf16 rounding).  ``dims`` =
+    (hidden, inter) overrides the config's sizes (small test layers)."""
+    cfg = CONFIGS[cfg_name]
+    r = cfg["rank"] if rank is None else rank
+    h, i = (cfg["hidden"], cfg["inter"]) if dims is None else dims
+    size = {"hidden": h, "inter": i}
+    out = {}
+    for m, (name, din, dout) in enumerate(LORA_MATS):
+        a = normal(stream_key(cfg["seed"], TAG_LORA_A, m, e, r), (r, size[din]), cfg["lora_sigma_a"], device)
+        b = normal(stream_key(cfg["seed"], TAG_LORA_B, m, e, r), (size[dout], r), cfg["lora_sigma_b"], device)
+        out["A_" + name] = a.to(torch.bfloat16)
+        out["B_" + name] = b.to(torch.bfloat16)
+    return out
 
 
 def router_weights(cfg_name, device="cpu", kappa=None):
