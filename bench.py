@@ -136,6 +136,55 @@ class Workload:
         return 2.0 * rows * 3 * h * i
 
 
+class LoraWorkload:
+    """LoRA-mode layer (frozen INT4 dense FFN + rank-r adapters per expert) + router +
+    tokens + preallocated buffers; a step is router -> moe_lora_ffn_forward."""
+
+    def __init__(self, lib, torch, synth, cfg_name, t):
+        self.lib, self.torch = lib, torch
+        cfg = synth.CONFIGS[cfg_name]
+        self.cfg_name, self.cfg, self.t = cfg_name, cfg, t
+        self.mode = None
+        e, h, i, k, r = cfg["experts"], cfg["hidden"], cfg["inter"], cfg["top_k"], cfg["rank"]
+        self.layer = lib.LoRALayer(e, h, i, k, r)
+        self.layer.set_base(*(m.cuda() for m in synth.lora_base(cfg_name)))
+        for j in range(e):
+            self.layer.set_adapters(j, {n: v.cuda() for n, v in synth.lora_adapters(cfg_name, j).items()})
+        self.wr, _ = synth.router_weights(cfg_name, device="cuda")
+        self.x = synth.tokens(cfg_name, t, device="cuda")
+        self.logits = torch.empty((t, e), dtype=torch.float32, device="cuda")
+        self.ids = torch.empty((t, k), dtype=torch.int32, device="cuda")
+        self.w = torch.empty((t, k), dtype=torch.float32, device="cuda")
+        self.rws_bytes = int(lib._lib.raw.moe_route_workspace_bytes(t, h, e))
+        self.rws = torch.empty(max(self.rws_bytes, 1), dtype=torch.uint8, device="cuda")
+        self.out = torch.empty((t, h), dtype=torch.bfloat16, device="cuda")
+        self.ws_bytes = self.layer.workspace_bytes(t)
+        self.ws = torch.empty(max(self.ws_bytes, 1), dtype=torch.uint8, device="cuda")
+        torch.cuda.synchronize()
+
+    def step(self):
+        L = self.lib._lib
+        raw, P, st = L.raw, L._ptr, L._stream()
+        e, h, k = self.cfg["experts"], self.cfg["hidden"], self.cfg["top_k"]
+        rc = raw.moe_route_topk(P(self.x), P(self.wr), None, self.t, h, e, k, P(self.logits), P(self.ids),
+                                P(self.w), P(self.rws), self.rws_bytes, st)
+        if rc:
+            raise L.Q4Error("moe_route_topk", rc)
+        rc = raw.moe_lora_ffn_forward(L.ctypes.byref(self.layer.desc), P(self.x), self.t, P(self.ids), P(self.w),
+                                      P(self.out), P(self.ws), self.ws_bytes, st)
+        if rc:
+            raise L.Q4Error("moe_lora_ffn_forward", rc)
+
+    def summary(self, sec):
+        h, i, r, k = self.cfg["hidden"], self.cfg["inter"], self.cfg["rank"], self.cfg["top_k"]
+        flops = 2.0 * self.t * 3 * h * i + 2.0 * self.t * k * 3 * r * (h + i)
+        return {"tokens": self.t, "tokens_per_s": self.t / sec, "ms_per_step": sec * 1e3,
+                "weight_bytes": self.layer.weight_bytes(),
+                "effective_weight_GBps": self.layer.weight_bytes() / sec / 1e9,
+                "hbm_frac": self.layer.weight_bytes() / sec / 1e9 / HBM_PEAK_GBS,
+                "mfma_frac": flops / sec / 1e12 / BF16_PEAK_TFLOPS}
+
+
 def time_steps(torch, wl, steps, warmup, stage_events, graph=True):
     """Wall-clock per step over ``steps`` replays of a HIP graph holding one whole step
     (router + forward; the CPU launch cost of the ~10 kernels is then off the clock),
@@ -294,6 +343,12 @@ def main():
             extra[f"moe256_T{t}_{mode}"] = summarize(wl2, s2, st2)
             del wl2
             torch.cuda.empty_cache()
+        for t in (1, 64, 2048):
+            log(f"[bench] extra lora8 T={t}")
+            lw = LoraWorkload(lib, torch, synth, "lora8", t)
+            s4, _ = time_steps(torch, lw, 20 if t > 1000 else 50, 5, stage_events=False, graph=not args.no_graph)
+            extra[f"lora8_T{t}_w4a16"] = lw.summary(s4)
+            del lw
         log("[bench] extra moe8 W4A8 prefill T=2048")
         w8 = Workload(lib, torch, synth, "moe8_w4a8", 2048, "w4a8")
         s3, st3 = time_steps(torch, w8, 20, 5, stage_events=True, graph=not args.no_graph)

@@ -262,6 +262,48 @@ Q4_API int moe_int4_ffn_debug(const q4_moe_layer_t* layer, const uint16_t* x_bf1
                        q4_ffn_views_t* views, hipStream_t stream);
 
 /*
+ * q4_lora_layer_t / moe_lora_ffn_forward -- LoRA-mode experts (page
+ * "高效大语言模型推理实践：INT4量化与MoE架构的融合探索", 第三阶段: experts built from LoRA
+ * adapters on frozen dense weights).  Expert e of matrix m in {gate, up, down} is
+ * W_hat_m + B_m,e A_m,e with W_hat_m one shared INT4 g128 dense matrix and rank-r
+ * bf16 adapters (any LoRA scaling folded into B);
+ *   out[t] = sum_j topk_w[t, j] * FFN_{ids[t, j]}(x[t]),
+ *   FFN_e(v) = W_down,e (silu(W_gate,e v) * (W_up,e v)).
+ * Computed as: INT4 base gate/up GEMM once per token (fp32); per slot the rank-r
+ * updates B (A x) and SwiGLU (fp32); hw = sum_j w_j h_j rounded to bf16; INT4 base
+ * down GEMM once per token on hw (fp32); plus sum_j w_j B_down (A_down h_j); the
+ * output rounded to bf16.  W4A16 arithmetic (bf16 activations into the base GEMMs).
+ *
+ *  base_gate_up  device layout (Q4_REPACK_PLAIN) of [gate; up], 2I x H.
+ *  base_down     device layout (Q4_REPACK_PLAIN), H x I.
+ *  a_gate_up     bf16 [E][2r][H]: rows [0, r) A_gate,e, rows [r, 2r) A_up,e.
+ *  b_gate, b_up  bf16 [E][I][r].    a_down  bf16 [E][r][I].    b_down  bf16 [E][H][r].
+ *  Requires H % 128 == 0, I % 128 == 0, rank in {8, 16, ..., 64},
+ *  1 <= top_k <= num_experts <= 4096; all pointers 16-byte aligned.
+ *  x_bf16 [t][H], topk_ids / topk_w [t][top_k], out_bf16 [t][H] (may not alias x);
+ *  workspace of moe_lora_ffn_workspace_bytes(layer, t) bytes.  t == 0 is a no-op.
+ */
+typedef struct q4_lora_layer_t {
+  int32_t num_experts;
+  int32_t hidden;
+  int32_t inter;
+  int32_t top_k;
+  int32_t rank;
+  int32_t asymmetric;
+  const void* base_gate_up;
+  const void* base_down;
+  const uint16_t* a_gate_up;
+  const uint16_t* b_gate;
+  const uint16_t* b_up;
+  const uint16_t* a_down;
+  const uint16_t* b_down;
+} q4_lora_layer_t;
+Q4_API size_t moe_lora_ffn_workspace_bytes(const q4_lora_layer_t* layer, int64_t t);
+Q4_API int moe_lora_ffn_forward(const q4_lora_layer_t* layer, const uint16_t* x_bf16, int64_t t,
+                         const int32_t* topk_ids, const float* topk_w, uint16_t* out_bf16,
+                         void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/*
  * int4_linear_forward -- one INT4 g128 linear y = x W_hat^T (fp32 output), the
  * W4A16 core on a plain token matrix.
  *  x      device [t][k], dtype Q4_F16 or Q4_BF16.

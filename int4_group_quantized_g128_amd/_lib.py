@@ -42,6 +42,16 @@ class Q4MoELayer(ctypes.Structure):
     ]
 
 
+class Q4LoraLayer(ctypes.Structure):
+    """Mirror of q4_lora_layer_t."""
+    _fields_ = [
+        ("num_experts", _i32), ("hidden", _i32), ("inter", _i32), ("top_k", _i32),
+        ("rank", _i32), ("asymmetric", _i32),
+        ("base_gate_up", _vp), ("base_down", _vp), ("a_gate_up", _vp), ("b_gate", _vp),
+        ("b_up", _vp), ("a_down", _vp), ("b_down", _vp),
+    ]
+
+
 class Q4FfnViews(ctypes.Structure):
     """Mirror of q4_ffn_views_t."""
     _fields_ = [
@@ -72,6 +82,8 @@ _sig("moe_int4_ffn_workspace_bytes", _sz, [ctypes.POINTER(Q4MoELayer), _i64, _in
 _sig("moe_int4_ffn_forward", _int, [ctypes.POINTER(Q4MoELayer), _vp, _i64, _vp, _vp, _int, _vp, _vp, _sz, _vp])
 _sig("moe_int4_ffn_debug", _int, [ctypes.POINTER(Q4MoELayer), _vp, _i64, _vp, _vp, _int, _vp, _vp, _sz,
                                   ctypes.POINTER(Q4FfnViews), _vp])
+_sig("moe_lora_ffn_workspace_bytes", _sz, [ctypes.POINTER(Q4LoraLayer), _i64])
+_sig("moe_lora_ffn_forward", _int, [ctypes.POINTER(Q4LoraLayer), _vp, _i64, _vp, _vp, _vp, _vp, _sz, _vp])
 _sig("int4_linear_forward", _int, [_vp, _int, _i64, _i64, _vp, _i64, _int, _vp, _vp])
 _sig("int4_w4a8_group_acc", _int, [_vp, _i64, _i64, _vp, _i64, _int, _vp, _vp])
 
@@ -337,6 +349,76 @@ def moe_int4_ffn_debug(layer, x, ids, weights, mode=Q4_W4A16):
         "workspace": ws,
     }
     return out, views
+
+
+class LoRALayer:
+    """LoRA-mode MoE layer: one frozen INT4 g128 dense SwiGLU FFN (device layout) and
+    rank-r bf16 adapters per expert, stacked as q4_lora_layer_t describes."""
+
+    def __init__(self, num_experts, hidden, inter, top_k, rank, asymmetric=False, device="cuda"):
+        self.num_experts, self.hidden, self.inter, self.top_k, self.rank = num_experts, hidden, inter, top_k, rank
+        self.asymmetric = bool(asymmetric)
+        E, H, I, r = num_experts, hidden, inter, rank
+        self.gu_bytes = q4_device_bytes(2 * I, H, asymmetric)
+        self.dn_bytes = q4_device_bytes(H, I, asymmetric)
+        if self.gu_bytes == 0 or self.dn_bytes == 0:
+            raise ValueError("hidden and inter must be multiples of 128")
+        self.base_gate_up = torch.empty(self.gu_bytes, dtype=torch.uint8, device=device)
+        self.base_down = torch.empty(self.dn_bytes, dtype=torch.uint8, device=device)
+        bf = dict(dtype=torch.bfloat16, device=device)
+        self.a_gate_up = torch.zeros((E, 2 * r, H), **bf)
+        self.b_gate = torch.zeros((E, I, r), **bf)
+        self.b_up = torch.zeros((E, I, r), **bf)
+        self.a_down = torch.zeros((E, r, I), **bf)
+        self.b_down = torch.zeros((E, H, r), **bf)
+        self.desc = Q4LoraLayer(E, H, I, top_k, r, int(self.asymmetric), self.base_gate_up.data_ptr(),
+                                self.base_down.data_ptr(), self.a_gate_up.data_ptr(), self.b_gate.data_ptr(),
+                                self.b_up.data_ptr(), self.a_down.data_ptr(), self.b_down.data_ptr())
+
+    def set_base(self, gate, up, down):
+        """Quantise (on the GPU) and place the frozen dense FFN."""
+        I, H = self.inter, self.hidden
+        gu = torch.cat([gate, up], dim=0).contiguous()
+        p, s, z = quantize_int4_g128(gu, self.asymmetric)
+        q4_repack_device(p, s, z, 2 * I, H, self.asymmetric, gate_up=False, out=self.base_gate_up)
+        p, s, z = quantize_int4_g128(down.contiguous(), self.asymmetric)
+        q4_repack_device(p, s, z, H, I, self.asymmetric, gate_up=False, out=self.base_down)
+
+    def set_adapters(self, e, ad):
+        """ad: {"A_gate", "B_gate", "A_up", "B_up", "A_down", "B_down"} tensors (bf16 values)."""
+        r = self.rank
+        self.a_gate_up[e, :r] = ad["A_gate"]
+        self.a_gate_up[e, r:] = ad["A_up"]
+        self.b_gate[e] = ad["B_gate"]
+        self.b_up[e] = ad["B_up"]
+        self.a_down[e] = ad["A_down"]
+        self.b_down[e] = ad["B_down"]
+
+    def weight_bytes(self):
+        ad = sum(t.numel() * 2 for t in (self.a_gate_up, self.b_gate, self.b_up, self.a_down, self.b_down))
+        return self.gu_bytes + self.dn_bytes + ad
+
+    def workspace_bytes(self, t):
+        return int(_lib.moe_lora_ffn_workspace_bytes(ctypes.byref(self.desc), t))
+
+
+def moe_lora_ffn_forward(layer, x, ids, weights, out=None, workspace=None):
+    """out [t, H] bf16 = sum_j w[t, j] FFN_{ids[t, j]}(x[t]) for LoRA-mode experts."""
+    _need(x, torch.bfloat16, "x", 2)
+    _need(ids, torch.int32, "ids", 2)
+    _need(weights, torch.float32, "weights", 2)
+    t = x.shape[0]
+    if x.shape[1] != layer.hidden or tuple(ids.shape) != (t, layer.top_k) or tuple(weights.shape) != (t, layer.top_k):
+        raise ValueError("shape mismatch between x, ids, weights and the layer")
+    if out is None:
+        out = torch.empty_like(x)
+    nbytes = layer.workspace_bytes(t)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=x.device)
+    _check("moe_lora_ffn_forward", _lib.moe_lora_ffn_forward(
+        ctypes.byref(layer.desc), _ptr(x), t, _ptr(ids), _ptr(weights), _ptr(out), _ptr(workspace),
+        workspace.numel(), _stream()))
+    return out
 
 
 def int4_linear_forward(x, w_dev, n, asymmetric=False):

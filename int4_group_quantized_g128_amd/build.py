@@ -10,7 +10,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libq4moe.so")
-SOURCES = ["api.hip", "quantize.hip", "router.hip", "permute.hip", "gemm.hip", "gemm_prefill.hip"]
+SOURCES = ["api.hip", "quantize.hip", "router.hip", "permute.hip", "gemm.hip", "gemm_prefill.hip", "lora.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

@@ -420,6 +420,137 @@ int moe_int4_ffn_debug(const q4_moe_layer_t* L, const uint16_t* x_bf16, int64_t 
   return ffn_forward(L, x_bf16, t, topk_ids, topk_w, mode, out_bf16, workspace, ws_bytes, stream, views);
 }
 
+// ------------------------------------------------------------------ LoRA-mode experts
+namespace {
+
+struct LoraWorkspace {
+  float* base_gu = nullptr;   // [t][2I]
+  float* a = nullptr;         // [t k][K chunks][2r] partial input projections
+  float* d = nullptr;         // [t k][column blocks][r] partial down-adapter projections
+  uint16_t* hw = nullptr;     // [t][I] bf16
+  float* y = nullptr;         // [t][H]
+  TileDesc* tiles = nullptr;  // dense row tiles (prefill GEMM)
+  int32_t* num_tiles = nullptr;
+  float* rs_x = nullptr;      // [t][H/128]
+  float* rs_h = nullptr;      // [t][I/128]
+  bool prefill = false;
+  int64_t bytes = 0;
+};
+
+LoraWorkspace carve_lora(const q4_lora_layer_t* L, int64_t t, void* base) {
+  LoraWorkspace w;
+  const int64_t H = L->hidden, I = L->inter, r = L->rank, P = t * L->top_k;
+  w.prefill = t >= 64 && prefill_fits(t, H, 0, int64_t(q4_device_bytes(2 * I, H, L->asymmetric))) &&
+              prefill_fits(t, I, 0, int64_t(q4_device_bytes(H, I, L->asymmetric)));
+  int64_t off = 0;
+  auto take = [&](int64_t bytes) {
+    const int64_t at = off;
+    off += a256(bytes);
+    return base ? static_cast<uint8_t*>(base) + at : nullptr;
+  };
+  w.base_gu = reinterpret_cast<float*>(take(t * 2 * I * 4));
+  w.a = reinterpret_cast<float*>(take(P * lora_kchunks(H) * 2 * r * 4));
+  w.d = reinterpret_cast<float*>(take(P * lora_col_blocks(I) * r * 4));
+  w.hw = reinterpret_cast<uint16_t*>(take(t * I * 2));
+  w.y = reinterpret_cast<float*>(take(t * H * 4));
+  if (w.prefill) {
+    w.tiles = reinterpret_cast<TileDesc*>(take((t / 128 + 1) * int64_t(sizeof(TileDesc))));
+    w.num_tiles = reinterpret_cast<int32_t*>(take(4));
+    w.rs_x = reinterpret_cast<float*>(take(t * (H / 128) * 4));
+    w.rs_h = reinterpret_cast<float*>(take(t * (I / 128) * 4));
+  }
+  w.bytes = off;
+  return w;
+}
+
+int validate_lora(const q4_lora_layer_t* L) {
+  Q4_REQUIRE(L, Q4_ERR_NULL, "layer descriptor is NULL");
+  Q4_REQUIRE(L->num_experts >= 1 && L->num_experts <= 4096, Q4_ERR_SHAPE, "num_experts %d not in [1, 4096]",
+             L->num_experts);
+  Q4_REQUIRE(L->top_k >= 1 && L->top_k <= L->num_experts, Q4_ERR_SHAPE, "top_k %d not in [1, num_experts]", L->top_k);
+  Q4_REQUIRE(L->hidden > 0 && L->hidden % 128 == 0, Q4_ERR_SHAPE, "hidden %d must be a positive multiple of 128",
+             L->hidden);
+  Q4_REQUIRE(L->inter > 0 && L->inter % 128 == 0, Q4_ERR_SHAPE, "inter %d must be a positive multiple of 128",
+             L->inter);
+  Q4_REQUIRE(L->rank >= 8 && L->rank <= 64 && L->rank % 8 == 0, Q4_ERR_SHAPE, "rank %d not in {8, 16, ..., 64}",
+             L->rank);
+  Q4_REQUIRE(L->asymmetric == 0 || L->asymmetric == 1, Q4_ERR_SHAPE, "asymmetric must be 0 or 1");
+  Q4_REQUIRE(L->base_gate_up && L->base_down && L->a_gate_up && L->b_gate && L->b_up && L->a_down && L->b_down,
+             Q4_ERR_NULL, "missing layer pointer");
+  Q4_REQUIRE(!misaligned(L->base_gate_up) && !misaligned(L->base_down) && !misaligned(L->a_gate_up) &&
+                 !misaligned(L->b_gate) && !misaligned(L->b_up) && !misaligned(L->a_down) && !misaligned(L->b_down),
+             Q4_ERR_ALIGN, "layer pointers must be 16-byte aligned");
+  return Q4_OK;
+}
+
+// y[rows][n] = a[rows][k] W^T for a PLAIN device-layout INT4 matrix (bf16 activations):
+// the decode kernel for few rows, the prefill kernel (dense row tiles) for many.
+int dense_gemm(const uint16_t* a, int64_t rows, int64_t k, const void* w_dev, int64_t n, int asym, float* y,
+               bool prefill, TileDesc* tiles, int32_t* num_tiles, float* rs, hipStream_t stream) {
+  GemmArgs g{};
+  g.a = a;
+  g.a_rows = rows;
+  g.w = static_cast<const uint8_t*>(w_dev);
+  g.w_stride = int64_t(q4_device_bytes(n, k, asym));
+  g.num_experts = 1;
+  g.asym = asym;
+  g.N = n;
+  g.K = k;
+  g.out = y;
+  if (prefill) {
+    int rc;
+    if ((rc = check_hip(launch_dense_tiles(rows, 128, tiles, num_tiles, stream), "dense tiles"))) return rc;
+    if ((rc = check_hip(launch_rowsum(a, 0, rows, k, rs, stream), "row sums"))) return rc;
+    g.tiles = tiles;
+    g.num_tiles = num_tiles;
+    g.max_tiles = int32_t(rows / 128 + 1);
+    g.a_gsum = rs;
+    return check_hip(launch_gemm_prefill(g, 0, GEMM_PLAIN, stream), "prefill gemm");
+  }
+  g.dense_rows = rows;
+  const int rb = rows <= 16 ? 1 : (rows <= 32 ? 2 : 4);
+  return check_hip(launch_gemm(g, 0, GEMM_PLAIN, rb, stream), "gemm");
+}
+
+}  // namespace
+
+size_t moe_lora_ffn_workspace_bytes(const q4_lora_layer_t* layer, int64_t t) {
+  if (!layer || t < 0 || validate_lora(layer) != Q4_OK) return 0;
+  return size_t(carve_lora(layer, t, nullptr).bytes);
+}
+
+int moe_lora_ffn_forward(const q4_lora_layer_t* L, const uint16_t* x_bf16, int64_t t, const int32_t* topk_ids,
+                         const float* topk_w, uint16_t* out_bf16, void* workspace, size_t ws_bytes,
+                         hipStream_t stream) {
+  g_last_error.clear();
+  if (int rc = validate_lora(L)) return rc;
+  Q4_REQUIRE(t >= 0, Q4_ERR_SHAPE, "t < 0");
+  if (t == 0) return ok();
+  Q4_REQUIRE(t * L->top_k < (int64_t(1) << 31) && t * 2 * L->inter < (int64_t(1) << 40), Q4_ERR_SHAPE, "t too large");
+  Q4_REQUIRE(x_bf16 && topk_ids && topk_w && out_bf16 && workspace, Q4_ERR_NULL, "missing pointer");
+  Q4_REQUIRE(!misaligned(x_bf16) && !misaligned(out_bf16) && !misaligned(workspace), Q4_ERR_ALIGN,
+             "x, out and workspace must be 16-byte aligned");
+  LoraWorkspace w = carve_lora(L, t, workspace);
+  Q4_REQUIRE(ws_bytes >= size_t(w.bytes), Q4_ERR_WORKSPACE, "workspace %zu < %lld", ws_bytes, (long long)w.bytes);
+  const int64_t H = L->hidden, I = L->inter;
+  const int r = L->rank, kk = L->top_k, E = L->num_experts;
+  int rc;
+  if ((rc = dense_gemm(x_bf16, t, H, L->base_gate_up, 2 * I, L->asymmetric, w.base_gu, w.prefill, w.tiles,
+                       w.num_tiles, w.rs_x, stream)))
+    return rc;
+  if ((rc = check_hip(launch_lora_in(x_bf16, t, H, topk_ids, kk, E, L->a_gate_up, r, w.a, stream), "lora in")))
+    return rc;
+  if ((rc = check_hip(launch_lora_mid(w.base_gu, t, H, I, topk_ids, topk_w, kk, E, r, w.a, L->b_gate, L->b_up,
+                                      L->a_down, w.d, w.hw, stream),
+                      "lora mid")))
+    return rc;
+  if ((rc = dense_gemm(w.hw, t, I, L->base_down, H, L->asymmetric, w.y, w.prefill, w.tiles, w.num_tiles, w.rs_h,
+                       stream)))
+    return rc;
+  return check_hip(launch_lora_out(w.y, t, H, I, topk_ids, topk_w, kk, E, r, w.d, L->b_down, out_bf16, stream),
+                   "lora out");
+}
+
 int int4_linear_forward(const void* x, int x_dtype, int64_t t, int64_t k, const void* w_dev, int64_t n, int asymmetric,
                         float* y, hipStream_t stream) {
   g_last_error.clear();

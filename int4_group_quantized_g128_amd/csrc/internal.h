@@ -77,6 +77,19 @@ hipError_t launch_gemm_prefill(const GemmArgs& g, int act /*0 bf16, 2 i8*/, int 
 // Per-(row, group of 128) sums: bf16 -> fp32, or int8 -> int32.
 hipError_t launch_rowsum(const void* a, int is_i8, int64_t rows, int64_t K, void* out, hipStream_t st);
 
+// LoRA-mode experts (lora.hip).
+hipError_t launch_dense_tiles(int64_t t, int tile_rows, TileDesc* tiles, int32_t* num_tiles, hipStream_t st);
+hipError_t launch_lora_in(const uint16_t* x, int64_t t, int64_t h, const int32_t* ids, int32_t kk, int32_t e,
+                          const uint16_t* a_gu, int r, float* a_part, hipStream_t st);
+hipError_t launch_lora_mid(const float* base_gu, int64_t t, int64_t h, int64_t inter, const int32_t* ids,
+                           const float* w, int32_t kk, int32_t e, int r, const float* a_part, const uint16_t* b_gate,
+                           const uint16_t* b_up, const uint16_t* a_down, float* d_part, uint16_t* hw, hipStream_t st);
+hipError_t launch_lora_out(const float* y, int64_t t, int64_t hidden, int64_t inter, const int32_t* ids,
+                           const float* w, int32_t kk, int32_t e, int r, const float* d_part, const uint16_t* b_down,
+                           uint16_t* out, hipStream_t st);
+int lora_kchunks(int64_t h);       // K chunks (512 wide) of the adapter input projections
+int lora_col_blocks(int64_t inter);  // column blocks of the SwiGLU / down-projection kernel
+
 hipError_t launch_combine(const float* y, const int32_t* inv, const float* w, int64_t t, int32_t k, int shared,
                           int64_t h, uint16_t* out, hipStream_t st);
 

@@ -1,0 +1,267 @@
+// LoRA-mode experts: per-expert low-rank adapters on one frozen INT4 g128 dense FFN.
+//
+// Page "高效大语言模型推理实践：INT4量化与MoE架构的融合探索", 第三阶段 (LoRA mode:
+// experts start from LoRA adapters on frozen dense weights); expert e of matrix m is
+// W_hat_m + B_m,e A_m,e.  The forward uses two exact identities of that definition:
+//  - gate/up: (W_hat + B A) x = W_hat x + B (A x), so the INT4 base GEMM runs once per
+//    token and every (token, choice) slot adds a rank-r update;
+//  - down is linear: sum_j w_j (W_hat + B_j A_j) h_j = W_hat (sum_j w_j h_j)
+//    + sum_j w_j B_j (A_j h_j), so the INT4 base down GEMM also runs once per token.
+// Kernels here: the rank-r input projections (k_lora_in), SwiGLU + weighted sum + the
+// down-adapter input projection (k_lora_mid), the final combine (k_lora_out), and the
+// row-tile list of a dense matrix for the prefill GEMM (k_dense_tiles).
+#include "common.h"
+#include "internal.h"
+
+namespace q4 {
+
+__global__ void k_dense_tiles(int64_t t, int tile_rows, TileDesc* __restrict__ tiles, int32_t* __restrict__ num_tiles) {
+  const int64_t n = (t + tile_rows - 1) / tile_rows;
+  const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i == 0) *num_tiles = int32_t(n);
+  if (i < n) {
+    TileDesc d;
+    d.expert = 0;
+    d.row_start = int32_t(i * tile_rows);
+    d.rows = int32_t(std::min<int64_t>(tile_rows, t - i * tile_rows));
+    d.pad = 0;
+    tiles[i] = d;
+  }
+}
+
+Q4_DEVICE float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// Partial input projections: a_part[p][ks][q] = sum_{k in chunk ks} A_e[q][k] x_t[k]
+// (q < 2r: A_gate,e rows then A_up,e rows) for slot p = t * kk + j, e = ids[p], and
+// the 512-wide K chunk ks (one wave per (slot, chunk); lane l covers k = 512 ks + 8 l
+// .. + 7).  The 64 lane partials of each q are summed in lane order through LDS.
+template <int R2>
+__global__ void __launch_bounds__(64) k_lora_in(const uint16_t* __restrict__ x, int64_t h, const int32_t* __restrict__ ids,
+                                                int32_t kk, int32_t e_count, const uint16_t* __restrict__ a_gu, int r2,
+                                                float* __restrict__ a_part) {
+  __shared__ float part[R2][65];
+  const int lane = threadIdx.x;
+  const int64_t p = blockIdx.x, ks = blockIdx.y, nks = gridDim.y;
+  const int64_t t = p / kk;
+  const int e = min(max(ids[p], 0), e_count - 1);
+  const int64_t k0 = ks * 512 + int64_t(lane) * 8;
+  float acc[R2];
+#pragma unroll
+  for (int q = 0; q < R2; ++q) acc[q] = 0.f;
+  if (k0 < h) {
+    const uint4 xv = load16(x + t * h + k0);
+    float xf[8];
+    const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      xf[2 * i] = bf16_to_f32(uint16_t(xw[i] & 0xffff));
+      xf[2 * i + 1] = bf16_to_f32(uint16_t(xw[i] >> 16));
+    }
+    uint4 av[R2];
+#pragma unroll
+    for (int q = 0; q < R2; ++q) av[q] = q < r2 ? load16(a_gu + (int64_t(e) * r2 + q) * h + k0) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int q = 0; q < R2; ++q) {
+      const uint32_t aw[4] = {av[q].x, av[q].y, av[q].z, av[q].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[q] = fmaf(bf16_to_f32(uint16_t(aw[i] & 0xffff)), xf[2 * i], acc[q]);
+        acc[q] = fmaf(bf16_to_f32(uint16_t(aw[i] >> 16)), xf[2 * i + 1], acc[q]);
+      }
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < R2; ++q) part[q][lane] = acc[q];
+  __syncthreads();
+  if (lane < r2) {
+    float s = 0.f;
+    for (int l = 0; l < 64; ++l) s += part[lane][l];
+    a_part[(p * nks + ks) * r2 + lane] = s;
+  }
+}
+
+// Column block cb of token t (256 threads x 4 consecutive columns): for each choice j
+// (expert e, weight w_j, slot p), with a = sum over K chunks of a_part[p] (in order):
+//   g_c = base_gu[t][c] + sum_q B_gate,e[c][q] a[q]
+//   u_c = base_gu[t][I + c] + sum_q B_up,e[c][q] a[r + q]
+//   h_c = silu(g_c) u_c;  hw_c += w_j h_c;  d_part[p][cb][q] = sum_{c in block} A_down,e[q][c] h_c
+// then hw[t][c] = bf16(hw_c).  r is a multiple of 8 and at most RM.
+constexpr int kMidCols = 1024;   // columns per workgroup
+template <int RM>
+__global__ void __launch_bounds__(256) k_lora_mid(const float* __restrict__ base_gu, int64_t inter,
+                                                  const int32_t* __restrict__ ids, const float* __restrict__ w,
+                                                  int32_t kk, int32_t e_count, int r, int nks,
+                                                  const float* __restrict__ a_part, const uint16_t* __restrict__ b_gate,
+                                                  const uint16_t* __restrict__ b_up, const uint16_t* __restrict__ a_down,
+                                                  float* __restrict__ d_part, uint16_t* __restrict__ hw) {
+  __shared__ float s_a[2 * RM];
+  __shared__ float s_red[4][RM];
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int64_t t = blockIdx.y, cb = blockIdx.x, ncb = gridDim.x;
+  const int64_t c0 = cb * kMidCols + int64_t(tid) * 4;
+  const bool cv = c0 < inter;     // inter % 128 == 0, so a thread's 4 columns are all valid or all not
+  float hacc[4] = {0.f, 0.f, 0.f, 0.f};
+  float4 bgu0 = make_float4(0.f, 0.f, 0.f, 0.f), bgu1 = bgu0;
+  if (cv) {
+    bgu0 = *reinterpret_cast<const float4*>(base_gu + t * 2 * inter + c0);
+    bgu1 = *reinterpret_cast<const float4*>(base_gu + t * 2 * inter + inter + c0);
+  }
+  const float g0[4] = {bgu0.x, bgu0.y, bgu0.z, bgu0.w}, u0[4] = {bgu1.x, bgu1.y, bgu1.z, bgu1.w};
+  for (int j = 0; j < kk; ++j) {
+    const int64_t p = t * kk + j;
+    const int e = min(max(ids[p], 0), e_count - 1);
+    const float wj = w[p];
+    __syncthreads();   // s_a / s_red of the previous choice are consumed
+    if (tid < 2 * r) {
+      float s = 0.f;
+      for (int ks = 0; ks < nks; ++ks) s += a_part[(p * nks + ks) * 2 * r + tid];
+      s_a[tid] = s;
+    }
+    __syncthreads();
+    float dp[RM];
+#pragma unroll
+    for (int q = 0; q < RM; ++q) dp[q] = 0.f;
+    if (cv) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t c = c0 + i;
+        float g = g0[i], u = u0[i];
+        const uint16_t* bg = b_gate + (int64_t(e) * inter + c) * r;
+        const uint16_t* bu = b_up + (int64_t(e) * inter + c) * r;
+#pragma unroll
+        for (int q8 = 0; q8 < RM; q8 += 8) {
+          if (q8 < r) {
+            const uint4 vg = load16(bg + q8), vu = load16(bu + q8);
+            const uint32_t wg[4] = {vg.x, vg.y, vg.z, vg.w}, wu[4] = {vu.x, vu.y, vu.z, vu.w};
+#pragma unroll
+            for (int z = 0; z < 4; ++z) {
+              g = fmaf(bf16_to_f32(uint16_t(wg[z] & 0xffff)), s_a[q8 + 2 * z], g);
+              g = fmaf(bf16_to_f32(uint16_t(wg[z] >> 16)), s_a[q8 + 2 * z + 1], g);
+              u = fmaf(bf16_to_f32(uint16_t(wu[z] & 0xffff)), s_a[r + q8 + 2 * z], u);
+              u = fmaf(bf16_to_f32(uint16_t(wu[z] >> 16)), s_a[r + q8 + 2 * z + 1], u);
+            }
+          }
+        }
+        const float hv = swiglu(g, u);
+        hacc[i] = fmaf(wj, hv, hacc[i]);
+        const uint16_t* ad = a_down + int64_t(e) * r * inter + c;
+#pragma unroll
+        for (int q = 0; q < RM; ++q)
+          if (q < r) dp[q] = fmaf(bf16_to_f32(ad[int64_t(q) * inter]), hv, dp[q]);
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < RM; ++q) {
+      const float s = wave_sum(dp[q]);
+      if (lane == 0 && q < r) s_red[wid][q] = s;
+    }
+    __syncthreads();
+    if (tid < r) d_part[(p * ncb + cb) * r + tid] = ((s_red[0][tid] + s_red[1][tid]) + s_red[2][tid]) + s_red[3][tid];
+  }
+  if (cv) {
+    const uint32_t lo = uint32_t(f32_to_bf16(hacc[0])) | (uint32_t(f32_to_bf16(hacc[1])) << 16);
+    const uint32_t hi = uint32_t(f32_to_bf16(hacc[2])) | (uint32_t(f32_to_bf16(hacc[3])) << 16);
+    *reinterpret_cast<uint2*>(hw + t * inter + c0) = make_uint2(lo, hi);
+  }
+}
+
+// out[t][c] = bf16( y[t][c] + sum_j w_j sum_q B_down,e_j[c][q] d[t kk + j][q] ), d the
+// sum over column blocks of d_part (in order).
+__global__ void __launch_bounds__(256) k_lora_out(const float* __restrict__ y, int64_t hidden,
+                                                  const int32_t* __restrict__ ids, const float* __restrict__ w,
+                                                  int32_t kk, int32_t e_count, int r, int ncb,
+                                                  const float* __restrict__ d_part, const uint16_t* __restrict__ b_down,
+                                                  uint16_t* __restrict__ out) {
+  extern __shared__ float s_d[];   // [kk][r]
+  const int tid = threadIdx.x;
+  const int64_t t = blockIdx.y;
+  for (int i = tid; i < kk * r; i += 256) {
+    const int j = i / r, q = i - j * r;
+    const int64_t p = t * kk + j;
+    float s = 0.f;
+    for (int cb = 0; cb < ncb; ++cb) s += d_part[(p * ncb + cb) * r + q];
+    s_d[i] = s;
+  }
+  __syncthreads();
+  const int64_t c = int64_t(blockIdx.x) * 256 + tid;
+  if (c >= hidden) return;
+  float acc = y[t * hidden + c];
+  for (int j = 0; j < kk; ++j) {
+    const int64_t p = t * kk + j;
+    const int e = min(max(ids[p], 0), e_count - 1);
+    const uint16_t* bd = b_down + (int64_t(e) * hidden + c) * r;
+    float s = 0.f;
+    for (int q8 = 0; q8 < r; q8 += 8) {
+      const uint4 v = load16(bd + q8);
+      const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int z = 0; z < 4; ++z) {
+        s = fmaf(bf16_to_f32(uint16_t(wv[z] & 0xffff)), s_d[j * r + q8 + 2 * z], s);
+        s = fmaf(bf16_to_f32(uint16_t(wv[z] >> 16)), s_d[j * r + q8 + 2 * z + 1], s);
+      }
+    }
+    acc = fmaf(w[p], s, acc);
+  }
+  out[t * hidden + c] = f32_to_bf16(acc);
+}
+
+int lora_kchunks(int64_t h) { return int((h + 511) / 512); }
+int lora_col_blocks(int64_t inter) { return int((inter + kMidCols - 1) / kMidCols); }
+
+hipError_t launch_dense_tiles(int64_t t, int tile_rows, TileDesc* tiles, int32_t* num_tiles, hipStream_t st) {
+  const int64_t n = (t + tile_rows - 1) / tile_rows;
+  const unsigned blocks = unsigned(std::max<int64_t>(1, (n + 255) / 256));
+  hipLaunchKernelGGL(k_dense_tiles, dim3(blocks), dim3(256), 0, st, t, tile_rows, tiles, num_tiles);
+  return hipGetLastError();
+}
+
+hipError_t launch_lora_in(const uint16_t* x, int64_t t, int64_t h, const int32_t* ids, int32_t kk, int32_t e,
+                          const uint16_t* a_gu, int r, float* a_part, hipStream_t st) {
+  const int64_t P = t * kk;
+  const int r2 = 2 * r;
+  if (P == 0) return hipSuccess;
+  const dim3 g = dim3(unsigned(P), unsigned(lora_kchunks(h))), b = dim3(64);
+  if (r2 <= 16)
+    hipLaunchKernelGGL(k_lora_in<16>, g, b, 0, st, x, h, ids, kk, e, a_gu, r2, a_part);
+  else if (r2 <= 32)
+    hipLaunchKernelGGL(k_lora_in<32>, g, b, 0, st, x, h, ids, kk, e, a_gu, r2, a_part);
+  else if (r2 <= 64)
+    hipLaunchKernelGGL(k_lora_in<64>, g, b, 0, st, x, h, ids, kk, e, a_gu, r2, a_part);
+  else
+    hipLaunchKernelGGL(k_lora_in<128>, g, b, 0, st, x, h, ids, kk, e, a_gu, r2, a_part);
+  return hipGetLastError();
+}
+
+hipError_t launch_lora_mid(const float* base_gu, int64_t t, int64_t h, int64_t inter, const int32_t* ids,
+                           const float* w, int32_t kk, int32_t e, int r, const float* a_part, const uint16_t* b_gate,
+                           const uint16_t* b_up, const uint16_t* a_down, float* d_part, uint16_t* hw, hipStream_t st) {
+  if (t == 0) return hipSuccess;
+  const dim3 g = dim3(unsigned(lora_col_blocks(inter)), unsigned(t)), b = dim3(256);
+  const int nks = lora_kchunks(h);
+  if (r <= 16)
+    hipLaunchKernelGGL(k_lora_mid<16>, g, b, 0, st, base_gu, inter, ids, w, kk, e, r, nks, a_part, b_gate, b_up, a_down,
+                       d_part, hw);
+  else if (r <= 32)
+    hipLaunchKernelGGL(k_lora_mid<32>, g, b, 0, st, base_gu, inter, ids, w, kk, e, r, nks, a_part, b_gate, b_up, a_down,
+                       d_part, hw);
+  else
+    hipLaunchKernelGGL(k_lora_mid<64>, g, b, 0, st, base_gu, inter, ids, w, kk, e, r, nks, a_part, b_gate, b_up, a_down,
+                       d_part, hw);
+  return hipGetLastError();
+}
+
+hipError_t launch_lora_out(const float* y, int64_t t, int64_t hidden, int64_t inter, const int32_t* ids,
+                           const float* w, int32_t kk, int32_t e, int r, const float* d_part, const uint16_t* b_down,
+                           uint16_t* out, hipStream_t st) {
+  if (t == 0) return hipSuccess;
+  const dim3 g = dim3(unsigned((hidden + 255) / 256), unsigned(t));
+  hipLaunchKernelGGL(k_lora_out, g, dim3(256), size_t(kk) * r * sizeof(float), st, y, hidden, ids, w, kk, e, r,
+                     lora_col_blocks(inter), d_part, b_down, out);
+  return hipGetLastError();
+}
+
+}  // namespace q4
