@@ -99,22 +99,23 @@ def widen_int8(qm):
     """4-bit code -> 8-bit integer with the zero point removed, no scaling."""
     q, s, z = qm
     q = np.asarray(q, dtype=np.int64)
-    if z is None:
-        return q
-    zz = np.repeat(np.asarray(z, dtype=np.int64), GROUP, axis=1)
-    return q - zz
+    if z is not None:
+        q = q - np.repeat(np.asarray(z, dtype=np.int64), GROUP, axis=1)
+    assert np.all(np.abs(q) <= 15)
+    return q
 
 
 def group_acc(qx, w8):
     """acc[t, n, g] = sum_{k in group g} qx[t, k] * w8[n, k], exact.
 
     The per-group products are evaluated by a float64 matrix product: every
-    operand is an integer with |qx| <= 128 and |w8| <= 15, so every partial sum is
-    an integer below 128 * 128 * 15 < 2^53 and float64 represents it exactly.
+    operand is an integer with |qx| <= 128 and |w8| <= 127 (<= 15 for 4-bit
+    codes), so every partial sum is an integer below 128 * 128 * 127 < 2^53 and
+    float64 represents it exactly.
     """
     qx = np.asarray(qx, dtype=np.int64)
     w8 = np.asarray(w8, dtype=np.int64)
-    assert np.all(np.abs(qx) <= 128) and np.all(np.abs(w8) <= 15)
+    assert np.all(np.abs(qx) <= 128) and np.all(np.abs(w8) <= 127)
     t, k = qx.shape
     n = w8.shape[0]
     g = k // GROUP
@@ -161,6 +162,41 @@ def moe_w4a8(x, expert, ids, weights, shared=None):
             out[r] += w[r, c] * y[i]
     if shared is not None:
         out += swiglu_w4a8(x32, *shared)
+    return out
+
+
+# ---------------------------------------------------------------- W8A8
+# The same pipeline with 8-bit weight codes (oracle/quant.quantize_sym8): no widening,
+# INT32 group sums of int8(x) * q, rescale by s_x * s_w per group.
+def linear_w8a8(qx, sx, qm):
+    """y[t, n] = s_x[t] * sum_g s_w[n, g] * acc[t, n, g] in float64, 8-bit codes."""
+    q, s, _ = qm
+    acc = group_acc(qx, q).astype(np.float64)
+    sw = np.asarray(s, dtype=np.float16).astype(np.float64)
+    y = np.einsum("tng,ng->tn", acc, sw)
+    return np.asarray(sx, dtype=np.float64)[:, None] * y
+
+
+def swiglu_w8a8(x, gate, up, down):
+    qx, sx = act_quant_int8(x)
+    h = silu(linear_w8a8(qx, sx, gate)) * linear_w8a8(qx, sx, up)
+    qh, sh = act_quant_int8(h.astype(np.float32))
+    return linear_w8a8(qh, sh, down)
+
+
+def moe_w8a8(x, expert, ids, weights, shared=None):
+    x32 = np.asarray(x, dtype=np.float32)
+    ids = np.asarray(ids)
+    w = np.asarray(weights, dtype=np.float64)
+    t, k = ids.shape
+    out = np.zeros((t, x32.shape[1]), dtype=np.float64)
+    for e in np.unique(ids):
+        rows, cols = np.nonzero(ids == e)
+        y = swiglu_w8a8(x32[rows], *expert(int(e)))
+        for i, (r, c) in enumerate(zip(rows, cols)):
+            out[r] += w[r, c] * y[i]
+    if shared is not None:
+        out += swiglu_w8a8(x32, *shared)
     return out
 
 

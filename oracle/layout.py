@@ -123,3 +123,56 @@ def from_device(dev, n, k, asymmetric, gate_up):
     inv = np.empty_like(src)
     inv[src] = np.arange(n)
     return q[inv], sc[inv].astype(np.uint16), (zz[inv] if zz is not None else None)
+
+
+# ---------------------------------------------------------------- 8-bit weights
+# INT8 device layout (W8A8): one 2048-byte tile per (16-column block cb, group g),
+# tiles cb-major at byte 2048 * (cb * G + g).  The tile is two 1024-byte halves,
+# half i for k in [128 g + 64 i, 128 g + 64 i + 64); inside a half, lane L in [0, 64)
+# (column c = L % 16, quarter kq = L // 16) owns 16 bytes: bytes 0..7 are
+# k = 128 g + 64 i + 8 kq + e and bytes 8..15 are k = 128 g + 64 i + 32 + 8 kq + e,
+# e in [0, 8), as two's-complement int8 codes.  Scales as for INT4, binary16
+# [N/16][G][16] at byte align256(N K).  Same column orders (plain / gate-up).
+
+def device_bytes8(n, k):
+    return _a256(n * k) + _a256(2 * n * (k // GROUP))
+
+
+def _offsets8(n, k):
+    g = k // GROUP
+    jj, kk = np.meshgrid(np.arange(n), np.arange(k), indexing="ij")
+    cb, c = jj // 16, jj % 16
+    gg, r = kk // GROUP, kk % GROUP
+    half, rr = r // 64, r % 64
+    hi, kq, e = rr // 32, (rr % 32) // 8, rr % 8
+    lane = kq * 16 + c
+    return (cb * g + gg) * 2048 + half * 1024 + lane * 16 + hi * 8 + e
+
+
+def to_device8(q, scale_bits, n, k, gate_up):
+    """INT8 codes [N, K] + scale bits [N, G] -> device bytes (device_bytes8(n, k))."""
+    if n % (32 if gate_up else 16) or k % GROUP:
+        raise ValueError("shape not supported by the device layout")
+    g = k // GROUP
+    src = column_source(n, gate_up)
+    qd = np.asarray(q, dtype=np.int64)[src]
+    s = np.asarray(scale_bits, dtype=np.uint16)[src]
+    out = np.zeros(device_bytes8(n, k), dtype=np.uint8)
+    out[_offsets8(n, k).ravel()] = (qd & 0xFF).astype(np.uint8).ravel()
+    so = _a256(n * k)
+    sc = s.reshape(n // 16, 16, g).transpose(0, 2, 1).reshape(-1)
+    out[so: so + 2 * n * g] = sc.astype("<u2").view(np.uint8)
+    return out
+
+
+def from_device8(dev, n, k, gate_up):
+    """Device bytes -> (q int64 [N, K], scale bits uint16 [N, G]) in canonical row order."""
+    g = k // GROUP
+    dev = np.asarray(dev, dtype=np.uint8)
+    q = dev[_offsets8(n, k)].view(np.int8).astype(np.int64)
+    so = _a256(n * k)
+    sc = dev[so: so + 2 * n * g].view("<u2").reshape(n // 16, g, 16).transpose(0, 2, 1).reshape(n, g)
+    src = column_source(n, gate_up)
+    inv = np.empty_like(src)
+    inv[src] = np.arange(n)
+    return q[inv], sc[inv].astype(np.uint16)

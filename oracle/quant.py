@@ -107,8 +107,35 @@ def quantize_asym(w):
     return (q.reshape(np.asarray(w).shape).astype(np.uint8), s16, z.astype(np.uint8))
 
 
+def quantize_sym8(w):
+    """Symmetric INT8 g128 quantisation: the W8A8 comparison format.
+
+    Returns (q int8 [N, K] in [-127, 127], scales float16 [N, K/128]).  Page
+    "MoE推理优化实战：4bit存储+INT8计算的W4A8路线解析" lists W8A8 (INT8 weights and
+    INT8 compute) as the accuracy-safe route to try first; its weight format is not
+    spelled out, so it takes the same per-group structure as the INT4 format: per
+    group of 128, s = amax / 127 as an IEEE float32 division, rounded *upward* to
+    binary16 (as for the asymmetric INT4 scale: with 127 levels a nearest-even
+    binary16 scale -- subnormal for small groups -- can fall below amax / 127 by more
+    than half a step, and the clamped group maximum would then miss the half-step
+    bound), q = clamp(rint(w / s), -127, 127) with the stored scale; a zero scale
+    gives codes 0.
+    """
+    wg = _groups(w)
+    amax = np.max(np.abs(wg), axis=2)
+    s16 = f32_to_f16_up(amax / np.float32(127.0))
+    if not np.all(np.isfinite(s16)):
+        raise ValueError("scale overflows binary16")
+    s32 = s16.astype(np.float32)
+    q = np.zeros(wg.shape, dtype=np.float32)
+    nz = s32 > 0
+    q[nz] = np.rint(wg[nz] / s32[nz][:, None])
+    q = np.clip(q, -127, 127)
+    return q.reshape(np.asarray(w).shape).astype(np.int8), s16
+
+
 def dequantize(q, scales, zeros=None):
-    """w_hat = (q - z) * s in float64 (exact: a 4-bit integer times a binary16)."""
+    """w_hat = (q - z) * s in float64 (exact: a small integer times a binary16)."""
     q = np.asarray(q, dtype=np.int64)
     n, k = q.shape
     s = np.asarray(scales, dtype=np.float16).astype(np.float64)
