@@ -41,7 +41,7 @@ def parse():
     p.add_argument("--steps", type=int, default=100)
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--tokens", type=int, default=64)
-    p.add_argument("--mode", choices=["w4a16", "w4a8"], default="w4a16")
+    p.add_argument("--mode", choices=["w4a16", "w4a8", "w8a8"], default="w4a16")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-tokens", type=int, default=2, help="tokens in the oracle's timed sample")
     p.add_argument("--no-extra", action="store_true", help="skip the secondary workloads")
@@ -58,10 +58,11 @@ class Workload:
         self.lib, self.torch = lib, torch
         cfg = synth.CONFIGS[cfg_name]
         self.cfg_name, self.cfg, self.t = cfg_name, cfg, t
-        self.mode = lib.Q4_W4A8 if mode == "w4a8" else lib.Q4_W4A16
+        self.mode = {"w4a16": lib.Q4_W4A16, "w4a8": lib.Q4_W4A8, "w8a8": lib.Q4_W8A8}[mode]
+        self.wbits = 8 if mode == "w8a8" else 4
         e, h, i, k = cfg["experts"], cfg["hidden"], cfg["inter"], cfg["top_k"]
         shared = bool(cfg.get("shared", False))
-        self.layer = lib.MoELayer(e, h, i, k, asymmetric=cfg["asymmetric"], shared=shared)
+        self.layer = lib.MoELayer(e, h, i, k, asymmetric=cfg["asymmetric"], shared=shared, weight_bits=self.wbits)
         for j in range(e + (1 if shared else 0)):
             g, u, d = synth.expert_weights(cfg_name, j, device="cuda")
             self.layer.set_expert(j, g, u, d)
@@ -120,10 +121,11 @@ class Workload:
         return n + (1 if self.layer.shared else 0)
 
     def expert_bytes(self):
-        """Canonical packed bytes of one expert: nibbles + fp16 scales (+ zero points)."""
+        """Canonical packed bytes of one expert: codes (4- or 8-bit) + fp16 scales (+ zero points)."""
         h, i = self.cfg["hidden"], self.cfg["inter"]
-        gu = 2 * i * h // 2 + 2 * i * (h // 128) * 2
-        dn = h * i // 2 + h * (i // 128) * 2
+        cb = self.wbits // 4     # code bytes per 2 weights
+        gu = 2 * i * h * cb // 2 + 2 * i * (h // 128) * 2
+        dn = h * i * cb // 2 + h * (i // 128) * 2
         if self.cfg["asymmetric"]:
             gu += 2 * i * ((h // 128 + 1) // 2)
             dn += h * ((i // 128 + 1) // 2)
@@ -250,10 +252,11 @@ def summarize(wl, sec_per_step, stage_ms):
         "stage_ms": {k: round(v, 5) for k, v in stage_ms.items()},
     }
     flops = wl.flops()
-    peak = INT8_PEAK_TOPS if wl.mode == wl.lib.Q4_W4A8 else BF16_PEAK_TFLOPS
+    int8 = wl.mode in (wl.lib.Q4_W4A8, wl.lib.Q4_W8A8)
+    peak = INT8_PEAK_TOPS if int8 else BF16_PEAK_TFLOPS
     res["mfma_frac"] = flops / sec_per_step / 1e12 / peak
     if "gate_up" in stage_ms:
-        act = rows * h * (1 if wl.mode == wl.lib.Q4_W4A8 else 2) + rows * i * (4 if wl.mode == wl.lib.Q4_W4A8 else 2)
+        act = rows * h * (1 if int8 else 2) + rows * i * (4 if int8 else 2)
         res["gate_up_bytes"] = touched * gu_b + act
         res["gate_up_GBps"] = res["gate_up_bytes"] / (stage_ms["gate_up"] * 1e-3) / 1e9
         res["gate_up_flops"] = 2.0 * rows * 2 * i * h
@@ -349,11 +352,19 @@ def main():
             s4, _ = time_steps(torch, lw, 20 if t > 1000 else 50, 5, stage_events=False, graph=not args.no_graph)
             extra[f"lora8_T{t}_w4a16"] = lw.summary(s4)
             del lw
-        log("[bench] extra moe8 W4A8 prefill T=2048")
-        w8 = Workload(lib, torch, synth, "moe8_w4a8", 2048, "w4a8")
-        s3, st3 = time_steps(torch, w8, 20, 5, stage_events=True, graph=not args.no_graph)
-        extra["moe8_T2048_w4a8"] = summarize(w8, s3, st3)
-        del w8
+        for mode in ("w4a8", "w8a8"):
+            log(f"[bench] extra moe8 {mode} prefill T=2048")
+            w8 = Workload(lib, torch, synth, "moe8_w4a8", 2048, mode)
+            s3, st3 = time_steps(torch, w8, 20, 5, stage_events=True, graph=not args.no_graph)
+            extra[f"moe8_T2048_{mode}"] = summarize(w8, s3, st3)
+            del w8
+        if args.mode != "w8a8":
+            log(f"[bench] extra moe256 W8A8 T={args.tokens}")
+            w8 = Workload(lib, torch, synth, "moe256", args.tokens, "w8a8")
+            s5, st5 = time_steps(torch, w8, 50, 5, stage_events=True, graph=not args.no_graph)
+            extra[f"moe256_T{args.tokens}_w8a8"] = summarize(w8, s5, st5)
+            del w8
+            torch.cuda.empty_cache()
 
     if args.copy_calibration:
         n = 512 * 1024 * 1024

@@ -68,6 +68,7 @@ extern "C" {
 /* forward modes */
 #define Q4_W4A16 0 /* weights dequantised in-kernel, bf16 activations, fp32 accumulate */
 #define Q4_W4A8 1  /* per-token INT8 activations x INT4->INT8 weights, INT32 per group   */
+#define Q4_W8A8 2  /* per-token INT8 activations x INT8 weights (weight_bits == 8)        */
 
 /* repack flags */
 #define Q4_REPACK_PLAIN 0
@@ -136,6 +137,28 @@ Q4_API int q4_repack_device(const uint8_t* packed, const uint16_t* scales, const
                      size_t dev_bytes, hipStream_t stream);
 
 /*
+ * quantize_int8_g128 / q8_device_bytes / q8_repack_device -- INT8 g128 weights for the
+ * W8A8 comparison route (page "MoE推理优化实战：4bit存储+INT8计算的W4A8路线解析":
+ * W8A8 = INT8 weights and INT8 compute, the accuracy-safe route to set up first).
+ * The same group structure as the INT4 format: per row and group of 128,
+ * s = binary16 rounded up of fp32(amax) / 127, q = clamp(rint(w / s), -127, 127)
+ * (IEEE fp32 division by the stored scale, half-to-even); a zero scale gives codes 0.
+ *  q       device [n][k] int8 codes (canonical), scales device [n][k/128] binary16 bits.
+ *  flags_dev as for quantize_int4_g128.
+ * Device layout: one 2048-byte tile per (16-column block cb, group g), cb-major; the
+ * tile is two 1024-byte halves (k in [128 g + 64 i, 128 g + 64 i + 64)), and inside a
+ * half lane L (column L % 16, quarter kq = L / 16) owns 16 bytes: bytes 0..7 are
+ * k = 128 g + 64 i + 8 kq + e, bytes 8..15 the same k + 32 (e in [0, 8)); scales
+ * binary16 [n/16][k/128][16] at byte align256(n k).  Column orders as for
+ * q4_repack_device (Q4_REPACK_PLAIN / Q4_REPACK_GATE_UP).
+ */
+Q4_API int quantize_int8_g128(const void* w, int w_dtype, int64_t n, int64_t k, int8_t* q,
+                       uint16_t* scales, int32_t* flags_dev, hipStream_t stream);
+Q4_API size_t q8_device_bytes(int64_t n, int64_t k);
+Q4_API int q8_repack_device(const int8_t* q, const uint16_t* scales, int64_t n, int64_t k, int flags,
+                     void* dev_out, size_t dev_bytes, hipStream_t stream);
+
+/*
  * moe_route_topk -- A3 + A4: fp32 router logits, top-k and renormalised weights.
  * (Dense/MoE page, MoE section: a Linear router; W4A8 page §3.2: router kept in float.)
  *
@@ -185,6 +208,8 @@ Q4_API int act_quant_int8(const void* x, int x_dtype, int64_t rows, int64_t cols
  *           each repacked with Q4_REPACK_GATE_UP from the expert's [gate; up] rows.
  *  down:    num_experts consecutive blocks of q4_device_bytes(H, I, asymmetric) bytes
  *           (Q4_REPACK_PLAIN).
+ *  (weight_bits == 8: the blocks are q8_device_bytes(2I, H) / q8_device_bytes(H, I)
+ *           bytes of q8_repack_device output instead.)
  *  shared_inter: 0 = no shared expert; else the shared expert's intermediate size,
  *           which must equal inter in this build; shared_gate_up / shared_down are
  *           one block each, laid out as above.
@@ -200,6 +225,8 @@ typedef struct q4_moe_layer_t {
   const void* down;
   const void* shared_gate_up;
   const void* shared_down;
+  int32_t weight_bits;   /* 0 or 4: INT4 device layout (modes W4A16 / W4A8); 8: INT8 device
+                            layout of q8_repack_device, symmetric, mode Q4_W8A8 only */
 } q4_moe_layer_t;
 
 /*
@@ -210,6 +237,7 @@ typedef struct q4_moe_layer_t {
  *   accumulation, one fp32 scale step per group; h rounded to bf16.
  * W4A8: x quantised per token and h per (token, choice) row to INT8 (amax / 127);
  *   INT32 accumulation per group of int8(x) * (q - z); y = s_x * sum_g s_w * acc.
+ * W8A8 (layer weight_bits == 8): the same with the 8-bit codes q.
  * The combine adds the k routed outputs in ascending j in fp32, then the shared
  * expert, then rounds to bf16.  A dense SwiGLU FFN is the case num_experts = 1,
  * top_k = 1, topk_w = 1.
@@ -325,6 +353,16 @@ Q4_API int int4_linear_forward(const void* x, int x_dtype, int64_t t, int64_t k,
  */
 Q4_API int int4_w4a8_group_acc(const int8_t* q, int64_t rows, int64_t k, const void* w_dev, int64_t n,
                         int asymmetric, int32_t* acc, hipStream_t stream);
+
+/*
+ * int8_w8a8_group_acc -- the INT32 group accumulators of the W8A8 core,
+ * acc[r][c][g] = sum_{k in group g} q[r][k] * code[c][k], same MFMA core as the forward.
+ *  q      device [rows][k] int8 activation codes.
+ *  w_dev  q8_repack_device output (Q4_REPACK_PLAIN) of an [n][k] matrix.
+ *  acc    device [rows][n][k/128] int32.   Requires k % 128 == 0, n % 64 == 0.
+ */
+Q4_API int int8_w8a8_group_acc(const int8_t* q, int64_t rows, int64_t k, const void* w_dev, int64_t n,
+                        int32_t* acc, hipStream_t stream);
 
 /*
  * q4_set_stage_events -- optional per-stage timing markers for profiling tools.

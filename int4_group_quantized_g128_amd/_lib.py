@@ -25,7 +25,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 Q4_OK, Q4_ERR_NULL, Q4_ERR_SHAPE, Q4_ERR_ALIGN, Q4_ERR_DTYPE = 0, 1, 2, 3, 4
 Q4_ERR_WORKSPACE, Q4_ERR_UNSUPPORTED, Q4_ERR_HIP = 5, 6, 7
 Q4_F32, Q4_F16, Q4_BF16 = 0, 1, 2
-Q4_W4A16, Q4_W4A8 = 0, 1
+Q4_W4A16, Q4_W4A8, Q4_W8A8 = 0, 1, 2
 Q4_REPACK_PLAIN, Q4_REPACK_GATE_UP = 0, 1
 Q4_QFLAG_NONFINITE, Q4_QFLAG_SCALE_OVERFLOW = 1, 2
 
@@ -39,6 +39,7 @@ class Q4MoELayer(ctypes.Structure):
         ("num_experts", _i32), ("hidden", _i32), ("inter", _i32), ("top_k", _i32),
         ("asymmetric", _i32), ("shared_inter", _i32),
         ("gate_up", _vp), ("down", _vp), ("shared_gate_up", _vp), ("shared_down", _vp),
+        ("weight_bits", _i32),
     ]
 
 
@@ -74,6 +75,10 @@ _sig("q4_version", ctypes.c_char_p, [])
 _sig("quantize_int4_g128", _int, [_vp, _int, _i64, _i64, _int, _vp, _vp, _vp, _vp, _vp])
 _sig("q4_device_bytes", _sz, [_i64, _i64, _int])
 _sig("q4_repack_device", _int, [_vp, _vp, _vp, _i64, _i64, _int, _int, _vp, _sz, _vp])
+_sig("quantize_int8_g128", _int, [_vp, _int, _i64, _i64, _vp, _vp, _vp, _vp])
+_sig("q8_device_bytes", _sz, [_i64, _i64])
+_sig("q8_repack_device", _int, [_vp, _vp, _i64, _i64, _int, _vp, _sz, _vp])
+_sig("int8_w8a8_group_acc", _int, [_vp, _i64, _i64, _vp, _i64, _vp, _vp])
 _sig("moe_route_workspace_bytes", _sz, [_i64, _i64, _i32])
 _sig("moe_route_topk", _int, [_vp, _vp, _vp, _i64, _i64, _i32, _i32, _vp, _vp, _vp, _vp, _sz, _vp])
 _sig("moe_permute", _int, [_vp, _i64, _i32, _i32, _vp, _vp, _vp, _vp, _vp])
@@ -149,6 +154,33 @@ def set_stage_events(begin, end):
 
 
 # ------------------------------------------------------------------ A1 / A2
+def quantize_int8_g128(w, flags=None):
+    """INT8 g128 quantisation (the W8A8 weight format) of w [n, k] -> (q int8 [n, k],
+    scales int16 [n, k/128] (binary16 bits))."""
+    _need(w, (torch.float32, torch.float16, torch.bfloat16), "w", 2)
+    n, k = w.shape
+    q = torch.empty((n, k), dtype=torch.int8, device=w.device)
+    scales = torch.empty((n, max(k // 128, 1)), dtype=torch.int16, device=w.device)
+    _check("quantize_int8_g128", _lib.quantize_int8_g128(
+        _ptr(w), _DT[w.dtype], n, k, _ptr(q), _ptr(scales), _ptr(flags), _stream()))
+    return q, scales
+
+
+def q8_device_bytes(n, k):
+    return int(_lib.q8_device_bytes(n, k))
+
+
+def q8_repack_device(q, scales, n, k, gate_up=False, out=None):
+    """INT8 codes + scales -> device tiles (uint8 tensor of q8_device_bytes(n, k))."""
+    nbytes = q8_device_bytes(n, k)
+    if out is None:
+        out = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    _check("q8_repack_device", _lib.q8_repack_device(
+        _ptr(q), _ptr(scales), n, k, Q4_REPACK_GATE_UP if gate_up else Q4_REPACK_PLAIN, _ptr(out), out.numel(),
+        _stream()))
+    return out
+
+
 def quantize_int4_g128(w, asymmetric=False, flags=None):
     """Canonical INT4 g128 quantisation of w [n, k] -> (packed u8 [n, k/2],
     scales int16 [n, k/128] (binary16 bits), zeros u8 [n, ceil(G/2)] or None)."""
@@ -232,12 +264,20 @@ def act_quant_int8(x):
 class MoELayer:
     """Device-resident INT4 MoE layer (stacked experts in the device tile layout)."""
 
-    def __init__(self, num_experts, hidden, inter, top_k, asymmetric=False, shared=False, device="cuda"):
+    def __init__(self, num_experts, hidden, inter, top_k, asymmetric=False, shared=False, device="cuda",
+                 weight_bits=4):
         self.num_experts, self.hidden, self.inter, self.top_k = num_experts, hidden, inter, top_k
         self.asymmetric = bool(asymmetric)
         self.shared = bool(shared)
-        self.gu_bytes = q4_device_bytes(2 * inter, hidden, asymmetric)
-        self.dn_bytes = q4_device_bytes(hidden, inter, asymmetric)
+        if weight_bits not in (4, 8) or (weight_bits == 8 and asymmetric):
+            raise ValueError("weight_bits must be 4, or 8 with symmetric weights")
+        self.weight_bits = weight_bits
+        if weight_bits == 8:
+            self.gu_bytes = q8_device_bytes(2 * inter, hidden)
+            self.dn_bytes = q8_device_bytes(hidden, inter)
+        else:
+            self.gu_bytes = q4_device_bytes(2 * inter, hidden, asymmetric)
+            self.dn_bytes = q4_device_bytes(hidden, inter, asymmetric)
         if self.gu_bytes == 0 or self.dn_bytes == 0:
             raise ValueError("hidden and inter must be multiples of 128")
         self.gate_up = torch.empty(num_experts * self.gu_bytes, dtype=torch.uint8, device=device)
@@ -247,7 +287,7 @@ class MoELayer:
         self.desc = Q4MoELayer(num_experts, hidden, inter, top_k, int(self.asymmetric),
                                inter if shared else 0, self.gate_up.data_ptr(), self.down.data_ptr(),
                                self.shared_gate_up.data_ptr() if shared else None,
-                               self.shared_down.data_ptr() if shared else None)
+                               self.shared_down.data_ptr() if shared else None, weight_bits)
 
     def weight_bytes(self):
         """Device bytes of all expert weights."""
@@ -260,6 +300,19 @@ class MoELayer:
             _need(t, (torch.float32, torch.float16, torch.bfloat16), name, 2)
             if tuple(t.shape) != shape:
                 raise ValueError(f"{name} must be {shape}, got {tuple(t.shape)}")
+        if e == self.num_experts:
+            if not self.shared:
+                raise ValueError("layer has no shared expert")
+            gu_out, dn_out = self.shared_gate_up, self.shared_down
+        else:
+            gu_out = self.gate_up[e * self.gu_bytes:(e + 1) * self.gu_bytes]
+            dn_out = self.down[e * self.dn_bytes:(e + 1) * self.dn_bytes]
+        if self.weight_bits == 8:
+            q, s = quantize_int8_g128(torch.cat([gate, up], dim=0).contiguous())
+            q8_repack_device(q, s, 2 * I, H, gate_up=True, out=gu_out)
+            q, s = quantize_int8_g128(down.contiguous())
+            q8_repack_device(q, s, H, I, gate_up=False, out=dn_out)
+            return
         g = H // 128
         dev = gate.device
         packed = torch.empty((2 * I, H // 2), dtype=torch.uint8, device=dev)
@@ -270,13 +323,6 @@ class MoELayer:
             _check("quantize_int4_g128", _lib.quantize_int4_g128(
                 _ptr(w), _DT[w.dtype], I, H, int(self.asymmetric), _ptr(packed[sl]), _ptr(scales[sl]),
                 _ptr(zeros[sl]) if zeros is not None else ctypes.c_void_p(0), ctypes.c_void_p(0), _stream()))
-        if e == self.num_experts:
-            if not self.shared:
-                raise ValueError("layer has no shared expert")
-            gu_out, dn_out = self.shared_gate_up, self.shared_down
-        else:
-            gu_out = self.gate_up[e * self.gu_bytes:(e + 1) * self.gu_bytes]
-            dn_out = self.down[e * self.dn_bytes:(e + 1) * self.dn_bytes]
         q4_repack_device(packed, scales, zeros, 2 * I, H, self.asymmetric, gate_up=True, out=gu_out)
         dp, ds, dz = quantize_int4_g128(down, self.asymmetric)
         q4_repack_device(dp, ds, dz, H, I, self.asymmetric, gate_up=False, out=dn_out)
@@ -430,6 +476,18 @@ def int4_linear_forward(x, w_dev, n, asymmetric=False):
     _check("int4_linear_forward", _lib.int4_linear_forward(
         _ptr(x), _DT[x.dtype], t, k, _ptr(w_dev), n, int(bool(asymmetric)), _ptr(y), _stream()))
     return y
+
+
+def int8_w8a8_group_acc(q, w_dev, n):
+    """INT32 group accumulators acc [rows, n, k/128] of int8 codes q [rows, k] with
+    8-bit weights (q8_repack_device output)."""
+    _need(q, torch.int8, "q", 2)
+    _need(w_dev, torch.uint8, "w_dev")
+    rows, k = q.shape
+    acc = torch.empty((rows, n, k // 128), dtype=torch.int32, device=q.device)
+    _check("int8_w8a8_group_acc", _lib.int8_w8a8_group_acc(
+        _ptr(q), rows, k, _ptr(w_dev), n, _ptr(acc), _stream()))
+    return acc
 
 
 def int4_w4a8_group_acc(q, w_dev, n, asymmetric=False):

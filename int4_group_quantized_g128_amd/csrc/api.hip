@@ -72,6 +72,14 @@ struct FwdWorkspace {
   int tile_rows = 16;
 };
 
+bool int8_acts(int mode) { return mode == Q4_W4A8 || mode == Q4_W8A8; }
+int wbits_of(const q4_moe_layer_t* L) { return L->weight_bits == 8 ? 8 : 4; }
+
+// Device bytes of one [n][k] expert matrix in the layer's weight format.
+int64_t mat_bytes(const q4_moe_layer_t* L, int64_t n, int64_t k) {
+  return wbits_of(L) == 8 ? int64_t(q8_device_bytes(n, k)) : int64_t(q4_device_bytes(n, k, L->asymmetric));
+}
+
 // Average routed rows per expert decides the GEMM shape: 16-row decode tiles, 32 / 64-row
 // mid tiles, or the 128-row prefill kernel.
 double avg_rows(const q4_moe_layer_t* L, int64_t t) { return double(t) * L->top_k / L->num_experts; }
@@ -84,11 +92,11 @@ int row_blocks_for(const q4_moe_layer_t* L, int64_t t) {
 }
 
 bool use_prefill(const q4_moe_layer_t* L, int64_t t, int mode) {
-  const int act = mode == Q4_W4A8 ? 2 : 0;
+  const int act = int8_acts(mode) ? 2 : 0;
   const int64_t S = L->top_k + (L->shared_inter > 0 ? 1 : 0);
   return avg_rows(L, t) >= 64 && (2 * int64_t(L->inter)) % 128 == 0 && L->hidden % 128 == 0 &&
-         prefill_fits(t, L->hidden, act, int64_t(q4_device_bytes(2 * L->inter, L->hidden, L->asymmetric))) &&
-         prefill_fits(t * S, L->inter, act, int64_t(q4_device_bytes(L->hidden, L->inter, L->asymmetric)));
+         prefill_fits(t, L->hidden, act, mat_bytes(L, 2 * L->inter, L->hidden)) &&
+         prefill_fits(t * S, L->inter, act, mat_bytes(L, L->hidden, L->inter));
 }
 
 FwdWorkspace carve(const q4_moe_layer_t* L, int64_t t, int mode, void* base) {
@@ -113,9 +121,9 @@ FwdWorkspace carve(const q4_moe_layer_t* L, int64_t t, int mode, void* base) {
   w.inv = reinterpret_cast<int32_t*>(take(P * 4));
   w.tiles = reinterpret_cast<TileDesc*>(take(int64_t(w.max_tiles) * sizeof(TileDesc)));
   w.num_tiles = reinterpret_cast<int32_t*>(take(4));
-  w.h = take(P * I * (mode == Q4_W4A8 ? 4 : 2));
+  w.h = take(P * I * (int8_acts(mode) ? 4 : 2));
   w.y = reinterpret_cast<float*>(take(P * H * 4));
-  if (mode == Q4_W4A8) {
+  if (int8_acts(mode)) {
     w.qx = reinterpret_cast<int8_t*>(take(t * H));
     w.sx = reinterpret_cast<float*>(take(t * 4));
     w.qh = reinterpret_cast<int8_t*>(take(P * I));
@@ -142,6 +150,9 @@ int validate_layer(const q4_moe_layer_t* L) {
   Q4_REQUIRE(L->asymmetric == 0 || L->asymmetric == 1, Q4_ERR_SHAPE, "asymmetric must be 0 or 1");
   Q4_REQUIRE(L->gate_up && L->down, Q4_ERR_NULL, "expert weight pointers are NULL");
   Q4_REQUIRE(!misaligned(L->gate_up) && !misaligned(L->down), Q4_ERR_ALIGN, "expert weights not 16-byte aligned");
+  Q4_REQUIRE(L->weight_bits == 0 || L->weight_bits == 4 || L->weight_bits == 8, Q4_ERR_SHAPE,
+             "weight_bits %d not in {0, 4, 8}", L->weight_bits);
+  Q4_REQUIRE(L->weight_bits != 8 || L->asymmetric == 0, Q4_ERR_UNSUPPORTED, "8-bit weights are symmetric only");
   if (L->shared_inter != 0) {
     Q4_REQUIRE(L->shared_inter == L->inter, Q4_ERR_UNSUPPORTED,
                "shared_inter %d must equal inter %d in this build", L->shared_inter, L->inter);
@@ -230,6 +241,36 @@ int q4_repack_device(const uint8_t* packed, const uint16_t* scales, const uint8_
                    "repack launch");
 }
 
+int quantize_int8_g128(const void* w, int w_dtype, int64_t n, int64_t k, int8_t* q, uint16_t* scales,
+                       int32_t* flags_dev, hipStream_t stream) {
+  g_last_error.clear();
+  Q4_REQUIRE(w_dtype == Q4_F32 || w_dtype == Q4_F16 || w_dtype == Q4_BF16, Q4_ERR_DTYPE, "w_dtype %d", w_dtype);
+  Q4_REQUIRE(n >= 1 && k >= 128 && k % 128 == 0, Q4_ERR_SHAPE, "need n >= 1 and k a positive multiple of 128");
+  Q4_REQUIRE(n * (k / 128) < (int64_t(1) << 31), Q4_ERR_SHAPE, "matrix too large");
+  Q4_REQUIRE(w && q && scales, Q4_ERR_NULL, "w, q and scales are required");
+  Q4_REQUIRE(!misaligned(w) && !misaligned(q) && !misaligned(scales), Q4_ERR_ALIGN,
+             "device pointers must be 16-byte aligned");
+  return check_hip(launch_quantize8(w, w_dtype, n, k, q, scales, flags_dev, stream), "quantize8 launch");
+}
+
+size_t q8_device_bytes(int64_t n, int64_t k) {
+  if (n < 16 || n % 16 || k < 128 || k % 128) return 0;
+  return size_t(a256(n * k) + a256(2 * n * (k / 128)));
+}
+
+int q8_repack_device(const int8_t* q, const uint16_t* scales, int64_t n, int64_t k, int flags, void* dev_out,
+                     size_t dev_bytes, hipStream_t stream) {
+  g_last_error.clear();
+  Q4_REQUIRE(flags == Q4_REPACK_PLAIN || flags == Q4_REPACK_GATE_UP, Q4_ERR_DTYPE, "flags %d", flags);
+  Q4_REQUIRE(k >= 128 && k % 128 == 0 && n >= 16 && n % (flags == Q4_REPACK_GATE_UP ? 32 : 16) == 0,
+             Q4_ERR_SHAPE, "need k %% 128 == 0 and n %% %d == 0", flags == Q4_REPACK_GATE_UP ? 32 : 16);
+  Q4_REQUIRE(q && scales && dev_out, Q4_ERR_NULL, "q, scales and dev_out are required");
+  Q4_REQUIRE(!misaligned(q) && !misaligned(dev_out), Q4_ERR_ALIGN, "device pointers must be 16-byte aligned");
+  Q4_REQUIRE(dev_bytes >= q8_device_bytes(n, k), Q4_ERR_WORKSPACE, "dev_out holds %zu bytes, need %zu", dev_bytes,
+             q8_device_bytes(n, k));
+  return check_hip(launch_repack8(q, scales, n, k, flags == Q4_REPACK_GATE_UP, dev_out, stream), "repack8 launch");
+}
+
 size_t moe_route_workspace_bytes(int64_t t, int64_t h, int32_t e) {
   if (t <= 0 || h <= 0 || e <= 0) return 0;
   return size_t(route_kslices(t, h, e)) * size_t(t) * size_t(e) * sizeof(float);
@@ -274,7 +315,8 @@ int act_quant_int8(const void* x, int x_dtype, int64_t rows, int64_t cols, int8_
 }
 
 size_t moe_int4_ffn_workspace_bytes(const q4_moe_layer_t* layer, int64_t t, int mode) {
-  if (!layer || t < 0 || (mode != Q4_W4A16 && mode != Q4_W4A8) || validate_layer(layer) != Q4_OK) return 0;
+  if (!layer || t < 0 || validate_layer(layer) != Q4_OK) return 0;
+  if (wbits_of(layer) == 8 ? mode != Q4_W8A8 : (mode != Q4_W4A16 && mode != Q4_W4A8)) return 0;
   return size_t(carve(layer, t, mode, nullptr).bytes);
 }
 
@@ -286,7 +328,8 @@ int ffn_forward(const q4_moe_layer_t* L, const uint16_t* x_bf16, int64_t t, cons
   g_last_error.clear();
   if (views) *views = q4_ffn_views_t{};
   if (int rc = validate_layer(L)) return rc;
-  Q4_REQUIRE(mode == Q4_W4A16 || mode == Q4_W4A8, Q4_ERR_DTYPE, "mode %d", mode);
+  Q4_REQUIRE(wbits_of(L) == 8 ? mode == Q4_W8A8 : (mode == Q4_W4A16 || mode == Q4_W4A8), Q4_ERR_DTYPE,
+             "mode %d does not match weight_bits %d", mode, L->weight_bits);
   Q4_REQUIRE(t >= 0, Q4_ERR_SHAPE, "t < 0");
   if (t == 0) return ok();
   const int shared = L->shared_inter > 0 ? 1 : 0;
@@ -304,7 +347,7 @@ int ffn_forward(const q4_moe_layer_t* L, const uint16_t* x_bf16, int64_t t, cons
     views->perm = w.perm;
     views->inv = w.inv;
     views->h = w.h;
-    views->h_is_f32 = mode == Q4_W4A8 ? 1 : 0;
+    views->h_is_f32 = int8_acts(mode) ? 1 : 0;
     views->slots_per_token = int32_t(S);
     views->positions = t * S;
     views->y = w.y;
@@ -326,7 +369,8 @@ int ffn_forward(const q4_moe_layer_t* L, const uint16_t* x_bf16, int64_t t, cons
   gu.perm = w.perm;
   gu.slots_per_token = int32_t(S);
   gu.w = static_cast<const uint8_t*>(L->gate_up);
-  gu.w_stride = int64_t(q4_device_bytes(2 * I, H, L->asymmetric));
+  gu.w_stride = mat_bytes(L, 2 * I, H);
+  gu.wbits = wbits_of(L);
   gu.w_shared = static_cast<const uint8_t*>(L->shared_gate_up);
   gu.num_experts = L->num_experts;
   gu.asym = L->asymmetric;
@@ -341,7 +385,7 @@ int ffn_forward(const q4_moe_layer_t* L, const uint16_t* x_bf16, int64_t t, cons
   dn.a_rows = t * S;
   dn.perm = nullptr;
   dn.w = static_cast<const uint8_t*>(L->down);
-  dn.w_stride = int64_t(q4_device_bytes(H, I, L->asymmetric));
+  dn.w_stride = mat_bytes(L, H, I);
   dn.w_shared = static_cast<const uint8_t*>(L->shared_down);
   dn.N = H;
   dn.K = I;
@@ -573,6 +617,27 @@ int int4_linear_forward(const void* x, int x_dtype, int64_t t, int64_t k, const 
   g.out = y;
   const int rb = t <= 16 ? 1 : (t <= 32 ? 2 : 4);
   return check_hip(launch_gemm(g, x_dtype == Q4_F16 ? 1 : 0, GEMM_PLAIN, rb, stream), "linear gemm");
+}
+
+int int8_w8a8_group_acc(const int8_t* q, int64_t rows, int64_t k, const void* w_dev, int64_t n, int32_t* acc,
+                        hipStream_t stream) {
+  g_last_error.clear();
+  Q4_REQUIRE(rows >= 0 && k >= 128 && k % 128 == 0 && n >= 64 && n % 64 == 0, Q4_ERR_SHAPE,
+             "need k %% 128 == 0 and n %% 64 == 0");
+  if (rows == 0) return ok();
+  Q4_REQUIRE(q && w_dev && acc, Q4_ERR_NULL, "missing pointer");
+  Q4_REQUIRE(!misaligned(q) && !misaligned(w_dev), Q4_ERR_ALIGN, "pointers must be 16-byte aligned");
+  GemmArgs g{};
+  g.a = q;
+  g.w = static_cast<const uint8_t*>(w_dev);
+  g.num_experts = 1;
+  g.wbits = 8;
+  g.N = n;
+  g.K = k;
+  g.dense_rows = rows;
+  g.a_rows = rows;
+  g.acc_out = acc;
+  return check_hip(launch_gemm(g, 2, GEMM_GROUP_ACC, 1, stream), "group acc gemm");
 }
 
 int int4_w4a8_group_acc(const int8_t* q, int64_t rows, int64_t k, const void* w_dev, int64_t n, int asymmetric,

@@ -101,10 +101,13 @@ struct RowInfo {
 //  MB  16-row blocks per tile (rows of one expert, gathered through perm),
 //  KW  waves of the workgroup that split the K groups (reduced through LDS),
 //  NBW 16-column blocks per wave (the workgroup covers (4 / KW) * NBW blocks),
-//  D   depth of the register pipeline (groups whose loads are in flight).
+//  D   depth of the register pipeline (groups whose loads are in flight),
+//  W8  8-bit weights (2 KB tiles, int8 activations, no widening) instead of 4-bit.
 // The workgroup's scales (and zero points) are staged in LDS once per work item.
-template <Act A, int KIND, bool ASYM, int MB, int KW, int NBW, int D>
+template <Act A, int KIND, bool ASYM, int MB, int KW, int NBW, int D, bool W8>
 __global__ void __launch_bounds__(256) k_gemm(GemmArgs args) {
+  static_assert(!W8 || (A == Act::I8 && !ASYM), "8-bit weights: symmetric, int8 activations");
+  constexpr int64_t TB = W8 ? 2 * kTileBytes : kTileBytes;   // bytes per (column block, group) tile
   constexpr int kColGroups = 4 / KW;
   constexpr int kCBWG = kColGroups * NBW;  // column blocks per workgroup
   extern __shared__ __align__(16) uint8_t smem[];
@@ -117,7 +120,7 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs args) {
   const int64_t tile_rows = 16 * MB;
   const int64_t ntiles = args.tiles ? int64_t(*args.num_tiles) : (args.dense_rows + tile_rows - 1) / tile_rows;
   const int64_t items = ntiles * nblk;
-  const int64_t w_scale_off = align256(N * K / 2);
+  const int64_t w_scale_off = align256(W8 ? N * K : N * K / 2);
   const int64_t w_zero_off = w_scale_off + align256(2 * N * G);
   const int64_t gper = (G + KW - 1) / KW;
   const int64_t g_beg = std::min<int64_t>(G, kw * gper), g_end = std::min<int64_t>(G, g_beg + gper);
@@ -170,7 +173,7 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs args) {
     // per-item base pointers; each group then only adds a constant stride
     const uint8_t* wp[NBW];
 #pragma unroll
-    for (int nb = 0; nb < NBW; ++nb) wp[nb] = wbase + ((cb0 + lcb + nb) * G) * kTileBytes + lane * 16;
+    for (int nb = 0; nb < NBW; ++nb) wp[nb] = wbase + ((cb0 + lcb + nb) * G) * TB + lane * 16;
     const uint8_t* ap[MB];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
@@ -184,14 +187,18 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs args) {
       for (int nb = 0; nb < NBW; ++nb) acc[mb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
     struct Stage {
-      uint32_t wv[NBW][4];
+      uint32_t wv[NBW][W8 ? 8 : 4];
       uint32_t av[MB][4][4];
     };
     auto load_stage = [&](Stage& st, int g) {
 #pragma unroll
       for (int nb = 0; nb < NBW; ++nb) {
-        const uint4 v = load16_stream(wp[nb] + g * kTileBytes);
+        const uint4 v = load16_stream(wp[nb] + g * TB);
         st.wv[nb][0] = v.x; st.wv[nb][1] = v.y; st.wv[nb][2] = v.z; st.wv[nb][3] = v.w;
+        if constexpr (W8) {
+          const uint4 v2 = load16_stream(wp[nb] + g * TB + kTileBytes);
+          st.wv[nb][4] = v2.x; st.wv[nb][5] = v2.y; st.wv[nb][6] = v2.z; st.wv[nb][7] = v2.w;
+        }
       }
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
@@ -290,10 +297,17 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs args) {
 #pragma unroll
         for (int nb = 0; nb < NBW; ++nb) {
           uint32_t b[2][4];
+          if constexpr (W8) {
 #pragma unroll
-          for (int i = 0; i < 2; ++i) {
-            widen_word_i8(st.wv[nb][2 * i], b[i][0], b[i][1]);
-            widen_word_i8(st.wv[nb][2 * i + 1], b[i][2], b[i][3]);
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+              for (int j = 0; j < 4; ++j) b[i][j] = st.wv[nb][4 * i + j];
+          } else {
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+              widen_word_i8(st.wv[nb][2 * i], b[i][0], b[i][1]);
+              widen_word_i8(st.wv[nb][2 * i + 1], b[i][2], b[i][3]);
+            }
           }
           const int32_t zoff = int32_t(zp[nb]) - 8;
 #pragma unroll
@@ -303,7 +317,8 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs args) {
             gacc = mfma_i8_16x16x64(st.av[mb][1], b[1], gacc);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              int32_t a32 = gacc[i] >> 4;                    // exact: gacc = 16 * sum q (d - 8)
+              // 4-bit: exact, gacc = 16 * sum q (d - 8); 8-bit: the group sum itself
+              int32_t a32 = W8 ? gacc[i] : (gacc[i] >> 4);
               if constexpr (ASYM) a32 -= zoff * __shfl(qs[mb], 4 * kq + i, 64);
               if constexpr (KIND == GEMM_GROUP_ACC) {
                 const int64_t r = mb * 16 + 4 * kq + i;
@@ -403,7 +418,7 @@ static size_t gemm_lds_bytes(int64_t K, int asym, int mb, int kw, int nbw) {
   return b;
 }
 
-template <Act A, int KIND, int MB, int KW, int NBW, int D>
+template <Act A, int KIND, int MB, int KW, int NBW, int D, bool W8 = false>
 static hipError_t launch_cfg(const GemmArgs& g, hipStream_t st) {
   constexpr int cbwg = (4 / KW) * NBW;
   const int64_t nblk = g.N / (16 * cbwg);
@@ -417,10 +432,12 @@ static hipError_t launch_cfg(const GemmArgs& g, hipStream_t st) {
   const unsigned grid = unsigned(std::min<int64_t>(items, Q4_GRID_CAP));
   const size_t lds = gemm_lds_bytes(g.K, g.asym, MB, KW, NBW);
   if (lds > 160 * 1024) return hipErrorInvalidValue;  // K too large for the staged scales
-  if (g.asym)
-    hipLaunchKernelGGL((k_gemm<A, KIND, true, MB, KW, NBW, D>), dim3(grid), dim3(256), lds, st, g);
+  if constexpr (W8)
+    hipLaunchKernelGGL((k_gemm<A, KIND, false, MB, KW, NBW, D, true>), dim3(grid), dim3(256), lds, st, g);
+  else if (g.asym)
+    hipLaunchKernelGGL((k_gemm<A, KIND, true, MB, KW, NBW, D, false>), dim3(grid), dim3(256), lds, st, g);
   else
-    hipLaunchKernelGGL((k_gemm<A, KIND, false, MB, KW, NBW, D>), dim3(grid), dim3(256), lds, st, g);
+    hipLaunchKernelGGL((k_gemm<A, KIND, false, MB, KW, NBW, D, false>), dim3(grid), dim3(256), lds, st, g);
   return hipGetLastError();
 }
 
@@ -436,16 +453,16 @@ static hipError_t launch_cfg(const GemmArgs& g, hipStream_t st) {
 #endif
 
 // Configuration table: (MB, KW, NBW, D) by row blocks and the column count.
-template <Act A, int KIND>
+template <Act A, int KIND, bool W8 = false>
 static hipError_t launch_kind(const GemmArgs& g, int rb, int split, hipStream_t st) {
   if (rb <= 1) {
     constexpr int dec_cb = (4 / Q4_DEC_KW) * Q4_DEC_NBW;
-    if (split && g.N % (16 * 2) == 0) return launch_cfg<A, KIND, 1, 4, 2, 2>(g, st);
-    if (g.N % (16 * dec_cb) == 0) return launch_cfg<A, KIND, 1, Q4_DEC_KW, Q4_DEC_NBW, Q4_DEC_D>(g, st);
-    return launch_cfg<A, KIND, 1, 4, 2, 2>(g, st);
+    if (split && g.N % (16 * 2) == 0) return launch_cfg<A, KIND, 1, 4, 2, 2, W8>(g, st);
+    if (g.N % (16 * dec_cb) == 0) return launch_cfg<A, KIND, 1, Q4_DEC_KW, Q4_DEC_NBW, Q4_DEC_D, W8>(g, st);
+    return launch_cfg<A, KIND, 1, 4, 2, 2, W8>(g, st);
   }
-  if (rb <= 2) return launch_cfg<A, KIND, 2, 4, 4, 2>(g, st);
-  return launch_cfg<A, KIND, 4, 4, 4, 2>(g, st);
+  if (rb <= 2) return launch_cfg<A, KIND, 2, 4, 4, 2, W8>(g, st);
+  return launch_cfg<A, KIND, 4, 4, 4, 2, W8>(g, st);
 }
 
 hipError_t launch_gemm(const GemmArgs& g, int act, int kind, int row_blocks, hipStream_t st) {
@@ -457,6 +474,11 @@ hipError_t launch_gemm(const GemmArgs& g, int act, int kind, int row_blocks, hip
     return launch_kind<Act::BF16, GEMM_PLAIN>(g, row_blocks, split, st);
   }
   if (act == 1) return launch_kind<Act::F16, GEMM_PLAIN>(g, row_blocks, split, st);
+  if (g.wbits == 8) {
+    if (kind == GEMM_GATE_UP) return launch_kind<Act::I8, GEMM_GATE_UP, true>(g, row_blocks, split, st);
+    if (kind == GEMM_GROUP_ACC) return launch_cfg<Act::I8, GEMM_GROUP_ACC, 1, 4, 1, 2, true>(g, st);
+    return launch_kind<Act::I8, GEMM_PLAIN, true>(g, row_blocks, split, st);
+  }
   if (kind == GEMM_GATE_UP) return launch_kind<Act::I8, GEMM_GATE_UP>(g, row_blocks, split, st);
   if (kind == GEMM_GROUP_ACC) return launch_cfg<Act::I8, GEMM_GROUP_ACC, 1, 4, 1, 2>(g, st);
   return launch_kind<Act::I8, GEMM_PLAIN>(g, row_blocks, split, st);

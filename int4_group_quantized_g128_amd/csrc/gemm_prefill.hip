@@ -134,16 +134,17 @@ Q4_DEVICE void copy_to_lds(const u32x4_t& rsrc, uint32_t lds_in, uint32_t voff, 
 
 // Per-stage LDS image of one group (K = 128) of one work item:
 //   A tile  [128 rows][ROWB]  (16-byte chunks XOR-swizzled by row)
-//   W tiles [8 column blocks][64 lanes][16 B]  (the device tiles as stored)
+//   W tiles [8 column blocks][TB]  (the device tiles as stored: 1 KB 4-bit, 2 KB 8-bit)
 //   scales  [8][16] fp16, zero points [8][16] u8 (asymmetric)
 //   rsum    [128] fp32 row sums (bf16) / int32 code sums (int8, asymmetric)
-template <Act A>
+template <Act A, bool W8 = false>
 struct PfStage {
   static constexpr int ESZ = (A == Act::I8) ? 1 : 2;
   static constexpr int ROWB = kGroup * ESZ;
   static constexpr int A_BYTES = kPfRows * ROWB;
+  static constexpr int TB = W8 ? 2 * kTileBytes : kTileBytes;
   static constexpr int W_OFF = A_BYTES;
-  static constexpr int S_OFF = W_OFF + kPfCB * kTileBytes;
+  static constexpr int S_OFF = W_OFF + kPfCB * TB;
   static constexpr int Z_OFF = S_OFF + kPfCB * 32;
   static constexpr int R_OFF = S_OFF + 512;
   static constexpr int BYTES = R_OFF + kPfRows * 4;
@@ -176,9 +177,12 @@ Q4_DEVICE ItemRange item_range(int64_t items) {
   return {xcd * chunk + blockIdx.x / 8, last, nwg / 8};
 }
 
-template <Act A, int KIND, bool ASYM>
+template <Act A, int KIND, bool ASYM, bool W8>
 __global__ void __launch_bounds__(256, 1) k_gemm_pf(GemmArgs args) {
-  using St = PfStage<A>;
+  static_assert(!W8 || (A == Act::I8 && !ASYM), "8-bit weights: symmetric, int8 activations");
+  using St = PfStage<A, W8>;
+  constexpr int TB = St::TB;
+  constexpr int WCOPIES = W8 ? 4 : 2;                 // 1 KB weight copies per wave per stage
   constexpr int ROWB = St::ROWB;
   constexpr int CHUNKS = ROWB / 16;                   // 16-byte chunks per row
   constexpr int ROWS_PER_INST = 64 / CHUNKS;          // rows one copy instruction covers
@@ -191,7 +195,7 @@ __global__ void __launch_bounds__(256, 1) k_gemm_pf(GemmArgs args) {
   auto swz = [](int r) -> int { return CHUNKS == 16 ? (r & 15) : ((r >> 1) & 7); };
   // ring of NS stage slots (the loop below is unrolled by NS so every slot offset is a
   // compile-time constant)
-  constexpr int NS = PfStage<A>::SLOTS;
+  constexpr int NS = St::SLOTS;
   __shared__ __align__(16) uint8_t ring[NS * St::BYTES];
   __shared__ float s_sa[kPfRows];   // int8: per-row activation scales of the item
 
@@ -205,7 +209,7 @@ __global__ void __launch_bounds__(256, 1) k_gemm_pf(GemmArgs args) {
   const int G = int(K / kGroup);
   const int64_t nblk = N / (16 * kPfCB);
   const int64_t items = *args.num_tiles * nblk;
-  const int64_t w_scale_off = align256(N * K / 2);
+  const int64_t w_scale_off = align256(W8 ? N * K : N * K / 2);
   const int64_t w_zero_off = w_scale_off + align256(2 * N * int64_t(G));
   const auto a_rsrc = buffer_rsrc(args.a, args.a_rows * K * St::ESZ);
   const void* rs_base = (A == Act::I8) ? static_cast<const void*>(args.a_qsum) : static_cast<const void*>(args.a_gsum);
@@ -233,9 +237,11 @@ __global__ void __launch_bounds__(256, 1) k_gemm_pf(GemmArgs args) {
       const int c = (lane % CHUNKS) ^ swz(r);         // global chunk that lands in this slot
       a_off[j] = uint32_t(src_of(r) * K * St::ESZ + c * 16);
     }
-    uint32_t w_off[2];
+    // weight copies: column blocks 2 wid + (j / (WCOPIES / 2)), 1 KB part j % (WCOPIES / 2)
+    uint32_t w_off[WCOPIES];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) w_off[j] = uint32_t((cb0 + 2 * wid + j) * G * kTileBytes + lane * 16);
+    for (int j = 0; j < WCOPIES; ++j)
+      w_off[j] = uint32_t((cb0 + 2 * wid + j / (WCOPIES / 2)) * G * TB + (j % (WCOPIES / 2)) * kTileBytes + lane * 16);
     // wave 0: scales of the 8 blocks (lanes 0..15, 32 B per block and group) and zero
     // points (lanes 16..23, 16 B per block and group)
     uint32_t m_off = 0, m_step = 0;
@@ -257,8 +263,9 @@ __global__ void __launch_bounds__(256, 1) k_gemm_pf(GemmArgs args) {
       for (int j = 0; j < A_INSTS; ++j)
         copy_to_lds<16>(a_rsrc, base + (32 * wid + ROWS_PER_INST * j) * ROWB, a_off[j], uint32_t(g * ROWB));
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-        copy_to_lds<16>(w_rsrc, base + St::W_OFF + (2 * wid + j) * kTileBytes, w_off[j], uint32_t(g * kTileBytes));
+      for (int j = 0; j < WCOPIES; ++j)
+        copy_to_lds<16>(w_rsrc, base + St::W_OFF + (2 * wid + j / (WCOPIES / 2)) * TB + (j % (WCOPIES / 2)) * kTileBytes,
+                        w_off[j], uint32_t(g * TB));
       if (wid == 0 && (lane < 16 || (ASYM && lane < 24)))
         copy_to_lds<16>(w_rsrc, base + St::S_OFF, m_off + uint32_t(g) * m_step, 0u);
       if constexpr (RSUM) {
@@ -292,10 +299,13 @@ __global__ void __launch_bounds__(256, 1) k_gemm_pf(GemmArgs args) {
       auto pin = [](const f32x4_t& v) { asm volatile("" ::"v"(v[0]), "v"(v[1]), "v"(v[2]), "v"(v[3])); };
       auto pass = [](u32x4_t& x) { asm volatile("" : "+v"(x)); };
       auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
-      uint4 wraw[4];
+      uint4 wraw[4][W8 ? 2 : 1];
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb)
-        wraw[nb] = *reinterpret_cast<const uint4*>(base + St::W_OFF + (wn * 4 + nb) * kTileBytes + lane * 16);
+#pragma unroll
+        for (int hh = 0; hh < (W8 ? 2 : 1); ++hh)
+          wraw[nb][hh] =
+              *reinterpret_cast<const uint4*>(base + St::W_OFF + (wn * 4 + nb) * TB + hh * kTileBytes + lane * 16);
       if constexpr (A == Act::BF16) {
         float sc[4], negz[4];
         u32x4_t b[4][4];
@@ -306,7 +316,7 @@ __global__ void __launch_bounds__(256, 1) k_gemm_pf(GemmArgs args) {
           negz[nb] = -(magic_offset<A>() + (ASYM ? float(s_z[cbl * 16 + col]) : 8.0f));
         }
         auto widen = [&](int nb) {
-          const uint32_t w4[4] = {wraw[nb].x, wraw[nb].y, wraw[nb].z, wraw[nb].w};
+          const uint32_t w4[4] = {wraw[nb][0].x, wraw[nb][0].y, wraw[nb][0].z, wraw[nb][0].w};
 #pragma unroll
           for (int s = 0; s < 4; ++s) {
             uint32_t o[4];
@@ -363,25 +373,31 @@ __global__ void __launch_bounds__(256, 1) k_gemm_pf(GemmArgs args) {
           for (int i = 0; i < 4; ++i) acc[NMB - 1][3][i] = fmaf(sc[3], gl[i], acc[NMB - 1][3][i]);
         }
       } else {
-        // widened codes are 16 (d - 8); s / 16 is exact in fp32, so scaling the raw
-        // accumulator by s / 16 equals scaling the group sum by s
+        // 4-bit: widened codes are 16 (d - 8); s / 16 is exact in fp32, so scaling the
+        // raw accumulator by s / 16 equals scaling the group sum by s.  8-bit: the codes
+        // go to the matrix core as stored, the scale is s.
         float sc16[4];
         int32_t zoff16[4];
         u32x4_t b[4][2];
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb) {
           const int cbl = wn * 4 + nb;
-          sc16[nb] = f16_bits_to_f32(s_sc[cbl * 16 + col]) * 0.0625f;
+          sc16[nb] = f16_bits_to_f32(s_sc[cbl * 16 + col]) * (W8 ? 1.0f : 0.0625f);
           zoff16[nb] = ASYM ? 16 * (int32_t(s_z[cbl * 16 + col]) - 8) : 0;
         }
         auto widen = [&](int nb) {
-          uint32_t o[8];
-          widen_word_i8(wraw[nb].x, o[0], o[1]);
-          widen_word_i8(wraw[nb].y, o[2], o[3]);
-          widen_word_i8(wraw[nb].z, o[4], o[5]);
-          widen_word_i8(wraw[nb].w, o[6], o[7]);
-          b[nb][0] = u32x4_t{o[0], o[1], o[2], o[3]};
-          b[nb][1] = u32x4_t{o[4], o[5], o[6], o[7]};
+          if constexpr (W8) {
+            b[nb][0] = u32x4_t{wraw[nb][0].x, wraw[nb][0].y, wraw[nb][0].z, wraw[nb][0].w};
+            b[nb][1] = u32x4_t{wraw[nb][1].x, wraw[nb][1].y, wraw[nb][1].z, wraw[nb][1].w};
+          } else {
+            uint32_t o[8];
+            widen_word_i8(wraw[nb][0].x, o[0], o[1]);
+            widen_word_i8(wraw[nb][0].y, o[2], o[3]);
+            widen_word_i8(wraw[nb][0].z, o[4], o[5]);
+            widen_word_i8(wraw[nb][0].w, o[6], o[7]);
+            b[nb][0] = u32x4_t{o[0], o[1], o[2], o[3]};
+            b[nb][1] = u32x4_t{o[4], o[5], o[6], o[7]};
+          }
         };
         const int32_t* s_qs = reinterpret_cast<const int32_t*>(base + St::R_OFF);
         auto read_a = [&](int mb, u32x4_t (&af)[2], i32x4_t& qv) {
@@ -445,12 +461,12 @@ __global__ void __launch_bounds__(256, 1) k_gemm_pf(GemmArgs args) {
     // NS-slot ring: while stage g is computed, stages g + 1 .. g + NS - 1 are in flight.
     // The copies of stage g + NS - 1 go to the slot that stage g - 1 used, which every
     // wave has finished reading (barrier at the end of the previous step).  Each wave
-    // issues at least PER = A_INSTS + 2 copies per stage and copies complete in order,
+    // issues at least PER = A_INSTS + WCOPIES copies per stage and copies complete in order,
     // so after step g waiting until n * PER are outstanding (n = stages issued after
     // stage g + 1) leaves stage g + 1 complete; the barrier then publishes every wave's
     // copies.  (The raw barrier carries no wait of its own; the empty asm statements
     // keep the compiler from moving memory accesses across it.)
-    constexpr int PER = A_INSTS + 2;
+    constexpr int PER = A_INSTS + WCOPIES;
     auto sync = [&](int newer) {
       static_assert((NS - 2) * PER < 64, "vmcnt range");
       if (newer >= 2 && NS > 3) wait_vmcnt<(NS > 3 ? 2 * PER : 0)>();
@@ -536,10 +552,16 @@ static hipError_t launch_pf_kind(const GemmArgs& g, hipStream_t st) {
   const int64_t items = int64_t(g.max_tiles) * nblk;
   if (items == 0) return hipSuccess;
   const unsigned grid = unsigned(std::min<int64_t>(items, 256));
+  if constexpr (A == Act::I8) {
+    if (g.wbits == 8) {
+      hipLaunchKernelGGL((k_gemm_pf<A, KIND, false, true>), dim3(grid), dim3(256), 0, st, g);
+      return hipGetLastError();
+    }
+  }
   if (g.asym)
-    hipLaunchKernelGGL((k_gemm_pf<A, KIND, true>), dim3(grid), dim3(256), 0, st, g);
+    hipLaunchKernelGGL((k_gemm_pf<A, KIND, true, false>), dim3(grid), dim3(256), 0, st, g);
   else
-    hipLaunchKernelGGL((k_gemm_pf<A, KIND, false>), dim3(grid), dim3(256), 0, st, g);
+    hipLaunchKernelGGL((k_gemm_pf<A, KIND, false, false>), dim3(grid), dim3(256), 0, st, g);
   return hipGetLastError();
 }
 

@@ -21,6 +21,12 @@ hipError_t launch_quantize(const void* w, int dtype, int64_t n, int64_t k, int a
 hipError_t launch_repack(const uint8_t* packed, const uint16_t* scales, const uint8_t* zeros, int64_t n,
                          int64_t k, int asym, int gate_up, void* out, hipStream_t st);
 
+// INT8 g128 weights (W8A8): quantisation and device tiles (2 KB per (16-column block, group)).
+hipError_t launch_quantize8(const void* w, int dtype, int64_t n, int64_t k, int8_t* q, uint16_t* scales,
+                            int32_t* flags, hipStream_t st);
+hipError_t launch_repack8(const int8_t* q, const uint16_t* scales, int64_t n, int64_t k, int gate_up, void* out,
+                          hipStream_t st);
+
 // Router: fp32 logits split over kslices partial sums, then reduction + top-k.
 int route_kslices(int64_t t, int64_t h, int32_t e);
 hipError_t launch_route(const uint16_t* x, const float* wr, const float* bias, int64_t t, int64_t h,
@@ -53,6 +59,7 @@ struct GemmArgs {
   const uint8_t* w_shared;  // shared expert block (expert index == num_experts) or NULL
   int32_t num_experts;
   int32_t asym;
+  int32_t wbits;          // 4 (INT4 tiles) or 8 (INT8 tiles, int8 activations only)
   int64_t N;              // device columns (2I for gate/up)
   int64_t K;
   // tiles

@@ -170,6 +170,107 @@ __global__ void k_zero_bytes(uint8_t* __restrict__ p, int64_t n) {
     p[i] = 0;
 }
 
+// INT8 g128 (the W8A8 weight format): one wave per (row, group), lane j covers
+// k = 128 g + 2 j and 2 j + 1.  s = binary16 rounded up of fp32(amax) / 127,
+// q = clamp(rint(w / s), -127, 127).
+template <int DT>
+__global__ void __launch_bounds__(64) k_quantize8_g128(const void* __restrict__ w, int64_t n, int64_t k,
+                                                      int8_t* __restrict__ q, uint16_t* __restrict__ scales,
+                                                      int32_t* __restrict__ flags) {
+  const int64_t G = k / kGroup;
+  const int64_t row = int64_t(blockIdx.x) / G, g = int64_t(blockIdx.x) % G;
+  const int lane = threadIdx.x;
+  const int64_t base = row * k + g * kGroup + 2 * lane;
+  float v0, v1;
+  if constexpr (DT == 0) {
+    const float2 p = *reinterpret_cast<const float2*>(static_cast<const float*>(w) + base);
+    v0 = p.x;
+    v1 = p.y;
+  } else {
+    const uint32_t p = *reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(w) + base);
+    if constexpr (DT == 1) {
+      v0 = f16_bits_to_f32(uint16_t(p & 0xffff));
+      v1 = f16_bits_to_f32(uint16_t(p >> 16));
+    } else {
+      v0 = bf16_to_f32(uint16_t(p & 0xffff));
+      v1 = bf16_to_f32(uint16_t(p >> 16));
+    }
+  }
+  int flag = (!__builtin_isfinite(v0) || !__builtin_isfinite(v1)) ? 1 : 0;
+  const float amax = wave_max(fmaxf(fabsf(v0), fabsf(v1)));
+  const uint16_t sb = f32_to_f16_up(__fdiv_rn(amax, 127.0f));
+  if ((sb & 0x7fff) >= 0x7c00) flag |= 2;
+  const float s = f16_bits_to_f32(sb);
+  float q0 = 0.f, q1 = 0.f;
+  if (s > 0.f) {
+    q0 = fminf(fmaxf(rintf(__fdiv_rn(v0, s)), -127.f), 127.f);
+    q1 = fminf(fmaxf(rintf(__fdiv_rn(v1, s)), -127.f), 127.f);
+  }
+  const uint16_t pair = uint16_t((uint32_t(int(q0)) & 0xff) | ((uint32_t(int(q1)) & 0xff) << 8));
+  *reinterpret_cast<uint16_t*>(q + base) = pair;
+  if (lane == 0) scales[row * G + g] = sb;
+  if (flags) {
+    const unsigned long long any = __ballot(flag != 0);
+    if (any) {
+      int all = flag;
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) all |= __shfl_xor(all, o, 64);
+      if (lane == 0) atomicOr(flags, all);
+    }
+  }
+}
+
+// INT8 device tiles: one thread per (tile, half, lane) 16-byte chunk: bytes 0..7 are
+// k = 128 g + 64 half + 8 kq + (0..7), bytes 8..15 the same + 32, of device column
+// 16 cb + lane % 16.
+__global__ void k_repack8_weights(const int8_t* __restrict__ q, int64_t n, int64_t k, int gate_up,
+                                  uint4* __restrict__ out) {
+  const int64_t G = k / kGroup;
+  const int64_t total = n * k / 16;
+  for (int64_t ci = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; ci < total;
+       ci += int64_t(gridDim.x) * blockDim.x) {
+    const int lane = int(ci & 63);
+    const int half = int((ci >> 6) & 1);
+    const int64_t tile = ci >> 7;
+    const int64_t g = tile % G, cb = tile / G;
+    const int c = lane & 15, kq = lane >> 4;
+    int64_t src = cb * 16 + c;
+    if (gate_up) {
+      const int64_t hn = n / 2;
+      src = (cb & 1) ? hn + (cb >> 1) * 16 + c : (cb >> 1) * 16 + c;
+    }
+    const int8_t* row = q + src * k + g * kGroup + 64 * half + 8 * kq;
+    const uint2 lo = *reinterpret_cast<const uint2*>(row);
+    const uint2 hi = *reinterpret_cast<const uint2*>(row + 32);
+    out[ci] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+  }
+}
+
+hipError_t launch_quantize8(const void* w, int dtype, int64_t n, int64_t k, int8_t* q, uint16_t* scales,
+                            int32_t* flags, hipStream_t st) {
+  const dim3 grid(unsigned(n * (k / kGroup)));
+  if (dtype == 0) hipLaunchKernelGGL(k_quantize8_g128<0>, grid, dim3(64), 0, st, w, n, k, q, scales, flags);
+  else if (dtype == 1) hipLaunchKernelGGL(k_quantize8_g128<1>, grid, dim3(64), 0, st, w, n, k, q, scales, flags);
+  else hipLaunchKernelGGL(k_quantize8_g128<2>, grid, dim3(64), 0, st, w, n, k, q, scales, flags);
+  return hipGetLastError();
+}
+
+hipError_t launch_repack8(const int8_t* q, const uint16_t* scales, int64_t n, int64_t k, int gate_up, void* out,
+                          hipStream_t st) {
+  uint8_t* base = static_cast<uint8_t*>(out);
+  const int64_t G = k / kGroup;
+  const int64_t chunks = n * k / 16;
+  const int64_t sb = align256(n * k);
+  unsigned blocks = unsigned(std::min<int64_t>((chunks + 255) / 256, 65536));
+  hipLaunchKernelGGL(k_repack8_weights, dim3(blocks), dim3(256), 0, st, q, n, k, gate_up, reinterpret_cast<uint4*>(base));
+  unsigned mblocks = unsigned(std::min<int64_t>((n * G + 255) / 256, 65536));
+  hipLaunchKernelGGL(k_repack_meta, dim3(mblocks), dim3(256), 0, st, scales, nullptr, n, k, gate_up,
+                     reinterpret_cast<uint16_t*>(base + sb), nullptr);
+  const int64_t scale_pad = align256(2 * n * G) - 2 * n * G;
+  if (scale_pad > 0) hipLaunchKernelGGL(k_zero_bytes, dim3(1), dim3(256), 0, st, base + sb + 2 * n * G, scale_pad);
+  return hipGetLastError();
+}
+
 hipError_t launch_quantize(const void* w, int dtype, int64_t n, int64_t k, int asym, uint8_t* packed,
                            uint16_t* scales, uint8_t* zeros, int32_t* flags, hipStream_t st) {
   const int64_t G = k / kGroup;
