@@ -200,6 +200,45 @@ def moe_w8a8(x, expert, ids, weights, shared=None):
     return out
 
 
+# ---------------------------------------------------------------- mixed widths
+# Per-expert weight precision (page "MoE推理优化实战：4bit存储+INT8计算的W4A8路线解析",
+# §5.3 and §6.1: frequently hit / sensitive experts keep more bits; page "大模型之Dense、
+# MoE与量化", APEX: precision by expert importance).  Every expert runs the INT8-activation
+# pipeline above; an expert's own width picks the 4-bit (widened) or the 8-bit codes.
+def swiglu_int8_acts(x, gate, up, down, bits):
+    """SwiGLU FFN of one expert with INT8 activations and `bits`-wide weight codes."""
+    return swiglu_w8a8(x, gate, up, down) if bits == 8 else swiglu_w4a8(x, gate, up, down)
+
+
+def moe_mixed(x, expert, bits, ids, weights, shared=None, shared_bits=8):
+    """out[t] = sum_j w[t, j] FFN_{ids[t, j]}(x[t]) (+ shared), expert e evaluated with
+    bits[e]-wide weights; ``expert(e)`` returns its (gate, up, down) quantised matrices."""
+    x32 = np.asarray(x, dtype=np.float32)
+    ids = np.asarray(ids)
+    w = np.asarray(weights, dtype=np.float64)
+    out = np.zeros((ids.shape[0], x32.shape[1]), dtype=np.float64)
+    for e in np.unique(ids):
+        rows, cols = np.nonzero(ids == e)
+        y = swiglu_int8_acts(x32[rows], *expert(int(e)), bits[int(e)])
+        for i, (r, c) in enumerate(zip(rows, cols)):
+            out[r] += w[r, c] * y[i]
+    if shared is not None:
+        out += swiglu_int8_acts(x32, *shared, shared_bits)
+    return out
+
+
+def bits_by_hotness(counts, frac8, shared=False):
+    """Widths from hit counts: the ceil(frac8 * E) most-hit experts 8 bits (ties: lower
+    index first), the others 4; a shared expert (hit by every token) 8."""
+    counts = np.asarray(counts, dtype=np.int64)
+    e = counts.shape[0]
+    n8 = min(e, int(np.ceil(frac8 * e - 1e-9)))
+    order = np.lexsort((np.arange(e), -counts))   # by count descending, then index
+    bits = np.full(e, 4, dtype=np.int64)
+    bits[order[:n8]] = 8
+    return list(bits) + ([8] if shared else [])
+
+
 # ---------------------------------------------------------------- comparison
 def max_rel_l2(y, ref):
     """max over rows of ||y - ref||_2 / ||ref||_2; a zero reference row needs a zero row."""
