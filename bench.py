@@ -54,15 +54,18 @@ def parse():
 class Workload:
     """Device-resident layer + router + tokens + preallocated buffers for one config."""
 
-    def __init__(self, lib, torch, synth, cfg_name, t, mode):
+    def __init__(self, lib, torch, synth, cfg_name, t, mode, expert_bits=None):
+        """mode "w4a16" / "w4a8" / "w8a8", or "mixed": per-expert widths ``expert_bits``
+        (4 or 8 per expert and the shared expert) with INT8 activations."""
         self.lib, self.torch = lib, torch
         cfg = synth.CONFIGS[cfg_name]
         self.cfg_name, self.cfg, self.t = cfg_name, cfg, t
-        self.mode = {"w4a16": lib.Q4_W4A16, "w4a8": lib.Q4_W4A8, "w8a8": lib.Q4_W8A8}[mode]
+        self.mode = {"w4a16": lib.Q4_W4A16, "w4a8": lib.Q4_W4A8, "w8a8": lib.Q4_W8A8, "mixed": lib.Q4_W4A8}[mode]
         self.wbits = 8 if mode == "w8a8" else 4
         e, h, i, k = cfg["experts"], cfg["hidden"], cfg["inter"], cfg["top_k"]
         shared = bool(cfg.get("shared", False))
-        self.layer = lib.MoELayer(e, h, i, k, asymmetric=cfg["asymmetric"], shared=shared, weight_bits=self.wbits)
+        self.layer = lib.MoELayer(e, h, i, k, asymmetric=cfg["asymmetric"], shared=shared, weight_bits=self.wbits,
+                                  expert_bits=expert_bits if mode == "mixed" else None)
         for j in range(e + (1 if shared else 0)):
             g, u, d = synth.expert_weights(cfg_name, j, device="cuda")
             self.layer.set_expert(j, g, u, d)
@@ -114,21 +117,31 @@ class Workload:
         if rc:
             raise L.Q4Error("moe_int4_ffn_forward", rc)
 
-    def touched(self):
+    def touched_experts(self):
         """Experts with at least one routed row (+ the shared expert)."""
-        ids = self.ids.cpu()
-        n = int(self.torch.unique(ids).numel())
-        return n + (1 if self.layer.shared else 0)
+        ids = [int(v) for v in self.torch.unique(self.ids.cpu()).tolist()]
+        return ids + ([self.cfg["experts"]] if self.layer.shared else [])
 
-    def expert_bytes(self):
+    def touched(self):
+        return len(self.touched_experts())
+
+    def expert_bytes(self, bits=None):
         """Canonical packed bytes of one expert: codes (4- or 8-bit) + fp16 scales (+ zero points)."""
         h, i = self.cfg["hidden"], self.cfg["inter"]
-        cb = self.wbits // 4     # code bytes per 2 weights
+        cb = (bits or self.wbits) // 4     # code bytes per 2 weights
         gu = 2 * i * h * cb // 2 + 2 * i * (h // 128) * 2
         dn = h * i * cb // 2 + h * (i // 128) * 2
         if self.cfg["asymmetric"]:
             gu += 2 * i * ((h // 128 + 1) // 2)
             dn += h * ((i // 128 + 1) // 2)
+        return gu, dn
+
+    def touched_bytes(self):
+        """Canonical bytes (gate/up, down) of the touched experts, each at its own width."""
+        gu = dn = 0
+        for e in self.touched_experts():
+            a, b = self.expert_bytes(self.layer.bits[e])
+            gu, dn = gu + a, dn + b
         return gu, dn
 
     def flops(self):
@@ -238,10 +251,10 @@ def time_steps(torch, wl, steps, warmup, stage_events, graph=True):
 
 def summarize(wl, sec_per_step, stage_ms):
     touched = wl.touched()
-    gu_b, dn_b = wl.expert_bytes()
+    gu_all, dn_all = wl.touched_bytes()
     h, i = wl.cfg["hidden"], wl.cfg["inter"]
     rows = wl.t * (wl.cfg["top_k"] + (1 if wl.layer.shared else 0))
-    layer_bytes = touched * (gu_b + dn_b)
+    layer_bytes = gu_all + dn_all
     res = {
         "tokens": wl.t,
         "tokens_per_s": wl.t / sec_per_step,
@@ -257,10 +270,21 @@ def summarize(wl, sec_per_step, stage_ms):
     res["mfma_frac"] = flops / sec_per_step / 1e12 / peak
     if "gate_up" in stage_ms:
         act = rows * h * (1 if int8 else 2) + rows * i * (4 if int8 else 2)
-        res["gate_up_bytes"] = touched * gu_b + act
+        res["gate_up_bytes"] = gu_all + act
         res["gate_up_GBps"] = res["gate_up_bytes"] / (stage_ms["gate_up"] * 1e-3) / 1e9
         res["gate_up_flops"] = 2.0 * rows * 2 * i * h
     return res
+
+
+def hotness_bits(lib, torch, synth, cfg_name, frac8, calib_tokens=4096):
+    """Per-expert widths from routing hit counts of a seeded calibration batch (routed
+    by the library's router): the ceil(frac8 * E) most-hit experts in 8 bits."""
+    cfg = synth.CONFIGS[cfg_name]
+    x = synth.tokens(cfg_name, calib_tokens, device="cuda", salt=7)
+    wr, b = synth.router_weights(cfg_name, device="cuda")
+    _, ids, _ = lib.moe_route_topk(x, wr, b, cfg["top_k"])
+    counts = torch.bincount(ids.reshape(-1).long(), minlength=cfg["experts"]).cpu().tolist()
+    return lib.expert_bits_by_hotness(counts, frac8, shared=bool(cfg.get("shared", False)))
 
 
 def cpu_baseline(synth, wl, ntok):
@@ -358,6 +382,18 @@ def main():
             s3, st3 = time_steps(torch, w8, 20, 5, stage_events=True, graph=not args.no_graph)
             extra[f"moe8_T2048_{mode}"] = summarize(w8, s3, st3)
             del w8
+        log("[bench] extra moe256 mixed widths (top 5 % of experts by hit count in 8 bits), W4A8")
+        bits = hotness_bits(lib, torch, synth, "moe256", 0.05)
+        mx = Workload(lib, torch, synth, "moe256", args.tokens, "mixed", expert_bits=bits)
+        for t in (args.tokens, 4096):
+            mt = mx if t == args.tokens else mx.retoken(synth, t)
+            s6, st6 = time_steps(torch, mt, 10 if t > 1000 else 50, 3, stage_events=True,
+                                 graph=not args.no_graph)
+            extra[f"moe256_T{t}_mixed_top5pct_int8"] = dict(summarize(mt, s6, st6), experts_8bit=sum(
+                b == 8 for b in bits))
+            del mt
+        del mx
+        torch.cuda.empty_cache()
         if args.mode != "w8a8":
             log(f"[bench] extra moe256 W8A8 T={args.tokens}")
             w8 = Workload(lib, torch, synth, "moe256", args.tokens, "w8a8")

@@ -227,6 +227,15 @@ typedef struct q4_moe_layer_t {
   const void* shared_down;
   int32_t weight_bits;   /* 0 or 4: INT4 device layout (modes W4A16 / W4A8); 8: INT8 device
                             layout of q8_repack_device, symmetric, mode Q4_W8A8 only */
+  /* Mixed layers (per-expert bit width; page "大模型之Dense、MoE与量化", APEX: experts get
+   * different precisions by importance).  When expert_bits != NULL: weight_bits must be
+   * 0, asymmetric 0 and mode Q4_W4A8 (INT8 activations for every expert); expert e's
+   * gate/up block starts at byte gate_up_offsets[e] of gate_up (down: down_offsets[e]
+   * of down) and holds q4_device_bytes(., ., 0) or q8_device_bytes(., .) bytes by its
+   * bits; the shared expert's bits are expert_bits[num_experts]. */
+  const uint8_t* expert_bits;      /* device [num_experts + shared] values 4 or 8 */
+  const int64_t* gate_up_offsets;  /* device [num_experts] */
+  const int64_t* down_offsets;     /* device [num_experts] */
 } q4_moe_layer_t;
 
 /*

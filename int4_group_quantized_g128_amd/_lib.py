@@ -7,6 +7,7 @@ kernels; there is no fallback: if the library is missing, importing this module
 raises.
 """
 import ctypes
+import math
 import os
 
 import torch
@@ -40,6 +41,7 @@ class Q4MoELayer(ctypes.Structure):
         ("asymmetric", _i32), ("shared_inter", _i32),
         ("gate_up", _vp), ("down", _vp), ("shared_gate_up", _vp), ("shared_down", _vp),
         ("weight_bits", _i32),
+        ("expert_bits", _vp), ("gate_up_offsets", _vp), ("down_offsets", _vp),
     ]
 
 
@@ -261,37 +263,84 @@ def act_quant_int8(x):
 
 
 # ------------------------------------------------------------------ layer + forward
+def expert_bits_by_hotness(counts, frac8=0.05, shared=False):
+    """Per-expert weight bit widths from routing hit counts: the ceil(frac8 * E) most-hit
+    experts get 8 bits, the rest 4 (equal counts: the lower expert index first).  With a
+    shared expert (used by every token, so the hottest) one more entry, 8, follows.
+    Page "MoE推理优化实战：4bit存储+INT8计算的W4A8路线解析", §5.3 (the top 5 % most-hit
+    experts keep more precision) and §6.1 (per-expert W8 / W4 assignment); page
+    "大模型之Dense、MoE与量化", APEX (precision by expert importance)."""
+    counts = [int(c) for c in counts]
+    e = len(counts)
+    if not 0.0 <= frac8 <= 1.0:
+        raise ValueError("frac8 must lie in [0, 1]")
+    n8 = min(e, int(math.ceil(frac8 * e - 1e-9)))
+    hot = sorted(range(e), key=lambda i: (-counts[i], i))[:n8]
+    bits = [4] * e
+    for i in hot:
+        bits[i] = 8
+    return bits + ([8] if shared else [])
+
+
 class MoELayer:
-    """Device-resident INT4 MoE layer (stacked experts in the device tile layout)."""
+    """Device-resident MoE layer (experts in the device tile layouts).
+
+    weight_bits 4 (INT4 g128, symmetric or asymmetric) or 8 (INT8 g128, symmetric) for
+    every expert; or expert_bits, one width (4 or 8) per expert plus one for the shared
+    expert, for a mixed symmetric layer run in W4A8 (INT8 activations everywhere)."""
 
     def __init__(self, num_experts, hidden, inter, top_k, asymmetric=False, shared=False, device="cuda",
-                 weight_bits=4):
+                 weight_bits=4, expert_bits=None):
         self.num_experts, self.hidden, self.inter, self.top_k = num_experts, hidden, inter, top_k
         self.asymmetric = bool(asymmetric)
         self.shared = bool(shared)
         if weight_bits not in (4, 8) or (weight_bits == 8 and asymmetric):
             raise ValueError("weight_bits must be 4, or 8 with symmetric weights")
-        self.weight_bits = weight_bits
-        if weight_bits == 8:
-            self.gu_bytes = q8_device_bytes(2 * inter, hidden)
-            self.dn_bytes = q8_device_bytes(hidden, inter)
+        self.mixed = expert_bits is not None
+        if self.mixed:
+            bits = [int(b) for b in expert_bits]
+            if len(bits) != num_experts + int(self.shared) or any(b not in (4, 8) for b in bits):
+                raise ValueError("expert_bits needs one width, 4 or 8, per expert (and the shared expert)")
+            if asymmetric:
+                raise ValueError("mixed layers are symmetric")
         else:
-            self.gu_bytes = q4_device_bytes(2 * inter, hidden, asymmetric)
-            self.dn_bytes = q4_device_bytes(hidden, inter, asymmetric)
-        if self.gu_bytes == 0 or self.dn_bytes == 0:
+            bits = [weight_bits] * (num_experts + int(self.shared))
+        self.bits = bits
+        self.weight_bits = 0 if self.mixed else weight_bits
+
+        def sizes(b):
+            if b == 8:
+                return q8_device_bytes(2 * inter, hidden), q8_device_bytes(hidden, inter)
+            return q4_device_bytes(2 * inter, hidden, asymmetric), q4_device_bytes(hidden, inter, asymmetric)
+
+        sz = [sizes(b) for b in bits]
+        if any(a == 0 or b == 0 for a, b in sz):
             raise ValueError("hidden and inter must be multiples of 128")
-        self.gate_up = torch.empty(num_experts * self.gu_bytes, dtype=torch.uint8, device=device)
-        self.down = torch.empty(num_experts * self.dn_bytes, dtype=torch.uint8, device=device)
-        self.shared_gate_up = torch.empty(self.gu_bytes, dtype=torch.uint8, device=device) if shared else None
-        self.shared_down = torch.empty(self.dn_bytes, dtype=torch.uint8, device=device) if shared else None
+        self.gu_offs, self.dn_offs = [0], [0]
+        for a, b in sz[:num_experts]:
+            self.gu_offs.append(self.gu_offs[-1] + a)
+            self.dn_offs.append(self.dn_offs[-1] + b)
+        self.gu_bytes, self.dn_bytes = sz[0]   # uniform layers: bytes of one expert
+        self.gate_up = torch.empty(self.gu_offs[-1], dtype=torch.uint8, device=device)
+        self.down = torch.empty(self.dn_offs[-1], dtype=torch.uint8, device=device)
+        self.shared_gate_up = torch.empty(sz[-1][0], dtype=torch.uint8, device=device) if shared else None
+        self.shared_down = torch.empty(sz[-1][1], dtype=torch.uint8, device=device) if shared else None
+        if self.mixed:
+            self.bits_dev = torch.tensor(bits, dtype=torch.uint8, device=device)
+            self.gu_offs_dev = torch.tensor(self.gu_offs[:-1], dtype=torch.int64, device=device)
+            self.dn_offs_dev = torch.tensor(self.dn_offs[:-1], dtype=torch.int64, device=device)
         self.desc = Q4MoELayer(num_experts, hidden, inter, top_k, int(self.asymmetric),
                                inter if shared else 0, self.gate_up.data_ptr(), self.down.data_ptr(),
                                self.shared_gate_up.data_ptr() if shared else None,
-                               self.shared_down.data_ptr() if shared else None, weight_bits)
+                               self.shared_down.data_ptr() if shared else None, self.weight_bits,
+                               self.bits_dev.data_ptr() if self.mixed else None,
+                               self.gu_offs_dev.data_ptr() if self.mixed else None,
+                               self.dn_offs_dev.data_ptr() if self.mixed else None)
 
     def weight_bytes(self):
         """Device bytes of all expert weights."""
-        return self.gate_up.numel() + self.down.numel() + (self.gu_bytes + self.dn_bytes if self.shared else 0)
+        return self.gate_up.numel() + self.down.numel() + (
+            self.shared_gate_up.numel() + self.shared_down.numel() if self.shared else 0)
 
     def set_expert(self, e, gate, up, down):
         """Quantise (on the GPU) and place expert e; e == num_experts is the shared expert."""
@@ -305,9 +354,9 @@ class MoELayer:
                 raise ValueError("layer has no shared expert")
             gu_out, dn_out = self.shared_gate_up, self.shared_down
         else:
-            gu_out = self.gate_up[e * self.gu_bytes:(e + 1) * self.gu_bytes]
-            dn_out = self.down[e * self.dn_bytes:(e + 1) * self.dn_bytes]
-        if self.weight_bits == 8:
+            gu_out = self.gate_up[self.gu_offs[e]:self.gu_offs[e + 1]]
+            dn_out = self.down[self.dn_offs[e]:self.dn_offs[e + 1]]
+        if self.bits[e] == 8:
             q, s = quantize_int8_g128(torch.cat([gate, up], dim=0).contiguous())
             q8_repack_device(q, s, 2 * I, H, gate_up=True, out=gu_out)
             q, s = quantize_int8_g128(down.contiguous())

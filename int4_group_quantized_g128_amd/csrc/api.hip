@@ -75,9 +75,11 @@ struct FwdWorkspace {
 bool int8_acts(int mode) { return mode == Q4_W4A8 || mode == Q4_W8A8; }
 int wbits_of(const q4_moe_layer_t* L) { return L->weight_bits == 8 ? 8 : 4; }
 
-// Device bytes of one [n][k] expert matrix in the layer's weight format.
+// Device bytes of one [n][k] expert matrix in the layer's weight format (the larger,
+// 8-bit, size for mixed layers).
 int64_t mat_bytes(const q4_moe_layer_t* L, int64_t n, int64_t k) {
-  return wbits_of(L) == 8 ? int64_t(q8_device_bytes(n, k)) : int64_t(q4_device_bytes(n, k, L->asymmetric));
+  return (wbits_of(L) == 8 || L->expert_bits) ? int64_t(q8_device_bytes(n, k))
+                                              : int64_t(q4_device_bytes(n, k, L->asymmetric));
 }
 
 // Average routed rows per expert decides the GEMM shape: 16-row decode tiles, 32 / 64-row
@@ -153,6 +155,11 @@ int validate_layer(const q4_moe_layer_t* L) {
   Q4_REQUIRE(L->weight_bits == 0 || L->weight_bits == 4 || L->weight_bits == 8, Q4_ERR_SHAPE,
              "weight_bits %d not in {0, 4, 8}", L->weight_bits);
   Q4_REQUIRE(L->weight_bits != 8 || L->asymmetric == 0, Q4_ERR_UNSUPPORTED, "8-bit weights are symmetric only");
+  if (L->expert_bits) {
+    Q4_REQUIRE(L->weight_bits == 0 && L->asymmetric == 0, Q4_ERR_UNSUPPORTED,
+               "mixed layers: weight_bits 0 and symmetric weights");
+    Q4_REQUIRE(L->gate_up_offsets && L->down_offsets, Q4_ERR_NULL, "mixed layers need the block offsets");
+  }
   if (L->shared_inter != 0) {
     Q4_REQUIRE(L->shared_inter == L->inter, Q4_ERR_UNSUPPORTED,
                "shared_inter %d must equal inter %d in this build", L->shared_inter, L->inter);
@@ -316,7 +323,9 @@ int act_quant_int8(const void* x, int x_dtype, int64_t rows, int64_t cols, int8_
 
 size_t moe_int4_ffn_workspace_bytes(const q4_moe_layer_t* layer, int64_t t, int mode) {
   if (!layer || t < 0 || validate_layer(layer) != Q4_OK) return 0;
-  if (wbits_of(layer) == 8 ? mode != Q4_W8A8 : (mode != Q4_W4A16 && mode != Q4_W4A8)) return 0;
+  if (layer->expert_bits ? mode != Q4_W4A8
+                         : (wbits_of(layer) == 8 ? mode != Q4_W8A8 : (mode != Q4_W4A16 && mode != Q4_W4A8)))
+    return 0;
   return size_t(carve(layer, t, mode, nullptr).bytes);
 }
 
@@ -328,8 +337,9 @@ int ffn_forward(const q4_moe_layer_t* L, const uint16_t* x_bf16, int64_t t, cons
   g_last_error.clear();
   if (views) *views = q4_ffn_views_t{};
   if (int rc = validate_layer(L)) return rc;
-  Q4_REQUIRE(wbits_of(L) == 8 ? mode == Q4_W8A8 : (mode == Q4_W4A16 || mode == Q4_W4A8), Q4_ERR_DTYPE,
-             "mode %d does not match weight_bits %d", mode, L->weight_bits);
+  Q4_REQUIRE(L->expert_bits ? mode == Q4_W4A8
+                             : (wbits_of(L) == 8 ? mode == Q4_W8A8 : (mode == Q4_W4A16 || mode == Q4_W4A8)),
+             Q4_ERR_DTYPE, "mode %d does not match the layer's weight format", mode);
   Q4_REQUIRE(t >= 0, Q4_ERR_SHAPE, "t < 0");
   if (t == 0) return ok();
   const int shared = L->shared_inter > 0 ? 1 : 0;
@@ -371,6 +381,8 @@ int ffn_forward(const q4_moe_layer_t* L, const uint16_t* x_bf16, int64_t t, cons
   gu.w = static_cast<const uint8_t*>(L->gate_up);
   gu.w_stride = mat_bytes(L, 2 * I, H);
   gu.wbits = wbits_of(L);
+  gu.ebits = L->expert_bits;
+  gu.woffs = L->gate_up_offsets;
   gu.w_shared = static_cast<const uint8_t*>(L->shared_gate_up);
   gu.num_experts = L->num_experts;
   gu.asym = L->asymmetric;
@@ -386,12 +398,22 @@ int ffn_forward(const q4_moe_layer_t* L, const uint16_t* x_bf16, int64_t t, cons
   dn.perm = nullptr;
   dn.w = static_cast<const uint8_t*>(L->down);
   dn.w_stride = mat_bytes(L, H, I);
+  dn.woffs = L->down_offsets;
   dn.w_shared = static_cast<const uint8_t*>(L->shared_down);
   dn.N = H;
   dn.K = I;
   dn.out = w.y;
-  auto gemm = [&](const GemmArgs& g, int act, int kind) {
+  auto gemm1 = [&](const GemmArgs& g, int act, int kind) {
     return w.prefill ? launch_gemm_prefill(g, act, kind, stream) : launch_gemm(g, act, kind, rb, stream);
+  };
+  // mixed layers: one launch per weight format, each skipping the other format's experts
+  auto gemm = [&](const GemmArgs& g, int act, int kind) {
+    if (!g.ebits) return gemm1(g, act, kind);
+    GemmArgs g4 = g, g8 = g;
+    g4.wbits = 4;
+    g8.wbits = 8;
+    const hipError_t e = gemm1(g4, act, kind);
+    return e != hipSuccess ? e : gemm1(g8, act, kind);
   };
   if (mode == Q4_W4A16) {
     gu.a = x_bf16;

@@ -144,7 +144,10 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs args) {
       row_start = tile * tile_rows;
       rows = std::min<int64_t>(tile_rows, args.dense_rows - row_start);
     }
-    const uint8_t* wbase = expert < args.num_experts ? args.w + int64_t(expert) * args.w_stride : args.w_shared;
+    if (args.ebits && args.ebits[expert] != (W8 ? 8 : 4)) continue;   // other format (uniform skip)
+    const uint8_t* wbase = expert >= args.num_experts ? args.w_shared
+                           : args.woffs                 ? args.w + args.woffs[expert]
+                                                        : args.w + int64_t(expert) * args.w_stride;
 
     // stage the workgroup's scales / zero points (contiguous in the device layout)
     {

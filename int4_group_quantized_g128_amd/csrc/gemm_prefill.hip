@@ -97,9 +97,10 @@ Q4_DEVICE u32x4_t buffer_rsrc(const void* base, int64_t bytes) {
   return u32x4_t{uint32_t(a), uint32_t(a >> 32) & 0xffffu, uint32_t(bytes), 0x00020000u};
 }
 
-Q4_DEVICE uint32_t lds_addr(const void* p) {
-  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_ptr_t)(const_cast<void*>(p))));
-}
+// LDS byte address of a generic pointer into LDS: the low half of a flat LDS address is
+// the LDS offset (the high half is the shared aperture), so no address-space cast (and
+// its null check) is needed.
+Q4_DEVICE uint32_t lds_addr(const void* p) { return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p)); }
 
 // Direct-to-LDS copy of SIZE (16 or 4) bytes per lane: lane L's bytes land at
 // lds + L * SIZE.  Written as inline asm with no register outputs other than a scratch
@@ -219,12 +220,20 @@ __global__ void __launch_bounds__(256, 1) k_gemm_pf(GemmArgs args) {
   for (int64_t item = ir.first; item < ir.last; item += ir.step) {
     const int64_t tile = item / nblk;
     const int64_t cb0 = (item % nblk) * kPfCB;
-    if constexpr (A == Act::I8) __syncthreads();   // previous item's epilogue is done with s_sa
     const TileDesc d = args.tiles[tile];
+    if (args.ebits && args.ebits[d.expert] != (W8 ? 8 : 4)) continue;   // other format (uniform skip)
+    if constexpr (A == Act::I8) __syncthreads();   // previous item's epilogue is done with s_sa
     const int64_t row_start = d.row_start;
     const int rows = d.rows;
-    const uint8_t* wbase = d.expert < args.num_experts ? args.w + int64_t(d.expert) * args.w_stride : args.w_shared;
-    const auto w_rsrc = buffer_rsrc(wbase, args.w_stride);
+    const bool shared = d.expert >= args.num_experts;
+    typedef __attribute__((address_space(1))) const int64_t* gptr_i64;   // global (not flat) load
+    int64_t woff = shared ? 0 : args.woffs ? ((gptr_i64)args.woffs)[d.expert] : int64_t(d.expert) * args.w_stride;
+    woff = int64_t(uint64_t(uint32_t(__builtin_amdgcn_readfirstlane(uint32_t(uint64_t(woff) >> 32)))) << 32 |
+                   uint32_t(__builtin_amdgcn_readfirstlane(uint32_t(woff))));   // wave-uniform
+    const uint8_t* wbase = (shared ? args.w_shared : args.w) + woff;
+    // bytes of one expert matrix in this kernel's format
+    const int64_t w_bytes = w_scale_off + align256(2 * N * int64_t(G)) + (ASYM ? align256(N * int64_t(G)) : 0);
+    const auto w_rsrc = buffer_rsrc(wbase, w_bytes);
     auto src_of = [&](int r) -> int64_t {   // activation row of tile row r (clamped)
       const int64_t pos = row_start + (r < rows ? r : 0);
       return args.perm ? args.perm[pos] / args.slots_per_token : pos;

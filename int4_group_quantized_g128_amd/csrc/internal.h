@@ -60,6 +60,8 @@ struct GemmArgs {
   int32_t num_experts;
   int32_t asym;
   int32_t wbits;          // 4 (INT4 tiles) or 8 (INT8 tiles, int8 activations only)
+  const uint8_t* ebits;   // mixed layers: bits per expert (tiles of other experts are skipped), or NULL
+  const int64_t* woffs;   // mixed layers: byte offset of each routed expert's block in w, or NULL
   int64_t N;              // device columns (2I for gate/up)
   int64_t K;
   // tiles

@@ -144,3 +144,30 @@ def test_binding_refuses_cpu_tensors(L):
     import torch
     with pytest.raises(ValueError):
         L.quantize_int4_g128(torch.zeros((16, 128)))
+
+
+def test_expert_bits_by_hotness_matches_the_oracle_rule(L):
+    import numpy as np
+    from oracle import ffn
+    rng = np.random.default_rng(5)
+    for E, frac, shared in ((256, 0.05, False), (8, 0.25, True), (17, 0.0, False), (9, 1.0, True), (64, 0.1, False)):
+        counts = rng.integers(0, 6, E)
+        assert L.expert_bits_by_hotness(counts.tolist(), frac, shared) == ffn.bits_by_hotness(counts, frac, shared)
+    with pytest.raises(ValueError):
+        L.expert_bits_by_hotness([1, 2], 1.5)
+
+
+def test_mixed_layer_validation(L):
+    r = L.raw
+    fake = ctypes.c_void_p(4096)
+    desc = L.Q4MoELayer(8, 256, 128, 2, 0, 0, 4096, 4096, None, None, 0, 4096, 4096, 4096)
+    # mixed layers run with INT8 activations only
+    assert r.moe_int4_ffn_workspace_bytes(ctypes.byref(desc), 4, L.Q4_W4A16) == 0
+    assert r.moe_int4_ffn_workspace_bytes(ctypes.byref(desc), 4, L.Q4_W4A8) > 0
+    for bad in (dict(asymmetric=1), dict(weight_bits=8), dict(down_offsets=None)):
+        d = L.Q4MoELayer(8, 256, 128, 2, 0, 0, 4096, 4096, None, None, 0, 4096, 4096, 4096)
+        for key, v in bad.items():
+            setattr(d, key, v)
+        assert r.moe_int4_ffn_workspace_bytes(ctypes.byref(d), 4, L.Q4_W4A8) == 0
+    assert r.moe_int4_ffn_forward(ctypes.byref(desc), fake, 4, fake, fake, L.Q4_W4A16, fake, fake, 1 << 20,
+                                  None) == L.Q4_ERR_DTYPE

@@ -1,0 +1,178 @@
+"""Full-size parity of the 256-expert layer (hidden 7168, 256 experts of intermediate
+2048 + one shared expert, top-8, symmetric INT4 g128, fp32 router with the Zipf bias),
+built and run exactly as the benchmark runs it: bench.Workload, one step = the
+library's router, then moe_int4_ffn_forward, at the benchmark's batch sizes (T = 1 and
+64 decode, T = 4096 prefill) and in each arithmetic mode it reports.
+
+The oracle routes the same tokens itself (fp64 logits) and evaluates a seeded sample of
+tokens one by one; a sampled token is compared where both routings choose the same
+experts (fp32 and fp64 logits may order near-ties differently; nearly all tokens
+agree, which is asserted).  Expert weights for the oracle come from the seeded
+generator run by torch on the GPU and copied to the host (bit-identical to the host
+generator, checked by test_generator_bit_identical_on_gpu), then quantised by the
+oracle; nothing the library computes is fed to the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import ffn, quant, router
+from tests.helpers import require_gpu
+
+pytestmark = pytest.mark.gpu
+CFG = "moe256"
+TOL = {"w4a16": 5e-3, "w4a8": 2e-2, "w8a8": 2e-2, "mixed": 2e-2}
+
+
+@pytest.fixture(scope="module")
+def lib():
+    require_gpu()
+    import int4_group_quantized_g128_amd as lib
+    return lib
+
+
+def _np(t):
+    return synth.to_numpy(t)
+
+
+class OracleExperts:
+    """Oracle-quantised experts of the layer, by (expert, bits); codes kept as int8."""
+
+    def __init__(self):
+        self.cache = {}
+
+    def get(self, e, bits):
+        key = (e, bits)
+        if key not in self.cache:
+            mats = synth.expert_weights(CFG, e, device="cuda")
+            out = []
+            for m in mats:
+                w = _np(m)
+                q, s = quant.quantize_sym8(w) if bits == 8 else quant.quantize_sym(w)
+                out.append((q.astype(np.int8), s, None))
+            self.cache[key] = tuple(out)
+        return self.cache[key]
+
+    def have(self, e, bits):
+        return (e, bits) in self.cache
+
+
+@pytest.fixture(scope="module")
+def oracle_experts():
+    return OracleExperts()
+
+
+@pytest.fixture(scope="module")
+def bench_mod():
+    import bench
+    return bench
+
+
+@pytest.fixture(scope="module")
+def wl4(lib, bench_mod):
+    return bench_mod.Workload(lib, torch, synth, CFG, 64, "w4a16")
+
+
+def _oracle_routing(x, t):
+    cfg = synth.CONFIGS[CFG]
+    wr, b = synth.router_weights(CFG)
+    L = router.logits_fp64(x, _np(wr), _np(b))
+    ids = router.select_topk(L, cfg["top_k"])
+    return ids, router.topk_weights(L, ids)
+
+
+def _pick(agree, ids, n, seed, bits, have):
+    """n agreeing tokens, preferring ones whose experts the oracle already holds."""
+    cand = list(np.random.default_rng(seed).permutation(np.nonzero(agree)[0]))
+    chosen = []
+    while len(chosen) < n and cand:
+        window = cand[:16]
+        best = min(window, key=lambda r: sum(not have(int(e), bits[int(e)]) for e in ids[r]))
+        chosen.append(int(best))
+        cand.remove(best)
+    return np.array(sorted(chosen))
+
+
+def _check(lib, wl, kind, oe, nsample, seed, bits=None):
+    E = synth.CONFIGS[CFG]["experts"]
+    t = wl.t
+    print(f"[fullsize] {kind} T={t}: step", flush=True)
+    wl.step()
+    torch.cuda.synchronize()
+    x = _np(synth.tokens(CFG, t))
+    assert np.array_equal(_np(wl.x), x)
+    ids_o, w_o = _oracle_routing(x, t)
+    agree = np.all(_np(wl.ids) == ids_o, axis=1)
+    assert agree.mean() >= (0.9 if t > 1 else 1.0), f"routing agrees on {agree.mean():.3f} of the tokens"
+    if bits is None:
+        bits = [8 if kind == "w8a8" else 4] * (E + 1)
+    rows = _pick(agree, ids_o, nsample, seed, bits, oe.have)
+    print(f"[fullsize] {kind} T={t}: oracle on tokens {rows.tolist()}", flush=True)
+    expert = lambda e: oe.get(e, bits[e])
+    shared = expert(E)
+    xs, ids_s, w_s = x[rows], ids_o[rows], w_o[rows]
+    if kind == "w4a16":
+        ref = ffn.moe_w4a16(xs, expert, ids_s, w_s, shared=shared)
+    elif kind == "w4a8":
+        ref = ffn.moe_w4a8(xs, expert, ids_s, w_s, shared=shared)
+    elif kind == "w8a8":
+        ref = ffn.moe_w8a8(xs, expert, ids_s, w_s, shared=shared)
+    else:
+        ref = ffn.moe_mixed(xs, expert, bits, ids_s, w_s, shared=shared, shared_bits=bits[E])
+    err = ffn.max_rel_l2(_np(wl.out)[rows], ref)
+    print(f"[fullsize] {kind} T={t}: max rel L2 {err:.2e}", flush=True)
+    assert err <= TOL[kind]
+    out = _np(wl.out)
+    assert np.all(np.isfinite(out))
+
+
+def test_decode_t64_w4a16(lib, wl4, oracle_experts):
+    _check(lib, wl4, "w4a16", oracle_experts, 3, 1)
+
+
+def test_decode_t1_w4a16(lib, wl4, oracle_experts):
+    _check(lib, wl4.retoken(synth, 1), "w4a16", oracle_experts, 1, 2)
+
+
+def test_prefill_t4096_w4a16(lib, wl4, oracle_experts):
+    _check(lib, wl4.retoken(synth, 4096), "w4a16", oracle_experts, 2, 3)
+
+
+@pytest.mark.parametrize("t", [1, 64])
+def test_decode_w4a8(lib, wl4, oracle_experts, t):
+    _check(lib, wl4.retoken(synth, t, "w4a8"), "w4a8", oracle_experts, 2, 4)
+
+
+def test_prefill_t4096_w4a8(lib, wl4, oracle_experts):
+    _check(lib, wl4.retoken(synth, 4096, "w4a8"), "w4a8", oracle_experts, 2, 5)
+
+
+def test_decode_t64_w8a8(lib, bench_mod, oracle_experts):
+    wl = bench_mod.Workload(lib, torch, synth, CFG, 64, "w8a8")
+    _check(lib, wl, "w8a8", oracle_experts, 2, 6)
+    del wl
+    torch.cuda.empty_cache()
+
+
+@pytest.fixture(scope="module")
+def mixed(lib, bench_mod):
+    """Top 5 % of the experts by hit count (the oracle's routing of a seeded calibration
+    batch) in 8 bits, the others in 4; the shared expert in 8."""
+    cfg = synth.CONFIGS[CFG]
+    xc = _np(synth.tokens(CFG, 4096, salt=7))
+    ids_c, _ = _oracle_routing(xc, 4096)
+    counts = np.bincount(ids_c.ravel(), minlength=cfg["experts"])
+    bits = ffn.bits_by_hotness(counts, 0.05, shared=True)
+    assert sum(b == 8 for b in bits) == 13 + 1
+    wl = bench_mod.Workload(lib, torch, synth, CFG, 64, "mixed", expert_bits=bits)
+    yield wl, bits
+    del wl
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("t", [64, 4096])
+def test_mixed_widths_by_hotness(lib, mixed, oracle_experts, t):
+    """INT8 activations; the decode (T = 64) and prefill (T = 4096) paths each launch one
+    GEMM per width over the same tile list."""
+    wl, bits = mixed
+    _check(lib, wl if t == 64 else wl.retoken(synth, t), "mixed", oracle_experts, 2, 7 + t, bits=bits)
