@@ -40,6 +40,8 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=100)
     p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--config", choices=["moe256", "moe8_w4a8"], default="moe256",
+                   help="layer of the main line: the 256-expert layer, or the 8-expert W4A8 prefill layer")
     p.add_argument("--tokens", type=int, default=64)
     p.add_argument("--mode", choices=["w4a16", "w4a8", "w8a8"], default="w4a16")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -304,10 +306,14 @@ def cpu_baseline(synth, wl, ntok):
     ids0 = router.select_topk(router.logits_fp64(x, wr, b), k)
     need = sorted(set(int(v) for v in ids0.ravel()))
     shared_e = wl.cfg["experts"] if wl.layer.shared else None
+    lib = wl.lib
+    name, fwd = {lib.Q4_W4A16: ("W4A16", ffn.moe_w4a16), lib.Q4_W4A8: ("W4A8", ffn.moe_w4a8),
+                 lib.Q4_W8A8: ("W8A8", ffn.moe_w8a8)}[wl.mode]
+    qz = quant.quantize_sym8 if wl.mode == lib.Q4_W8A8 else quant.quantize_sym
     experts = {}
     for e in need + ([shared_e] if shared_e is not None else []):
         g, u, d = synth.expert_weights(wl.cfg_name, e)
-        experts[e] = tuple((lambda q: (q[0].astype(np.int64), q[1], None))(quant.quantize_sym(synth.to_numpy(m)))
+        experts[e] = tuple((lambda q: (q[0].astype(np.int64), q[1], None))(qz(synth.to_numpy(m)))
                            for m in (g, u, d))
     # the timed sample is repeated until about 10 s of CPU work have been done
     reps, dt = 0, 0.0
@@ -316,13 +322,14 @@ def cpu_baseline(synth, wl, ntok):
         L = router.logits_fp64(x, wr, b)
         ids = router.select_topk(L, k)
         w = router.topk_weights(L, ids)
-        out = ffn.moe_w4a16(x, lambda e: experts[e], ids, w, shared=experts.get(shared_e))
+        out = fwd(x, lambda e: experts[e], ids, w, shared=experts.get(shared_e))
         reps += 1
         dt = time.perf_counter() - t0
     assert np.all(np.isfinite(out))
     return {"value": ntok * reps / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"oracle router + W4A16 MoE forward (fp64 NumPy) on {ntok} of the {wl.t} tokens "
-                      f"({len(need)} routed experts + shared), repeated {reps}x: {dt:.1f} s"}
+            "sample": f"oracle router + {name} MoE forward (fp64 NumPy) on {ntok} of the {wl.t} tokens "
+                      f"({len(need)} routed experts{' + shared' if shared_e is not None else ''}), "
+                      f"repeated {reps}x: {dt:.1f} s"}
 
 
 def main():
@@ -336,15 +343,22 @@ def main():
     import synth
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
-    log(f"[bench] building moe256 layer (T={args.tokens}, {args.mode})")
-    wl = Workload(lib, torch, synth, "moe256", args.tokens, args.mode)
+    log(f"[bench] building {args.config} layer (T={args.tokens}, {args.mode})")
+    wl = Workload(lib, torch, synth, args.config, args.tokens, args.mode)
     log(f"[bench] layer weights {wl.layer.weight_bytes() / 1e9:.3f} GB; timing {args.steps} steps")
     sec, stage_ms = time_steps(torch, wl, args.steps, args.warmup, stage_events=True, graph=not args.no_graph)
     main_res = summarize(wl, sec, stage_ms)
     log(f"[bench] main: {json.dumps(main_res)}")
 
     roof = None
-    if "gate_up_GBps" in main_res:
+    if args.config != "moe256":
+        gu_ms = main_res["stage_ms"]["gate_up"]
+        roof = {"kernel": "k_gemm_pf gate/up + SwiGLU (128-row tiles)", "bound": "mfma",
+                "achieved": round(main_res["gate_up_flops"] / (gu_ms * 1e-3) / 1e12, 1),
+                "peak": INT8_PEAK_TOPS if wl.mode != lib.Q4_W4A16 else BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "traffic": None, "algorithmic_flops_per_launch": main_res["gate_up_flops"], "avg_launch_ms": gu_ms}
+        roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    elif "gate_up_GBps" in main_res:
         roof = {"kernel": "k_gemm gate/up + SwiGLU (W4A16, 16-row tiles)", "bound": "hbm",
                 "achieved": round(main_res["gate_up_GBps"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(main_res["gate_up_GBps"] / HBM_PEAK_GBS, 4), "traffic": None,
@@ -358,7 +372,7 @@ def main():
                 roof["traffic_source"] = os.path.relpath(TRAFFIC_PROFILE, ROOT)
 
     extra = {}
-    if not args.no_extra:
+    if not args.no_extra and args.config == "moe256":
         other = "w4a8" if args.mode == "w4a16" else "w4a16"
         for t, mode in ((1, args.mode), (4096, args.mode), (1, other), (args.tokens, other)):
             if t == args.tokens and mode == args.mode:
@@ -429,8 +443,11 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if args.mode == "w4a16" else "int8",
         "data": "synthetic",
-        "config": {"workload": f"moe256 decode: hidden 7168, 256 experts x inter 2048 + 1 shared, top-8, "
-                               f"INT4 g128 sym, T={args.tokens}, {args.mode}",
+        "config": {"workload": (f"moe256 {'decode' if args.tokens <= 256 else 'prefill'}: hidden 7168, 256 experts "
+                                f"x inter 2048 + 1 shared, top-8, INT4 g128 sym, T={args.tokens}, {args.mode}"
+                                if args.config == "moe256" else
+                                f"moe8 prefill: hidden 2048, 8 experts x inter 1024, top-2, INT4 g128 sym, 1 % hot "
+                                f"channels x10, T={args.tokens}, {args.mode}"),
                    "tokens": args.tokens, "experts_touched": main_res["experts_touched"],
                    "effective_weight_GBps": round(main_res["effective_weight_GBps"], 1),
                    "hbm_frac": round(main_res["hbm_frac"], 4)},
