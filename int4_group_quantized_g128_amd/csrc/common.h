@@ -90,9 +90,11 @@ constexpr float magic_offset() { return A == Act::BF16 ? 128.0f : 1024.0f; }
 // lane's elements (0..3) and (4..7) in k order: the low nibbles shifted up, and the
 // high nibbles in place.
 Q4_DEVICE void widen_word_i8(uint32_t w, uint32_t& lo, uint32_t& hi) {
-  const uint32_t t = w ^ 0x88888888u;           // d -> d - 8 (two's complement nibble)
-  lo = (t << 4) & 0xF0F0F0F0u;
-  hi = t & 0xF0F0F0F0u;
+  // flipping a nibble's top bit maps d to d - 8 in two's complement; with the nibble
+  // already in a byte's high half that is an xor with 0x80 per byte, applied after the
+  // mask (a shift and one three-input bit operation for lo, one for hi)
+  lo = ((w << 4) & 0xF0F0F0F0u) ^ 0x80808080u;
+  hi = (w & 0xF0F0F0F0u) ^ 0x80808080u;
 }
 
 // ---------------------------------------------------------------- MFMA wrappers

@@ -138,6 +138,16 @@ Q4_DEVICE void copy_to_lds(const u32x4_t& rsrc, uint32_t lds_in, uint32_t voff, 
 //   W tiles [8 column blocks][TB]  (the device tiles as stored: 1 KB 4-bit, 2 KB 8-bit)
 //   scales  [8][16] fp16, zero points [8][16] u8 (asymmetric)
 //   rsum    [128] fp32 row sums (bf16) / int32 code sums (int8, asymmetric)
+// int8 activations: two workgroups per CU (a two-slot ring: 51 KB of LDS with 4-bit
+// weights, 67 KB with 8-bit ones, and at most 256 registers per lane) so the waves of one
+// hide the barrier and LDS latencies of the other
+#ifndef Q4_PF_GRID_I8
+#define Q4_PF_GRID_I8 512
+#endif
+#ifndef Q4_PF_SLOTS_I8
+#define Q4_PF_SLOTS_I8 2
+#endif
+
 template <Act A, bool W8 = false>
 struct PfStage {
   static constexpr int ESZ = (A == Act::I8) ? 1 : 2;
@@ -149,8 +159,9 @@ struct PfStage {
   static constexpr int Z_OFF = S_OFF + kPfCB * 32;
   static constexpr int R_OFF = S_OFF + 512;
   static constexpr int BYTES = R_OFF + kPfRows * 4;
-  // LDS ring depth (3 x 41 KB bf16, 3 x 25.6 KB int8)
-  static constexpr int SLOTS = 3;
+  // LDS ring depth (3 x 41 KB bf16; int8: Q4_PF_SLOTS_I8 x 25.6 KB, x 33.4 KB with 8-bit
+  // weights)
+  static constexpr int SLOTS = (A != Act::I8) ? 3 : (W8 && Q4_PF_SLOTS_I8 > 4) ? 4 : Q4_PF_SLOTS_I8;
 };
 
 // f(integral_constant<int, i>) for i = 0 .. N - 1, in order.
@@ -179,7 +190,7 @@ Q4_DEVICE ItemRange item_range(int64_t items) {
 }
 
 template <Act A, int KIND, bool ASYM, bool W8>
-__global__ void __launch_bounds__(256, 1) k_gemm_pf(GemmArgs args) {
+__global__ void __launch_bounds__(256, (A == Act::I8) ? 2 : 1) k_gemm_pf(GemmArgs args) {
   static_assert(!W8 || (A == Act::I8 && !ASYM), "8-bit weights: symmetric, int8 activations");
   using St = PfStage<A, W8>;
   constexpr int TB = St::TB;
@@ -478,9 +489,9 @@ __global__ void __launch_bounds__(256, 1) k_gemm_pf(GemmArgs args) {
     constexpr int PER = A_INSTS + WCOPIES;
     auto sync = [&](int newer) {
       static_assert((NS - 2) * PER < 64, "vmcnt range");
-      if (newer >= 2 && NS > 3) wait_vmcnt<(NS > 3 ? 2 * PER : 0)>();
-      else if (newer >= 1) wait_vmcnt<PER>();
-      else wait_vmcnt<0>();
+      static_for<NS - 1>([&](auto u) {   // newer in 0 .. NS - 2 (wave-uniform)
+        if (newer == decltype(u)::value) wait_vmcnt<decltype(u)::value * PER>();
+      });
       asm volatile("" ::: "memory");
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
@@ -560,7 +571,8 @@ static hipError_t launch_pf_kind(const GemmArgs& g, hipStream_t st) {
   const int64_t nblk = g.N / (16 * kPfCB);
   const int64_t items = int64_t(g.max_tiles) * nblk;
   if (items == 0) return hipSuccess;
-  const unsigned grid = unsigned(std::min<int64_t>(items, 256));
+  const int64_t cap = (A == Act::I8) ? Q4_PF_GRID_I8 : 256;
+  const unsigned grid = unsigned(std::min<int64_t>(items, cap));
   if constexpr (A == Act::I8) {
     if (g.wbits == 8) {
       hipLaunchKernelGGL((k_gemm_pf<A, KIND, false, true>), dim3(grid), dim3(256), 0, st, g);
