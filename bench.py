@@ -24,9 +24,14 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
-# HBM counter summary (rocprofv3 FETCH_SIZE / WRITE_SIZE, copy-calibrated) of the default workload's
-# gate/up kernel; used as roofline traffic only while the GEMM sources still hash the same
-TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "k_gemm_gate_up_moe256_T64_w4a16.txt")
+# HBM counter summaries (rocprofv3 FETCH_SIZE / WRITE_SIZE, copy-calibrated) of the gate/up kernel
+# by (layer, tokens, mode) of the main line; used as roofline traffic only while the GEMM sources
+# still hash the same
+TRAFFIC_PROFILES = {
+    ("moe256", 64, "w4a16"): os.path.join(ROOT, "profiles", "k_gemm_gate_up_moe256_T64_w4a16.txt"),
+    ("moe256", 4096, "w4a16"): os.path.join(ROOT, "profiles", "k_gemm_pf_moe256_T4096_w4a16.txt"),
+    ("moe8_w4a8", 2048, "w4a8"): os.path.join(ROOT, "profiles", "k_gemm_pf_moe8_T2048_w4a8.txt"),
+}
 BF16_PEAK_TFLOPS = 2500.0      # dense bf16 MFMA
 INT8_PEAK_TOPS = 5000.0        # dense int8 MFMA
 
@@ -351,7 +356,7 @@ def main():
     log(f"[bench] main: {json.dumps(main_res)}")
 
     roof = None
-    if args.config != "moe256":
+    if args.config != "moe256" or args.tokens > 256:   # prefill: the matrix core bounds the kernel
         gu_ms = main_res["stage_ms"]["gate_up"]
         roof = {"kernel": "k_gemm_pf gate/up + SwiGLU (128-row tiles)", "bound": "mfma",
                 "achieved": round(main_res["gate_up_flops"] / (gu_ms * 1e-3) / 1e12, 1),
@@ -364,12 +369,14 @@ def main():
                 "frac": round(main_res["gate_up_GBps"] / HBM_PEAK_GBS, 4), "traffic": None,
                 "algorithmic_bytes_per_launch": main_res["gate_up_bytes"],
                 "avg_launch_ms": main_res["stage_ms"]["gate_up"]}
-        if args.tokens == 64 and args.mode == "w4a16":
-            from int4_group_quantized_g128_amd import profiling
-            kv = profiling.read_kv(TRAFFIC_PROFILE)
-            if kv.get("source_hash") == profiling.source_hash() and "traffic_bytes[gate_up]" in kv:
-                roof["traffic"] = int(kv["traffic_bytes[gate_up]"])
-                roof["traffic_source"] = os.path.relpath(TRAFFIC_PROFILE, ROOT)
+
+    prof = TRAFFIC_PROFILES.get((args.config, args.tokens, args.mode))
+    if roof is not None and prof is not None:
+        from int4_group_quantized_g128_amd import profiling
+        kv = profiling.read_kv(prof)
+        if kv.get("source_hash") == profiling.source_hash() and "traffic_bytes[gate_up]" in kv:
+            roof["traffic"] = int(kv["traffic_bytes[gate_up]"])
+            roof["traffic_source"] = os.path.relpath(prof, ROOT)
 
     extra = {}
     if not args.no_extra and args.config == "moe256":

@@ -454,13 +454,26 @@ static hipError_t launch_cfg(const GemmArgs& g, hipStream_t st) {
 #ifndef Q4_DEC_D
 #define Q4_DEC_D 2
 #endif
+// down projection (shorter K, wider N)
+#ifndef Q4_DN_KW
+#define Q4_DN_KW Q4_DEC_KW
+#endif
+#ifndef Q4_DN_NBW
+#define Q4_DN_NBW Q4_DEC_NBW
+#endif
+#ifndef Q4_DN_D
+#define Q4_DN_D Q4_DEC_D
+#endif
 
 // Configuration table: (MB, KW, NBW, D) by row blocks and the column count.
 template <Act A, int KIND, bool W8 = false>
 static hipError_t launch_kind(const GemmArgs& g, int rb, int split, hipStream_t st) {
   if (rb <= 1) {
     constexpr int dec_cb = (4 / Q4_DEC_KW) * Q4_DEC_NBW;
+    constexpr int dn_cb = (4 / Q4_DN_KW) * Q4_DN_NBW;
     if (split && g.N % (16 * 2) == 0) return launch_cfg<A, KIND, 1, 4, 2, 2, W8>(g, st);
+    if (KIND == GEMM_PLAIN && g.N % (16 * dn_cb) == 0)
+      return launch_cfg<A, KIND, 1, Q4_DN_KW, Q4_DN_NBW, Q4_DN_D, W8>(g, st);
     if (g.N % (16 * dec_cb) == 0) return launch_cfg<A, KIND, 1, Q4_DEC_KW, Q4_DEC_NBW, Q4_DEC_D, W8>(g, st);
     return launch_cfg<A, KIND, 1, 4, 2, 2, W8>(g, st);
   }
