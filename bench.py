@@ -381,7 +381,7 @@ def main():
     extra = {}
     if not args.no_extra and args.config == "moe256":
         other = "w4a8" if args.mode == "w4a16" else "w4a16"
-        for t, mode in ((1, args.mode), (4096, args.mode), (1, other), (args.tokens, other)):
+        for t, mode in ((1, args.mode), (4096, args.mode), (1, other), (args.tokens, other), (4096, other)):
             if t == args.tokens and mode == args.mode:
                 continue
             log(f"[bench] extra moe256 T={t} {mode}")
