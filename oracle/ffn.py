@@ -44,7 +44,7 @@ W4A16 gate/up).
 """
 import numpy as np
 
-from .quant import GROUP, dequantize
+from .quant import GROUP, dequantize, group_of
 
 
 def silu(v):
@@ -100,13 +100,14 @@ def widen_int8(qm):
     q, s, z = qm
     q = np.asarray(q, dtype=np.int64)
     if z is not None:
-        q = q - np.repeat(np.asarray(z, dtype=np.int64), GROUP, axis=1)
+        q = q - np.repeat(np.asarray(z, dtype=np.int64), group_of(q.shape[1], s), axis=1)
     assert np.all(np.abs(q) <= 15)
     return q
 
 
-def group_acc(qx, w8):
-    """acc[t, n, g] = sum_{k in group g} qx[t, k] * w8[n, k], exact.
+def group_acc(qx, w8, group=GROUP):
+    """acc[t, n, g] = sum_{k in group g} qx[t, k] * w8[n, k], exact (groups of
+    ``group`` elements along K).
 
     The per-group products are evaluated by a float64 matrix product: every
     operand is an integer with |qx| <= 128 and |w8| <= 127 (<= 15 for 4-bit
@@ -118,20 +119,20 @@ def group_acc(qx, w8):
     assert np.all(np.abs(qx) <= 128) and np.all(np.abs(w8) <= 127)
     t, k = qx.shape
     n = w8.shape[0]
-    g = k // GROUP
+    g = k // group
     qf = qx.astype(np.float64)
     wf = w8.astype(np.float64)
     acc = np.empty((t, n, g), dtype=np.int64)
     for gi in range(g):
-        sl = slice(gi * GROUP, (gi + 1) * GROUP)
+        sl = slice(gi * group, (gi + 1) * group)
         acc[:, :, gi] = (qf[:, sl] @ wf[:, sl].T).astype(np.int64)
     return acc
 
 
 def linear_w4a8(qx, sx, qm):
     """y[t, n] = s_x[t] * sum_g s_w[n, g] * acc[t, n, g] in float64."""
-    _, s, _ = qm
-    acc = group_acc(qx, widen_int8(qm)).astype(np.float64)
+    q, s, _ = qm
+    acc = group_acc(qx, widen_int8(qm), group_of(np.asarray(q).shape[1], s)).astype(np.float64)
     sw = np.asarray(s, dtype=np.float16).astype(np.float64)
     y = np.einsum("tng,ng->tn", acc, sw)
     return np.asarray(sx, dtype=np.float64)[:, None] * y
@@ -237,6 +238,23 @@ def bits_by_hotness(counts, frac8, shared=False):
     bits = np.full(e, 4, dtype=np.int64)
     bits[order[:n8]] = 8
     return list(bits) + ([8] if shared else [])
+
+
+def groups_by_hotness(counts, hot_frac=0.05, cold_share=0.1, shared=False):
+    """Group sizes from hit counts (page "MoE推理优化实战：4bit存储+INT8计算的W4A8路线解析",
+    §5.3: the most-hit experts, its top 5 %, get groups of 32; ordinary experts 64;
+    experts almost no token reaches 128 or even 256): the ceil(hot_frac * E) most-hit
+    experts (ties: lower index first) 32; experts hit less than cold_share times the
+    even share (total hits / E) 256; the others 64; a shared expert (hit by every
+    token) 32."""
+    counts = np.asarray(counts, dtype=np.int64)
+    e = counts.shape[0]
+    n_hot = min(e, int(np.ceil(hot_frac * e - 1e-9)))
+    order = np.lexsort((np.arange(e), -counts))
+    groups = np.full(e, 64, dtype=np.int64)
+    groups[counts * e < cold_share * counts.sum()] = 256
+    groups[order[:n_hot]] = 32
+    return list(groups) + ([32] if shared else [])
 
 
 # ---------------------------------------------------------------- comparison

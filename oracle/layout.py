@@ -23,13 +23,19 @@ k = 128 g + 32 s + 8 kq + e, e in [0, 8), element e at nibble position
 p(e) = [0, 2, 4, 6, 1, 3, 5, 7][e] (bits 4p .. 4p+3): byte j of the word holds
 element j in its low nibble and element j + 4 in its high nibble.
 
-Scales.  Binary16 bits, [N/16][G][16] (same column order), starting at byte
-align256(N K / 2).
+Scales.  Binary16 bits, [N/16][G][SG][16] (same column order), starting at byte
+align256(N K / 2).  SG is the number of scale groups per 128-element tile: 1 for
+the default group of 128, 128 / group for groups of 32 or 64 (entry j of tile g is
+the scale of k in [128 g + j 128/SG, 128 g + (j + 1) 128/SG)), and 1 for groups of
+256, where each tile carries the scale of the 256-group it lies in (both tiles of a
+group hold the same value).  In general entry (tile g, j) holds canonical group
+(128 g + j 128/SG) // group.
 
-Zeros (asymmetric only).  One byte z per (column, group), [N/16][G][16],
-starting after the scales at align256(.) of their end.
+Zeros (asymmetric only; groups of 128 or 256).  One byte z per (column, tile),
+[N/16][G][16] (the zero point of the tile's group), starting after the scales at
+align256(.) of their end.
 
-Total size: align256(N K/2) + align256(2 N G) (+ align256(N G)).
+Total size: align256(N K/2) + align256(2 N G SG) (+ align256(N G)), G = K / 128.
 
 Pinned by (tests/test_oracle_layout.py): unpack(layout(x)) == x on random
 canonical inputs (both column orders, both formats), and a hand-computed
@@ -37,7 +43,7 @@ single-element placement.
 """
 import numpy as np
 
-from .quant import GROUP, unpack_canonical
+from .quant import GROUP, GROUPS, unpack_canonical
 
 NIBBLE_POS = np.array([0, 2, 4, 6, 1, 3, 5, 7])
 
@@ -46,9 +52,14 @@ def _a256(x):
     return (x + 255) // 256 * 256
 
 
-def device_bytes(n, k, asymmetric):
+def sub_groups(group):
+    """Scale groups per 128-element tile."""
+    return 128 // group if group < 128 else 1
+
+
+def device_bytes(n, k, asymmetric, group=GROUP):
     g = k // GROUP
-    total = _a256(n * k // 2) + _a256(2 * n * g)
+    total = _a256(n * k // 2) + _a256(2 * n * g * sub_groups(group))
     if asymmetric:
         total += _a256(n * g)
     return total
@@ -64,17 +75,28 @@ def column_source(n, gate_up):
     return np.where(cb % 2 == 0, 16 * (cb // 2) + c, half + 16 * (cb // 2) + c)
 
 
-def to_device(packed, scale_bits, zeros_packed, n, k, asymmetric, gate_up):
-    """Canonical bytes -> device bytes (uint8 array of device_bytes(n, k, asym))."""
-    if n % (32 if gate_up else 16) or k % GROUP:
+def _scale_source(k, group):
+    """Canonical group index of each device scale entry (tile g, j), shape [G, SG]."""
+    sg = sub_groups(group)
+    g = np.arange(k // GROUP)[:, None]
+    j = np.arange(sg)[None, :]
+    return (GROUP * g + j * (GROUP // sg)) // group
+
+
+def to_device(packed, scale_bits, zeros_packed, n, k, asymmetric, gate_up, group=GROUP):
+    """Canonical bytes -> device bytes (uint8 array of device_bytes(n, k, asym, group))."""
+    if n % (32 if gate_up else 16) or k % GROUP or k % group or group not in GROUPS:
         raise ValueError("shape not supported by the device layout")
+    if asymmetric and group < GROUP:
+        raise ValueError("zero points need groups of 128 or 256")
     g = k // GROUP
-    q, s, z = unpack_canonical(packed, scale_bits, zeros_packed, k, asymmetric)
+    sg = sub_groups(group)
+    q, s, z = unpack_canonical(packed, scale_bits, zeros_packed, k, asymmetric, group)
     d = q + 8 if not asymmetric else q                       # unsigned nibble values
     src = column_source(n, gate_up)
     d = d[src]
     s = s[src]
-    out = np.zeros(device_bytes(n, k, asymmetric), dtype=np.uint8)
+    out = np.zeros(device_bytes(n, k, asymmetric, group), dtype=np.uint8)
     # weights: element (col j, k) -> tile (j//16, k//128), lane, word, nibble
     words = np.zeros(n * k // 8, dtype=np.uint64)
     jj, kk = np.meshgrid(np.arange(n), np.arange(k), indexing="ij")
@@ -87,21 +109,26 @@ def to_device(packed, scale_bits, zeros_packed, n, k, asymmetric, gate_up):
     shift = 4 * NIBBLE_POS[e]
     np.add.at(words, word_index.ravel(), (d.astype(np.uint64) << shift.astype(np.uint64)).ravel())
     out[: n * k // 2] = words.astype("<u4").view(np.uint8)
-    # scales [N/16][G][16]
+    # scales [N/16][G][SG][16]: entry (tile, j) of column j16 from its canonical group
     so = _a256(n * k // 2)
-    sc = s.view(np.uint16).reshape(n // 16, 16, g).transpose(0, 2, 1).reshape(-1)
-    out[so: so + 2 * n * g] = sc.astype("<u2").view(np.uint8)
+    srcg = _scale_source(k, group)                                    # [G, SG]
+    se = s.view(np.uint16)[:, srcg]                                   # [N, G, SG]
+    sc = se.reshape(n // 16, 16, g, sg).transpose(0, 2, 3, 1).reshape(-1)
+    out[so: so + 2 * n * g * sg] = sc.astype("<u2").view(np.uint8)
     if asymmetric:
-        zo = so + _a256(2 * n * g)
-        zz = z[src].reshape(n // 16, 16, g).transpose(0, 2, 1).reshape(-1)
+        zo = so + _a256(2 * n * g * sg)
+        ze = z[src][:, srcg[:, 0]]                                    # [N, G]
+        zz = ze.reshape(n // 16, 16, g).transpose(0, 2, 1).reshape(-1)
         out[zo: zo + n * g] = zz.astype(np.uint8)
     return out
 
 
-def from_device(dev, n, k, asymmetric, gate_up):
-    """Device bytes -> (q int64 [N, K], scale bits uint16 [N, G], zeros int64 [N, G] or None),
-    in canonical row order."""
+def from_device(dev, n, k, asymmetric, gate_up, group=GROUP):
+    """Device bytes -> (q int64 [N, K], scale bits uint16 [N, K/group], zeros int64
+    [N, K/group] or None), in canonical row order (for groups of 256 the scale and zero
+    point are read from the first tile of each group)."""
     g = k // GROUP
+    sg = sub_groups(group)
     dev = np.asarray(dev, dtype=np.uint8)
     words = dev[: n * k // 2].view("<u4").astype(np.int64)
     jj, kk = np.meshgrid(np.arange(n), np.arange(k), indexing="ij")
@@ -113,11 +140,16 @@ def from_device(dev, n, k, asymmetric, gate_up):
     word_index = ((cb * g + gg) * 1024 + lane * 16 + sidx * 4) // 4
     d = (words[word_index] >> (4 * NIBBLE_POS[e])) & 0xF
     so = _a256(n * k // 2)
-    sc = dev[so: so + 2 * n * g].view("<u2").reshape(n // 16, g, 16).transpose(0, 2, 1).reshape(n, g)
+    sc = dev[so: so + 2 * n * g * sg].view("<u2").reshape(n // 16, g, sg, 16).transpose(0, 3, 1, 2)
+    sc = sc.reshape(n, g * sg)
+    if group > GROUP:
+        sc = sc[:, :: group // GROUP]
     zz = None
     if asymmetric:
-        zo = so + _a256(2 * n * g)
+        zo = so + _a256(2 * n * g * sg)
         zz = dev[zo: zo + n * g].reshape(n // 16, g, 16).transpose(0, 2, 1).reshape(n, g).astype(np.int64)
+        if group > GROUP:
+            zz = zz[:, :: group // GROUP]
     q = d if asymmetric else d - 8
     src = column_source(n, gate_up)
     inv = np.empty_like(src)

@@ -25,7 +25,13 @@ Readings where the pages leave a step open (each listed in the design doc):
   q = clamp(rint(w / s) + z, 0, 15);
 * a group whose scale is zero gets s = 0, codes 0 (and z = 0).
 
-Pinned by (tests/test_oracle_quant.py): brute-force nearest-code search over
+Other group sizes (page "MoE推理优化实战：4bit存储+INT8计算的W4A8路线解析", §5.3:
+group sizes 32 / 64 / 128 / 256 chosen per expert by how often it is hit): the same
+definitions with groups of ``group`` elements along K (K a multiple of it); the
+scale tables then have K / group columns.  The group of a quantised matrix is implied
+by its shapes (K / number of scale columns).
+
+Pinned by (tests/test_oracle_quant.py, tests/test_oracle_groups.py): brute-force nearest-code search over
 all 16 codes for every element, the half-step error bound, constructed exact
 ties (half-to-even), the +-7 / code-0 invariants, exhaustive nibble
 round-trip of all 256 bytes, and the packed-size formula against the "about
@@ -34,18 +40,26 @@ a quarter of fp16" statement.
 import numpy as np
 
 GROUP = 128
+GROUPS = (32, 64, 128, 256)
 
 
-def _groups(w):
+def _groups(w, group=GROUP):
     w32 = np.asarray(w, dtype=np.float32)
     if w32.ndim != 2:
         raise ValueError("weight must be 2-D [N, K]")
+    if group not in GROUPS:
+        raise ValueError("group must be 32, 64, 128 or 256")
     n, k = w32.shape
-    if k % GROUP != 0:
-        raise ValueError("K must be a multiple of 128")
+    if k % group != 0:
+        raise ValueError(f"K must be a multiple of {group}")
     if not np.all(np.isfinite(w32)):
         raise ValueError("non-finite weight")
-    return w32.reshape(n, k // GROUP, GROUP)
+    return w32.reshape(n, k // group, group)
+
+
+def group_of(k, scales):
+    """Group size implied by a matrix of K columns and its scale table."""
+    return k // np.asarray(scales).shape[1]
 
 
 def f32_to_f16_up(t):
@@ -62,14 +76,14 @@ def f32_to_f16_up(t):
     return h
 
 
-def quantize_sym(w):
-    """Symmetric INT4 g128 quantisation.
+def quantize_sym(w, group=GROUP):
+    """Symmetric INT4 quantisation (groups of ``group`` along K, 128 by default).
 
-    Returns (q int8 [N, K] in [-8, 7], scales float16 [N, K/128]).
+    Returns (q int8 [N, K] in [-8, 7], scales float16 [N, K/group]).
     Follows §1.3 of the FP32->INT4 guide (per-group scale, no zero point for
     the symmetric variant) with the amax / 7 reading of the scale.
     """
-    wg = _groups(w)
+    wg = _groups(w, group)
     amax = np.max(np.abs(wg), axis=2)                       # exact in fp32
     s16 = (amax / np.float32(7.0)).astype(np.float16)       # fp32 divide, RNE to fp16
     if not np.all(np.isfinite(s16)):
@@ -83,14 +97,14 @@ def quantize_sym(w):
     return q.reshape(np.asarray(w).shape).astype(np.int8), s16
 
 
-def quantize_asym(w):
-    """Asymmetric INT4 g128 quantisation with an unsigned 4-bit zero point.
+def quantize_asym(w, group=GROUP):
+    """Asymmetric INT4 quantisation with an unsigned 4-bit zero point.
 
     Returns (q uint8 [N, K] in [0, 15], scales float16 [N, G], zeros uint8 [N, G]).
     Follows §1.3 of the FP32->INT4 guide (each group computes its own min/max,
     the asymmetric variant stores a zero point).
     """
-    wg = _groups(w)
+    wg = _groups(w, group)
     mn = np.minimum(np.min(wg, axis=2), np.float32(0))
     mx = np.maximum(np.max(wg, axis=2), np.float32(0))
     t = (mx - mn) / np.float32(15.0)                          # fp32 ops, RNE
@@ -140,7 +154,8 @@ def dequantize(q, scales, zeros=None):
     n, k = q.shape
     s = np.asarray(scales, dtype=np.float16).astype(np.float64)
     z = np.zeros_like(s) if zeros is None else np.asarray(zeros, dtype=np.float64)
-    qg = q.reshape(n, k // GROUP, GROUP).astype(np.float64)
+    group = group_of(k, s)
+    qg = q.reshape(n, k // group, group).astype(np.float64)
     return ((qg - z[:, :, None]) * s[:, :, None]).reshape(n, k)
 
 
@@ -170,29 +185,29 @@ def unpack_nibbles(packed, count, signed):
     return out
 
 
-def quantize_pack(w, asymmetric):
+def quantize_pack(w, asymmetric, group=GROUP):
     """Canonical byte layout of one matrix: (packed [N, K/2], scale bits [N, G] as
-    uint16, zeros [N, ceil(G/2)] or None)."""
+    uint16, zeros [N, ceil(G/2)] or None), G = K / group."""
     if asymmetric:
-        q, s, z = quantize_asym(w)
+        q, s, z = quantize_asym(w, group)
         return pack_nibbles(q), s.view(np.uint16), pack_nibbles(z)
-    q, s = quantize_sym(w)
+    q, s = quantize_sym(w, group)
     return pack_nibbles(q), s.view(np.uint16), None
 
 
-def unpack_canonical(packed, scale_bits, zeros_packed, k, asymmetric):
+def unpack_canonical(packed, scale_bits, zeros_packed, k, asymmetric, group=GROUP):
     """Canonical bytes -> (q int64 [N, K], scales float16 [N, G], zeros int64 [N, G] or None)."""
-    g = k // GROUP
+    g = k // group
     q = unpack_nibbles(packed, k, signed=not asymmetric)
     s = np.asarray(scale_bits, dtype=np.uint16).view(np.float16)
     z = unpack_nibbles(zeros_packed, g, signed=False) if asymmetric else None
     return q, s, z
 
 
-def packed_bytes(n, k, asymmetric):
+def packed_bytes(n, k, asymmetric, group=GROUP):
     """Bytes of the canonical format: N*K/2 nibble bytes + 2*N*G scale bytes
-    (+ N*ceil(G/2) zero-point bytes)."""
-    g = k // GROUP
+    (+ N*ceil(G/2) zero-point bytes), G = K / group."""
+    g = k // group
     b = n * k // 2 + 2 * n * g
     if asymmetric:
         b += n * ((g + 1) // 2)
