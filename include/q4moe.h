@@ -137,6 +137,31 @@ Q4_API int q4_repack_device(const uint8_t* packed, const uint16_t* scales, const
                      size_t dev_bytes, hipStream_t stream);
 
 /*
+ * quantize_int4_grouped / q4_device_bytes_grouped / q4_repack_device_grouped -- INT4
+ * weights with groups of 32, 64, 128 or 256 along K (page "MoE推理优化实战：4bit存储+
+ * INT8计算的W4A8路线解析", §5.3: the group size chosen per expert by how often it is
+ * hit -- 32 for the hottest, 64 for ordinary, 128 or 256 for rarely used experts).
+ * The same definitions as quantize_int4_g128 over groups of `group` elements; group
+ * 128 gives exactly quantize_int4_g128 / q4_device_bytes / q4_repack_device.
+ *  scales   device [n][k/group] binary16; zeros [n][ceil((k/group)/2)] (asymmetric).
+ *  Requires group in {32, 64, 128, 256}, k % 128 == 0 and k % group == 0; zero points
+ *  (asymmetric) only with groups of 128 or 256 (Q4_ERR_UNSUPPORTED otherwise).
+ * Device layout: the weight tiles of q4_repack_device (they do not depend on the
+ * group); scales binary16 [n/16][k/128][SG][16] with SG = 128 / group scale entries
+ * per 1 KB tile for groups of 32 or 64 (entry j covers k in
+ * [128 g + j 128/SG, 128 g + (j + 1) 128/SG)) and SG = 1 otherwise, a 256-group's
+ * scale repeated on both of its tiles; zeros (asymmetric) one byte per (column,
+ * tile), [n/16][k/128][16], the tile's group's zero point.
+ */
+Q4_API int quantize_int4_grouped(const void* w, int w_dtype, int64_t n, int64_t k, int32_t group,
+                                 int asymmetric, uint8_t* packed, uint16_t* scales, uint8_t* zeros,
+                                 int32_t* flags_dev, hipStream_t stream);
+Q4_API size_t q4_device_bytes_grouped(int64_t n, int64_t k, int asymmetric, int32_t group);
+Q4_API int q4_repack_device_grouped(const uint8_t* packed, const uint16_t* scales, const uint8_t* zeros,
+                                    int64_t n, int64_t k, int asymmetric, int32_t group, int flags,
+                                    void* dev_out, size_t dev_bytes, hipStream_t stream);
+
+/*
  * quantize_int8_g128 / q8_device_bytes / q8_repack_device -- INT8 g128 weights for the
  * W8A8 comparison route (page "MoE推理优化实战：4bit存储+INT8计算的W4A8路线解析":
  * W8A8 = INT8 weights and INT8 compute, the accuracy-safe route to set up first).
@@ -236,6 +261,15 @@ typedef struct q4_moe_layer_t {
   const uint8_t* expert_bits;      /* device [num_experts + shared] values 4 or 8 */
   const int64_t* gate_up_offsets;  /* device [num_experts] */
   const int64_t* down_offsets;     /* device [num_experts] */
+  /* Per-expert group size (page "MoE推理优化实战：4bit存储+INT8计算的W4A8路线解析",
+   * §5.3: smaller groups for hotter experts).  When expert_groups != NULL: weight_bits
+   * 0, asymmetric 0, the block offsets above are required, and expert e's blocks hold
+   * q4_repack_device_grouped output for its group (q4_device_bytes_grouped(2I, H, 0,
+   * group) and (H, I, 0, group) bytes); modes W4A16 and W4A8 (W4A8 only if expert_bits
+   * is also given, in which case 8-bit experts must have group 128).  The values are
+   * the group size / 32 (1, 2, 4 or 8); the shared expert's is expert_groups[num_experts].
+   * Invalid values make the expert's tiles be skipped (its output rows undefined). */
+  const uint8_t* expert_groups;    /* device [num_experts + shared] values 1, 2, 4 or 8 */
 } q4_moe_layer_t;
 
 /*

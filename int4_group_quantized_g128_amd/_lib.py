@@ -42,6 +42,7 @@ class Q4MoELayer(ctypes.Structure):
         ("gate_up", _vp), ("down", _vp), ("shared_gate_up", _vp), ("shared_down", _vp),
         ("weight_bits", _i32),
         ("expert_bits", _vp), ("gate_up_offsets", _vp), ("down_offsets", _vp),
+        ("expert_groups", _vp),
     ]
 
 
@@ -77,6 +78,9 @@ _sig("q4_version", ctypes.c_char_p, [])
 _sig("quantize_int4_g128", _int, [_vp, _int, _i64, _i64, _int, _vp, _vp, _vp, _vp, _vp])
 _sig("q4_device_bytes", _sz, [_i64, _i64, _int])
 _sig("q4_repack_device", _int, [_vp, _vp, _vp, _i64, _i64, _int, _int, _vp, _sz, _vp])
+_sig("quantize_int4_grouped", _int, [_vp, _int, _i64, _i64, _i32, _int, _vp, _vp, _vp, _vp, _vp])
+_sig("q4_device_bytes_grouped", _sz, [_i64, _i64, _int, _i32])
+_sig("q4_repack_device_grouped", _int, [_vp, _vp, _vp, _i64, _i64, _int, _i32, _int, _vp, _sz, _vp])
 _sig("quantize_int8_g128", _int, [_vp, _int, _i64, _i64, _vp, _vp, _vp, _vp])
 _sig("q8_device_bytes", _sz, [_i64, _i64])
 _sig("q8_repack_device", _int, [_vp, _vp, _i64, _i64, _int, _vp, _sz, _vp])
@@ -202,6 +206,40 @@ def q4_device_bytes(n, k, asymmetric=False):
     return int(_lib.q4_device_bytes(n, k, int(bool(asymmetric))))
 
 
+def quantize_int4_grouped(w, group, asymmetric=False, flags=None):
+    """INT4 quantisation of w [n, k] with groups of `group` (32, 64, 128, 256) along k ->
+    (packed u8 [n, k/2], scales int16 [n, k/group] (binary16 bits), zeros u8 or None)."""
+    _need(w, (torch.float32, torch.float16, torch.bfloat16), "w", 2)
+    n, k = w.shape
+    g = max(k // group, 1)
+    packed = torch.empty((n, k // 2), dtype=torch.uint8, device=w.device)
+    scales = torch.empty((n, g), dtype=torch.int16, device=w.device)
+    zeros = torch.empty((n, (g + 1) // 2), dtype=torch.uint8, device=w.device) if asymmetric else None
+    _check("quantize_int4_grouped", _lib.quantize_int4_grouped(
+        _ptr(w), _DT[w.dtype], n, k, group, int(bool(asymmetric)), _ptr(packed), _ptr(scales), _ptr(zeros),
+        _ptr(flags), _stream()))
+    return packed, scales, zeros
+
+
+def q4_device_bytes_grouped(n, k, asymmetric=False, group=128):
+    return int(_lib.q4_device_bytes_grouped(n, k, int(bool(asymmetric)), group))
+
+
+def q4_repack_device_grouped(packed, scales, zeros, n, k, group, asymmetric=False, gate_up=False, out=None):
+    """Canonical bytes (groups of `group`) -> device tile layout with SG scale entries per tile."""
+    _need(packed, torch.uint8, "packed")
+    _need(scales, torch.int16, "scales")
+    if zeros is not None:
+        _need(zeros, torch.uint8, "zeros")
+    nbytes = q4_device_bytes_grouped(n, k, asymmetric, group)
+    if out is None:
+        out = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=packed.device)
+    _check("q4_repack_device_grouped", _lib.q4_repack_device_grouped(
+        _ptr(packed), _ptr(scales), _ptr(zeros), n, k, int(bool(asymmetric)), group,
+        Q4_REPACK_GATE_UP if gate_up else Q4_REPACK_PLAIN, _ptr(out), out.numel(), _stream()))
+    return out
+
+
 def q4_repack_device(packed, scales, zeros, n, k, asymmetric=False, gate_up=False, out=None):
     """Canonical bytes -> device tile layout (u8 tensor of q4_device_bytes bytes)."""
     _need(packed, torch.uint8, "packed")
@@ -282,6 +320,25 @@ def expert_bits_by_hotness(counts, frac8=0.05, shared=False):
     return bits + ([8] if shared else [])
 
 
+def expert_groups_by_hotness(counts, hot_frac=0.05, cold_share=0.1, shared=False):
+    """Per-expert group sizes from routing hit counts (page "MoE推理优化实战：4bit存储+
+    INT8计算的W4A8路线解析", §5.3: groups of 32 for the most-hit experts, 64 for ordinary
+    ones, 128 or 256 for experts almost no token reaches): the ceil(hot_frac * E)
+    most-hit experts (equal counts: lower index first) 32, experts hit less than
+    cold_share times the even share (total / E) 256, the others 64; with a shared
+    expert (hit by every token) one more entry, 32."""
+    counts = [int(c) for c in counts]
+    e = len(counts)
+    if not 0.0 <= hot_frac <= 1.0:
+        raise ValueError("hot_frac must lie in [0, 1]")
+    total = sum(counts)
+    groups = [256 if c * e < cold_share * total else 64 for c in counts]
+    n_hot = min(e, int(math.ceil(hot_frac * e - 1e-9)))
+    for i in sorted(range(e), key=lambda i: (-counts[i], i))[:n_hot]:
+        groups[i] = 32
+    return groups + ([32] if shared else [])
+
+
 class MoELayer:
     """Device-resident MoE layer (experts in the device tile layouts).
 
@@ -290,30 +347,43 @@ class MoELayer:
     expert, for a mixed symmetric layer run in W4A8 (INT8 activations everywhere)."""
 
     def __init__(self, num_experts, hidden, inter, top_k, asymmetric=False, shared=False, device="cuda",
-                 weight_bits=4, expert_bits=None):
+                 weight_bits=4, expert_bits=None, expert_groups=None):
         self.num_experts, self.hidden, self.inter, self.top_k = num_experts, hidden, inter, top_k
         self.asymmetric = bool(asymmetric)
         self.shared = bool(shared)
         if weight_bits not in (4, 8) or (weight_bits == 8 and asymmetric):
             raise ValueError("weight_bits must be 4, or 8 with symmetric weights")
-        self.mixed = expert_bits is not None
-        if self.mixed:
+        self.mixed = expert_bits is not None or expert_groups is not None
+        nexp = num_experts + int(self.shared)
+        if expert_groups is not None:
+            groups = [int(g) for g in expert_groups]
+            if len(groups) != nexp or any(g not in (32, 64, 128, 256) for g in groups):
+                raise ValueError("expert_groups needs one group size (32, 64, 128, 256) per expert (and shared)")
+            if asymmetric:
+                raise ValueError("layers with per-expert group sizes are symmetric")
+        else:
+            groups = [128] * nexp
+        self.groups = groups
+        if expert_bits is not None:
             bits = [int(b) for b in expert_bits]
             if len(bits) != num_experts + int(self.shared) or any(b not in (4, 8) for b in bits):
                 raise ValueError("expert_bits needs one width, 4 or 8, per expert (and the shared expert)")
             if asymmetric:
                 raise ValueError("mixed layers are symmetric")
         else:
-            bits = [weight_bits] * (num_experts + int(self.shared))
+            bits = [weight_bits] * nexp
+        if any(b == 8 and g != 128 for b, g in zip(bits, groups)):
+            raise ValueError("8-bit experts use groups of 128")
         self.bits = bits
         self.weight_bits = 0 if self.mixed else weight_bits
 
-        def sizes(b):
+        def sizes(b, g):
             if b == 8:
                 return q8_device_bytes(2 * inter, hidden), q8_device_bytes(hidden, inter)
-            return q4_device_bytes(2 * inter, hidden, asymmetric), q4_device_bytes(hidden, inter, asymmetric)
+            return (q4_device_bytes_grouped(2 * inter, hidden, asymmetric, g),
+                    q4_device_bytes_grouped(hidden, inter, asymmetric, g))
 
-        sz = [sizes(b) for b in bits]
+        sz = [sizes(b, g) for b, g in zip(bits, groups)]
         if any(a == 0 or b == 0 for a, b in sz):
             raise ValueError("hidden and inter must be multiples of 128")
         self.gu_offs, self.dn_offs = [0], [0]
@@ -326,16 +396,19 @@ class MoELayer:
         self.shared_gate_up = torch.empty(sz[-1][0], dtype=torch.uint8, device=device) if shared else None
         self.shared_down = torch.empty(sz[-1][1], dtype=torch.uint8, device=device) if shared else None
         if self.mixed:
-            self.bits_dev = torch.tensor(bits, dtype=torch.uint8, device=device)
+            self.bits_dev = torch.tensor(bits, dtype=torch.uint8, device=device) if expert_bits is not None else None
+            self.groups_dev = (torch.tensor([g // 32 for g in groups], dtype=torch.uint8, device=device)
+                               if expert_groups is not None else None)
             self.gu_offs_dev = torch.tensor(self.gu_offs[:-1], dtype=torch.int64, device=device)
             self.dn_offs_dev = torch.tensor(self.dn_offs[:-1], dtype=torch.int64, device=device)
         self.desc = Q4MoELayer(num_experts, hidden, inter, top_k, int(self.asymmetric),
                                inter if shared else 0, self.gate_up.data_ptr(), self.down.data_ptr(),
                                self.shared_gate_up.data_ptr() if shared else None,
                                self.shared_down.data_ptr() if shared else None, self.weight_bits,
-                               self.bits_dev.data_ptr() if self.mixed else None,
+                               self.bits_dev.data_ptr() if self.mixed and self.bits_dev is not None else None,
                                self.gu_offs_dev.data_ptr() if self.mixed else None,
-                               self.dn_offs_dev.data_ptr() if self.mixed else None)
+                               self.dn_offs_dev.data_ptr() if self.mixed else None,
+                               self.groups_dev.data_ptr() if self.mixed and self.groups_dev is not None else None)
 
     def weight_bytes(self):
         """Device bytes of all expert weights."""
@@ -361,6 +434,15 @@ class MoELayer:
             q8_repack_device(q, s, 2 * I, H, gate_up=True, out=gu_out)
             q, s = quantize_int8_g128(down.contiguous())
             q8_repack_device(q, s, H, I, gate_up=False, out=dn_out)
+            return
+        if self.groups[e] != 128:
+            grp = self.groups[e]
+            pg, sg_, _ = quantize_int4_grouped(gate.contiguous(), grp)
+            pu, su, _ = quantize_int4_grouped(up.contiguous(), grp)
+            q4_repack_device_grouped(torch.cat([pg, pu], 0), torch.cat([sg_, su], 0), None, 2 * I, H, grp,
+                                     gate_up=True, out=gu_out)
+            dp, ds, _ = quantize_int4_grouped(down.contiguous(), grp)
+            q4_repack_device_grouped(dp, ds, None, H, I, grp, out=dn_out)
             return
         g = H // 128
         dev = gate.device

@@ -78,8 +78,16 @@ int wbits_of(const q4_moe_layer_t* L) { return L->weight_bits == 8 ? 8 : 4; }
 // Device bytes of one [n][k] expert matrix in the layer's weight format (the larger,
 // 8-bit, size for mixed layers).
 int64_t mat_bytes(const q4_moe_layer_t* L, int64_t n, int64_t k) {
-  return (wbits_of(L) == 8 || L->expert_bits) ? int64_t(q8_device_bytes(n, k))
-                                              : int64_t(q4_device_bytes(n, k, L->asymmetric));
+  if (wbits_of(L) == 8 || L->expert_bits) return int64_t(q8_device_bytes(n, k));
+  if (L->expert_groups) return int64_t(q4_device_bytes_grouped(n, k, 0, 32));   // the largest scale table
+  return int64_t(q4_device_bytes(n, k, L->asymmetric));
+}
+
+// Arithmetic modes a layer supports.
+bool mode_ok(const q4_moe_layer_t* L, int mode) {
+  if (L->expert_bits) return mode == Q4_W4A8;
+  if (wbits_of(L) == 8) return mode == Q4_W8A8;
+  return mode == Q4_W4A16 || mode == Q4_W4A8;
 }
 
 // Average routed rows per expert decides the GEMM shape: 16-row decode tiles, 32 / 64-row
@@ -132,8 +140,9 @@ FwdWorkspace carve(const q4_moe_layer_t* L, int64_t t, int mode, void* base) {
     w.sh = reinterpret_cast<float*>(take(P * 4));
   }
   if (w.prefill && (mode == Q4_W4A16 || L->asymmetric)) {
-    w.rs_x = take(t * (H / 128) * 4);
-    w.rs_h = take(P * (I / 128) * 4);
+    const int64_t sg = L->expert_groups ? 4 : 1;   // sums per 128-element group (finest: groups of 32)
+    w.rs_x = take(t * (H / 128) * sg * 4);
+    w.rs_h = take(P * (I / 128) * sg * 4);
   }
   w.bytes = off;
   return w;
@@ -159,6 +168,11 @@ int validate_layer(const q4_moe_layer_t* L) {
     Q4_REQUIRE(L->weight_bits == 0 && L->asymmetric == 0, Q4_ERR_UNSUPPORTED,
                "mixed layers: weight_bits 0 and symmetric weights");
     Q4_REQUIRE(L->gate_up_offsets && L->down_offsets, Q4_ERR_NULL, "mixed layers need the block offsets");
+  }
+  if (L->expert_groups) {
+    Q4_REQUIRE(L->weight_bits == 0 && L->asymmetric == 0, Q4_ERR_UNSUPPORTED,
+               "per-expert group sizes: weight_bits 0 and symmetric weights");
+    Q4_REQUIRE(L->gate_up_offsets && L->down_offsets, Q4_ERR_NULL, "per-expert group sizes need the block offsets");
   }
   if (L->shared_inter != 0) {
     Q4_REQUIRE(L->shared_inter == L->inter, Q4_ERR_UNSUPPORTED,
@@ -230,6 +244,59 @@ size_t q4_device_bytes(int64_t n, int64_t k, int asymmetric) {
   int64_t b = a256(n * k / 2) + a256(2 * n * g);
   if (asymmetric) b += a256(n * g);
   return size_t(b);
+}
+
+static bool valid_group(int32_t g) { return g == 32 || g == 64 || g == 128 || g == 256; }
+
+int quantize_int4_grouped(const void* w, int w_dtype, int64_t n, int64_t k, int32_t group, int asymmetric,
+                          uint8_t* packed, uint16_t* scales, uint8_t* zeros, int32_t* flags_dev, hipStream_t stream) {
+  g_last_error.clear();
+  Q4_REQUIRE(valid_group(group), Q4_ERR_SHAPE, "group %d not in {32, 64, 128, 256}", group);
+  Q4_REQUIRE(!asymmetric || group >= 128, Q4_ERR_UNSUPPORTED, "zero points need groups of 128 or 256");
+  Q4_REQUIRE(k % 128 == 0 && k % group == 0, Q4_ERR_SHAPE, "k must be a multiple of 128 and of the group");
+  if (group == 128) return quantize_int4_g128(w, w_dtype, n, k, asymmetric, packed, scales, zeros, flags_dev, stream);
+  Q4_REQUIRE(w_dtype == Q4_F32 || w_dtype == Q4_F16 || w_dtype == Q4_BF16, Q4_ERR_DTYPE, "w_dtype %d", w_dtype);
+  Q4_REQUIRE(asymmetric == 0 || asymmetric == 1, Q4_ERR_SHAPE, "asymmetric must be 0 or 1");
+  Q4_REQUIRE(n >= 1 && k >= 128, Q4_ERR_SHAPE, "need n >= 1 and k >= 128");
+  Q4_REQUIRE(n * (k / 512 + 1) < (int64_t(1) << 31), Q4_ERR_SHAPE, "matrix too large");
+  Q4_REQUIRE(w && packed && scales, Q4_ERR_NULL, "w, packed and scales are required");
+  Q4_REQUIRE(asymmetric ? zeros != nullptr : zeros == nullptr, Q4_ERR_NULL,
+             "zeros must be given iff asymmetric");
+  Q4_REQUIRE(!misaligned(w) && !misaligned(packed) && !misaligned(scales) && !(zeros && misaligned(zeros)),
+             Q4_ERR_ALIGN, "device pointers must be 16-byte aligned");
+  return check_hip(launch_quantize_grouped(w, w_dtype, n, k, group, asymmetric, packed, scales, zeros, flags_dev,
+                                           stream),
+                   "grouped quantize launch");
+}
+
+size_t q4_device_bytes_grouped(int64_t n, int64_t k, int asymmetric, int32_t group) {
+  if (!valid_group(group) || (asymmetric && group < 128) || k % group) return 0;
+  if (n < 16 || n % 16 || k < 128 || k % 128) return 0;
+  const int64_t g = k / 128, sg = group < 128 ? 128 / group : 1;
+  int64_t b = a256(n * k / 2) + a256(2 * n * g * sg);
+  if (asymmetric) b += a256(n * g);
+  return size_t(b);
+}
+
+int q4_repack_device_grouped(const uint8_t* packed, const uint16_t* scales, const uint8_t* zeros, int64_t n,
+                             int64_t k, int asymmetric, int32_t group, int flags, void* dev_out, size_t dev_bytes,
+                             hipStream_t stream) {
+  g_last_error.clear();
+  Q4_REQUIRE(valid_group(group), Q4_ERR_SHAPE, "group %d not in {32, 64, 128, 256}", group);
+  Q4_REQUIRE(!asymmetric || group >= 128, Q4_ERR_UNSUPPORTED, "zero points need groups of 128 or 256");
+  Q4_REQUIRE(k % group == 0, Q4_ERR_SHAPE, "k must be a multiple of the group");
+  Q4_REQUIRE(flags == Q4_REPACK_PLAIN || flags == Q4_REPACK_GATE_UP, Q4_ERR_DTYPE, "flags %d", flags);
+  Q4_REQUIRE(asymmetric == 0 || asymmetric == 1, Q4_ERR_SHAPE, "asymmetric must be 0 or 1");
+  Q4_REQUIRE(k >= 128 && k % 128 == 0 && n >= 16 && n % (flags == Q4_REPACK_GATE_UP ? 32 : 16) == 0,
+             Q4_ERR_SHAPE, "need k %% 128 == 0 and n %% %d == 0", flags == Q4_REPACK_GATE_UP ? 32 : 16);
+  Q4_REQUIRE(packed && scales && dev_out, Q4_ERR_NULL, "packed, scales and dev_out are required");
+  Q4_REQUIRE(!asymmetric || zeros, Q4_ERR_NULL, "zeros required for the asymmetric format");
+  Q4_REQUIRE(!misaligned(packed) && !misaligned(dev_out), Q4_ERR_ALIGN, "device pointers must be 16-byte aligned");
+  const size_t need = q4_device_bytes_grouped(n, k, asymmetric, group);
+  Q4_REQUIRE(dev_bytes >= need, Q4_ERR_WORKSPACE, "dev_out holds %zu bytes, need %zu", dev_bytes, need);
+  return check_hip(launch_repack(packed, scales, zeros, n, k, asymmetric, flags == Q4_REPACK_GATE_UP, dev_out, stream,
+                                 group),
+                   "repack launch");
 }
 
 int q4_repack_device(const uint8_t* packed, const uint16_t* scales, const uint8_t* zeros, int64_t n, int64_t k,
@@ -323,9 +390,7 @@ int act_quant_int8(const void* x, int x_dtype, int64_t rows, int64_t cols, int8_
 
 size_t moe_int4_ffn_workspace_bytes(const q4_moe_layer_t* layer, int64_t t, int mode) {
   if (!layer || t < 0 || validate_layer(layer) != Q4_OK) return 0;
-  if (layer->expert_bits ? mode != Q4_W4A8
-                         : (wbits_of(layer) == 8 ? mode != Q4_W8A8 : (mode != Q4_W4A16 && mode != Q4_W4A8)))
-    return 0;
+  if (!mode_ok(layer, mode)) return 0;
   return size_t(carve(layer, t, mode, nullptr).bytes);
 }
 
@@ -337,9 +402,7 @@ int ffn_forward(const q4_moe_layer_t* L, const uint16_t* x_bf16, int64_t t, cons
   g_last_error.clear();
   if (views) *views = q4_ffn_views_t{};
   if (int rc = validate_layer(L)) return rc;
-  Q4_REQUIRE(L->expert_bits ? mode == Q4_W4A8
-                             : (wbits_of(L) == 8 ? mode == Q4_W8A8 : (mode == Q4_W4A16 || mode == Q4_W4A8)),
-             Q4_ERR_DTYPE, "mode %d does not match the layer's weight format", mode);
+  Q4_REQUIRE(mode_ok(L, mode), Q4_ERR_DTYPE, "mode %d does not match the layer's weight format", mode);
   Q4_REQUIRE(t >= 0, Q4_ERR_SHAPE, "t < 0");
   if (t == 0) return ok();
   const int shared = L->shared_inter > 0 ? 1 : 0;
@@ -381,7 +444,9 @@ int ffn_forward(const q4_moe_layer_t* L, const uint16_t* x_bf16, int64_t t, cons
   gu.w = static_cast<const uint8_t*>(L->gate_up);
   gu.w_stride = mat_bytes(L, 2 * I, H);
   gu.wbits = wbits_of(L);
+  gu.sg = 1;
   gu.ebits = L->expert_bits;
+  gu.egroups = L->expert_groups;
   gu.woffs = L->gate_up_offsets;
   gu.w_shared = static_cast<const uint8_t*>(L->shared_gate_up);
   gu.num_experts = L->num_experts;
@@ -406,14 +471,28 @@ int ffn_forward(const q4_moe_layer_t* L, const uint16_t* x_bf16, int64_t t, cons
   auto gemm1 = [&](const GemmArgs& g, int act, int kind) {
     return w.prefill ? launch_gemm_prefill(g, act, kind, stream) : launch_gemm(g, act, kind, rb, stream);
   };
-  // mixed layers: one launch per weight format, each skipping the other format's experts
-  auto gemm = [&](const GemmArgs& g, int act, int kind) {
-    if (!g.ebits) return gemm1(g, act, kind);
-    GemmArgs g4 = g, g8 = g;
-    g4.wbits = 4;
-    g8.wbits = 8;
-    const hipError_t e = gemm1(g4, act, kind);
-    return e != hipSuccess ? e : gemm1(g8, act, kind);
+  // Layers whose experts differ in width or group size: one launch per format (width,
+  // scale entries per tile), each skipping the tiles of other formats.  The bf16 prefill
+  // kernel reads activation sums per scale group; they are recomputed at each launch's
+  // granularity (rs_a: the activations, rs_rows their rows) before it.
+  auto gemm = [&](const GemmArgs& g, int act, int kind, const void* rs_a = nullptr, int64_t rs_rows = 0) {
+    if (!g.ebits && !g.egroups) return gemm1(g, act, kind);
+    const int widths = g.ebits ? 2 : 1;
+    for (int wi = 0; wi < widths; ++wi) {
+      for (int sg = 1; sg <= 4; sg *= 2) {
+        if (sg > 1 && (!g.egroups || wi == 1)) continue;
+        GemmArgs a = g;
+        a.wbits = wi ? 8 : 4;
+        a.sg = sg;
+        if (rs_a && a.a_gsum) {
+          const hipError_t e = launch_rowsum(rs_a, 0, rs_rows, a.K, const_cast<float*>(a.a_gsum), stream, sg);
+          if (e != hipSuccess) return e;
+        }
+        const hipError_t e = gemm1(a, act, kind);
+        if (e != hipSuccess) return e;
+      }
+    }
+    return hipSuccess;
   };
   if (mode == Q4_W4A16) {
     gu.a = x_bf16;
@@ -426,7 +505,7 @@ int ffn_forward(const q4_moe_layer_t* L, const uint16_t* x_bf16, int64_t t, cons
       dn.a_gsum = static_cast<const float*>(w.rs_h);
     }
     stage_begin(Q4_STAGE_GATE_UP, stream);
-    if ((rc = check_hip(gemm(gu, 0, GEMM_GATE_UP), "gate/up gemm"))) return rc;
+    if ((rc = check_hip(gemm(gu, 0, GEMM_GATE_UP, x_bf16, t), "gate/up gemm"))) return rc;
     stage_end(Q4_STAGE_GATE_UP, stream);
     if (w.prefill) {
       stage_begin(Q4_STAGE_H_QUANT, stream);
@@ -434,7 +513,7 @@ int ffn_forward(const q4_moe_layer_t* L, const uint16_t* x_bf16, int64_t t, cons
       stage_end(Q4_STAGE_H_QUANT, stream);
     }
     stage_begin(Q4_STAGE_DOWN, stream);
-    if ((rc = check_hip(gemm(dn, 0, GEMM_PLAIN), "down gemm"))) return rc;
+    if ((rc = check_hip(gemm(dn, 0, GEMM_PLAIN, w.h, t * S), "down gemm"))) return rc;
     stage_end(Q4_STAGE_DOWN, stream);
   } else {
     stage_begin(Q4_STAGE_X_QUANT, stream);

@@ -128,6 +128,14 @@ Q4_DEVICE i32x4_t mfma_i8_16x16x64(u32x4_t a, u32x4_t b, i32x4_t c) {
   return __builtin_amdgcn_mfma_i32_16x16x64_i8(bitcast<i32x4_t>(a), bitcast<i32x4_t>(b), c, 0, 0, 0);
 }
 
+// INT8 16x16x32: lane (row l % 16, quarter l / 16) holds k = 8 (l / 16) .. + 7 of A and
+// B, 8 bytes each -- the first or second 8 bytes of a 16x16x64 operand.
+Q4_DEVICE i32x4_t mfma_i8_16x16x32(uint32_t a0, uint32_t a1, uint32_t b0, uint32_t b1, i32x4_t c) {
+  const long a = static_cast<long>((uint64_t(a1) << 32) | a0);
+  const long b = static_cast<long>((uint64_t(b1) << 32) | b0);
+  return __builtin_amdgcn_mfma_i32_16x16x32_i8(a, b, c, 0, 0, 0);
+}
+
 Q4_DEVICE f32x4_t mfma_f32_16x16x4(float a, float b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }

@@ -104,9 +104,11 @@ struct RowInfo {
 //  D   depth of the register pipeline (groups whose loads are in flight),
 //  W8  8-bit weights (2 KB tiles, int8 activations, no widening) instead of 4-bit.
 // The workgroup's scales (and zero points) are staged in LDS once per work item.
-template <Act A, int KIND, bool ASYM, int MB, int KW, int NBW, int D, bool W8>
+template <Act A, int KIND, bool ASYM, int MB, int KW, int NBW, int D, bool W8, int SG>
 __global__ void __launch_bounds__(256) k_gemm(GemmArgs args) {
   static_assert(!W8 || (A == Act::I8 && !ASYM), "8-bit weights: symmetric, int8 activations");
+  // SG scale entries per 1 KB tile (groups of 128 / SG elements): symmetric 4-bit only
+  static_assert(SG == 1 || (!ASYM && !W8 && KIND != GEMM_GROUP_ACC && (SG == 2 || SG == 4)), "scale groups");
   constexpr int64_t TB = W8 ? 2 * kTileBytes : kTileBytes;   // bytes per (column block, group) tile
   constexpr int kColGroups = 4 / KW;
   constexpr int kCBWG = kColGroups * NBW;  // column blocks per workgroup
@@ -121,13 +123,13 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs args) {
   const int64_t ntiles = args.tiles ? int64_t(*args.num_tiles) : (args.dense_rows + tile_rows - 1) / tile_rows;
   const int64_t items = ntiles * nblk;
   const int64_t w_scale_off = align256(W8 ? N * K : N * K / 2);
-  const int64_t w_zero_off = w_scale_off + align256(2 * N * G);
+  const int64_t w_zero_off = w_scale_off + align256(2 * N * G * SG);
   const int64_t gper = (G + KW - 1) / KW;
   const int64_t g_beg = std::min<int64_t>(G, kw * gper), g_end = std::min<int64_t>(G, g_beg + gper);
-  // LDS: scales [kCBWG][G][16] fp16, zero points [kCBWG][G][16] u8, reduction buffer
+  // LDS: scales [kCBWG][G][SG][16] fp16, zero points [kCBWG][G][16] u8, reduction buffer
   uint16_t* s_scale = reinterpret_cast<uint16_t*>(smem);
-  uint8_t* s_zero = smem + align256(int64_t(kCBWG) * G * 32);
-  float* s_red = reinterpret_cast<float*>(smem + align256(int64_t(kCBWG) * G * 32) +
+  uint8_t* s_zero = smem + align256(int64_t(kCBWG) * G * 32 * SG);
+  float* s_red = reinterpret_cast<float*>(smem + align256(int64_t(kCBWG) * G * 32 * SG) +
                                           (ASYM ? align256(int64_t(kCBWG) * G * 16) : 0));
 
   for (int64_t item = blockIdx.x; item < items; item += gridDim.x) {
@@ -145,14 +147,15 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs args) {
       rows = std::min<int64_t>(tile_rows, args.dense_rows - row_start);
     }
     if (args.ebits && args.ebits[expert] != (W8 ? 8 : 4)) continue;   // other format (uniform skip)
+    if (args.egroups && sg_of_code(args.egroups[expert]) != SG) continue;
     const uint8_t* wbase = expert >= args.num_experts ? args.w_shared
                            : args.woffs                 ? args.w + args.woffs[expert]
                                                         : args.w + int64_t(expert) * args.w_stride;
 
     // stage the workgroup's scales / zero points (contiguous in the device layout)
     {
-      const uint4* src = reinterpret_cast<const uint4*>(wbase + w_scale_off + cb0 * G * 32);
-      const int64_t n16 = int64_t(kCBWG) * G * 2;
+      const uint4* src = reinterpret_cast<const uint4*>(wbase + w_scale_off + cb0 * G * 32 * SG);
+      const int64_t n16 = int64_t(kCBWG) * G * 2 * SG;
       for (int64_t i = threadIdx.x; i < n16; i += 256) reinterpret_cast<uint4*>(s_scale)[i] = src[i];
       if constexpr (ASYM) {
         const uint8_t* zsrc = wbase + w_zero_off + cb0 * G * 16;
@@ -181,7 +184,7 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs args) {
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
       ap[mb] = static_cast<const uint8_t*>(args.a) + (ri[mb].src * K + 8 * kq) * (A == Act::I8 ? 1 : 2);
-    const int sbase = (lcb * int(G)) * 16 + col;
+    const int sbase = (lcb * int(G) * SG) * 16 + col;
 
     f32x4_t acc[MB][NBW];
 #pragma unroll
@@ -223,27 +226,32 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs args) {
         }
       }
     };
+    constexpr int SPS = 4 / SG;   // 32-element K steps per scale group
     auto compute_stage = [&](const Stage& st, int g) {
-      float sc[NBW], zp[NBW];
+      float sc[NBW][SG], zp[NBW];
 #pragma unroll
       for (int nb = 0; nb < NBW; ++nb) {
-        const int li = sbase + (nb * int(G) + g) * 16;
-        sc[nb] = f16_bits_to_f32(s_scale[li]);
-        zp[nb] = ASYM ? float(s_zero[li]) : 8.0f;
+        const int li = sbase + (nb * int(G) + g) * SG * 16;
+#pragma unroll
+        for (int j = 0; j < SG; ++j) sc[nb][j] = f16_bits_to_f32(s_scale[li + j * 16]);
+        zp[nb] = ASYM ? float(s_zero[li]) : 8.0f;   // SG == 1 with zero points
       }
       if constexpr (A == Act::BF16) {
         // The correction -(magic + z) * sum x enters as the initial accumulator.  Its row
         // sums come from the matrix core: B = -(128 + 8) for symmetric weights (one
         // product serves every column), B = 1 then a per-column multiply otherwise.
-        f32x4_t ini[MB];
+        // (per scale group: the sums run over its own K steps)
+        f32x4_t ini[MB][SG];
         const uint32_t cb = ASYM ? 0x3f803f80u : 0xc308c308u;   // bf16 1.0 / -136.0
         const uint32_t cvec[4] = {cb, cb, cb, cb};
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-          ini[mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-          for (int s = 0; s < 4; ++s) ini[mb] = mfma16x16x32<A>(st.av[mb][s], cvec, ini[mb]);
-        }
+          for (int j = 0; j < SG; ++j) {
+            ini[mb][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = j * SPS; s < (j + 1) * SPS; ++s) ini[mb][j] = mfma16x16x32<A>(st.av[mb][s], cvec, ini[mb][j]);
+          }
 #pragma unroll
         for (int nb = 0; nb < NBW; ++nb) {
           uint32_t b[4][4];
@@ -252,12 +260,15 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs args) {
           const float negz = -(magic_offset<A>() + zp[nb]);
 #pragma unroll
           for (int mb = 0; mb < MB; ++mb) {
-            f32x4_t gacc = ini[mb];
-            if constexpr (ASYM) gacc *= negz;
 #pragma unroll
-            for (int s = 0; s < 4; ++s) gacc = mfma16x16x32<A>(st.av[mb][s], b[s], gacc);
+            for (int j = 0; j < SG; ++j) {
+              f32x4_t gacc = ini[mb][j];
+              if constexpr (ASYM) gacc *= negz;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) acc[mb][nb][i] = fmaf(sc[nb], gacc[i], acc[mb][nb][i]);
+              for (int s = j * SPS; s < (j + 1) * SPS; ++s) gacc = mfma16x16x32<A>(st.av[mb][s], b[s], gacc);
+#pragma unroll
+              for (int i = 0; i < 4; ++i) acc[mb][nb][i] = fmaf(sc[nb][j], gacc[i], acc[mb][nb][i]);
+            }
           }
         }
       } else if constexpr (A == Act::F16) {
@@ -275,11 +286,14 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs args) {
           }
 #pragma unroll
           for (int mb = 0; mb < MB; ++mb) {
-            f32x4_t gacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int s = 0; s < 4; ++s) gacc = mfma16x16x32<A>(st.av[mb][s], b[s], gacc);
+            for (int j = 0; j < SG; ++j) {
+              f32x4_t gacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int i = 0; i < 4; ++i) acc[mb][nb][i] = fmaf(sc[nb], gacc[i], acc[mb][nb][i]);
+              for (int s = j * SPS; s < (j + 1) * SPS; ++s) gacc = mfma16x16x32<A>(st.av[mb][s], b[s], gacc);
+#pragma unroll
+              for (int i = 0; i < 4; ++i) acc[mb][nb][i] = fmaf(sc[nb][j], gacc[i], acc[mb][nb][i]);
+            }
           }
         }
       } else {
@@ -315,6 +329,28 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs args) {
           const int32_t zoff = int32_t(zp[nb]) - 8;
 #pragma unroll
           for (int mb = 0; mb < MB; ++mb) {
+            if constexpr (SG > 1) {
+              // one accumulator per scale group: a 64-element MFMA per group of 64, the two
+              // 32-element halves of each operand per group of 32 (exact, 16 (d - 8) codes)
+#pragma unroll
+              for (int h = 0; h < 2; ++h) {
+                if constexpr (SG == 2) {
+                  const i32x4_t ga = mfma_i8_16x16x64(st.av[mb][h], b[h], i32x4_t{0, 0, 0, 0});
+#pragma unroll
+                  for (int i = 0; i < 4; ++i) acc[mb][nb][i] = fmaf(sc[nb][h], float(ga[i] >> 4), acc[mb][nb][i]);
+                } else {
+#pragma unroll
+                  for (int q = 0; q < 2; ++q) {
+                    const i32x4_t ga = mfma_i8_16x16x32(st.av[mb][h][2 * q], st.av[mb][h][2 * q + 1], b[h][2 * q],
+                                                        b[h][2 * q + 1], i32x4_t{0, 0, 0, 0});
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                      acc[mb][nb][i] = fmaf(sc[nb][2 * h + q], float(ga[i] >> 4), acc[mb][nb][i]);
+                  }
+                }
+              }
+              continue;
+            }
             i32x4_t gacc = {0, 0, 0, 0};
             gacc = mfma_i8_16x16x64(st.av[mb][0], b[0], gacc);
             gacc = mfma_i8_16x16x64(st.av[mb][1], b[1], gacc);
@@ -328,7 +364,7 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs args) {
                 if (r < rows)
                   args.acc_out[((row_start + r) * N + (cb0 + lcb + nb) * 16 + col) * G + g] = a32;
               } else {
-                acc[mb][nb][i] = fmaf(sc[nb], float(a32), acc[mb][nb][i]);
+                acc[mb][nb][i] = fmaf(sc[nb][0], float(a32), acc[mb][nb][i]);
               }
             }
           }
@@ -412,16 +448,16 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs args) {
 }
 
 // LDS bytes of one configuration (scales, zero points, reduction buffer).
-static size_t gemm_lds_bytes(int64_t K, int asym, int mb, int kw, int nbw) {
+static size_t gemm_lds_bytes(int64_t K, int asym, int mb, int kw, int nbw, int sg) {
   const int64_t G = K / kGroup;
   const int64_t cbwg = (4 / kw) * nbw;
-  size_t b = size_t(align256(cbwg * G * 32));
+  size_t b = size_t(align256(cbwg * G * 32 * sg));
   if (asym) b += size_t(align256(cbwg * G * 16));
   if (kw > 1) b += size_t(4) * mb * nbw * 64 * 4 * sizeof(float);
   return b;
 }
 
-template <Act A, int KIND, int MB, int KW, int NBW, int D, bool W8 = false>
+template <Act A, int KIND, int MB, int KW, int NBW, int D, bool W8 = false, int SG = 1>
 static hipError_t launch_cfg(const GemmArgs& g, hipStream_t st) {
   constexpr int cbwg = (4 / KW) * NBW;
   const int64_t nblk = g.N / (16 * cbwg);
@@ -433,14 +469,18 @@ static hipError_t launch_cfg(const GemmArgs& g, hipStream_t st) {
 #define Q4_GRID_CAP (256 * 16)
 #endif
   const unsigned grid = unsigned(std::min<int64_t>(items, Q4_GRID_CAP));
-  const size_t lds = gemm_lds_bytes(g.K, g.asym, MB, KW, NBW);
+  const size_t lds = gemm_lds_bytes(g.K, g.asym, MB, KW, NBW, SG);
   if (lds > 160 * 1024) return hipErrorInvalidValue;  // K too large for the staged scales
-  if constexpr (W8)
-    hipLaunchKernelGGL((k_gemm<A, KIND, false, MB, KW, NBW, D, true>), dim3(grid), dim3(256), lds, st, g);
-  else if (g.asym)
-    hipLaunchKernelGGL((k_gemm<A, KIND, true, MB, KW, NBW, D, false>), dim3(grid), dim3(256), lds, st, g);
-  else
-    hipLaunchKernelGGL((k_gemm<A, KIND, false, MB, KW, NBW, D, false>), dim3(grid), dim3(256), lds, st, g);
+  if constexpr (SG > 1) {
+    if (g.asym) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((k_gemm<A, KIND, false, MB, KW, NBW, D, false, SG>), dim3(grid), dim3(256), lds, st, g);
+  } else if constexpr (W8) {
+    hipLaunchKernelGGL((k_gemm<A, KIND, false, MB, KW, NBW, D, true, 1>), dim3(grid), dim3(256), lds, st, g);
+  } else if (g.asym) {
+    hipLaunchKernelGGL((k_gemm<A, KIND, true, MB, KW, NBW, D, false, 1>), dim3(grid), dim3(256), lds, st, g);
+  } else {
+    hipLaunchKernelGGL((k_gemm<A, KIND, false, MB, KW, NBW, D, false, 1>), dim3(grid), dim3(256), lds, st, g);
+  }
   return hipGetLastError();
 }
 
@@ -466,19 +506,30 @@ static hipError_t launch_cfg(const GemmArgs& g, hipStream_t st) {
 #endif
 
 // Configuration table: (MB, KW, NBW, D) by row blocks and the column count.
-template <Act A, int KIND, bool W8 = false>
-static hipError_t launch_kind(const GemmArgs& g, int rb, int split, hipStream_t st) {
+template <Act A, int KIND, bool W8, int SG>
+static hipError_t launch_kind_sg(const GemmArgs& g, int rb, int split, hipStream_t st) {
   if (rb <= 1) {
     constexpr int dec_cb = (4 / Q4_DEC_KW) * Q4_DEC_NBW;
     constexpr int dn_cb = (4 / Q4_DN_KW) * Q4_DN_NBW;
-    if (split && g.N % (16 * 2) == 0) return launch_cfg<A, KIND, 1, 4, 2, 2, W8>(g, st);
+    if (split && g.N % (16 * 2) == 0) return launch_cfg<A, KIND, 1, 4, 2, 2, W8, SG>(g, st);
     if (KIND == GEMM_PLAIN && g.N % (16 * dn_cb) == 0)
-      return launch_cfg<A, KIND, 1, Q4_DN_KW, Q4_DN_NBW, Q4_DN_D, W8>(g, st);
-    if (g.N % (16 * dec_cb) == 0) return launch_cfg<A, KIND, 1, Q4_DEC_KW, Q4_DEC_NBW, Q4_DEC_D, W8>(g, st);
-    return launch_cfg<A, KIND, 1, 4, 2, 2, W8>(g, st);
+      return launch_cfg<A, KIND, 1, Q4_DN_KW, Q4_DN_NBW, Q4_DN_D, W8, SG>(g, st);
+    if (g.N % (16 * dec_cb) == 0) return launch_cfg<A, KIND, 1, Q4_DEC_KW, Q4_DEC_NBW, Q4_DEC_D, W8, SG>(g, st);
+    return launch_cfg<A, KIND, 1, 4, 2, 2, W8, SG>(g, st);
   }
-  if (rb <= 2) return launch_cfg<A, KIND, 2, 4, 4, 2, W8>(g, st);
-  return launch_cfg<A, KIND, 4, 4, 4, 2, W8>(g, st);
+  if (rb <= 2) return launch_cfg<A, KIND, 2, 4, 4, 2, W8, SG>(g, st);
+  return launch_cfg<A, KIND, 4, 4, 4, 2, W8, SG>(g, st);
+}
+
+// scale entries per tile: 1 (groups of 128 / 256), 2 (64), 4 (32; 4-bit weights only)
+template <Act A, int KIND, bool W8 = false>
+static hipError_t launch_kind(const GemmArgs& g, int rb, int split, hipStream_t st) {
+  if constexpr (!W8 && A != Act::F16) {
+    if (g.sg == 2) return launch_kind_sg<A, KIND, false, 2>(g, rb, split, st);
+    if (g.sg == 4) return launch_kind_sg<A, KIND, false, 4>(g, rb, split, st);
+  }
+  if (g.sg > 1) return hipErrorInvalidValue;
+  return launch_kind_sg<A, KIND, W8, 1>(g, rb, split, st);
 }
 
 hipError_t launch_gemm(const GemmArgs& g, int act, int kind, int row_blocks, hipStream_t st) {

@@ -28,16 +28,18 @@ namespace q4 {
 constexpr int kPfRows = 128;   // rows per tile
 constexpr int kPfCB = 8;       // 16-column blocks per workgroup
 
-// Row sums per group of 128 (bf16 -> fp32, int8 -> int32), in element order.
+// Row sums per scale group (bf16 -> fp32 over C chunks of 8: groups of 128, 64 or 32;
+// int8 -> int32 over groups of 128), in element order.
+template <int C>
 __global__ void __launch_bounds__(256) k_rowsum_bf16(const uint16_t* __restrict__ x, int64_t rows, int64_t K,
                                                      float* __restrict__ out) {
-  const int64_t G = K / kGroup;
+  const int64_t G = K / (8 * C);
   const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
   if (i >= rows * G) return;
-  const uint16_t* p = x + i / G * K + (i % G) * kGroup;
+  const uint16_t* p = x + i / G * K + (i % G) * (8 * C);
   float s = 0.f;
 #pragma unroll
-  for (int c = 0; c < 16; ++c) {
+  for (int c = 0; c < C; ++c) {
     const uint4 v = load16(p + 8 * c);
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
@@ -67,16 +69,22 @@ __global__ void __launch_bounds__(256) k_rowsum_i8(const int8_t* __restrict__ q,
   out[i] = s;
 }
 
-hipError_t launch_rowsum(const void* a, int is_i8, int64_t rows, int64_t K, void* out, hipStream_t st) {
-  const int64_t n = rows * (K / kGroup);
+hipError_t launch_rowsum(const void* a, int is_i8, int64_t rows, int64_t K, void* out, hipStream_t st, int sg) {
+  if (is_i8 && sg > 1) return hipErrorInvalidValue;
+  const int64_t n = rows * (K / kGroup) * sg;
   if (n == 0) return hipSuccess;
   const unsigned blocks = unsigned((n + 255) / 256);
+  const uint16_t* x = static_cast<const uint16_t*>(a);
+  float* o = static_cast<float*>(out);
   if (is_i8)
     hipLaunchKernelGGL(k_rowsum_i8, dim3(blocks), dim3(256), 0, st, static_cast<const int8_t*>(a), rows, K,
                        static_cast<int32_t*>(out));
+  else if (sg == 4)
+    hipLaunchKernelGGL(k_rowsum_bf16<4>, dim3(blocks), dim3(256), 0, st, x, rows, K, o);
+  else if (sg == 2)
+    hipLaunchKernelGGL(k_rowsum_bf16<8>, dim3(blocks), dim3(256), 0, st, x, rows, K, o);
   else
-    hipLaunchKernelGGL(k_rowsum_bf16, dim3(blocks), dim3(256), 0, st, static_cast<const uint16_t*>(a), rows, K,
-                       static_cast<float*>(out));
+    hipLaunchKernelGGL(k_rowsum_bf16<16>, dim3(blocks), dim3(256), 0, st, x, rows, K, o);
   return hipGetLastError();
 }
 
@@ -136,8 +144,9 @@ Q4_DEVICE void copy_to_lds(const u32x4_t& rsrc, uint32_t lds_in, uint32_t voff, 
 // Per-stage LDS image of one group (K = 128) of one work item:
 //   A tile  [128 rows][ROWB]  (16-byte chunks XOR-swizzled by row)
 //   W tiles [8 column blocks][TB]  (the device tiles as stored: 1 KB 4-bit, 2 KB 8-bit)
-//   scales  [8][16] fp16, zero points [8][16] u8 (asymmetric)
-//   rsum    [128] fp32 row sums (bf16) / int32 code sums (int8, asymmetric)
+//   scales  [8][SG][16] fp16, zero points [8][16] u8 (asymmetric, SG == 1)
+//   rsum    [SG][128] fp32 row sums (bf16) / int32 code sums (int8, asymmetric)
+// (SG scale entries per tile: groups of 128 / SG elements)
 // int8 activations: two workgroups per CU (a two-slot ring: 51 KB of LDS with 4-bit
 // weights, 67 KB with 8-bit ones, and at most 256 registers per lane) so the waves of one
 // hide the barrier and LDS latencies of the other
@@ -148,7 +157,7 @@ Q4_DEVICE void copy_to_lds(const u32x4_t& rsrc, uint32_t lds_in, uint32_t voff, 
 #define Q4_PF_SLOTS_I8 2
 #endif
 
-template <Act A, bool W8 = false>
+template <Act A, bool W8 = false, int SG = 1>
 struct PfStage {
   static constexpr int ESZ = (A == Act::I8) ? 1 : 2;
   static constexpr int ROWB = kGroup * ESZ;
@@ -156,9 +165,9 @@ struct PfStage {
   static constexpr int TB = W8 ? 2 * kTileBytes : kTileBytes;
   static constexpr int W_OFF = A_BYTES;
   static constexpr int S_OFF = W_OFF + kPfCB * TB;
-  static constexpr int Z_OFF = S_OFF + kPfCB * 32;
-  static constexpr int R_OFF = S_OFF + 512;
-  static constexpr int BYTES = R_OFF + kPfRows * 4;
+  static constexpr int Z_OFF = S_OFF + kPfCB * 32 * SG;
+  static constexpr int R_OFF = S_OFF + (SG == 1 ? 512 : kPfCB * 32 * SG);
+  static constexpr int BYTES = R_OFF + kPfRows * 4 * SG;
   // LDS ring depth (3 x 41 KB bf16; int8: Q4_PF_SLOTS_I8 x 25.6 KB, x 33.4 KB with 8-bit
   // weights)
   static constexpr int SLOTS = (A != Act::I8) ? 3 : (W8 && Q4_PF_SLOTS_I8 > 4) ? 4 : Q4_PF_SLOTS_I8;
@@ -189,10 +198,11 @@ Q4_DEVICE ItemRange item_range(int64_t items) {
   return {xcd * chunk + blockIdx.x / 8, last, nwg / 8};
 }
 
-template <Act A, int KIND, bool ASYM, bool W8>
+template <Act A, int KIND, bool ASYM, bool W8, int SG>
 __global__ void __launch_bounds__(256, (A == Act::I8) ? 2 : 1) k_gemm_pf(GemmArgs args) {
   static_assert(!W8 || (A == Act::I8 && !ASYM), "8-bit weights: symmetric, int8 activations");
-  using St = PfStage<A, W8>;
+  static_assert(SG == 1 || (!ASYM && !W8 && (SG == 2 || SG == 4)), "scale groups: symmetric 4-bit only");
+  using St = PfStage<A, W8, SG>;
   constexpr int TB = St::TB;
   constexpr int WCOPIES = W8 ? 4 : 2;                 // 1 KB weight copies per wave per stage
   constexpr int ROWB = St::ROWB;
@@ -222,10 +232,10 @@ __global__ void __launch_bounds__(256, (A == Act::I8) ? 2 : 1) k_gemm_pf(GemmArg
   const int64_t nblk = N / (16 * kPfCB);
   const int64_t items = *args.num_tiles * nblk;
   const int64_t w_scale_off = align256(W8 ? N * K : N * K / 2);
-  const int64_t w_zero_off = w_scale_off + align256(2 * N * int64_t(G));
+  const int64_t w_zero_off = w_scale_off + align256(2 * N * int64_t(G) * SG);
   const auto a_rsrc = buffer_rsrc(args.a, args.a_rows * K * St::ESZ);
   const void* rs_base = (A == Act::I8) ? static_cast<const void*>(args.a_qsum) : static_cast<const void*>(args.a_gsum);
-  const auto r_rsrc = buffer_rsrc(rs_base, RSUM ? args.a_rows * G * 4 : 0);
+  const auto r_rsrc = buffer_rsrc(rs_base, RSUM ? args.a_rows * G * SG * 4 : 0);
 
   const ItemRange ir = item_range(items);
   for (int64_t item = ir.first; item < ir.last; item += ir.step) {
@@ -233,6 +243,7 @@ __global__ void __launch_bounds__(256, (A == Act::I8) ? 2 : 1) k_gemm_pf(GemmArg
     const int64_t cb0 = (item % nblk) * kPfCB;
     const TileDesc d = args.tiles[tile];
     if (args.ebits && args.ebits[d.expert] != (W8 ? 8 : 4)) continue;   // other format (uniform skip)
+    if (args.egroups && sg_of_code(args.egroups[d.expert]) != SG) continue;
     if constexpr (A == Act::I8) __syncthreads();   // previous item's epilogue is done with s_sa
     const int64_t row_start = d.row_start;
     const int rows = d.rows;
@@ -243,7 +254,7 @@ __global__ void __launch_bounds__(256, (A == Act::I8) ? 2 : 1) k_gemm_pf(GemmArg
                    uint32_t(__builtin_amdgcn_readfirstlane(uint32_t(woff))));   // wave-uniform
     const uint8_t* wbase = (shared ? args.w_shared : args.w) + woff;
     // bytes of one expert matrix in this kernel's format
-    const int64_t w_bytes = w_scale_off + align256(2 * N * int64_t(G)) + (ASYM ? align256(N * int64_t(G)) : 0);
+    const int64_t w_bytes = w_scale_off + align256(2 * N * int64_t(G) * SG) + (ASYM ? align256(N * int64_t(G)) : 0);
     const auto w_rsrc = buffer_rsrc(wbase, w_bytes);
     auto src_of = [&](int r) -> int64_t {   // activation row of tile row r (clamped)
       const int64_t pos = row_start + (r < rows ? r : 0);
@@ -262,19 +273,19 @@ __global__ void __launch_bounds__(256, (A == Act::I8) ? 2 : 1) k_gemm_pf(GemmArg
 #pragma unroll
     for (int j = 0; j < WCOPIES; ++j)
       w_off[j] = uint32_t((cb0 + 2 * wid + j / (WCOPIES / 2)) * G * TB + (j % (WCOPIES / 2)) * kTileBytes + lane * 16);
-    // wave 0: scales of the 8 blocks (lanes 0..15, 32 B per block and group) and zero
-    // points (lanes 16..23, 16 B per block and group)
+    // wave 0: scales of the 8 blocks (lanes 0 .. 16 SG - 1, 32 SG bytes per block and
+    // group) and zero points (lanes 16..23, 16 B per block and group; SG == 1)
     uint32_t m_off = 0, m_step = 0;
-    if (lane < 16) {
-      m_off = uint32_t(w_scale_off + (cb0 + lane / 2) * G * 32 + (lane & 1) * 16);
-      m_step = 32;
-    } else if (lane < 24) {
+    if (lane < 16 * SG) {
+      m_off = uint32_t(w_scale_off + (cb0 + lane / (2 * SG)) * G * 32 * SG + (lane % (2 * SG)) * 16);
+      m_step = 32 * SG;
+    } else if (SG == 1 && lane < 24) {
       m_off = uint32_t(w_zero_off + (cb0 + lane - 16) * G * 16);
       m_step = 16;
     }
     // waves 1 and 2: the row sums of tile rows (wid - 1) * 64 + lane
     uint32_t r_off = 0;
-    if (RSUM && (wid == 1 || wid == 2)) r_off = uint32_t(src_of((wid - 1) * 64 + lane) * G * 4);
+    if (RSUM && (wid == 1 || wid == 2)) r_off = uint32_t(src_of((wid - 1) * 64 + lane) * G * SG * 4);
 
     auto slot_of = [&](auto sl) -> uint8_t* { return ring + decltype(sl)::value * St::BYTES; };
     auto issue = [&](int g, auto sl) {
@@ -286,11 +297,14 @@ __global__ void __launch_bounds__(256, (A == Act::I8) ? 2 : 1) k_gemm_pf(GemmArg
       for (int j = 0; j < WCOPIES; ++j)
         copy_to_lds<16>(w_rsrc, base + St::W_OFF + (2 * wid + j / (WCOPIES / 2)) * TB + (j % (WCOPIES / 2)) * kTileBytes,
                         w_off[j], uint32_t(g * TB));
-      if (wid == 0 && (lane < 16 || (ASYM && lane < 24)))
+      if (wid == 0 && (lane < 16 * SG || (ASYM && lane < 24)))
         copy_to_lds<16>(w_rsrc, base + St::S_OFF, m_off + uint32_t(g) * m_step, 0u);
       if constexpr (RSUM) {
-        if (wid == 1 || wid == 2)
-          copy_to_lds<4>(r_rsrc, base + St::R_OFF + (wid - 1) * 256, r_off, uint32_t(g * 4));
+        if (wid == 1 || wid == 2) {
+#pragma unroll
+          for (int j = 0; j < SG; ++j)
+            copy_to_lds<4>(r_rsrc, base + St::R_OFF + j * 512 + (wid - 1) * 256, r_off + 4 * j, uint32_t(g * 4 * SG));
+        }
       }
     };
 
@@ -326,7 +340,102 @@ __global__ void __launch_bounds__(256, (A == Act::I8) ? 2 : 1) k_gemm_pf(GemmArg
         for (int hh = 0; hh < (W8 ? 2 : 1); ++hh)
           wraw[nb][hh] =
               *reinterpret_cast<const uint4*>(base + St::W_OFF + (wn * 4 + nb) * TB + hh * kTileBytes + lane * 16);
-      if constexpr (A == Act::BF16) {
+      if constexpr (SG > 1) {
+        // Groups of 64 or 32 (SG scale entries per tile): one accumulator per scale group,
+        // rescaled after its own MFMAs (a plain loop; groups of 128 take the pipelined
+        // path below).
+        const float* s_rs = reinterpret_cast<const float*>(base + St::R_OFF);
+        if constexpr (A == Act::BF16) {
+          constexpr int SPS = 4 / SG;
+          u32x4_t b[4][4];
+          float sc[4][SG];
+#pragma unroll
+          for (int nb = 0; nb < 4; ++nb) {
+            const uint32_t w4[4] = {wraw[nb][0].x, wraw[nb][0].y, wraw[nb][0].z, wraw[nb][0].w};
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+              uint32_t o[4];
+              widen_word_fp<A>(w4[s], o);
+              b[nb][s] = u32x4_t{o[0], o[1], o[2], o[3]};
+            }
+#pragma unroll
+            for (int j = 0; j < SG; ++j) sc[nb][j] = f16_bits_to_f32(s_sc[((wn * 4 + nb) * SG + j) * 16 + col]);
+          }
+          const float negz = -(magic_offset<A>() + 8.0f);
+#pragma unroll
+          for (int mb = 0; mb < NMB; ++mb) {
+            const int rb = 2 * mb + wm;
+            const int r = rb * 16 + col;
+            u32x4_t af[4];
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+              const int c = (4 * s + kq) ^ swz(r);
+              af[s] = *reinterpret_cast<const u32x4_t*>(base + r * ROWB + c * 16);
+            }
+            f32x4_t xv[SG];
+#pragma unroll
+            for (int j = 0; j < SG; ++j) xv[j] = *reinterpret_cast<const f32x4_t*>(s_rs + j * 128 + rb * 16 + 4 * kq);
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+              for (int j = 0; j < SG; ++j) {
+                f32x4_t g = xv[j] * negz;
+#pragma unroll
+                for (int s = j * SPS; s < (j + 1) * SPS; ++s) g = mfma16x16x32<A>(af[s], b[nb][s], g);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[mb][nb][i] = fmaf(sc[nb][j], g[i], acc[mb][nb][i]);
+              }
+          }
+        } else {
+          u32x4_t b[4][2];
+          float sc16[4][SG];
+#pragma unroll
+          for (int nb = 0; nb < 4; ++nb) {
+            uint32_t o[8];
+            widen_word_i8(wraw[nb][0].x, o[0], o[1]);
+            widen_word_i8(wraw[nb][0].y, o[2], o[3]);
+            widen_word_i8(wraw[nb][0].z, o[4], o[5]);
+            widen_word_i8(wraw[nb][0].w, o[6], o[7]);
+            b[nb][0] = u32x4_t{o[0], o[1], o[2], o[3]};
+            b[nb][1] = u32x4_t{o[4], o[5], o[6], o[7]};
+#pragma unroll
+            for (int j = 0; j < SG; ++j)
+              sc16[nb][j] = f16_bits_to_f32(s_sc[((wn * 4 + nb) * SG + j) * 16 + col]) * 0.0625f;
+          }
+#pragma unroll
+          for (int mb = 0; mb < NMB; ++mb) {
+            const int rb = 2 * mb + wm;
+            const int r = rb * 16 + col;
+            u32x4_t af[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+              const int c1 = (4 * i + (kq >> 1)) ^ swz(r), c2 = (4 * i + 2 + (kq >> 1)) ^ swz(r);
+              const uint2 lo = *reinterpret_cast<const uint2*>(base + r * ROWB + c1 * 16 + 8 * (kq & 1));
+              const uint2 hi = *reinterpret_cast<const uint2*>(base + r * ROWB + c2 * 16 + 8 * (kq & 1));
+              af[i] = u32x4_t{lo.x, lo.y, hi.x, hi.y};
+            }
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+              for (int h = 0; h < 2; ++h) {
+                if constexpr (SG == 2) {
+                  const i32x4_t ga = mfma_i8_16x16x64(af[h], b[nb][h], i32x4_t{0, 0, 0, 0});
+#pragma unroll
+                  for (int i = 0; i < 4; ++i) acc[mb][nb][i] = fmaf(sc16[nb][h], float(ga[i]), acc[mb][nb][i]);
+                } else {
+#pragma unroll
+                  for (int q = 0; q < 2; ++q) {
+                    const i32x4_t ga = mfma_i8_16x16x32(af[h][2 * q], af[h][2 * q + 1], b[nb][h][2 * q],
+                                                        b[nb][h][2 * q + 1], i32x4_t{0, 0, 0, 0});
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                      acc[mb][nb][i] = fmaf(sc16[nb][2 * h + q], float(ga[i]), acc[mb][nb][i]);
+                  }
+                }
+              }
+          }
+        }
+      } else if constexpr (A == Act::BF16) {
         float sc[4], negz[4];
         u32x4_t b[4][4];
 #pragma unroll
@@ -573,16 +682,21 @@ static hipError_t launch_pf_kind(const GemmArgs& g, hipStream_t st) {
   if (items == 0) return hipSuccess;
   const int64_t cap = (A == Act::I8) ? Q4_PF_GRID_I8 : 256;
   const unsigned grid = unsigned(std::min<int64_t>(items, cap));
+  if (g.sg > 1 && (g.asym || g.wbits == 8)) return hipErrorInvalidValue;
   if constexpr (A == Act::I8) {
     if (g.wbits == 8) {
-      hipLaunchKernelGGL((k_gemm_pf<A, KIND, false, true>), dim3(grid), dim3(256), 0, st, g);
+      hipLaunchKernelGGL((k_gemm_pf<A, KIND, false, true, 1>), dim3(grid), dim3(256), 0, st, g);
       return hipGetLastError();
     }
   }
-  if (g.asym)
-    hipLaunchKernelGGL((k_gemm_pf<A, KIND, true, false>), dim3(grid), dim3(256), 0, st, g);
+  if (g.sg == 4)
+    hipLaunchKernelGGL((k_gemm_pf<A, KIND, false, false, 4>), dim3(grid), dim3(256), 0, st, g);
+  else if (g.sg == 2)
+    hipLaunchKernelGGL((k_gemm_pf<A, KIND, false, false, 2>), dim3(grid), dim3(256), 0, st, g);
+  else if (g.asym)
+    hipLaunchKernelGGL((k_gemm_pf<A, KIND, true, false, 1>), dim3(grid), dim3(256), 0, st, g);
   else
-    hipLaunchKernelGGL((k_gemm_pf<A, KIND, false, false>), dim3(grid), dim3(256), 0, st, g);
+    hipLaunchKernelGGL((k_gemm_pf<A, KIND, false, false, 1>), dim3(grid), dim3(256), 0, st, g);
   return hipGetLastError();
 }
 

@@ -19,7 +19,11 @@ struct TileDesc {
 hipError_t launch_quantize(const void* w, int dtype, int64_t n, int64_t k, int asym, uint8_t* packed,
                            uint16_t* scales, uint8_t* zeros, int32_t* flags, hipStream_t st);
 hipError_t launch_repack(const uint8_t* packed, const uint16_t* scales, const uint8_t* zeros, int64_t n,
-                         int64_t k, int asym, int gate_up, void* out, hipStream_t st);
+                         int64_t k, int asym, int gate_up, void* out, hipStream_t st, int group = 128);
+// Groups of 32, 64 or 256 along K (128 goes to launch_quantize).
+hipError_t launch_quantize_grouped(const void* w, int dtype, int64_t n, int64_t k, int group, int asym,
+                                   uint8_t* packed, uint16_t* scales, uint8_t* zeros, int32_t* flags,
+                                   hipStream_t st);
 
 // INT8 g128 weights (W8A8): quantisation and device tiles (2 KB per (16-column block, group)).
 hipError_t launch_quantize8(const void* w, int dtype, int64_t n, int64_t k, int8_t* q, uint16_t* scales,
@@ -62,6 +66,8 @@ struct GemmArgs {
   int32_t wbits;          // 4 (INT4 tiles) or 8 (INT8 tiles, int8 activations only)
   const uint8_t* ebits;   // mixed layers: bits per expert (tiles of other experts are skipped), or NULL
   const int64_t* woffs;   // mixed layers: byte offset of each routed expert's block in w, or NULL
+  const uint8_t* egroups; // per-expert group size / 32 (tiles of experts of another sg are skipped), or NULL
+  int32_t sg;             // scale entries per 128-element tile of this launch (1, 2, 4)
   int64_t N;              // device columns (2I for gate/up)
   int64_t K;
   // tiles
@@ -83,8 +89,12 @@ hipError_t launch_gemm(const GemmArgs& g, int act /*0 bf16, 1 f16, 2 i8*/, int k
 // prefill_fits: the buffers stay within the kernel's 32-bit buffer offsets.
 bool prefill_fits(int64_t a_rows, int64_t K, int act, int64_t w_stride);
 hipError_t launch_gemm_prefill(const GemmArgs& g, int act /*0 bf16, 2 i8*/, int kind, hipStream_t st);
-// Per-(row, group of 128) sums: bf16 -> fp32, or int8 -> int32.
-hipError_t launch_rowsum(const void* a, int is_i8, int64_t rows, int64_t K, void* out, hipStream_t st);
+// Per-(row, group of 128 / sg) sums: bf16 -> fp32 (sg 1, 2, 4), or int8 -> int32 (sg 1).
+hipError_t launch_rowsum(const void* a, int is_i8, int64_t rows, int64_t K, void* out, hipStream_t st, int sg = 1);
+
+// Scale entries per 1 KB tile of an expert with the given group-size code (group / 32):
+// 4 for groups of 32, 2 for 64, 1 for 128 and 256 (the 256-group's scale on both tiles).
+__host__ __device__ inline int sg_of_code(int code) { return code == 1 ? 4 : code == 2 ? 2 : 1; }
 
 // LoRA-mode experts (lora.hip).
 hipError_t launch_dense_tiles(int64_t t, int tile_rows, TileDesc* tiles, int32_t* num_tiles, hipStream_t st);

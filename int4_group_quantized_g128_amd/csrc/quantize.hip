@@ -104,6 +104,103 @@ __global__ void __launch_bounds__(64) k_quantize_g128(const void* __restrict__ w
   }
 }
 
+// Other group sizes (32, 64, 256; page "MoE推理优化实战：4bit存储+INT8计算的W4A8路线解析"
+// §5.3 sizes groups by expert hotness): one wave per (row, two 256-element chunks);
+// lane j covers k = 256 c + 4 j .. 4 j + 3 and writes 2 packed bytes; a group spans
+// group / 4 aligned lanes, reduced with xor shuffles.  Same arithmetic as the 128
+// kernel.  Zero points (asymmetric, groups of 256 only): the two chunks of a wave are
+// the two groups of one zero-point byte.
+template <int DT, bool ASYM>
+__global__ void __launch_bounds__(64) k_quantize_grp(const void* __restrict__ w, int64_t n, int64_t k, int group,
+                                                    uint8_t* __restrict__ packed, uint16_t* __restrict__ scales,
+                                                    uint8_t* __restrict__ zeros, int32_t* __restrict__ flags) {
+  const int64_t chunks = (k + 255) / 256;
+  const int64_t pairs = (chunks + 1) / 2;
+  const int64_t row = int64_t(blockIdx.x) / pairs;
+  const int64_t pair = int64_t(blockIdx.x) % pairs;
+  const int64_t Gc = k / group;
+  const int lane = threadIdx.x;
+  const int lpg = group / 4;            // lanes per group: 8, 16 or 64
+  uint32_t zbyte = 0;
+  int flag = 0;
+  for (int h = 0; h < 2; ++h) {
+    const int64_t c = pair * 2 + h;
+    if (c >= chunks) break;
+    const int64_t k0 = c * 256 + 4 * lane;
+    const bool valid = k0 < k;          // whole groups are valid or not (k % group == 0)
+    float v[4] = {0.f, 0.f, 0.f, 0.f};
+    if (valid) {
+      const int64_t base = row * k + k0;
+      if constexpr (DT == 0) {
+        const float4 p = *reinterpret_cast<const float4*>(static_cast<const float*>(w) + base);
+        v[0] = p.x; v[1] = p.y; v[2] = p.z; v[3] = p.w;
+      } else {
+        const uint2 p = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(w) + base);
+        const uint16_t b[4] = {uint16_t(p.x & 0xffff), uint16_t(p.x >> 16), uint16_t(p.y & 0xffff),
+                               uint16_t(p.y >> 16)};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = DT == 1 ? f16_bits_to_f32(b[e]) : bf16_to_f32(b[e]);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (!__builtin_isfinite(v[e])) flag |= 1;
+    }
+    uint32_t codes = 0;
+    if constexpr (!ASYM) {
+      float amax = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
+      for (int o = 1; o < lpg; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+      const float t = __fdiv_rn(amax, 7.0f);
+      const __half sh = __float2half_rn(t);
+      const uint16_t sb = __half_as_ushort(sh);
+      if (valid && (sb & 0x7fff) >= 0x7c00) flag |= 2;
+      const float s = __half2float(sh);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float q = 0.f;
+        if (s > 0.f) q = fminf(fmaxf(rintf(__fdiv_rn(v[e], s)), -8.f), 7.f);
+        codes |= (uint32_t(int(q)) & 0xF) << (4 * e);
+      }
+      if (valid && lane % lpg == 0) scales[row * Gc + k0 / group] = sb;
+    } else {
+      float mn = fminf(fminf(v[0], v[1]), fminf(v[2], v[3]));
+      float mx = fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3]));
+      for (int o = 1; o < lpg; o <<= 1) {
+        mn = fminf(mn, __shfl_xor(mn, o, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+      }
+      mn = fminf(mn, 0.f);
+      mx = fmaxf(mx, 0.f);
+      const float t = __fdiv_rn(__fsub_rn(mx, mn), 15.0f);
+      const uint16_t sb = f32_to_f16_up(t);
+      if (valid && (sb & 0x7fff) >= 0x7c00) flag |= 2;
+      const float s = f16_bits_to_f32(sb);
+      float z = 0.f;
+      if (s > 0.f) z = fminf(fmaxf(rintf(__fdiv_rn(-mn, s)), 0.f), 15.f);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float q = 0.f;
+        if (s > 0.f) q = fminf(fmaxf(__fadd_rn(rintf(__fdiv_rn(v[e], s)), z), 0.f), 15.f);
+        codes |= uint32_t(int(q)) << (4 * e);
+      }
+      zbyte |= uint32_t(int(z)) << (4 * h);
+      if (valid && lane % lpg == 0) scales[row * Gc + k0 / group] = sb;
+    }
+    if (valid) *reinterpret_cast<uint16_t*>(packed + (row * k + k0) / 2) = uint16_t(codes);
+  }
+  if constexpr (ASYM) {
+    if (lane == 0) zeros[row * ((Gc + 1) / 2) + pair] = uint8_t(zbyte);
+  }
+  if (flags) {
+    const unsigned long long any = __ballot(flag != 0);
+    if (any) {
+      int all = flag;
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) all |= __shfl_xor(all, o, 64);
+      if (lane == 0) atomicOr(flags, all);
+    }
+  }
+}
+
 // A2: one thread per 32-bit word of the device weights.  Word index
 // ((cb * G + g) * 64 + lane) * 4 + s; it gathers elements k = 128 g + 32 s + 8 kq + e,
 // e in [0, 8) (4 canonical bytes) of device column 16 cb + lane % 16.
@@ -140,26 +237,33 @@ __global__ void k_repack_weights(const uint8_t* __restrict__ packed, int64_t n, 
   }
 }
 
-// Scales (and zero points) into [n/16][G][16] with the device column order.
+// Scales (and zero points) into [n/16][G][SG][16] with the device column order.  SG
+// scale entries per 128-element tile (128 / group for groups of 32 and 64, else 1);
+// entry (tile g, j) holds canonical group (128 g + j 128 / SG) / group, so a 256-group's
+// scale (and zero point) is repeated on both of its tiles.
 __global__ void k_repack_meta(const uint16_t* __restrict__ scales, const uint8_t* __restrict__ zeros,
-                              int64_t n, int64_t k, int gate_up, uint16_t* __restrict__ sout,
+                              int64_t n, int64_t k, int group, int gate_up, uint16_t* __restrict__ sout,
                               uint8_t* __restrict__ zout) {
   const int64_t G = k / kGroup;
-  const int64_t total = n * G;
+  const int SG = group < kGroup ? kGroup / group : 1;
+  const int64_t Gc = k / group;
+  const int64_t total = n * G * SG;
   for (int64_t i = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; i < total;
        i += int64_t(gridDim.x) * blockDim.x) {
     const int c = int(i & 15);
-    const int64_t g = (i >> 4) % G;
-    const int64_t cb = (i >> 4) / G;
+    const int j = int((i >> 4) % SG);
+    const int64_t g = (i >> 4) / SG % G;
+    const int64_t cb = (i >> 4) / SG / G;
     int64_t src = cb * 16 + c;
     if (gate_up) {
       const int64_t half = n / 2;
       src = (cb & 1) ? half + (cb >> 1) * 16 + c : (cb >> 1) * 16 + c;
     }
-    sout[i] = scales[src * G + g];
-    if (zout) {
-      const uint8_t zb = zeros[src * ((G + 1) / 2) + g / 2];
-      zout[i] = (g & 1) ? (zb >> 4) : (zb & 0xF);
+    const int64_t cg = (g * kGroup + j * (kGroup / SG)) / group;
+    sout[i] = scales[src * Gc + cg];
+    if (zout) {   // SG == 1
+      const uint8_t zb = zeros[src * ((Gc + 1) / 2) + cg / 2];
+      zout[i] = (cg & 1) ? (zb >> 4) : (zb & 0xF);
     }
   }
 }
@@ -264,7 +368,7 @@ hipError_t launch_repack8(const int8_t* q, const uint16_t* scales, int64_t n, in
   unsigned blocks = unsigned(std::min<int64_t>((chunks + 255) / 256, 65536));
   hipLaunchKernelGGL(k_repack8_weights, dim3(blocks), dim3(256), 0, st, q, n, k, gate_up, reinterpret_cast<uint4*>(base));
   unsigned mblocks = unsigned(std::min<int64_t>((n * G + 255) / 256, 65536));
-  hipLaunchKernelGGL(k_repack_meta, dim3(mblocks), dim3(256), 0, st, scales, nullptr, n, k, gate_up,
+  hipLaunchKernelGGL(k_repack_meta, dim3(mblocks), dim3(256), 0, st, scales, nullptr, n, k, int(kGroup), gate_up,
                      reinterpret_cast<uint16_t*>(base + sb), nullptr);
   const int64_t scale_pad = align256(2 * n * G) - 2 * n * G;
   if (scale_pad > 0) hipLaunchKernelGGL(k_zero_bytes, dim3(1), dim3(256), 0, st, base + sb + 2 * n * G, scale_pad);
@@ -290,22 +394,44 @@ hipError_t launch_quantize(const void* w, int dtype, int64_t n, int64_t k, int a
   return hipGetLastError();
 }
 
+hipError_t launch_quantize_grouped(const void* w, int dtype, int64_t n, int64_t k, int group, int asym,
+                                   uint8_t* packed, uint16_t* scales, uint8_t* zeros, int32_t* flags,
+                                   hipStream_t st) {
+  if (group == kGroup) return launch_quantize(w, dtype, n, k, asym, packed, scales, zeros, flags, st);
+  const int64_t chunks = (k + 255) / 256;
+  dim3 grid(unsigned(n * ((chunks + 1) / 2)));
+#define Q4_QLAUNCH(DT, AS) \
+  hipLaunchKernelGGL((k_quantize_grp<DT, AS>), grid, dim3(64), 0, st, w, n, k, group, packed, scales, zeros, flags)
+  if (asym) {
+    if (dtype == 0) Q4_QLAUNCH(0, true);
+    else if (dtype == 1) Q4_QLAUNCH(1, true);
+    else Q4_QLAUNCH(2, true);
+  } else {
+    if (dtype == 0) Q4_QLAUNCH(0, false);
+    else if (dtype == 1) Q4_QLAUNCH(1, false);
+    else Q4_QLAUNCH(2, false);
+  }
+#undef Q4_QLAUNCH
+  return hipGetLastError();
+}
+
 hipError_t launch_repack(const uint8_t* packed, const uint16_t* scales, const uint8_t* zeros, int64_t n,
-                         int64_t k, int asym, int gate_up, void* out, hipStream_t st) {
+                         int64_t k, int asym, int gate_up, void* out, hipStream_t st, int group) {
   uint8_t* base = static_cast<uint8_t*>(out);
   const int64_t G = k / kGroup;
+  const int64_t SG = group < kGroup ? kGroup / group : 1;
   const int64_t words = n * k / 8;
   const int64_t sb = align256(n * k / 2);
-  const int64_t zb = sb + align256(2 * n * G);
+  const int64_t zb = sb + align256(2 * n * G * SG);
   unsigned blocks = unsigned(std::min<int64_t>((words + 255) / 256, 65536));
   hipLaunchKernelGGL(k_repack_weights, dim3(blocks), dim3(256), 0, st, packed, n, k, asym, gate_up,
                      reinterpret_cast<uint32_t*>(base));
-  unsigned mblocks = unsigned(std::min<int64_t>((n * G + 255) / 256, 65536));
-  hipLaunchKernelGGL(k_repack_meta, dim3(mblocks), dim3(256), 0, st, scales, asym ? zeros : nullptr, n, k,
+  unsigned mblocks = unsigned(std::min<int64_t>((n * G * SG + 255) / 256, 65536));
+  hipLaunchKernelGGL(k_repack_meta, dim3(mblocks), dim3(256), 0, st, scales, asym ? zeros : nullptr, n, k, group,
                      gate_up, reinterpret_cast<uint16_t*>(base + sb), asym ? base + zb : nullptr);
-  const int64_t scale_pad = zb - (sb + 2 * n * G);
+  const int64_t scale_pad = zb - (sb + 2 * n * G * SG);
   if (scale_pad > 0)
-    hipLaunchKernelGGL(k_zero_bytes, dim3(1), dim3(256), 0, st, base + sb + 2 * n * G, scale_pad);
+    hipLaunchKernelGGL(k_zero_bytes, dim3(1), dim3(256), 0, st, base + sb + 2 * n * G * SG, scale_pad);
   if (asym) {
     const int64_t zero_pad = align256(n * G) - n * G;
     if (zero_pad > 0) hipLaunchKernelGGL(k_zero_bytes, dim3(1), dim3(256), 0, st, base + zb + n * G, zero_pad);

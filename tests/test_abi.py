@@ -171,3 +171,49 @@ def test_mixed_layer_validation(L):
         assert r.moe_int4_ffn_workspace_bytes(ctypes.byref(d), 4, L.Q4_W4A8) == 0
     assert r.moe_int4_ffn_forward(ctypes.byref(desc), fake, 4, fake, fake, L.Q4_W4A16, fake, fake, 1 << 20,
                                   None) == L.Q4_ERR_DTYPE
+
+
+def test_grouped_format_sizes_and_validation(L):
+    from oracle import layout
+    r = L.raw
+    for n, k, asym, g in ((64, 512, 0, 32), (64, 512, 0, 64), (32, 256, 0, 128), (96, 1024, 0, 256),
+                          (96, 1024, 1, 256), (64, 512, 1, 128)):
+        assert r.q4_device_bytes_grouped(n, k, asym, g) == layout.device_bytes(n, k, bool(asym), g)
+    assert r.q4_device_bytes_grouped(64, 512, 0, 128) == r.q4_device_bytes(64, 512, 0)
+    assert r.q4_device_bytes_grouped(64, 512, 1, 32) == 0      # zero points need groups >= 128
+    assert r.q4_device_bytes_grouped(64, 384, 0, 256) == 0     # k % group
+    assert r.q4_device_bytes_grouped(64, 512, 0, 48) == 0
+    fake = ctypes.c_void_p(4096)
+    assert r.quantize_int4_grouped(fake, L.Q4_F32, 4, 256, 48, 0, fake, fake, None, None, None) == L.Q4_ERR_SHAPE
+    assert r.quantize_int4_grouped(fake, L.Q4_F32, 4, 256, 32, 1, fake, fake, fake, None, None) == \
+        L.Q4_ERR_UNSUPPORTED
+    assert r.quantize_int4_grouped(fake, L.Q4_F32, 4, 384, 256, 0, fake, fake, None, None, None) == L.Q4_ERR_SHAPE
+    assert r.q4_repack_device_grouped(fake, fake, None, 64, 512, 0, 32, L.Q4_REPACK_PLAIN, fake, 16, None) == \
+        L.Q4_ERR_WORKSPACE
+
+
+def test_expert_groups_by_hotness_matches_the_oracle_rule(L):
+    import numpy as np
+    from oracle import ffn
+    rng = np.random.default_rng(6)
+    for E, shared in ((256, False), (8, True), (17, False), (64, True)):
+        counts = rng.integers(0, 50, E)
+        counts[rng.integers(0, E)] = 0
+        assert L.expert_groups_by_hotness(counts.tolist(), 0.05, 0.1, shared) == \
+            ffn.groups_by_hotness(counts, 0.05, 0.1, shared)
+
+
+def test_grouped_layer_validation(L):
+    r = L.raw
+
+    def desc(**kw):
+        d = L.Q4MoELayer(8, 256, 256, 2, 0, 0, 4096, 4096, None, None, 0, None, 4096, 4096, 4096)
+        for key, v in kw.items():
+            setattr(d, key, v)
+        return d
+    for mode in (L.Q4_W4A16, L.Q4_W4A8):
+        assert r.moe_int4_ffn_workspace_bytes(ctypes.byref(desc()), 300, mode) > 0
+    assert r.moe_int4_ffn_workspace_bytes(ctypes.byref(desc()), 4, L.Q4_W8A8) == 0
+    assert r.moe_int4_ffn_workspace_bytes(ctypes.byref(desc(expert_bits=4096)), 4, L.Q4_W4A16) == 0
+    for bad in (dict(asymmetric=1), dict(weight_bits=8), dict(gate_up_offsets=None)):
+        assert r.moe_int4_ffn_workspace_bytes(ctypes.byref(desc(**bad)), 4, L.Q4_W4A16) == 0
