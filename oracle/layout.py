@@ -23,8 +23,9 @@ k = 128 g + 32 s + 8 kq + e, e in [0, 8), element e at nibble position
 p(e) = [0, 2, 4, 6, 1, 3, 5, 7][e] (bits 4p .. 4p+3): byte j of the word holds
 element j in its low nibble and element j + 4 in its high nibble.
 
-Scales.  Binary16 bits, [N/16][G][SG][16] (same column order), starting at byte
-align256(N K / 2).  SG is the number of scale groups per 128-element tile: 1 for
+Scales.  Binary16 bits, [N/16][G][16][SG] (same column order; a column's SG entries
+of one tile are adjacent), starting at byte align256(N K / 2).  SG is the number of
+scale groups per 128-element tile: 1 for
 the default group of 128, 128 / group for groups of 32 or 64 (entry j of tile g is
 the scale of k in [128 g + j 128/SG, 128 g + (j + 1) 128/SG)), and 1 for groups of
 256, where each tile carries the scale of the 256-group it lies in (both tiles of a
@@ -109,11 +110,11 @@ def to_device(packed, scale_bits, zeros_packed, n, k, asymmetric, gate_up, group
     shift = 4 * NIBBLE_POS[e]
     np.add.at(words, word_index.ravel(), (d.astype(np.uint64) << shift.astype(np.uint64)).ravel())
     out[: n * k // 2] = words.astype("<u4").view(np.uint8)
-    # scales [N/16][G][SG][16]: entry (tile, j) of column j16 from its canonical group
+    # scales [N/16][G][16][SG]: entry (tile, j) of a column from its canonical group
     so = _a256(n * k // 2)
     srcg = _scale_source(k, group)                                    # [G, SG]
     se = s.view(np.uint16)[:, srcg]                                   # [N, G, SG]
-    sc = se.reshape(n // 16, 16, g, sg).transpose(0, 2, 3, 1).reshape(-1)
+    sc = se.reshape(n // 16, 16, g, sg).transpose(0, 2, 1, 3).reshape(-1)
     out[so: so + 2 * n * g * sg] = sc.astype("<u2").view(np.uint8)
     if asymmetric:
         zo = so + _a256(2 * n * g * sg)
@@ -140,7 +141,7 @@ def from_device(dev, n, k, asymmetric, gate_up, group=GROUP):
     word_index = ((cb * g + gg) * 1024 + lane * 16 + sidx * 4) // 4
     d = (words[word_index] >> (4 * NIBBLE_POS[e])) & 0xF
     so = _a256(n * k // 2)
-    sc = dev[so: so + 2 * n * g * sg].view("<u2").reshape(n // 16, g, sg, 16).transpose(0, 3, 1, 2)
+    sc = dev[so: so + 2 * n * g * sg].view("<u2").reshape(n // 16, g, 16, sg).transpose(0, 2, 1, 3)
     sc = sc.reshape(n, g * sg)
     if group > GROUP:
         sc = sc[:, :: group // GROUP]

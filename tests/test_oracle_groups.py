@@ -92,10 +92,10 @@ def test_layout_scale_entries_by_hand():
     w = _w(n, k, 12)
     so = layout._a256(n * k // 2)
     # groups of 32: entry (column block 1, tile 2, j = 3) of column 16 + 5 is at
-    # ((1 * 4 + 2) * 4 + 3) * 16 + 5 and holds the scale of k in [2*128 + 96, 2*128 + 128)
+    # ((1 * 4 + 2) * 16 + 5) * 4 + 3 and holds the scale of k in [2*128 + 96, 2*128 + 128)
     packed, sbits, _ = quant.quantize_pack(w, False, 32)
     dev = layout.to_device(packed, sbits, None, n, k, False, False, 32)
-    at = so + 2 * (((1 * 4 + 2) * 4 + 3) * 16 + 5)
+    at = so + 2 * (((1 * 4 + 2) * 16 + 5) * 4 + 3)
     assert int(dev[at]) | (int(dev[at + 1]) << 8) == int(sbits[21, (256 + 96) // 32])
     # groups of 256: tiles 2 and 3 of column 7 both hold the scale of group 1
     packed, sbits, _ = quant.quantize_pack(w, False, 256)
