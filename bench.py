@@ -61,9 +61,10 @@ def parse():
 class Workload:
     """Device-resident layer + router + tokens + preallocated buffers for one config."""
 
-    def __init__(self, lib, torch, synth, cfg_name, t, mode, expert_bits=None):
+    def __init__(self, lib, torch, synth, cfg_name, t, mode, expert_bits=None, expert_groups=None):
         """mode "w4a16" / "w4a8" / "w8a8", or "mixed": per-expert widths ``expert_bits``
-        (4 or 8 per expert and the shared expert) with INT8 activations."""
+        (4 or 8 per expert and the shared expert) with INT8 activations; ``expert_groups``:
+        per-expert group sizes of the INT4 weights (modes w4a16 / w4a8)."""
         self.lib, self.torch = lib, torch
         cfg = synth.CONFIGS[cfg_name]
         self.cfg_name, self.cfg, self.t = cfg_name, cfg, t
@@ -72,7 +73,8 @@ class Workload:
         e, h, i, k = cfg["experts"], cfg["hidden"], cfg["inter"], cfg["top_k"]
         shared = bool(cfg.get("shared", False))
         self.layer = lib.MoELayer(e, h, i, k, asymmetric=cfg["asymmetric"], shared=shared, weight_bits=self.wbits,
-                                  expert_bits=expert_bits if mode == "mixed" else None)
+                                  expert_bits=expert_bits if mode == "mixed" else None,
+                                  expert_groups=expert_groups)
         for j in range(e + (1 if shared else 0)):
             g, u, d = synth.expert_weights(cfg_name, j, device="cuda")
             self.layer.set_expert(j, g, u, d)
@@ -132,12 +134,12 @@ class Workload:
     def touched(self):
         return len(self.touched_experts())
 
-    def expert_bytes(self, bits=None):
+    def expert_bytes(self, bits=None, group=128):
         """Canonical packed bytes of one expert: codes (4- or 8-bit) + fp16 scales (+ zero points)."""
         h, i = self.cfg["hidden"], self.cfg["inter"]
         cb = (bits or self.wbits) // 4     # code bytes per 2 weights
-        gu = 2 * i * h * cb // 2 + 2 * i * (h // 128) * 2
-        dn = h * i * cb // 2 + h * (i // 128) * 2
+        gu = 2 * i * h * cb // 2 + 2 * i * (h // group) * 2
+        dn = h * i * cb // 2 + h * (i // group) * 2
         if self.cfg["asymmetric"]:
             gu += 2 * i * ((h // 128 + 1) // 2)
             dn += h * ((i // 128 + 1) // 2)
@@ -147,7 +149,7 @@ class Workload:
         """Canonical bytes (gate/up, down) of the touched experts, each at its own width."""
         gu = dn = 0
         for e in self.touched_experts():
-            a, b = self.expert_bytes(self.layer.bits[e])
+            a, b = self.expert_bytes(self.layer.bits[e], self.layer.groups[e])
             gu, dn = gu + a, dn + b
         return gu, dn
 
@@ -294,6 +296,17 @@ def hotness_bits(lib, torch, synth, cfg_name, frac8, calib_tokens=4096):
     return lib.expert_bits_by_hotness(counts, frac8, shared=bool(cfg.get("shared", False)))
 
 
+def hotness_groups(lib, torch, synth, cfg_name, calib_tokens=4096):
+    """Per-expert group sizes from routing hit counts of the same calibration batch: the
+    top 5 % of the experts 32, experts under a tenth of the even share 256, others 64."""
+    cfg = synth.CONFIGS[cfg_name]
+    x = synth.tokens(cfg_name, calib_tokens, device="cuda", salt=7)
+    wr, b = synth.router_weights(cfg_name, device="cuda")
+    _, ids, _ = lib.moe_route_topk(x, wr, b, cfg["top_k"])
+    counts = torch.bincount(ids.reshape(-1).long(), minlength=cfg["experts"]).cpu().tolist()
+    return lib.expert_groups_by_hotness(counts, 0.05, 0.1, shared=bool(cfg.get("shared", False)))
+
+
 def cpu_baseline(synth, wl, ntok):
     """The oracle (fp64 NumPy) on the first ``ntok`` tokens of the batch: router + MoE
     forward with the shared expert; expert quantisation (offline) is not timed."""
@@ -414,6 +427,17 @@ def main():
                 b == 8 for b in bits))
             del mt
         del mx
+        torch.cuda.empty_cache()
+        log("[bench] extra moe256 per-expert group sizes (hit counts: top 5 % 32, cold 256, others 64)")
+        groups = hotness_groups(lib, torch, synth, "moe256")
+        gw = Workload(lib, torch, synth, "moe256", args.tokens, "w4a16", expert_groups=groups)
+        for t, mode in ((args.tokens, "w4a16"), (args.tokens, "w4a8"), (4096, "w4a16"), (4096, "w4a8")):
+            gt = gw if (t, mode) == (args.tokens, "w4a16") else gw.retoken(synth, t, mode)
+            s7, st7 = time_steps(torch, gt, 10 if t > 1000 else 50, 3, stage_events=True, graph=not args.no_graph)
+            extra[f"moe256_T{t}_groups_{mode}"] = dict(summarize(gt, s7, st7), groups={
+                str(g): sum(v == g for v in groups) for g in (32, 64, 128, 256)})
+            del gt
+        del gw
         torch.cuda.empty_cache()
         if args.mode != "w8a8":
             log(f"[bench] extra moe256 W8A8 T={args.tokens}")

@@ -147,9 +147,10 @@ Q4_API int q4_repack_device(const uint8_t* packed, const uint16_t* scales, const
  *  Requires group in {32, 64, 128, 256}, k % 128 == 0 and k % group == 0; zero points
  *  (asymmetric) only with groups of 128 or 256 (Q4_ERR_UNSUPPORTED otherwise).
  * Device layout: the weight tiles of q4_repack_device (they do not depend on the
- * group); scales binary16 [n/16][k/128][SG][16] with SG = 128 / group scale entries
- * per 1 KB tile for groups of 32 or 64 (entry j covers k in
- * [128 g + j 128/SG, 128 g + (j + 1) 128/SG)) and SG = 1 otherwise, a 256-group's
+ * group); scales binary16 [n/16][k/128][16][SG] (a column's entries of one tile
+ * adjacent) with SG = 128 / group scale entries per 1 KB tile for groups of 32 or 64
+ * (entry j covers k in [128 g + j 128/SG, 128 g + (j + 1) 128/SG)) and SG = 1
+ * otherwise, a 256-group's
  * scale repeated on both of its tiles; zeros (asymmetric) one byte per (column,
  * tile), [n/16][k/128][16], the tile's group's zero point.
  */

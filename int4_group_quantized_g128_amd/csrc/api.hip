@@ -58,6 +58,7 @@ struct FwdWorkspace {
   int32_t* inv = nullptr;
   TileDesc* tiles = nullptr;
   int32_t* num_tiles = nullptr;
+  int32_t* fmt_tiles = nullptr;   // [5] tile range of each weight format
   void* h = nullptr;
   float* y = nullptr;
   int8_t* qx = nullptr;
@@ -131,6 +132,7 @@ FwdWorkspace carve(const q4_moe_layer_t* L, int64_t t, int mode, void* base) {
   w.inv = reinterpret_cast<int32_t*>(take(P * 4));
   w.tiles = reinterpret_cast<TileDesc*>(take(int64_t(w.max_tiles) * sizeof(TileDesc)));
   w.num_tiles = reinterpret_cast<int32_t*>(take(4));
+  w.fmt_tiles = reinterpret_cast<int32_t*>(take(5 * 4));
   w.h = take(P * I * (int8_acts(mode) ? 4 : 2));
   w.y = reinterpret_cast<float*>(take(P * H * 4));
   if (int8_acts(mode)) {
@@ -434,7 +436,8 @@ int ffn_forward(const q4_moe_layer_t* L, const uint16_t* x_bf16, int64_t t, cons
   int rc;
   stage_begin(Q4_STAGE_PERMUTE, stream);
   if ((rc = check_hip(launch_permute(topk_ids, t, L->top_k, L->num_experts, shared, w.counts, w.offsets, w.perm,
-                                     w.inv, w.tiles, w.num_tiles, w.tile_rows, stream),
+                                     w.inv, w.tiles, w.num_tiles, w.tile_rows, stream, L->expert_bits,
+                                     L->expert_groups, w.fmt_tiles),
                       "permute")))
     return rc;
   stage_end(Q4_STAGE_PERMUTE, stream);
@@ -471,19 +474,23 @@ int ffn_forward(const q4_moe_layer_t* L, const uint16_t* x_bf16, int64_t t, cons
   auto gemm1 = [&](const GemmArgs& g, int act, int kind) {
     return w.prefill ? launch_gemm_prefill(g, act, kind, stream) : launch_gemm(g, act, kind, rb, stream);
   };
-  // Layers whose experts differ in width or group size: one launch per format (width,
-  // scale entries per tile), each skipping the tiles of other formats.  The bf16 prefill
-  // kernel reads activation sums per scale group; they are recomputed at each launch's
+  // Layers whose experts differ in width or group size: the permutation orders the row
+  // tiles by weight format (0: 4-bit, one scale entry per tile; 1: two; 2: four; 3: 8-bit)
+  // and one launch per format walks that format's tile range.  The bf16 prefill kernel
+  // reads activation sums per scale group; they are recomputed at each launch's
   // granularity (rs_a: the activations, rs_rows their rows) before it.
   auto gemm = [&](const GemmArgs& g, int act, int kind, const void* rs_a = nullptr, int64_t rs_rows = 0) {
     if (!g.ebits && !g.egroups) return gemm1(g, act, kind);
-    const int widths = g.ebits ? 2 : 1;
-    for (int wi = 0; wi < widths; ++wi) {
-      for (int sg = 1; sg <= 4; sg *= 2) {
-        if (sg > 1 && (!g.egroups || wi == 1)) continue;
+    for (int f = 0; f < 4; ++f) {
+      {
+        if (f == 3 && !g.ebits) continue;
+        if ((f == 1 || f == 2) && !g.egroups) continue;
+        const int sg = f == 2 ? 4 : f == 1 ? 2 : 1;
         GemmArgs a = g;
-        a.wbits = wi ? 8 : 4;
+        a.wbits = f == 3 ? 8 : 4;
         a.sg = sg;
+        a.fmt_tiles = w.fmt_tiles;
+        a.fmt = f;
         if (rs_a && a.a_gsum) {
           const hipError_t e = launch_rowsum(rs_a, 0, rs_rows, a.K, const_cast<float*>(a.a_gsum), stream, sg);
           if (e != hipSuccess) return e;

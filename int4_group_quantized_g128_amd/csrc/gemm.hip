@@ -120,20 +120,27 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs args) {
   const int64_t N = args.N, K = args.K, G = K / kGroup;
   const int64_t nblk = N / (16 * kCBWG);
   const int64_t tile_rows = 16 * MB;
-  const int64_t ntiles = args.tiles ? int64_t(*args.num_tiles) : (args.dense_rows + tile_rows - 1) / tile_rows;
+  int64_t t_first = 0;   // layers with several weight formats: this launch's tile range
+  int64_t ntiles = args.tiles ? int64_t(*args.num_tiles) : (args.dense_rows + tile_rows - 1) / tile_rows;
+  if (args.fmt_tiles) {
+    t_first = args.fmt_tiles[args.fmt];
+    ntiles = args.fmt_tiles[args.fmt + 1] - t_first;
+  }
   const int64_t items = ntiles * nblk;
   const int64_t w_scale_off = align256(W8 ? N * K : N * K / 2);
   const int64_t w_zero_off = w_scale_off + align256(2 * N * G * SG);
   const int64_t gper = (G + KW - 1) / KW;
   const int64_t g_beg = std::min<int64_t>(G, kw * gper), g_end = std::min<int64_t>(G, g_beg + gper);
-  // LDS: scales [kCBWG][G][SG][16] fp16, zero points [kCBWG][G][16] u8, reduction buffer
+  // LDS: scales [kCBWG][G][16] fp16 (one entry per tile; with SG > 1 entries per tile
+  // each lane loads its column's entries with the weights instead), zero points
+  // [kCBWG][G][16] u8, reduction buffer
+  const int64_t scale_lds = SG == 1 ? align256(int64_t(kCBWG) * G * 32) : 0;
   uint16_t* s_scale = reinterpret_cast<uint16_t*>(smem);
-  uint8_t* s_zero = smem + align256(int64_t(kCBWG) * G * 32 * SG);
-  float* s_red = reinterpret_cast<float*>(smem + align256(int64_t(kCBWG) * G * 32 * SG) +
-                                          (ASYM ? align256(int64_t(kCBWG) * G * 16) : 0));
+  uint8_t* s_zero = smem + scale_lds;
+  float* s_red = reinterpret_cast<float*>(smem + scale_lds + (ASYM ? align256(int64_t(kCBWG) * G * 16) : 0));
 
   for (int64_t item = blockIdx.x; item < items; item += gridDim.x) {
-    const int64_t tile = item / nblk;
+    const int64_t tile = t_first + item / nblk;
     const int64_t cb0 = (item % nblk) * kCBWG;     // first column block of the workgroup
     int32_t expert = 0;
     int64_t row_start, rows;
@@ -146,16 +153,14 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs args) {
       row_start = tile * tile_rows;
       rows = std::min<int64_t>(tile_rows, args.dense_rows - row_start);
     }
-    if (args.ebits && args.ebits[expert] != (W8 ? 8 : 4)) continue;   // other format (uniform skip)
-    if (args.egroups && sg_of_code(args.egroups[expert]) != SG) continue;
     const uint8_t* wbase = expert >= args.num_experts ? args.w_shared
                            : args.woffs                 ? args.w + args.woffs[expert]
                                                         : args.w + int64_t(expert) * args.w_stride;
 
     // stage the workgroup's scales / zero points (contiguous in the device layout)
-    {
-      const uint4* src = reinterpret_cast<const uint4*>(wbase + w_scale_off + cb0 * G * 32 * SG);
-      const int64_t n16 = int64_t(kCBWG) * G * 2 * SG;
+    if constexpr (SG == 1) {
+      const uint4* src = reinterpret_cast<const uint4*>(wbase + w_scale_off + cb0 * G * 32);
+      const int64_t n16 = int64_t(kCBWG) * G * 2;
       for (int64_t i = threadIdx.x; i < n16; i += 256) reinterpret_cast<uint4*>(s_scale)[i] = src[i];
       if constexpr (ASYM) {
         const uint8_t* zsrc = wbase + w_zero_off + cb0 * G * 16;
@@ -184,7 +189,7 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs args) {
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
       ap[mb] = static_cast<const uint8_t*>(args.a) + (ri[mb].src * K + 8 * kq) * (A == Act::I8 ? 1 : 2);
-    const int sbase = (lcb * int(G) * SG) * 16 + col;
+    const int sbase = (lcb * int(G)) * 16 + col;
 
     f32x4_t acc[MB][NBW];
 #pragma unroll
@@ -195,8 +200,23 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs args) {
     struct Stage {
       uint32_t wv[NBW][W8 ? 8 : 4];
       uint32_t av[MB][4][4];
+      uint32_t sv[NBW][SG > 1 ? SG / 2 : 1];   // SG > 1: the column's SG binary16 scales
     };
+    // SG > 1: this lane's column's scale entries of group g, column block nb
+    const uint8_t* sp = wbase + w_scale_off + (int64_t(cb0 + lcb) * G * 16 + col) * 2 * SG;
     auto load_stage = [&](Stage& st, int g) {
+      if constexpr (SG == 2) {
+#pragma unroll
+        for (int nb = 0; nb < NBW; ++nb)
+          st.sv[nb][0] = *reinterpret_cast<const uint32_t*>(sp + (int64_t(nb) * G + g) * 16 * 2 * SG);
+      } else if constexpr (SG == 4) {
+#pragma unroll
+        for (int nb = 0; nb < NBW; ++nb) {
+          const uint2 v = load8(sp + (int64_t(nb) * G + g) * 16 * 2 * SG);
+          st.sv[nb][0] = v.x;
+          st.sv[nb][1] = v.y;
+        }
+      }
 #pragma unroll
       for (int nb = 0; nb < NBW; ++nb) {
         const uint4 v = load16_stream(wp[nb] + g * TB);
@@ -231,9 +251,13 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs args) {
       float sc[NBW][SG], zp[NBW];
 #pragma unroll
       for (int nb = 0; nb < NBW; ++nb) {
-        const int li = sbase + (nb * int(G) + g) * SG * 16;
+        const int li = sbase + (nb * int(G) + g) * 16;
+        if constexpr (SG == 1) {
+          sc[nb][0] = f16_bits_to_f32(s_scale[li]);
+        } else {
 #pragma unroll
-        for (int j = 0; j < SG; ++j) sc[nb][j] = f16_bits_to_f32(s_scale[li + j * 16]);
+          for (int j = 0; j < SG; ++j) sc[nb][j] = f16_bits_to_f32(uint16_t(st.sv[nb][j / 2] >> (16 * (j & 1))));
+        }
         zp[nb] = ASYM ? float(s_zero[li]) : 8.0f;   // SG == 1 with zero points
       }
       if constexpr (A == Act::BF16) {
@@ -451,7 +475,7 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs args) {
 static size_t gemm_lds_bytes(int64_t K, int asym, int mb, int kw, int nbw, int sg) {
   const int64_t G = K / kGroup;
   const int64_t cbwg = (4 / kw) * nbw;
-  size_t b = size_t(align256(cbwg * G * 32 * sg));
+  size_t b = sg == 1 ? size_t(align256(cbwg * G * 32)) : 0;
   if (asym) b += size_t(align256(cbwg * G * 16));
   if (kw > 1) b += size_t(4) * mb * nbw * 64 * 4 * sizeof(float);
   return b;

@@ -144,7 +144,7 @@ Q4_DEVICE void copy_to_lds(const u32x4_t& rsrc, uint32_t lds_in, uint32_t voff, 
 // Per-stage LDS image of one group (K = 128) of one work item:
 //   A tile  [128 rows][ROWB]  (16-byte chunks XOR-swizzled by row)
 //   W tiles [8 column blocks][TB]  (the device tiles as stored: 1 KB 4-bit, 2 KB 8-bit)
-//   scales  [8][SG][16] fp16, zero points [8][16] u8 (asymmetric, SG == 1)
+//   scales  [8][16][SG] fp16, zero points [8][16] u8 (asymmetric, SG == 1)
 //   rsum    [SG][128] fp32 row sums (bf16) / int32 code sums (int8, asymmetric)
 // (SG scale entries per tile: groups of 128 / SG elements)
 // int8 activations: two workgroups per CU (a two-slot ring: 51 KB of LDS with 4-bit
@@ -230,7 +230,12 @@ __global__ void __launch_bounds__(256, (A == Act::I8) ? 2 : 1) k_gemm_pf(GemmArg
   const int64_t N = args.N, K = args.K;
   const int G = int(K / kGroup);
   const int64_t nblk = N / (16 * kPfCB);
-  const int64_t items = *args.num_tiles * nblk;
+  int64_t t_first = 0, ntiles = *args.num_tiles;   // several weight formats: this launch's tiles
+  if (args.fmt_tiles) {
+    t_first = args.fmt_tiles[args.fmt];
+    ntiles = args.fmt_tiles[args.fmt + 1] - t_first;
+  }
+  const int64_t items = ntiles * nblk;
   const int64_t w_scale_off = align256(W8 ? N * K : N * K / 2);
   const int64_t w_zero_off = w_scale_off + align256(2 * N * int64_t(G) * SG);
   const auto a_rsrc = buffer_rsrc(args.a, args.a_rows * K * St::ESZ);
@@ -239,11 +244,9 @@ __global__ void __launch_bounds__(256, (A == Act::I8) ? 2 : 1) k_gemm_pf(GemmArg
 
   const ItemRange ir = item_range(items);
   for (int64_t item = ir.first; item < ir.last; item += ir.step) {
-    const int64_t tile = item / nblk;
+    const int64_t tile = t_first + item / nblk;
     const int64_t cb0 = (item % nblk) * kPfCB;
     const TileDesc d = args.tiles[tile];
-    if (args.ebits && args.ebits[d.expert] != (W8 ? 8 : 4)) continue;   // other format (uniform skip)
-    if (args.egroups && sg_of_code(args.egroups[d.expert]) != SG) continue;
     if constexpr (A == Act::I8) __syncthreads();   // previous item's epilogue is done with s_sa
     const int64_t row_start = d.row_start;
     const int rows = d.rows;
@@ -359,7 +362,7 @@ __global__ void __launch_bounds__(256, (A == Act::I8) ? 2 : 1) k_gemm_pf(GemmArg
               b[nb][s] = u32x4_t{o[0], o[1], o[2], o[3]};
             }
 #pragma unroll
-            for (int j = 0; j < SG; ++j) sc[nb][j] = f16_bits_to_f32(s_sc[((wn * 4 + nb) * SG + j) * 16 + col]);
+            for (int j = 0; j < SG; ++j) sc[nb][j] = f16_bits_to_f32(s_sc[((wn * 4 + nb) * 16 + col) * SG + j]);
           }
           const float negz = -(magic_offset<A>() + 8.0f);
 #pragma unroll
@@ -400,7 +403,7 @@ __global__ void __launch_bounds__(256, (A == Act::I8) ? 2 : 1) k_gemm_pf(GemmArg
             b[nb][1] = u32x4_t{o[4], o[5], o[6], o[7]};
 #pragma unroll
             for (int j = 0; j < SG; ++j)
-              sc16[nb][j] = f16_bits_to_f32(s_sc[((wn * 4 + nb) * SG + j) * 16 + col]) * 0.0625f;
+              sc16[nb][j] = f16_bits_to_f32(s_sc[((wn * 4 + nb) * 16 + col) * SG + j]) * 0.0625f;
           }
 #pragma unroll
           for (int mb = 0; mb < NMB; ++mb) {

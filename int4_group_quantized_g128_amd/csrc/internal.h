@@ -39,9 +39,10 @@ hipError_t launch_route(const uint16_t* x, const float* wr, const float* bias, i
 
 // Permutation.  Slots s = t * S + j with S = k + shared; expert(s) = ids[t][j] for
 // j < k, num_experts for the shared slot.  Optionally builds the row-tile list.
-hipError_t launch_permute(const int32_t* ids, int64_t t, int32_t k, int32_t e, int shared,
-                          int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv,
-                          TileDesc* tiles, int32_t* num_tiles, int tile_rows, hipStream_t st);
+hipError_t launch_permute(const int32_t* ids, int64_t t, int32_t k, int32_t e, int shared, int32_t* counts,
+                          int32_t* offsets, int32_t* perm, int32_t* inv, TileDesc* tiles, int32_t* num_tiles,
+                          int tile_rows, hipStream_t st, const uint8_t* ebits = nullptr,
+                          const uint8_t* egroups = nullptr, int32_t* fmt_tiles = nullptr);
 
 // Per-row INT8 activation quantisation (x: bf16 or fp32 rows).
 hipError_t launch_act_quant(const void* x, int x_is_f32, int64_t rows, int64_t cols, int8_t* q, float* s,
@@ -66,8 +67,10 @@ struct GemmArgs {
   int32_t wbits;          // 4 (INT4 tiles) or 8 (INT8 tiles, int8 activations only)
   const uint8_t* ebits;   // mixed layers: bits per expert (tiles of other experts are skipped), or NULL
   const int64_t* woffs;   // mixed layers: byte offset of each routed expert's block in w, or NULL
-  const uint8_t* egroups; // per-expert group size / 32 (tiles of experts of another sg are skipped), or NULL
+  const uint8_t* egroups; // per-expert group size / 32, or NULL
   int32_t sg;             // scale entries per 128-element tile of this launch (1, 2, 4)
+  const int32_t* fmt_tiles;  // layers with several weight formats: tile range of each format [5], or NULL
+  int32_t fmt;            // this launch's format (tiles fmt_tiles[fmt] .. fmt_tiles[fmt + 1])
   int64_t N;              // device columns (2I for gate/up)
   int64_t K;
   // tiles

@@ -53,12 +53,25 @@ __device__ int32_t block_exclusive_scan(int32_t* data, int n, int32_t* wave_tot)
   return total;
 }
 
+// Weight format of expert x for the tile order: 0 = 4-bit with one scale entry per tile,
+// 1 = two entries (groups of 64), 2 = four (groups of 32), 3 = 8-bit.
+__device__ __forceinline__ int tile_format(const uint8_t* ebits, const uint8_t* egroups, int x) {
+  if (ebits && ebits[x] == 8) return 3;
+  if (egroups) {
+    const int sg = sg_of_code(egroups[x]);
+    return sg == 4 ? 2 : sg == 2 ? 1 : 0;
+  }
+  return 0;
+}
+
 __global__ void __launch_bounds__(kPermThreads) k_permute(const int32_t* __restrict__ ids, int64_t t, int32_t k,
                                                           int32_t e, int shared, int nwaves,
                                                           int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
                                                           int32_t* __restrict__ perm, int32_t* __restrict__ inv,
                                                           TileDesc* __restrict__ tiles, int32_t* __restrict__ num_tiles,
-                                                          int tile_rows) {
+                                                          int tile_rows, const uint8_t* __restrict__ ebits,
+                                                          const uint8_t* __restrict__ egroups,
+                                                          int32_t* __restrict__ fmt_tiles) {
   extern __shared__ int32_t lds[];
   __shared__ int32_t wave_tot[kPermThreads / 64 + 1];
   const int ee = e + shared;            // experts incl. the shared one
@@ -133,15 +146,31 @@ __global__ void __launch_bounds__(kPermThreads) k_permute(const int32_t* __restr
       __builtin_amdgcn_wave_barrier();
     }
   }
-  // tile list: ceil(count / tile_rows) tiles per expert, in expert order
+  // tile list: ceil(count / tile_rows) tiles per expert, ordered by (weight format,
+  // expert), so that a GEMM launch for one format walks one contiguous range of tiles;
+  // fmt_tiles[f] .. fmt_tiles[f + 1] is format f's range
   if (tiles) {
+    int32_t* ntl = lds + nwaves * ee + ee + 1;   // [ee] tiles per expert
+    int32_t* first = ntl + ee;                   // [ee] first tile of each expert
     __syncthreads();
-    for (int x = tid; x < ee; x += kPermThreads) tot[x] = (counts[x] + tile_rows - 1) / tile_rows;
+    for (int x = tid; x < ee; x += kPermThreads) ntl[x] = (counts[x] + tile_rows - 1) / tile_rows;
     __syncthreads();
-    const int32_t ntiles = block_exclusive_scan(tot, ee, wave_tot);
+    int32_t base = 0;
+    for (int f = 0; f < 4; ++f) {
+      for (int x = tid; x < ee; x += kPermThreads) tot[x] = tile_format(ebits, egroups, x) == f ? ntl[x] : 0;
+      __syncthreads();
+      const int32_t nf = block_exclusive_scan(tot, ee, wave_tot);
+      for (int x = tid; x < ee; x += kPermThreads)
+        if (tile_format(ebits, egroups, x) == f) first[x] = base + tot[x];
+      if (fmt_tiles && tid == 0) fmt_tiles[f] = base;
+      base += nf;
+      __syncthreads();
+    }
+    const int32_t ntiles = base;
+    if (fmt_tiles && tid == 0) fmt_tiles[4] = ntiles;
     for (int x = tid; x < ee; x += kPermThreads) {
       const int32_t c = counts[x], o = offsets[x];
-      int32_t ti = tot[x];
+      int32_t ti = first[x];
       for (int32_t r = 0; r < c; r += tile_rows, ++ti) {
         TileDesc d;
         d.expert = x;
@@ -157,14 +186,15 @@ __global__ void __launch_bounds__(kPermThreads) k_permute(const int32_t* __restr
 
 hipError_t launch_permute(const int32_t* ids, int64_t t, int32_t k, int32_t e, int shared, int32_t* counts,
                           int32_t* offsets, int32_t* perm, int32_t* inv, TileDesc* tiles, int32_t* num_tiles,
-                          int tile_rows, hipStream_t st) {
+                          int tile_rows, hipStream_t st, const uint8_t* ebits, const uint8_t* egroups,
+                          int32_t* fmt_tiles) {
   const int ee = e + shared;
   const size_t budget = 96 * 1024;
-  int nwaves = int(std::min<size_t>(16, (budget / sizeof(int32_t) - (ee + 1)) / ee));
+  int nwaves = int(std::min<size_t>(16, (budget / sizeof(int32_t) - (3 * ee + 1)) / ee));
   nwaves = std::max(1, nwaves);
-  const size_t lds = (size_t(nwaves) * ee + ee + 1) * sizeof(int32_t);
+  const size_t lds = (size_t(nwaves) * ee + 3 * ee + 1) * sizeof(int32_t);
   hipLaunchKernelGGL(k_permute, dim3(1), dim3(kPermThreads), lds, st, ids, t, k, e, shared, nwaves, counts,
-                     offsets, perm, inv, tiles, num_tiles, tile_rows);
+                     offsets, perm, inv, tiles, num_tiles, tile_rows, ebits, egroups, fmt_tiles);
   return hipGetLastError();
 }
 

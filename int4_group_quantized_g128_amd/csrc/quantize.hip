@@ -237,10 +237,10 @@ __global__ void k_repack_weights(const uint8_t* __restrict__ packed, int64_t n, 
   }
 }
 
-// Scales (and zero points) into [n/16][G][SG][16] with the device column order.  SG
-// scale entries per 128-element tile (128 / group for groups of 32 and 64, else 1);
-// entry (tile g, j) holds canonical group (128 g + j 128 / SG) / group, so a 256-group's
-// scale (and zero point) is repeated on both of its tiles.
+// Scales (and zero points) into [n/16][G][16][SG] with the device column order.  SG
+// scale entries per 128-element tile (128 / group for groups of 32 and 64, else 1),
+// adjacent per column; entry (tile g, j) holds canonical group (128 g + j 128 / SG) /
+// group, so a 256-group's scale (and zero point) is repeated on both of its tiles.
 __global__ void k_repack_meta(const uint16_t* __restrict__ scales, const uint8_t* __restrict__ zeros,
                               int64_t n, int64_t k, int group, int gate_up, uint16_t* __restrict__ sout,
                               uint8_t* __restrict__ zout) {
@@ -250,10 +250,10 @@ __global__ void k_repack_meta(const uint16_t* __restrict__ scales, const uint8_t
   const int64_t total = n * G * SG;
   for (int64_t i = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; i < total;
        i += int64_t(gridDim.x) * blockDim.x) {
-    const int c = int(i & 15);
-    const int j = int((i >> 4) % SG);
-    const int64_t g = (i >> 4) / SG % G;
-    const int64_t cb = (i >> 4) / SG / G;
+    const int j = int(i % SG);
+    const int c = int((i / SG) & 15);
+    const int64_t g = (i / SG >> 4) % G;
+    const int64_t cb = (i / SG >> 4) / G;
     int64_t src = cb * 16 + c;
     if (gate_up) {
       const int64_t half = n / 2;

@@ -36,25 +36,25 @@ def _np(t):
 
 
 class OracleExperts:
-    """Oracle-quantised experts of the layer, by (expert, bits); codes kept as int8."""
+    """Oracle-quantised experts of the layer, by (expert, bits, group); codes kept as int8."""
 
     def __init__(self):
         self.cache = {}
 
-    def get(self, e, bits):
-        key = (e, bits)
+    def get(self, e, bits, group=128):
+        key = (e, bits, group)
         if key not in self.cache:
             mats = synth.expert_weights(CFG, e, device="cuda")
             out = []
             for m in mats:
                 w = _np(m)
-                q, s = quant.quantize_sym8(w) if bits == 8 else quant.quantize_sym(w)
+                q, s = quant.quantize_sym8(w) if bits == 8 else quant.quantize_sym(w, group)
                 out.append((q.astype(np.int8), s, None))
             self.cache[key] = tuple(out)
         return self.cache[key]
 
-    def have(self, e, bits):
-        return (e, bits) in self.cache
+    def have(self, e, bits, group=128):
+        return (e, bits, group) in self.cache
 
 
 @pytest.fixture(scope="module")
@@ -81,19 +81,19 @@ def _oracle_routing(x, t):
     return ids, router.topk_weights(L, ids)
 
 
-def _pick(agree, ids, n, seed, bits, have):
+def _pick(agree, ids, n, seed, bits, groups, have):
     """n agreeing tokens, preferring ones whose experts the oracle already holds."""
     cand = list(np.random.default_rng(seed).permutation(np.nonzero(agree)[0]))
     chosen = []
     while len(chosen) < n and cand:
         window = cand[:16]
-        best = min(window, key=lambda r: sum(not have(int(e), bits[int(e)]) for e in ids[r]))
+        best = min(window, key=lambda r: sum(not have(int(e), bits[int(e)], groups[int(e)]) for e in ids[r]))
         chosen.append(int(best))
         cand.remove(best)
     return np.array(sorted(chosen))
 
 
-def _check(lib, wl, kind, oe, nsample, seed, bits=None):
+def _check(lib, wl, kind, oe, nsample, seed, bits=None, groups=None):
     E = synth.CONFIGS[CFG]["experts"]
     t = wl.t
     print(f"[fullsize] {kind} T={t}: step", flush=True)
@@ -106,9 +106,11 @@ def _check(lib, wl, kind, oe, nsample, seed, bits=None):
     assert agree.mean() >= (0.9 if t > 1 else 1.0), f"routing agrees on {agree.mean():.3f} of the tokens"
     if bits is None:
         bits = [8 if kind == "w8a8" else 4] * (E + 1)
-    rows = _pick(agree, ids_o, nsample, seed, bits, oe.have)
+    if groups is None:
+        groups = [128] * (E + 1)
+    rows = _pick(agree, ids_o, nsample, seed, bits, groups, oe.have)
     print(f"[fullsize] {kind} T={t}: oracle on tokens {rows.tolist()}", flush=True)
-    expert = lambda e: oe.get(e, bits[e])
+    expert = lambda e: oe.get(e, bits[e], groups[e])
     shared = expert(E)
     xs, ids_s, w_s = x[rows], ids_o[rows], w_o[rows]
     if kind == "w4a16":
@@ -176,3 +178,25 @@ def test_mixed_widths_by_hotness(lib, mixed, oracle_experts, t):
     GEMM per width over the same tile list."""
     wl, bits = mixed
     _check(lib, wl if t == 64 else wl.retoken(synth, t), "mixed", oracle_experts, 2, 7 + t, bits=bits)
+
+
+@pytest.fixture(scope="module")
+def grouped(lib, bench_mod):
+    """Group sizes from the oracle's routing of the calibration batch: the top 5 % of the
+    experts 32, experts under a tenth of the even share 256, the others 64, shared 32."""
+    cfg = synth.CONFIGS[CFG]
+    xc = _np(synth.tokens(CFG, 4096, salt=7))
+    ids_c, _ = _oracle_routing(xc, 4096)
+    groups = ffn.groups_by_hotness(np.bincount(ids_c.ravel(), minlength=cfg["experts"]), 0.05, 0.1, shared=True)
+    assert sum(g == 32 for g in groups) == 13 + 1
+    wl = bench_mod.Workload(lib, torch, synth, CFG, 64, "w4a16", expert_groups=groups)
+    yield wl, groups
+    del wl
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("t,mode", [(64, "w4a16"), (4096, "w4a8")])
+def test_per_expert_groups_by_hotness(lib, grouped, oracle_experts, t, mode):
+    wl, groups = grouped
+    _check(lib, wl if (t, mode) == (64, "w4a16") else wl.retoken(synth, t, mode), mode, oracle_experts, 2,
+           11 + t, groups=groups)
