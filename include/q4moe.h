@@ -269,7 +269,9 @@ typedef struct q4_moe_layer_t {
    * group) and (H, I, 0, group) bytes); modes W4A16 and W4A8 (W4A8 only if expert_bits
    * is also given, in which case 8-bit experts must have group 128).  The values are
    * the group size / 32 (1, 2, 4 or 8); the shared expert's is expert_groups[num_experts].
-   * Invalid values make the expert's tiles be skipped (its output rows undefined). */
+   * Any value other than 1 or 2 is read as one scale entry per tile (groups of 128 or
+   * 256).  The forward orders the row tiles by weight format and runs each GEMM once
+   * per format present in the layer's description. */
   const uint8_t* expert_groups;    /* device [num_experts + shared] values 1, 2, 4 or 8 */
 } q4_moe_layer_t;
 
