@@ -396,6 +396,7 @@ size_t moe_int4_ffn_workspace_bytes(const q4_moe_layer_t* layer, int64_t t, int 
   return size_t(carve(layer, t, mode, nullptr).bytes);
 }
 
+extern "C++" {  // internal helpers keep C++ linkage
 namespace {
 
 int ffn_forward(const q4_moe_layer_t* L, const uint16_t* x_bf16, int64_t t, const int32_t* topk_ids,
@@ -555,6 +556,7 @@ int ffn_forward(const q4_moe_layer_t* L, const uint16_t* x_bf16, int64_t t, cons
 }
 
 }  // namespace
+}  // extern "C++"
 
 int moe_int4_ffn_forward(const q4_moe_layer_t* L, const uint16_t* x_bf16, int64_t t, const int32_t* topk_ids,
                          const float* topk_w, int mode, uint16_t* out_bf16, void* workspace, size_t ws_bytes,
@@ -573,6 +575,7 @@ int moe_int4_ffn_debug(const q4_moe_layer_t* L, const uint16_t* x_bf16, int64_t 
 }
 
 // ------------------------------------------------------------------ LoRA-mode experts
+extern "C++" {  // internal helpers keep C++ linkage
 namespace {
 
 struct LoraWorkspace {
@@ -665,6 +668,7 @@ int dense_gemm(const uint16_t* a, int64_t rows, int64_t k, const void* w_dev, in
 }
 
 }  // namespace
+}  // extern "C++"
 
 size_t moe_lora_ffn_workspace_bytes(const q4_lora_layer_t* layer, int64_t t) {
   if (!layer || t < 0 || validate_lora(layer) != Q4_OK) return 0;
