@@ -32,14 +32,17 @@ __device__ int32_t block_exclusive_scan(int32_t* data, int n, int32_t* wave_tot)
   }
   if (lane == 63) wave_tot[wid] = v;
   __syncthreads();
-  if (tid == 0) {
-    int32_t run = 0;
-    for (int w = 0; w < kPermThreads / 64; ++w) {
-      const int32_t x = wave_tot[w];
-      wave_tot[w] = run;
-      run += x;
+  if (wid == 0) {   // exclusive scan of the wave totals by wave 0 (each lane reads, then writes, its own)
+    constexpr int nw = kPermThreads / 64;
+    const int32_t x = lane < nw ? wave_tot[lane] : 0;
+    int32_t incl = x;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int32_t u = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += u;
     }
-    wave_tot[kPermThreads / 64] = run;
+    if (lane < nw) wave_tot[lane] = incl - x;
+    if (lane == nw - 1) wave_tot[nw] = incl;
   }
   __syncthreads();
   int32_t run = v - local + wave_tot[wid];
@@ -156,7 +159,12 @@ __global__ void __launch_bounds__(kPermThreads) k_permute(const int32_t* __restr
     for (int x = tid; x < ee; x += kPermThreads) ntl[x] = (counts[x] + tile_rows - 1) / tile_rows;
     __syncthreads();
     int32_t base = 0;
+    const int nfmt = (ebits || egroups) ? 4 : 1;   // one format unless the layer mixes them
     for (int f = 0; f < 4; ++f) {
+      if (f >= nfmt) {
+        if (fmt_tiles && tid == 0) fmt_tiles[f] = base;
+        continue;
+      }
       for (int x = tid; x < ee; x += kPermThreads) tot[x] = tile_format(ebits, egroups, x) == f ? ntl[x] : 0;
       __syncthreads();
       const int32_t nf = block_exclusive_scan(tot, ee, wave_tot);
