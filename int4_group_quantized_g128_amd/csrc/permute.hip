@@ -94,9 +94,18 @@ __global__ void __launch_bounds__(kPermThreads) k_permute(const int32_t* __restr
     int x = ids[tok * k + j];
     return min(max(x, 0), e - 1);       // out-of-range ids are clamped
   };
-  // pass 1
+  // pass 1 (the experts of a lane's first kKeep slots stay in registers for pass 3)
+  constexpr int kKeep = 4;
+  int kept[kKeep];
   if (wid < nwaves) {
-    for (int64_t s = beg + lane; s < end; s += 64) atomicAdd(&cnt[wid * ee + expert_of(s)], 1);
+    int i = 0;
+    for (int64_t s = beg + lane; s < end; s += 64, ++i) {
+      const int x = expert_of(s);
+#pragma unroll
+      for (int j = 0; j < kKeep; ++j)
+        if (i == j) kept[j] = x;
+      atomicAdd(&cnt[wid * ee + x], 1);
+    }
   }
   __syncthreads();
   // pass 2: totals, offsets, per-wave bases
@@ -106,11 +115,21 @@ __global__ void __launch_bounds__(kPermThreads) k_permute(const int32_t* __restr
     tot[x] = run;
   }
   __syncthreads();
-  for (int x = tid; x < ee; x += kPermThreads) counts[x] = tot[x];
+  // LDS after cnt [nwaves][ee] and tot [ee + 1]: counts, offsets, tiles per expert,
+  // first tile of each expert ([ee] each)
+  int32_t* cntl = lds + nwaves * ee + ee + 1;
+  int32_t* offl = cntl + ee;
+  int32_t* ntl = offl + ee;
+  int32_t* first = ntl + ee;
+  for (int x = tid; x < ee; x += kPermThreads) {
+    counts[x] = tot[x];
+    cntl[x] = tot[x];
+  }
   __syncthreads();
   const int32_t total = block_exclusive_scan(tot, ee, wave_tot);
   for (int x = tid; x < ee; x += kPermThreads) {
     offsets[x] = tot[x];
+    offl[x] = tot[x];
     int32_t run = tot[x];
     for (int w = 0; w < nwaves; ++w) {
       const int32_t c = cnt[w * ee + x];
@@ -124,10 +143,18 @@ __global__ void __launch_bounds__(kPermThreads) k_permute(const int32_t* __restr
   int nbits = 1;
   while ((1 << nbits) <= ee) ++nbits;
   if (wid < nwaves) {
-    for (int64_t s0 = beg; s0 < end; s0 += 64) {
+    int i = 0;
+    for (int64_t s0 = beg; s0 < end; s0 += 64, ++i) {
       const int64_t s = s0 + lane;
       const bool valid = s < end;
-      const int ex = valid ? expert_of(s) : 0;
+      int ex = 0;
+      if (i < kKeep) {
+#pragma unroll
+        for (int j = 0; j < kKeep; ++j)
+          if (i == j && valid) ex = kept[j];
+      } else if (valid) {
+        ex = expert_of(s);
+      }
       unsigned long long peers = __ballot(valid);
       for (int b = 0; b < nbits; ++b) {
         const unsigned long long m = __ballot((ex >> b) & 1);
@@ -153,10 +180,8 @@ __global__ void __launch_bounds__(kPermThreads) k_permute(const int32_t* __restr
   // expert), so that a GEMM launch for one format walks one contiguous range of tiles;
   // fmt_tiles[f] .. fmt_tiles[f + 1] is format f's range
   if (tiles) {
-    int32_t* ntl = lds + nwaves * ee + ee + 1;   // [ee] tiles per expert
-    int32_t* first = ntl + ee;                   // [ee] first tile of each expert
     __syncthreads();
-    for (int x = tid; x < ee; x += kPermThreads) ntl[x] = (counts[x] + tile_rows - 1) / tile_rows;
+    for (int x = tid; x < ee; x += kPermThreads) ntl[x] = (cntl[x] + tile_rows - 1) / tile_rows;
     __syncthreads();
     int32_t base = 0;
     const int nfmt = (ebits || egroups) ? 4 : 1;   // one format unless the layer mixes them
@@ -177,7 +202,7 @@ __global__ void __launch_bounds__(kPermThreads) k_permute(const int32_t* __restr
     const int32_t ntiles = base;
     if (fmt_tiles && tid == 0) fmt_tiles[4] = ntiles;
     for (int x = tid; x < ee; x += kPermThreads) {
-      const int32_t c = counts[x], o = offsets[x];
+      const int32_t c = cntl[x], o = offl[x];
       int32_t ti = first[x];
       for (int32_t r = 0; r < c; r += tile_rows, ++ti) {
         TileDesc d;
@@ -198,9 +223,9 @@ hipError_t launch_permute(const int32_t* ids, int64_t t, int32_t k, int32_t e, i
                           int32_t* fmt_tiles) {
   const int ee = e + shared;
   const size_t budget = 96 * 1024;
-  int nwaves = int(std::min<size_t>(16, (budget / sizeof(int32_t) - (3 * ee + 1)) / ee));
+  int nwaves = int(std::min<size_t>(16, (budget / sizeof(int32_t) - (5 * ee + 1)) / ee));
   nwaves = std::max(1, nwaves);
-  const size_t lds = (size_t(nwaves) * ee + 3 * ee + 1) * sizeof(int32_t);
+  const size_t lds = (size_t(nwaves) * ee + 5 * ee + 1) * sizeof(int32_t);
   hipLaunchKernelGGL(k_permute, dim3(1), dim3(kPermThreads), lds, st, ids, t, k, e, shared, nwaves, counts,
                      offsets, perm, inv, tiles, num_tiles, tile_rows, ebits, egroups, fmt_tiles);
   return hipGetLastError();
