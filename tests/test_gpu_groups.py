@@ -195,3 +195,47 @@ def test_moe8_grouped(lib, moe8, mode, t):
     fn = ffn.moe_w4a16 if mode == 0 else ffn.moe_w4a8
     ref = fn(_np(x)[rows], oe, ids[rows], w[rows])
     assert ffn.max_rel_l2(_np(out)[rows], ref) <= TOL[mode]
+
+
+@pytest.mark.parametrize("mode", [0, 1], ids=["w4a16", "w4a8"])
+def test_grouped_layer_edge_cases(lib, small, mode):
+    """No tokens (a no-op), one token, and a batch whose routing uses only experts of one
+    group size (the other formats' tile ranges are empty)."""
+    layer, oe = small
+    E, k, H = 16, 4, 256
+    x = torch.empty((0, H), dtype=torch.bfloat16, device="cuda")
+    out = lib.moe_int4_ffn_forward(layer, x, torch.empty((0, k), dtype=torch.int32, device="cuda"),
+                                   torch.empty((0, k), dtype=torch.float32, device="cuda"), mode=mode)
+    assert out.shape == (0, H)
+    x1, ids1, w1 = _case(1, E, k, H, 102)
+    o1 = lib.moe_int4_ffn_forward(layer, x1.cuda(), torch.as_tensor(ids1, dtype=torch.int32).cuda(),
+                                  torch.as_tensor(w1, dtype=torch.float32).cuda(), mode=mode)
+    torch.cuda.synchronize()
+    fn = ffn.moe_w4a16 if mode == 0 else ffn.moe_w4a8
+    assert ffn.max_rel_l2(_np(o1), fn(_np(x1), oe, ids1, w1, shared=oe(E))) <= TOL[mode]
+    only64 = [e for e in range(E) if SMALL_GROUPS[e] == 64]
+    t = 70
+    xs = synth.normal(synth.stream_key(103, t), (t, H), 1.0).to(torch.bfloat16)
+    rng = np.random.default_rng(104)
+    ids = np.stack([rng.permutation(only64)[:k] for _ in range(t)]).astype(np.int64)
+    w = rng.dirichlet(np.ones(k), size=t)
+    out = lib.moe_int4_ffn_forward(layer, xs.cuda(), torch.as_tensor(ids, dtype=torch.int32).cuda(),
+                                   torch.as_tensor(w, dtype=torch.float32).cuda(), mode=mode)
+    torch.cuda.synchronize()
+    assert ffn.max_rel_l2(_np(out), fn(_np(xs), oe, ids, w, shared=oe(E))) <= TOL[mode]
+
+
+def test_grouped_hidden_not_a_multiple_of_256(lib):
+    """K = 384 (three 128-tiles): groups of 32, 64 and 128 only."""
+    make = random_expert_maker(105, 384, 128)
+    groups = [32, 64, 128, 32, 64, 128]
+    layer = _layer(lib, make, 6, 384, 128, 2, False, groups)
+    oe = GroupedExperts(make, groups)
+    for t in (3, 260):
+        x, ids, w = _case(t, 6, 2, 384, 106)
+        for mode in (0, 1):
+            out = lib.moe_int4_ffn_forward(layer, x.cuda(), torch.as_tensor(ids, dtype=torch.int32).cuda(),
+                                           torch.as_tensor(w, dtype=torch.float32).cuda(), mode=mode)
+            torch.cuda.synchronize()
+            fn = ffn.moe_w4a16 if mode == 0 else ffn.moe_w4a8
+            assert ffn.max_rel_l2(_np(out), fn(_np(x), oe, ids, w)) <= TOL[mode], (t, mode)
