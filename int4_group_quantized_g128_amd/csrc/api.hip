@@ -118,7 +118,8 @@ FwdWorkspace carve(const q4_moe_layer_t* L, int64_t t, int mode, void* base) {
   const int64_t P = t * S;
   const int64_t H = L->hidden, I = L->inter;
   w.prefill = use_prefill(L, t, mode);
-  w.tile_rows = w.prefill ? 128 : 16 * row_blocks_for(L, t);
+  // (layers with groups of 32 / 64 use at most 32-row decode tiles)
+  w.tile_rows = w.prefill ? 128 : 16 * (L->expert_groups ? std::min(2, row_blocks_for(L, t)) : row_blocks_for(L, t));
   w.max_tiles = int32_t(P / w.tile_rows + std::min<int64_t>(ee, P) + 1);
   int64_t off = 0;
   auto take = [&](int64_t bytes) {
@@ -480,18 +481,23 @@ int ffn_forward(const q4_moe_layer_t* L, const uint16_t* x_bf16, int64_t t, cons
   // and one launch per format walks that format's tile range.  The bf16 prefill kernel
   // reads activation sums per scale group; they are recomputed at each launch's
   // granularity (rs_a: the activations, rs_rows their rows) before it.
+  // The decode GEMM takes all 4-bit formats in one launch (each item picks its expert's
+  // scale entries per tile).
   auto gemm = [&](const GemmArgs& g, int act, int kind, const void* rs_a = nullptr, int64_t rs_rows = 0) {
     if (!g.ebits && !g.egroups) return gemm1(g, act, kind);
     for (int f = 0; f < 4; ++f) {
       {
         if (f == 3 && !g.ebits) continue;
         if ((f == 1 || f == 2) && !g.egroups) continue;
-        const int sg = f == 2 ? 4 : f == 1 ? 2 : 1;
+        const bool merged = !w.prefill && g.egroups && f < 3;   // formats 0..2 in one decode launch
+        if (merged && f > 0) continue;
+        const int sg = merged ? -1 : f == 2 ? 4 : f == 1 ? 2 : 1;
         GemmArgs a = g;
         a.wbits = f == 3 ? 8 : 4;
         a.sg = sg;
         a.fmt_tiles = w.fmt_tiles;
         a.fmt = f;
+        a.fmt_end = merged ? 3 : f + 1;
         if (rs_a && a.a_gsum) {
           const hipError_t e = launch_rowsum(rs_a, 0, rs_rows, a.K, const_cast<float*>(a.a_gsum), stream, sg);
           if (e != hipSuccess) return e;

@@ -104,11 +104,13 @@ struct RowInfo {
 //  D   depth of the register pipeline (groups whose loads are in flight),
 //  W8  8-bit weights (2 KB tiles, int8 activations, no widening) instead of 4-bit.
 // The workgroup's scales (and zero points) are staged in LDS once per work item.
-template <Act A, int KIND, bool ASYM, int MB, int KW, int NBW, int D, bool W8, int SG>
+template <Act A, int KIND, bool ASYM, int MB, int KW, int NBW, int D, bool W8, int SGT>
 __global__ void __launch_bounds__(256) k_gemm(GemmArgs args) {
   static_assert(!W8 || (A == Act::I8 && !ASYM), "8-bit weights: symmetric, int8 activations");
-  // SG scale entries per 1 KB tile (groups of 128 / SG elements): symmetric 4-bit only
-  static_assert(SG == 1 || (!ASYM && !W8 && KIND != GEMM_GROUP_ACC && (SG == 2 || SG == 4)), "scale groups");
+  // SGT scale entries per 1 KB tile (groups of 128 / SGT elements; 0: per item, from the
+  // expert's group size): symmetric 4-bit only
+  static_assert(SGT == 1 || (!ASYM && !W8 && KIND != GEMM_GROUP_ACC && (SGT == 0 || SGT == 2 || SGT == 4)),
+                "scale groups");
   constexpr int64_t TB = W8 ? 2 * kTileBytes : kTileBytes;   // bytes per (column block, group) tile
   constexpr int kColGroups = 4 / KW;
   constexpr int kCBWG = kColGroups * NBW;  // column blocks per workgroup
@@ -124,17 +126,17 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs args) {
   int64_t ntiles = args.tiles ? int64_t(*args.num_tiles) : (args.dense_rows + tile_rows - 1) / tile_rows;
   if (args.fmt_tiles) {
     t_first = args.fmt_tiles[args.fmt];
-    ntiles = args.fmt_tiles[args.fmt + 1] - t_first;
+    ntiles = args.fmt_tiles[args.fmt_end] - t_first;
   }
   const int64_t items = ntiles * nblk;
   const int64_t w_scale_off = align256(W8 ? N * K : N * K / 2);
-  const int64_t w_zero_off = w_scale_off + align256(2 * N * G * SG);
+  const int64_t w_zero_off = w_scale_off + align256(2 * N * G);   // zero points: one scale entry per tile
   const int64_t gper = (G + KW - 1) / KW;
   const int64_t g_beg = std::min<int64_t>(G, kw * gper), g_end = std::min<int64_t>(G, g_beg + gper);
   // LDS: scales [kCBWG][G][16] fp16 (one entry per tile; with SG > 1 entries per tile
   // each lane loads its column's entries with the weights instead), zero points
   // [kCBWG][G][16] u8, reduction buffer
-  const int64_t scale_lds = SG == 1 ? align256(int64_t(kCBWG) * G * 32) : 0;
+  const int64_t scale_lds = (SGT == 0 || SGT == 1) ? align256(int64_t(kCBWG) * G * 32) : 0;
   uint16_t* s_scale = reinterpret_cast<uint16_t*>(smem);
   uint8_t* s_zero = smem + scale_lds;
   float* s_red = reinterpret_cast<float*>(smem + scale_lds + (ASYM ? align256(int64_t(kCBWG) * G * 16) : 0));
@@ -157,6 +159,9 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs args) {
                            : args.woffs                 ? args.w + args.woffs[expert]
                                                         : args.w + int64_t(expert) * args.w_stride;
 
+    // the rest of the item, for SG scale entries per tile
+    auto body = [&](auto sgc) {
+    constexpr int SG = decltype(sgc)::value;
     // stage the workgroup's scales / zero points (contiguous in the device layout)
     if constexpr (SG == 1) {
       const uint4* src = reinterpret_cast<const uint4*>(wbase + w_scale_off + cb0 * G * 32);
@@ -468,6 +473,18 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs args) {
       }
     }
     __syncthreads();
+    };
+    if constexpr (SGT == 0) {   // the expert's own scale entries per tile (wave-uniform)
+      const int sge = __builtin_amdgcn_readfirstlane(args.egroups ? sg_of_code(args.egroups[expert]) : 1);
+      if (sge == 4)
+        body(std::integral_constant<int, 4>{});
+      else if (sge == 2)
+        body(std::integral_constant<int, 2>{});
+      else
+        body(std::integral_constant<int, 1>{});
+    } else {
+      body(std::integral_constant<int, SGT>{});
+    }
   }
 }
 
@@ -475,7 +492,7 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs args) {
 static size_t gemm_lds_bytes(int64_t K, int asym, int mb, int kw, int nbw, int sg) {
   const int64_t G = K / kGroup;
   const int64_t cbwg = (4 / kw) * nbw;
-  size_t b = sg == 1 ? size_t(align256(cbwg * G * 32)) : 0;
+  size_t b = (sg == 0 || sg == 1) ? size_t(align256(cbwg * G * 32)) : 0;   // 0: per item
   if (asym) b += size_t(align256(cbwg * G * 16));
   if (kw > 1) b += size_t(4) * mb * nbw * 64 * 4 * sizeof(float);
   return b;
@@ -495,7 +512,7 @@ static hipError_t launch_cfg(const GemmArgs& g, hipStream_t st) {
   const unsigned grid = unsigned(std::min<int64_t>(items, Q4_GRID_CAP));
   const size_t lds = gemm_lds_bytes(g.K, g.asym, MB, KW, NBW, SG);
   if (lds > 160 * 1024) return hipErrorInvalidValue;  // K too large for the staged scales
-  if constexpr (SG > 1) {
+  if constexpr (SG > 1 || SG == 0) {
     if (g.asym) return hipErrorInvalidValue;
     hipLaunchKernelGGL((k_gemm<A, KIND, false, MB, KW, NBW, D, false, SG>), dim3(grid), dim3(256), lds, st, g);
   } else if constexpr (W8) {
@@ -542,17 +559,26 @@ static hipError_t launch_kind_sg(const GemmArgs& g, int rb, int split, hipStream
     return launch_cfg<A, KIND, 1, 4, 2, 2, W8, SG>(g, st);
   }
   if (rb <= 2) return launch_cfg<A, KIND, 2, 4, 4, 2, W8, SG>(g, st);
-  return launch_cfg<A, KIND, 4, 4, 4, 2, W8, SG>(g, st);
+  // 64-row tiles: one scale entry per tile only (the forward caps the tiles of layers
+  // with other group sizes at 32 rows; four row blocks with per-group accumulators
+  // would not fit the registers)
+  if constexpr (SG == 1) return launch_cfg<A, KIND, 4, 4, 4, 2, W8, SG>(g, st);
+  return hipErrorInvalidValue;
 }
 
-// scale entries per tile: 1 (groups of 128 / 256), 2 (64), 4 (32; 4-bit weights only)
+// scale entries per tile: 1 (groups of 128 / 256), 2 (64), 4 (32; 4-bit weights only), or
+// -1: per item from the expert's group size (one launch for all 4-bit formats)
 template <Act A, int KIND, bool W8 = false>
 static hipError_t launch_kind(const GemmArgs& g, int rb, int split, hipStream_t st) {
   if constexpr (!W8 && A != Act::F16) {
     if (g.sg == 2) return launch_kind_sg<A, KIND, false, 2>(g, rb, split, st);
     if (g.sg == 4) return launch_kind_sg<A, KIND, false, 4>(g, rb, split, st);
+    if (g.sg == -1) {
+      if (g.asym) return hipErrorInvalidValue;
+      return launch_kind_sg<A, KIND, false, 0>(g, rb, split, st);
+    }
   }
-  if (g.sg > 1) return hipErrorInvalidValue;
+  if (g.sg > 1 || g.sg < 0) return hipErrorInvalidValue;
   return launch_kind_sg<A, KIND, W8, 1>(g, rb, split, st);
 }
 

@@ -233,7 +233,7 @@ __global__ void __launch_bounds__(256, (A == Act::I8) ? 2 : 1) k_gemm_pf(GemmArg
   int64_t t_first = 0, ntiles = *args.num_tiles;   // several weight formats: this launch's tiles
   if (args.fmt_tiles) {
     t_first = args.fmt_tiles[args.fmt];
-    ntiles = args.fmt_tiles[args.fmt + 1] - t_first;
+    ntiles = args.fmt_tiles[args.fmt_end] - t_first;
   }
   const int64_t items = ntiles * nblk;
   const int64_t w_scale_off = align256(W8 ? N * K : N * K / 2);

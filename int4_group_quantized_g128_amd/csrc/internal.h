@@ -68,9 +68,9 @@ struct GemmArgs {
   const uint8_t* ebits;   // mixed layers: bits per expert (tiles of other experts are skipped), or NULL
   const int64_t* woffs;   // mixed layers: byte offset of each routed expert's block in w, or NULL
   const uint8_t* egroups; // per-expert group size / 32, or NULL
-  int32_t sg;             // scale entries per 128-element tile of this launch (1, 2, 4)
+  int32_t sg;             // scale entries per 128-element tile of this launch (1, 2, 4; -1: per item)
   const int32_t* fmt_tiles;  // layers with several weight formats: tile range of each format [5], or NULL
-  int32_t fmt;            // this launch's format (tiles fmt_tiles[fmt] .. fmt_tiles[fmt + 1])
+  int32_t fmt, fmt_end;   // this launch's formats: tiles fmt_tiles[fmt] .. fmt_tiles[fmt_end]
   int64_t N;              // device columns (2I for gate/up)
   int64_t K;
   // tiles

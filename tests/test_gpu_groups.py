@@ -106,9 +106,11 @@ def _case(t, E, k, H, seed):
 
 
 @pytest.mark.parametrize("mode", [0, 1], ids=["w4a16", "w4a8"])
-@pytest.mark.parametrize("t", [5, 300])
+@pytest.mark.parametrize("t", [5, 100, 200, 300])
 def test_small_grouped_layer(lib, small, mode, t):
-    """T = 5 runs the decode GEMMs, T = 300 (about 88 rows per expert) the prefill ones."""
+    """T = 5, 100 and 200 run the decode GEMMs (one launch for every group size; about 59
+    rows per expert at 200, in 32-row tiles), T = 300 (about 88 rows per expert) the
+    prefill ones."""
     layer, oe = small
     E, k, H = 16, 4, 256
     x, ids, w = _case(t, E, k, H, 98)
