@@ -678,6 +678,227 @@ __global__ void __launch_bounds__(256, (A == Act::I8) ? 2 : 1) k_gemm_pf(GemmArg
   }
 }
 
+// bf16 prefill with wide tiles: 128 rows x 256 columns (16 column blocks) per workgroup
+// of 8 waves (2 x 4 waves of 64 x 64), a three-slot LDS ring of 49 KB stages (A 32 KB,
+// W 16 KB, scales, zero points, row sums).  Each wave walks the four 32-element K steps
+// of a group outermost: only one K step's widened weights (16 registers) and the
+// per-tile group accumulators are live, which keeps the kernel within 256 registers so
+// two waves share each SIMD, and every activation byte copied to LDS feeds 256 columns.
+// One scale entry per tile (groups of 128 / 256).
+constexpr int kPfwCB = 16;
+
+template <int KIND, bool ASYM>
+__global__ void __launch_bounds__(512) k_gemm_pf16w(GemmArgs args) {
+  constexpr int ROWB = kGroup * 2;                      // bf16 bytes of one row of a group
+  constexpr int W_OFF = kPfRows * ROWB;                 // 32 KB of activations
+  constexpr int S_OFF = W_OFF + kPfwCB * kTileBytes;    // 16 KB of weight tiles
+  constexpr int Z_OFF = S_OFF + kPfwCB * 32;            // scales [16][16] fp16
+  constexpr int R_OFF = Z_OFF + kPfwCB * 16;            // zero points [16][16] u8
+  constexpr int BYTES = R_OFF + kPfRows * 4;            // row sums [128] fp32
+  constexpr int NS = 3;
+  constexpr int A_INSTS = 4;                            // 16 rows per wave, 4 rows per copy
+  constexpr int WCOPIES = 2;                            // two 1 KB tiles per wave
+  constexpr int PER = A_INSTS + WCOPIES;
+  __shared__ __align__(16) uint8_t ring[NS * BYTES];
+  auto swz = [](int r) -> int { return r & 15; };      // 256-byte rows: chunk c at c ^ (r % 16)
+
+  const int lane = threadIdx.x & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6));
+  const int wm = wid & 1, wn = wid >> 1;                // row blocks 2 mb + wm, column blocks 4 wn ..
+  const int col = lane & 15, kq = lane >> 4;
+  const int64_t N = args.N, K = args.K;
+  const int G = int(K / kGroup);
+  const int64_t nblk = N / (16 * kPfwCB);
+  int64_t t_first = 0, ntiles = *args.num_tiles;
+  if (args.fmt_tiles) {
+    t_first = args.fmt_tiles[args.fmt];
+    ntiles = args.fmt_tiles[args.fmt_end] - t_first;
+  }
+  const int64_t items = ntiles * nblk;
+  const int64_t w_scale_off = align256(N * K / 2);
+  const int64_t w_zero_off = w_scale_off + align256(2 * N * int64_t(G));
+  const auto a_rsrc = buffer_rsrc(args.a, args.a_rows * K * 2);
+  const auto r_rsrc = buffer_rsrc(args.a_gsum, args.a_rows * G * 4);
+
+  const ItemRange ir = item_range(items);
+  for (int64_t item = ir.first; item < ir.last; item += ir.step) {
+    const int64_t tile = t_first + item / nblk;
+    const int64_t cb0 = (item % nblk) * kPfwCB;
+    const TileDesc d = args.tiles[tile];
+    const int64_t row_start = d.row_start;
+    const int rows = d.rows;
+    const bool shared = d.expert >= args.num_experts;
+    typedef __attribute__((address_space(1))) const int64_t* gptr_i64;
+    int64_t woff = shared ? 0 : args.woffs ? ((gptr_i64)args.woffs)[d.expert] : int64_t(d.expert) * args.w_stride;
+    woff = int64_t(uint64_t(uint32_t(__builtin_amdgcn_readfirstlane(uint32_t(uint64_t(woff) >> 32)))) << 32 |
+                   uint32_t(__builtin_amdgcn_readfirstlane(uint32_t(woff))));
+    const uint8_t* wbase = (shared ? args.w_shared : args.w) + woff;
+    const int64_t w_bytes = w_scale_off + align256(2 * N * int64_t(G)) + (ASYM ? align256(N * int64_t(G)) : 0);
+    const auto w_rsrc = buffer_rsrc(wbase, w_bytes);
+    auto src_of = [&](int r) -> int64_t {
+      const int64_t pos = row_start + (r < rows ? r : 0);
+      return args.perm ? args.perm[pos] / args.slots_per_token : pos;
+    };
+    // copies: activation rows 16 wid + 4 j + lane / 16 (chunk slot lane % 16), weight
+    // tiles of column blocks 2 wid and 2 wid + 1
+    uint32_t a_off[A_INSTS];
+#pragma unroll
+    for (int j = 0; j < A_INSTS; ++j) {
+      const int r = 16 * wid + 4 * j + lane / 16;
+      const int c = (lane % 16) ^ swz(r);
+      a_off[j] = uint32_t(src_of(r) * K * 2 + c * 16);
+    }
+    uint32_t w_off[WCOPIES];
+#pragma unroll
+    for (int j = 0; j < WCOPIES; ++j) w_off[j] = uint32_t((cb0 + 2 * wid + j) * G * kTileBytes + lane * 16);
+    // wave 0: scales (lanes 0..31, 32 B per block and group) and zero points (lanes
+    // 32..47, 16 B per block and group)
+    uint32_t m_off = 0, m_step = 0;
+    if (lane < 32) {
+      m_off = uint32_t(w_scale_off + (cb0 + lane / 2) * G * 32 + (lane & 1) * 16);
+      m_step = 32;
+    } else if (lane < 48) {
+      m_off = uint32_t(w_zero_off + (cb0 + lane - 32) * G * 16);
+      m_step = 16;
+    }
+    // waves 1 and 2: the row sums of tile rows (wid - 1) * 64 + lane
+    uint32_t r_off = 0;
+    if (wid == 1 || wid == 2) r_off = uint32_t(src_of((wid - 1) * 64 + lane) * G * 4);
+
+    auto slot_of = [&](auto sl) -> uint8_t* { return ring + decltype(sl)::value * BYTES; };
+    auto issue = [&](int g, auto sl) {
+      const uint32_t base = lds_addr(slot_of(sl));
+#pragma unroll
+      for (int j = 0; j < A_INSTS; ++j) copy_to_lds<16>(a_rsrc, base + (16 * wid + 4 * j) * ROWB, a_off[j], uint32_t(g * ROWB));
+#pragma unroll
+      for (int j = 0; j < WCOPIES; ++j)
+        copy_to_lds<16>(w_rsrc, base + W_OFF + (2 * wid + j) * kTileBytes, w_off[j], uint32_t(g * kTileBytes));
+      if (wid == 0 && (lane < 32 || (ASYM && lane < 48)))
+        copy_to_lds<16>(w_rsrc, base + S_OFF, m_off + uint32_t(g) * m_step, 0u);
+      if (wid == 1 || wid == 2) copy_to_lds<4>(r_rsrc, base + R_OFF + (wid - 1) * 256, r_off, uint32_t(g * 4));
+    };
+
+    f32x4_t acc[4][4];
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    auto compute = [&](auto sl, auto nmb_c) {
+      constexpr int NMB = decltype(nmb_c)::value;
+      if constexpr (NMB > 0) {
+        const uint8_t* base = slot_of(sl);
+        const uint16_t* s_sc = reinterpret_cast<const uint16_t*>(base + S_OFF);
+        const uint8_t* s_z = base + Z_OFF;
+        const float* s_rs = reinterpret_cast<const float*>(base + R_OFF);
+        float sc[4], negz[4];
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) {
+          const int cbl = wn * 4 + nb;
+          sc[nb] = f16_bits_to_f32(s_sc[cbl * 16 + col]);
+          negz[nb] = -(magic_offset<Act::BF16>() + (ASYM ? float(s_z[cbl * 16 + col]) : 8.0f));
+        }
+        const uint8_t* wl = base + W_OFF + wn * 4 * kTileBytes + lane * 16;   // word s of block nb at + nb KB + 4 s
+        // group accumulators start at -(magic + z) * (row sum of the group)
+        f32x4_t g[NMB][4];
+#pragma unroll
+        for (int mb = 0; mb < NMB; ++mb) {
+          const f32x4_t xv = *reinterpret_cast<const f32x4_t*>(s_rs + (2 * mb + wm) * 16 + 4 * kq);
+#pragma unroll
+          for (int nb = 0; nb < 4; ++nb) g[mb][nb] = xv * negz[nb];
+        }
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          u32x4_t b[4];
+#pragma unroll
+          for (int nb = 0; nb < 4; ++nb) {
+            const uint32_t wd = *reinterpret_cast<const uint32_t*>(wl + nb * kTileBytes + 4 * s);
+            uint32_t o[4];
+            widen_word_fp<Act::BF16>(wd, o);
+            b[nb] = u32x4_t{o[0], o[1], o[2], o[3]};
+          }
+#pragma unroll
+          for (int mb = 0; mb < NMB; ++mb) {
+            const int r = (2 * mb + wm) * 16 + col;
+            const int c = (4 * s + kq) ^ swz(r);
+            const u32x4_t a = *reinterpret_cast<const u32x4_t*>(base + r * ROWB + c * 16);
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb) g[mb][nb] = mfma16x16x32<Act::BF16>(a, b[nb], g[mb][nb]);
+          }
+        }
+#pragma unroll
+        for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+          for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[mb][nb][i] = fmaf(sc[nb], g[mb][nb][i], acc[mb][nb][i]);
+      }
+    };
+
+    auto sync = [&](int newer) {
+      static_for<NS - 1>([&](auto u) {
+        if (newer == decltype(u)::value) wait_vmcnt<decltype(u)::value * PER>();
+      });
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+    };
+    auto kloop = [&](auto nmb_c) {
+      static_for<NS - 1>([&](auto u) {
+        if (decltype(u)::value < G) issue(decltype(u)::value, u);
+      });
+      sync(std::min(NS - 2, G - 1));
+      for (int g0 = 0; g0 < G; g0 += NS) {
+        bool done = false;
+        static_for<NS>([&](auto u) {
+          constexpr int U = decltype(u)::value;
+          const int g = g0 + U;
+          if (done || g >= G) {
+            done = true;
+            return;
+          }
+          if (g + NS - 1 < G) issue(g + NS - 1, std::integral_constant<int, (U + NS - 1) % NS>{});
+          compute(u, nmb_c);
+          sync(std::max(0, std::min(NS - 2, G - 2 - g)));
+        });
+      }
+    };
+    const int nrb = (rows + 15) / 16;
+    const int nmb = std::min(4, std::max(0, (nrb - wm + 1) / 2));
+    switch (nmb) {
+      case 4: kloop(std::integral_constant<int, 4>{}); break;
+      case 3: kloop(std::integral_constant<int, 3>{}); break;
+      case 2: kloop(std::integral_constant<int, 2>{}); break;
+      case 1: kloop(std::integral_constant<int, 1>{}); break;
+      default: kloop(std::integral_constant<int, 0>{}); break;
+    }
+
+    // epilogue: row (2 mb + wm) * 16 + 4 kq + i, columns of blocks cb0 + 4 wn + nb
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = (2 * mb + wm) * 16 + 4 * kq + i;
+        if (r >= rows) continue;
+        const int64_t pos = row_start + r;
+        if constexpr (KIND == GEMM_PLAIN) {
+#pragma unroll
+          for (int nb = 0; nb < 4; ++nb)
+            static_cast<float*>(args.out)[pos * N + (cb0 + wn * 4 + nb) * 16 + col] = acc[mb][nb][i];
+        } else {
+          const int64_t I = N / 2;
+#pragma unroll
+          for (int p = 0; p < 2; ++p) {
+            const float hv = swiglu(acc[mb][2 * p][i], acc[mb][2 * p + 1][i]);
+            const int64_t hcol = ((cb0 + wn * 4) / 2 + p) * 16 + col;
+            static_cast<uint16_t*>(args.out)[pos * I + hcol] = f32_to_bf16(hv);
+          }
+        }
+      }
+    }
+  }
+}
+
 template <Act A, int KIND>
 static hipError_t launch_pf_kind(const GemmArgs& g, hipStream_t st) {
   const int64_t nblk = g.N / (16 * kPfCB);
@@ -686,6 +907,17 @@ static hipError_t launch_pf_kind(const GemmArgs& g, hipStream_t st) {
   const int64_t cap = (A == Act::I8) ? Q4_PF_GRID_I8 : 256;
   const unsigned grid = unsigned(std::min<int64_t>(items, cap));
   if (g.sg > 1 && (g.asym || g.wbits == 8)) return hipErrorInvalidValue;
+  if constexpr (A == Act::BF16) {
+    if (g.sg <= 1 && g.N % (16 * kPfwCB) == 0) {   // wide tiles: 8 waves, 128 x 256
+      const int64_t wblk = g.N / (16 * kPfwCB);
+      const unsigned wgrid = unsigned(std::min<int64_t>(int64_t(g.max_tiles) * wblk, 256));
+      if (g.asym)
+        hipLaunchKernelGGL((k_gemm_pf16w<KIND, true>), dim3(wgrid), dim3(512), 0, st, g);
+      else
+        hipLaunchKernelGGL((k_gemm_pf16w<KIND, false>), dim3(wgrid), dim3(512), 0, st, g);
+      return hipGetLastError();
+    }
+  }
   if constexpr (A == Act::I8) {
     if (g.wbits == 8) {
       hipLaunchKernelGGL((k_gemm_pf<A, KIND, false, true, 1>), dim3(grid), dim3(256), 0, st, g);
