@@ -908,8 +908,9 @@ static hipError_t launch_pf_kind(const GemmArgs& g, hipStream_t st) {
   const unsigned grid = unsigned(std::min<int64_t>(items, cap));
   if (g.sg > 1 && (g.asym || g.wbits == 8)) return hipErrorInvalidValue;
   if constexpr (A == Act::BF16) {
-    if (g.sg <= 1 && g.N % (16 * kPfwCB) == 0) {   // wide tiles: 8 waves, 128 x 256
-      const int64_t wblk = g.N / (16 * kPfwCB);
+    // wide tiles (8 waves, 128 x 256) when they still give every CU a work item
+    const int64_t wblk = g.N / (16 * kPfwCB);
+    if (g.sg <= 1 && g.N % (16 * kPfwCB) == 0 && int64_t(g.max_tiles) * wblk >= 256) {
       const unsigned wgrid = unsigned(std::min<int64_t>(int64_t(g.max_tiles) * wblk, 256));
       if (g.asym)
         hipLaunchKernelGGL((k_gemm_pf16w<KIND, true>), dim3(wgrid), dim3(512), 0, st, g);

@@ -176,3 +176,22 @@ def test_moe8_w4a8(lib, moe8, t):
     rows = np.arange(t) if t <= 64 else np.sort(np.random.default_rng(4).choice(t, 48, replace=False))
     ref = ffn.moe_w4a8(_np(x)[rows], oe, ids[rows], w[rows])
     assert ffn.max_rel_l2(_np(out)[rows], ref) <= TOL_W4A8
+
+
+@pytest.mark.parametrize("asym", [False, True], ids=["sym", "asym"])
+def test_wide_bf16_prefill_tiles(lib, asym):
+    """Enough 128-row tiles x 256-column blocks to take the wide bf16 prefill kernel
+    (8 waves, 128 x 256 outputs) for both GEMMs: 8 experts, hidden 512, inter 1024,
+    top-2, T = 2048; a seeded sample of tokens against the oracle."""
+    E, H, I, k, t = 8, 512, 1024, 2, 2048
+    make = random_expert_maker(107, H, I, sigma=0.03)
+    layer = build_gpu_layer(lib, make, E, H, I, k, asym=asym)
+    oe = OracleExperts(make, asym)
+    x = synth.normal(synth.stream_key(108, t), (t, H), 1.0).to(torch.bfloat16)
+    rng = np.random.default_rng(109)
+    ids = np.stack([rng.permutation(E)[:k] for _ in range(t)]).astype(np.int64)
+    w = rng.dirichlet(np.ones(k), size=t)
+    out = _forward(lib, layer, x, ids, w, 0)
+    rows = np.sort(rng.choice(t, 40, replace=False))
+    ref = ffn.moe_w4a16(_np(x)[rows], oe, ids[rows], w[rows])
+    assert ffn.max_rel_l2(_np(out)[rows], ref) <= TOL_W4A16
