@@ -684,17 +684,20 @@ __global__ void __launch_bounds__(256, (A == Act::I8) ? 2 : 1) k_gemm_pf(GemmArg
 // of a group outermost: only one K step's widened weights (16 registers) and the
 // per-tile group accumulators are live, which keeps the kernel within 256 registers so
 // two waves share each SIMD, and every activation byte copied to LDS feeds 256 columns.
-// One scale entry per tile (groups of 128 / 256).
+// SG scale entries per tile (groups of 128 / SG): a scale group's accumulators are
+// rescaled after its own K steps, so the register count does not depend on SG.
 constexpr int kPfwCB = 16;
 
-template <int KIND, bool ASYM>
+template <int KIND, bool ASYM, int SG>
 __global__ void __launch_bounds__(512) k_gemm_pf16w(GemmArgs args) {
+  static_assert(SG == 1 || (!ASYM && (SG == 2 || SG == 4)), "scale groups: symmetric weights only");
+  constexpr int SPS = 4 / SG;                           // 32-element K steps per scale group
   constexpr int ROWB = kGroup * 2;                      // bf16 bytes of one row of a group
   constexpr int W_OFF = kPfRows * ROWB;                 // 32 KB of activations
   constexpr int S_OFF = W_OFF + kPfwCB * kTileBytes;    // 16 KB of weight tiles
-  constexpr int Z_OFF = S_OFF + kPfwCB * 32;            // scales [16][16] fp16
-  constexpr int R_OFF = Z_OFF + kPfwCB * 16;            // zero points [16][16] u8
-  constexpr int BYTES = R_OFF + kPfRows * 4;            // row sums [128] fp32
+  constexpr int Z_OFF = S_OFF + kPfwCB * 32 * SG;       // scales [16][16][SG] fp16
+  constexpr int R_OFF = Z_OFF + (SG == 1 ? kPfwCB * 16 : 0);   // zero points [16][16] u8
+  constexpr int BYTES = R_OFF + kPfRows * 4 * SG;       // row sums [SG][128] fp32
   constexpr int NS = 3;
   constexpr int A_INSTS = 4;                            // 16 rows per wave, 4 rows per copy
   constexpr int WCOPIES = 2;                            // two 1 KB tiles per wave
@@ -718,7 +721,7 @@ __global__ void __launch_bounds__(512) k_gemm_pf16w(GemmArgs args) {
   const int64_t w_scale_off = align256(N * K / 2);
   const int64_t w_zero_off = w_scale_off + align256(2 * N * int64_t(G));
   const auto a_rsrc = buffer_rsrc(args.a, args.a_rows * K * 2);
-  const auto r_rsrc = buffer_rsrc(args.a_gsum, args.a_rows * G * 4);
+  const auto r_rsrc = buffer_rsrc(args.a_gsum, args.a_rows * G * SG * 4);
 
   const ItemRange ir = item_range(items);
   for (int64_t item = ir.first; item < ir.last; item += ir.step) {
@@ -733,7 +736,7 @@ __global__ void __launch_bounds__(512) k_gemm_pf16w(GemmArgs args) {
     woff = int64_t(uint64_t(uint32_t(__builtin_amdgcn_readfirstlane(uint32_t(uint64_t(woff) >> 32)))) << 32 |
                    uint32_t(__builtin_amdgcn_readfirstlane(uint32_t(woff))));
     const uint8_t* wbase = (shared ? args.w_shared : args.w) + woff;
-    const int64_t w_bytes = w_scale_off + align256(2 * N * int64_t(G)) + (ASYM ? align256(N * int64_t(G)) : 0);
+    const int64_t w_bytes = w_scale_off + align256(2 * N * int64_t(G) * SG) + (ASYM ? align256(N * int64_t(G)) : 0);
     const auto w_rsrc = buffer_rsrc(wbase, w_bytes);
     auto src_of = [&](int r) -> int64_t {
       const int64_t pos = row_start + (r < rows ? r : 0);
@@ -751,19 +754,21 @@ __global__ void __launch_bounds__(512) k_gemm_pf16w(GemmArgs args) {
     uint32_t w_off[WCOPIES];
 #pragma unroll
     for (int j = 0; j < WCOPIES; ++j) w_off[j] = uint32_t((cb0 + 2 * wid + j) * G * kTileBytes + lane * 16);
-    // wave 0: scales (lanes 0..31, 32 B per block and group) and zero points (lanes
-    // 32..47, 16 B per block and group)
+    // scales, 32 SG bytes per block and group: wave 0 (16 B per lane; with four entries
+    // per tile waves 0 and 3 copy 1 KB each); zero points: wave 0 lanes 32..47
+    const int sidx = lane + (wid == 3 ? 64 : 0);
+    const bool scale_lane = (wid == 0 && sidx < 32 * SG) || (SG == 4 && wid == 3);
     uint32_t m_off = 0, m_step = 0;
-    if (lane < 32) {
-      m_off = uint32_t(w_scale_off + (cb0 + lane / 2) * G * 32 + (lane & 1) * 16);
-      m_step = 32;
-    } else if (lane < 48) {
+    if (scale_lane) {
+      m_off = uint32_t(w_scale_off + (cb0 + sidx / (2 * SG)) * G * 32 * SG + (sidx % (2 * SG)) * 16);
+      m_step = 32 * SG;
+    } else if (SG == 1 && wid == 0 && lane >= 32 && lane < 48) {
       m_off = uint32_t(w_zero_off + (cb0 + lane - 32) * G * 16);
       m_step = 16;
     }
-    // waves 1 and 2: the row sums of tile rows (wid - 1) * 64 + lane
+    // waves 1 and 2: the row sums (one per scale group) of tile rows (wid - 1) * 64 + lane
     uint32_t r_off = 0;
-    if (wid == 1 || wid == 2) r_off = uint32_t(src_of((wid - 1) * 64 + lane) * G * 4);
+    if (wid == 1 || wid == 2) r_off = uint32_t(src_of((wid - 1) * 64 + lane) * G * SG * 4);
 
     auto slot_of = [&](auto sl) -> uint8_t* { return ring + decltype(sl)::value * BYTES; };
     auto issue = [&](int g, auto sl) {
@@ -773,9 +778,13 @@ __global__ void __launch_bounds__(512) k_gemm_pf16w(GemmArgs args) {
 #pragma unroll
       for (int j = 0; j < WCOPIES; ++j)
         copy_to_lds<16>(w_rsrc, base + W_OFF + (2 * wid + j) * kTileBytes, w_off[j], uint32_t(g * kTileBytes));
-      if (wid == 0 && (lane < 32 || (ASYM && lane < 48)))
-        copy_to_lds<16>(w_rsrc, base + S_OFF, m_off + uint32_t(g) * m_step, 0u);
-      if (wid == 1 || wid == 2) copy_to_lds<4>(r_rsrc, base + R_OFF + (wid - 1) * 256, r_off, uint32_t(g * 4));
+      if (scale_lane || (ASYM && wid == 0 && lane < 48))
+        copy_to_lds<16>(w_rsrc, base + S_OFF + (wid == 3 ? 1024 : 0), m_off + uint32_t(g) * m_step, 0u);
+      if (wid == 1 || wid == 2) {
+#pragma unroll
+        for (int j = 0; j < SG; ++j)
+          copy_to_lds<4>(r_rsrc, base + R_OFF + j * 512 + (wid - 1) * 256, r_off + 4 * j, uint32_t(g * 4 * SG));
+      }
     };
 
     f32x4_t acc[4][4];
@@ -791,24 +800,26 @@ __global__ void __launch_bounds__(512) k_gemm_pf16w(GemmArgs args) {
         const uint16_t* s_sc = reinterpret_cast<const uint16_t*>(base + S_OFF);
         const uint8_t* s_z = base + Z_OFF;
         const float* s_rs = reinterpret_cast<const float*>(base + R_OFF);
-        float sc[4], negz[4];
+        // scale j of column block 4 wn + nb (read when scale group j is rescaled)
+        auto scale = [&](int nb, int j) -> float { return f16_bits_to_f32(s_sc[((wn * 4 + nb) * 16 + col) * SG + j]); };
+        float negz[4];
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb) {
-          const int cbl = wn * 4 + nb;
-          sc[nb] = f16_bits_to_f32(s_sc[cbl * 16 + col]);
-          negz[nb] = -(magic_offset<Act::BF16>() + (ASYM ? float(s_z[cbl * 16 + col]) : 8.0f));
-        }
+        for (int nb = 0; nb < 4; ++nb)
+          negz[nb] = -(magic_offset<Act::BF16>() + (ASYM ? float(s_z[(wn * 4 + nb) * 16 + col]) : 8.0f));
         const uint8_t* wl = base + W_OFF + wn * 4 * kTileBytes + lane * 16;   // word s of block nb at + nb KB + 4 s
-        // group accumulators start at -(magic + z) * (row sum of the group)
         f32x4_t g[NMB][4];
 #pragma unroll
-        for (int mb = 0; mb < NMB; ++mb) {
-          const f32x4_t xv = *reinterpret_cast<const f32x4_t*>(s_rs + (2 * mb + wm) * 16 + 4 * kq);
-#pragma unroll
-          for (int nb = 0; nb < 4; ++nb) g[mb][nb] = xv * negz[nb];
-        }
-#pragma unroll
         for (int s = 0; s < 4; ++s) {
+          if (s % SPS == 0) {
+            // a scale group's accumulators start at -(magic + z) * (its row sum)
+#pragma unroll
+            for (int mb = 0; mb < NMB; ++mb) {
+              const f32x4_t xv =
+                  *reinterpret_cast<const f32x4_t*>(s_rs + (s / SPS) * 128 + (2 * mb + wm) * 16 + 4 * kq);
+#pragma unroll
+              for (int nb = 0; nb < 4; ++nb) g[mb][nb] = xv * negz[nb];
+            }
+          }
           u32x4_t b[4];
 #pragma unroll
           for (int nb = 0; nb < 4; ++nb) {
@@ -825,13 +836,25 @@ __global__ void __launch_bounds__(512) k_gemm_pf16w(GemmArgs args) {
 #pragma unroll
             for (int nb = 0; nb < 4; ++nb) g[mb][nb] = mfma16x16x32<Act::BF16>(a, b[nb], g[mb][nb]);
           }
+          if (s % SPS == SPS - 1) {   // the scale group is complete: rescale into the totals
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb) {
+              const float sc = scale(nb, s / SPS);
+#pragma unroll
+              for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[mb][nb][i] = fmaf(sc, g[mb][nb][i], acc[mb][nb][i]);
+            }
+            // make the rescale happen here: otherwise the compiler sinks it past the
+            // following scale groups and keeps all of their accumulators live
+            if constexpr (SG > 1) {
+#pragma unroll
+              for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+                for (int nb = 0; nb < 4; ++nb) asm volatile("" : "+v"(acc[mb][nb]));
+            }
+          }
         }
-#pragma unroll
-        for (int mb = 0; mb < NMB; ++mb)
-#pragma unroll
-          for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) acc[mb][nb][i] = fmaf(sc[nb], g[mb][nb][i], acc[mb][nb][i]);
       }
     };
 
@@ -910,12 +933,16 @@ static hipError_t launch_pf_kind(const GemmArgs& g, hipStream_t st) {
   if constexpr (A == Act::BF16) {
     // wide tiles (8 waves, 128 x 256) when they still give every CU a work item
     const int64_t wblk = g.N / (16 * kPfwCB);
-    if (g.sg <= 1 && g.N % (16 * kPfwCB) == 0 && int64_t(g.max_tiles) * wblk >= 256) {
+    if (g.N % (16 * kPfwCB) == 0 && int64_t(g.max_tiles) * wblk >= 256) {
       const unsigned wgrid = unsigned(std::min<int64_t>(int64_t(g.max_tiles) * wblk, 256));
-      if (g.asym)
-        hipLaunchKernelGGL((k_gemm_pf16w<KIND, true>), dim3(wgrid), dim3(512), 0, st, g);
+      if (g.sg == 4)
+        hipLaunchKernelGGL((k_gemm_pf16w<KIND, false, 4>), dim3(wgrid), dim3(512), 0, st, g);
+      else if (g.sg == 2)
+        hipLaunchKernelGGL((k_gemm_pf16w<KIND, false, 2>), dim3(wgrid), dim3(512), 0, st, g);
+      else if (g.asym)
+        hipLaunchKernelGGL((k_gemm_pf16w<KIND, true, 1>), dim3(wgrid), dim3(512), 0, st, g);
       else
-        hipLaunchKernelGGL((k_gemm_pf16w<KIND, false>), dim3(wgrid), dim3(512), 0, st, g);
+        hipLaunchKernelGGL((k_gemm_pf16w<KIND, false, 1>), dim3(wgrid), dim3(512), 0, st, g);
       return hipGetLastError();
     }
   }

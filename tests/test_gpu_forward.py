@@ -181,9 +181,10 @@ def test_moe8_w4a8(lib, moe8, t):
 @pytest.mark.parametrize("asym", [False, True], ids=["sym", "asym"])
 def test_wide_bf16_prefill_tiles(lib, asym):
     """Enough 128-row tiles x 256-column blocks to take the wide bf16 prefill kernel
-    (8 waves, 128 x 256 outputs) for both GEMMs: 8 experts, hidden 512, inter 1024,
-    top-2, T = 2048; a seeded sample of tokens against the oracle."""
-    E, H, I, k, t = 8, 512, 1024, 2, 2048
+    (8 waves, 128 x 256 outputs) for both GEMMs (41 tiles x 8 column blocks each): 8
+    experts, hidden 2048, inter 1024, top-2, T = 2048; a seeded sample of tokens against
+    the oracle."""
+    E, H, I, k, t = 8, 2048, 1024, 2, 2048
     make = random_expert_maker(107, H, I, sigma=0.03)
     layer = build_gpu_layer(lib, make, E, H, I, k, asym=asym)
     oe = OracleExperts(make, asym)

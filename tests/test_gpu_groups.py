@@ -241,3 +241,24 @@ def test_grouped_hidden_not_a_multiple_of_256(lib):
             torch.cuda.synchronize()
             fn = ffn.moe_w4a16 if mode == 0 else ffn.moe_w4a8
             assert ffn.max_rel_l2(_np(out), fn(_np(x), oe, ids, w)) <= TOL[mode], (t, mode)
+
+
+def test_wide_bf16_prefill_with_every_group_size(lib):
+    """W4A16 prefill with 41 tiles x 8 column blocks per GEMM takes the wide bf16 kernel
+    (128 x 256 outputs) for both GEMMs, once per weight format: experts with groups of 32
+    and 64 rescale after every one or two 32-element K steps, groups of 128 and 256 once
+    per tile.  8 experts, hidden 2048, inter 1024, top-2, T = 2048; 64 sampled tokens
+    that cover every expert, against the oracle."""
+    E, H, I, k, t = 8, 2048, 1024, 2, 2048
+    groups = [32, 64, 128, 256, 64, 32, 256, 128]
+    make = random_expert_maker(111, H, I, sigma=0.03)
+    layer = _layer(lib, make, E, H, I, k, False, groups)
+    oe = GroupedExperts(make, groups)
+    x, ids, w = _case(t, E, k, H, 112)
+    out = lib.moe_int4_ffn_forward(layer, x.cuda(), torch.as_tensor(ids, dtype=torch.int32).cuda(),
+                                   torch.as_tensor(w, dtype=torch.float32).cuda(), mode=0)
+    torch.cuda.synchronize()
+    rows = np.sort(np.random.default_rng(113).choice(t, 64, replace=False))
+    assert set(ids[rows].ravel()) == set(range(E))
+    ref = ffn.moe_w4a16(_np(x)[rows], oe, ids[rows], w[rows])
+    assert ffn.max_rel_l2(_np(out)[rows], ref) <= TOL[0]
