@@ -8,21 +8,26 @@
 
 namespace q4 {
 
-// Partial logits over one K slice: a (16 TB)-token x (16 EB)-expert tile per wave,
-// fp32 MFMA 16x16x4.  Lane (m = lane % 16, kq = lane / 16) feeds x[t0 + 16 i + m][k]
-// and W[e0 + 16 j + m][k] for k = k0 + 4 kq + s to MFMA s of each 16-wide K step; U
-// steps of loads are issued before their MFMAs.  Small batches use 16 x 16 tiles and
-// many K slices; large batches use 32 x 64 or 64 x 64 tiles (each loaded x value
-// feeds four expert blocks, each W value two or four token blocks).
-template <int TB, int EB, int U>
-__global__ void __launch_bounds__(64) k_router_partial(const uint16_t* __restrict__ x, const float* __restrict__ wr,
-                                                       int64_t t, int64_t h, int32_t e, int64_t kslice,
-                                                       float* __restrict__ partial) {
-  const int lane = threadIdx.x;
+// Partial logits over K slices: a (16 TB)-token x (16 EB)-expert tile per wave, fp32
+// MFMA 16x16x4.  Lane (m = lane % 16, kq = lane / 16) feeds x[t0 + 16 i + m][k] and
+// W[e0 + 16 j + m][k] for k = k0 + 4 kq + s to MFMA s of each 16-wide K step; U steps
+// of loads are issued before their MFMAs.  Small batches use 16 x 16 tiles and many K
+// slices, with RED the workgroup's waves (up to 16) on consecutive slices whose sums are
+// added in LDS (in wave order) so that one partial per workgroup is written; large
+// batches use 32 x 64 or 64 x 64 tiles (each loaded x value feeds four expert blocks,
+// each W value two or four token blocks), one wave per slice.
+template <int TB, int EB, int U, bool RED>
+__global__ void __launch_bounds__(RED ? 1024 : 64) k_router_partial(const uint16_t* __restrict__ x,
+                                                                   const float* __restrict__ wr, int64_t t, int64_t h,
+                                                                   int32_t e, int64_t kslice,
+                                                                   float* __restrict__ partial) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6));
+  const int kw = RED ? int(blockDim.x >> 6) : 1;
   const int m = lane & 15, kq = lane >> 4;
   const int64_t e0 = int64_t(blockIdx.x) * 16 * EB, t0 = int64_t(blockIdx.y) * 16 * TB;
-  const int64_t ks = blockIdx.z;
-  const int64_t kb = ks * kslice, ke = std::min<int64_t>(h, kb + kslice);
+  const int64_t ks = int64_t(blockIdx.z) * kw + wave;
+  const int64_t kb = std::min<int64_t>(h, ks * kslice), ke = std::min<int64_t>(h, kb + kslice);
   const uint16_t* xr[TB];
   const float* wrow[EB];
   bool tv[TB], ev[EB];
@@ -76,7 +81,24 @@ __global__ void __launch_bounds__(64) k_router_partial(const uint16_t* __restric
           }
     }
   }
+  if constexpr (RED) {
+    __shared__ f32x4_t red[15][TB * EB][64];
+    if (wave > 0) {
+#pragma unroll
+      for (int i = 0; i < TB; ++i)
+#pragma unroll
+        for (int j = 0; j < EB; ++j) red[wave - 1][i * EB + j][lane] = acc[i][j];
+    }
+    __syncthreads();
+    if (wave > 0) return;
+    for (int w = 1; w < kw; ++w)
+#pragma unroll
+      for (int i = 0; i < TB; ++i)
+#pragma unroll
+        for (int j = 0; j < EB; ++j) acc[i][j] += red[w - 1][i * EB + j][lane];
+  }
   // C layout: lane holds tokens t0 + 16 i + 4 kq + r, expert e0 + 16 j + m
+  const int64_t slot = blockIdx.z;
 #pragma unroll
   for (int i = 0; i < TB; ++i)
 #pragma unroll
@@ -84,11 +106,17 @@ __global__ void __launch_bounds__(64) k_router_partial(const uint16_t* __restric
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int64_t tt = t0 + 16 * i + 4 * kq + r;
-        if (tt < t && ev[j]) partial[(ks * t + tt) * e + e0 + 16 * j + m] = acc[i][j][r];
+        if (tt < t && ev[j]) partial[(slot * t + tt) * e + e0 + 16 * j + m] = acc[i][j][r];
       }
 }
 
 constexpr int kMaxSlices = 32;
+
+// workgroups of the small-batch logit kernel to aim for (one per CU); overridable at
+// build time
+#ifndef Q4_ROUTE_WGS
+#define Q4_ROUTE_WGS 256
+#endif
 
 // Unsigned image of a float that orders like the float (non-NaN inputs).
 Q4_DEVICE uint32_t ordered_bits(float f) {
@@ -128,7 +156,7 @@ Q4_DEVICE uint64_t wave_max_u64(uint64_t x) {
 // the renormalised softmax weights of the selected experts.  Lane l holds experts
 // l + 64 i (i < NI, NI = ceil(e / 64)); the round winners go through LDS so that ids
 // and weights are written once, coalesced.
-template <int NI>
+template <int NI, int MS>
 __global__ void __launch_bounds__(64) k_topk(const float* __restrict__ partial, int32_t kslices,
                                              const float* __restrict__ bias, int64_t t, int32_t e,
                                              int32_t k, float* __restrict__ logits, int32_t* __restrict__ ids,
@@ -143,15 +171,16 @@ __global__ void __launch_bounds__(64) k_topk(const float* __restrict__ partial, 
   // slice sums in slice order (0 + p0 = p0 exactly); addresses clamped into range
   int ks = 0;
   if constexpr (NI <= 4) {
-    // every partial load in flight at once (clamped slice index; unused slices add 0)
-    float p[kMaxSlices][NI];
+    // every partial load in flight at once (MS >= kslices; clamped slice index, unused
+    // slices add 0)
+    float p[MS][NI];
 #pragma unroll
-    for (int u = 0; u < kMaxSlices; ++u)
+    for (int u = 0; u < MS; ++u)
 #pragma unroll
       for (int i = 0; i < NI; ++i)
         p[u][i] = partial[(int64_t(min(u, kslices - 1)) * t + tok) * e + min(lane + 64 * i, e - 1)];
 #pragma unroll
-    for (int u = 0; u < kMaxSlices; ++u)
+    for (int u = 0; u < MS; ++u)
 #pragma unroll
       for (int i = 0; i < NI; ++i) v[i] += u < kslices ? p[u][i] : 0.f;
     ks = kslices;
@@ -228,6 +257,27 @@ int route_kslices(int64_t t, int64_t h, int32_t e) {
   return int(ks);
 }
 
+// One wave per token; up to 8 or 16 partial sums are all loaded by variants sized for them.
+template <int NI>
+static hipError_t launch_topk(const float* partial, int nparts, const float* bias, int64_t t, int32_t e, int32_t k,
+                              float* logits, int32_t* ids, float* w, hipStream_t st) {
+  if constexpr (NI <= 4) {
+    if (nparts <= 8) {
+      hipLaunchKernelGGL((k_topk<NI, 8>), dim3(unsigned(t)), dim3(64), 0, st, partial, nparts, bias, t, e, k, logits,
+                         ids, w);
+      return hipGetLastError();
+    }
+    if (nparts <= 16) {
+      hipLaunchKernelGGL((k_topk<NI, 16>), dim3(unsigned(t)), dim3(64), 0, st, partial, nparts, bias, t, e, k, logits,
+                         ids, w);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((k_topk<NI, kMaxSlices>), dim3(unsigned(t)), dim3(64), 0, st, partial, nparts, bias, t, e, k,
+                     logits, ids, w);
+  return hipGetLastError();
+}
+
 hipError_t launch_route(const uint16_t* x, const float* wr, const float* bias, int64_t t, int64_t h,
                         int32_t e, int32_t k, float* logits, int32_t* ids, float* w, float* partial,
                         hipStream_t st) {
@@ -235,28 +285,29 @@ hipError_t launch_route(const uint16_t* x, const float* wr, const float* bias, i
   int64_t kslice = (h + ks - 1) / ks;
   kslice = (kslice + 15) / 16 * 16;
   const int kused = int((h + kslice - 1) / kslice);
+  int nparts = kused;   // partial sums written (one per K slice, or per workgroup of slices)
   if (route_huge_tiles(t, e)) {
     dim3 grid(unsigned((e + 63) / 64), unsigned((t + 63) / 64), unsigned(kused));
-    hipLaunchKernelGGL((k_router_partial<4, 4, 2>), grid, dim3(64), 0, st, x, wr, t, h, e, kslice, partial);
+    hipLaunchKernelGGL((k_router_partial<4, 4, 2, false>), grid, dim3(64), 0, st, x, wr, t, h, e, kslice, partial);
   } else if (route_big_tiles(t, e)) {
     dim3 grid(unsigned((e + 63) / 64), unsigned((t + 31) / 32), unsigned(kused));
-    hipLaunchKernelGGL((k_router_partial<2, 4, 4>), grid, dim3(64), 0, st, x, wr, t, h, e, kslice, partial);
+    hipLaunchKernelGGL((k_router_partial<2, 4, 4, false>), grid, dim3(64), 0, st, x, wr, t, h, e, kslice, partial);
   } else {
-    dim3 grid(unsigned((e + 15) / 16), unsigned((t + 15) / 16), unsigned(kused));
-    hipLaunchKernelGGL((k_router_partial<1, 1, 16>), grid, dim3(64), 0, st, x, wr, t, h, e, kslice, partial);
+    // about one workgroup per CU: the slices of a tile are shared out over
+    // Q4_ROUTE_WGS / tiles workgroups (at least one), at most 16 waves each
+    const int64_t tiles = int64_t((e + 15) / 16) * ((t + 15) / 16);
+    const int want = int(std::max<int64_t>(1, std::min<int64_t>(kused, Q4_ROUTE_WGS / tiles)));
+    const int kw = std::min(16, (kused + want - 1) / want);
+    nparts = (kused + kw - 1) / kw;
+    dim3 grid(unsigned((e + 15) / 16), unsigned((t + 15) / 16), unsigned(nparts));
+    hipLaunchKernelGGL((k_router_partial<1, 1, 16, true>), grid, dim3(64 * kw), 0, st, x, wr, t, h, e, kslice,
+                       partial);
   }
-  const dim3 g = dim3(unsigned(t)), b = dim3(64);
-  if (e <= 64)
-    hipLaunchKernelGGL(k_topk<1>, g, b, 0, st, partial, kused, bias, t, e, k, logits, ids, w);
-  else if (e <= 128)
-    hipLaunchKernelGGL(k_topk<2>, g, b, 0, st, partial, kused, bias, t, e, k, logits, ids, w);
-  else if (e <= 256)
-    hipLaunchKernelGGL(k_topk<4>, g, b, 0, st, partial, kused, bias, t, e, k, logits, ids, w);
-  else if (e <= 512)
-    hipLaunchKernelGGL(k_topk<8>, g, b, 0, st, partial, kused, bias, t, e, k, logits, ids, w);
-  else
-    hipLaunchKernelGGL(k_topk<16>, g, b, 0, st, partial, kused, bias, t, e, k, logits, ids, w);
-  return hipGetLastError();
+  if (e <= 64) return launch_topk<1>(partial, nparts, bias, t, e, k, logits, ids, w, st);
+  if (e <= 128) return launch_topk<2>(partial, nparts, bias, t, e, k, logits, ids, w, st);
+  if (e <= 256) return launch_topk<4>(partial, nparts, bias, t, e, k, logits, ids, w, st);
+  if (e <= 512) return launch_topk<8>(partial, nparts, bias, t, e, k, logits, ids, w, st);
+  return launch_topk<16>(partial, nparts, bias, t, e, k, logits, ids, w, st);
 }
 
 }  // namespace q4
