@@ -97,6 +97,20 @@ struct RowInfo {
   bool valid;
 };
 
+// Copies n16 16-byte chunks from global memory to LDS with the workgroup's 256 threads;
+// each thread issues up to 4 loads before its stores, so they share one memory latency.
+Q4_DEVICE void stage16_to_lds(uint4* __restrict__ dst, const uint4* __restrict__ src, int64_t n16) {
+  constexpr int U = 4;
+  for (int64_t i0 = threadIdx.x; i0 < n16; i0 += 256 * U) {
+    uint4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = i0 + 256 * u < n16 ? src[i0 + 256 * u] : make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (i0 + 256 * u < n16) dst[i0 + 256 * u] = v[u];
+  }
+}
+
 // Grouped INT4 GEMM.  Template parameters:
 //  MB  16-row blocks per tile (rows of one expert, gathered through perm),
 //  KW  waves of the workgroup that split the K groups (reduced through LDS),
@@ -162,18 +176,6 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs args) {
     // the rest of the item, for SG scale entries per tile
     auto body = [&](auto sgc) {
     constexpr int SG = decltype(sgc)::value;
-    // stage the workgroup's scales / zero points (contiguous in the device layout)
-    if constexpr (SG == 1) {
-      const uint4* src = reinterpret_cast<const uint4*>(wbase + w_scale_off + cb0 * G * 32);
-      const int64_t n16 = int64_t(kCBWG) * G * 2;
-      for (int64_t i = threadIdx.x; i < n16; i += 256) reinterpret_cast<uint4*>(s_scale)[i] = src[i];
-      if constexpr (ASYM) {
-        const uint8_t* zsrc = wbase + w_zero_off + cb0 * G * 16;
-        for (int64_t i = threadIdx.x; i < int64_t(kCBWG) * G * 16; i += 256) s_zero[i] = zsrc[i];
-      }
-    }
-    __syncthreads();
-
     // Rows past the tile end read the tile's first row: every MFMA output row depends on
     // its own A row only, and those rows are never stored, so no zero fill is needed.
     RowInfo ri[MB];
@@ -400,6 +402,16 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs args) {
         }
       }
     };
+
+    // stage the workgroup's scales / zero points (contiguous in the device layout)
+    if constexpr (SG == 1) {
+      stage16_to_lds(reinterpret_cast<uint4*>(s_scale),
+                     reinterpret_cast<const uint4*>(wbase + w_scale_off + cb0 * G * 32), int64_t(kCBWG) * G * 2);
+      if constexpr (ASYM)
+        stage16_to_lds(reinterpret_cast<uint4*>(s_zero), reinterpret_cast<const uint4*>(wbase + w_zero_off + cb0 * G * 16),
+                       int64_t(kCBWG) * G);
+    }
+    __syncthreads();
 
     // D-stage register pipeline over this wave's groups: while group g is computed the
     // loads of groups g + 1 .. g + D - 1 are in flight
