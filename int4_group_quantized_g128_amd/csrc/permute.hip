@@ -223,8 +223,11 @@ hipError_t launch_permute(const int32_t* ids, int64_t t, int32_t k, int32_t e, i
                           int32_t* fmt_tiles) {
   const int ee = e + shared;
   const size_t budget = 96 * 1024;
+  // one wave per 64 slots (at most 16, and as many as the LDS budget allows): the
+  // per-expert loops of pass 2 walk every wave's counts, so idle waves only cost time
+  const int64_t P = t * (k + shared);
   int nwaves = int(std::min<size_t>(16, (budget / sizeof(int32_t) - (5 * ee + 1)) / ee));
-  nwaves = std::max(1, nwaves);
+  nwaves = int(std::max<int64_t>(1, std::min<int64_t>(nwaves, (P + 63) / 64)));
   const size_t lds = (size_t(nwaves) * ee + 5 * ee + 1) * sizeof(int32_t);
   hipLaunchKernelGGL(k_permute, dim3(1), dim3(kPermThreads), lds, st, ids, t, k, e, shared, nwaves, counts,
                      offsets, perm, inv, tiles, num_tiles, tile_rows, ebits, egroups, fmt_tiles);
