@@ -820,21 +820,35 @@ __global__ void __launch_bounds__(512) k_gemm_pf16w(GemmArgs args) {
               for (int nb = 0; nb < 4; ++nb) g[mb][nb] = xv * negz[nb];
             }
           }
-          u32x4_t b[4];
-#pragma unroll
-          for (int nb = 0; nb < 4; ++nb) {
-            const uint32_t wd = *reinterpret_cast<const uint32_t*>(wl + nb * kTileBytes + 4 * s);
-            uint32_t o[4];
-            widen_word_fp<Act::BF16>(wd, o);
-            b[nb] = u32x4_t{o[0], o[1], o[2], o[3]};
-          }
+          // the step's activation fragments, then the weight blocks one at a time: block
+          // nb + 1 is widened (VALU) while block nb's MFMAs run
+          u32x4_t a[NMB];
 #pragma unroll
           for (int mb = 0; mb < NMB; ++mb) {
             const int r = (2 * mb + wm) * 16 + col;
             const int c = (4 * s + kq) ^ swz(r);
-            const u32x4_t a = *reinterpret_cast<const u32x4_t*>(base + r * ROWB + c * 16);
+            a[mb] = *reinterpret_cast<const u32x4_t*>(base + r * ROWB + c * 16);
+          }
+          auto widen_block = [&](int nb) -> u32x4_t {
+            const uint32_t wd = *reinterpret_cast<const uint32_t*>(wl + nb * kTileBytes + 4 * s);
+            uint32_t o[4];
+            widen_word_fp<Act::BF16>(wd, o);
+            return u32x4_t{o[0], o[1], o[2], o[3]};
+          };
+          u32x4_t bc = widen_block(0);
 #pragma unroll
-            for (int nb = 0; nb < 4; ++nb) g[mb][nb] = mfma16x16x32<Act::BF16>(a, b[nb], g[mb][nb]);
+          for (int nb = 0; nb < 4; ++nb) {
+            const u32x4_t bn = nb < 3 ? widen_block(nb + 1) : bc;
+#pragma unroll
+            for (int mb = 0; mb < NMB; ++mb) g[mb][nb] = mfma16x16x32<Act::BF16>(a[mb], bc, g[mb][nb]);
+            // issue order: each MFMA followed by two VALU instructions (the next block's
+            // widening), so the vector ALU works while the matrix core is busy
+#pragma unroll
+            for (int mb = 0; mb < NMB; ++mb) {
+              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+              __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+            }
+            bc = bn;
           }
           if (s % SPS == SPS - 1) {   // the scale group is complete: rescale into the totals
 #pragma unroll
