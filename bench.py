@@ -199,14 +199,18 @@ class LoraWorkload:
         if rc:
             raise L.Q4Error("moe_lora_ffn_forward", rc)
 
-    def summary(self, sec):
+    def summary(self, sec, cold_sec=None):
         h, i, r, k = self.cfg["hidden"], self.cfg["inter"], self.cfg["rank"], self.cfg["top_k"]
         flops = 2.0 * self.t * 3 * h * i + 2.0 * self.t * k * 3 * r * (h + i)
-        return {"tokens": self.t, "tokens_per_s": self.t / sec, "ms_per_step": sec * 1e3,
-                "weight_bytes": self.layer.weight_bytes(),
-                "effective_weight_GBps": self.layer.weight_bytes() / sec / 1e9,
-                "hbm_frac": self.layer.weight_bytes() / sec / 1e9 / HBM_PEAK_GBS,
-                "mfma_frac": flops / sec / 1e12 / BF16_PEAK_TFLOPS}
+        res = {"tokens": self.t, "tokens_per_s": self.t / sec, "ms_per_step": sec * 1e3,
+               "weight_bytes": self.layer.weight_bytes(),
+               "effective_weight_GBps": self.layer.weight_bytes() / sec / 1e9,
+               "hbm_frac": self.layer.weight_bytes() / sec / 1e9 / HBM_PEAK_GBS,
+               "mfma_frac": flops / sec / 1e12 / BF16_PEAK_TFLOPS}
+        if cold_sec is not None:
+            res["ms_per_step_cold"] = cold_sec * 1e3
+            res["hbm_frac_cold"] = self.layer.weight_bytes() / cold_sec / 1e9 / HBM_PEAK_GBS
+        return res
 
 
 def time_steps(torch, wl, steps, warmup, stage_events, graph=True):
@@ -258,7 +262,42 @@ def time_steps(torch, wl, steps, warmup, stage_events, graph=True):
     return (t1 - t0) / steps, stage_ms
 
 
-def summarize(wl, sec_per_step, stage_ms):
+_FLUSH = []
+
+
+def flush_caches(torch):
+    """Reads 1 GiB (asynchronously, on the current stream), so that nothing of the
+    previous step is left in the 256 MB Infinity Cache or the L2s."""
+    if not _FLUSH:
+        _FLUSH.append(torch.ones(1 << 28, dtype=torch.float32, device="cuda"))
+    _FLUSH[0].sum()
+
+
+def time_cold(torch, wl, steps):
+    """Median time of one graph-replayed step that finds neither weights nor activations
+    in any cache: a 1 GiB read runs before every replay, outside the events around it."""
+    wl.step()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        wl.step()
+    g.replay()
+    torch.cuda.synchronize()
+    evs = []
+    for _ in range(steps):
+        flush_caches(torch)
+        b, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        b.record()
+        g.replay()
+        e.record()
+        evs.append((b, e))
+    torch.cuda.synchronize()
+    ms = sorted(b.elapsed_time(e) for b, e in evs)
+    del g
+    return ms[len(ms) // 2] * 1e-3
+
+
+def summarize(wl, sec_per_step, stage_ms, cold_sec=None):
     touched = wl.touched()
     gu_all, dn_all = wl.touched_bytes()
     h, i = wl.cfg["hidden"], wl.cfg["inter"]
@@ -273,6 +312,9 @@ def summarize(wl, sec_per_step, stage_ms):
         "hbm_frac": layer_bytes / sec_per_step / 1e9 / HBM_PEAK_GBS,
         "stage_ms": {k: round(v, 5) for k, v in stage_ms.items()},
     }
+    if cold_sec is not None:   # every step from HBM (caches flushed before it)
+        res["ms_per_step_cold"] = cold_sec * 1e3
+        res["hbm_frac_cold"] = layer_bytes / cold_sec / 1e9 / HBM_PEAK_GBS
     flops = wl.flops()
     int8 = wl.mode in (wl.lib.Q4_W4A8, wl.lib.Q4_W8A8)
     peak = INT8_PEAK_TOPS if int8 else BF16_PEAK_TFLOPS
@@ -365,7 +407,8 @@ def main():
     wl = Workload(lib, torch, synth, args.config, args.tokens, args.mode)
     log(f"[bench] layer weights {wl.layer.weight_bytes() / 1e9:.3f} GB; timing {args.steps} steps")
     sec, stage_ms = time_steps(torch, wl, args.steps, args.warmup, stage_events=True, graph=not args.no_graph)
-    main_res = summarize(wl, sec, stage_ms)
+    cold = time_cold(torch, wl, min(args.steps, 50)) if not args.no_graph else None
+    main_res = summarize(wl, sec, stage_ms, cold)
     log(f"[bench] main: {json.dumps(main_res)}")
 
     roof = None
@@ -401,20 +444,23 @@ def main():
             wl2 = wl.retoken(synth, t, mode)
             steps = 10 if t > 1000 else 50
             s2, st2 = time_steps(torch, wl2, steps, 3, stage_events=True, graph=not args.no_graph)
-            extra[f"moe256_T{t}_{mode}"] = summarize(wl2, s2, st2)
+            c2 = time_cold(torch, wl2, steps) if not args.no_graph else None
+            extra[f"moe256_T{t}_{mode}"] = summarize(wl2, s2, st2, c2)
             del wl2
             torch.cuda.empty_cache()
         for t in (1, 64, 2048):
             log(f"[bench] extra lora8 T={t}")
             lw = LoraWorkload(lib, torch, synth, "lora8", t)
             s4, _ = time_steps(torch, lw, 20 if t > 1000 else 50, 5, stage_events=False, graph=not args.no_graph)
-            extra[f"lora8_T{t}_w4a16"] = lw.summary(s4)
+            c4 = time_cold(torch, lw, 20 if t > 1000 else 50) if not args.no_graph else None
+            extra[f"lora8_T{t}_w4a16"] = lw.summary(s4, c4)
             del lw
         for mode in ("w4a8", "w8a8"):
             log(f"[bench] extra moe8 {mode} prefill T=2048")
             w8 = Workload(lib, torch, synth, "moe8_w4a8", 2048, mode)
             s3, st3 = time_steps(torch, w8, 20, 5, stage_events=True, graph=not args.no_graph)
-            extra[f"moe8_T2048_{mode}"] = summarize(w8, s3, st3)
+            c3 = time_cold(torch, w8, 20) if not args.no_graph else None
+            extra[f"moe8_T2048_{mode}"] = summarize(w8, s3, st3, c3)
             del w8
         log("[bench] extra moe256 mixed widths (top 5 % of experts by hit count in 8 bits), W4A8")
         bits = hotness_bits(lib, torch, synth, "moe256", 0.05)
@@ -485,6 +531,8 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
         "stage_ms": main_res["stage_ms"],
+        # the same step with the caches flushed before it (median; 1 GiB read in between)
+        "ms_per_step_cold": round(main_res["ms_per_step_cold"], 5) if "ms_per_step_cold" in main_res else None,
         "extra": extra,
     }
     print(json.dumps(res), flush=True)
