@@ -537,37 +537,31 @@ static hipError_t launch_cfg(const GemmArgs& g, hipStream_t st) {
   return hipGetLastError();
 }
 
-// Decode configuration (16-row tiles, many tiles); overridable at build time.
-#ifndef Q4_DEC_KW
-#define Q4_DEC_KW 1
-#endif
-#ifndef Q4_DEC_NBW
-#define Q4_DEC_NBW 4
-#endif
-#ifndef Q4_DEC_D
-#define Q4_DEC_D 2
-#endif
-// down projection (shorter K, wider N)
-#ifndef Q4_DN_KW
-#define Q4_DN_KW Q4_DEC_KW
-#endif
-#ifndef Q4_DN_NBW
-#define Q4_DN_NBW Q4_DEC_NBW
-#endif
-#ifndef Q4_DN_D
-#define Q4_DN_D Q4_DEC_D
-#endif
+// Decode configuration (16-row tiles, many tiles), by operation and activation type.
+// gate/up: two waves per column group split K (KW = 2, 128 columns per workgroup), so a
+// work item streams half as long and the launch's closing ramp, where fewer and fewer
+// items are in flight, is shorter (256-expert layer T = 64: bf16 354 -> 345 us with a
+// three-stage register pipeline, int8 350 -> 330 us); down (K = 2048, shorter items
+// already): one wave per column group for bf16 (KW = 2 measured 191 -> 203 us), two for
+// int8 (188 -> 184 us).  Layers with other group sizes (SG != 1) keep one wave per column
+// group (two would need 250-280 registers), and three stages are used only where the
+// registers allow it (bf16, one scale entry per tile).
+template <Act A, int KIND, bool W8, int SG>
+struct DecodeCfg {
+  static constexpr bool kPlain = KIND == GEMM_PLAIN;
+  static constexpr int KW = (SG == 1 && (!kPlain || A == Act::I8)) ? 2 : 1;
+  static constexpr int NBW = 4;
+  static constexpr int D = (!kPlain && A == Act::BF16 && SG == 1 && !W8) ? 3 : 2;
+  static constexpr int CB = (4 / KW) * NBW;   // column blocks per workgroup
+};
 
 // Configuration table: (MB, KW, NBW, D) by row blocks and the column count.
 template <Act A, int KIND, bool W8, int SG>
 static hipError_t launch_kind_sg(const GemmArgs& g, int rb, int split, hipStream_t st) {
   if (rb <= 1) {
-    constexpr int dec_cb = (4 / Q4_DEC_KW) * Q4_DEC_NBW;
-    constexpr int dn_cb = (4 / Q4_DN_KW) * Q4_DN_NBW;
+    using C = DecodeCfg<A, KIND, W8, SG>;
     if (split && g.N % (16 * 2) == 0) return launch_cfg<A, KIND, 1, 4, 2, 2, W8, SG>(g, st);
-    if (KIND == GEMM_PLAIN && g.N % (16 * dn_cb) == 0)
-      return launch_cfg<A, KIND, 1, Q4_DN_KW, Q4_DN_NBW, Q4_DN_D, W8, SG>(g, st);
-    if (g.N % (16 * dec_cb) == 0) return launch_cfg<A, KIND, 1, Q4_DEC_KW, Q4_DEC_NBW, Q4_DEC_D, W8, SG>(g, st);
+    if (g.N % (16 * C::CB) == 0) return launch_cfg<A, KIND, 1, C::KW, C::NBW, C::D, W8, SG>(g, st);
     return launch_cfg<A, KIND, 1, 4, 2, 2, W8, SG>(g, st);
   }
   if (rb <= 2) return launch_cfg<A, KIND, 2, 4, 4, 2, W8, SG>(g, st);
