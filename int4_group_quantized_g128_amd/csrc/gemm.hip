@@ -53,8 +53,22 @@ __global__ void __launch_bounds__(256) k_act_quant(const void* __restrict__ x, i
       }
     }
   };
+  // The first kHeld chunks of 8 per thread (rows of up to 8192 columns) stay in
+  // registers between the two passes, so such a row is read once, with all of its loads
+  // in flight together; the rest of a longer row is read again for the second pass.
+  constexpr int kHeld = 4;
+  float held[kHeld][8];
   float amax = 0.f;
-  for (int64_t c = int64_t(tid) * 8; c < cols; c += 256 * 8) {
+#pragma unroll
+  for (int j = 0; j < kHeld; ++j) {
+    const int64_t c = (int64_t(j) * 256 + tid) * 8;
+    if (c < cols) {
+      load8v(c, held[j]);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(held[j][i]));
+    }
+  }
+  for (int64_t c = (int64_t(kHeld) * 256 + tid) * 8; c < cols; c += 256 * 8) {
     float v[8];
     load8v(c, v);
 #pragma unroll
@@ -66,9 +80,7 @@ __global__ void __launch_bounds__(256) k_act_quant(const void* __restrict__ x, i
   amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   const float s = __fdiv_rn(amax, 127.0f);
   if (tid == 0) s_out[row] = s;
-  for (int64_t c = int64_t(tid) * 8; c < cols; c += 256 * 8) {
-    float v[8];
-    load8v(c, v);
+  auto store8 = [&](int64_t c, const float* v) {
     uint32_t packed[2] = {0u, 0u};
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -77,6 +89,16 @@ __global__ void __launch_bounds__(256) k_act_quant(const void* __restrict__ x, i
       packed[i >> 2] |= (uint32_t(int(qv)) & 0xffu) << (8 * (i & 3));
     }
     *reinterpret_cast<uint2*>(q + row * cols + c) = make_uint2(packed[0], packed[1]);
+  };
+#pragma unroll
+  for (int j = 0; j < kHeld; ++j) {
+    const int64_t c = (int64_t(j) * 256 + tid) * 8;
+    if (c < cols) store8(c, held[j]);
+  }
+  for (int64_t c = (int64_t(kHeld) * 256 + tid) * 8; c < cols; c += 256 * 8) {
+    float v[8];
+    load8v(c, v);
+    store8(c, v);
   }
 }
 
