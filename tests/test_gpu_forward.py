@@ -66,6 +66,26 @@ def test_small_shared_layer(lib, small, mode, t):
     assert ffn.max_rel_l2(_np(out), ref) <= (TOL_W4A16 if mode == 0 else TOL_W4A8)
 
 
+@pytest.mark.parametrize("mode", [0, 1], ids=["w4a16", "w4a8"])
+@pytest.mark.parametrize("t", [3, 40])
+def test_hidden_not_a_multiple_of_256(lib, mode, t):
+    """Hidden 384: the down projection's 16-row decode tiles cannot take the 256-column
+    bf16 workgroups (384 = 1.5 x 256) and fall back to the narrow configuration; int8's
+    128-column workgroups divide it.  6 experts x inter 128, top-2, shared expert."""
+    E, H, I, k = 6, 384, 128, 2
+    make = random_expert_maker(17, H, I)
+    layer = build_gpu_layer(lib, make, E, H, I, k, shared=True)
+    oe = OracleExperts(make, False)
+    x = synth.normal(synth.stream_key(18, t), (t, H), 1.0).to(torch.bfloat16)
+    rng = np.random.default_rng(19 + t)
+    ids = np.stack([rng.permutation(E)[:k] for _ in range(t)]).astype(np.int32)
+    w = rng.dirichlet(np.ones(k), size=t)
+    out = _forward(lib, layer, x, ids, w, mode)
+    fn = ffn.moe_w4a16 if mode == 0 else ffn.moe_w4a8
+    ref = fn(_np(x), oe, ids, w, shared=oe(E))
+    assert ffn.max_rel_l2(_np(out), ref) <= (TOL_W4A16 if mode == 0 else TOL_W4A8)
+
+
 def test_zero_tokens_is_noop(lib, small):
     layer, _ = small
     x = torch.zeros((0, SMALL["h"]), dtype=torch.bfloat16)
