@@ -10,6 +10,8 @@
 // Kernels here: the rank-r input projections (k_lora_in), SwiGLU + weighted sum + the
 // down-adapter input projection (k_lora_mid), the final combine (k_lora_out), and the
 // row-tile list of a dense matrix for the prefill GEMM (k_dense_tiles).
+#include <type_traits>
+
 #include "common.h"
 #include "internal.h"
 
@@ -36,13 +38,15 @@ Q4_DEVICE float wave_sum(float v) {
 }
 
 // Partial input projections: a_part[p][ks][q] = sum_{k in chunk ks} A_e[q][k] x_t[k]
-// (q < 2r: A_gate,e rows then A_up,e rows) for slot p = t * kk + j, e = ids[p], and
+// (q < 2R: A_gate,e rows then A_up,e rows) for slot p = t * kk + j, e = ids[p], and
 // the 512-wide K chunk ks (one wave per (slot, chunk); lane l covers k = 512 ks + 8 l
-// .. + 7).  The 64 lane partials of each q are summed in lane order through LDS.
-template <int R2>
+// .. + 7).  The 64 lane partials of each q are summed in lane order through LDS.  The
+// rank R is a template argument, so every adapter load of a lane is issued at once.
+template <int R>
 __global__ void __launch_bounds__(64) k_lora_in(const uint16_t* __restrict__ x, int64_t h, const int32_t* __restrict__ ids,
-                                                int32_t kk, int32_t e_count, const uint16_t* __restrict__ a_gu, int r2,
+                                                int32_t kk, int32_t e_count, const uint16_t* __restrict__ a_gu,
                                                 float* __restrict__ a_part) {
+  constexpr int R2 = 2 * R;
   __shared__ float part[R2][65];
   const int lane = threadIdx.x;
   const int64_t p = blockIdx.x, ks = blockIdx.y, nks = gridDim.y;
@@ -54,6 +58,9 @@ __global__ void __launch_bounds__(64) k_lora_in(const uint16_t* __restrict__ x, 
   for (int q = 0; q < R2; ++q) acc[q] = 0.f;
   if (k0 < h) {
     const uint4 xv = load16(x + t * h + k0);
+    uint4 av[R2];
+#pragma unroll
+    for (int q = 0; q < R2; ++q) av[q] = load16(a_gu + (int64_t(e) * R2 + q) * h + k0);
     float xf[8];
     const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
 #pragma unroll
@@ -61,9 +68,6 @@ __global__ void __launch_bounds__(64) k_lora_in(const uint16_t* __restrict__ x, 
       xf[2 * i] = bf16_to_f32(uint16_t(xw[i] & 0xffff));
       xf[2 * i + 1] = bf16_to_f32(uint16_t(xw[i] >> 16));
     }
-    uint4 av[R2];
-#pragma unroll
-    for (int q = 0; q < R2; ++q) av[q] = q < r2 ? load16(a_gu + (int64_t(e) * r2 + q) * h + k0) : make_uint4(0, 0, 0, 0);
 #pragma unroll
     for (int q = 0; q < R2; ++q) {
       const uint32_t aw[4] = {av[q].x, av[q].y, av[q].z, av[q].w};
@@ -77,29 +81,31 @@ __global__ void __launch_bounds__(64) k_lora_in(const uint16_t* __restrict__ x, 
 #pragma unroll
   for (int q = 0; q < R2; ++q) part[q][lane] = acc[q];
   __syncthreads();
-  if (lane < r2) {
+  for (int q = lane; q < R2; q += 64) {   // 2R can exceed the 64 lanes
     float s = 0.f;
-    for (int l = 0; l < 64; ++l) s += part[lane][l];
-    a_part[(p * nks + ks) * r2 + lane] = s;
+    for (int l = 0; l < 64; ++l) s += part[q][l];
+    a_part[(p * nks + ks) * R2 + q] = s;
   }
 }
 
 // Column block cb of token t (256 threads x 4 consecutive columns): for each choice j
 // (expert e, weight w_j, slot p), with a = sum over K chunks of a_part[p] (in order):
 //   g_c = base_gu[t][c] + sum_q B_gate,e[c][q] a[q]
-//   u_c = base_gu[t][I + c] + sum_q B_up,e[c][q] a[r + q]
+//   u_c = base_gu[t][I + c] + sum_q B_up,e[c][q] a[R + q]
 //   h_c = silu(g_c) u_c;  hw_c += w_j h_c;  d_part[p][cb][q] = sum_{c in block} A_down,e[q][c] h_c
-// then hw[t][c] = bf16(hw_c).  r is a multiple of 8 and at most RM.
+// then hw[t][c] = bf16(hw_c).  A thread's adapter rows (B_gate / B_up: R contiguous
+// values per column; A_down: its 4 columns of each of the R rows) are all loaded before
+// any is used.
 constexpr int kMidCols = 1024;   // columns per workgroup
-template <int RM>
+template <int R>
 __global__ void __launch_bounds__(256) k_lora_mid(const float* __restrict__ base_gu, int64_t inter,
                                                   const int32_t* __restrict__ ids, const float* __restrict__ w,
-                                                  int32_t kk, int32_t e_count, int r, int nks,
+                                                  int32_t kk, int32_t e_count, int nks,
                                                   const float* __restrict__ a_part, const uint16_t* __restrict__ b_gate,
                                                   const uint16_t* __restrict__ b_up, const uint16_t* __restrict__ a_down,
                                                   float* __restrict__ d_part, uint16_t* __restrict__ hw) {
-  __shared__ float s_a[2 * RM];
-  __shared__ float s_red[4][RM];
+  __shared__ float s_a[2 * R];
+  __shared__ float s_red[4][R];
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int64_t t = blockIdx.y, cb = blockIdx.x, ncb = gridDim.x;
   const int64_t c0 = cb * kMidCols + int64_t(tid) * 4;
@@ -115,52 +121,87 @@ __global__ void __launch_bounds__(256) k_lora_mid(const float* __restrict__ base
     const int64_t p = t * kk + j;
     const int e = min(max(ids[p], 0), e_count - 1);
     const float wj = w[p];
+    // adapter loads first (they do not depend on s_a): the B rows of CB columns and QB
+    // rows of A_down at a time, all of a batch issued together (every batch at once for
+    // R <= 16; larger ranks keep the registers within bounds)
+    constexpr int CB = R <= 16 ? 4 : R <= 32 ? 2 : 1;
+    constexpr int QB = R <= 16 ? R : R % 16 == 0 ? 16 : 8;   // divides R
+    static_assert(R % QB == 0 && 4 % CB == 0, "load batches must tile the rows and columns");
+    const uint16_t* bg = b_gate + (int64_t(e) * inter + c0) * R;
+    const uint16_t* bu = b_up + (int64_t(e) * inter + c0) * R;
+    const uint16_t* ad = a_down + int64_t(e) * R * inter + c0;
+    uint4 vg[CB][R / 8], vu[CB][R / 8];
+    uint2 va[QB];
+    auto load_b = [&](int i0) {
+#pragma unroll
+      for (int i = 0; i < CB; ++i)
+#pragma unroll
+        for (int q8 = 0; q8 < R / 8; ++q8) {
+          vg[i][q8] = load16(bg + (i0 + i) * R + 8 * q8);
+          vu[i][q8] = load16(bu + (i0 + i) * R + 8 * q8);
+        }
+    };
+    auto load_a = [&](int q0) {
+#pragma unroll
+      for (int q = 0; q < QB; ++q) va[q] = *reinterpret_cast<const uint2*>(ad + int64_t(q0 + q) * inter);
+    };
+    if (cv) {
+      load_b(0);
+      load_a(0);
+    }
     __syncthreads();   // s_a / s_red of the previous choice are consumed
-    if (tid < 2 * r) {
+    if (tid < 2 * R) {
       float s = 0.f;
-      for (int ks = 0; ks < nks; ++ks) s += a_part[(p * nks + ks) * 2 * r + tid];
+      for (int ks = 0; ks < nks; ++ks) s += a_part[(p * nks + ks) * 2 * R + tid];
       s_a[tid] = s;
     }
     __syncthreads();
-    float dp[RM];
+    float dp[R];
 #pragma unroll
-    for (int q = 0; q < RM; ++q) dp[q] = 0.f;
+    for (int q = 0; q < R; ++q) dp[q] = 0.f;
     if (cv) {
+      float hv[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int64_t c = c0 + i;
-        float g = g0[i], u = u0[i];
-        const uint16_t* bg = b_gate + (int64_t(e) * inter + c) * r;
-        const uint16_t* bu = b_up + (int64_t(e) * inter + c) * r;
+      for (int i0 = 0; i0 < 4; i0 += CB) {
+        if (i0 > 0) load_b(i0);
 #pragma unroll
-        for (int q8 = 0; q8 < RM; q8 += 8) {
-          if (q8 < r) {
-            const uint4 vg = load16(bg + q8), vu = load16(bu + q8);
-            const uint32_t wg[4] = {vg.x, vg.y, vg.z, vg.w}, wu[4] = {vu.x, vu.y, vu.z, vu.w};
+        for (int i = 0; i < CB; ++i) {
+          float g = g0[i0 + i], u = u0[i0 + i];
+#pragma unroll
+          for (int q8 = 0; q8 < R / 8; ++q8) {
+            const uint32_t wg[4] = {vg[i][q8].x, vg[i][q8].y, vg[i][q8].z, vg[i][q8].w};
+            const uint32_t wu[4] = {vu[i][q8].x, vu[i][q8].y, vu[i][q8].z, vu[i][q8].w};
 #pragma unroll
             for (int z = 0; z < 4; ++z) {
-              g = fmaf(bf16_to_f32(uint16_t(wg[z] & 0xffff)), s_a[q8 + 2 * z], g);
-              g = fmaf(bf16_to_f32(uint16_t(wg[z] >> 16)), s_a[q8 + 2 * z + 1], g);
-              u = fmaf(bf16_to_f32(uint16_t(wu[z] & 0xffff)), s_a[r + q8 + 2 * z], u);
-              u = fmaf(bf16_to_f32(uint16_t(wu[z] >> 16)), s_a[r + q8 + 2 * z + 1], u);
+              g = fmaf(bf16_to_f32(uint16_t(wg[z] & 0xffff)), s_a[8 * q8 + 2 * z], g);
+              g = fmaf(bf16_to_f32(uint16_t(wg[z] >> 16)), s_a[8 * q8 + 2 * z + 1], g);
+              u = fmaf(bf16_to_f32(uint16_t(wu[z] & 0xffff)), s_a[R + 8 * q8 + 2 * z], u);
+              u = fmaf(bf16_to_f32(uint16_t(wu[z] >> 16)), s_a[R + 8 * q8 + 2 * z + 1], u);
             }
           }
+          hv[i0 + i] = swiglu(g, u);
+          hacc[i0 + i] = fmaf(wj, hv[i0 + i], hacc[i0 + i]);
         }
-        const float hv = swiglu(g, u);
-        hacc[i] = fmaf(wj, hv, hacc[i]);
-        const uint16_t* ad = a_down + int64_t(e) * r * inter + c;
+      }
 #pragma unroll
-        for (int q = 0; q < RM; ++q)
-          if (q < r) dp[q] = fmaf(bf16_to_f32(ad[int64_t(q) * inter]), hv, dp[q]);
+      for (int q0 = 0; q0 < R; q0 += QB) {
+        if (q0 > 0) load_a(q0);
+#pragma unroll
+        for (int q = 0; q < QB; ++q) {
+          const float a[4] = {bf16_to_f32(uint16_t(va[q].x & 0xffff)), bf16_to_f32(uint16_t(va[q].x >> 16)),
+                              bf16_to_f32(uint16_t(va[q].y & 0xffff)), bf16_to_f32(uint16_t(va[q].y >> 16))};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) dp[q0 + q] = fmaf(a[i], hv[i], dp[q0 + q]);
+        }
       }
     }
 #pragma unroll
-    for (int q = 0; q < RM; ++q) {
+    for (int q = 0; q < R; ++q) {
       const float s = wave_sum(dp[q]);
-      if (lane == 0 && q < r) s_red[wid][q] = s;
+      if (lane == 0) s_red[wid][q] = s;
     }
     __syncthreads();
-    if (tid < r) d_part[(p * ncb + cb) * r + tid] = ((s_red[0][tid] + s_red[1][tid]) + s_red[2][tid]) + s_red[3][tid];
+    if (tid < R) d_part[(p * ncb + cb) * R + tid] = ((s_red[0][tid] + s_red[1][tid]) + s_red[2][tid]) + s_red[3][tid];
   }
   if (cv) {
     const uint32_t lo = uint32_t(f32_to_bf16(hacc[0])) | (uint32_t(f32_to_bf16(hacc[1])) << 16);
@@ -171,19 +212,20 @@ __global__ void __launch_bounds__(256) k_lora_mid(const float* __restrict__ base
 
 // out[t][c] = bf16( y[t][c] + sum_j w_j sum_q B_down,e_j[c][q] d[t kk + j][q] ), d the
 // sum over column blocks of d_part (in order).
+template <int R>
 __global__ void __launch_bounds__(256) k_lora_out(const float* __restrict__ y, int64_t hidden,
                                                   const int32_t* __restrict__ ids, const float* __restrict__ w,
-                                                  int32_t kk, int32_t e_count, int r, int ncb,
+                                                  int32_t kk, int32_t e_count, int ncb,
                                                   const float* __restrict__ d_part, const uint16_t* __restrict__ b_down,
                                                   uint16_t* __restrict__ out) {
-  extern __shared__ float s_d[];   // [kk][r]
+  extern __shared__ float s_d[];   // [kk][R]
   const int tid = threadIdx.x;
   const int64_t t = blockIdx.y;
-  for (int i = tid; i < kk * r; i += 256) {
-    const int j = i / r, q = i - j * r;
+  for (int i = tid; i < kk * R; i += 256) {
+    const int j = i / R, q = i - j * R;
     const int64_t p = t * kk + j;
     float s = 0.f;
-    for (int cb = 0; cb < ncb; ++cb) s += d_part[(p * ncb + cb) * r + q];
+    for (int cb = 0; cb < ncb; ++cb) s += d_part[(p * ncb + cb) * R + q];
     s_d[i] = s;
   }
   __syncthreads();
@@ -193,20 +235,39 @@ __global__ void __launch_bounds__(256) k_lora_out(const float* __restrict__ y, i
   for (int j = 0; j < kk; ++j) {
     const int64_t p = t * kk + j;
     const int e = min(max(ids[p], 0), e_count - 1);
-    const uint16_t* bd = b_down + (int64_t(e) * hidden + c) * r;
+    const uint16_t* bd = b_down + (int64_t(e) * hidden + c) * R;
+    uint4 v[R / 8];
+#pragma unroll
+    for (int q8 = 0; q8 < R / 8; ++q8) v[q8] = load16(bd + 8 * q8);
     float s = 0.f;
-    for (int q8 = 0; q8 < r; q8 += 8) {
-      const uint4 v = load16(bd + q8);
-      const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int q8 = 0; q8 < R / 8; ++q8) {
+      const uint32_t wv[4] = {v[q8].x, v[q8].y, v[q8].z, v[q8].w};
 #pragma unroll
       for (int z = 0; z < 4; ++z) {
-        s = fmaf(bf16_to_f32(uint16_t(wv[z] & 0xffff)), s_d[j * r + q8 + 2 * z], s);
-        s = fmaf(bf16_to_f32(uint16_t(wv[z] >> 16)), s_d[j * r + q8 + 2 * z + 1], s);
+        s = fmaf(bf16_to_f32(uint16_t(wv[z] & 0xffff)), s_d[j * R + 8 * q8 + 2 * z], s);
+        s = fmaf(bf16_to_f32(uint16_t(wv[z] >> 16)), s_d[j * R + 8 * q8 + 2 * z + 1], s);
       }
     }
     acc = fmaf(w[p], s, acc);
   }
   out[t * hidden + c] = f32_to_bf16(acc);
+}
+
+// Calls f(integral_constant<int, R>) for the rank r in {8, 16, ..., 64}.
+template <typename F>
+static hipError_t with_rank(int r, F&& f) {
+  switch (r) {
+    case 8: return f(std::integral_constant<int, 8>{});
+    case 16: return f(std::integral_constant<int, 16>{});
+    case 24: return f(std::integral_constant<int, 24>{});
+    case 32: return f(std::integral_constant<int, 32>{});
+    case 40: return f(std::integral_constant<int, 40>{});
+    case 48: return f(std::integral_constant<int, 48>{});
+    case 56: return f(std::integral_constant<int, 56>{});
+    case 64: return f(std::integral_constant<int, 64>{});
+    default: return hipErrorInvalidValue;
+  }
 }
 
 int lora_kchunks(int64_t h) { return int((h + 511) / 512); }
@@ -222,18 +283,12 @@ hipError_t launch_dense_tiles(int64_t t, int tile_rows, TileDesc* tiles, int32_t
 hipError_t launch_lora_in(const uint16_t* x, int64_t t, int64_t h, const int32_t* ids, int32_t kk, int32_t e,
                           const uint16_t* a_gu, int r, float* a_part, hipStream_t st) {
   const int64_t P = t * kk;
-  const int r2 = 2 * r;
   if (P == 0) return hipSuccess;
   const dim3 g = dim3(unsigned(P), unsigned(lora_kchunks(h))), b = dim3(64);
-  if (r2 <= 16)
-    hipLaunchKernelGGL(k_lora_in<16>, g, b, 0, st, x, h, ids, kk, e, a_gu, r2, a_part);
-  else if (r2 <= 32)
-    hipLaunchKernelGGL(k_lora_in<32>, g, b, 0, st, x, h, ids, kk, e, a_gu, r2, a_part);
-  else if (r2 <= 64)
-    hipLaunchKernelGGL(k_lora_in<64>, g, b, 0, st, x, h, ids, kk, e, a_gu, r2, a_part);
-  else
-    hipLaunchKernelGGL(k_lora_in<128>, g, b, 0, st, x, h, ids, kk, e, a_gu, r2, a_part);
-  return hipGetLastError();
+  return with_rank(r, [&](auto rc) {
+    hipLaunchKernelGGL((k_lora_in<decltype(rc)::value>), g, b, 0, st, x, h, ids, kk, e, a_gu, a_part);
+    return hipGetLastError();
+  });
 }
 
 hipError_t launch_lora_mid(const float* base_gu, int64_t t, int64_t h, int64_t inter, const int32_t* ids,
@@ -242,16 +297,11 @@ hipError_t launch_lora_mid(const float* base_gu, int64_t t, int64_t h, int64_t i
   if (t == 0) return hipSuccess;
   const dim3 g = dim3(unsigned(lora_col_blocks(inter)), unsigned(t)), b = dim3(256);
   const int nks = lora_kchunks(h);
-  if (r <= 16)
-    hipLaunchKernelGGL(k_lora_mid<16>, g, b, 0, st, base_gu, inter, ids, w, kk, e, r, nks, a_part, b_gate, b_up, a_down,
-                       d_part, hw);
-  else if (r <= 32)
-    hipLaunchKernelGGL(k_lora_mid<32>, g, b, 0, st, base_gu, inter, ids, w, kk, e, r, nks, a_part, b_gate, b_up, a_down,
-                       d_part, hw);
-  else
-    hipLaunchKernelGGL(k_lora_mid<64>, g, b, 0, st, base_gu, inter, ids, w, kk, e, r, nks, a_part, b_gate, b_up, a_down,
-                       d_part, hw);
-  return hipGetLastError();
+  return with_rank(r, [&](auto rc) {
+    hipLaunchKernelGGL((k_lora_mid<decltype(rc)::value>), g, b, 0, st, base_gu, inter, ids, w, kk, e, nks, a_part,
+                       b_gate, b_up, a_down, d_part, hw);
+    return hipGetLastError();
+  });
 }
 
 hipError_t launch_lora_out(const float* y, int64_t t, int64_t hidden, int64_t inter, const int32_t* ids,
@@ -259,9 +309,11 @@ hipError_t launch_lora_out(const float* y, int64_t t, int64_t hidden, int64_t in
                            uint16_t* out, hipStream_t st) {
   if (t == 0) return hipSuccess;
   const dim3 g = dim3(unsigned((hidden + 255) / 256), unsigned(t));
-  hipLaunchKernelGGL(k_lora_out, g, dim3(256), size_t(kk) * r * sizeof(float), st, y, hidden, ids, w, kk, e, r,
-                     lora_col_blocks(inter), d_part, b_down, out);
-  return hipGetLastError();
+  return with_rank(r, [&](auto rc) {
+    hipLaunchKernelGGL((k_lora_out<decltype(rc)::value>), g, dim3(256), size_t(kk) * r * sizeof(float), st, y, hidden,
+                       ids, w, kk, e, lora_col_blocks(inter), d_part, b_down, out);
+    return hipGetLastError();
+  });
 }
 
 }  // namespace q4

@@ -96,6 +96,23 @@ def test_zero_adapters_equal_dense(lib, small):
     assert ffn.max_rel_l2(_np(out), ffn.swiglu_w4a16(_np(x), *ob)) <= TOL
 
 
+@pytest.mark.parametrize("r", [24, 40, 64])
+def test_lora_ranks(lib, r):
+    """Ranks above 16: the adapter kernels load the rows of two columns or one at a time
+    and the down-adapter rows 16 at a time (rank 16 and below load everything at once)."""
+    E, H, I, k = 4, 256, 384, 2
+    base = (synth.normal(synth.stream_key(64, 1), (I, H), 0.05), synth.normal(synth.stream_key(64, 2), (I, H), 0.05),
+            synth.normal(synth.stream_key(64, 3), (H, I), 0.05))
+    adapters = lambda e: synth.lora_adapters("lora8", e, rank=r, dims=(H, I))
+    layer, ob, oa = _build(lib, base, adapters, E, H, I, k, r, False)
+    for t in (3, 70):
+        x = synth.normal(synth.stream_key(65, t, r), (t, H), 1.0).to(torch.bfloat16)
+        ids, w = _route(t, E, k, t + r)
+        out = _run(lib, layer, x, ids, w)
+        ref = lora.moe_lora(_np(x), ob, oa, ids, w)
+        assert ffn.max_rel_l2(_np(out), ref) <= TOL, (r, t)
+
+
 @pytest.fixture(scope="module")
 def lora8(lib):
     cfg = synth.CONFIGS["lora8"]
