@@ -88,15 +88,19 @@ __global__ void __launch_bounds__(64) k_lora_in(const uint16_t* __restrict__ x, 
   }
 }
 
-// Column block cb of token t (256 threads x 4 consecutive columns): for each choice j
-// (expert e, weight w_j, slot p), with a = sum over K chunks of a_part[p] (in order):
+// Column block cb of token t (256 threads; thread tid owns columns
+// c_i = 1024 cb + tid + 256 i, i < 4): for each choice j (expert e, weight w_j, slot p),
+// with a = sum over K chunks of a_part[p] (in order):
 //   g_c = base_gu[t][c] + sum_q B_gate,e[c][q] a[q]
 //   u_c = base_gu[t][I + c] + sum_q B_up,e[c][q] a[R + q]
 //   h_c = silu(g_c) u_c;  hw_c += w_j h_c;  d_part[p][cb][q] = sum_{c in block} A_down,e[q][c] h_c
-// then hw[t][c] = bf16(hw_c).  A thread's adapter rows (B_gate / B_up: R contiguous
-// values per column; A_down: its 4 columns of each of the R rows) are all loaded before
-// any is used.
-constexpr int kMidCols = 1024;   // columns per workgroup
+// then hw[t][c] = bf16(hw_c).  With consecutive columns on consecutive lanes, one
+// 16-byte load of a wave covers R / 8 * 64 * 16 bytes of B rows (16 cache lines at
+// R = 16, not 64 as with four consecutive columns per lane).  A thread's adapter rows
+// are all loaded before any is used; columns past I load the last column (in bounds)
+// and are masked.
+constexpr int kMidNC = 4;                // columns per thread (measured faster than 1 or 2)
+constexpr int kMidCols = 256 * kMidNC;   // columns per workgroup
 template <int R>
 __global__ void __launch_bounds__(256) k_lora_mid(const float* __restrict__ base_gu, int64_t inter,
                                                   const int32_t* __restrict__ ids, const float* __restrict__ w,
@@ -108,15 +112,21 @@ __global__ void __launch_bounds__(256) k_lora_mid(const float* __restrict__ base
   __shared__ float s_red[4][R];
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int64_t t = blockIdx.y, cb = blockIdx.x, ncb = gridDim.x;
-  const int64_t c0 = cb * kMidCols + int64_t(tid) * 4;
-  const bool cv = c0 < inter;     // inter % 128 == 0, so a thread's 4 columns are all valid or all not
-  float hacc[4] = {0.f, 0.f, 0.f, 0.f};
-  float4 bgu0 = make_float4(0.f, 0.f, 0.f, 0.f), bgu1 = bgu0;
-  if (cv) {
-    bgu0 = *reinterpret_cast<const float4*>(base_gu + t * 2 * inter + c0);
-    bgu1 = *reinterpret_cast<const float4*>(base_gu + t * 2 * inter + inter + c0);
+  int64_t col[kMidNC];   // clamped into [0, inter)
+  bool cv[kMidNC];
+#pragma unroll
+  for (int i = 0; i < kMidNC; ++i) {
+    const int64_t c = cb * kMidCols + tid + 256 * i;
+    cv[i] = c < inter;
+    col[i] = cv[i] ? c : inter - 1;
   }
-  const float g0[4] = {bgu0.x, bgu0.y, bgu0.z, bgu0.w}, u0[4] = {bgu1.x, bgu1.y, bgu1.z, bgu1.w};
+  float hacc[kMidNC], g0[kMidNC], u0[kMidNC];
+#pragma unroll
+  for (int i = 0; i < kMidNC; ++i) {
+    hacc[i] = 0.f;
+    g0[i] = base_gu[t * 2 * inter + col[i]];
+    u0[i] = base_gu[t * 2 * inter + inter + col[i]];
+  }
   for (int j = 0; j < kk; ++j) {
     const int64_t p = t * kk + j;
     const int e = min(max(ids[p], 0), e_count - 1);
@@ -124,31 +134,31 @@ __global__ void __launch_bounds__(256) k_lora_mid(const float* __restrict__ base
     // adapter loads first (they do not depend on s_a): the B rows of CB columns and QB
     // rows of A_down at a time, all of a batch issued together (every batch at once for
     // R <= 16; larger ranks keep the registers within bounds)
-    constexpr int CB = R <= 16 ? 4 : R <= 32 ? 2 : 1;
+    constexpr int CB = R <= 16 ? kMidNC : R <= 32 ? (kMidNC >= 2 ? 2 : 1) : 1;
     constexpr int QB = R <= 16 ? R : R % 16 == 0 ? 16 : 8;   // divides R
-    static_assert(R % QB == 0 && 4 % CB == 0, "load batches must tile the rows and columns");
-    const uint16_t* bg = b_gate + (int64_t(e) * inter + c0) * R;
-    const uint16_t* bu = b_up + (int64_t(e) * inter + c0) * R;
-    const uint16_t* ad = a_down + int64_t(e) * R * inter + c0;
+    static_assert(R % QB == 0 && kMidNC % CB == 0, "load batches must tile the rows and columns");
+    const uint16_t* bg = b_gate + int64_t(e) * inter * R;
+    const uint16_t* bu = b_up + int64_t(e) * inter * R;
+    const uint16_t* ad = a_down + int64_t(e) * R * inter;
     uint4 vg[CB][R / 8], vu[CB][R / 8];
-    uint2 va[QB];
+    uint16_t va[QB][kMidNC];
     auto load_b = [&](int i0) {
 #pragma unroll
       for (int i = 0; i < CB; ++i)
 #pragma unroll
         for (int q8 = 0; q8 < R / 8; ++q8) {
-          vg[i][q8] = load16(bg + (i0 + i) * R + 8 * q8);
-          vu[i][q8] = load16(bu + (i0 + i) * R + 8 * q8);
+          vg[i][q8] = load16(bg + col[i0 + i] * R + 8 * q8);
+          vu[i][q8] = load16(bu + col[i0 + i] * R + 8 * q8);
         }
     };
     auto load_a = [&](int q0) {
 #pragma unroll
-      for (int q = 0; q < QB; ++q) va[q] = *reinterpret_cast<const uint2*>(ad + int64_t(q0 + q) * inter);
+      for (int q = 0; q < QB; ++q)
+#pragma unroll
+        for (int i = 0; i < kMidNC; ++i) va[q][i] = ad[int64_t(q0 + q) * inter + col[i]];
     };
-    if (cv) {
-      load_b(0);
-      load_a(0);
-    }
+    load_b(0);
+    load_a(0);
     __syncthreads();   // s_a / s_red of the previous choice are consumed
     if (tid < 2 * R) {
       float s = 0.f;
@@ -159,41 +169,37 @@ __global__ void __launch_bounds__(256) k_lora_mid(const float* __restrict__ base
     float dp[R];
 #pragma unroll
     for (int q = 0; q < R; ++q) dp[q] = 0.f;
-    if (cv) {
-      float hv[4];
+    float hv[kMidNC];
 #pragma unroll
-      for (int i0 = 0; i0 < 4; i0 += CB) {
-        if (i0 > 0) load_b(i0);
+    for (int i0 = 0; i0 < kMidNC; i0 += CB) {
+      if (i0 > 0) load_b(i0);
 #pragma unroll
-        for (int i = 0; i < CB; ++i) {
-          float g = g0[i0 + i], u = u0[i0 + i];
+      for (int i = 0; i < CB; ++i) {
+        float g = g0[i0 + i], u = u0[i0 + i];
 #pragma unroll
-          for (int q8 = 0; q8 < R / 8; ++q8) {
-            const uint32_t wg[4] = {vg[i][q8].x, vg[i][q8].y, vg[i][q8].z, vg[i][q8].w};
-            const uint32_t wu[4] = {vu[i][q8].x, vu[i][q8].y, vu[i][q8].z, vu[i][q8].w};
+        for (int q8 = 0; q8 < R / 8; ++q8) {
+          const uint32_t wg[4] = {vg[i][q8].x, vg[i][q8].y, vg[i][q8].z, vg[i][q8].w};
+          const uint32_t wu[4] = {vu[i][q8].x, vu[i][q8].y, vu[i][q8].z, vu[i][q8].w};
 #pragma unroll
-            for (int z = 0; z < 4; ++z) {
-              g = fmaf(bf16_to_f32(uint16_t(wg[z] & 0xffff)), s_a[8 * q8 + 2 * z], g);
-              g = fmaf(bf16_to_f32(uint16_t(wg[z] >> 16)), s_a[8 * q8 + 2 * z + 1], g);
-              u = fmaf(bf16_to_f32(uint16_t(wu[z] & 0xffff)), s_a[R + 8 * q8 + 2 * z], u);
-              u = fmaf(bf16_to_f32(uint16_t(wu[z] >> 16)), s_a[R + 8 * q8 + 2 * z + 1], u);
-            }
+          for (int z = 0; z < 4; ++z) {
+            g = fmaf(bf16_to_f32(uint16_t(wg[z] & 0xffff)), s_a[8 * q8 + 2 * z], g);
+            g = fmaf(bf16_to_f32(uint16_t(wg[z] >> 16)), s_a[8 * q8 + 2 * z + 1], g);
+            u = fmaf(bf16_to_f32(uint16_t(wu[z] & 0xffff)), s_a[R + 8 * q8 + 2 * z], u);
+            u = fmaf(bf16_to_f32(uint16_t(wu[z] >> 16)), s_a[R + 8 * q8 + 2 * z + 1], u);
           }
-          hv[i0 + i] = swiglu(g, u);
-          hacc[i0 + i] = fmaf(wj, hv[i0 + i], hacc[i0 + i]);
         }
+        hv[i0 + i] = swiglu(g, u);
+        hacc[i0 + i] = fmaf(wj, hv[i0 + i], hacc[i0 + i]);
       }
+    }
 #pragma unroll
-      for (int q0 = 0; q0 < R; q0 += QB) {
-        if (q0 > 0) load_a(q0);
+    for (int q0 = 0; q0 < R; q0 += QB) {
+      if (q0 > 0) load_a(q0);
 #pragma unroll
-        for (int q = 0; q < QB; ++q) {
-          const float a[4] = {bf16_to_f32(uint16_t(va[q].x & 0xffff)), bf16_to_f32(uint16_t(va[q].x >> 16)),
-                              bf16_to_f32(uint16_t(va[q].y & 0xffff)), bf16_to_f32(uint16_t(va[q].y >> 16))};
+      for (int q = 0; q < QB; ++q)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) dp[q0 + q] = fmaf(a[i], hv[i], dp[q0 + q]);
-        }
-      }
+        for (int i = 0; i < kMidNC; ++i)
+          if (cv[i]) dp[q0 + q] = fmaf(bf16_to_f32(va[q][i]), hv[i], dp[q0 + q]);
     }
 #pragma unroll
     for (int q = 0; q < R; ++q) {
@@ -203,11 +209,9 @@ __global__ void __launch_bounds__(256) k_lora_mid(const float* __restrict__ base
     __syncthreads();
     if (tid < R) d_part[(p * ncb + cb) * R + tid] = ((s_red[0][tid] + s_red[1][tid]) + s_red[2][tid]) + s_red[3][tid];
   }
-  if (cv) {
-    const uint32_t lo = uint32_t(f32_to_bf16(hacc[0])) | (uint32_t(f32_to_bf16(hacc[1])) << 16);
-    const uint32_t hi = uint32_t(f32_to_bf16(hacc[2])) | (uint32_t(f32_to_bf16(hacc[3])) << 16);
-    *reinterpret_cast<uint2*>(hw + t * inter + c0) = make_uint2(lo, hi);
-  }
+#pragma unroll
+  for (int i = 0; i < kMidNC; ++i)
+    if (cv[i]) hw[t * inter + col[i]] = f32_to_bf16(hacc[i]);
 }
 
 // out[t][c] = bf16( y[t][c] + sum_j w_j sum_q B_down,e_j[c][q] d[t kk + j][q] ), d the
