@@ -213,6 +213,39 @@ class LoraWorkload:
         return res
 
 
+class DenseWorkload(Workload):
+    """The LLaMA-3.2-1B-shaped dense SwiGLU FFN (hidden 2048, intermediate 8192,
+    asymmetric INT4 g128) as a one-expert layer with weight 1 and no router; a step is
+    moe_int4_ffn_forward alone."""
+
+    def __init__(self, lib, torch, synth, t, mode):
+        self.lib, self.torch = lib, torch
+        base = synth.CONFIGS["dense"]
+        self.cfg_name, self.cfg, self.t = "dense", dict(base, experts=1, top_k=1), t
+        self.mode = {"w4a16": lib.Q4_W4A16, "w4a8": lib.Q4_W4A8}[mode]
+        self.wbits = 4
+        h, i = base["hidden"], base["inter"]
+        self.layer = lib.MoELayer(1, h, i, 1, asymmetric=True)
+        g, u, d = synth.dense_ffn_weights("dense", device="cuda")
+        self.layer.set_expert(0, g, u, d)
+        del g, u, d
+        self.x = synth.tokens("dense", t, device="cuda")
+        self.ids = torch.zeros((t, 1), dtype=torch.int32, device="cuda")
+        self.w = torch.ones((t, 1), dtype=torch.float32, device="cuda")
+        self.out = torch.empty((t, h), dtype=torch.bfloat16, device="cuda")
+        self.ws_bytes = self.layer.workspace_bytes(t, self.mode)
+        self.ws = torch.empty(max(self.ws_bytes, 1), dtype=torch.uint8, device="cuda")
+        torch.cuda.synchronize()
+
+    def step(self):
+        L = self.lib._lib
+        raw, P, st = L.raw, L._ptr, L._stream()
+        rc = raw.moe_int4_ffn_forward(L.ctypes.byref(self.layer.desc), P(self.x), self.t, P(self.ids), P(self.w),
+                                      self.mode, P(self.out), P(self.ws), self.ws_bytes, st)
+        if rc:
+            raise L.Q4Error("moe_int4_ffn_forward", rc)
+
+
 def time_steps(torch, wl, steps, warmup, stage_events, graph=True):
     """Wall-clock per step over ``steps`` replays of a HIP graph holding one whole step
     (router + forward; the CPU launch cost of the ~10 kernels is then off the clock),
@@ -455,6 +488,21 @@ def main():
             c4 = time_cold(torch, lw, 20 if t > 1000 else 50) if not args.no_graph else None
             extra[f"lora8_T{t}_w4a16"] = lw.summary(s4, c4)
             del lw
+        for t in synth.CONFIGS["dense"]["tokens"]:
+            log(f"[bench] extra dense 2048/8192 FFN decode T={t}")
+            dw = DenseWorkload(lib, torch, synth, t, "w4a16")
+            sd, std = time_steps(torch, dw, 100, 10, stage_events=True, graph=not args.no_graph)
+            cd = time_cold(torch, dw, 100) if not args.no_graph else None
+            extra[f"dense_T{t}_w4a16"] = summarize(dw, sd, std, cd)
+            del dw
+        m8 = None
+        for t in (1, 16, 256):
+            log(f"[bench] extra moe8 decode T={t}")
+            m8 = Workload(lib, torch, synth, "moe8", t, "w4a16") if m8 is None else m8.retoken(synth, t)
+            s8, st8 = time_steps(torch, m8, 100, 10, stage_events=True, graph=not args.no_graph)
+            c8 = time_cold(torch, m8, 100) if not args.no_graph else None
+            extra[f"moe8_T{t}_w4a16"] = summarize(m8, s8, st8, c8)
+        del m8
         for mode in ("w4a8", "w8a8"):
             log(f"[bench] extra moe8 {mode} prefill T=2048")
             w8 = Workload(lib, torch, synth, "moe8_w4a8", 2048, mode)
