@@ -71,6 +71,7 @@ struct FwdWorkspace {
   int64_t bytes = 0;
   int32_t max_tiles = 0;
   int tile_rows = 16;
+  int ksplit = 1;   // K slices of the down projection (y holds ksplit partial slices)
 };
 
 bool int8_acts(int mode) { return mode == Q4_W4A8 || mode == Q4_W8A8; }
@@ -135,7 +136,15 @@ FwdWorkspace carve(const q4_moe_layer_t* L, int64_t t, int mode, void* base) {
   w.num_tiles = reinterpret_cast<int32_t*>(take(4));
   w.fmt_tiles = reinterpret_cast<int32_t*>(take(5 * 4));
   w.h = take(P * I * (int8_acts(mode) ? 4 : 2));
-  w.y = reinterpret_cast<float*>(take(P * H * 4));
+  // Decode down projections with few work items (narrow layers: the dense FFN, a few
+  // touched experts) split K over workgroups, aiming at about 512 items; the combine sums
+  // the partial slices in order.  Layers of one weight format only.
+  if (!w.prefill && w.tile_rows == 16 && !L->expert_bits && !L->expert_groups) {
+    const int64_t est = std::min<int64_t>(ee, P) * (H / 32);   // items of two column blocks, one tile per expert
+    const int64_t G = I / 128;
+    if (est > 0 && est < 512) w.ksplit = int(std::min<int64_t>({(512 + est - 1) / est, 8, std::max<int64_t>(1, G / 2)}));
+  }
+  w.y = reinterpret_cast<float*>(take(w.ksplit * P * H * 4));
   if (int8_acts(mode)) {
     w.qx = reinterpret_cast<int8_t*>(take(t * H));
     w.sx = reinterpret_cast<float*>(take(t * 4));
@@ -473,6 +482,8 @@ int ffn_forward(const q4_moe_layer_t* L, const uint16_t* x_bf16, int64_t t, cons
   dn.N = H;
   dn.K = I;
   dn.out = w.y;
+  dn.ksplit = views ? 1 : w.ksplit;   // the debug views show whole y rows
+  dn.out_slice = t * S * H;
   auto gemm1 = [&](const GemmArgs& g, int act, int kind) {
     return w.prefill ? launch_gemm_prefill(g, act, kind, stream) : launch_gemm(g, act, kind, rb, stream);
   };
@@ -556,7 +567,8 @@ int ffn_forward(const q4_moe_layer_t* L, const uint16_t* x_bf16, int64_t t, cons
     stage_end(Q4_STAGE_DOWN, stream);
   }
   stage_begin(Q4_STAGE_COMBINE, stream);
-  rc = check_hip(launch_combine(w.y, w.inv, topk_w, t, L->top_k, shared, H, out_bf16, stream), "combine");
+  rc = check_hip(launch_combine(w.y, w.inv, topk_w, t, L->top_k, shared, H, out_bf16, stream, dn.ksplit, dn.out_slice),
+                 "combine");
   stage_end(Q4_STAGE_COMBINE, stream);
   return rc;
 }

@@ -164,11 +164,16 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs args) {
     t_first = args.fmt_tiles[args.fmt];
     ntiles = args.fmt_tiles[args.fmt_end] - t_first;
   }
-  const int64_t items = ntiles * nblk;
+  // plain GEMM with few work items (the few-items configuration only): ksplit K slices per
+  // (tile, column blocks), each a work item of its own writing its partial sums to its own
+  // output slice; every other configuration compiles with ksplit = 1
+  constexpr bool kCanSplit = KIND == GEMM_PLAIN && MB == 1 && KW == 4 && NBW == 2;
+  const int ksplit = (kCanSplit && args.ksplit > 1) ? args.ksplit : 1;
+  const int64_t base_items = ntiles * nblk;
+  const int64_t items = base_items * ksplit;
+  const int64_t gslice = (G + ksplit - 1) / ksplit;
   const int64_t w_scale_off = align256(W8 ? N * K : N * K / 2);
   const int64_t w_zero_off = w_scale_off + align256(2 * N * G);   // zero points: one scale entry per tile
-  const int64_t gper = (G + KW - 1) / KW;
-  const int64_t g_beg = std::min<int64_t>(G, kw * gper), g_end = std::min<int64_t>(G, g_beg + gper);
   // LDS: scales [kCBWG][G][16] fp16 (one entry per tile; with SG > 1 entries per tile
   // each lane loads its column's entries with the weights instead), zero points
   // [kCBWG][G][16] u8, reduction buffer
@@ -178,8 +183,17 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs args) {
   float* s_red = reinterpret_cast<float*>(smem + scale_lds + (ASYM ? align256(int64_t(kCBWG) * G * 16) : 0));
 
   for (int64_t item = blockIdx.x; item < items; item += gridDim.x) {
-    const int64_t tile = t_first + item / nblk;
-    const int64_t cb0 = (item % nblk) * kCBWG;     // first column block of the workgroup
+    int64_t it = item, ks = 0;
+    if (ksplit > 1) {
+      ks = it / base_items;
+      it -= ks * base_items;
+    }
+    const int64_t tile = t_first + it / nblk;
+    const int64_t cb0 = (it % nblk) * kCBWG;     // first column block of the workgroup
+    // this item's groups [kg0, kg1), shared out over the KW waves of a column group
+    const int64_t kg0 = std::min<int64_t>(G, ks * gslice), kg1 = std::min<int64_t>(G, kg0 + gslice);
+    const int64_t gper = (kg1 - kg0 + KW - 1) / KW;
+    const int64_t g_beg = std::min<int64_t>(kg1, kg0 + kw * gper), g_end = std::min<int64_t>(kg1, g_beg + gper);
     int32_t expert = 0;
     int64_t row_start, rows;
     if (args.tiles) {
@@ -487,7 +501,8 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs args) {
             if constexpr (KIND == GEMM_PLAIN) {
 #pragma unroll
               for (int nb = 0; nb < NBW; ++nb)
-                static_cast<float*>(args.out)[pos * N + (cb0 + lcb + nb) * 16 + col] = acc[mb][nb][i] * sa;
+                static_cast<float*>(args.out)[ks * args.out_slice + pos * N + (cb0 + lcb + nb) * 16 + col] =
+                    acc[mb][nb][i] * sa;
             } else {
               // device blocks alternate gate_j, up_j: pair p -> h columns of block (cb0 + lcb) / 2 + p
               const int64_t I = N / 2;
@@ -538,7 +553,8 @@ static hipError_t launch_cfg(const GemmArgs& g, hipStream_t st) {
   const int64_t nblk = g.N / (16 * cbwg);
   const int64_t trows = 16 * MB;
   const int64_t max_tiles = g.tiles ? g.max_tiles : (g.dense_rows + trows - 1) / trows;
-  const int64_t items = max_tiles * nblk;
+  constexpr bool can_split = KIND == GEMM_PLAIN && MB == 1 && KW == 4 && NBW == 2;
+  const int64_t items = max_tiles * nblk * ((can_split && g.ksplit > 1) ? g.ksplit : 1);
   if (items == 0) return hipSuccess;
 #ifndef Q4_GRID_CAP
 #define Q4_GRID_CAP (256 * 16)
@@ -611,6 +627,17 @@ static hipError_t launch_kind(const GemmArgs& g, int rb, int split, hipStream_t 
 }
 
 hipError_t launch_gemm(const GemmArgs& g, int act, int kind, int row_blocks, hipStream_t st) {
+  // K slices: plain GEMM on 16-row tiles only, in the few-items configuration (the one
+  // that implements them); each output slice holds the a_rows rows
+  if (g.ksplit > 1) {
+    if (kind != GEMM_PLAIN || row_blocks != 1 || g.N % 32 != 0 || g.out_slice < g.a_rows * g.N || g.ebits ||
+        g.egroups)
+      return hipErrorInvalidValue;
+    if (act == 0) return launch_cfg<Act::BF16, GEMM_PLAIN, 1, 4, 2, 2>(g, st);
+    if (act == 1) return launch_cfg<Act::F16, GEMM_PLAIN, 1, 4, 2, 2>(g, st);
+    if (g.wbits == 8) return launch_cfg<Act::I8, GEMM_PLAIN, 1, 4, 2, 2, true>(g, st);
+    return launch_cfg<Act::I8, GEMM_PLAIN, 1, 4, 2, 2>(g, st);
+  }
   // few tiles (small batches): split K over the 4 waves for more waves in flight
   const int64_t est_items = (g.tiles ? std::min<int64_t>(g.max_tiles, 64) : 1) * (g.N / 128);
   const int split = est_items < 1024 ? 1 : 0;
@@ -630,16 +657,32 @@ hipError_t launch_gemm(const GemmArgs& g, int act, int kind, int row_blocks, hip
 }
 
 // ------------------------------------------------------------------ A9 combine
-// out[t][n] = bf16( sum_{j<k, ascending} w[t][j] * y[inv[t S + j]][n] (+ y[inv[t S + k]][n]) )
+// out[t][n] = bf16( sum_{j<k, ascending} w[t][j] * y[inv[t S + j]][n] (+ y[inv[t S + k]][n]) ),
+// with y = the sum of the ksplit slices y + s * slice in slice order when the down
+// projection split K (SPLIT)
+template <bool SPLIT>
 __global__ void __launch_bounds__(256) k_combine(const float* __restrict__ y, const int32_t* __restrict__ inv,
                                                  const float* __restrict__ w, int64_t t, int32_t k, int shared,
-                                                 int64_t h, uint16_t* __restrict__ out) {
+                                                 int64_t h, uint16_t* __restrict__ out, int ksplit, int64_t slice) {
   const int64_t per_tok = h / 4;
   const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
   if (i >= t * per_tok) return;
   const int64_t tok = i / per_tok;
   const int64_t c = (i - tok * per_tok) * 4;
   const int S = k + shared;
+  auto row = [&](int64_t pos) {
+    float4 v = *reinterpret_cast<const float4*>(y + pos * h + c);
+    if constexpr (SPLIT) {
+      for (int s = 1; s < ksplit; ++s) {
+        const float4 u = *reinterpret_cast<const float4*>(y + s * slice + pos * h + c);
+        v.x += u.x;
+        v.y += u.y;
+        v.z += u.z;
+        v.w += u.w;
+      }
+    }
+    return v;
+  };
   float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
   // eight slots at a time: all index / weight loads, then all row loads, then the sums
   // in slot order
@@ -655,8 +698,7 @@ __global__ void __launch_bounds__(256) k_combine(const float* __restrict__ y, co
       wj[u] = ok ? w[tok * k + j0 + u] : 0.f;
     }
 #pragma unroll
-    for (int u = 0; u < U; ++u)
-      v[u] = j0 + u < k ? *reinterpret_cast<const float4*>(y + pos[u] * h + c) : make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int u = 0; u < U; ++u) v[u] = j0 + u < k ? row(pos[u]) : make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (j0 + u < k) {
@@ -668,8 +710,7 @@ __global__ void __launch_bounds__(256) k_combine(const float* __restrict__ y, co
     }
   }
   if (shared) {
-    const int64_t pos = inv[tok * S + k];
-    const float4 v = *reinterpret_cast<const float4*>(y + pos * h + c);
+    const float4 v = row(inv[tok * S + k]);
     a0 += v.x;
     a1 += v.y;
     a2 += v.z;
@@ -681,10 +722,14 @@ __global__ void __launch_bounds__(256) k_combine(const float* __restrict__ y, co
 }
 
 hipError_t launch_combine(const float* y, const int32_t* inv, const float* w, int64_t t, int32_t k, int shared,
-                          int64_t h, uint16_t* out, hipStream_t st) {
+                          int64_t h, uint16_t* out, hipStream_t st, int ksplit, int64_t slice) {
   const int64_t n = t * (h / 4);
   if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_combine, dim3(unsigned((n + 255) / 256)), dim3(256), 0, st, y, inv, w, t, k, shared, h, out);
+  const dim3 grid(unsigned((n + 255) / 256));
+  if (ksplit > 1)
+    hipLaunchKernelGGL(k_combine<true>, grid, dim3(256), 0, st, y, inv, w, t, k, shared, h, out, ksplit, slice);
+  else
+    hipLaunchKernelGGL(k_combine<false>, grid, dim3(256), 0, st, y, inv, w, t, k, shared, h, out, 1, int64_t(0));
   return hipGetLastError();
 }
 

@@ -80,6 +80,8 @@ struct GemmArgs {
   int64_t dense_rows;
   // outputs
   void* out;              // gate/up: h [rows][N/2] (bf16, or fp32 in int8 mode); else fp32 [rows][N]
+  int32_t ksplit;         // plain decode GEMM: K split over this many workgroups (0 / 1: none);
+  int64_t out_slice;      //   slice s (groups [s G/ksplit, (s+1) G/ksplit)) writes out + s * out_slice
   int32_t* acc_out;       // debug: int32 [rows][N][G] group accumulators (int8 mode, plain)
 };
 
@@ -113,6 +115,6 @@ int lora_kchunks(int64_t h);       // K chunks (512 wide) of the adapter input p
 int lora_col_blocks(int64_t inter);  // column blocks of the SwiGLU / down-projection kernel
 
 hipError_t launch_combine(const float* y, const int32_t* inv, const float* w, int64_t t, int32_t k, int shared,
-                          int64_t h, uint16_t* out, hipStream_t st);
+                          int64_t h, uint16_t* out, hipStream_t st, int ksplit = 1, int64_t slice = 0);
 
 }  // namespace q4

@@ -130,6 +130,20 @@ def test_forward_validation(L):
     assert r.moe_int4_ffn_workspace_bytes(None, 10, 0) == 0
 
 
+def test_forward_workspace_sizes(L):
+    """Host sizing only: zero tokens, and the K-split partial slices of y that narrow
+    decode layers get (a one-expert 2048/8192 FFN at t = 1: eight slices of 2048 fp32)."""
+    r = L.raw
+    for mode in (0, 1):
+        assert r.moe_int4_ffn_workspace_bytes(ctypes.byref(_layer(L)), 0, mode) >= 0
+    dense = _layer(L, num_experts=1, top_k=1, hidden=2048, inter=8192)
+    need = r.moe_int4_ffn_workspace_bytes(ctypes.byref(dense), 1, 0)
+    assert need >= 8 * 2048 * 4 + 8192 * 2
+    wide = _layer(L, num_experts=256, top_k=8, hidden=7168, inter=2048)
+    # 64 tokens: enough work items, one slice (y of 512 positions x 7168 fp32)
+    assert r.moe_int4_ffn_workspace_bytes(ctypes.byref(wide), 64, 0) < 2 * 512 * 7168 * 4 + 512 * 2048 * 2 + (1 << 20)
+
+
 def test_linear_and_group_acc_validation(L):
     r = L.raw
     fake = ctypes.c_void_p(4096)
