@@ -285,7 +285,10 @@ typedef struct q4_moe_layer_t {
  *   INT32 accumulation per group of int8(x) * (q - z); y = s_x * sum_g s_w * acc.
  * W8A8 (layer weight_bits == 8): the same with the 8-bit codes q.
  * The combine adds the k routed outputs in ascending j in fp32, then the shared
- * expert, then rounds to bf16.  A dense SwiGLU FFN is the case num_experts = 1,
+ * expert, then rounds to bf16.  For narrow layers at small t (touched experts x H / 32
+ * under 512 work items) the down projection splits K over up to 8 workgroups and each
+ * routed output is the fp32 sum of its slices, in slice order (the workspace holds the
+ * slices).  A dense SwiGLU FFN is the case num_experts = 1,
  * top_k = 1, topk_w = 1.
  *
  *  x_bf16   device [t][H] bf16; out_bf16 device [t][H] bf16 (may not alias x).
