@@ -247,28 +247,33 @@ class DenseWorkload(Workload):
 
 
 def time_steps(torch, wl, steps, warmup, stage_events, graph=True):
-    """Wall-clock per step over ``steps`` replays of a HIP graph holding one whole step
-    (router + forward; the CPU launch cost of the ~10 kernels is then off the clock),
-    bracketed by device synchronisation.  ``stage_events``: a second, eager pass of the
-    same number of steps with HIP events around each stage (recorded by the library on
-    its stream), for the per-kernel averages."""
+    """Wall-clock per step over ``steps`` whole steps (router + forward) run from a HIP
+    graph that holds ``per`` consecutive steps (10, 5, 2 or 1, dividing ``steps``), as a
+    model's graph holds its layers one after another: the CPU launch cost of the kernels
+    and the graph launch itself are then off the per-step clock; bracketed by device
+    synchronisation.  ``stage_events``: a second, eager pass of the same number of steps
+    with HIP events around each stage (recorded by the library on its stream), for the
+    per-kernel averages."""
     lib = wl.lib
     for _ in range(warmup):
         wl.step()
     torch.cuda.synchronize()
     g = None
+    per = next(p for p in (10, 5, 2, 1) if steps % p == 0)
     if graph:
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            wl.step()
-        for _ in range(max(warmup, 1)):
+            for _ in range(per):
+                wl.step()
+        for _ in range(max(warmup // per, 1)):
             g.replay()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(steps):
-        if g is not None:
+    if g is not None:
+        for _ in range(steps // per):
             g.replay()
-        else:
+    else:
+        for _ in range(steps):
             wl.step()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
