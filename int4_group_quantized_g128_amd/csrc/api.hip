@@ -103,7 +103,8 @@ int row_blocks_for(const q4_moe_layer_t* L, int64_t t) {
   return 4;
 }
 
-// The 128-row prefill kernel from 64 rows per expert on average, and from 17 when the
+// The 128-row prefill kernel from 64 rows per expert on average, and from 17 (9 with
+// INT8 activations; bf16 measured slower there: T = 512 1.84 -> 2.03 ms) when the
 // launch has enough work items for its tiles to fill the chip several times (estimated
 // gate/up items >= 2048): 256-expert layer T = 768 / 1024 / 1536 W4A16 2.29 / 2.79 /
 // 4.83 -> 2.18 / 2.36 / 2.87 ms, W4A8 T = 1280 4.38 -> 1.88 ms; small layers (the
@@ -114,7 +115,8 @@ bool use_prefill(const q4_moe_layer_t* L, int64_t t, int mode) {
   const int64_t P = t * S, ee = int64_t(L->num_experts) + (L->shared_inter > 0 ? 1 : 0);
   const int64_t pf_items = (std::min<int64_t>(ee, P) + P / 128) * (2 * int64_t(L->inter) / 128);
   const double avg = avg_rows(L, t);
-  return (avg >= 64 || (avg > 16 && pf_items >= 2048)) && (2 * int64_t(L->inter)) % 128 == 0 && L->hidden % 128 == 0 &&
+  const double lo = act == 2 ? 8 : 16;   // INT8 activations: from 9 rows (T = 512: 1.78 -> 1.51 ms)
+  return (avg >= 64 || (avg > lo && pf_items >= 2048)) && (2 * int64_t(L->inter)) % 128 == 0 && L->hidden % 128 == 0 &&
          prefill_fits(t, L->hidden, act, mat_bytes(L, 2 * L->inter, L->hidden)) &&
          prefill_fits(t * S, L->inter, act, mat_bytes(L, L->hidden, L->inter));
 }

@@ -149,10 +149,10 @@ def test_prefill_t4096_w4a8(lib, wl4, oracle_experts):
     _check(lib, wl4.retoken(synth, 4096, "w4a8"), "w4a8", oracle_experts, 2, 5)
 
 
-@pytest.mark.parametrize("t,mode", [(768, "w4a16"), (1280, "w4a8")])
+@pytest.mark.parametrize("t,mode", [(768, "w4a16"), (1280, "w4a8"), (512, "w4a8")])
 def test_prefill_kernel_below_64_rows_per_expert(lib, wl4, oracle_experts, t, mode):
-    """24 and 40 routed rows per expert on average: enough work items that the forward
-    takes the 128-row prefill kernel (mostly partly filled tiles)."""
+    """24, 40 and 16 routed rows per expert on average: enough work items that the
+    forward takes the 128-row prefill kernel (mostly partly filled tiles)."""
     _check(lib, wl4.retoken(synth, t, mode), mode, oracle_experts, 2, 6 + t)
 
 
