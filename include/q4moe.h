@@ -113,8 +113,11 @@ Q4_API int quantize_int4_g128(const void* w, int w_dtype, int64_t n, int64_t k, 
 
 /*
  * q4_device_bytes / q4_repack_device -- A2: canonical layout -> device tile layout.
- * The device layout is a fixed permutation of the canonical bytes (plus one
- * byte per (column, group) for asymmetric zero points):
+ * The pages fix only the canonical format (quantize_int4_g128); the device layout is
+ * this library's own specification, made for the gfx950 kernels: 128-bit coalesced
+ * loads, one 1 KB tile per wave load, nibble order matched to the register widening.
+ * It is a fixed permutation of the canonical bytes (plus one byte per (column,
+ * group) for asymmetric zero points):
  *  - columns: PLAIN keeps order; GATE_UP takes [gate; up] (n = 2I rows) and places
  *    gate rows [16b, 16b+16) in device block 2b, up rows [I+16b, I+16b+16) in 2b+1;
  *  - nibble value d = q + 8 (symmetric) or q (asymmetric);
@@ -204,7 +207,12 @@ Q4_API int moe_route_topk(const uint16_t* x_bf16, const float* w_router, const f
                    float* topk_w, void* workspace, size_t ws_bytes, hipStream_t stream);
 
 /*
- * moe_permute -- A5: group the t*k routed slots (slot s = t_idx * k + j) by expert.
+ * moe_permute -- A5: group the t*k routed slots (slot s = t_idx * k + j) by expert
+ * (page "MoE推理优化实战：4bit存储+INT8计算的W4A8路线解析", §1: routing dispatch sends
+ * each token to its chosen experts and the results are combined afterwards; page
+ * "大模型之Dense、MoE与量化", MoE section: the chosen experts process the token).  The
+ * expert-grouped order lets each expert's rows be processed as one GEMM; the stable
+ * order within an expert is this library's choice (any order is correct).
  *  ids     device [t][k] int32 in [0, e).
  *  counts  device [e] int32: slots per expert.
  *  offsets device [e + 1] int32: exclusive prefix sum of counts.
@@ -304,18 +312,29 @@ Q4_API int moe_int4_ffn_forward(const q4_moe_layer_t* layer, const uint16_t* x_b
                          hipStream_t stream);
 
 /*
- * moe_int4_ffn_debug -- moe_int4_ffn_forward (same arguments, same results) that
- * also returns views of its intermediates, for stage-by-stage parity checks: the
- * INT8 codes and scales of x and h (page "MoE推理优化实战：4bit存储+INT8计算的W4A8路线解析"
- * §3, per-token activation quantisation) and the per-position expert outputs before
- * the weighted combine (page "大模型之Dense、MoE与量化", MoE section).
+ * moe_int4_ffn_debug -- moe_int4_ffn_forward (same arguments, the same launches and
+ * the same results) that also returns views of its intermediates, for stage-by-stage
+ * parity checks: the INT8 codes and scales of x and h (page "MoE推理优化实战：4bit存储+
+ * INT8计算的W4A8路线解析" §3, per-token activation quantisation) and the per-position
+ * expert outputs before the weighted combine (page "大模型之Dense、MoE与量化", MoE
+ * section).
  * On success `views` points into `workspace` (valid once the stream has executed the
  * call, until the workspace is reused); P = t * slots_per_token positions, position
  * p holds slot perm[p] = token * slots_per_token + j (j == top_k: the shared expert):
  *   counts [E + shared] int32, offsets [E + shared + 1] int32, perm / inv [P] int32;
  *   h   [P][I]: silu(gate) * up per position, bf16 (W4A16) or fp32 (W4A8);
- *   y   [P][H] fp32: the down projection per position;
+ *   y   [y_slices][P][H] fp32: the down projection per position, as y_slices partial
+ *       sums over consecutive K ranges of y_slice_groups groups each (y_slices == 1
+ *       except where the forward splits the down projection's K, see
+ *       moe_int4_ffn_forward); the routed output of a position is the fp32 sum of its
+ *       slices in slice order;
  *   q_x [t][H] int8, s_x [t] fp32, q_h [P][I] int8, s_h [P] fp32 (W4A8; NULL in W4A16).
+ * The gate and up products before SwiGLU are not stored by the fused kernel; the same
+ * GEMM core gives them on the forward's own inputs: int4_linear_forward (W4A16, fp32
+ * g and u) and int4_w4a8_group_acc (the INT32 group accumulators of either GEMM) on an
+ * expert's gate/up or down block of the layer (a Q4_REPACK_GATE_UP block is read as a
+ * PLAIN [2I][H] matrix whose 16-column block 2b holds gate rows 16b.., block 2b + 1
+ * up rows 16b..).
  * views == NULL -> Q4_ERR_NULL; on any error *views is zeroed.
  */
 typedef struct q4_ffn_views_t {
@@ -332,11 +351,64 @@ typedef struct q4_ffn_views_t {
   const float* s_x;
   const int8_t* q_h;
   const float* s_h;
+  int32_t y_slices;        /* K slices of the down projection held in y (1: whole rows) */
+  int32_t y_slice_groups;  /* groups of 128 per slice: slice s covers groups
+                              [s * y_slice_groups, min(I / 128, (s + 1) * y_slice_groups)) */
+  int64_t y_slice_stride;  /* floats between slices (= positions * H) */
 } q4_ffn_views_t;
 Q4_API int moe_int4_ffn_debug(const q4_moe_layer_t* layer, const uint16_t* x_bf16, int64_t t,
                        const int32_t* topk_ids, const float* topk_w, int mode,
                        uint16_t* out_bf16, void* workspace, size_t ws_bytes,
                        q4_ffn_views_t* views, hipStream_t stream);
+
+/*
+ * moe_int4_ffn_plan -- host-only query of the launch plan moe_int4_ffn_forward uses
+ * for (layer, t, mode); no device work, no pointer is dereferenced except layer.
+ *  kernel         Q4_PLAN_DECODE: the streaming GEMM kernel with 16 / 32 / 64-row tiles
+ *                 (tile_rows), or Q4_PLAN_PREFILL: the 128-row matrix-core tiles staged
+ *                 through LDS.  The prefill tiles are chosen from 64 routed rows per
+ *                 expert on average, or from 17 (9 with INT8 activations) when the
+ *                 launch has at least 2048 estimated gate/up work items, but only where
+ *                 every activation buffer of the launch is below 2^31 bytes (the
+ *                 prefill kernels address activations with 32-bit buffer offsets);
+ *                 beyond that the decode kernel (64-bit addressing) runs and
+ *                 prefill_addr_limited is 1.
+ *  down_ksplit    K slices of the down projection (1: none).
+ *  workspace_bytes moe_int4_ffn_workspace_bytes(layer, t, mode).
+ * Errors as moe_int4_ffn_forward's validation (the layer's device pointers are checked
+ * for NULL and alignment only).
+ */
+#define Q4_PLAN_DECODE 0
+#define Q4_PLAN_PREFILL 1
+typedef struct q4_ffn_plan_t {
+  int32_t kernel;
+  int32_t tile_rows;
+  int32_t down_ksplit;
+  int32_t prefill_addr_limited;
+  int64_t workspace_bytes;
+} q4_ffn_plan_t;
+Q4_API int moe_int4_ffn_plan(const q4_moe_layer_t* layer, int64_t t, int mode, q4_ffn_plan_t* plan);
+
+/*
+ * moe_expert_bits_by_hotness / moe_expert_groups_by_hotness -- per-expert weight format
+ * from routing hit counts (host arrays; counts[e] = routed slots of expert e over a
+ * calibration batch, e.g. the counts moe_permute returns).  Page "MoE推理优化实战：4bit存储
+ * +INT8计算的W4A8路线解析", §5.3: the most frequently hit experts, its top 5 %, keep more
+ * precision (finer groups); ordinary experts groups of 64; experts almost no token
+ * reaches 128 or even 256; §6.1: a W8 / W4 choice per expert; page "大模型之Dense、MoE与
+ * 量化", APEX: expert precision by importance.  Hit counts stand in for importance.
+ *  bits:   the ceil(frac8 * e) most-hit experts (equal counts: lower index first) 8,
+ *          the others 4; with shared != 0 one more entry, 8, for the shared expert
+ *          (hit by every token).
+ *  groups: the ceil(hot_frac * e) most-hit experts 32; of the others, experts with
+ *          counts[i] * e < cold_share * sum(counts) 256, the rest 64; shared: 32.
+ *  The ceil is of (fraction * e - 1e-9) in double precision.  Output arrays hold
+ *  e + (shared != 0) entries.  Requires 1 <= e <= 4096, counts >= 0, fractions in
+ *  [0, 1], cold_share >= 0.
+ */
+Q4_API int moe_expert_bits_by_hotness(const int64_t* counts, int32_t e, double frac8, int shared, int32_t* bits_out);
+Q4_API int moe_expert_groups_by_hotness(const int64_t* counts, int32_t e, double hot_frac, double cold_share,
+                                        int shared, int32_t* groups_out);
 
 /*
  * q4_lora_layer_t / moe_lora_ffn_forward -- LoRA-mode experts (page
@@ -382,7 +454,11 @@ Q4_API int moe_lora_ffn_forward(const q4_lora_layer_t* layer, const uint16_t* x_
 
 /*
  * int4_linear_forward -- one INT4 g128 linear y = x W_hat^T (fp32 output), the
- * W4A16 core on a plain token matrix.
+ * W4A16 core on a plain token matrix (page "从FP32到INT4：大语言模型量化压缩实战指南",
+ * §1.3: a linear layer's weight quantised in groups of 128 along K, each group
+ * dequantised with its own scale and zero point; page "MoE推理优化实战：4bit存储+INT8
+ * 计算的W4A8路线解析", §2.1: W4A16 keeps activations in 16 bits and dequantises the
+ * 4-bit weights for the product).
  *  x      device [t][k], dtype Q4_F16 or Q4_BF16.
  *  w_dev  device layout (Q4_REPACK_PLAIN) of an [n][k] matrix.
  *  y      device [t][n] fp32.

@@ -62,7 +62,14 @@ class Q4FfnViews(ctypes.Structure):
         ("counts", _vp), ("offsets", _vp), ("perm", _vp), ("inv", _vp), ("h", _vp),
         ("h_is_f32", _i32), ("slots_per_token", _i32), ("positions", _i64),
         ("y", _vp), ("q_x", _vp), ("s_x", _vp), ("q_h", _vp), ("s_h", _vp),
+        ("y_slices", _i32), ("y_slice_groups", _i32), ("y_slice_stride", _i64),
     ]
+
+
+class Q4FfnPlan(ctypes.Structure):
+    """Mirror of q4_ffn_plan_t."""
+    _fields_ = [("kernel", _i32), ("tile_rows", _i32), ("down_ksplit", _i32), ("prefill_addr_limited", _i32),
+                ("workspace_bytes", _i64)]
 
 
 def _sig(name, res, args):
@@ -98,6 +105,10 @@ _sig("moe_lora_ffn_forward", _int, [ctypes.POINTER(Q4LoraLayer), _vp, _i64, _vp,
 _sig("int4_linear_forward", _int, [_vp, _int, _i64, _i64, _vp, _i64, _int, _vp, _vp])
 _sig("int4_w4a8_group_acc", _int, [_vp, _i64, _i64, _vp, _i64, _int, _vp, _vp])
 
+_sig("moe_int4_ffn_plan", _int, [ctypes.POINTER(Q4MoELayer), _i64, _int, ctypes.POINTER(Q4FfnPlan)])
+_sig("moe_expert_bits_by_hotness", _int, [ctypes.POINTER(_i64), _i32, ctypes.c_double, _int, ctypes.POINTER(_i32)])
+_sig("moe_expert_groups_by_hotness", _int, [ctypes.POINTER(_i64), _i32, ctypes.c_double, ctypes.c_double, _int,
+                                            ctypes.POINTER(_i32)])
 _sig("q4_set_stage_events", _int, [ctypes.POINTER(_vp), ctypes.POINTER(_vp), _int])
 
 raw = _lib  # the C entry points, for tests of the ABI itself
@@ -301,42 +312,36 @@ def act_quant_int8(x):
 
 
 # ------------------------------------------------------------------ layer + forward
-def expert_bits_by_hotness(counts, frac8=0.05, shared=False):
-    """Per-expert weight bit widths from routing hit counts: the ceil(frac8 * E) most-hit
-    experts get 8 bits, the rest 4 (equal counts: the lower expert index first).  With a
-    shared expert (used by every token, so the hottest) one more entry, 8, follows.
-    Page "MoE推理优化实战：4bit存储+INT8计算的W4A8路线解析", §5.3 (the top 5 % most-hit
-    experts keep more precision) and §6.1 (per-expert W8 / W4 assignment); page
-    "大模型之Dense、MoE与量化", APEX (precision by expert importance)."""
+def _hotness(name, counts, shared, *fracs):
     counts = [int(c) for c in counts]
     e = len(counts)
-    if not 0.0 <= frac8 <= 1.0:
-        raise ValueError("frac8 must lie in [0, 1]")
-    n8 = min(e, int(math.ceil(frac8 * e - 1e-9)))
-    hot = sorted(range(e), key=lambda i: (-counts[i], i))[:n8]
-    bits = [4] * e
-    for i in hot:
-        bits[i] = 8
-    return bits + ([8] if shared else [])
+    out = (_i32 * (e + (1 if shared else 0)))()
+    _check(name, getattr(_lib, name)((_i64 * e)(*counts), e, *fracs, int(bool(shared)), out))
+    return list(out)
+
+
+def expert_bits_by_hotness(counts, frac8=0.05, shared=False):
+    """Per-expert weight widths (4 or 8) from routing hit counts; the rule is the C
+    library's moe_expert_bits_by_hotness (host arrays, no device work)."""
+    return _hotness("moe_expert_bits_by_hotness", counts, shared, float(frac8))
 
 
 def expert_groups_by_hotness(counts, hot_frac=0.05, cold_share=0.1, shared=False):
-    """Per-expert group sizes from routing hit counts (page "MoE推理优化实战：4bit存储+
-    INT8计算的W4A8路线解析", §5.3: groups of 32 for the most-hit experts, 64 for ordinary
-    ones, 128 or 256 for experts almost no token reaches): the ceil(hot_frac * E)
-    most-hit experts (equal counts: lower index first) 32, experts hit less than
-    cold_share times the even share (total / E) 256, the others 64; with a shared
-    expert (hit by every token) one more entry, 32."""
-    counts = [int(c) for c in counts]
-    e = len(counts)
-    if not 0.0 <= hot_frac <= 1.0:
-        raise ValueError("hot_frac must lie in [0, 1]")
-    total = sum(counts)
-    groups = [256 if c * e < cold_share * total else 64 for c in counts]
-    n_hot = min(e, int(math.ceil(hot_frac * e - 1e-9)))
-    for i in sorted(range(e), key=lambda i: (-counts[i], i))[:n_hot]:
-        groups[i] = 32
-    return groups + ([32] if shared else [])
+    """Per-expert group sizes (32, 64 or 256) from routing hit counts; the rule is the C
+    library's moe_expert_groups_by_hotness (host arrays, no device work)."""
+    return _hotness("moe_expert_groups_by_hotness", counts, shared, float(hot_frac), float(cold_share))
+
+
+def moe_int4_ffn_plan(layer, t, mode):
+    """Launch plan of moe_int4_ffn_forward for (layer, t, mode): a dict with kernel
+    ("decode" / "prefill"), tile_rows, down_ksplit, prefill_addr_limited, workspace_bytes.
+    ``layer`` is a MoELayer or a Q4MoELayer descriptor."""
+    desc = layer.desc if hasattr(layer, "desc") else layer
+    p = Q4FfnPlan()
+    _check("moe_int4_ffn_plan", _lib.moe_int4_ffn_plan(ctypes.byref(desc), t, mode, ctypes.byref(p)))
+    return {"kernel": "prefill" if p.kernel == 1 else "decode", "tile_rows": p.tile_rows,
+            "down_ksplit": p.down_ksplit, "prefill_addr_limited": bool(p.prefill_addr_limited),
+            "workspace_bytes": int(p.workspace_bytes)}
 
 
 class MoELayer:
@@ -518,7 +523,10 @@ def moe_int4_ffn_debug(layer, x, ids, weights, mode=Q4_W4A16):
         "perm": view(v.perm, torch.int32, (P,)),
         "inv": view(v.inv, torch.int32, (P,)),
         "h": view(v.h, torch.float32 if v.h_is_f32 else torch.bfloat16, (P, I)),
-        "y": view(v.y, torch.float32, (P, H)),
+        "y_slices": int(v.y_slices),
+        "y_slice_groups": int(v.y_slice_groups),
+        # [y_slices][P][H]: partial sums over consecutive K ranges (one slice: whole rows)
+        "y": view(v.y, torch.float32, (int(v.y_slices), P, H)),
         "q_x": view(v.q_x, torch.int8, (t, H)),
         "s_x": view(v.s_x, torch.float32, (t,)),
         "q_h": view(v.q_h, torch.int8, (P, I)),

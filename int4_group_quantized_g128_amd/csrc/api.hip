@@ -4,6 +4,8 @@
 #include <cstdio>
 #include <cstring>
 #include <string>
+#include <cmath>
+#include <vector>
 
 #include "../../include/q4moe.h"
 #include "internal.h"
@@ -109,15 +111,26 @@ int row_blocks_for(const q4_moe_layer_t* L, int64_t t) {
 // gate/up items >= 2048): 256-expert layer T = 768 / 1024 / 1536 W4A16 2.29 / 2.79 /
 // 4.83 -> 2.18 / 2.36 / 2.87 ms, W4A8 T = 1280 4.38 -> 1.88 ms; small layers (the
 // 8-expert one at 48 rows per expert) stay faster on the decode kernel's 64-row tiles.
-bool use_prefill(const q4_moe_layer_t* L, int64_t t, int mode) {
+// The row-count rule alone (wants_prefill) and with the prefill kernels' 32-bit buffer
+// offsets (use_prefill: every activation buffer of both launches below 2^31 bytes; past
+// that the decode kernel, which addresses with 64-bit offsets, runs instead).
+bool wants_prefill(const q4_moe_layer_t* L, int64_t t, int mode) {
   const int act = int8_acts(mode) ? 2 : 0;
   const int64_t S = L->top_k + (L->shared_inter > 0 ? 1 : 0);
   const int64_t P = t * S, ee = int64_t(L->num_experts) + (L->shared_inter > 0 ? 1 : 0);
   const int64_t pf_items = (std::min<int64_t>(ee, P) + P / 128) * (2 * int64_t(L->inter) / 128);
   const double avg = avg_rows(L, t);
   const double lo = act == 2 ? 8 : 16;   // INT8 activations: from 9 rows (T = 512: 1.78 -> 1.51 ms)
-  return (avg >= 64 || (avg > lo && pf_items >= 2048)) && (2 * int64_t(L->inter)) % 128 == 0 && L->hidden % 128 == 0 &&
-         prefill_fits(t, L->hidden, act, mat_bytes(L, 2 * L->inter, L->hidden)) &&
+  // the lower thresholds were measured on layers of one weight format only
+  const bool uniform = !L->expert_bits && !L->expert_groups;
+  return (avg >= 64 || (uniform && avg > lo && pf_items >= 2048)) && (2 * int64_t(L->inter)) % 128 == 0 &&
+         L->hidden % 128 == 0;
+}
+
+bool use_prefill(const q4_moe_layer_t* L, int64_t t, int mode) {
+  const int act = int8_acts(mode) ? 2 : 0;
+  const int64_t S = L->top_k + (L->shared_inter > 0 ? 1 : 0);
+  return wants_prefill(L, t, mode) && prefill_fits(t, L->hidden, act, mat_bytes(L, 2 * L->inter, L->hidden)) &&
          prefill_fits(t * S, L->inter, act, mat_bytes(L, L->hidden, L->inter));
 }
 
@@ -152,7 +165,12 @@ FwdWorkspace carve(const q4_moe_layer_t* L, int64_t t, int mode, void* base) {
   if (!w.prefill && w.tile_rows == 16 && !L->expert_bits && !L->expert_groups) {
     const int64_t est = std::min<int64_t>(ee, P) * (H / 32);   // items of two column blocks, one tile per expert
     const int64_t G = I / 128;
-    if (est > 0 && est < 512) w.ksplit = int(std::min<int64_t>({(512 + est - 1) / est, 8, std::max<int64_t>(1, G / 2)}));
+    if (est > 0 && est < 512) {
+      const int64_t ks = std::min<int64_t>({(512 + est - 1) / est, 8, std::max<int64_t>(1, G / 2)});
+      // as many slices as the ceil(G / ks)-group slices need: none is left empty
+      const int64_t per = (G + ks - 1) / ks;
+      w.ksplit = int((G + per - 1) / per);
+    }
   }
   w.y = reinterpret_cast<float*>(take(w.ksplit * P * H * 4));
   if (int8_acts(mode)) {
@@ -416,6 +434,75 @@ size_t moe_int4_ffn_workspace_bytes(const q4_moe_layer_t* layer, int64_t t, int 
   return size_t(carve(layer, t, mode, nullptr).bytes);
 }
 
+int moe_int4_ffn_plan(const q4_moe_layer_t* L, int64_t t, int mode, q4_ffn_plan_t* plan) {
+  g_last_error.clear();
+  Q4_REQUIRE(plan, Q4_ERR_NULL, "plan is NULL");
+  *plan = q4_ffn_plan_t{};
+  if (int rc = validate_layer(L)) return rc;
+  Q4_REQUIRE(mode_ok(L, mode), Q4_ERR_DTYPE, "mode %d does not match the layer's weight format", mode);
+  Q4_REQUIRE(t >= 0, Q4_ERR_SHAPE, "t < 0");
+  const FwdWorkspace w = carve(L, t, mode, nullptr);
+  plan->kernel = w.prefill ? Q4_PLAN_PREFILL : Q4_PLAN_DECODE;
+  plan->tile_rows = w.tile_rows;
+  plan->down_ksplit = w.ksplit;
+  plan->prefill_addr_limited = (!w.prefill && wants_prefill(L, t, mode)) ? 1 : 0;
+  plan->workspace_bytes = w.bytes;
+  return ok();
+}
+
+extern "C++" {  // internal helpers keep C++ linkage
+namespace {
+
+// Experts ordered by hit count, descending; equal counts keep the lower index first.
+std::vector<int32_t> by_hotness(const int64_t* counts, int32_t e) {
+  std::vector<int32_t> order(e);
+  for (int32_t i = 0; i < e; ++i) order[i] = i;
+  std::stable_sort(order.begin(), order.end(), [&](int32_t a, int32_t b) { return counts[a] > counts[b]; });
+  return order;
+}
+
+int check_counts(const int64_t* counts, int32_t e, const void* out) {
+  Q4_REQUIRE(counts && out, Q4_ERR_NULL, "counts and the output array are required");
+  Q4_REQUIRE(e >= 1 && e <= 4096, Q4_ERR_SHAPE, "e %d not in [1, 4096]", e);
+  for (int32_t i = 0; i < e; ++i) Q4_REQUIRE(counts[i] >= 0, Q4_ERR_SHAPE, "counts[%d] < 0", i);
+  return ok();
+}
+
+int64_t top_count(double frac, int32_t e) {
+  return std::min<int64_t>(e, int64_t(std::ceil(frac * double(e) - 1e-9)));
+}
+
+}  // namespace
+}  // extern "C++"
+
+int moe_expert_bits_by_hotness(const int64_t* counts, int32_t e, double frac8, int shared, int32_t* bits_out) {
+  g_last_error.clear();
+  if (int rc = check_counts(counts, e, bits_out)) return rc;
+  Q4_REQUIRE(frac8 >= 0.0 && frac8 <= 1.0, Q4_ERR_SHAPE, "frac8 must lie in [0, 1]");
+  const std::vector<int32_t> order = by_hotness(counts, e);
+  const int64_t n8 = top_count(frac8, e);
+  for (int32_t i = 0; i < e; ++i) bits_out[i] = 4;
+  for (int64_t i = 0; i < n8; ++i) bits_out[order[i]] = 8;
+  if (shared) bits_out[e] = 8;   // the shared expert sees every token
+  return ok();
+}
+
+int moe_expert_groups_by_hotness(const int64_t* counts, int32_t e, double hot_frac, double cold_share, int shared,
+                                 int32_t* groups_out) {
+  g_last_error.clear();
+  if (int rc = check_counts(counts, e, groups_out)) return rc;
+  Q4_REQUIRE(hot_frac >= 0.0 && hot_frac <= 1.0 && cold_share >= 0.0, Q4_ERR_SHAPE,
+             "hot_frac must lie in [0, 1] and cold_share be >= 0");
+  int64_t total = 0;
+  for (int32_t i = 0; i < e; ++i) total += counts[i];
+  for (int32_t i = 0; i < e; ++i) groups_out[i] = double(counts[i] * e) < cold_share * double(total) ? 256 : 64;
+  const std::vector<int32_t> order = by_hotness(counts, e);
+  const int64_t nh = top_count(hot_frac, e);
+  for (int64_t i = 0; i < nh; ++i) groups_out[order[i]] = 32;
+  if (shared) groups_out[e] = 32;
+  return ok();
+}
+
 extern "C++" {  // internal helpers keep C++ linkage
 namespace {
 
@@ -447,6 +534,9 @@ int ffn_forward(const q4_moe_layer_t* L, const uint16_t* x_bf16, int64_t t, cons
     views->slots_per_token = int32_t(S);
     views->positions = t * S;
     views->y = w.y;
+    views->y_slices = w.ksplit;
+    views->y_slice_groups = int32_t((L->inter / 128 + w.ksplit - 1) / w.ksplit);
+    views->y_slice_stride = t * S * L->hidden;
     views->q_x = w.qx;
     views->s_x = w.sx;
     views->q_h = w.qh;
@@ -492,7 +582,7 @@ int ffn_forward(const q4_moe_layer_t* L, const uint16_t* x_bf16, int64_t t, cons
   dn.N = H;
   dn.K = I;
   dn.out = w.y;
-  dn.ksplit = views ? 1 : w.ksplit;   // the debug views show whole y rows
+  dn.ksplit = w.ksplit;
   dn.out_slice = t * S * H;
   auto gemm1 = [&](const GemmArgs& g, int act, int kind) {
     return w.prefill ? launch_gemm_prefill(g, act, kind, stream) : launch_gemm(g, act, kind, rb, stream);

@@ -65,19 +65,28 @@ def swiglu_w4a16(x, gate, up, down):
     return linear_w4a16(silu(g) * u, down)
 
 
-def moe_w4a16(x, expert, ids, weights, shared=None):
+def _routed_sum(ids, weights, hidden, expert_out, pmap=map):
+    """out[t] = sum over the routed (t, j) of w[t, j] * y_{ids[t, j]}(x[t]): experts in
+    ascending index, each expert's rows in token order.  ``expert_out(e, rows)`` gives
+    the expert's outputs for those token rows; ``pmap`` may evaluate the (independent)
+    experts concurrently -- the sums are still formed in the order above."""
+    ids = np.asarray(ids)
+    w = np.asarray(weights, dtype=np.float64)
+    out = np.zeros((ids.shape[0], hidden), dtype=np.float64)
+    experts = [int(e) for e in np.unique(ids)]
+    where = [np.nonzero(ids == e) for e in experts]
+    ys = list(pmap(lambda a: expert_out(a[0], a[1][0]), zip(experts, where)))
+    for (rows, cols), y in zip(where, ys):
+        for i, (r, c) in enumerate(zip(rows, cols)):
+            out[r] += w[r, c] * y[i]
+    return out
+
+
+def moe_w4a16(x, expert, ids, weights, shared=None, pmap=map):
     """``expert(e)`` returns (gate, up, down) quantised matrices of expert e;
     ``shared`` is such a triple or None."""
     x64 = np.asarray(x, dtype=np.float64)
-    ids = np.asarray(ids)
-    w = np.asarray(weights, dtype=np.float64)
-    t, k = ids.shape
-    out = np.zeros((t, x64.shape[1]), dtype=np.float64)
-    for e in np.unique(ids):
-        rows, cols = np.nonzero(ids == e)
-        y = swiglu_w4a16(x64[rows], *expert(int(e)))
-        for i, (r, c) in enumerate(zip(rows, cols)):
-            out[r] += w[r, c] * y[i]
+    out = _routed_sum(ids, weights, x64.shape[1], lambda e, rows: swiglu_w4a16(x64[rows], *expert(e)), pmap)
     if shared is not None:
         out += swiglu_w4a16(x64, *shared)
     return out
@@ -150,17 +159,9 @@ def swiglu_w4a8(x, gate, up, down, return_parts=False):
     return y
 
 
-def moe_w4a8(x, expert, ids, weights, shared=None):
+def moe_w4a8(x, expert, ids, weights, shared=None, pmap=map):
     x32 = np.asarray(x, dtype=np.float32)
-    ids = np.asarray(ids)
-    w = np.asarray(weights, dtype=np.float64)
-    t, k = ids.shape
-    out = np.zeros((t, x32.shape[1]), dtype=np.float64)
-    for e in np.unique(ids):
-        rows, cols = np.nonzero(ids == e)
-        y = swiglu_w4a8(x32[rows], *expert(int(e)))
-        for i, (r, c) in enumerate(zip(rows, cols)):
-            out[r] += w[r, c] * y[i]
+    out = _routed_sum(ids, weights, x32.shape[1], lambda e, rows: swiglu_w4a8(x32[rows], *expert(e)), pmap)
     if shared is not None:
         out += swiglu_w4a8(x32, *shared)
     return out
@@ -185,17 +186,9 @@ def swiglu_w8a8(x, gate, up, down):
     return linear_w8a8(qh, sh, down)
 
 
-def moe_w8a8(x, expert, ids, weights, shared=None):
+def moe_w8a8(x, expert, ids, weights, shared=None, pmap=map):
     x32 = np.asarray(x, dtype=np.float32)
-    ids = np.asarray(ids)
-    w = np.asarray(weights, dtype=np.float64)
-    t, k = ids.shape
-    out = np.zeros((t, x32.shape[1]), dtype=np.float64)
-    for e in np.unique(ids):
-        rows, cols = np.nonzero(ids == e)
-        y = swiglu_w8a8(x32[rows], *expert(int(e)))
-        for i, (r, c) in enumerate(zip(rows, cols)):
-            out[r] += w[r, c] * y[i]
+    out = _routed_sum(ids, weights, x32.shape[1], lambda e, rows: swiglu_w8a8(x32[rows], *expert(e)), pmap)
     if shared is not None:
         out += swiglu_w8a8(x32, *shared)
     return out
@@ -211,18 +204,12 @@ def swiglu_int8_acts(x, gate, up, down, bits):
     return swiglu_w8a8(x, gate, up, down) if bits == 8 else swiglu_w4a8(x, gate, up, down)
 
 
-def moe_mixed(x, expert, bits, ids, weights, shared=None, shared_bits=8):
+def moe_mixed(x, expert, bits, ids, weights, shared=None, shared_bits=8, pmap=map):
     """out[t] = sum_j w[t, j] FFN_{ids[t, j]}(x[t]) (+ shared), expert e evaluated with
     bits[e]-wide weights; ``expert(e)`` returns its (gate, up, down) quantised matrices."""
     x32 = np.asarray(x, dtype=np.float32)
-    ids = np.asarray(ids)
-    w = np.asarray(weights, dtype=np.float64)
-    out = np.zeros((ids.shape[0], x32.shape[1]), dtype=np.float64)
-    for e in np.unique(ids):
-        rows, cols = np.nonzero(ids == e)
-        y = swiglu_int8_acts(x32[rows], *expert(int(e)), bits[int(e)])
-        for i, (r, c) in enumerate(zip(rows, cols)):
-            out[r] += w[r, c] * y[i]
+    out = _routed_sum(ids, weights, x32.shape[1],
+                      lambda e, rows: swiglu_int8_acts(x32[rows], *expert(e), bits[e]), pmap)
     if shared is not None:
         out += swiglu_int8_acts(x32, *shared, shared_bits)
     return out

@@ -127,7 +127,7 @@ TAG_X, TAG_W, TAG_ROUTER, TAG_GATE, TAG_UP, TAG_DOWN = 1, 2, 3, 4, 5, 6
 TAG_LORA_A, TAG_LORA_B = 7, 8
 
 # Zipf shaping of the 256-expert router: bias b_e = -zipf_s * KAPPA * ln(rank_e).
-# KAPPA is fitted by oracle/fit_zipf_kappa.py (see that script) so that the
+# KAPPA is fitted by synth/fit_zipf_kappa.py (see that script) so that the
 # per-expert load over ranks 9..128 at T = 4096 has log-log slope -zipf_s.
 ZIPF_KAPPA = 0.80
 

@@ -60,3 +60,20 @@ def random_expert_maker(seed, hidden, inter, sigma=0.05):
 def rel_l2_rows(y, ref):
     from oracle.ffn import max_rel_l2
     return max_rel_l2(y, ref)
+
+
+def y_positions(v):
+    """Per-position routed outputs from the debug views: the fp32 sum of the down
+    projection's K slices in slice order (the forward's own combine order); whole rows
+    when the forward does not split K.  Returned as float64."""
+    y = synth.to_numpy(v["y"]).astype(np.float32)
+    acc = y[0].copy()
+    for s in range(1, y.shape[0]):
+        acc = acc + y[s]
+    return acc.astype(np.float64)
+
+
+def k_slice(qm, g0, g1):
+    """Columns [128 g0, 128 g1) of an oracle quantised matrix (q, s, z) (groups of 128)."""
+    q, s, z = qm
+    return (q[:, 128 * g0:128 * g1], s[:, g0:g1], None if z is None else z[:, g0:g1])

@@ -167,8 +167,19 @@ def test_expert_bits_by_hotness_matches_the_oracle_rule(L):
     for E, frac, shared in ((256, 0.05, False), (8, 0.25, True), (17, 0.0, False), (9, 1.0, True), (64, 0.1, False)):
         counts = rng.integers(0, 6, E)
         assert L.expert_bits_by_hotness(counts.tolist(), frac, shared) == ffn.bits_by_hotness(counts, frac, shared)
-    with pytest.raises(ValueError):
+    with pytest.raises(L.Q4Error):
         L.expert_bits_by_hotness([1, 2], 1.5)
+    with pytest.raises(L.Q4Error):
+        L.expert_bits_by_hotness([1, -2], 0.5)
+    # the raw C entry point, host arrays only
+    counts = (ctypes.c_int64 * 4)(3, 9, 9, 1)
+    out = (ctypes.c_int32 * 5)()
+    assert L.raw.moe_expert_bits_by_hotness(counts, 4, 0.5, 1, out) == L.Q4_OK
+    assert list(out) == [4, 8, 8, 4, 8]      # ties: the lower index first; shared 8
+    assert L.raw.moe_expert_bits_by_hotness(counts, 4, 0.25, 0, out) == L.Q4_OK
+    assert list(out)[:4] == [4, 8, 4, 4]
+    assert L.raw.moe_expert_bits_by_hotness(None, 4, 0.25, 0, out) == L.Q4_ERR_NULL
+    assert L.raw.moe_expert_bits_by_hotness(counts, 0, 0.25, 0, out) == L.Q4_ERR_SHAPE
 
 
 def test_mixed_layer_validation(L):
@@ -215,6 +226,13 @@ def test_expert_groups_by_hotness_matches_the_oracle_rule(L):
         counts[rng.integers(0, E)] = 0
         assert L.expert_groups_by_hotness(counts.tolist(), 0.05, 0.1, shared) == \
             ffn.groups_by_hotness(counts, 0.05, 0.1, shared)
+    # hand case: total 100 over 4 experts, even share 25, cold below 2.5 -> 256
+    counts = (ctypes.c_int64 * 4)(2, 60, 35, 3)
+    out = (ctypes.c_int32 * 5)()
+    assert L.raw.moe_expert_groups_by_hotness(counts, 4, 0.25, 0.1, 1, out) == L.Q4_OK
+    assert list(out) == [256, 32, 64, 64, 32]
+    with pytest.raises(L.Q4Error):
+        L.expert_groups_by_hotness([1, 2], 0.05, -1.0)
 
 
 def test_grouped_layer_validation(L):
@@ -231,3 +249,83 @@ def test_grouped_layer_validation(L):
     assert r.moe_int4_ffn_workspace_bytes(ctypes.byref(desc(expert_bits=4096)), 4, L.Q4_W4A16) == 0
     for bad in (dict(asymmetric=1), dict(weight_bits=8), dict(gate_up_offsets=None)):
         assert r.moe_int4_ffn_workspace_bytes(ctypes.byref(desc(**bad)), 4, L.Q4_W4A16) == 0
+
+
+def _plan_desc(L, E, H, I, k, shared=False, asym=0, **kw):
+    d = L.Q4MoELayer(E, H, I, k, asym, I if shared else 0, 4096, 4096, 4096 if shared else None,
+                     4096 if shared else None, 0, None, None, None, None)
+    for key, v in kw.items():
+        setattr(d, key, v)
+    return d
+
+
+def test_plan_kernel_choice(L):
+    """Host-only plan query: which GEMM kernel and tiles the forward takes (no GPU)."""
+    moe256 = _plan_desc(L, 256, 7168, 2048, 8, shared=True)
+    moe8 = _plan_desc(L, 8, 2048, 1024, 2)
+    dense = _plan_desc(L, 1, 2048, 8192, 1, asym=1)
+    W16, W8 = L.Q4_W4A16, L.Q4_W4A8
+    cases = [
+        # (layer, t, mode) -> (kernel, tile rows, down K slices)
+        ((moe256, 1, W16), ("decode", 16, 1)),
+        ((moe256, 64, W16), ("decode", 16, 1)),
+        ((moe256, 512, W16), ("decode", 16, 1)),      # 16 rows per expert, bf16: decode tiles
+        ((moe256, 512, W8), ("prefill", 128, 1)),     # from 9 rows with INT8 activations
+        ((moe256, 768, W16), ("prefill", 128, 1)),    # 24 rows, >= 2048 items
+        ((moe256, 1280, W8), ("prefill", 128, 1)),
+        ((moe256, 4096, W16), ("prefill", 128, 1)),
+        ((moe8, 1, W16), ("decode", 16, 4)),          # narrow: the down projection splits K
+        ((moe8, 2, W8), ("decode", 16, 2)),
+        ((moe8, 40, W8), ("decode", 16, 1)),          # est. 512 items: no split
+        ((moe8, 192, W16), ("decode", 64, 1)),        # 48 rows, few items: decode tiles
+        ((moe8, 256, W8), ("prefill", 128, 1)),       # 64 rows per expert
+        ((dense, 1, W16), ("decode", 16, 8)),
+        ((dense, 16, W16), ("decode", 16, 8)),
+        ((dense, 17, W16), ("decode", 32, 1)),
+    ]
+    for (desc, t, mode), (kernel, rows, ks) in cases:
+        p = L.moe_int4_ffn_plan(desc, t, mode)
+        assert (p["kernel"], p["tile_rows"], p["down_ksplit"]) == (kernel, rows, ks), (t, mode, p)
+        assert p["workspace_bytes"] == L.raw.moe_int4_ffn_workspace_bytes(ctypes.byref(desc), t, mode)
+        assert not p["prefill_addr_limited"]
+    # layers with several weight formats keep the 64-rows-per-expert rule
+    mixed = _plan_desc(L, 256, 7168, 2048, 8, shared=True, expert_bits=4096, gate_up_offsets=4096,
+                       down_offsets=4096)
+    assert L.moe_int4_ffn_plan(mixed, 1280, W8)["kernel"] == "decode"
+    assert L.moe_int4_ffn_plan(mixed, 2048, W8)["kernel"] == "prefill"
+    grouped = _plan_desc(L, 256, 7168, 2048, 8, shared=True, expert_groups=4096, gate_up_offsets=4096,
+                         down_offsets=4096)
+    assert L.moe_int4_ffn_plan(grouped, 768, W16)["kernel"] == "decode"
+    assert L.moe_int4_ffn_plan(grouped, 4096, W16)["kernel"] == "prefill"
+
+
+def test_plan_no_empty_k_slice(L):
+    """I = 1152 (9 groups): 4 slices of ceil(9/4) = 3 groups would leave the last one
+    empty; the plan takes 3."""
+    p = L.moe_int4_ffn_plan(_plan_desc(L, 8, 2048, 1152, 2), 1, L.Q4_W4A16)
+    assert p["down_ksplit"] == 3
+
+
+def test_plan_prefill_addressing_limit(L):
+    """Past the prefill kernels' 32-bit activation offsets (h of the 256-expert W4A16 down
+    projection passes 2^31 bytes at t * 9 * 2048 * 2 >= 2^31) the forward takes the
+    decode kernel, which addresses with 64-bit offsets, and the plan says so."""
+    moe256 = _plan_desc(L, 256, 7168, 2048, 8, shared=True)
+    t_lim = (1 << 31) // (9 * 2048 * 2)
+    p = L.moe_int4_ffn_plan(moe256, t_lim, L.Q4_W4A16)
+    assert p["kernel"] == "prefill" and not p["prefill_addr_limited"]
+    p = L.moe_int4_ffn_plan(moe256, t_lim + 1, L.Q4_W4A16)
+    assert p["kernel"] == "decode" and p["prefill_addr_limited"]
+    # INT8 activations: x codes are 1 byte, h codes 1 byte per element (limit at 2^31 / (9 * 2048))
+    t8 = (1 << 31) // (9 * 2048)
+    assert L.moe_int4_ffn_plan(moe256, t8 - 8, L.Q4_W4A8)["kernel"] == "prefill"
+    assert L.moe_int4_ffn_plan(moe256, t8 + 8, L.Q4_W4A8)["prefill_addr_limited"]
+
+
+def test_plan_validation(L):
+    p = L.Q4FfnPlan()
+    assert L.raw.moe_int4_ffn_plan(None, 4, L.Q4_W4A16, ctypes.byref(p)) == L.Q4_ERR_NULL
+    d = _plan_desc(L, 8, 2048, 1024, 2)
+    assert L.raw.moe_int4_ffn_plan(ctypes.byref(d), 4, L.Q4_W4A16, None) == L.Q4_ERR_NULL
+    assert L.raw.moe_int4_ffn_plan(ctypes.byref(d), -1, L.Q4_W4A16, ctypes.byref(p)) == L.Q4_ERR_SHAPE
+    assert L.raw.moe_int4_ffn_plan(ctypes.byref(d), 4, L.Q4_W8A8, ctypes.byref(p)) == L.Q4_ERR_DTYPE

@@ -7,17 +7,25 @@ library's router, then moe_int4_ffn_forward, at the benchmark's batch sizes (T =
 The oracle routes the same tokens itself (fp64 logits) and evaluates a seeded sample of
 tokens one by one; a sampled token is compared where both routings choose the same
 experts (fp32 and fp64 logits may order near-ties differently; nearly all tokens
-agree, which is asserted).  Expert weights for the oracle come from the seeded
+agree, which is asserted).  At the timed decode batch (T = 64) every token is compared:
+the forward is given the oracle's own routing (ids and weights are inputs of
+moe_int4_ffn_forward), so no token is skipped.  At T = 4096 every position of four
+chosen experts (the most loaded, a middle one, a 1-8-row cold one and the shared
+expert) is checked stage by stage through moe_int4_ffn_debug, gate/up against the
+oracle from x and down against the oracle on the GPU's own h.  Expert weights for the oracle come from the seeded
 generator run by torch on the GPU and copied to the host (bit-identical to the host
 generator, checked by test_generator_bit_identical_on_gpu), then quantised by the
 oracle; nothing the library computes is fed to the oracle."""
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import pytest
 import torch
 
 import synth
-from oracle import ffn, quant, router
+from oracle import ffn, permute as operm, quant, router
 from tests.helpers import require_gpu
+from tests.stagewise import check_stagewise
 
 pytestmark = pytest.mark.gpu
 CFG = "moe256"
@@ -153,7 +161,9 @@ def test_prefill_t4096_w4a8(lib, wl4, oracle_experts):
 def test_prefill_kernel_below_64_rows_per_expert(lib, wl4, oracle_experts, t, mode):
     """24, 40 and 16 routed rows per expert on average: enough work items that the
     forward takes the 128-row prefill kernel (mostly partly filled tiles)."""
-    _check(lib, wl4.retoken(synth, t, mode), mode, oracle_experts, 2, 6 + t)
+    wl = wl4.retoken(synth, t, mode)
+    assert lib.moe_int4_ffn_plan(wl.layer, t, wl.mode)["kernel"] == "prefill"
+    _check(lib, wl, mode, oracle_experts, 2, 6 + t)
 
 
 def test_decode_t64_w8a8(lib, bench_mod, oracle_experts):
@@ -207,3 +217,57 @@ def test_per_expert_groups_by_hotness(lib, grouped, oracle_experts, t, mode):
     wl, groups = grouped
     _check(lib, wl if (t, mode) == (64, "w4a16") else wl.retoken(synth, t, mode), mode, oracle_experts, 2,
            11 + t, groups=groups)
+
+
+def _pool_map(fn, items):
+    """The oracle's experts are independent: evaluate them on 8 threads (BLAS at 2 threads
+    each); the oracle still forms every sum in its own order."""
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(2), ThreadPoolExecutor(8) as ex:
+        return list(ex.map(fn, list(items)))
+
+
+@pytest.mark.parametrize("mode", ["w4a16", "w4a8"])
+def test_decode_t64_every_token(lib, wl4, oracle_experts, mode):
+    """All 64 tokens of the timed decode batch against the oracle (141 routed experts +
+    the shared expert), with the oracle's routing fed to the forward."""
+    E = synth.CONFIGS[CFG]["experts"]
+    t = 64
+    x = _np(synth.tokens(CFG, t))
+    ids_o, w_o = _oracle_routing(x, t)
+    m = {"w4a16": lib.Q4_W4A16, "w4a8": lib.Q4_W4A8}[mode]
+    assert lib.moe_int4_ffn_plan(wl4.layer, t, m)["kernel"] == "decode"
+    print(f"[fullsize] every token T=64 {mode}: forward", flush=True)
+    out = lib.moe_int4_ffn_forward(wl4.layer, wl4.x, torch.as_tensor(ids_o, dtype=torch.int32).cuda(),
+                                   torch.as_tensor(w_o, dtype=torch.float32).cuda(), mode=m)
+    torch.cuda.synchronize()
+    expert = lambda e: oracle_experts.get(e, 4)
+    need = sorted(set(int(e) for e in ids_o.ravel())) + [E]
+    print(f"[fullsize] every token T=64 {mode}: oracle over {len(need)} experts", flush=True)
+    _pool_map(expert, need)                      # quantise the needed experts (cached)
+    fwd = ffn.moe_w4a16 if mode == "w4a16" else ffn.moe_w4a8
+    ref = fwd(x, expert, ids_o, w_o, shared=expert(E), pmap=_pool_map)
+    err = ffn.max_rel_l2(_np(out), ref)
+    print(f"[fullsize] every token T=64 {mode}: max rel L2 {err:.2e}", flush=True)
+    assert err <= TOL[mode]
+
+
+@pytest.mark.parametrize("mode", ["w4a16", "w4a8"])
+def test_prefill_t4096_chosen_experts_every_position(lib, wl4, oracle_experts, mode):
+    cfg = synth.CONFIGS[CFG]
+    E, t = cfg["experts"], 4096
+    x = synth.tokens(CFG, t)
+    ids_o, w_o = _oracle_routing(_np(x), t)
+    counts = np.bincount(ids_o.ravel(), minlength=E)
+    order = np.argsort(-counts, kind="stable")
+    nz = order[counts[order] > 0]
+    cold = [int(e) for e in nz[::-1] if 1 <= counts[e] <= 8]
+    chosen = [int(nz[0]), int(nz[len(nz) // 2])] + cold[:1] + [E]
+    print(f"[fullsize] T=4096 {mode}: experts {chosen} with rows "
+          f"{[int(counts[e]) if e < E else t for e in chosen]}", flush=True)
+    assert cold, "the Zipf load leaves an expert with 1..8 rows"
+    m = {"w4a16": lib.Q4_W4A16, "w4a8": lib.Q4_W4A8}[mode]
+    assert lib.moe_int4_ffn_plan(wl4.layer, t, m)["kernel"] == "prefill"
+    _pool_map(lambda e: oracle_experts.get(e, 4), chosen)
+    check_stagewise(lib, wl4.layer, lambda e: oracle_experts.get(e, 4), x, ids_o, w_o, m, shared=True,
+                    experts=chosen, gate_up_rows=32)

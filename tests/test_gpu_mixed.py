@@ -11,7 +11,7 @@ import torch
 import synth
 from oracle import ffn, quant, router
 from oracle import permute as operm
-from tests.helpers import random_expert_maker, require_gpu
+from tests.helpers import random_expert_maker, require_gpu, y_positions
 
 pytestmark = pytest.mark.gpu
 TOL = 2e-2
@@ -107,7 +107,7 @@ def test_small_mixed_stagewise(lib, small, t):
     qh_ref, sh_ref = ffn.act_quant_int8(_np(v["h"]))
     assert np.array_equal(qh_gpu, qh_ref) and np.array_equal(sh_gpu.view(np.uint32), sh_ref.view(np.uint32))
     h = _np(v["h"]).astype(np.float64)
-    y = _np(v["y"]).astype(np.float64)
+    y = y_positions(v)
     for e in range(E + 1):
         lo, hi = int(offsets[e]), int(offsets[e + 1])
         if lo == hi:

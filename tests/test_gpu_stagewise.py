@@ -11,6 +11,12 @@ inputs of that stage, so the bars can be tight:
   rescale of them;
 * W4A16: h (bf16) within 5e-3 per row of the fp64 h; y within 2e-5 per row of the
   oracle's down projection of the GPU's bf16 h;
+* gate and up before SwiGLU, through the same GEMM core on the layer's own gate/up
+  block: the INT32 group accumulators bit-exact on the GPU's x codes (W4A8), the fp32
+  products within 2e-5 per row of the fp64 ones (W4A16);
+* where the forward splits the down projection's K over workgroups (narrow layers at
+  small batches), every K slice of y against the oracle's down projection restricted
+  to that slice's groups, and their in-order sum as above;
 * combine: the bf16 output within 4e-3 per row of the fp64 weighted sum of the GPU's
   per-position y (one bf16 rounding).
 """
@@ -19,8 +25,9 @@ import pytest
 import torch
 
 import synth
-from oracle import ffn, permute as operm, router
+from oracle import router
 from tests.helpers import OracleExperts, build_gpu_layer, random_expert_maker, require_gpu
+from tests.stagewise import _np, check_stagewise
 
 pytestmark = pytest.mark.gpu
 
@@ -30,73 +37,6 @@ def lib():
     require_gpu()
     import int4_group_quantized_g128_amd as lib
     return lib
-
-
-def _np(t):
-    return synth.to_numpy(t)
-
-
-def _rows_rel(y, ref):
-    """per-row relative L2 (zero reference rows need zero rows)"""
-    return ffn.max_rel_l2(y, ref)
-
-
-def check_stagewise(lib, layer, oe, x, ids, w, mode, shared):
-    t, k = ids.shape
-    E = layer.num_experts
-    out, v = lib.moe_int4_ffn_debug(layer, x.cuda(), torch.as_tensor(ids, dtype=torch.int32).cuda(),
-                                    torch.as_tensor(w, dtype=torch.float32).cuda(), mode=mode)
-    torch.cuda.synchronize()
-    S = v["slots_per_token"]
-    assert S == k + (1 if shared else 0)
-    # permutation over slots t * S + j (j == k: the shared expert)
-    slot_ids = np.concatenate([ids, np.full((t, 1), E, np.int64)], axis=1) if shared else ids
-    counts, offsets, perm, inv = operm.permute(slot_ids, E + (1 if shared else 0))
-    assert np.array_equal(_np(v["counts"]), counts)
-    assert np.array_equal(_np(v["offsets"]), offsets)
-    assert np.array_equal(_np(v["perm"]), perm)
-    assert np.array_equal(_np(v["inv"]), inv)
-    x32 = _np(x).astype(np.float32)
-    h = _np(v["h"]).astype(np.float64)
-    y = _np(v["y"]).astype(np.float64)
-    if mode == 1:
-        qx, sx = ffn.act_quant_int8(x32)
-        assert np.array_equal(_np(v["q_x"]), qx)
-        assert np.array_equal(_np(v["s_x"]).view(np.uint32), sx.view(np.uint32))
-        qh_gpu, sh_gpu = _np(v["q_h"]), _np(v["s_h"])
-        qh_ref, sh_ref = ffn.act_quant_int8(_np(v["h"]))
-        assert np.array_equal(qh_gpu, qh_ref)
-        assert np.array_equal(sh_gpu.view(np.uint32), sh_ref.view(np.uint32))
-    for e in range(E + (1 if shared else 0)):
-        lo, hi = int(offsets[e]), int(offsets[e + 1])
-        if lo == hi:
-            continue
-        toks = perm[lo:hi] // S
-        gate, up, down = oe(e)
-        if mode == 1:
-            g = ffn.linear_w4a8(qx[toks], sx[toks], gate)
-            u = ffn.linear_w4a8(qx[toks], sx[toks], up)
-            assert _rows_rel(h[lo:hi], ffn.silu(g) * u) <= 2e-5, f"h, expert {e}"
-            # down-projection INT32 accumulators on the GPU's own h codes
-            wdev = (layer.down[e * layer.dn_bytes:(e + 1) * layer.dn_bytes] if e < E else layer.shared_down)
-            acc = lib.int4_w4a8_group_acc(v["q_h"][lo:hi].contiguous(), wdev, layer.hidden, layer.asymmetric)
-            torch.cuda.synchronize()
-            assert np.array_equal(_np(acc), ffn.group_acc(qh_gpu[lo:hi], ffn.widen_int8(down))), f"acc, expert {e}"
-            y_ref = ffn.linear_w4a8(qh_gpu[lo:hi], sh_gpu[lo:hi], down)
-        else:
-            g = ffn.linear_w4a16(x32[toks], gate)
-            u = ffn.linear_w4a16(x32[toks], up)
-            assert _rows_rel(h[lo:hi], ffn.silu(g) * u) <= 5e-3, f"h, expert {e}"
-            y_ref = ffn.linear_w4a16(h[lo:hi], down)
-        assert _rows_rel(y[lo:hi], y_ref) <= 2e-5, f"y, expert {e}"
-    # combine of the GPU's per-position outputs
-    ref = np.zeros((t, layer.hidden))
-    for tok in range(t):
-        for j in range(k):
-            ref[tok] += w[tok, j] * y[inv[tok * S + j]]
-        if shared:
-            ref[tok] += y[inv[tok * S + k]]
-    assert _rows_rel(_np(out), ref) <= 4e-3
 
 
 @pytest.fixture(scope="module")
@@ -135,3 +75,37 @@ def test_shared_layer_stagewise(lib, small_shared, mode, t):
     ids = np.stack([rng.permutation(16)[:4] for _ in range(t)]).astype(np.int64)
     w = rng.dirichlet(np.ones(4), size=t)
     check_stagewise(lib, layer, oe, x, ids, w, mode, shared=True)
+
+
+@pytest.mark.parametrize("mode,t,ksplit", [(1, 1, 4), (0, 1, 4), (1, 2, 2), (0, 2, 2)],
+                         ids=["w4a8-T1", "w4a16-T1", "w4a8-T2", "w4a16-T2"])
+def test_moe8_stagewise_ksplit(lib, moe8, mode, t, ksplit):
+    """The 8-expert layer at T = 1 and 2: the down projection splits K (4 and 2 slices)."""
+    layer, oe = moe8
+    x = synth.tokens("moe8", t)
+    wr, _ = synth.router_weights("moe8")
+    _, ids, w = router.route(_np(x), _np(wr), None, 2)
+    check_stagewise(lib, layer, oe, x, ids, w, mode, shared=False, expect_ksplit=ksplit)
+
+
+@pytest.fixture(scope="module")
+def dense(lib):
+    """The 2048/8192 dense SwiGLU FFN (asymmetric) as a one-expert layer."""
+    cfg = synth.CONFIGS["dense"]
+    g, u, d = synth.dense_ffn_weights("dense")
+    layer = lib.MoELayer(1, cfg["hidden"], cfg["inter"], 1, asymmetric=True)
+    layer.set_expert(0, g.cuda(), u.cuda(), d.cuda())
+    torch.cuda.synchronize()
+    return layer, OracleExperts(lambda e: (g, u, d), True)
+
+
+@pytest.mark.parametrize("mode,t,ksplit", [(0, 1, 8), (1, 1, 8), (0, 4, 8), (0, 16, 8)],
+                         ids=["w4a16-T1", "w4a8-T1", "w4a16-T4", "w4a16-T16"])
+def test_dense_stagewise_ksplit(lib, dense, mode, t, ksplit):
+    """Dense T = 1 / 4 / 16: 64 work items of two column blocks, so the down projection
+    (K = 8192) splits into 8 slices that the combine adds in order."""
+    layer, oe = dense
+    x = synth.tokens("dense", t)
+    ids = np.zeros((t, 1), np.int64)
+    w = np.ones((t, 1))
+    check_stagewise(lib, layer, oe, x, ids, w, mode, shared=False, expect_ksplit=ksplit)

@@ -9,7 +9,7 @@ import torch
 import synth
 from oracle import ffn, layout, quant, router
 from oracle import permute as operm
-from tests.helpers import random_expert_maker, require_gpu
+from tests.helpers import random_expert_maker, require_gpu, y_positions
 
 pytestmark = pytest.mark.gpu
 TOL = 2e-2
@@ -154,7 +154,7 @@ def test_small_shared_w8a8_stagewise(lib, small8, t):
     qh_gpu, sh_gpu = _np(v["q_h"]), _np(v["s_h"])
     qh_ref, sh_ref = ffn.act_quant_int8(_np(v["h"]))
     assert np.array_equal(qh_gpu, qh_ref) and np.array_equal(sh_gpu.view(np.uint32), sh_ref.view(np.uint32))
-    y = _np(v["y"]).astype(np.float64)
+    y = y_positions(v)
     for e in range(E + 1):
         lo, hi = int(offsets[e]), int(offsets[e + 1])
         if lo == hi:
@@ -168,3 +168,35 @@ def test_small_shared_w8a8_stagewise(lib, small8, t):
         torch.cuda.synchronize()
         assert np.array_equal(_np(acc), ffn.group_acc(qh_gpu[lo:hi], down[0]))
         assert ffn.max_rel_l2(y[lo:hi], ffn.linear_w8a8(qh_gpu[lo:hi], sh_gpu[lo:hi], down)) <= 2e-5
+
+
+@pytest.mark.parametrize("t,ksplit", [(1, 4), (2, 2)])
+def test_moe8_w8a8_ksplit(lib, moe8, t, ksplit):
+    """T = 1 and 2 on the 8-expert layer: the down projection splits K (the 8-bit
+    few-items kernel); every slice against the oracle's sum over its groups, and the
+    output end to end."""
+    from tests.helpers import k_slice
+    layer, oe = moe8
+    assert lib.moe_int4_ffn_plan(layer, t, lib.Q4_W8A8)["down_ksplit"] == ksplit
+    x = synth.tokens("moe8", t)
+    wr, _ = synth.router_weights("moe8")
+    _, ids, w = router.route(_np(x), _np(wr), None, 2)
+    out, v = lib.moe_int4_ffn_debug(layer, x.cuda(), torch.as_tensor(ids, dtype=torch.int32).cuda(),
+                                    torch.as_tensor(w, dtype=torch.float32).cuda(), mode=lib.Q4_W8A8)
+    torch.cuda.synchronize()
+    assert ffn.max_rel_l2(_np(out), ffn.moe_w8a8(_np(x), oe, ids, w)) <= TOL
+    assert v["y_slices"] == ksplit
+    _, offsets, perm, _ = operm.permute(ids, 8)
+    qh, sh = _np(v["q_h"]), _np(v["s_h"])
+    ys = _np(v["y"]).astype(np.float64)
+    gsl = v["y_slice_groups"]
+    for e in range(8):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if lo == hi:
+            continue
+        down = oe(e)[2]
+        for s in range(ksplit):
+            g0, g1 = s * gsl, min(1024 // 128, (s + 1) * gsl)
+            ref = ffn.linear_w8a8(qh[lo:hi, 128 * g0:128 * g1], sh[lo:hi], k_slice(down, g0, g1))
+            assert ffn.max_rel_l2(ys[s, lo:hi], ref) <= 2e-5, (e, s)
+        assert ffn.max_rel_l2(y_positions(v)[lo:hi], ffn.linear_w8a8(qh[lo:hi], sh[lo:hi], down)) <= 2e-5
