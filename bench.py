@@ -32,6 +32,7 @@ TRAFFIC_PROFILES = {
     ("moe256", 4096, "w4a16"): os.path.join(ROOT, "profiles", "k_gemm_pf_moe256_T4096_w4a16.txt"),
     ("moe8_w4a8", 2048, "w4a8"): os.path.join(ROOT, "profiles", "k_gemm_pf_moe8_T2048_w4a8.txt"),
 }
+WARM_SECONDS = 0.3             # minimum untimed graph replay time before a timed region
 BF16_PEAK_TFLOPS = 2500.0      # dense bf16 MFMA
 INT8_PEAK_TOPS = 5000.0        # dense int8 MFMA
 
@@ -246,6 +247,64 @@ class DenseWorkload(Workload):
             raise L.Q4Error("moe_int4_ffn_forward", rc)
 
 
+class LinearWorkload:
+    """The single INT4 g128 linear y = x W^T (x fp16 [4, 2048], W [2048, 2048] with 0.1 %
+    outliers x20, symmetric), quantised and repacked on the GPU; a step is
+    int4_linear_forward (fp32 output)."""
+
+    def __init__(self, lib, torch, synth):
+        self.lib, self.torch = lib, torch
+        cfg = synth.CONFIGS["linear"]
+        self.cfg, self.t, self.mode = cfg, cfg["t"], None
+        self.n, self.k = cfg["n"], cfg["k"]
+        self.x, w = synth.linear_inputs(device="cuda")
+        packed, scales, zeros = lib.quantize_int4_g128(w)
+        self.w_dev = lib.q4_repack_device(packed, scales, zeros, self.n, self.k)
+        del w, packed, scales, zeros
+        self.y = torch.empty((self.t, self.n), dtype=torch.float32, device="cuda")
+        torch.cuda.synchronize()
+
+    def step(self):
+        L = self.lib._lib
+        rc = L.raw.int4_linear_forward(L._ptr(self.x), L.Q4_F16, self.t, self.k, L._ptr(self.w_dev), self.n, 0,
+                                       L._ptr(self.y), L._stream())
+        if rc:
+            raise L.Q4Error("int4_linear_forward", rc)
+
+    def summary(self, sec, cold_sec=None):
+        g = self.k // 128
+        wbytes = self.n * self.k // 2 + 2 * self.n * g       # nibbles + fp16 scales
+        res = {"tokens": self.t, "tokens_per_s": self.t / sec, "ms_per_step": sec * 1e3, "weight_bytes": wbytes,
+               "effective_weight_GBps": wbytes / sec / 1e9, "hbm_frac": wbytes / sec / 1e9 / HBM_PEAK_GBS,
+               "flops": 2.0 * self.t * self.n * self.k}
+        if cold_sec is not None:
+            res["ms_per_step_cold"] = cold_sec * 1e3
+            res["hbm_frac_cold"] = wbytes / cold_sec / 1e9 / HBM_PEAK_GBS
+        return res
+
+
+def expert_load(wl):
+    """Realised per-expert load of the batch (routed slots per expert, from the router's
+    ids): the sorted histogram's head, how many experts are touched, the smallest
+    non-zero load and, for the Zipf-shaped router, the log-log slope over ranks 9..128
+    and the KL divergence of the load shares from Zipf(s)."""
+    import numpy as np
+    from synth import fit_zipf_kappa as fz
+    E = wl.cfg["experts"]
+    if E <= 1:
+        return None
+    counts = np.bincount(wl.ids.cpu().numpy().ravel(), minlength=E)
+    srt = np.sort(counts)[::-1]
+    res = {"slots": int(counts.sum()), "touched": int(np.count_nonzero(counts)), "top16": srt[:16].tolist(),
+           "min_nonzero": int(srt[srt > 0].min()), "max_share": round(float(srt[0]) / wl.t, 4)}
+    if "zipf_s" in wl.cfg:
+        res["zipf_s"] = wl.cfg["zipf_s"]
+        res["kl_to_zipf"] = round(fz.kl_to_zipf(counts, wl.cfg["zipf_s"]), 4)
+        if res["touched"] >= 128:
+            res["slope_ranks_9_128"] = round(fz.slope_of_load(counts), 4)
+    return res
+
+
 def time_steps(torch, wl, steps, warmup, stage_events, graph=True):
     """Wall-clock per step over ``steps`` whole steps (router + forward) run from a HIP
     graph that holds ``per`` consecutive steps (10, 5, 2 or 1, dividing ``steps``), as a
@@ -265,8 +324,15 @@ def time_steps(torch, wl, steps, warmup, stage_events, graph=True):
         with torch.cuda.graph(g):
             for _ in range(per):
                 wl.step()
-        for _ in range(max(warmup // per, 1)):
+        # untimed replays: at least the warm-up steps and at least WARM_SECONDS of work, so
+        # that clocks have settled when the timed region starts (with only a few warm-up
+        # steps the first timed replays ran measurably slower than later ones)
+        n, t_w = 0, time.perf_counter()
+        while n < max(warmup // per, 1) or time.perf_counter() - t_w < WARM_SECONDS:
             g.replay()
+            n += 1
+            if n % 8 == 0:
+                torch.cuda.synchronize()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     if g is not None:
@@ -353,6 +419,9 @@ def summarize(wl, sec_per_step, stage_ms, cold_sec=None):
     if cold_sec is not None:   # every step from HBM (caches flushed before it)
         res["ms_per_step_cold"] = cold_sec * 1e3
         res["hbm_frac_cold"] = layer_bytes / cold_sec / 1e9 / HBM_PEAK_GBS
+    load = expert_load(wl)
+    if load is not None:
+        res["expert_load"] = load
     flops = wl.flops()
     int8 = wl.mode in (wl.lib.Q4_W4A8, wl.lib.Q4_W8A8)
     peak = INT8_PEAK_TOPS if int8 else BF16_PEAK_TFLOPS
@@ -468,9 +537,18 @@ def main():
     if roof is not None and prof is not None:
         from int4_group_quantized_g128_amd import profiling
         kv = profiling.read_kv(prof)
-        if kv.get("source_hash") == profiling.source_hash() and "traffic_bytes[gate_up]" in kv:
-            roof["traffic"] = int(kv["traffic_bytes[gate_up]"])
-            roof["traffic_source"] = os.path.relpath(prof, ROOT)
+        if kv.get("source_hash") == profiling.source_hash():
+            roof["profile"] = os.path.relpath(prof, ROOT)
+            if "traffic_bytes[gate_up]" in kv:
+                roof["traffic"] = int(kv["traffic_bytes[gate_up]"])
+            if "avg_us[gate_up]" in kv:
+                # the same kernel's average in the committed rocprofv3 kernel trace, and the
+                # fraction it gives with the same algorithmic work (frac uses the live average)
+                p_ms = float(kv["avg_us[gate_up]"]) * 1e-3
+                work = roof.get("algorithmic_bytes_per_launch") or roof.get("algorithmic_flops_per_launch")
+                scale = 1e9 if roof["unit"] == "GB/s" else 1e12
+                roof["profile_avg_ms"] = round(p_ms, 5)
+                roof["profile_frac"] = round(work / (p_ms * 1e-3) / scale / roof["peak"], 4)
 
     extra = {}
     if not args.no_extra and args.config == "moe256":
@@ -493,6 +571,12 @@ def main():
             c4 = time_cold(torch, lw, 20 if t > 1000 else 50) if not args.no_graph else None
             extra[f"lora8_T{t}_w4a16"] = lw.summary(s4, c4)
             del lw
+        log("[bench] extra linear 2048x2048 INT4 g128, T=4 (fp16 x, fp32 y)")
+        lw = LinearWorkload(lib, torch, synth)
+        sl, _ = time_steps(torch, lw, 100, 10, stage_events=False, graph=not args.no_graph)
+        cl = time_cold(torch, lw, 100) if not args.no_graph else None
+        extra["linear_T4_w4a16"] = lw.summary(sl, cl)
+        del lw
         for t in synth.CONFIGS["dense"]["tokens"]:
             log(f"[bench] extra dense 2048/8192 FFN decode T={t}")
             dw = DenseWorkload(lib, torch, synth, t, "w4a16")
@@ -579,6 +663,7 @@ def main():
                                 f"moe8 prefill: hidden 2048, 8 experts x inter 1024, top-2, INT4 g128 sym, 1 % hot "
                                 f"channels x10, T={args.tokens}, {args.mode}"),
                    "tokens": args.tokens, "experts_touched": main_res["experts_touched"],
+                   "expert_load": main_res.get("expert_load"),
                    "effective_weight_GBps": round(main_res["effective_weight_GBps"], 1),
                    "hbm_frac": round(main_res["hbm_frac"], 4)},
         "roofline": roof,

@@ -21,12 +21,18 @@ import synth
 RANKS = (9, 128)   # the ranks whose load the slope is fitted over
 
 
-def load_slope(ids, num_experts, ranks=RANKS):
-    """(log-log slope of the descending per-expert load over ``ranks``, the load)."""
-    load = np.sort(np.bincount(np.asarray(ids).ravel(), minlength=num_experts))[::-1].astype(np.float64)
+def slope_of_load(load, ranks=RANKS):
+    """Log-log slope of the per-expert load, sorted descending, over ``ranks`` (a zero
+    load counts as 0.5)."""
+    srt = np.sort(np.asarray(load, dtype=np.float64))[::-1]
     r = np.arange(ranks[0], ranks[1] + 1)
-    y = np.log(np.maximum(load[r - 1], 0.5))
-    return float(np.polyfit(np.log(r), y, 1)[0]), load
+    return float(np.polyfit(np.log(r), np.log(np.maximum(srt[r - 1], 0.5)), 1)[0])
+
+
+def load_slope(ids, num_experts, ranks=RANKS):
+    """(slope_of_load of the routed ids' per-expert load, the load sorted descending)."""
+    load = np.sort(np.bincount(np.asarray(ids).ravel(), minlength=num_experts))[::-1].astype(np.float64)
+    return slope_of_load(load, ranks), load
 
 
 def kl_to_zipf(load, s):
