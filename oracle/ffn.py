@@ -200,7 +200,9 @@ def moe_w8a8(x, expert, ids, weights, shared=None, pmap=map):
 # MoE与量化", APEX: precision by expert importance).  Every expert runs the INT8-activation
 # pipeline above; an expert's own width picks the 4-bit (widened) or the 8-bit codes.
 def swiglu_int8_acts(x, gate, up, down, bits):
-    """SwiGLU FFN of one expert with INT8 activations and `bits`-wide weight codes."""
+    """SwiGLU FFN of one expert with INT8 activations and `bits`-wide weight codes (2 and 4
+    bits: the codes are the 8-bit integers of the W4A8 pipeline as they are, no zero
+    point; 8 bits: the W8A8 pipeline)."""
     return swiglu_w8a8(x, gate, up, down) if bits == 8 else swiglu_w4a8(x, gate, up, down)
 
 
@@ -225,6 +227,24 @@ def bits_by_hotness(counts, frac8, shared=False):
     bits = np.full(e, 4, dtype=np.int64)
     bits[order[:n8]] = 8
     return list(bits) + ([8] if shared else [])
+
+
+def bits_apex(counts, frac8=0.0, cold_share=0.25, shared=False):
+    """Widths 2 / 4 / 8 from hit counts (page "大模型之Dense、MoE与量化", APEX section:
+    commonly used experts 4 bits, rarely used experts 2 bits; page "MoE推理优化实战：
+    4bit存储+INT8计算的W4A8路线解析", §5.3: the most-hit experts keep more precision):
+    experts hit less than cold_share times the even share (total / E) get 2 bits, the
+    ceil(frac8 * E) most-hit experts (ties: lower index first) 8 bits -- over the cold
+    rule --, the others 4; a shared expert (hit by every token) 8 bits if frac8 > 0,
+    else 4."""
+    counts = np.asarray(counts, dtype=np.int64)
+    e = counts.shape[0]
+    bits = np.full(e, 4, dtype=np.int64)
+    bits[counts * e < cold_share * counts.sum()] = 2
+    n8 = min(e, int(np.ceil(frac8 * e - 1e-9)))
+    order = np.lexsort((np.arange(e), -counts))
+    bits[order[:n8]] = 8
+    return list(bits) + ([8 if frac8 > 0 else 4] if shared else [])
 
 
 def groups_by_hotness(counts, hot_frac=0.05, cold_share=0.1, shared=False):

@@ -44,7 +44,7 @@ single-element placement.
 """
 import numpy as np
 
-from .quant import GROUP, GROUPS, unpack_canonical
+from .quant import GROUP, GROUPS, unpack_canonical, unpack_crumbs
 
 NIBBLE_POS = np.array([0, 2, 4, 6, 1, 3, 5, 7])
 
@@ -205,6 +205,74 @@ def from_device8(dev, n, k, gate_up):
     q = dev[_offsets8(n, k)].view(np.int8).astype(np.int64)
     so = _a256(n * k)
     sc = dev[so: so + 2 * n * g].view("<u2").reshape(n // 16, g, 16).transpose(0, 2, 1).reshape(n, g)
+    src = column_source(n, gate_up)
+    inv = np.empty_like(src)
+    inv[src] = np.arange(n)
+    return q[inv], sc[inv].astype(np.uint16)
+
+
+# ---------------------------------------------------------------- 2-bit weights
+# INT2 device layout (cold experts): one 512-byte tile per (16-column block cb, group g),
+# tiles cb-major at byte 512 * (cb * G + g).  Lane L in [0, 64) (column c = L % 16,
+# quarter kq = L // 16) owns bytes [8 L, 8 L + 8): two little-endian 32-bit words.  The
+# element k = 128 g + 32 s + 8 kq + e (K step s in [0, 4), e in [0, 8)) is in word s // 2,
+# byte m = e % 4 of that word, bit field f = 2 (s % 2) + e // 4 (bits 8 m + 2 f and
+# 8 m + 2 f + 1), as the unsigned value d = q + 2.  (One shift-and-mask then gives the
+# four elements of a field as bytes, for the INT8 operand; one shift-mask-or gives two
+# of them, four apart in k -- bytes m and m + 2 -- as a bf16 pair under a constant
+# exponent, for the bf16 operand.)  Scales as for INT4, binary16 [N/16][G][16] at byte
+# align256(N K / 4).  Same column orders (plain / gate-up).
+
+def device_bytes2(n, k):
+    return _a256(n * k // 4) + _a256(2 * n * (k // GROUP))
+
+
+def _offsets2(n, k):
+    """(byte offset, bit shift) of every element (column j, k) in device order."""
+    g = k // GROUP
+    jj, kk = np.meshgrid(np.arange(n), np.arange(k), indexing="ij")
+    cb, c = jj // 16, jj % 16
+    gg, r = kk // GROUP, kk % GROUP
+    s, rem = r // 32, r % 32
+    kq, e = rem // 8, rem % 8
+    lane = kq * 16 + c
+    word = s // 2
+    m, f = e % 4, 2 * (s % 2) + e // 4
+    byte = (cb * g + gg) * 512 + lane * 8 + word * 4 + m
+    return byte, 2 * f
+
+
+def to_device2(packed, scale_bits, n, k, gate_up):
+    """Canonical 2-bit bytes [N, K/4] + scale bits [N, G] -> device bytes
+    (device_bytes2(n, k))."""
+    if n % (32 if gate_up else 16) or k % GROUP:
+        raise ValueError("shape not supported by the device layout")
+    g = k // GROUP
+    q = unpack_crumbs(packed, k)
+    src = column_source(n, gate_up)
+    d = (q[src] + 2).astype(np.int64)
+    s = np.asarray(scale_bits, dtype=np.uint16)[src]
+    out = np.zeros(device_bytes2(n, k), dtype=np.uint8)
+    byte, shift = _offsets2(n, k)
+    acc = np.zeros(n * k // 4, dtype=np.int64)
+    np.add.at(acc, byte.ravel(), (d << shift).ravel())
+    out[: n * k // 4] = acc.astype(np.uint8)
+    so = _a256(n * k // 4)
+    sc = s.reshape(n // 16, 16, g).transpose(0, 2, 1).reshape(-1)
+    out[so: so + 2 * n * g] = sc.astype("<u2").view(np.uint8)
+    return out
+
+
+def from_device2(dev, n, k, gate_up):
+    """Device bytes -> (q int64 [N, K] in [-2, 1], scale bits uint16 [N, G]) in canonical
+    row order."""
+    g = k // GROUP
+    dev = np.asarray(dev, dtype=np.uint8).astype(np.int64)
+    byte, shift = _offsets2(n, k)
+    q = ((dev[byte] >> shift) & 0x3) - 2
+    so = _a256(n * k // 4)
+    sc = np.asarray(dev[so: so + 2 * n * g], dtype=np.uint8).view("<u2")
+    sc = sc.reshape(n // 16, g, 16).transpose(0, 2, 1).reshape(n, g)
     src = column_source(n, gate_up)
     inv = np.empty_like(src)
     inv[src] = np.arange(n)

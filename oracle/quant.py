@@ -31,7 +31,10 @@ definitions with groups of ``group`` elements along K (K a multiple of it); the
 scale tables then have K / group columns.  The group of a quantised matrix is implied
 by its shapes (K / number of scale columns).
 
-Pinned by (tests/test_oracle_quant.py, tests/test_oracle_groups.py): brute-force nearest-code search over
+2-bit codes for cold experts (quantize_sym2, pack_crumbs): see quantize_sym2.
+
+Pinned by (tests/test_oracle_quant.py, tests/test_oracle_groups.py, tests/test_oracle_int2.py):
+brute-force nearest-code search over
 all 16 codes for every element, the half-step error bound, constructed exact
 ties (half-to-even), the +-7 / code-0 invariants, exhaustive nibble
 round-trip of all 256 bytes, and the packed-size formula against the "about
@@ -146,6 +149,60 @@ def quantize_sym8(w):
     q[nz] = np.rint(wg[nz] / s32[nz][:, None])
     q = np.clip(q, -127, 127)
     return q.reshape(np.asarray(w).shape).astype(np.int8), s16
+
+
+def quantize_sym2(w):
+    """Symmetric INT2 g128 quantisation: the cold-expert format.
+
+    Returns (q int8 [N, K] in [-2, 1], scales float16 [N, K/128]).  Page "大模型之
+    Dense、MoE与量化", APEX section: experts get precision by importance, commonly
+    used experts 4 bits and rarely used ("cold") experts 2 bits.  The page does not
+    spell the 2-bit format out; it takes the INT4 format's structure with b = 2: per
+    group of 128 along K, s = amax / (2^(b-1) - 1) = amax, q = clamp(rint(w / s), -2, 1)
+    with the stored scale (IEEE fp32 division, half-to-even), two's-complement codes,
+    four per byte.  The scale is amax rounded *upward* to binary16 (as for the 8-bit
+    format): with a single positive level, a nearest-even scale below amax (subnormal
+    for tiny groups) would clamp the group maximum past half a step.  So |w / s| <= 1
+    and the codes are -1, 0 and 1 (-2, like -8 in INT4, is never produced); a zero
+    scale gives codes 0.
+    """
+    wg = _groups(w)
+    amax = np.max(np.abs(wg), axis=2)
+    s16 = f32_to_f16_up(amax)
+    if not np.all(np.isfinite(s16)):
+        raise ValueError("scale overflows binary16")
+    s32 = s16.astype(np.float32)
+    q = np.zeros(wg.shape, dtype=np.float32)
+    nz = s32 > 0
+    q[nz] = np.rint(wg[nz] / s32[nz][:, None])
+    q = np.clip(q, -2, 1)
+    return q.reshape(np.asarray(w).shape).astype(np.int8), s16
+
+
+def pack_crumbs(codes):
+    """Four 2-bit codes per byte along the last axis, index 4 j + i in bits 2 i, 2 i + 1
+    of byte j (two's complement, code & 3); a partial last byte is zero-padded."""
+    c = np.asarray(codes).astype(np.int64) & 0x3
+    pad = (-c.shape[-1]) % 4
+    if pad:
+        c = np.concatenate([c, np.zeros(c.shape[:-1] + (pad,), dtype=np.int64)], axis=-1)
+    out = c[..., 0::4] | (c[..., 1::4] << 2) | (c[..., 2::4] << 4) | (c[..., 3::4] << 6)
+    return out.astype(np.uint8)
+
+
+def unpack_crumbs(packed, count):
+    """Inverse of pack_crumbs: the first ``count`` signed codes along the last axis."""
+    p = np.asarray(packed, dtype=np.int64)
+    out = np.empty(p.shape[:-1] + (4 * p.shape[-1],), dtype=np.int64)
+    for i in range(4):
+        out[..., i::4] = (p >> (2 * i)) & 0x3
+    out = out[..., :count]
+    return np.where(out >= 2, out - 4, out)
+
+
+def packed_bytes2(n, k):
+    """Bytes of the canonical 2-bit format: N*K/4 code bytes + 2*N*(K/128) scale bytes."""
+    return n * k // 4 + 2 * n * (k // GROUP)
 
 
 def dequantize(q, scales, zeros=None):
