@@ -362,6 +362,25 @@ Q4_API int moe_int4_ffn_debug(const q4_moe_layer_t* layer, const uint16_t* x_bf1
                        q4_ffn_views_t* views, hipStream_t stream);
 
 /*
+ * moe_int4_ffn_forward_noalloc -- for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * moe_int4_ffn_forward with the same arguments minus the workspace.  Its workspace is
+ * a file-scope device array of Q4_NOALLOC_SCRATCH_BYTES in the library, one per GPU,
+ * held until the process ends; the call allocates nothing (no hipMalloc / hipFree,
+ * no allocating library routine).  Batches whose workspace
+ * (moe_int4_ffn_workspace_bytes) exceeds that size return Q4_ERR_WORKSPACE.  Every
+ * call on a GPU shares that GPU's array: calls that overlap on one GPU (other
+ * streams, other threads) race and must be serialised by the caller.  The first call
+ * on a device looks up the array's device address (hipGetSymbolAddress).
+ * Results equal moe_int4_ffn_forward's bit for bit (same kernels).
+ */
+#define Q4_NOALLOC_SCRATCH_BYTES (64u * 1024u * 1024u)
+#define Q4_MAX_DEVICES 64
+Q4_API int moe_int4_ffn_forward_noalloc(const q4_moe_layer_t* layer, const uint16_t* x_bf16, int64_t t,
+                                        const int32_t* topk_ids, const float* topk_w, int mode,
+                                        uint16_t* out_bf16, hipStream_t stream);
+
+/*
  * moe_int4_ffn_plan -- host-only query of the launch plan moe_int4_ffn_forward uses
  * for (layer, t, mode); no device work, no pointer is dereferenced except layer.
  *  kernel         Q4_PLAN_DECODE: the streaming GEMM kernel with 16 / 32 / 64-row tiles

@@ -28,6 +28,7 @@ Q4_ERR_WORKSPACE, Q4_ERR_UNSUPPORTED, Q4_ERR_HIP = 5, 6, 7
 Q4_F32, Q4_F16, Q4_BF16 = 0, 1, 2
 Q4_W4A16, Q4_W4A8, Q4_W8A8 = 0, 1, 2
 Q4_REPACK_PLAIN, Q4_REPACK_GATE_UP = 0, 1
+Q4_NOALLOC_SCRATCH_BYTES = 64 * 1024 * 1024
 Q4_QFLAG_NONFINITE, Q4_QFLAG_SCALE_OVERFLOW = 1, 2
 
 _vp, _i64, _i32, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
@@ -105,6 +106,7 @@ _sig("moe_lora_ffn_forward", _int, [ctypes.POINTER(Q4LoraLayer), _vp, _i64, _vp,
 _sig("int4_linear_forward", _int, [_vp, _int, _i64, _i64, _vp, _i64, _int, _vp, _vp])
 _sig("int4_w4a8_group_acc", _int, [_vp, _i64, _i64, _vp, _i64, _int, _vp, _vp])
 
+_sig("moe_int4_ffn_forward_noalloc", _int, [ctypes.POINTER(Q4MoELayer), _vp, _i64, _vp, _vp, _int, _vp, _vp])
 _sig("moe_int4_ffn_plan", _int, [ctypes.POINTER(Q4MoELayer), _i64, _int, ctypes.POINTER(Q4FfnPlan)])
 _sig("moe_expert_bits_by_hotness", _int, [ctypes.POINTER(_i64), _i32, ctypes.c_double, _int, ctypes.POINTER(_i32)])
 _sig("moe_expert_groups_by_hotness", _int, [ctypes.POINTER(_i64), _i32, ctypes.c_double, ctypes.c_double, _int,
@@ -483,6 +485,24 @@ def moe_int4_ffn_forward(layer, x, ids, weights, mode=Q4_W4A16, out=None, worksp
     _check("moe_int4_ffn_forward", _lib.moe_int4_ffn_forward(
         ctypes.byref(layer.desc), _ptr(x), t, _ptr(ids), _ptr(weights), mode, _ptr(out),
         _ptr(workspace), workspace.numel(), _stream()))
+    return out
+
+
+def moe_int4_ffn_forward_noalloc(layer, x, ids, weights, mode=Q4_W4A16, out=None):
+    """moe_int4_ffn_forward with the library's own fixed device scratch as workspace
+    (moe_int4_ffn_forward_noalloc): no workspace argument, no device allocation in the
+    call; batches whose workspace exceeds the scratch size raise Q4Error."""
+    _need(x, torch.bfloat16, "x", 2)
+    _need(ids, torch.int32, "ids", 2)
+    _need(weights, torch.float32, "weights", 2)
+    t = x.shape[0]
+    if x.shape[1] != layer.hidden or tuple(ids.shape) != (t, layer.top_k) or tuple(weights.shape) != (t, layer.top_k):
+        raise ValueError("shape mismatch between x, ids, weights and the layer")
+    if out is None:
+        out = torch.empty_like(x)
+    _need(out, torch.bfloat16, "out", 2)
+    _check("moe_int4_ffn_forward_noalloc", _lib.moe_int4_ffn_forward_noalloc(
+        ctypes.byref(layer.desc), _ptr(x), t, _ptr(ids), _ptr(weights), mode, _ptr(out), _stream()))
     return out
 
 

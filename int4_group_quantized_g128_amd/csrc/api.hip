@@ -5,6 +5,7 @@
 #include <cstring>
 #include <string>
 #include <cmath>
+#include <mutex>
 #include <vector>
 
 #include "../../include/q4moe.h"
@@ -690,6 +691,63 @@ int moe_int4_ffn_debug(const q4_moe_layer_t* L, const uint16_t* x_bf16, int64_t 
     return Q4_ERR_NULL;
   }
   return ffn_forward(L, x_bf16, t, topk_ids, topk_w, mode, out_bf16, workspace, ws_bytes, stream, views);
+}
+
+}  // extern "C"
+
+// ------------------------------------------------------------------ allocation-free forward
+// The forward's workspace in a file-scope device array, one copy per GPU, for callers
+// that cannot allocate.  Host code never passes `scratch` itself (on the host it only
+// names the symbol): its device address is looked up once per device with
+// hipGetSymbolAddress and that address is what the kernels get.  Nothing in the
+// forward's workspace needs to start at zero (every buffer is written before it is
+// read), so the last call's contents do no harm; overlapping calls on one GPU race.
+static __device__ __align__(256) uint8_t scratch[Q4_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[Q4_MAX_DEVICES] = {};
+
+// Device address of this device's scratch array (looked up on the first call with the
+// device current), or NULL with the error text set.
+void* scratch_for_current_device(int* rc) {
+  int dev = -1;
+  if ((*rc = check_hip(hipGetDevice(&dev), "hipGetDevice"))) return nullptr;
+  if (dev < 0 || dev >= Q4_MAX_DEVICES) {
+    *rc = fail(Q4_ERR_UNSUPPORTED, "device %d beyond the %d this build tracks", dev, Q4_MAX_DEVICES);
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if ((*rc = check_hip(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)"))) return nullptr;
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_int4_ffn_forward_noalloc(const q4_moe_layer_t* L, const uint16_t* x_bf16, int64_t t, const int32_t* topk_ids,
+                                 const float* topk_w, int mode, uint16_t* out_bf16, hipStream_t stream) {
+  g_last_error.clear();
+  if (int rc = validate_layer(L)) return rc;
+  Q4_REQUIRE(mode_ok(L, mode), Q4_ERR_DTYPE, "mode %d does not match the layer's weight format", mode);
+  Q4_REQUIRE(t >= 0, Q4_ERR_SHAPE, "t < 0");
+  if (t == 0) return ok();
+  Q4_REQUIRE(t * (L->top_k + (L->shared_inter > 0 ? 1 : 0)) < (int64_t(1) << 31), Q4_ERR_SHAPE, "t too large");
+  const int64_t need = carve(L, t, mode, nullptr).bytes;
+  Q4_REQUIRE(need <= int64_t(Q4_NOALLOC_SCRATCH_BYTES), Q4_ERR_WORKSPACE,
+             "t = %lld needs %lld workspace bytes; the allocation-free forward holds %lld", (long long)t,
+             (long long)need, (long long)Q4_NOALLOC_SCRATCH_BYTES);
+  int rc = Q4_OK;
+  void* ws = scratch_for_current_device(&rc);
+  if (!ws) return rc;
+  return ffn_forward(L, x_bf16, t, topk_ids, topk_w, mode, out_bf16, ws, size_t(Q4_NOALLOC_SCRATCH_BYTES), stream,
+                     nullptr);
 }
 
 // ------------------------------------------------------------------ LoRA-mode experts
