@@ -138,9 +138,9 @@ class Workload:
     def expert_bytes(self, bits=None, group=128):
         """Canonical packed bytes of one expert: codes (4- or 8-bit) + fp16 scales (+ zero points)."""
         h, i = self.cfg["hidden"], self.cfg["inter"]
-        cb = (bits or self.wbits) // 4     # code bytes per 2 weights
-        gu = 2 * i * h * cb // 2 + 2 * i * (h // group) * 2
-        dn = h * i * cb // 2 + h * (i // group) * 2
+        b = bits or self.wbits             # code bits per weight
+        gu = 2 * i * h * b // 8 + 2 * i * (h // group) * 2
+        dn = h * i * b // 8 + h * (i // group) * 2
         if self.cfg["asymmetric"]:
             gu += 2 * i * ((h // 128 + 1) // 2)
             dn += h * ((i // 128 + 1) // 2)
@@ -445,6 +445,17 @@ def hotness_bits(lib, torch, synth, cfg_name, frac8, calib_tokens=4096):
     return lib.expert_bits_by_hotness(counts, frac8, shared=bool(cfg.get("shared", False)))
 
 
+def hotness_apex(lib, torch, synth, cfg_name, cold_share=0.25, calib_tokens=4096):
+    """APEX widths from hit counts of the same calibration batch: experts hit less than
+    cold_share times the even share 2 bits, the others (and the shared expert) 4."""
+    cfg = synth.CONFIGS[cfg_name]
+    x = synth.tokens(cfg_name, calib_tokens, device="cuda", salt=7)
+    wr, b = synth.router_weights(cfg_name, device="cuda")
+    _, ids, _ = lib.moe_route_topk(x, wr, b, cfg["top_k"])
+    counts = torch.bincount(ids.reshape(-1).long(), minlength=cfg["experts"]).cpu().tolist()
+    return lib.expert_bits_apex(counts, 0.0, cold_share, shared=bool(cfg.get("shared", False)))
+
+
 def hotness_groups(lib, torch, synth, cfg_name, calib_tokens=4096):
     """Per-expert group sizes from routing hit counts of the same calibration batch: the
     top 5 % of the experts 32, experts under a tenth of the even share 256, others 64."""
@@ -610,6 +621,16 @@ def main():
                 b == 8 for b in bits))
             del mt
         del mx
+        torch.cuda.empty_cache()
+        log("[bench] extra moe256 APEX widths (experts under a quarter of the even share in 2 bits), W4A8")
+        abits = hotness_apex(lib, torch, synth, "moe256")
+        aw = Workload(lib, torch, synth, "moe256", args.tokens, "mixed", expert_bits=abits)
+        for t in (args.tokens, 4096):
+            at = aw if t == args.tokens else aw.retoken(synth, t)
+            s9, st9 = time_steps(torch, at, 10 if t > 1000 else 50, 3, stage_events=True, graph=not args.no_graph)
+            extra[f"moe256_T{t}_apex_int2"] = dict(summarize(at, s9, st9), experts_2bit=sum(b == 2 for b in abits))
+            del at
+        del aw
         torch.cuda.empty_cache()
         log("[bench] extra moe256 per-expert group sizes (hit counts: top 5 % 32, cold 256, others 64)")
         groups = hotness_groups(lib, torch, synth, "moe256")

@@ -188,6 +188,29 @@ Q4_API int q8_repack_device(const int8_t* q, const uint16_t* scales, int64_t n, 
                      void* dev_out, size_t dev_bytes, hipStream_t stream);
 
 /*
+ * quantize_int2_g128 / q2_device_bytes / q2_repack_device -- 2-bit g128 weights for
+ * rarely used ("cold") experts (page "大模型之Dense、MoE与量化", APEX section: experts
+ * get precision by importance, commonly used ones 4 bits, cold ones 2 bits).  The INT4
+ * format's structure with two bits: per row and group of 128, s = binary16 rounded up
+ * of fp32(amax) (so |w / s| <= 1), q = clamp(rint(w / s), -2, 1) (IEEE fp32 division
+ * by the stored scale, half-to-even; -2 is never produced); a zero scale gives codes 0.
+ *  packed  device [n][k/4] bytes, four two's-complement codes per byte, k = 4 j + i in
+ *          bits 2 i, 2 i + 1 of byte j.   scales device [n][k/128] binary16 bits.
+ *  flags_dev as for quantize_int4_g128.
+ * Device layout (this library's own): one 512-byte tile per (16-column block cb,
+ * group g), cb-major; lane L (column L % 16, quarter kq = L / 16) owns 8 bytes, two
+ * little-endian words; element k = 128 g + 32 s + 8 kq + e sits in word s / 2, byte
+ * e % 4, bit field 2 (s % 2) + e / 4 (bits 2 f, 2 f + 1 of the byte) as d = q + 2.
+ * Scales binary16 [n/16][k/128][16] at byte align256(n k / 4).  Column orders as for
+ * q4_repack_device.
+ */
+Q4_API int quantize_int2_g128(const void* w, int w_dtype, int64_t n, int64_t k, uint8_t* packed, uint16_t* scales,
+                              int32_t* flags_dev, hipStream_t stream);
+Q4_API size_t q2_device_bytes(int64_t n, int64_t k);
+Q4_API int q2_repack_device(const uint8_t* packed, const uint16_t* scales, int64_t n, int64_t k, int flags,
+                            void* dev_out, size_t dev_bytes, hipStream_t stream);
+
+/*
  * moe_route_topk -- A3 + A4: fp32 router logits, top-k and renormalised weights.
  * (Dense/MoE page, MoE section: a Linear router; W4A8 page §3.2: router kept in float.)
  *
@@ -265,9 +288,11 @@ typedef struct q4_moe_layer_t {
    * different precisions by importance).  When expert_bits != NULL: weight_bits must be
    * 0, asymmetric 0 and mode Q4_W4A8 (INT8 activations for every expert); expert e's
    * gate/up block starts at byte gate_up_offsets[e] of gate_up (down: down_offsets[e]
-   * of down) and holds q4_device_bytes(., ., 0) or q8_device_bytes(., .) bytes by its
-   * bits; the shared expert's bits are expert_bits[num_experts]. */
-  const uint8_t* expert_bits;      /* device [num_experts + shared] values 4 or 8 */
+   * of down) and holds q4_device_bytes(., ., 0), q8_device_bytes(., .) or
+   * q2_device_bytes(., .) bytes by its bits; the shared expert's bits are
+   * expert_bits[num_experts].  2-bit experts (group 128) run on the streaming GEMM
+   * kernel at every batch size. */
+  const uint8_t* expert_bits;      /* device [num_experts + shared] values 2, 4 or 8 */
   const int64_t* gate_up_offsets;  /* device [num_experts] */
   const int64_t* down_offsets;     /* device [num_experts] */
   /* Per-expert group size (page "MoE推理优化实战：4bit存储+INT8计算的W4A8路线解析",
@@ -428,6 +453,11 @@ Q4_API int moe_int4_ffn_plan(const q4_moe_layer_t* layer, int64_t t, int mode, q
 Q4_API int moe_expert_bits_by_hotness(const int64_t* counts, int32_t e, double frac8, int shared, int32_t* bits_out);
 Q4_API int moe_expert_groups_by_hotness(const int64_t* counts, int32_t e, double hot_frac, double cold_share,
                                         int shared, int32_t* groups_out);
+/*  bits (APEX): experts with counts[i] * e < cold_share * sum(counts) 2 bits, the
+ *          ceil(frac8 * e) most-hit experts 8 bits (over the cold rule), the others 4;
+ *          shared: 8 if frac8 > 0, else 4. */
+Q4_API int moe_expert_bits_apex(const int64_t* counts, int32_t e, double frac8, double cold_share, int shared,
+                                int32_t* bits_out);
 
 /*
  * q4_lora_layer_t / moe_lora_ffn_forward -- LoRA-mode experts (page
@@ -497,6 +527,16 @@ Q4_API int int4_linear_forward(const void* x, int x_dtype, int64_t t, int64_t k,
  */
 Q4_API int int4_w4a8_group_acc(const int8_t* q, int64_t rows, int64_t k, const void* w_dev, int64_t n,
                         int asymmetric, int32_t* acc, hipStream_t stream);
+
+/*
+ * int2_w2a8_group_acc -- the INT32 group accumulators of the 2-bit core,
+ * acc[r][c][g] = sum_{k in group g} q[r][k] * code[c][k], same MFMA core as the forward.
+ *  q      device [rows][k] int8 activation codes.
+ *  w_dev  q2_repack_device output (Q4_REPACK_PLAIN) of an [n][k] matrix.
+ *  acc    device [rows][n][k/128] int32.   Requires k % 128 == 0, n % 64 == 0.
+ */
+Q4_API int int2_w2a8_group_acc(const int8_t* q, int64_t rows, int64_t k, const void* w_dev, int64_t n,
+                               int32_t* acc, hipStream_t stream);
 
 /*
  * int8_w8a8_group_acc -- the INT32 group accumulators of the W8A8 core,

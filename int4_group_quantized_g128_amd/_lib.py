@@ -91,6 +91,12 @@ _sig("q4_device_bytes_grouped", _sz, [_i64, _i64, _int, _i32])
 _sig("q4_repack_device_grouped", _int, [_vp, _vp, _vp, _i64, _i64, _int, _i32, _int, _vp, _sz, _vp])
 _sig("quantize_int8_g128", _int, [_vp, _int, _i64, _i64, _vp, _vp, _vp, _vp])
 _sig("q8_device_bytes", _sz, [_i64, _i64])
+_sig("quantize_int2_g128", _int, [_vp, _int, _i64, _i64, _vp, _vp, _vp, _vp])
+_sig("q2_device_bytes", _sz, [_i64, _i64])
+_sig("q2_repack_device", _int, [_vp, _vp, _i64, _i64, _int, _vp, _sz, _vp])
+_sig("int2_w2a8_group_acc", _int, [_vp, _i64, _i64, _vp, _i64, _vp, _vp])
+_sig("moe_expert_bits_apex", _int, [ctypes.POINTER(_i64), _i32, ctypes.c_double, ctypes.c_double, _int,
+                                    ctypes.POINTER(_i32)])
 _sig("q8_repack_device", _int, [_vp, _vp, _i64, _i64, _int, _vp, _sz, _vp])
 _sig("int8_w8a8_group_acc", _int, [_vp, _i64, _i64, _vp, _i64, _vp, _vp])
 _sig("moe_route_workspace_bytes", _sz, [_i64, _i64, _i32])
@@ -197,6 +203,31 @@ def q8_repack_device(q, scales, n, k, gate_up=False, out=None):
     _check("q8_repack_device", _lib.q8_repack_device(
         _ptr(q), _ptr(scales), n, k, Q4_REPACK_GATE_UP if gate_up else Q4_REPACK_PLAIN, _ptr(out), out.numel(),
         _stream()))
+    return out
+
+
+def quantize_int2_g128(w, flags=None):
+    """2-bit g128 quantisation on the GPU: (packed uint8 [n, k/4], scale bits int16 [n, k/128])."""
+    _need(w, (torch.float32, torch.float16, torch.bfloat16), "w", 2)
+    n, k = w.shape
+    packed = torch.empty((n, k // 4), dtype=torch.uint8, device=w.device)
+    scales = torch.empty((n, k // 128), dtype=torch.int16, device=w.device)
+    _check("quantize_int2_g128", _lib.quantize_int2_g128(_ptr(w), _DT[w.dtype], n, k, _ptr(packed), _ptr(scales),
+                                                         _ptr(flags), _stream()))
+    return packed, scales
+
+
+def q2_device_bytes(n, k):
+    return int(_lib.q2_device_bytes(n, k))
+
+
+def q2_repack_device(packed, scales, n, k, gate_up=False, out=None):
+    nbytes = q2_device_bytes(n, k)
+    if out is None:
+        out = torch.empty(nbytes, dtype=torch.uint8, device=packed.device)
+    _check("q2_repack_device", _lib.q2_repack_device(_ptr(packed), _ptr(scales), n, k,
+                                                     Q4_REPACK_GATE_UP if gate_up else Q4_REPACK_PLAIN,
+                                                     _ptr(out), out.numel(), _stream()))
     return out
 
 
@@ -328,6 +359,12 @@ def expert_bits_by_hotness(counts, frac8=0.05, shared=False):
     return _hotness("moe_expert_bits_by_hotness", counts, shared, float(frac8))
 
 
+def expert_bits_apex(counts, frac8=0.0, cold_share=0.25, shared=False):
+    """Per-expert widths (2, 4 or 8) from routing hit counts; the rule is the C library's
+    moe_expert_bits_apex (host arrays, no device work)."""
+    return _hotness("moe_expert_bits_apex", counts, shared, float(frac8), float(cold_share))
+
+
 def expert_groups_by_hotness(counts, hot_frac=0.05, cold_share=0.1, shared=False):
     """Per-expert group sizes (32, 64 or 256) from routing hit counts; the rule is the C
     library's moe_expert_groups_by_hotness (host arrays, no device work)."""
@@ -373,20 +410,22 @@ class MoELayer:
         self.groups = groups
         if expert_bits is not None:
             bits = [int(b) for b in expert_bits]
-            if len(bits) != num_experts + int(self.shared) or any(b not in (4, 8) for b in bits):
-                raise ValueError("expert_bits needs one width, 4 or 8, per expert (and the shared expert)")
+            if len(bits) != num_experts + int(self.shared) or any(b not in (2, 4, 8) for b in bits):
+                raise ValueError("expert_bits needs one width, 2, 4 or 8, per expert (and the shared expert)")
             if asymmetric:
                 raise ValueError("mixed layers are symmetric")
         else:
             bits = [weight_bits] * nexp
-        if any(b == 8 and g != 128 for b, g in zip(bits, groups)):
-            raise ValueError("8-bit experts use groups of 128")
+        if any(b != 4 and g != 128 for b, g in zip(bits, groups)):
+            raise ValueError("2- and 8-bit experts use groups of 128")
         self.bits = bits
         self.weight_bits = 0 if self.mixed else weight_bits
 
         def sizes(b, g):
             if b == 8:
                 return q8_device_bytes(2 * inter, hidden), q8_device_bytes(hidden, inter)
+            if b == 2:
+                return q2_device_bytes(2 * inter, hidden), q2_device_bytes(hidden, inter)
             return (q4_device_bytes_grouped(2 * inter, hidden, asymmetric, g),
                     q4_device_bytes_grouped(hidden, inter, asymmetric, g))
 
@@ -441,6 +480,12 @@ class MoELayer:
             q8_repack_device(q, s, 2 * I, H, gate_up=True, out=gu_out)
             q, s = quantize_int8_g128(down.contiguous())
             q8_repack_device(q, s, H, I, gate_up=False, out=dn_out)
+            return
+        if self.bits[e] == 2:
+            q, s = quantize_int2_g128(torch.cat([gate, up], dim=0).contiguous())
+            q2_repack_device(q, s, 2 * I, H, gate_up=True, out=gu_out)
+            q, s = quantize_int2_g128(down.contiguous())
+            q2_repack_device(q, s, H, I, gate_up=False, out=dn_out)
             return
         if self.groups[e] != 128:
             grp = self.groups[e]
@@ -646,6 +691,17 @@ def int8_w8a8_group_acc(q, w_dev, n):
     acc = torch.empty((rows, n, k // 128), dtype=torch.int32, device=q.device)
     _check("int8_w8a8_group_acc", _lib.int8_w8a8_group_acc(
         _ptr(q), rows, k, _ptr(w_dev), n, _ptr(acc), _stream()))
+    return acc
+
+
+def int2_w2a8_group_acc(q, w_dev, n):
+    """INT32 group accumulators acc [rows, n, k/128] of int8 codes q [rows, k] with a
+    2-bit device-layout weight."""
+    _need(q, torch.int8, "q", 2)
+    _need(w_dev, torch.uint8, "w_dev")
+    rows, k = q.shape
+    acc = torch.empty((rows, n, k // 128), dtype=torch.int32, device=q.device)
+    _check("int2_w2a8_group_acc", _lib.int2_w2a8_group_acc(_ptr(q), rows, k, _ptr(w_dev), n, _ptr(acc), _stream()))
     return acc
 
 

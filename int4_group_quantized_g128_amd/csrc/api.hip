@@ -61,7 +61,7 @@ struct FwdWorkspace {
   int32_t* inv = nullptr;
   TileDesc* tiles = nullptr;
   int32_t* num_tiles = nullptr;
-  int32_t* fmt_tiles = nullptr;   // [5] tile range of each weight format
+  int32_t* fmt_tiles = nullptr;   // [kNumFormats + 1] tile range of each weight format
   void* h = nullptr;
   float* y = nullptr;
   int8_t* qx = nullptr;
@@ -158,7 +158,7 @@ FwdWorkspace carve(const q4_moe_layer_t* L, int64_t t, int mode, void* base) {
   w.inv = reinterpret_cast<int32_t*>(take(P * 4));
   w.tiles = reinterpret_cast<TileDesc*>(take(int64_t(w.max_tiles) * sizeof(TileDesc)));
   w.num_tiles = reinterpret_cast<int32_t*>(take(4));
-  w.fmt_tiles = reinterpret_cast<int32_t*>(take(5 * 4));
+  w.fmt_tiles = reinterpret_cast<int32_t*>(take((kNumFormats + 1) * 4));
   w.h = take(P * I * (int8_acts(mode) ? 4 : 2));
   // Decode down projections with few work items (narrow layers: the dense FFN, a few
   // touched experts) split K over workgroups, aiming at about 512 items; the combine sums
@@ -386,6 +386,36 @@ int q8_repack_device(const int8_t* q, const uint16_t* scales, int64_t n, int64_t
   return check_hip(launch_repack8(q, scales, n, k, flags == Q4_REPACK_GATE_UP, dev_out, stream), "repack8 launch");
 }
 
+int quantize_int2_g128(const void* w, int w_dtype, int64_t n, int64_t k, uint8_t* packed, uint16_t* scales,
+                       int32_t* flags_dev, hipStream_t stream) {
+  g_last_error.clear();
+  Q4_REQUIRE(w_dtype == Q4_F32 || w_dtype == Q4_F16 || w_dtype == Q4_BF16, Q4_ERR_DTYPE, "w_dtype %d", w_dtype);
+  Q4_REQUIRE(n >= 1 && k >= 128 && k % 128 == 0, Q4_ERR_SHAPE, "need n >= 1 and k a positive multiple of 128");
+  Q4_REQUIRE(n * (k / 128) < (int64_t(1) << 31), Q4_ERR_SHAPE, "matrix too large");
+  Q4_REQUIRE(w && packed && scales, Q4_ERR_NULL, "w, packed and scales are required");
+  Q4_REQUIRE(!misaligned(w) && !misaligned(packed) && !misaligned(scales), Q4_ERR_ALIGN,
+             "device pointers must be 16-byte aligned");
+  return check_hip(launch_quantize2(w, w_dtype, n, k, packed, scales, flags_dev, stream), "quantize2 launch");
+}
+
+size_t q2_device_bytes(int64_t n, int64_t k) {
+  if (n < 16 || n % 16 || k < 128 || k % 128) return 0;
+  return size_t(a256(n * k / 4) + a256(2 * n * (k / 128)));
+}
+
+int q2_repack_device(const uint8_t* packed, const uint16_t* scales, int64_t n, int64_t k, int flags, void* dev_out,
+                     size_t dev_bytes, hipStream_t stream) {
+  g_last_error.clear();
+  Q4_REQUIRE(flags == Q4_REPACK_PLAIN || flags == Q4_REPACK_GATE_UP, Q4_ERR_DTYPE, "flags %d", flags);
+  Q4_REQUIRE(k >= 128 && k % 128 == 0 && n >= 16 && n % (flags == Q4_REPACK_GATE_UP ? 32 : 16) == 0,
+             Q4_ERR_SHAPE, "need k %% 128 == 0 and n %% %d == 0", flags == Q4_REPACK_GATE_UP ? 32 : 16);
+  Q4_REQUIRE(packed && scales && dev_out, Q4_ERR_NULL, "packed, scales and dev_out are required");
+  Q4_REQUIRE(!misaligned(packed) && !misaligned(dev_out), Q4_ERR_ALIGN, "device pointers must be 16-byte aligned");
+  Q4_REQUIRE(dev_bytes >= q2_device_bytes(n, k), Q4_ERR_WORKSPACE, "dev_out holds %zu bytes, need %zu", dev_bytes,
+             q2_device_bytes(n, k));
+  return check_hip(launch_repack2(packed, scales, n, k, flags == Q4_REPACK_GATE_UP, dev_out, stream), "repack2 launch");
+}
+
 size_t moe_route_workspace_bytes(int64_t t, int64_t h, int32_t e) {
   if (t <= 0 || h <= 0 || e <= 0) return 0;
   return size_t(route_kslices(t, h, e)) * size_t(t) * size_t(e) * sizeof(float);
@@ -485,6 +515,22 @@ int moe_expert_bits_by_hotness(const int64_t* counts, int32_t e, double frac8, i
   for (int32_t i = 0; i < e; ++i) bits_out[i] = 4;
   for (int64_t i = 0; i < n8; ++i) bits_out[order[i]] = 8;
   if (shared) bits_out[e] = 8;   // the shared expert sees every token
+  return ok();
+}
+
+int moe_expert_bits_apex(const int64_t* counts, int32_t e, double frac8, double cold_share, int shared,
+                         int32_t* bits_out) {
+  g_last_error.clear();
+  if (int rc = check_counts(counts, e, bits_out)) return rc;
+  Q4_REQUIRE(frac8 >= 0.0 && frac8 <= 1.0 && cold_share >= 0.0, Q4_ERR_SHAPE,
+             "frac8 must lie in [0, 1] and cold_share be >= 0");
+  int64_t total = 0;
+  for (int32_t i = 0; i < e; ++i) total += counts[i];
+  for (int32_t i = 0; i < e; ++i) bits_out[i] = double(counts[i] * e) < cold_share * double(total) ? 2 : 4;
+  const std::vector<int32_t> order = by_hotness(counts, e);
+  const int64_t n8 = top_count(frac8, e);
+  for (int64_t i = 0; i < n8; ++i) bits_out[order[i]] = 8;
+  if (shared) bits_out[e] = frac8 > 0.0 ? 8 : 4;
   return ok();
 }
 
@@ -589,27 +635,35 @@ int ffn_forward(const q4_moe_layer_t* L, const uint16_t* x_bf16, int64_t t, cons
     return w.prefill ? launch_gemm_prefill(g, act, kind, stream) : launch_gemm(g, act, kind, rb, stream);
   };
   // Layers whose experts differ in width or group size: the permutation orders the row
-  // tiles by weight format (0: 4-bit, one scale entry per tile; 1: two; 2: four; 3: 8-bit)
-  // and one launch per format walks that format's tile range.  The bf16 prefill kernel
+  // tiles by weight format (0: 4-bit, one scale entry per tile; 1: two; 2: four; 3: 8-bit;
+  // 4: 2-bit) and one launch per format walks that format's tile range.  The 2-bit
+  // experts (rarely routed ones) always run on the streaming kernel; in a prefill-sized
+  // launch it walks the 128-row tiles in 64-row sub-tiles.  The bf16 prefill kernel
   // reads activation sums per scale group; they are recomputed at each launch's
   // granularity (rs_a: the activations, rs_rows their rows) before it.
   // The decode GEMM takes all 4-bit formats in one launch (each item picks its expert's
   // scale entries per tile).
   auto gemm = [&](const GemmArgs& g, int act, int kind, const void* rs_a = nullptr, int64_t rs_rows = 0) {
     if (!g.ebits && !g.egroups) return gemm1(g, act, kind);
-    for (int f = 0; f < 4; ++f) {
+    for (int f = 0; f < kNumFormats; ++f) {
       {
-        if (f == 3 && !g.ebits) continue;
+        if (f >= 3 && !g.ebits) continue;
         if ((f == 1 || f == 2) && !g.egroups) continue;
         const bool merged = !w.prefill && g.egroups && f < 3;   // formats 0..2 in one decode launch
         if (merged && f > 0) continue;
         const int sg = merged ? -1 : f == 2 ? 4 : f == 1 ? 2 : 1;
         GemmArgs a = g;
-        a.wbits = f == 3 ? 8 : 4;
+        a.wbits = f == 3 ? 8 : f == 4 ? 2 : 4;
         a.sg = sg;
         a.fmt_tiles = w.fmt_tiles;
         a.fmt = f;
         a.fmt_end = merged ? 3 : f + 1;
+        if (f == 4) {
+          if (w.prefill) a.built_rows = w.tile_rows;
+          const hipError_t e = launch_gemm(a, act, kind, w.prefill ? 4 : rb, stream);
+          if (e != hipSuccess) return e;
+          continue;
+        }
         if (rs_a && a.a_gsum) {
           const hipError_t e = launch_rowsum(rs_a, 0, rs_rows, a.K, const_cast<float*>(a.a_gsum), stream, sg);
           if (e != hipSuccess) return e;
@@ -927,6 +981,27 @@ int int8_w8a8_group_acc(const int8_t* q, int64_t rows, int64_t k, const void* w_
   g.w = static_cast<const uint8_t*>(w_dev);
   g.num_experts = 1;
   g.wbits = 8;
+  g.N = n;
+  g.K = k;
+  g.dense_rows = rows;
+  g.a_rows = rows;
+  g.acc_out = acc;
+  return check_hip(launch_gemm(g, 2, GEMM_GROUP_ACC, 1, stream), "group acc gemm");
+}
+
+int int2_w2a8_group_acc(const int8_t* q, int64_t rows, int64_t k, const void* w_dev, int64_t n, int32_t* acc,
+                        hipStream_t stream) {
+  g_last_error.clear();
+  Q4_REQUIRE(rows >= 0 && k >= 128 && k % 128 == 0 && n >= 64 && n % 64 == 0, Q4_ERR_SHAPE,
+             "need k %% 128 == 0 and n %% 64 == 0");
+  if (rows == 0) return ok();
+  Q4_REQUIRE(q && w_dev && acc, Q4_ERR_NULL, "missing pointer");
+  Q4_REQUIRE(!misaligned(q) && !misaligned(w_dev), Q4_ERR_ALIGN, "pointers must be 16-byte aligned");
+  GemmArgs g{};
+  g.a = q;
+  g.w = static_cast<const uint8_t*>(w_dev);
+  g.num_experts = 1;
+  g.wbits = 2;
   g.N = n;
   g.K = k;
   g.dense_rows = rows;

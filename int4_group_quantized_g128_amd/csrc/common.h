@@ -13,6 +13,7 @@ typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 namespace q4 {
 
@@ -97,6 +98,18 @@ Q4_DEVICE void widen_word_i8(uint32_t w, uint32_t& lo, uint32_t& hi) {
   hi = (w & 0xF0F0F0F0u) ^ 0x80808080u;
 }
 
+// INT8 widening of 2-bit codes: a 32-bit device word of the 2-bit layout holds 16
+// unsigned fields d = q + 2, four per byte; field f of byte m is element 4 (f % 2) + m
+// of K step f / 2 of the word's two steps.  Moving field f to a byte's top two bits and
+// flipping the top bit gives 64 (d - 2) = 64 q, exact in int8, for the four elements of
+// the field in k order: out[f] is the int8x4 register of field f.
+Q4_DEVICE void widen_word_i8_2bit(uint32_t w, uint32_t out[4]) {
+  out[0] = ((w << 6) & 0xC0C0C0C0u) ^ 0x80808080u;
+  out[1] = ((w << 4) & 0xC0C0C0C0u) ^ 0x80808080u;
+  out[2] = ((w << 2) & 0xC0C0C0C0u) ^ 0x80808080u;
+  out[3] = (w & 0xC0C0C0C0u) ^ 0x80808080u;
+}
+
 // ---------------------------------------------------------------- MFMA wrappers
 template <Act A>
 Q4_DEVICE f32x4_t mfma16x16x32(const uint32_t a[4], const uint32_t b[4], f32x4_t c) {
@@ -151,6 +164,16 @@ Q4_DEVICE uint4 load16_stream(const void* p) {
 #else
   const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
   return make_uint4(v[0], v[1], v[2], v[3]);
+#endif
+}
+
+// Non-temporal 8-byte load (the 2-bit weight tiles: 8 bytes per lane).
+Q4_DEVICE uint2 load8_stream(const void* p) {
+#ifdef Q4_NO_NT
+  return load8(p);
+#else
+  const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
+  return make_uint2(v[0], v[1]);
 #endif
 }
 

@@ -138,16 +138,23 @@ Q4_DEVICE void stage16_to_lds(uint4* __restrict__ dst, const uint4* __restrict__
 //  KW  waves of the workgroup that split the K groups (reduced through LDS),
 //  NBW 16-column blocks per wave (the workgroup covers (4 / KW) * NBW blocks),
 //  D   depth of the register pipeline (groups whose loads are in flight),
-//  W8  8-bit weights (2 KB tiles, int8 activations, no widening) instead of 4-bit.
+//  WB  weight bits: 4 (1 KB tiles of nibbles), 8 (2 KB tiles of INT8 codes, int8
+//      activations, no widening) or 2 (512-byte tiles of 2-bit codes, int8
+//      activations: each field widened to 64 q in a byte).
+// Tiles are TS = 16 MB rows; a launch over tiles built taller (the prefill tiles of a
+// layer whose 2-bit experts run on this kernel) walks each in TS-row sub-tiles.
 // The workgroup's scales (and zero points) are staged in LDS once per work item.
-template <Act A, int KIND, bool ASYM, int MB, int KW, int NBW, int D, bool W8, int SGT>
+template <Act A, int KIND, bool ASYM, int MB, int KW, int NBW, int D, int WB, int SGT>
 __global__ void __launch_bounds__(256) k_gemm(GemmArgs args) {
+  constexpr bool W8 = WB == 8, W2 = WB == 2;
+  static_assert(WB == 2 || WB == 4 || WB == 8, "weight bits");
   static_assert(!W8 || (A == Act::I8 && !ASYM), "8-bit weights: symmetric, int8 activations");
+  static_assert(!W2 || (A == Act::I8 && !ASYM && SGT == 1), "2-bit weights: symmetric, int8 activations, g128");
   // SGT scale entries per 1 KB tile (groups of 128 / SGT elements; 0: per item, from the
   // expert's group size): symmetric 4-bit only
   static_assert(SGT == 1 || (!ASYM && !W8 && KIND != GEMM_GROUP_ACC && (SGT == 0 || SGT == 2 || SGT == 4)),
                 "scale groups");
-  constexpr int64_t TB = W8 ? 2 * kTileBytes : kTileBytes;   // bytes per (column block, group) tile
+  constexpr int64_t TB = W8 ? 2 * kTileBytes : W2 ? kTileBytes / 2 : kTileBytes;   // bytes per (column block, group) tile
   constexpr int kColGroups = 4 / KW;
   constexpr int kCBWG = kColGroups * NBW;  // column blocks per workgroup
   extern __shared__ __align__(16) uint8_t smem[];
@@ -169,10 +176,12 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs args) {
   // output slice; every other configuration compiles with ksplit = 1
   constexpr bool kCanSplit = KIND == GEMM_PLAIN && MB == 1 && KW == 4 && NBW == 2;
   const int ksplit = (kCanSplit && args.ksplit > 1) ? args.ksplit : 1;
-  const int64_t base_items = ntiles * nblk;
+  // tiles built taller than TS rows (a prefill tile list): nsub sub-tiles each
+  const int64_t nsub = (args.tiles && args.built_rows > tile_rows) ? (args.built_rows + tile_rows - 1) / tile_rows : 1;
+  const int64_t base_items = ntiles * nsub * nblk;
   const int64_t items = base_items * ksplit;
   const int64_t gslice = (G + ksplit - 1) / ksplit;
-  const int64_t w_scale_off = align256(W8 ? N * K : N * K / 2);
+  const int64_t w_scale_off = align256(W8 ? N * K : W2 ? N * K / 4 : N * K / 2);
   const int64_t w_zero_off = w_scale_off + align256(2 * N * G);   // zero points: one scale entry per tile
   // LDS: scales [kCBWG][G][16] fp16 (one entry per tile; with SG > 1 entries per tile
   // each lane loads its column's entries with the weights instead), zero points
@@ -188,7 +197,8 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs args) {
       ks = it / base_items;
       it -= ks * base_items;
     }
-    const int64_t tile = t_first + it / nblk;
+    const int64_t tile = t_first + it / (nblk * nsub);
+    const int64_t sub = (it / nblk) % nsub;
     const int64_t cb0 = (it % nblk) * kCBWG;     // first column block of the workgroup
     // this item's groups [kg0, kg1), shared out over the KW waves of a column group
     const int64_t kg0 = std::min<int64_t>(G, ks * gslice), kg1 = std::min<int64_t>(G, kg0 + gslice);
@@ -199,12 +209,13 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs args) {
     if (args.tiles) {
       const TileDesc d = args.tiles[tile];
       expert = d.expert;
-      row_start = d.row_start;
-      rows = d.rows;
+      row_start = d.row_start + sub * tile_rows;
+      rows = std::min<int64_t>(tile_rows, int64_t(d.rows) - sub * tile_rows);
     } else {
       row_start = tile * tile_rows;
       rows = std::min<int64_t>(tile_rows, args.dense_rows - row_start);
     }
+    if (rows <= 0) continue;   // an empty sub-tile (the whole workgroup skips it)
     const uint8_t* wbase = expert >= args.num_experts ? args.w_shared
                            : args.woffs                 ? args.w + args.woffs[expert]
                                                         : args.w + int64_t(expert) * args.w_stride;
@@ -227,7 +238,7 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs args) {
     // per-item base pointers; each group then only adds a constant stride
     const uint8_t* wp[NBW];
 #pragma unroll
-    for (int nb = 0; nb < NBW; ++nb) wp[nb] = wbase + ((cb0 + lcb + nb) * G) * TB + lane * 16;
+    for (int nb = 0; nb < NBW; ++nb) wp[nb] = wbase + ((cb0 + lcb + nb) * G) * TB + lane * (W2 ? 8 : 16);
     const uint8_t* ap[MB];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
@@ -241,7 +252,7 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs args) {
       for (int nb = 0; nb < NBW; ++nb) acc[mb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
     struct Stage {
-      uint32_t wv[NBW][W8 ? 8 : 4];
+      uint32_t wv[NBW][W8 ? 8 : W2 ? 2 : 4];
       uint32_t av[MB][4][4];
       uint32_t sv[NBW][SG > 1 ? SG / 2 : 1];   // SG > 1: the column's SG binary16 scales
     };
@@ -262,6 +273,11 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs args) {
       }
 #pragma unroll
       for (int nb = 0; nb < NBW; ++nb) {
+        if constexpr (W2) {
+          const uint2 v = load8_stream(wp[nb] + g * TB);
+          st.wv[nb][0] = v.x; st.wv[nb][1] = v.y;
+          continue;
+        }
         const uint4 v = load16_stream(wp[nb] + g * TB);
         st.wv[nb][0] = v.x; st.wv[nb][1] = v.y; st.wv[nb][2] = v.z; st.wv[nb][3] = v.w;
         if constexpr (W8) {
@@ -386,6 +402,11 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs args) {
             for (int i = 0; i < 2; ++i)
 #pragma unroll
               for (int j = 0; j < 4; ++j) b[i][j] = st.wv[nb][4 * i + j];
+          } else if constexpr (W2) {
+            // word i holds K steps 2i, 2i + 1; field f of its four bytes is elements
+            // 0..3 (f even) or 4..7 (f odd) of step 2i + f / 2, in the operand's k order
+#pragma unroll
+            for (int i = 0; i < 2; ++i) widen_word_i8_2bit(st.wv[nb][i], b[i]);
           } else {
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
@@ -423,8 +444,9 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs args) {
             gacc = mfma_i8_16x16x64(st.av[mb][1], b[1], gacc);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              // 4-bit: exact, gacc = 16 * sum q (d - 8); 8-bit: the group sum itself
-              int32_t a32 = W8 ? gacc[i] : (gacc[i] >> 4);
+              // 4-bit: exact, gacc = 16 * sum q (d - 8); 2-bit: 64 * sum q (d - 2); 8-bit: the
+              // group sum itself
+              int32_t a32 = W8 ? gacc[i] : W2 ? (gacc[i] >> 6) : (gacc[i] >> 4);
               if constexpr (ASYM) a32 -= zoff * __shfl(qs[mb], 4 * kq + i, 64);
               if constexpr (KIND == GEMM_GROUP_ACC) {
                 const int64_t r = mb * 16 + 4 * kq + i;
@@ -547,14 +569,15 @@ static size_t gemm_lds_bytes(int64_t K, int asym, int mb, int kw, int nbw, int s
   return b;
 }
 
-template <Act A, int KIND, int MB, int KW, int NBW, int D, bool W8 = false, int SG = 1>
+template <Act A, int KIND, int MB, int KW, int NBW, int D, int WB = 4, int SG = 1>
 static hipError_t launch_cfg(const GemmArgs& g, hipStream_t st) {
   constexpr int cbwg = (4 / KW) * NBW;
   const int64_t nblk = g.N / (16 * cbwg);
   const int64_t trows = 16 * MB;
   const int64_t max_tiles = g.tiles ? g.max_tiles : (g.dense_rows + trows - 1) / trows;
   constexpr bool can_split = KIND == GEMM_PLAIN && MB == 1 && KW == 4 && NBW == 2;
-  const int64_t items = max_tiles * nblk * ((can_split && g.ksplit > 1) ? g.ksplit : 1);
+  const int64_t nsub = (g.tiles && g.built_rows > trows) ? (g.built_rows + trows - 1) / trows : 1;
+  const int64_t items = max_tiles * nsub * nblk * ((can_split && g.ksplit > 1) ? g.ksplit : 1);
   if (items == 0) return hipSuccess;
 #ifndef Q4_GRID_CAP
 #define Q4_GRID_CAP (256 * 16)
@@ -564,13 +587,14 @@ static hipError_t launch_cfg(const GemmArgs& g, hipStream_t st) {
   if (lds > 160 * 1024) return hipErrorInvalidValue;  // K too large for the staged scales
   if constexpr (SG > 1 || SG == 0) {
     if (g.asym) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((k_gemm<A, KIND, false, MB, KW, NBW, D, false, SG>), dim3(grid), dim3(256), lds, st, g);
-  } else if constexpr (W8) {
-    hipLaunchKernelGGL((k_gemm<A, KIND, false, MB, KW, NBW, D, true, 1>), dim3(grid), dim3(256), lds, st, g);
+    hipLaunchKernelGGL((k_gemm<A, KIND, false, MB, KW, NBW, D, 4, SG>), dim3(grid), dim3(256), lds, st, g);
+  } else if constexpr (WB != 4) {
+    if (g.asym) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((k_gemm<A, KIND, false, MB, KW, NBW, D, WB, 1>), dim3(grid), dim3(256), lds, st, g);
   } else if (g.asym) {
-    hipLaunchKernelGGL((k_gemm<A, KIND, true, MB, KW, NBW, D, false, 1>), dim3(grid), dim3(256), lds, st, g);
+    hipLaunchKernelGGL((k_gemm<A, KIND, true, MB, KW, NBW, D, 4, 1>), dim3(grid), dim3(256), lds, st, g);
   } else {
-    hipLaunchKernelGGL((k_gemm<A, KIND, false, MB, KW, NBW, D, false, 1>), dim3(grid), dim3(256), lds, st, g);
+    hipLaunchKernelGGL((k_gemm<A, KIND, false, MB, KW, NBW, D, 4, 1>), dim3(grid), dim3(256), lds, st, g);
   }
   return hipGetLastError();
 }
@@ -584,49 +608,50 @@ static hipError_t launch_cfg(const GemmArgs& g, hipStream_t st) {
 // int8 (188 -> 184 us).  Layers with other group sizes (SG != 1) keep one wave per column
 // group (two would need 250-280 registers), and three stages are used only where the
 // registers allow it (bf16, one scale entry per tile).
-template <Act A, int KIND, bool W8, int SG>
+template <Act A, int KIND, int WB, int SG>
 struct DecodeCfg {
   static constexpr bool kPlain = KIND == GEMM_PLAIN;
   static constexpr int KW = (SG == 1 && (!kPlain || A == Act::I8)) ? 2 : 1;
   static constexpr int NBW = 4;
-  static constexpr int D = (!kPlain && A == Act::BF16 && SG == 1 && !W8) ? 3 : 2;
+  static constexpr int D = (!kPlain && A == Act::BF16 && SG == 1 && WB == 4) ? 3 : 2;
   static constexpr int CB = (4 / KW) * NBW;   // column blocks per workgroup
 };
 
 // Configuration table: (MB, KW, NBW, D) by row blocks and the column count.
-template <Act A, int KIND, bool W8, int SG>
+template <Act A, int KIND, int WB, int SG>
 static hipError_t launch_kind_sg(const GemmArgs& g, int rb, int split, hipStream_t st) {
   if (rb <= 1) {
-    using C = DecodeCfg<A, KIND, W8, SG>;
-    if (split && g.N % (16 * 2) == 0) return launch_cfg<A, KIND, 1, 4, 2, 2, W8, SG>(g, st);
-    if (g.N % (16 * C::CB) == 0) return launch_cfg<A, KIND, 1, C::KW, C::NBW, C::D, W8, SG>(g, st);
-    return launch_cfg<A, KIND, 1, 4, 2, 2, W8, SG>(g, st);
+    using C = DecodeCfg<A, KIND, WB, SG>;
+    if (split && g.N % (16 * 2) == 0) return launch_cfg<A, KIND, 1, 4, 2, 2, WB, SG>(g, st);
+    if (g.N % (16 * C::CB) == 0) return launch_cfg<A, KIND, 1, C::KW, C::NBW, C::D, WB, SG>(g, st);
+    return launch_cfg<A, KIND, 1, 4, 2, 2, WB, SG>(g, st);
   }
-  if (rb <= 2) return launch_cfg<A, KIND, 2, 4, 4, 2, W8, SG>(g, st);
+  if (rb <= 2) return launch_cfg<A, KIND, 2, 4, 4, 2, WB, SG>(g, st);
   // 64-row tiles: one scale entry per tile only (the forward caps the tiles of layers
   // with other group sizes at 32 rows; four row blocks with per-group accumulators
   // would not fit the registers)
-  if constexpr (SG == 1) return launch_cfg<A, KIND, 4, 4, 4, 2, W8, SG>(g, st);
+  if constexpr (SG == 1) return launch_cfg<A, KIND, 4, 4, 4, 2, WB, SG>(g, st);
   return hipErrorInvalidValue;
 }
 
 // scale entries per tile: 1 (groups of 128 / 256), 2 (64), 4 (32; 4-bit weights only), or
 // -1: per item from the expert's group size (one launch for all 4-bit formats)
-template <Act A, int KIND, bool W8 = false>
+template <Act A, int KIND, int WB = 4>
 static hipError_t launch_kind(const GemmArgs& g, int rb, int split, hipStream_t st) {
-  if constexpr (!W8 && A != Act::F16) {
+  if constexpr (WB == 4 && A != Act::F16) {
     if (g.sg == 2) return launch_kind_sg<A, KIND, false, 2>(g, rb, split, st);
     if (g.sg == 4) return launch_kind_sg<A, KIND, false, 4>(g, rb, split, st);
     if (g.sg == -1) {
       if (g.asym) return hipErrorInvalidValue;
-      return launch_kind_sg<A, KIND, false, 0>(g, rb, split, st);
+      return launch_kind_sg<A, KIND, 4, 0>(g, rb, split, st);
     }
   }
   if (g.sg > 1 || g.sg < 0) return hipErrorInvalidValue;
-  return launch_kind_sg<A, KIND, W8, 1>(g, rb, split, st);
+  return launch_kind_sg<A, KIND, WB, 1>(g, rb, split, st);
 }
 
 hipError_t launch_gemm(const GemmArgs& g, int act, int kind, int row_blocks, hipStream_t st) {
+  if (act != 2 && g.wbits != 0 && g.wbits != 4) return hipErrorInvalidValue;   // 2 / 8-bit weights: int8 only
   // K slices: plain GEMM on 16-row tiles only, in the few-items configuration (the one
   // that implements them); each output slice holds the a_rows rows
   if (g.ksplit > 1) {
@@ -635,7 +660,8 @@ hipError_t launch_gemm(const GemmArgs& g, int act, int kind, int row_blocks, hip
       return hipErrorInvalidValue;
     if (act == 0) return launch_cfg<Act::BF16, GEMM_PLAIN, 1, 4, 2, 2>(g, st);
     if (act == 1) return launch_cfg<Act::F16, GEMM_PLAIN, 1, 4, 2, 2>(g, st);
-    if (g.wbits == 8) return launch_cfg<Act::I8, GEMM_PLAIN, 1, 4, 2, 2, true>(g, st);
+    if (g.wbits == 8) return launch_cfg<Act::I8, GEMM_PLAIN, 1, 4, 2, 2, 8>(g, st);
+    if (g.wbits == 2) return hipErrorInvalidValue;
     return launch_cfg<Act::I8, GEMM_PLAIN, 1, 4, 2, 2>(g, st);
   }
   // few tiles (small batches): split K over the 4 waves for more waves in flight
@@ -647,9 +673,14 @@ hipError_t launch_gemm(const GemmArgs& g, int act, int kind, int row_blocks, hip
   }
   if (act == 1) return launch_kind<Act::F16, GEMM_PLAIN>(g, row_blocks, split, st);
   if (g.wbits == 8) {
-    if (kind == GEMM_GATE_UP) return launch_kind<Act::I8, GEMM_GATE_UP, true>(g, row_blocks, split, st);
-    if (kind == GEMM_GROUP_ACC) return launch_cfg<Act::I8, GEMM_GROUP_ACC, 1, 4, 1, 2, true>(g, st);
-    return launch_kind<Act::I8, GEMM_PLAIN, true>(g, row_blocks, split, st);
+    if (kind == GEMM_GATE_UP) return launch_kind<Act::I8, GEMM_GATE_UP, 8>(g, row_blocks, split, st);
+    if (kind == GEMM_GROUP_ACC) return launch_cfg<Act::I8, GEMM_GROUP_ACC, 1, 4, 1, 2, 8>(g, st);
+    return launch_kind<Act::I8, GEMM_PLAIN, 8>(g, row_blocks, split, st);
+  }
+  if (g.wbits == 2) {
+    if (kind == GEMM_GATE_UP) return launch_kind<Act::I8, GEMM_GATE_UP, 2>(g, row_blocks, split, st);
+    if (kind == GEMM_GROUP_ACC) return launch_cfg<Act::I8, GEMM_GROUP_ACC, 1, 4, 1, 2, 2>(g, st);
+    return launch_kind<Act::I8, GEMM_PLAIN, 2>(g, row_blocks, split, st);
   }
   if (kind == GEMM_GATE_UP) return launch_kind<Act::I8, GEMM_GATE_UP>(g, row_blocks, split, st);
   if (kind == GEMM_GROUP_ACC) return launch_cfg<Act::I8, GEMM_GROUP_ACC, 1, 4, 1, 2>(g, st);

@@ -31,11 +31,22 @@ hipError_t launch_quantize8(const void* w, int dtype, int64_t n, int64_t k, int8
 hipError_t launch_repack8(const int8_t* q, const uint16_t* scales, int64_t n, int64_t k, int gate_up, void* out,
                           hipStream_t st);
 
+// 2-bit g128 weights (cold experts): quantisation and device tiles (512 B per
+// (16-column block, group)).
+hipError_t launch_quantize2(const void* w, int dtype, int64_t n, int64_t k, uint8_t* packed, uint16_t* scales,
+                            int32_t* flags, hipStream_t st);
+hipError_t launch_repack2(const uint8_t* packed, const uint16_t* scales, int64_t n, int64_t k, int gate_up, void* out,
+                          hipStream_t st);
+
 // Router: fp32 logits split over kslices partial sums, then reduction + top-k.
 int route_kslices(int64_t t, int64_t h, int32_t e);
 hipError_t launch_route(const uint16_t* x, const float* wr, const float* bias, int64_t t, int64_t h,
                         int32_t e, int32_t k, float* logits, int32_t* ids, float* w, float* partial,
                         hipStream_t st);
+
+// Weight formats a layer may mix (tile order of the permutation): 4-bit with 1 / 2 / 4
+// scale entries per tile, 8-bit, 2-bit.
+constexpr int kNumFormats = 5;
 
 // Permutation.  Slots s = t * S + j with S = k + shared; expert(s) = ids[t][j] for
 // j < k, num_experts for the shared slot.  Optionally builds the row-tile list.
@@ -64,17 +75,20 @@ struct GemmArgs {
   const uint8_t* w_shared;  // shared expert block (expert index == num_experts) or NULL
   int32_t num_experts;
   int32_t asym;
-  int32_t wbits;          // 4 (INT4 tiles) or 8 (INT8 tiles, int8 activations only)
+  int32_t wbits;          // 4 (INT4 tiles), 8 (INT8 tiles) or 2 (2-bit tiles); 8 and 2: int8 activations only
   const uint8_t* ebits;   // mixed layers: bits per expert (tiles of other experts are skipped), or NULL
   const int64_t* woffs;   // mixed layers: byte offset of each routed expert's block in w, or NULL
   const uint8_t* egroups; // per-expert group size / 32, or NULL
   int32_t sg;             // scale entries per 128-element tile of this launch (1, 2, 4; -1: per item)
-  const int32_t* fmt_tiles;  // layers with several weight formats: tile range of each format [5], or NULL
+  const int32_t* fmt_tiles;  // layers with several weight formats: tile range of each format [kNumFormats + 1], or NULL
   int32_t fmt, fmt_end;   // this launch's formats: tiles fmt_tiles[fmt] .. fmt_tiles[fmt_end]
+                          //   (0..2: 4-bit with 1 / 2 / 4 scale entries per tile, 3: 8-bit, 4: 2-bit)
   int64_t N;              // device columns (2I for gate/up)
   int64_t K;
   // tiles
   const TileDesc* tiles;  // NULL = dense rows [0, dense_rows)
+  int32_t built_rows;     // rows per tile as the permutation built them (0: the kernel's own);
+                          //   taller tiles are walked in sub-tiles (streaming kernel only)
   const int32_t* num_tiles;
   int32_t max_tiles;
   int64_t dense_rows;

@@ -57,9 +57,10 @@ __device__ int32_t block_exclusive_scan(int32_t* data, int n, int32_t* wave_tot)
 }
 
 // Weight format of expert x for the tile order: 0 = 4-bit with one scale entry per tile,
-// 1 = two entries (groups of 64), 2 = four (groups of 32), 3 = 8-bit.
+// 1 = two entries (groups of 64), 2 = four (groups of 32), 3 = 8-bit, 4 = 2-bit.
 __device__ __forceinline__ int tile_format(const uint8_t* ebits, const uint8_t* egroups, int x) {
   if (ebits && ebits[x] == 8) return 3;
+  if (ebits && ebits[x] == 2) return 4;
   if (egroups) {
     const int sg = sg_of_code(egroups[x]);
     return sg == 4 ? 2 : sg == 2 ? 1 : 0;
@@ -184,8 +185,8 @@ __global__ void __launch_bounds__(kPermThreads) k_permute(const int32_t* __restr
     for (int x = tid; x < ee; x += kPermThreads) ntl[x] = (cntl[x] + tile_rows - 1) / tile_rows;
     __syncthreads();
     int32_t base = 0;
-    const int nfmt = (ebits || egroups) ? 4 : 1;   // one format unless the layer mixes them
-    for (int f = 0; f < 4; ++f) {
+    const int nfmt = (ebits || egroups) ? kNumFormats : 1;   // one format unless the layer mixes them
+    for (int f = 0; f < kNumFormats; ++f) {
       if (f >= nfmt) {
         if (fmt_tiles && tid == 0) fmt_tiles[f] = base;
         continue;
@@ -200,7 +201,7 @@ __global__ void __launch_bounds__(kPermThreads) k_permute(const int32_t* __restr
       __syncthreads();
     }
     const int32_t ntiles = base;
-    if (fmt_tiles && tid == 0) fmt_tiles[4] = ntiles;
+    if (fmt_tiles && tid == 0) fmt_tiles[kNumFormats] = ntiles;
     for (int x = tid; x < ee; x += kPermThreads) {
       const int32_t c = cntl[x], o = offl[x];
       int32_t ti = first[x];

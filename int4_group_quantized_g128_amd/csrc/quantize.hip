@@ -350,6 +350,123 @@ __global__ void k_repack8_weights(const int8_t* __restrict__ q, int64_t n, int64
   }
 }
 
+// INT2 g128 (cold experts; page "大模型之Dense、MoE与量化", APEX section: rarely used
+// experts in 2 bits): one wave per (row, group), lane j covers k = 128 g + 2 j and
+// 2 j + 1.  s = binary16 rounded up of fp32(amax), q = clamp(rint(w / s), -2, 1), two's
+// complement, four codes per byte (lane 2 b writes byte b: its two codes low, lane
+// 2 b + 1's high).
+template <int DT>
+__global__ void __launch_bounds__(64) k_quantize2_g128(const void* __restrict__ w, int64_t n, int64_t k,
+                                                      uint8_t* __restrict__ packed, uint16_t* __restrict__ scales,
+                                                      int32_t* __restrict__ flags) {
+  const int64_t G = k / kGroup;
+  const int64_t row = int64_t(blockIdx.x) / G, g = int64_t(blockIdx.x) % G;
+  const int lane = threadIdx.x;
+  const int64_t base = row * k + g * kGroup + 2 * lane;
+  float v0, v1;
+  if constexpr (DT == 0) {
+    const float2 p = *reinterpret_cast<const float2*>(static_cast<const float*>(w) + base);
+    v0 = p.x;
+    v1 = p.y;
+  } else {
+    const uint32_t p = *reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(w) + base);
+    if constexpr (DT == 1) {
+      v0 = f16_bits_to_f32(uint16_t(p & 0xffff));
+      v1 = f16_bits_to_f32(uint16_t(p >> 16));
+    } else {
+      v0 = bf16_to_f32(uint16_t(p & 0xffff));
+      v1 = bf16_to_f32(uint16_t(p >> 16));
+    }
+  }
+  int flag = (!__builtin_isfinite(v0) || !__builtin_isfinite(v1)) ? 1 : 0;
+  const float amax = wave_max(fmaxf(fabsf(v0), fabsf(v1)));
+  const uint16_t sb = f32_to_f16_up(amax);
+  if ((sb & 0x7fff) >= 0x7c00) flag |= 2;
+  const float s = f16_bits_to_f32(sb);
+  float q0 = 0.f, q1 = 0.f;
+  if (s > 0.f) {
+    q0 = fminf(fmaxf(rintf(__fdiv_rn(v0, s)), -2.f), 1.f);
+    q1 = fminf(fmaxf(rintf(__fdiv_rn(v1, s)), -2.f), 1.f);
+  }
+  const uint32_t two = (uint32_t(int(q0)) & 3u) | ((uint32_t(int(q1)) & 3u) << 2);
+  const uint32_t other = uint32_t(__shfl_xor(int(two), 1, 64));
+  if ((lane & 1) == 0) packed[(row * k + g * kGroup) / 4 + lane / 2] = uint8_t(two | (other << 4));
+  if (lane == 0) scales[row * G + g] = sb;
+  if (flags) {
+    const unsigned long long any = __ballot(flag != 0);
+    if (any) {
+      int all = flag;
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) all |= __shfl_xor(all, o, 64);
+      if (lane == 0) atomicOr(flags, all);
+    }
+  }
+}
+
+// 2-bit device tiles: one thread per 32-bit device word, word index
+// ((cb * G + g) * 64 + lane) * 2 + j; word j holds K steps 2 j and 2 j + 1 of device
+// column 16 cb + lane % 16, quarter kq = lane / 16: element e of step s
+// (k = 128 g + 32 s + 8 kq + e) in byte e % 4, field 2 (s % 2) + e / 4, as d = q + 2.
+__global__ void k_repack2_weights(const uint8_t* __restrict__ packed, int64_t n, int64_t k, int gate_up,
+                                  uint32_t* __restrict__ out) {
+  const int64_t G = k / kGroup;
+  const int64_t total = n * k / 16;
+  for (int64_t wi = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; wi < total;
+       wi += int64_t(gridDim.x) * blockDim.x) {
+    const int j = int(wi & 1);
+    const int lane = int((wi >> 1) & 63);
+    const int64_t tile = wi >> 7;
+    const int64_t g = tile % G, cb = tile / G;
+    const int c = lane & 15, kq = lane >> 4;
+    int64_t src = cb * 16 + c;
+    if (gate_up) {
+      const int64_t half = n / 2;
+      src = (cb & 1) ? half + (cb >> 1) * 16 + c : (cb >> 1) * 16 + c;
+    }
+    uint32_t o = 0;
+#pragma unroll
+    for (int sp = 0; sp < 2; ++sp) {
+      const int s = 2 * j + sp;
+      const int64_t k0 = g * kGroup + 32 * s + 8 * kq;   // 8 codes = two canonical bytes
+      const uint32_t in = *reinterpret_cast<const uint16_t*>(packed + (src * k + k0) / 4);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t d = ((in >> (2 * e)) & 3u) ^ 2u;   // two's complement q -> q + 2
+        o |= d << (8 * (e & 3) + 2 * (2 * sp + (e >> 2)));
+      }
+    }
+    out[wi] = o;
+  }
+}
+
+hipError_t launch_quantize2(const void* w, int dtype, int64_t n, int64_t k, uint8_t* packed, uint16_t* scales,
+                            int32_t* flags, hipStream_t st) {
+  const dim3 grid(unsigned(n * (k / kGroup)));
+  if (dtype == 0) hipLaunchKernelGGL(k_quantize2_g128<0>, grid, dim3(64), 0, st, w, n, k, packed, scales, flags);
+  else if (dtype == 1) hipLaunchKernelGGL(k_quantize2_g128<1>, grid, dim3(64), 0, st, w, n, k, packed, scales, flags);
+  else hipLaunchKernelGGL(k_quantize2_g128<2>, grid, dim3(64), 0, st, w, n, k, packed, scales, flags);
+  return hipGetLastError();
+}
+
+hipError_t launch_repack2(const uint8_t* packed, const uint16_t* scales, int64_t n, int64_t k, int gate_up, void* out,
+                          hipStream_t st) {
+  uint8_t* base = static_cast<uint8_t*>(out);
+  const int64_t G = k / kGroup;
+  const int64_t words = n * k / 16;
+  const int64_t sb = align256(n * k / 4);
+  unsigned blocks = unsigned(std::min<int64_t>((words + 255) / 256, 65536));
+  hipLaunchKernelGGL(k_repack2_weights, dim3(blocks), dim3(256), 0, st, packed, n, k, gate_up,
+                     reinterpret_cast<uint32_t*>(base));
+  const int64_t wpad = sb - n * k / 4;
+  if (wpad > 0) hipLaunchKernelGGL(k_zero_bytes, dim3(1), dim3(256), 0, st, base + n * k / 4, wpad);
+  unsigned mblocks = unsigned(std::min<int64_t>((n * G + 255) / 256, 65536));
+  hipLaunchKernelGGL(k_repack_meta, dim3(mblocks), dim3(256), 0, st, scales, nullptr, n, k, int(kGroup), gate_up,
+                     reinterpret_cast<uint16_t*>(base + sb), nullptr);
+  const int64_t scale_pad = align256(2 * n * G) - 2 * n * G;
+  if (scale_pad > 0) hipLaunchKernelGGL(k_zero_bytes, dim3(1), dim3(256), 0, st, base + sb + 2 * n * G, scale_pad);
+  return hipGetLastError();
+}
+
 hipError_t launch_quantize8(const void* w, int dtype, int64_t n, int64_t k, int8_t* q, uint16_t* scales,
                             int32_t* flags, hipStream_t st) {
   const dim3 grid(unsigned(n * (k / kGroup)));

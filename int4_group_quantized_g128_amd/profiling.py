@@ -1,7 +1,9 @@
 """Summaries of rocprofv3 runs of the benchmark (kernel statistics and HBM counters).
 
 Usage, after the three rocprofv3 runs (``--kernel-trace --stats``, ``--pmc FETCH_SIZE``,
-``--pmc WRITE_SIZE``, each with ``-f csv -d DIR``) of the same bench.py command::
+``--pmc WRITE_SIZE``, each with ``-f csv -d DIR``) of the same bench.py command, plus for
+matrix-core kernels a fourth (``--pmc SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE
+SQ_INSTS_VALU_MFMA_MOPS_I8 SQ_INSTS_VALU_MFMA_MOPS_BF16``, passed as ``--mfma DIR``)::
 
     python -m int4_group_quantized_g128_amd.profiling \\
         --stats DIR_STATS --fetch DIR_FETCH --write DIR_WRITE \\
@@ -29,6 +31,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 KERNEL_SOURCES = ("csrc/common.h", "csrc/internal.h", "csrc/gemm.hip", "csrc/gemm_prefill.hip")
 COPY_BYTES = 512 * 1024 * 1024
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
+SIMD_NUM = 256 * 4                     # MI355X: 256 CUs x 4 SIMDs
+MOPS_UNIT = 512                        # one SQ_INSTS_VALU_MFMA_MOPS_* count = 512 operations
+PEAK = {"i8": 5.0e15, "bf16": 2.5e15}  # dense MFMA operations / s
 
 
 def source_hash():
@@ -93,6 +98,9 @@ def main():
     ap.add_argument("--role", action="append", default=[], help="NAME=REGEX")
     ap.add_argument("--workload", required=True)
     ap.add_argument("--commands", default="")
+    ap.add_argument("--mfma", default=None, help="pmc run with the MFMA busy / ops counters")
+    ap.add_argument("--live", action="append", default=[],
+                    help="NAME=MS: the same kernel's average from bench.py's HIP events in the stats run")
     ap.add_argument("--out", required=True)
     a = ap.parse_args()
 
@@ -135,6 +143,42 @@ def main():
         kv[f"write_bytes[{rname}]"] = f"{wb:.0f}"
         kv[f"traffic_bytes[{rname}]"] = f"{rb + wb:.0f}"
         kv[f"avg_us[{rname}]"] = f"{avg:.3f}"
+    live = dict(x.split("=", 1) for x in a.live)
+    if live:
+        lines += ["", "## Kernel averages: rocprofv3 trace vs the bench's HIP events (same run)", "",
+                  "| role | trace average µs | HIP-event average µs | ratio |", "|---|---|---|---|"]
+        for rname, ms in live.items():
+            tr = float(kv.get(f"avg_us[{rname}]", "nan"))
+            ev = float(ms) * 1e3
+            lines.append(f"| {rname} | {tr:.2f} | {ev:.2f} | {tr / ev:.4f} |")
+            kv[f"live_avg_us[{rname}]"] = f"{ev:.3f}"
+    if a.mfma:
+        busy = counter_values(a.mfma, "SQ_VALU_MFMA_BUSY_CYCLES")
+        gui = counter_values(a.mfma, "GRBM_GUI_ACTIVE")
+        mops = {"i8": counter_values(a.mfma, "SQ_INSTS_VALU_MFMA_MOPS_I8"),
+                "bf16": counter_values(a.mfma, "SQ_INSTS_VALU_MFMA_MOPS_BF16")}
+        lines += ["", "## Matrix-core counters per dispatch (--pmc SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE "
+                  "SQ_INSTS_VALU_MFMA_MOPS_I8 SQ_INSTS_VALU_MFMA_MOPS_BF16)", "",
+                  f"MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x {SIMD_NUM} SIMDs) (rocprofv3's "
+                  f"MfmaUtil); operations = MOPS x {MOPS_UNIT}; the rate divides them by the trace average.", "",
+                  "| role | dispatches | MFMA busy % | INT8 ops / dispatch | bf16 ops / dispatch | rate | "
+                  "of the dense peak |", "|---|---|---|---|---|---|---|"]
+        for role in a.role:
+            rname, rx = role.split("=", 1)
+            kn = _match(set(busy) | set(stats), rx)
+            bv, gv = busy.get(kn, []), gui.get(kn, [])
+            if not bv or not gv:
+                continue
+            pct = 100.0 * (sum(bv) / len(bv)) / ((sum(gv) / len(gv)) * SIMD_NUM)
+            ops = {t: (sum(v.get(kn, [0.0])) / max(len(v.get(kn, [])), 1)) * MOPS_UNIT for t, v in mops.items()}
+            kind = "i8" if ops["i8"] >= ops["bf16"] else "bf16"
+            avg_s = stats.get(kn, (0, 0.0))[1] * 1e-9
+            rate = ops[kind] / avg_s if avg_s else 0.0
+            lines.append(f"| {rname} | {len(bv)} | {pct:.1f} | {ops['i8']:.4g} | {ops['bf16']:.4g} | "
+                         f"{rate / 1e12:.1f} T{'OP' if kind == 'i8' else 'FLOP'}/s | {rate / PEAK[kind]:.3f} |")
+            kv[f"mfma_busy_pct[{rname}]"] = f"{pct:.2f}"
+            kv[f"mfma_ops[{rname}]"] = f"{ops[kind]:.0f}"
+            kv[f"mfma_frac_counter[{rname}]"] = f"{rate / PEAK[kind]:.4f}"
     os.makedirs(os.path.dirname(os.path.abspath(a.out)), exist_ok=True)
     with open(a.out + ".md", "w") as f:
         f.write("\n".join(lines) + "\n")

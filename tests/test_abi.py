@@ -329,3 +329,22 @@ def test_plan_validation(L):
     assert L.raw.moe_int4_ffn_plan(ctypes.byref(d), 4, L.Q4_W4A16, None) == L.Q4_ERR_NULL
     assert L.raw.moe_int4_ffn_plan(ctypes.byref(d), -1, L.Q4_W4A16, ctypes.byref(p)) == L.Q4_ERR_SHAPE
     assert L.raw.moe_int4_ffn_plan(ctypes.byref(d), 4, L.Q4_W8A8, ctypes.byref(p)) == L.Q4_ERR_DTYPE
+
+
+def test_two_bit_format_sizes_and_apex_rule(L):
+    import numpy as np
+    from oracle import ffn, layout
+    r = L.raw
+    for n, k in ((64, 512), (32, 256), (96, 7168)):
+        assert r.q2_device_bytes(n, k) == layout.device_bytes2(n, k)
+    assert r.q2_device_bytes(24, 256) == 0 and r.q2_device_bytes(64, 200) == 0
+    fake = ctypes.c_void_p(4096)
+    assert r.quantize_int2_g128(fake, L.Q4_F32, 4, 200, fake, fake, None, None) == L.Q4_ERR_SHAPE
+    assert r.quantize_int2_g128(fake, 9, 4, 256, fake, fake, None, None) == L.Q4_ERR_DTYPE
+    assert r.q2_repack_device(fake, fake, 64, 512, L.Q4_REPACK_PLAIN, fake, 16, None) == L.Q4_ERR_WORKSPACE
+    assert r.q2_repack_device(fake, fake, 48, 512, L.Q4_REPACK_GATE_UP, fake, 1 << 20, None) == L.Q4_ERR_SHAPE
+    rng = np.random.default_rng(8)
+    for E, frac8, cold, shared in ((256, 0.0, 0.25, True), (8, 0.25, 0.5, False), (17, 0.05, 1.0, True)):
+        counts = rng.integers(0, 40, E)
+        assert L.expert_bits_apex(counts.tolist(), frac8, cold, shared) == \
+            [int(b) for b in ffn.bits_apex(counts, frac8, cold, shared)]

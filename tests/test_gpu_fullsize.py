@@ -57,7 +57,8 @@ class OracleExperts:
             out = []
             for m in mats:
                 w = _np(m)
-                q, s = quant.quantize_sym8(w) if bits == 8 else quant.quantize_sym(w, group)
+                q, s = (quant.quantize_sym8(w) if bits == 8 else quant.quantize_sym2(w) if bits == 2
+                        else quant.quantize_sym(w, group))
                 out.append((q.astype(np.int8), s, None))
             self.cache[key] = tuple(out)
         return self.cache[key]
@@ -196,6 +197,31 @@ def test_mixed_widths_by_hotness(lib, mixed, oracle_experts, t):
     GEMM per width over the same tile list."""
     wl, bits = mixed
     _check(lib, wl if t == 64 else wl.retoken(synth, t), "mixed", oracle_experts, 2, 7 + t, bits=bits)
+
+
+@pytest.fixture(scope="module")
+def apex(lib, bench_mod):
+    """APEX widths from the oracle's routing of the calibration batch: experts hit less
+    than a quarter of the even share 2 bits (92 of 256), the others and the shared
+    expert 4."""
+    cfg = synth.CONFIGS[CFG]
+    xc = _np(synth.tokens(CFG, 4096, salt=7))
+    ids_c, _ = _oracle_routing(xc, 4096)
+    counts = np.bincount(ids_c.ravel(), minlength=cfg["experts"])
+    bits = [int(b) for b in ffn.bits_apex(counts, 0.0, 0.25, shared=True)]
+    assert sum(b == 2 for b in bits) == 92 and bits[-1] == 4
+    assert bits == lib.expert_bits_apex(counts.tolist(), 0.0, 0.25, shared=True)
+    wl = bench_mod.Workload(lib, torch, synth, CFG, 64, "mixed", expert_bits=bits)
+    yield wl, bits
+    del wl
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("t", [64, 4096])
+def test_apex_two_bit_cold_experts(lib, apex, oracle_experts, t):
+    """INT8 activations; the 2-bit experts run on the streaming kernel at both sizes."""
+    wl, bits = apex
+    _check(lib, wl if t == 64 else wl.retoken(synth, t), "mixed", oracle_experts, 3, 31 + t, bits=bits)
 
 
 @pytest.fixture(scope="module")
