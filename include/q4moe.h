@@ -354,6 +354,9 @@ Q4_API int moe_int4_ffn_forward(const q4_moe_layer_t* layer, const uint16_t* x_b
  *       moe_int4_ffn_forward); the routed output of a position is the fp32 sum of its
  *       slices in slice order;
  *   q_x [t][H] int8, s_x [t] fp32, q_h [P][I] int8, s_h [P] fp32 (W4A8; NULL in W4A16).
+ * For a one-expert layer at decode sizes (see moe_int4_ffn_plan) the debug call also
+ * runs the permutation, for its views, and keeps y in the workspace with the combine
+ * as a launch of its own (the same arithmetic, so the same results).
  * The gate and up products before SwiGLU are not stored by the fused kernel; the same
  * GEMM core gives them on the forward's own inputs: int4_linear_forward (W4A16, fp32
  * g and u) and int4_w4a8_group_acc (the INT32 group accumulators of either GEMM) on an
@@ -418,6 +421,11 @@ Q4_API int moe_int4_ffn_forward_noalloc(const q4_moe_layer_t* layer, const uint1
  *                 beyond that the decode kernel (64-bit addressing) runs and
  *                 prefill_addr_limited is 1.
  *  down_ksplit    K slices of the down projection (1: none).
+ *  rows_in_token_order 1 for a one-expert, one-choice layer without a shared expert (a
+ *                 dense SwiGLU FFN) at decode sizes: no permutation launch, the GEMMs
+ *                 read and write rows in token order;
+ *  combine_in_down 1 when, in addition, the down projection has no K slices: its
+ *                 epilogue applies the weight and rounds to bf16 (no combine launch).
  *  workspace_bytes moe_int4_ffn_workspace_bytes(layer, t, mode).
  * Errors as moe_int4_ffn_forward's validation (the layer's device pointers are checked
  * for NULL and alignment only).
@@ -429,6 +437,8 @@ typedef struct q4_ffn_plan_t {
   int32_t tile_rows;
   int32_t down_ksplit;
   int32_t prefill_addr_limited;
+  int32_t rows_in_token_order;
+  int32_t combine_in_down;
   int64_t workspace_bytes;
 } q4_ffn_plan_t;
 Q4_API int moe_int4_ffn_plan(const q4_moe_layer_t* layer, int64_t t, int mode, q4_ffn_plan_t* plan);

@@ -135,6 +135,14 @@ bool use_prefill(const q4_moe_layer_t* L, int64_t t, int mode) {
          prefill_fits(t * S, L->inter, act, mat_bytes(L, L->hidden, L->inter));
 }
 
+FwdWorkspace carve(const q4_moe_layer_t* L, int64_t t, int mode, void* base);
+
+// The forward's one-expert decode path (see ffn_forward).
+bool one_expert_decode(const q4_moe_layer_t* L, const FwdWorkspace& w) {
+  return L->num_experts == 1 && L->top_k == 1 && L->shared_inter == 0 && !L->expert_bits && !L->expert_groups &&
+         !w.prefill;
+}
+
 FwdWorkspace carve(const q4_moe_layer_t* L, int64_t t, int mode, void* base) {
   FwdWorkspace w;
   const int shared = L->shared_inter > 0 ? 1 : 0;
@@ -477,6 +485,8 @@ int moe_int4_ffn_plan(const q4_moe_layer_t* L, int64_t t, int mode, q4_ffn_plan_
   plan->tile_rows = w.tile_rows;
   plan->down_ksplit = w.ksplit;
   plan->prefill_addr_limited = (!w.prefill && wants_prefill(L, t, mode)) ? 1 : 0;
+  plan->rows_in_token_order = one_expert_decode(L, w) ? 1 : 0;
+  plan->combine_in_down = (plan->rows_in_token_order && w.ksplit == 1) ? 1 : 0;
   plan->workspace_bytes = w.bytes;
   return ok();
 }
@@ -591,13 +601,22 @@ int ffn_forward(const q4_moe_layer_t* L, const uint16_t* x_bf16, int64_t t, cons
   }
   const int64_t H = L->hidden, I = L->inter;
   const int rb = w.tile_rows / 16;
+  // A one-expert, one-choice layer without a shared expert (a dense SwiGLU FFN) at decode
+  // sizes: the permutation is the identity, so the GEMMs read and write rows in token
+  // order; without K slices the down projection also applies the weight and rounds to
+  // bf16 in its epilogue (the combine's own arithmetic), so only the two GEMMs run.  The
+  // debug call still runs the permutation and the separate combine, for its views.
+  const bool dense = one_expert_decode(L, w);
+  const bool fused_combine = dense && w.ksplit == 1 && !views;
   int rc;
   stage_begin(Q4_STAGE_PERMUTE, stream);
-  if ((rc = check_hip(launch_permute(topk_ids, t, L->top_k, L->num_experts, shared, w.counts, w.offsets, w.perm,
-                                     w.inv, w.tiles, w.num_tiles, w.tile_rows, stream, L->expert_bits,
-                                     L->expert_groups, w.fmt_tiles),
-                      "permute")))
-    return rc;
+  if (!dense || views) {
+    if ((rc = check_hip(launch_permute(topk_ids, t, L->top_k, L->num_experts, shared, w.counts, w.offsets, w.perm,
+                                       w.inv, w.tiles, w.num_tiles, w.tile_rows, stream, L->expert_bits,
+                                       L->expert_groups, w.fmt_tiles),
+                        "permute")))
+      return rc;
+  }
   stage_end(Q4_STAGE_PERMUTE, stream);
   GemmArgs gu{};
   gu.perm = w.perm;
@@ -614,11 +633,13 @@ int ffn_forward(const q4_moe_layer_t* L, const uint16_t* x_bf16, int64_t t, cons
   gu.asym = L->asymmetric;
   gu.N = 2 * I;
   gu.K = H;
-  gu.tiles = w.tiles;
+  gu.tiles = dense ? nullptr : w.tiles;
   gu.num_tiles = w.num_tiles;
   gu.max_tiles = w.max_tiles;
+  gu.dense_rows = t;
   gu.out = w.h;
   gu.a_rows = t;
+  if (dense) gu.perm = nullptr;
   GemmArgs dn = gu;
   dn.a_rows = t * S;
   dn.perm = nullptr;
@@ -631,6 +652,11 @@ int ffn_forward(const q4_moe_layer_t* L, const uint16_t* x_bf16, int64_t t, cons
   dn.out = w.y;
   dn.ksplit = w.ksplit;
   dn.out_slice = t * S * H;
+  dn.dense_rows = t * S;
+  if (fused_combine) {
+    dn.combine_w = topk_w;
+    dn.out_bf16 = out_bf16;
+  }
   auto gemm1 = [&](const GemmArgs& g, int act, int kind) {
     return w.prefill ? launch_gemm_prefill(g, act, kind, stream) : launch_gemm(g, act, kind, rb, stream);
   };
@@ -722,8 +748,10 @@ int ffn_forward(const q4_moe_layer_t* L, const uint16_t* x_bf16, int64_t t, cons
     stage_end(Q4_STAGE_DOWN, stream);
   }
   stage_begin(Q4_STAGE_COMBINE, stream);
-  rc = check_hip(launch_combine(w.y, w.inv, topk_w, t, L->top_k, shared, H, out_bf16, stream, dn.ksplit, dn.out_slice),
-                 "combine");
+  rc = fused_combine ? Q4_OK
+                     : check_hip(launch_combine(w.y, dense ? nullptr : w.inv, topk_w, t, L->top_k, shared, H, out_bf16,
+                                                stream, dn.ksplit, dn.out_slice),
+                                 "combine");
   stage_end(Q4_STAGE_COMBINE, stream);
   return rc;
 }

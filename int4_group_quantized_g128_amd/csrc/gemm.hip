@@ -521,10 +521,18 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs args) {
             float sa = 1.0f;
             if constexpr (A == Act::I8) sa = args.a_scale[args.perm ? args.perm[pos] / args.slots_per_token : pos];
             if constexpr (KIND == GEMM_PLAIN) {
+              if (args.combine_w) {
+                // the combine of a one-expert layer: its arithmetic exactly (fp32 w * y, then bf16)
+                const float wt = args.combine_w[pos];
 #pragma unroll
-              for (int nb = 0; nb < NBW; ++nb)
-                static_cast<float*>(args.out)[ks * args.out_slice + pos * N + (cb0 + lcb + nb) * 16 + col] =
-                    acc[mb][nb][i] * sa;
+                for (int nb = 0; nb < NBW; ++nb)
+                  args.out_bf16[pos * N + (cb0 + lcb + nb) * 16 + col] = f32_to_bf16(fmaf(wt, acc[mb][nb][i] * sa, 0.f));
+              } else {
+#pragma unroll
+                for (int nb = 0; nb < NBW; ++nb)
+                  static_cast<float*>(args.out)[ks * args.out_slice + pos * N + (cb0 + lcb + nb) * 16 + col] =
+                      acc[mb][nb][i] * sa;
+              }
             } else {
               // device blocks alternate gate_j, up_j: pair p -> h columns of block (cb0 + lcb) / 2 + p
               const int64_t I = N / 2;
@@ -689,6 +697,7 @@ hipError_t launch_gemm(const GemmArgs& g, int act, int kind, int row_blocks, hip
 
 // ------------------------------------------------------------------ A9 combine
 // out[t][n] = bf16( sum_{j<k, ascending} w[t][j] * y[inv[t S + j]][n] (+ y[inv[t S + k]][n]) ),
+// inv == NULL: positions in slot order (a one-expert layer's rows are its tokens),
 // with y = the sum of the ksplit slices y + s * slice in slice order when the down
 // projection split K (SPLIT)
 template <bool SPLIT>
@@ -725,7 +734,7 @@ __global__ void __launch_bounds__(256) k_combine(const float* __restrict__ y, co
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const bool ok = j0 + u < k;
-      pos[u] = ok ? inv[tok * S + j0 + u] : 0;
+      pos[u] = ok ? (inv ? inv[tok * S + j0 + u] : tok * S + j0 + u) : 0;
       wj[u] = ok ? w[tok * k + j0 + u] : 0.f;
     }
 #pragma unroll
@@ -741,7 +750,7 @@ __global__ void __launch_bounds__(256) k_combine(const float* __restrict__ y, co
     }
   }
   if (shared) {
-    const float4 v = row(inv[tok * S + k]);
+    const float4 v = row(inv ? inv[tok * S + k] : tok * S + k);
     a0 += v.x;
     a1 += v.y;
     a2 += v.z;

@@ -544,7 +544,12 @@ __global__ void __launch_bounds__(256, (A == Act::I8) ? 2 : 1) k_gemm_pf(GemmArg
           }
           if constexpr (ASYM) qv = *reinterpret_cast<const i32x4_t*>(s_qs + rb * 16 + 4 * kq);
         };
-        auto rescale = [&](int mb, int nb, const i32x4_t& g, const i32x4_t& qv) {
+        auto rescale = [&](int mb, int nb, const i32x4_t& g_in, const i32x4_t& qv) {
+          // the group sums enter the rescale through an empty asm statement: the
+          // conversions cannot then be hoisted up to the MFMAs that produce them (which
+          // made every rescale wait for its own tile's MFMA latency)
+          i32x4_t g = g_in;
+          asm volatile("" : "+v"(g));
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             int32_t a32 = g[i];
@@ -553,39 +558,47 @@ __global__ void __launch_bounds__(256, (A == Act::I8) ? 2 : 1) k_gemm_pf(GemmArg
           }
         };
         if constexpr (NMB > 0) {
+          // Tiles t = 4 mb + nb in order; step t issues tile t's two MFMAs and rescales
+          // tile t - 2, whose sums were ready a whole tile earlier, so the VALU work of a
+          // step never waits for the matrix core (a ring of three pending sums).
+          constexpr int NT = 4 * NMB;
           u32x4_t afc[2], afn[2];
           i32x4_t qvc = {0, 0, 0, 0}, qvn = {0, 0, 0, 0}, qvl = {0, 0, 0, 0};
           read_a(0, afc, qvc);
           widen(0);
-          i32x4_t gt[4], gl;
+          i32x4_t gq[3];
 #pragma unroll
-          for (int mb = 0; mb < NMB; ++mb) {
-#pragma unroll
-            for (int nb = 0; nb < 4; ++nb) {
-              pass(b[nb][0]);
-              pass(b[nb][1]);
-              i32x4_t g = {0, 0, 0, 0};
-              g = mfma_i8_16x16x64(afc[0], b[nb][0], g);
-              g = mfma_i8_16x16x64(afc[1], b[nb][1], g);
-              gt[nb] = g;
-              if (mb == 0 && nb < 3) widen(nb + 1);
-              if (nb == 0 && mb + 1 < NMB) read_a(mb + 1, afn, qvn);
-              if (nb > 0) {
-                rescale(mb, nb - 1, gt[nb - 1], qvc);
-                pin(acc[mb][nb - 1]);
-              } else if (mb > 0) {
-                rescale(mb - 1, 3, gl, qvl);
-                pin(acc[mb - 1][3]);
-              }
-              fence();
+          for (int t = 0; t < NT; ++t) {
+            const int mb = t / 4, nb = t % 4;
+            pass(b[nb][0]);
+            pass(b[nb][1]);
+            i32x4_t g = {0, 0, 0, 0};
+            g = mfma_i8_16x16x64(afc[0], b[nb][0], g);
+            g = mfma_i8_16x16x64(afc[1], b[nb][1], g);
+            gq[t % 3] = g;
+            if (mb == 0 && nb < 3) widen(nb + 1);
+            if (nb == 0 && mb + 1 < NMB) read_a(mb + 1, afn, qvn);
+            if (t >= 2) {
+              const int tp = t - 2, mp = tp / 4, np = tp % 4;
+              rescale(mp, np, gq[tp % 3], mp == mb ? qvc : qvl);
+              pin(acc[mp][np]);
             }
-            gl = gt[3];
-            qvl = qvc;
-            afc[0] = afn[0];
-            afc[1] = afn[1];
-            qvc = qvn;
+            // issue order inside the step: MFMA, VALU, MFMA, the rest
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 32, 0);
+            fence();
+            if (nb == 3) {
+              qvl = qvc;
+              afc[0] = afn[0];
+              afc[1] = afn[1];
+              qvc = qvn;
+            }
           }
-          rescale(NMB - 1, 3, gl, qvl);
+          // the last two tiles (qvl: the last row block's sums after the final swap)
+          if constexpr (NT >= 2) rescale((NT - 2) / 4, (NT - 2) % 4, gq[(NT - 2) % 3], qvl);
+          rescale((NT - 1) / 4, (NT - 1) % 4, gq[(NT - 1) % 3], qvl);
         }
       }
     };

@@ -97,6 +97,10 @@ struct GemmArgs {
   int32_t ksplit;         // plain decode GEMM: K split over this many workgroups (0 / 1: none);
   int64_t out_slice;      //   slice s (groups [s G/ksplit, (s+1) G/ksplit)) writes out + s * out_slice
   int32_t* acc_out;       // debug: int32 [rows][N][G] group accumulators (int8 mode, plain)
+  // plain streaming GEMM of a one-expert, one-choice layer without K slices: the
+  // weighted combine in the epilogue, out_bf16[r][n] = bf16(combine_w[r] * y[r][n])
+  const float* combine_w;
+  uint16_t* out_bf16;
 };
 
 enum GemmKind { GEMM_PLAIN = 0, GEMM_GATE_UP = 1, GEMM_GROUP_ACC = 2 };

@@ -288,6 +288,8 @@ def test_plan_kernel_choice(L):
         assert (p["kernel"], p["tile_rows"], p["down_ksplit"]) == (kernel, rows, ks), (t, mode, p)
         assert p["workspace_bytes"] == L.raw.moe_int4_ffn_workspace_bytes(ctypes.byref(desc), t, mode)
         assert not p["prefill_addr_limited"]
+        one = desc is dense and kernel == "decode"
+        assert p["rows_in_token_order"] == one and p["combine_in_down"] == (one and ks == 1)
     # layers with several weight formats keep the 64-rows-per-expert rule
     mixed = _plan_desc(L, 256, 7168, 2048, 8, shared=True, expert_bits=4096, gate_up_offsets=4096,
                        down_offsets=4096)

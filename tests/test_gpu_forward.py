@@ -146,6 +146,30 @@ def test_dense_ffn_asym_w4a8(lib, dense):
     assert ffn.max_rel_l2(_np(out), ref) <= TOL_W4A8
 
 
+@pytest.mark.parametrize("mode", [0, 1], ids=["w4a16", "w4a8"])
+@pytest.mark.parametrize("t", [1, 4, 16, 17, 40, 63])
+def test_dense_one_expert_path(lib, dense, t, mode):
+    """The one-expert decode path: no permutation launch, rows in token order; from 17
+    tokens (no K slices) the down projection applies the weight and rounds to bf16 in its
+    epilogue.  Weights other than 1 (the combine's multiply is exercised); the result
+    equals the debug call's (which runs the permutation and the separate combine) bit for
+    bit, and the oracle within the mode's bar."""
+    layer, oe = dense
+    plan = lib.moe_int4_ffn_plan(layer, t, mode)
+    assert plan["kernel"] == "decode" and plan["rows_in_token_order"]
+    assert plan["combine_in_down"] == (t > 16)
+    x = synth.tokens("dense", t)
+    ids = np.zeros((t, 1), np.int32)
+    w = np.random.default_rng(t).uniform(0.25, 1.75, (t, 1))
+    out = _forward(lib, layer, x, ids, w, mode)
+    dbg, _ = lib.moe_int4_ffn_debug(layer, x.cuda(), torch.as_tensor(ids).cuda(),
+                                    torch.as_tensor(w, dtype=torch.float32).cuda(), mode=mode)
+    torch.cuda.synchronize()
+    assert torch.equal(out.cpu(), dbg.cpu())
+    ref = (ffn.moe_w4a16 if mode == 0 else ffn.moe_w4a8)(_np(x), oe, ids, w)
+    assert ffn.max_rel_l2(_np(out), ref) <= (TOL_W4A16 if mode == 0 else TOL_W4A8)
+
+
 # ------------------------------------------------------------------ 8 experts, top-2 (slice mode)
 @pytest.fixture(scope="module")
 def moe8(lib):
