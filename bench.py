@@ -29,7 +29,9 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 # still hash the same
 TRAFFIC_PROFILES = {
     ("moe256", 64, "w4a16"): os.path.join(ROOT, "profiles", "k_gemm_gate_up_moe256_T64_w4a16.txt"),
+    ("moe256", 1, "w4a16"): os.path.join(ROOT, "profiles", "k_gemm_decode_moe256_T1_w4a16.txt"),
     ("moe256", 4096, "w4a16"): os.path.join(ROOT, "profiles", "k_gemm_pf_moe256_T4096_w4a16.txt"),
+    ("moe256", 4096, "w4a8"): os.path.join(ROOT, "profiles", "k_gemm_pf_moe256_T4096_w4a8.txt"),
     ("moe8_w4a8", 2048, "w4a8"): os.path.join(ROOT, "profiles", "k_gemm_pf_moe8_T2048_w4a8.txt"),
 }
 WARM_SECONDS = 0.3             # minimum untimed graph replay time before a timed region
@@ -560,6 +562,9 @@ def main():
                 scale = 1e9 if roof["unit"] == "GB/s" else 1e12
                 roof["profile_avg_ms"] = round(p_ms, 5)
                 roof["profile_frac"] = round(work / (p_ms * 1e-3) / scale / roof["peak"], 4)
+            if "mfma_busy_pct[gate_up]" in kv:   # matrix-core busy cycles (rocprofv3 MfmaUtil)
+                roof["mfma_busy_pct_counter"] = float(kv["mfma_busy_pct[gate_up]"])
+                roof["mfma_frac_counter"] = float(kv["mfma_frac_counter[gate_up]"])
 
     extra = {}
     if not args.no_extra and args.config == "moe256":

@@ -32,6 +32,7 @@ KERNEL_SOURCES = ("csrc/common.h", "csrc/internal.h", "csrc/gemm.hip", "csrc/gem
 COPY_BYTES = 512 * 1024 * 1024
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 SIMD_NUM = 256 * 4                     # MI355X: 256 CUs x 4 SIMDs
+XCD_NUM = 8                            # GRBM_GUI_ACTIVE comes summed over the 8 XCDs
 MOPS_UNIT = 512                        # one SQ_INSTS_VALU_MFMA_MOPS_* count = 512 operations
 PEAK = {"i8": 5.0e15, "bf16": 2.5e15}  # dense MFMA operations / s
 
@@ -159,8 +160,9 @@ def main():
                 "bf16": counter_values(a.mfma, "SQ_INSTS_VALU_MFMA_MOPS_BF16")}
         lines += ["", "## Matrix-core counters per dispatch (--pmc SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE "
                   "SQ_INSTS_VALU_MFMA_MOPS_I8 SQ_INSTS_VALU_MFMA_MOPS_BF16)", "",
-                  f"MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x {SIMD_NUM} SIMDs) (rocprofv3's "
-                  f"MfmaUtil); operations = MOPS x {MOPS_UNIT}; the rate divides them by the trace average.", "",
+                  f"MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE per XCD x {SIMD_NUM} SIMDs), "
+                  f"rocprofv3's MfmaUtil (its per-XCD maximum taken as the reported sum over the {XCD_NUM} XCDs / "
+                  f"{XCD_NUM}); operations = MOPS x {MOPS_UNIT}; the rate divides them by the trace average.", "",
                   "| role | dispatches | MFMA busy % | INT8 ops / dispatch | bf16 ops / dispatch | rate | "
                   "of the dense peak |", "|---|---|---|---|---|---|---|"]
         for role in a.role:
@@ -169,7 +171,7 @@ def main():
             bv, gv = busy.get(kn, []), gui.get(kn, [])
             if not bv or not gv:
                 continue
-            pct = 100.0 * (sum(bv) / len(bv)) / ((sum(gv) / len(gv)) * SIMD_NUM)
+            pct = 100.0 * (sum(bv) / len(bv)) / ((sum(gv) / len(gv)) / XCD_NUM * SIMD_NUM)
             ops = {t: (sum(v.get(kn, [0.0])) / max(len(v.get(kn, [])), 1)) * MOPS_UNIT for t, v in mops.items()}
             kind = "i8" if ops["i8"] >= ops["bf16"] else "bf16"
             avg_s = stats.get(kn, (0, 0.0))[1] * 1e-9
