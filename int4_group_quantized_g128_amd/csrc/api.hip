@@ -847,10 +847,26 @@ struct LoraWorkspace {
   float* rs_x = nullptr;      // [t][H/128]
   float* rs_h = nullptr;      // [t][I/128]
   bool prefill = false;
+  // grouped by expert (large batches): the permutation of the slots, its 64-slot tiles,
+  // h per slot [t k][I] fp32
+  bool grouped = false;
+  int32_t* counts = nullptr;
+  int32_t* offsets = nullptr;
+  int32_t* perm = nullptr;
+  int32_t* inv = nullptr;
+  TileDesc* gtiles = nullptr;
+  int32_t* gnum_tiles = nullptr;
+  int32_t gmax_tiles = 0;
+  float* h_slot = nullptr;
+  int ncb = 0;                // column blocks of d (the kernel's own block width)
   int64_t bytes = 0;
 };
 
 constexpr int64_t kLoraPrefillRows = 256;
+// From this many tokens (ranks 16 and 32) the adapter work runs grouped by expert, each
+// expert's adapter rows loaded once per tile of slots instead of once per slot (T = 2048:
+// the token-major kernel re-read 768 KB of adapter rows per slot).
+constexpr int64_t kLoraGroupedRows = 256;
 
 LoraWorkspace carve_lora(const q4_lora_layer_t* L, int64_t t, void* base) {
   LoraWorkspace w;
@@ -866,9 +882,22 @@ LoraWorkspace carve_lora(const q4_lora_layer_t* L, int64_t t, void* base) {
     off += a256(bytes);
     return base ? static_cast<uint8_t*>(base) + at : nullptr;
   };
+  w.grouped = t >= kLoraGroupedRows && lora_grouped_rank(int(r));
+  w.ncb = w.grouped ? lora_grp_col_blocks(I) : lora_col_blocks(I);
   w.base_gu = reinterpret_cast<float*>(take(t * 2 * I * 4));
   w.a = reinterpret_cast<float*>(take(P * lora_kchunks(H) * 2 * r * 4));
-  w.d = reinterpret_cast<float*>(take(P * lora_col_blocks(I) * r * 4));
+  w.d = reinterpret_cast<float*>(take(P * w.ncb * r * 4));
+  if (w.grouped) {
+    const int64_t E = L->num_experts;
+    w.counts = reinterpret_cast<int32_t*>(take((E + 1) * 4));
+    w.offsets = reinterpret_cast<int32_t*>(take((E + 2) * 4));
+    w.perm = reinterpret_cast<int32_t*>(take(P * 4));
+    w.inv = reinterpret_cast<int32_t*>(take(P * 4));
+    w.gmax_tiles = int32_t(P / 64 + std::min<int64_t>(E, P) + 1);
+    w.gtiles = reinterpret_cast<TileDesc*>(take(int64_t(w.gmax_tiles) * int64_t(sizeof(TileDesc))));
+    w.gnum_tiles = reinterpret_cast<int32_t*>(take(4));
+    w.h_slot = reinterpret_cast<float*>(take(P * I * 4));
+  }
   w.hw = reinterpret_cast<uint16_t*>(take(t * I * 2));
   w.y = reinterpret_cast<float*>(take(t * H * 4));
   if (w.prefill) {
@@ -961,14 +990,25 @@ int moe_lora_ffn_forward(const q4_lora_layer_t* L, const uint16_t* x_bf16, int64
     return rc;
   if ((rc = check_hip(launch_lora_in(x_bf16, t, H, topk_ids, kk, E, L->a_gate_up, r, w.a, stream), "lora in")))
     return rc;
-  if ((rc = check_hip(launch_lora_mid(w.base_gu, t, H, I, topk_ids, topk_w, kk, E, r, w.a, L->b_gate, L->b_up,
-                                      L->a_down, w.d, w.hw, stream),
-                      "lora mid")))
+  if (w.grouped) {
+    if ((rc = check_hip(launch_permute(topk_ids, t, kk, E, 0, w.counts, w.offsets, w.perm, w.inv, w.gtiles,
+                                       w.gnum_tiles, 64, stream),
+                        "lora permute")))
+      return rc;
+    if ((rc = check_hip(launch_lora_mid_grp(w.base_gu, I, w.perm, w.gtiles, w.gnum_tiles, w.gmax_tiles, kk, H, r,
+                                            w.a, L->b_gate, L->b_up, L->a_down, w.d, w.h_slot, stream),
+                        "lora mid (grouped)")))
+      return rc;
+    if ((rc = check_hip(launch_lora_hsum(w.h_slot, topk_w, t, kk, I, w.hw, stream), "lora hw")))
+      return rc;
+  } else if ((rc = check_hip(launch_lora_mid(w.base_gu, t, H, I, topk_ids, topk_w, kk, E, r, w.a, L->b_gate, L->b_up,
+                                             L->a_down, w.d, w.hw, stream),
+                             "lora mid")))
     return rc;
   if ((rc = dense_gemm(w.hw, t, I, L->base_down, H, L->asymmetric, w.y, w.prefill, w.tiles, w.num_tiles, w.rs_h,
                        stream)))
     return rc;
-  return check_hip(launch_lora_out(w.y, t, H, I, topk_ids, topk_w, kk, E, r, w.d, L->b_down, out_bf16, stream),
+  return check_hip(launch_lora_out(w.y, t, H, I, topk_ids, topk_w, kk, E, r, w.d, L->b_down, out_bf16, stream, w.ncb),
                    "lora out");
 }
 

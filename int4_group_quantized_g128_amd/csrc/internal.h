@@ -128,7 +128,17 @@ hipError_t launch_lora_mid(const float* base_gu, int64_t t, int64_t h, int64_t i
                            const uint16_t* b_up, const uint16_t* a_down, float* d_part, uint16_t* hw, hipStream_t st);
 hipError_t launch_lora_out(const float* y, int64_t t, int64_t hidden, int64_t inter, const int32_t* ids,
                            const float* w, int32_t kk, int32_t e, int r, const float* d_part, const uint16_t* b_down,
-                           uint16_t* out, hipStream_t st);
+                           uint16_t* out, hipStream_t st, int ncb = 0);
+// Large batches, slots grouped by expert (tiles of the permutation, at most 64 slots
+// each): h per slot and the down-adapter projections per 256-column block, then hw.
+bool lora_grouped_rank(int r);
+int lora_grp_col_blocks(int64_t inter);
+hipError_t launch_lora_mid_grp(const float* base_gu, int64_t inter, const int32_t* perm, const TileDesc* tiles,
+                               const int32_t* num_tiles, int32_t max_tiles, int32_t kk, int64_t h, int r,
+                               const float* a_part, const uint16_t* b_gate, const uint16_t* b_up,
+                               const uint16_t* a_down, float* d_part, float* h_slot, hipStream_t st);
+hipError_t launch_lora_hsum(const float* h_slot, const float* w, int64_t t, int32_t kk, int64_t inter, uint16_t* hw,
+                            hipStream_t st);
 int lora_kchunks(int64_t h);       // K chunks (512 wide) of the adapter input projections
 int lora_col_blocks(int64_t inter);  // column blocks of the SwiGLU / down-projection kernel
 

@@ -214,6 +214,134 @@ __global__ void __launch_bounds__(256) k_lora_mid(const float* __restrict__ base
     if (cv[i]) hw[t * inter + col[i]] = f32_to_bf16(hacc[i]);
 }
 
+// Large batches, grouped by expert: the routed slots sorted by expert (the permutation's
+// row tiles of at most 64 slots), a workgroup per (tile, 256 columns).  Each thread owns
+// one column: it loads that column's B_gate / B_up rows once for the whole tile (the
+// token-major kernel above reloads them for every slot), and for every slot of the tile
+// forms g, u and h with the same arithmetic as that kernel, writing h per slot.  The
+// down-adapter input projection d[slot][q] = sum_c A_down,e[q][c] h[slot][c] over the
+// workgroup's columns is a 16 x R x 256 fp32 matrix-core product per 16 slots (each
+// wave a quarter of the columns, the four partials added in wave order).  hw (the
+// weighted sum over a token's choices) is formed afterwards by k_lora_hsum.
+constexpr int kGrpCols = 256;    // columns per workgroup
+constexpr int kGrpSlots = 64;    // slots per tile (the permutation's tile rows)
+template <int R>
+__global__ void __launch_bounds__(256) k_lora_mid_grp(const float* __restrict__ base_gu, int64_t inter,
+                                                      const int32_t* __restrict__ perm,
+                                                      const TileDesc* __restrict__ tiles,
+                                                      const int32_t* __restrict__ num_tiles, int32_t kk, int nks,
+                                                      const float* __restrict__ a_part,
+                                                      const uint16_t* __restrict__ b_gate,
+                                                      const uint16_t* __restrict__ b_up,
+                                                      const uint16_t* __restrict__ a_down, float* __restrict__ d_part,
+                                                      float* __restrict__ h_slot) {
+  static_assert(R % 16 == 0 && R <= 32, "rank: 16 or 32");
+  __shared__ float s_a[kGrpSlots][2 * R];
+  __shared__ float s_h[16][kGrpCols + 1];
+  __shared__ float s_ad[R][kGrpCols + 1];
+  __shared__ f32x4_t s_dred[4][R / 16][64];
+  if (int(blockIdx.y) >= *num_tiles) return;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int m = lane & 15, kq = lane >> 4;
+  const int64_t cb = blockIdx.x, ncb = gridDim.x;
+  const TileDesc td = tiles[blockIdx.y];
+  const int e = td.expert, rows = td.rows;
+  const int64_t p0 = td.row_start;
+  const int64_t c = cb * kGrpCols + tid;
+  const bool cv = c < inter;
+  const int64_t cc = cv ? c : inter - 1;   // columns past I load the last one, masked
+  // this column's adapter rows, loaded once for the tile
+  float bg[R], bu[R];
+#pragma unroll
+  for (int q8 = 0; q8 < R / 8; ++q8) {
+    const uint4 vg = load16(b_gate + (int64_t(e) * inter + cc) * R + 8 * q8);
+    const uint4 vu = load16(b_up + (int64_t(e) * inter + cc) * R + 8 * q8);
+    const uint32_t wg[4] = {vg.x, vg.y, vg.z, vg.w}, wu[4] = {vu.x, vu.y, vu.z, vu.w};
+#pragma unroll
+    for (int z = 0; z < 4; ++z) {
+      bg[8 * q8 + 2 * z] = bf16_to_f32(uint16_t(wg[z] & 0xffff));
+      bg[8 * q8 + 2 * z + 1] = bf16_to_f32(uint16_t(wg[z] >> 16));
+      bu[8 * q8 + 2 * z] = bf16_to_f32(uint16_t(wu[z] & 0xffff));
+      bu[8 * q8 + 2 * z + 1] = bf16_to_f32(uint16_t(wu[z] >> 16));
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < R; ++q)
+    s_ad[q][tid] = cv ? bf16_to_f32(a_down[(int64_t(e) * R + q) * inter + cc]) : 0.f;
+  // the slots' input projections: the sum of their K-chunk partials, in chunk order
+  for (int idx = tid; idx < rows * 2 * R; idx += 256) {
+    const int i = idx / (2 * R), q = idx - i * 2 * R;
+    const int64_t sl = perm[p0 + i];
+    float sum = 0.f;
+    for (int ks = 0; ks < nks; ++ks) sum += a_part[(sl * nks + ks) * 2 * R + q];
+    s_a[i][q] = sum;
+  }
+  __syncthreads();
+  for (int i0 = 0; i0 < rows; i0 += 16) {
+    for (int ii = 0; ii < 16; ++ii) {
+      const int i = i0 + ii;
+      float hv = 0.f;
+      if (i < rows) {
+        const int64_t sl = perm[p0 + i], t = sl / kk;
+        float g = base_gu[t * 2 * inter + cc], u = base_gu[t * 2 * inter + inter + cc];
+#pragma unroll
+        for (int q = 0; q < R; ++q) g = fmaf(bg[q], s_a[i][q], g);
+#pragma unroll
+        for (int q = 0; q < R; ++q) u = fmaf(bu[q], s_a[i][R + q], u);
+        hv = swiglu(g, u);
+        if (cv) h_slot[sl * inter + c] = hv;
+      }
+      s_h[ii][tid] = cv ? hv : 0.f;
+    }
+    __syncthreads();
+    // D[slot ii][q] over this wave's 64 columns: lane (m, kq) feeds s_h[m][k] and
+    // s_ad[16 nb + m][k] for k = 64 wid + 4 st + kq to MFMA st
+#pragma unroll
+    for (int nb = 0; nb < R / 16; ++nb) {
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int st = 0; st < 16; ++st) {
+        const int k = 64 * wid + 4 * st + kq;
+        acc = mfma_f32_16x16x4(s_h[m][k], s_ad[16 * nb + m][k], acc);
+      }
+      s_dred[wid][nb][lane] = acc;
+    }
+    __syncthreads();
+    // C layout: lane (m, kq) element r holds slot 4 kq + r, q = 16 nb + m
+    for (int o = tid; o < 16 * R; o += 256) {
+      const int ii = o / R, q = o - ii * R;
+      if (i0 + ii >= rows) continue;
+      const int nb = q / 16, l = 16 * (ii / 4) + (q % 16), r = ii % 4;
+      const float v = ((s_dred[0][nb][l][r] + s_dred[1][nb][l][r]) + s_dred[2][nb][l][r]) + s_dred[3][nb][l][r];
+      d_part[(int64_t(perm[p0 + i0 + ii]) * ncb + cb) * R + q] = v;
+    }
+    __syncthreads();
+  }
+}
+
+// hw[t][c] = bf16( sum_j w[t][j] h[t kk + j][c] ), choices in order from 0 (the
+// token-major kernel's own accumulation); four columns per thread.
+__global__ void __launch_bounds__(256) k_lora_hsum(const float* __restrict__ h_slot, const float* __restrict__ w,
+                                                   int64_t t, int32_t kk, int64_t inter, uint16_t* __restrict__ hw) {
+  const int64_t per = inter / 4;
+  const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= t * per) return;
+  const int64_t tok = i / per, c = (i - tok * per) * 4;
+  float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+  for (int j = 0; j < kk; ++j) {
+    const int64_t sl = tok * kk + j;
+    const float wj = w[sl];
+    const float4 v = *reinterpret_cast<const float4*>(h_slot + sl * inter + c);
+    a0 = fmaf(wj, v.x, a0);
+    a1 = fmaf(wj, v.y, a1);
+    a2 = fmaf(wj, v.z, a2);
+    a3 = fmaf(wj, v.w, a3);
+  }
+  const uint32_t lo = uint32_t(f32_to_bf16(a0)) | (uint32_t(f32_to_bf16(a1)) << 16);
+  const uint32_t hi = uint32_t(f32_to_bf16(a2)) | (uint32_t(f32_to_bf16(a3)) << 16);
+  *reinterpret_cast<uint2*>(hw + tok * inter + c) = make_uint2(lo, hi);
+}
+
 // out[t][c] = bf16( y[t][c] + sum_j w_j sum_q B_down,e_j[c][q] d[t kk + j][q] ), d the
 // sum over column blocks of d_part (in order).
 template <int R>
@@ -310,14 +438,44 @@ hipError_t launch_lora_mid(const float* base_gu, int64_t t, int64_t h, int64_t i
 
 hipError_t launch_lora_out(const float* y, int64_t t, int64_t hidden, int64_t inter, const int32_t* ids,
                            const float* w, int32_t kk, int32_t e, int r, const float* d_part, const uint16_t* b_down,
-                           uint16_t* out, hipStream_t st) {
+                           uint16_t* out, hipStream_t st, int ncb) {
   if (t == 0) return hipSuccess;
   const dim3 g = dim3(unsigned((hidden + 255) / 256), unsigned(t));
+  if (ncb <= 0) ncb = lora_col_blocks(inter);
   return with_rank(r, [&](auto rc) {
     hipLaunchKernelGGL((k_lora_out<decltype(rc)::value>), g, dim3(256), size_t(kk) * r * sizeof(float), st, y, hidden,
-                       ids, w, kk, e, lora_col_blocks(inter), d_part, b_down, out);
+                       ids, w, kk, e, ncb, d_part, b_down, out);
     return hipGetLastError();
   });
+}
+
+bool lora_grouped_rank(int r) { return r == 16 || r == 32; }
+int lora_grp_col_blocks(int64_t inter) { return int((inter + kGrpCols - 1) / kGrpCols); }
+
+hipError_t launch_lora_mid_grp(const float* base_gu, int64_t inter, const int32_t* perm, const TileDesc* tiles,
+                               const int32_t* num_tiles, int32_t max_tiles, int32_t kk, int64_t h, int r,
+                               const float* a_part, const uint16_t* b_gate, const uint16_t* b_up,
+                               const uint16_t* a_down, float* d_part, float* h_slot, hipStream_t st) {
+  if (max_tiles <= 0) return hipSuccess;
+  const dim3 g = dim3(unsigned(lora_grp_col_blocks(inter)), unsigned(max_tiles));
+  const int nks = lora_kchunks(h);
+  if (r == 16)
+    hipLaunchKernelGGL((k_lora_mid_grp<16>), g, dim3(256), 0, st, base_gu, inter, perm, tiles, num_tiles, kk, nks,
+                       a_part, b_gate, b_up, a_down, d_part, h_slot);
+  else if (r == 32)
+    hipLaunchKernelGGL((k_lora_mid_grp<32>), g, dim3(256), 0, st, base_gu, inter, perm, tiles, num_tiles, kk, nks,
+                       a_part, b_gate, b_up, a_down, d_part, h_slot);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_lora_hsum(const float* h_slot, const float* w, int64_t t, int32_t kk, int64_t inter, uint16_t* hw,
+                            hipStream_t st) {
+  const int64_t n = t * (inter / 4);
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_lora_hsum, dim3(unsigned((n + 255) / 256)), dim3(256), 0, st, h_slot, w, t, kk, inter, hw);
+  return hipGetLastError();
 }
 
 }  // namespace q4

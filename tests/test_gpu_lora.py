@@ -113,6 +113,24 @@ def test_lora_ranks(lib, r):
         assert ffn.max_rel_l2(_np(out), ref) <= TOL, (r, t)
 
 
+@pytest.mark.parametrize("r", [16, 32])
+@pytest.mark.parametrize("t", [256, 300])
+def test_lora_grouped_by_expert(lib, r, t):
+    """From 256 tokens, ranks 16 and 32 run the adapter work grouped by expert (tiles of
+    at most 64 routed slots of one expert); I = 384 leaves a ragged second block of 256
+    columns and T = 300 ragged tiles."""
+    E, H, I, k = 4, 256, 384, 2
+    base = (synth.normal(synth.stream_key(66, 1), (I, H), 0.05), synth.normal(synth.stream_key(66, 2), (I, H), 0.05),
+            synth.normal(synth.stream_key(66, 3), (H, I), 0.05))
+    adapters = lambda e: synth.lora_adapters("lora8", e, rank=r, dims=(H, I))
+    layer, ob, oa = _build(lib, base, adapters, E, H, I, k, r, r == 32)
+    x = synth.normal(synth.stream_key(67, t, r), (t, H), 1.0).to(torch.bfloat16)
+    ids, w = _route(t, E, k, t + 3 * r)
+    out = _run(lib, layer, x, ids, w)
+    ref = lora.moe_lora(_np(x), ob, oa, ids, w)
+    assert ffn.max_rel_l2(_np(out), ref) <= TOL, (r, t)
+
+
 @pytest.fixture(scope="module")
 def lora8(lib):
     cfg = synth.CONFIGS["lora8"]
