@@ -932,8 +932,11 @@ int validate_lora(const q4_lora_layer_t* L) {
 
 // y[rows][n] = a[rows][k] W^T for a PLAIN device-layout INT4 matrix (bf16 activations):
 // the decode kernel for few rows, the prefill kernel (dense row tiles) for many.
+// (prefill: tiles_ready, the row tiles of the rows are already built; rs_ready, rs
+// already holds the row sums of a per group of 128.)
 int dense_gemm(const uint16_t* a, int64_t rows, int64_t k, const void* w_dev, int64_t n, int asym, float* y,
-               bool prefill, TileDesc* tiles, int32_t* num_tiles, float* rs, hipStream_t stream) {
+               bool prefill, TileDesc* tiles, int32_t* num_tiles, float* rs, hipStream_t stream,
+               bool tiles_ready = false, bool rs_ready = false) {
   GemmArgs g{};
   g.a = a;
   g.a_rows = rows;
@@ -946,8 +949,9 @@ int dense_gemm(const uint16_t* a, int64_t rows, int64_t k, const void* w_dev, in
   g.out = y;
   if (prefill) {
     int rc;
-    if ((rc = check_hip(launch_dense_tiles(rows, 128, tiles, num_tiles, stream), "dense tiles"))) return rc;
-    if ((rc = check_hip(launch_rowsum(a, 0, rows, k, rs, stream), "row sums"))) return rc;
+    if (!tiles_ready && (rc = check_hip(launch_dense_tiles(rows, 128, tiles, num_tiles, stream), "dense tiles")))
+      return rc;
+    if (!rs_ready && (rc = check_hip(launch_rowsum(a, 0, rows, k, rs, stream), "row sums"))) return rc;
     g.tiles = tiles;
     g.num_tiles = num_tiles;
     g.max_tiles = int32_t(rows / 128 + 1);
@@ -999,14 +1003,17 @@ int moe_lora_ffn_forward(const q4_lora_layer_t* L, const uint16_t* x_bf16, int64
                                             w.a, L->b_gate, L->b_up, L->a_down, w.d, w.h_slot, stream),
                         "lora mid (grouped)")))
       return rc;
-    if ((rc = check_hip(launch_lora_hsum(w.h_slot, topk_w, t, kk, I, w.hw, stream), "lora hw")))
+    if ((rc = check_hip(launch_lora_hsum(w.h_slot, topk_w, t, kk, I, w.hw, w.prefill ? w.rs_h : nullptr, stream),
+                        "lora hw")))
       return rc;
   } else if ((rc = check_hip(launch_lora_mid(w.base_gu, t, H, I, topk_ids, topk_w, kk, E, r, w.a, L->b_gate, L->b_up,
                                              L->a_down, w.d, w.hw, stream),
                              "lora mid")))
     return rc;
+  // the row tiles of the t rows are the gate/up GEMM's; grouped, k_lora_hsum also formed
+  // the row sums of hw
   if ((rc = dense_gemm(w.hw, t, I, L->base_down, H, L->asymmetric, w.y, w.prefill, w.tiles, w.num_tiles, w.rs_h,
-                       stream)))
+                       stream, true, w.grouped)))
     return rc;
   return check_hip(launch_lora_out(w.y, t, H, I, topk_ids, topk_w, kk, E, r, w.d, L->b_down, out_bf16, stream, w.ncb),
                    "lora out");

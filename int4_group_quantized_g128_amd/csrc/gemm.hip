@@ -8,21 +8,23 @@
 // (SwiGLU FFN experts); page "大模型之Dense、MoE与量化", MoE section (outputs combined
 // in proportion to the router scores, a shared expert used by every token).
 //
-// GEMM structure (gfx950):
-//  - a workgroup of 4 waves computes 16*MB rows x 64 device columns (4 column blocks of
-//    16); the 4 waves split the K groups into contiguous ranges and are reduced through
-//    LDS at the end;
+// GEMM structure (gfx950; the template parameters of k_gemm below):
+//  - a workgroup of 4 waves computes 16*MB rows x (4 / KW) * NBW column blocks of 16;
+//    KW waves split the K groups into contiguous ranges (reduced through LDS at the
+//    end) and each wave covers NBW column blocks;
 //  - each lane streams its 16-byte share of each 1 KB weight tile (one column block x
-//    one group), widens the nibbles in registers and feeds the matrix core;
+//    one group), widens the nibbles in registers and feeds the matrix core; the loads
+//    of the next D - 1 groups are in flight while a group is computed (a register
+//    pipeline of depth D);
 //  - W4A16 (bf16): the widened value is magic + d (exact in bf16); per group
 //    gacc = sum x * (magic + d) over 4 MFMA 16x16x32 and the row sums xs = sum x over
 //    4 MFMA with B = 1.0, then acc += s * (gacc - (magic + z) * xs) in fp32;
 //  - fp16 activations: magic + d - (magic + z) = d - z is formed exactly with a packed
 //    fp16 add, so gacc = sum x * (d - z) directly and acc += s * gacc;
-//  - the loads of group g + 1 are issued before group g is computed (two stages);
 //  - W4A8: 16 * (d - 8) as int8, two MFMA i32 16x16x64 per group, the INT32 group
 //    accumulator is gacc / 16 (- (z - 8) * sum q_x for asymmetric weights), then
-//    acc += s_w * acc_g in fp32 and the row scale s_x at the end.
+//    acc += s_w * acc_g in fp32 and the row scale s_x at the end; 8-bit weights go to
+//    the matrix core as stored and 2-bit ones are widened to 64 q per byte.
 #include "common.h"
 #include "internal.h"
 

@@ -138,7 +138,7 @@ hipError_t launch_lora_mid_grp(const float* base_gu, int64_t inter, const int32_
                                const float* a_part, const uint16_t* b_gate, const uint16_t* b_up,
                                const uint16_t* a_down, float* d_part, float* h_slot, hipStream_t st);
 hipError_t launch_lora_hsum(const float* h_slot, const float* w, int64_t t, int32_t kk, int64_t inter, uint16_t* hw,
-                            hipStream_t st);
+                            float* rs, hipStream_t st);
 int lora_kchunks(int64_t h);       // K chunks (512 wide) of the adapter input projections
 int lora_col_blocks(int64_t inter);  // column blocks of the SwiGLU / down-projection kernel
 

@@ -240,6 +240,7 @@ __global__ void __launch_bounds__(256) k_lora_mid_grp(const float* __restrict__ 
   __shared__ float s_h[16][kGrpCols + 1];
   __shared__ float s_ad[R][kGrpCols + 1];
   __shared__ f32x4_t s_dred[4][R / 16][64];
+  __shared__ int32_t s_slot[kGrpSlots];
   if (int(blockIdx.y) >= *num_tiles) return;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int m = lane & 15, kq = lane >> 4;
@@ -268,6 +269,7 @@ __global__ void __launch_bounds__(256) k_lora_mid_grp(const float* __restrict__ 
 #pragma unroll
   for (int q = 0; q < R; ++q)
     s_ad[q][tid] = cv ? bf16_to_f32(a_down[(int64_t(e) * R + q) * inter + cc]) : 0.f;
+  if (tid < rows) s_slot[tid] = perm[p0 + tid];
   // the slots' input projections: the sum of their K-chunk partials, in chunk order
   for (int idx = tid; idx < rows * 2 * R; idx += 256) {
     const int i = idx / (2 * R), q = idx - i * 2 * R;
@@ -277,13 +279,28 @@ __global__ void __launch_bounds__(256) k_lora_mid_grp(const float* __restrict__ 
     s_a[i][q] = sum;
   }
   __syncthreads();
+  // the base gate/up values of 16 slots, all loads in flight together; the next 16
+  // slots' loads are issued before the current ones are computed
+  float g0[16], u0[16], g1[16], u1[16];
+  auto load_base = [&](int i0, float (&g)[16], float (&u)[16]) {
+#pragma unroll
+    for (int ii = 0; ii < 16; ++ii) {
+      const int i = min(i0 + ii, rows - 1);
+      const int64_t t = s_slot[i] / kk;
+      g[ii] = base_gu[t * 2 * inter + cc];
+      u[ii] = base_gu[t * 2 * inter + inter + cc];
+    }
+  };
+  load_base(0, g0, u0);
   for (int i0 = 0; i0 < rows; i0 += 16) {
+    if (i0 + 16 < rows) load_base(i0 + 16, g1, u1);
+#pragma unroll
     for (int ii = 0; ii < 16; ++ii) {
       const int i = i0 + ii;
       float hv = 0.f;
       if (i < rows) {
-        const int64_t sl = perm[p0 + i], t = sl / kk;
-        float g = base_gu[t * 2 * inter + cc], u = base_gu[t * 2 * inter + inter + cc];
+        const int64_t sl = s_slot[i];
+        float g = g0[ii], u = u0[ii];
 #pragma unroll
         for (int q = 0; q < R; ++q) g = fmaf(bg[q], s_a[i][q], g);
 #pragma unroll
@@ -313,17 +330,25 @@ __global__ void __launch_bounds__(256) k_lora_mid_grp(const float* __restrict__ 
       if (i0 + ii >= rows) continue;
       const int nb = q / 16, l = 16 * (ii / 4) + (q % 16), r = ii % 4;
       const float v = ((s_dred[0][nb][l][r] + s_dred[1][nb][l][r]) + s_dred[2][nb][l][r]) + s_dred[3][nb][l][r];
-      d_part[(int64_t(perm[p0 + i0 + ii]) * ncb + cb) * R + q] = v;
+      d_part[(int64_t(s_slot[i0 + ii]) * ncb + cb) * R + q] = v;
     }
     __syncthreads();
+#pragma unroll
+    for (int ii = 0; ii < 16; ++ii) {
+      g0[ii] = g1[ii];
+      u0[ii] = u1[ii];
+    }
   }
 }
 
 // hw[t][c] = bf16( sum_j w[t][j] h[t kk + j][c] ), choices in order from 0 (the
-// token-major kernel's own accumulation); four columns per thread.
+// token-major kernel's own accumulation); four columns per thread.  rs (optional): the
+// row sums of hw per group of 128 columns (the down projection's prefill kernel takes
+// them), summed over the group's 32 threads in a fixed tree.
 __global__ void __launch_bounds__(256) k_lora_hsum(const float* __restrict__ h_slot, const float* __restrict__ w,
-                                                   int64_t t, int32_t kk, int64_t inter, uint16_t* __restrict__ hw) {
-  const int64_t per = inter / 4;
+                                                   int64_t t, int32_t kk, int64_t inter, uint16_t* __restrict__ hw,
+                                                   float* __restrict__ rs) {
+  const int64_t per = inter / 4;   // a multiple of 32: a group's 32 threads share a wave half
   const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
   if (i >= t * per) return;
   const int64_t tok = i / per, c = (i - tok * per) * 4;
@@ -337,9 +362,16 @@ __global__ void __launch_bounds__(256) k_lora_hsum(const float* __restrict__ h_s
     a2 = fmaf(wj, v.z, a2);
     a3 = fmaf(wj, v.w, a3);
   }
-  const uint32_t lo = uint32_t(f32_to_bf16(a0)) | (uint32_t(f32_to_bf16(a1)) << 16);
-  const uint32_t hi = uint32_t(f32_to_bf16(a2)) | (uint32_t(f32_to_bf16(a3)) << 16);
+  const uint16_t b0 = f32_to_bf16(a0), b1 = f32_to_bf16(a1), b2 = f32_to_bf16(a2), b3 = f32_to_bf16(a3);
+  const uint32_t lo = uint32_t(b0) | (uint32_t(b1) << 16);
+  const uint32_t hi = uint32_t(b2) | (uint32_t(b3) << 16);
   *reinterpret_cast<uint2*>(hw + tok * inter + c) = make_uint2(lo, hi);
+  if (rs) {
+    float s = ((bf16_to_f32(b0) + bf16_to_f32(b1)) + bf16_to_f32(b2)) + bf16_to_f32(b3);
+#pragma unroll
+    for (int o = 16; o >= 1; o >>= 1) s += __shfl_xor(s, o, 32);
+    if ((threadIdx.x & 31) == 0) rs[tok * (inter / 128) + c / 128] = s;
+  }
 }
 
 // out[t][c] = bf16( y[t][c] + sum_j w_j sum_q B_down,e_j[c][q] d[t kk + j][q] ), d the
@@ -350,27 +382,30 @@ __global__ void __launch_bounds__(256) k_lora_out(const float* __restrict__ y, i
                                                   int32_t kk, int32_t e_count, int ncb,
                                                   const float* __restrict__ d_part, const uint16_t* __restrict__ b_down,
                                                   uint16_t* __restrict__ out) {
-  extern __shared__ float s_d[];   // [kk][R]
+  extern __shared__ float s_d[];   // [kk][R], then the experts [kk] and weights [kk]
+  int32_t* s_e = reinterpret_cast<int32_t*>(s_d + kk * R);
+  float* s_w = s_d + kk * R + kk;
   const int tid = threadIdx.x;
   const int64_t t = blockIdx.y;
+  const int64_t c = int64_t(blockIdx.x) * 256 + tid;
+  const bool cv = c < hidden;
+  const float y0 = cv ? y[t * hidden + c] : 0.f;   // in flight while d is summed
   for (int i = tid; i < kk * R; i += 256) {
     const int j = i / R, q = i - j * R;
-    const int64_t p = t * kk + j;
+    const float* dp = d_part + (t * kk + j) * ncb * R + q;
     float s = 0.f;
-    for (int cb = 0; cb < ncb; ++cb) s += d_part[(p * ncb + cb) * R + q];
+#pragma unroll 8
+    for (int cb = 0; cb < ncb; ++cb) s += dp[cb * R];
     s_d[i] = s;
   }
+  if (tid < kk) {
+    s_e[tid] = min(max(ids[t * kk + tid], 0), e_count - 1);
+    s_w[tid] = w[t * kk + tid];
+  }
   __syncthreads();
-  const int64_t c = int64_t(blockIdx.x) * 256 + tid;
-  if (c >= hidden) return;
-  float acc = y[t * hidden + c];
-  for (int j = 0; j < kk; ++j) {
-    const int64_t p = t * kk + j;
-    const int e = min(max(ids[p], 0), e_count - 1);
-    const uint16_t* bd = b_down + (int64_t(e) * hidden + c) * R;
-    uint4 v[R / 8];
-#pragma unroll
-    for (int q8 = 0; q8 < R / 8; ++q8) v[q8] = load16(bd + 8 * q8);
+  if (!cv) return;
+  // sum_q B_down,e[c][q] d[j][q] for choice j, the row's loads issued together
+  auto proj = [&](const uint4 (&v)[R / 8], int j) {
     float s = 0.f;
 #pragma unroll
     for (int q8 = 0; q8 < R / 8; ++q8) {
@@ -381,7 +416,26 @@ __global__ void __launch_bounds__(256) k_lora_out(const float* __restrict__ y, i
         s = fmaf(bf16_to_f32(uint16_t(wv[z] >> 16)), s_d[j * R + 8 * q8 + 2 * z + 1], s);
       }
     }
-    acc = fmaf(w[p], s, acc);
+    return s;
+  };
+  auto load_row = [&](uint4 (&v)[R / 8], int j) {
+    const uint16_t* bd = b_down + (int64_t(s_e[j]) * hidden + c) * R;
+#pragma unroll
+    for (int q8 = 0; q8 < R / 8; ++q8) v[q8] = load16(bd + 8 * q8);
+  };
+  float acc = y0;
+  int j = 0;
+  for (; j + 1 < kk; j += 2) {   // two choices' rows in flight at once
+    uint4 va[R / 8], vb[R / 8];
+    load_row(va, j);
+    load_row(vb, j + 1);
+    acc = fmaf(s_w[j], proj(va, j), acc);
+    acc = fmaf(s_w[j + 1], proj(vb, j + 1), acc);
+  }
+  if (j < kk) {
+    uint4 va[R / 8];
+    load_row(va, j);
+    acc = fmaf(s_w[j], proj(va, j), acc);
   }
   out[t * hidden + c] = f32_to_bf16(acc);
 }
@@ -443,8 +497,8 @@ hipError_t launch_lora_out(const float* y, int64_t t, int64_t hidden, int64_t in
   const dim3 g = dim3(unsigned((hidden + 255) / 256), unsigned(t));
   if (ncb <= 0) ncb = lora_col_blocks(inter);
   return with_rank(r, [&](auto rc) {
-    hipLaunchKernelGGL((k_lora_out<decltype(rc)::value>), g, dim3(256), size_t(kk) * r * sizeof(float), st, y, hidden,
-                       ids, w, kk, e, ncb, d_part, b_down, out);
+    hipLaunchKernelGGL((k_lora_out<decltype(rc)::value>), g, dim3(256), size_t(kk) * (r + 2) * sizeof(float), st, y,
+                       hidden, ids, w, kk, e, ncb, d_part, b_down, out);
     return hipGetLastError();
   });
 }
@@ -471,10 +525,11 @@ hipError_t launch_lora_mid_grp(const float* base_gu, int64_t inter, const int32_
 }
 
 hipError_t launch_lora_hsum(const float* h_slot, const float* w, int64_t t, int32_t kk, int64_t inter, uint16_t* hw,
-                            hipStream_t st) {
+                            float* rs, hipStream_t st) {
   const int64_t n = t * (inter / 4);
   if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_lora_hsum, dim3(unsigned((n + 255) / 256)), dim3(256), 0, st, h_slot, w, t, kk, inter, hw);
+  if (inter % 128 != 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_lora_hsum, dim3(unsigned((n + 255) / 256)), dim3(256), 0, st, h_slot, w, t, kk, inter, hw, rs);
   return hipGetLastError();
 }
 
