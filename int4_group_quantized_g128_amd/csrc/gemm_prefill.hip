@@ -819,7 +819,7 @@ __global__ void __launch_bounds__(512) k_gemm_pf16w(GemmArgs args) {
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb)
           negz[nb] = -(magic_offset<Act::BF16>() + (ASYM ? float(s_z[(wn * 4 + nb) * 16 + col]) : 8.0f));
-        const uint8_t* wl = base + W_OFF + wn * 4 * kTileBytes + lane * 16;   // word s of block nb at + nb KB + 4 s
+        const uint8_t* wl = base + W_OFF + wn * 4 * kTileBytes + lane * 16;   // word w of block nb at + nb KB + 4 w
         f32x4_t g[NMB][4];
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
@@ -833,17 +833,23 @@ __global__ void __launch_bounds__(512) k_gemm_pf16w(GemmArgs args) {
               for (int nb = 0; nb < 4; ++nb) g[mb][nb] = xv * negz[nb];
             }
           }
+          // One scale entry per tile: lane quarter kq takes K step ws = (s + kq) % 4 at
+          // step s (each quarter still covers the four steps once, and its A and B
+          // fragments come from the same step), so the 64 lanes' 4-byte weight reads,
+          // 16 bytes apart, fall in 64 distinct LDS banks; with several scale entries the
+          // steps of a scale group must stay together, so every quarter takes step s.
+          const int ws = SG == 1 ? ((s + kq) & 3) : s;
           // the step's activation fragments, then the weight blocks one at a time: block
           // nb + 1 is widened (VALU) while block nb's MFMAs run
           u32x4_t a[NMB];
 #pragma unroll
           for (int mb = 0; mb < NMB; ++mb) {
             const int r = (2 * mb + wm) * 16 + col;
-            const int c = (4 * s + kq) ^ swz(r);
+            const int c = (4 * ws + kq) ^ swz(r);
             a[mb] = *reinterpret_cast<const u32x4_t*>(base + r * ROWB + c * 16);
           }
           auto widen_block = [&](int nb) -> u32x4_t {
-            const uint32_t wd = *reinterpret_cast<const uint32_t*>(wl + nb * kTileBytes + 4 * s);
+            const uint32_t wd = *reinterpret_cast<const uint32_t*>(wl + nb * kTileBytes + 4 * ws);
             uint32_t o[4];
             widen_word_fp<Act::BF16>(wd, o);
             return u32x4_t{o[0], o[1], o[2], o[3]};
