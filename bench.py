@@ -56,6 +56,9 @@ def parse():
     p.add_argument("--cpu-tokens", type=int, default=2, help="tokens in the oracle's timed sample")
     p.add_argument("--no-extra", action="store_true", help="skip the secondary workloads")
     p.add_argument("--no-graph", action="store_true", help="time eager launches instead of graph replays")
+    p.add_argument("--no-cold", action="store_true",
+                   help="skip the cache-flushed timing of the main line (profiler runs: the kernel "
+                        "trace averages then hold warm steps only, as the live averages do)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a plain 512 MiB device copy (HBM counter calibration)")
     return p.parse_args()
@@ -527,7 +530,7 @@ def main():
     wl = Workload(lib, torch, synth, args.config, args.tokens, args.mode)
     log(f"[bench] layer weights {wl.layer.weight_bytes() / 1e9:.3f} GB; timing {args.steps} steps")
     sec, stage_ms = time_steps(torch, wl, args.steps, args.warmup, stage_events=True, graph=not args.no_graph)
-    cold = time_cold(torch, wl, min(args.steps, 50)) if not args.no_graph else None
+    cold = time_cold(torch, wl, min(args.steps, 50)) if not (args.no_graph or args.no_cold) else None
     main_res = summarize(wl, sec, stage_ms, cold)
     log(f"[bench] main: {json.dumps(main_res)}")
 
