@@ -3,7 +3,8 @@
 Usage, after the three rocprofv3 runs (``--kernel-trace --stats``, ``--pmc FETCH_SIZE``,
 ``--pmc WRITE_SIZE``, each with ``-f csv -d DIR``) of the same bench.py command, plus for
 matrix-core kernels a fourth (``--pmc SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE
-SQ_INSTS_VALU_MFMA_MOPS_I8 SQ_INSTS_VALU_MFMA_MOPS_BF16``, passed as ``--mfma DIR``)::
+SQ_INSTS_VALU_MFMA_MOPS_I8 SQ_INSTS_VALU_MFMA_MOPS_BF16``, passed as ``--mfma DIR``) and a
+fifth with the instruction-issue counters (``ISSUE_COUNTERS``, passed as ``--issue DIR``)::
 
     python -m int4_group_quantized_g128_amd.profiling \\
         --stats DIR_STATS --fetch DIR_FETCH --write DIR_WRITE \\
@@ -35,6 +36,9 @@ SIMD_NUM = 256 * 4                     # MI355X: 256 CUs x 4 SIMDs
 XCD_NUM = 8                            # GRBM_GUI_ACTIVE comes summed over the 8 XCDs
 MOPS_UNIT = 512                        # one SQ_INSTS_VALU_MFMA_MOPS_* count = 512 operations
 PEAK = {"i8": 5.0e15, "bf16": 2.5e15}  # dense MFMA operations / s
+# one --pmc run (7 SQ counters and one GRBM counter: within one pass's limits)
+ISSUE_COUNTERS = ("SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_LDS", "SQ_LDS_BANK_CONFLICT", "SQ_WAVE_CYCLES",
+                  "SQ_WAIT_ANY", "SQ_BUSY_CYCLES", "GRBM_GUI_ACTIVE")
 
 
 def source_hash():
@@ -100,6 +104,7 @@ def main():
     ap.add_argument("--workload", required=True)
     ap.add_argument("--commands", default="")
     ap.add_argument("--mfma", default=None, help="pmc run with the MFMA busy / ops counters")
+    ap.add_argument("--issue", default=None, help="pmc run with the instruction-issue counters (ISSUE_COUNTERS)")
     ap.add_argument("--live", action="append", default=[],
                     help="NAME=MS: the same kernel's average from bench.py's HIP events in the stats run")
     ap.add_argument("--out", required=True)
@@ -181,6 +186,31 @@ def main():
             kv[f"mfma_busy_pct[{rname}]"] = f"{pct:.2f}"
             kv[f"mfma_ops[{rname}]"] = f"{ops[kind]:.0f}"
             kv[f"mfma_frac_counter[{rname}]"] = f"{rate / PEAK[kind]:.4f}"
+    if a.issue:
+        cv = {c: counter_values(a.issue, c) for c in ISSUE_COUNTERS}
+        lines += ["", f"## Instruction issue per dispatch (--pmc {' '.join(ISSUE_COUNTERS)})", "",
+                  "VALU issue = SQ_INSTS_VALU x 4 cycles (a wave64 VALU instruction occupies its 16-lane SIMD "
+                  f"4 cycles) / (GRBM_GUI_ACTIVE per XCD x {SIMD_NUM} SIMDs); waiting = SQ_WAIT_ANY / "
+                  "SQ_WAVE_CYCLES (wave cycles spent waiting on anything: barriers, memory and LDS counters, "
+                  "dependencies); LDS conflicts = SQ_LDS_BANK_CONFLICT cycles per SQ_INSTS_LDS instruction.", "",
+                  "| role | dispatches | VALU instructions per MFMA | VALU issue % | waiting % of wave cycles | "
+                  "LDS conflict cycles per LDS instruction |", "|---|---|---|---|---|---|"]
+        for role in a.role:
+            rname, rx = role.split("=", 1)
+            kn = _match(set(cv["SQ_INSTS_VALU"]) | set(stats), rx)
+            m = {c: (sum(v[kn]) / len(v[kn]) if v.get(kn) else 0.0) for c, v in cv.items()}
+            if not m["GRBM_GUI_ACTIVE"] or not m["SQ_INSTS_MFMA"] or not m["SQ_WAVE_CYCLES"]:
+                continue
+            valu_pct = 100.0 * m["SQ_INSTS_VALU"] * 4 / (m["GRBM_GUI_ACTIVE"] / XCD_NUM * SIMD_NUM)
+            wait_pct = 100.0 * m["SQ_WAIT_ANY"] / m["SQ_WAVE_CYCLES"]
+            per_mfma = m["SQ_INSTS_VALU"] / m["SQ_INSTS_MFMA"]
+            conf = m["SQ_LDS_BANK_CONFLICT"] / m["SQ_INSTS_LDS"] if m["SQ_INSTS_LDS"] else 0.0
+            lines.append(f"| {rname} | {len(cv['SQ_INSTS_VALU'].get(kn, []))} | {per_mfma:.2f} | {valu_pct:.1f} | "
+                         f"{wait_pct:.1f} | {conf:.2f} |")
+            kv[f"valu_per_mfma[{rname}]"] = f"{per_mfma:.3f}"
+            kv[f"valu_issue_pct[{rname}]"] = f"{valu_pct:.2f}"
+            kv[f"wait_pct[{rname}]"] = f"{wait_pct:.2f}"
+            kv[f"lds_conflict_per_inst[{rname}]"] = f"{conf:.3f}"
     os.makedirs(os.path.dirname(os.path.abspath(a.out)), exist_ok=True)
     with open(a.out + ".md", "w") as f:
         f.write("\n".join(lines) + "\n")
