@@ -691,9 +691,12 @@ __global__ void __launch_bounds__(256, (A == Act::I8) ? 2 : 1) k_gemm_pf(GemmArg
   }
 }
 
-// bf16 prefill with wide tiles: 128 rows x 256 columns (16 column blocks) per workgroup
-// of 8 waves (2 x 4 waves of 64 x 64), a three-slot LDS ring of 49 KB stages (A 32 KB,
-// W 16 KB, scales, zero points, row sums).  Each wave walks the four 32-element K steps
+// bf16 prefill with wide tiles: 64 RG rows x 256 columns (16 column blocks) per
+// workgroup of 4 RG waves (RG x 4 waves of 64 x 64).  RG = 2: 8 waves, a three-slot LDS
+// ring of 49 KB stages (A 32 KB, W 16 KB, scales, zero points, row sums), one workgroup
+// per CU; RG = 1: 4 waves on 64-row halves of the 128-row tiles, a two-slot ring of
+// 33 KB stages, two workgroups per CU (the waves of one run while the other's wait at
+// its per-group barrier).  Each wave walks the four 32-element K steps
 // of a group outermost: only one K step's widened weights (16 registers) and the
 // per-tile group accumulators are live, which keeps the kernel within 256 registers so
 // two waves share each SIMD, and every activation byte copied to LDS feeds 256 columns.
@@ -701,26 +704,30 @@ __global__ void __launch_bounds__(256, (A == Act::I8) ? 2 : 1) k_gemm_pf(GemmArg
 // rescaled after its own K steps, so the register count does not depend on SG.
 constexpr int kPfwCB = 16;
 
-template <int KIND, bool ASYM, int SG>
-__global__ void __launch_bounds__(512) k_gemm_pf16w(GemmArgs args) {
+template <int KIND, bool ASYM, int SG, int RG>
+__global__ void __launch_bounds__(256 * RG, RG == 1 ? 2 : 1) k_gemm_pf16w(GemmArgs args) {
+  static_assert(RG == 1 || RG == 2, "row groups");
   static_assert(SG == 1 || (!ASYM && (SG == 2 || SG == 4)), "scale groups: symmetric weights only");
   constexpr int SPS = 4 / SG;                           // 32-element K steps per scale group
   constexpr int ROWB = kGroup * 2;                      // bf16 bytes of one row of a group
-  constexpr int W_OFF = kPfRows * ROWB;                 // 32 KB of activations
+  constexpr int ROWS = 64 * RG;                         // rows per work item
+  constexpr int NSUB = kPfRows / ROWS;                  // work items per 128-row tile
+  constexpr int W_OFF = ROWS * ROWB;                    // 32 (16) KB of activations
   constexpr int S_OFF = W_OFF + kPfwCB * kTileBytes;    // 16 KB of weight tiles
   constexpr int Z_OFF = S_OFF + kPfwCB * 32 * SG;       // scales [16][16][SG] fp16
   constexpr int R_OFF = Z_OFF + (SG == 1 ? kPfwCB * 16 : 0);   // zero points [16][16] u8
-  constexpr int BYTES = R_OFF + kPfRows * 4 * SG;       // row sums [SG][128] fp32
-  constexpr int NS = 3;
+  constexpr int BYTES = R_OFF + ROWS * 4 * SG;          // row sums [SG][ROWS] fp32
+  constexpr int NS = RG == 1 ? 2 : 3;
   constexpr int A_INSTS = 4;                            // 16 rows per wave, 4 rows per copy
-  constexpr int WCOPIES = 2;                            // two 1 KB tiles per wave
+  constexpr int WCOPIES = 4 / RG;                       // 1 KB weight tiles per wave
   constexpr int PER = A_INSTS + WCOPIES;
   __shared__ __align__(16) uint8_t ring[NS * BYTES];
   auto swz = [](int r) -> int { return r & 15; };      // 256-byte rows: chunk c at c ^ (r % 16)
 
   const int lane = threadIdx.x & 63;
   const int wid = __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6));
-  const int wm = wid & 1, wn = wid >> 1;                // row blocks 2 mb + wm, column blocks 4 wn ..
+  // row blocks RG mb + wm, column blocks 4 wn ..
+  const int wm = RG == 1 ? 0 : (wid & 1), wn = RG == 1 ? wid : (wid >> 1);
   const int col = lane & 15, kq = lane >> 4;
   const int64_t N = args.N, K = args.K;
   const int G = int(K / kGroup);
@@ -730,7 +737,7 @@ __global__ void __launch_bounds__(512) k_gemm_pf16w(GemmArgs args) {
     t_first = args.fmt_tiles[args.fmt];
     ntiles = args.fmt_tiles[args.fmt_end] - t_first;
   }
-  const int64_t items = ntiles * nblk;
+  const int64_t items = ntiles * NSUB * nblk;
   const int64_t w_scale_off = align256(N * K / 2);
   const int64_t w_zero_off = w_scale_off + align256(2 * N * int64_t(G));
   const auto a_rsrc = buffer_rsrc(args.a, args.a_rows * K * 2);
@@ -738,11 +745,13 @@ __global__ void __launch_bounds__(512) k_gemm_pf16w(GemmArgs args) {
 
   const ItemRange ir = item_range(items);
   for (int64_t item = ir.first; item < ir.last; item += ir.step) {
-    const int64_t tile = t_first + item / nblk;
+    const int64_t tile = t_first + item / (NSUB * nblk);
+    const int sub = int((item / nblk) % NSUB);
     const int64_t cb0 = (item % nblk) * kPfwCB;
     const TileDesc d = args.tiles[tile];
-    const int64_t row_start = d.row_start;
-    const int rows = d.rows;
+    const int64_t row_start = d.row_start + int64_t(sub) * ROWS;
+    const int rows = std::min(ROWS, int(d.rows) - sub * ROWS);
+    if (rows <= 0) continue;   // an empty second half (the whole workgroup skips it)
     const bool shared = d.expert >= args.num_experts;
     typedef __attribute__((address_space(1))) const int64_t* gptr_i64;
     int64_t woff = shared ? 0 : args.woffs ? ((gptr_i64)args.woffs)[d.expert] : int64_t(d.expert) * args.w_stride;
@@ -756,7 +765,7 @@ __global__ void __launch_bounds__(512) k_gemm_pf16w(GemmArgs args) {
       return args.perm ? args.perm[pos] / args.slots_per_token : pos;
     };
     // copies: activation rows 16 wid + 4 j + lane / 16 (chunk slot lane % 16), weight
-    // tiles of column blocks 2 wid and 2 wid + 1
+    // tiles of column blocks WCOPIES wid + j
     uint32_t a_off[A_INSTS];
 #pragma unroll
     for (int j = 0; j < A_INSTS; ++j) {
@@ -766,7 +775,7 @@ __global__ void __launch_bounds__(512) k_gemm_pf16w(GemmArgs args) {
     }
     uint32_t w_off[WCOPIES];
 #pragma unroll
-    for (int j = 0; j < WCOPIES; ++j) w_off[j] = uint32_t((cb0 + 2 * wid + j) * G * kTileBytes + lane * 16);
+    for (int j = 0; j < WCOPIES; ++j) w_off[j] = uint32_t((cb0 + WCOPIES * wid + j) * G * kTileBytes + lane * 16);
     // scales, 32 SG bytes per block and group: wave 0 (16 B per lane; with four entries
     // per tile waves 0 and 3 copy 1 KB each); zero points: wave 0 lanes 32..47
     const int sidx = lane + (wid == 3 ? 64 : 0);
@@ -779,9 +788,9 @@ __global__ void __launch_bounds__(512) k_gemm_pf16w(GemmArgs args) {
       m_off = uint32_t(w_zero_off + (cb0 + lane - 32) * G * 16);
       m_step = 16;
     }
-    // waves 1 and 2: the row sums (one per scale group) of tile rows (wid - 1) * 64 + lane
+    // waves 1 .. RG: the row sums (one per scale group) of tile rows (wid - 1) * 64 + lane
     uint32_t r_off = 0;
-    if (wid == 1 || wid == 2) r_off = uint32_t(src_of((wid - 1) * 64 + lane) * G * SG * 4);
+    if (wid >= 1 && wid <= RG) r_off = uint32_t(src_of((wid - 1) * 64 + lane) * G * SG * 4);
 
     auto slot_of = [&](auto sl) -> uint8_t* { return ring + decltype(sl)::value * BYTES; };
     auto issue = [&](int g, auto sl) {
@@ -790,13 +799,14 @@ __global__ void __launch_bounds__(512) k_gemm_pf16w(GemmArgs args) {
       for (int j = 0; j < A_INSTS; ++j) copy_to_lds<16>(a_rsrc, base + (16 * wid + 4 * j) * ROWB, a_off[j], uint32_t(g * ROWB));
 #pragma unroll
       for (int j = 0; j < WCOPIES; ++j)
-        copy_to_lds<16>(w_rsrc, base + W_OFF + (2 * wid + j) * kTileBytes, w_off[j], uint32_t(g * kTileBytes));
+        copy_to_lds<16>(w_rsrc, base + W_OFF + (WCOPIES * wid + j) * kTileBytes, w_off[j],
+                        uint32_t(g * kTileBytes));
       if (scale_lane || (ASYM && wid == 0 && lane < 48))
         copy_to_lds<16>(w_rsrc, base + S_OFF + (wid == 3 ? 1024 : 0), m_off + uint32_t(g) * m_step, 0u);
-      if (wid == 1 || wid == 2) {
+      if (wid >= 1 && wid <= RG) {
 #pragma unroll
         for (int j = 0; j < SG; ++j)
-          copy_to_lds<4>(r_rsrc, base + R_OFF + j * 512 + (wid - 1) * 256, r_off + 4 * j, uint32_t(g * 4 * SG));
+          copy_to_lds<4>(r_rsrc, base + R_OFF + j * (ROWS * 4) + (wid - 1) * 256, r_off + 4 * j, uint32_t(g * 4 * SG));
       }
     };
 
@@ -828,7 +838,7 @@ __global__ void __launch_bounds__(512) k_gemm_pf16w(GemmArgs args) {
 #pragma unroll
             for (int mb = 0; mb < NMB; ++mb) {
               const f32x4_t xv =
-                  *reinterpret_cast<const f32x4_t*>(s_rs + (s / SPS) * 128 + (2 * mb + wm) * 16 + 4 * kq);
+                  *reinterpret_cast<const f32x4_t*>(s_rs + (s / SPS) * ROWS + (RG * mb + wm) * 16 + 4 * kq);
 #pragma unroll
               for (int nb = 0; nb < 4; ++nb) g[mb][nb] = xv * negz[nb];
             }
@@ -844,7 +854,7 @@ __global__ void __launch_bounds__(512) k_gemm_pf16w(GemmArgs args) {
           u32x4_t a[NMB];
 #pragma unroll
           for (int mb = 0; mb < NMB; ++mb) {
-            const int r = (2 * mb + wm) * 16 + col;
+            const int r = (RG * mb + wm) * 16 + col;
             const int c = (4 * ws + kq) ^ swz(r);
             a[mb] = *reinterpret_cast<const u32x4_t*>(base + r * ROWB + c * 16);
           }
@@ -920,7 +930,7 @@ __global__ void __launch_bounds__(512) k_gemm_pf16w(GemmArgs args) {
       }
     };
     const int nrb = (rows + 15) / 16;
-    const int nmb = std::min(4, std::max(0, (nrb - wm + 1) / 2));
+    const int nmb = std::min(4, std::max(0, (nrb - wm + RG - 1) / RG));
     switch (nmb) {
       case 4: kloop(std::integral_constant<int, 4>{}); break;
       case 3: kloop(std::integral_constant<int, 3>{}); break;
@@ -929,12 +939,12 @@ __global__ void __launch_bounds__(512) k_gemm_pf16w(GemmArgs args) {
       default: kloop(std::integral_constant<int, 0>{}); break;
     }
 
-    // epilogue: row (2 mb + wm) * 16 + 4 kq + i, columns of blocks cb0 + 4 wn + nb
+    // epilogue: row (RG mb + wm) * 16 + 4 kq + i, columns of blocks cb0 + 4 wn + nb
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int r = (2 * mb + wm) * 16 + 4 * kq + i;
+        const int r = (RG * mb + wm) * 16 + 4 * kq + i;
         if (r >= rows) continue;
         const int64_t pos = row_start + r;
         if constexpr (KIND == GEMM_PLAIN) {
@@ -967,15 +977,20 @@ static hipError_t launch_pf_kind(const GemmArgs& g, hipStream_t st) {
     // wide tiles (8 waves, 128 x 256) when they still give every CU a work item
     const int64_t wblk = g.N / (16 * kPfwCB);
     if (g.N % (16 * kPfwCB) == 0 && int64_t(g.max_tiles) * wblk >= 256) {
-      const unsigned wgrid = unsigned(std::min<int64_t>(int64_t(g.max_tiles) * wblk, 256));
+      // gate/up (long K): 8-wave workgroups, each weight tile feeding 128 rows; the plain
+      // (down) projection: two 4-wave workgroups per CU (256-expert T = 4096: gate/up
+      // 3.08 -> 3.20 ms with 4-wave workgroups, down 1.63 -> 1.56 ms)
+      constexpr int RG = KIND == GEMM_PLAIN ? 1 : 2;
+      const unsigned wgrid = unsigned(std::min<int64_t>(int64_t(g.max_tiles) * (kPfRows / (64 * RG)) * wblk, 512 / RG));
+      const dim3 blk(256 * RG);
       if (g.sg == 4)
-        hipLaunchKernelGGL((k_gemm_pf16w<KIND, false, 4>), dim3(wgrid), dim3(512), 0, st, g);
+        hipLaunchKernelGGL((k_gemm_pf16w<KIND, false, 4, RG>), dim3(wgrid), blk, 0, st, g);
       else if (g.sg == 2)
-        hipLaunchKernelGGL((k_gemm_pf16w<KIND, false, 2>), dim3(wgrid), dim3(512), 0, st, g);
+        hipLaunchKernelGGL((k_gemm_pf16w<KIND, false, 2, RG>), dim3(wgrid), blk, 0, st, g);
       else if (g.asym)
-        hipLaunchKernelGGL((k_gemm_pf16w<KIND, true, 1>), dim3(wgrid), dim3(512), 0, st, g);
+        hipLaunchKernelGGL((k_gemm_pf16w<KIND, true, 1, RG>), dim3(wgrid), blk, 0, st, g);
       else
-        hipLaunchKernelGGL((k_gemm_pf16w<KIND, false, 1>), dim3(wgrid), dim3(512), 0, st, g);
+        hipLaunchKernelGGL((k_gemm_pf16w<KIND, false, 1, RG>), dim3(wgrid), blk, 0, st, g);
       return hipGetLastError();
     }
   }
