@@ -4,7 +4,8 @@
 // experts and combining the results are costs of their own; this is the dispatch step.
 //
 // One workgroup of up to 16 waves.  Wave w owns a contiguous range of slots.
-//   pass 1: per-wave expert counts in LDS;
+//   pass 1: per-wave expert counts in LDS (and, when they fit, every slot's expert as
+//           a 16-bit value in LDS, so pass 3 does not read the ids again);
 //   pass 2: counts, offsets (exclusive scan) and each wave's base per expert;
 //   pass 3: each wave walks its range 64 slots at a time in slot order; lanes with the
 //           same expert find their rank with ballots, so the scatter is stable.
@@ -75,7 +76,7 @@ __global__ void __launch_bounds__(kPermThreads) k_permute(const int32_t* __restr
                                                           TileDesc* __restrict__ tiles, int32_t* __restrict__ num_tiles,
                                                           int tile_rows, const uint8_t* __restrict__ ebits,
                                                           const uint8_t* __restrict__ egroups,
-                                                          int32_t* __restrict__ fmt_tiles) {
+                                                          int32_t* __restrict__ fmt_tiles, int cache_ex) {
   extern __shared__ int32_t lds[];
   __shared__ int32_t wave_tot[kPermThreads / 64 + 1];
   const int ee = e + shared;            // experts incl. the shared one
@@ -83,14 +84,15 @@ __global__ void __launch_bounds__(kPermThreads) k_permute(const int32_t* __restr
   const int64_t P = t * S;
   int32_t* cnt = lds;                   // [nwaves][ee]
   int32_t* tot = lds + nwaves * ee;     // [ee + 1]
+  uint16_t* s_ex = reinterpret_cast<uint16_t*>(lds + nwaves * ee + 5 * ee + 1);   // [P] (cache_ex)
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   for (int i = tid; i < nwaves * ee + ee + 1; i += kPermThreads) lds[i] = 0;
   __syncthreads();
   const int64_t per = (P + nwaves - 1) / nwaves;
   const int64_t beg = std::min<int64_t>(P, int64_t(wid) * per), end = std::min<int64_t>(P, beg + per);
-  auto expert_of = [&](int64_t s) -> int {
-    const int64_t tok = s / S;
-    const int j = int(s - tok * S);
+  auto expert_of = [&](int64_t s) -> int {   // s < t * S < 2^31
+    const uint32_t tok = uint32_t(s) / uint32_t(S);
+    const int j = int(uint32_t(s) - tok * uint32_t(S));
     if (j >= k) return e;               // the shared expert
     int x = ids[tok * k + j];
     return min(max(x, 0), e - 1);       // out-of-range ids are clamped
@@ -99,13 +101,25 @@ __global__ void __launch_bounds__(kPermThreads) k_permute(const int32_t* __restr
   constexpr int kKeep = 4;
   int kept[kKeep];
   if (wid < nwaves) {
-    int i = 0;
-    for (int64_t s = beg + lane; s < end; s += 64, ++i) {
-      const int x = expert_of(s);
+    // kU rounds of 64 slots at a time: their id loads are all in flight before the
+    // counts that depend on them
+    constexpr int kU = 8;
+    static_assert(kKeep <= kU, "the kept rounds come from the first batch");
+    for (int64_t s0 = beg; s0 < end; s0 += 64 * kU) {
+      int xs[kU];
 #pragma unroll
-      for (int j = 0; j < kKeep; ++j)
-        if (i == j) kept[j] = x;
-      atomicAdd(&cnt[wid * ee + x], 1);
+      for (int u = 0; u < kU; ++u) {
+        const int64_t s = s0 + 64 * u + lane;
+        xs[u] = s < end ? expert_of(s) : -1;
+      }
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int64_t s = s0 + 64 * u + lane;
+        if (xs[u] < 0) continue;
+        if (cache_ex) s_ex[s] = uint16_t(xs[u]);
+        if (s0 == beg && u < kKeep) kept[u] = xs[u];
+        atomicAdd(&cnt[wid * ee + xs[u]], 1);
+      }
     }
   }
   __syncthreads();
@@ -149,7 +163,9 @@ __global__ void __launch_bounds__(kPermThreads) k_permute(const int32_t* __restr
       const int64_t s = s0 + lane;
       const bool valid = s < end;
       int ex = 0;
-      if (i < kKeep) {
+      if (cache_ex) {
+        if (valid) ex = s_ex[s];
+      } else if (i < kKeep) {
 #pragma unroll
         for (int j = 0; j < kKeep; ++j)
           if (i == j && valid) ex = kept[j];
@@ -229,9 +245,14 @@ hipError_t launch_permute(const int32_t* ids, int64_t t, int32_t k, int32_t e, i
   const int64_t P = t * (k + shared);
   int nwaves = int(std::min<size_t>(16, (budget / sizeof(int32_t) - (5 * ee + 1)) / ee));
   nwaves = int(std::max<int64_t>(1, std::min<int64_t>(nwaves, (P + 63) / 64)));
-  const size_t lds = (size_t(nwaves) * ee + 5 * ee + 1) * sizeof(int32_t);
+  size_t lds = (size_t(nwaves) * ee + 5 * ee + 1) * sizeof(int32_t);
+  // every slot's expert kept in LDS (16 bits each) while the total stays within 150 KB;
+  // larger batches read the ids again in the scatter pass
+  const size_t ex_bytes = size_t(P) * sizeof(uint16_t);
+  const int cache_ex = lds + ex_bytes <= 150 * 1024 ? 1 : 0;
+  if (cache_ex) lds += ex_bytes;
   hipLaunchKernelGGL(k_permute, dim3(1), dim3(kPermThreads), lds, st, ids, t, k, e, shared, nwaves, counts,
-                     offsets, perm, inv, tiles, num_tiles, tile_rows, ebits, egroups, fmt_tiles);
+                     offsets, perm, inv, tiles, num_tiles, tile_rows, ebits, egroups, fmt_tiles, cache_ex);
   return hipGetLastError();
 }
 
