@@ -354,9 +354,10 @@ Q4_API int moe_int4_ffn_forward(const q4_moe_layer_t* layer, const uint16_t* x_b
  *       moe_int4_ffn_forward); the routed output of a position is the fp32 sum of its
  *       slices in slice order;
  *   q_x [t][H] int8, s_x [t] fp32, q_h [P][I] int8, s_h [P] fp32 (W4A8; NULL in W4A16).
- * For a one-expert layer at decode sizes (see moe_int4_ffn_plan) the debug call also
- * runs the permutation, for its views, and keeps y in the workspace with the combine
- * as a launch of its own (the same arithmetic, so the same results).
+ * For a one-expert layer at decode sizes and for a single token (rows_in_token_order,
+ * slot_tiles of moe_int4_ffn_plan) the debug call also runs the permutation, for its
+ * views, and (one-expert layer) keeps y in the workspace with the combine as a launch of
+ * its own (the same arithmetic, so the same results).
  * The gate and up products before SwiGLU are not stored by the fused kernel; the same
  * GEMM core gives them on the forward's own inputs: int4_linear_forward (W4A16, fp32
  * g and u) and int4_w4a8_group_acc (the INT32 group accumulators of either GEMM) on an
@@ -426,6 +427,11 @@ Q4_API int moe_int4_ffn_forward_noalloc(const q4_moe_layer_t* layer, const uint1
  *                 read and write rows in token order;
  *  combine_in_down 1 when, in addition, the down projection has no K slices: its
  *                 epilogue applies the weight and rounds to bf16 (no combine launch).
+ *  slot_tiles     1 for a single token (t == 1) on any other layer with one weight
+ *                 format at decode sizes: its slots have distinct experts, so each
+ *                 slot is its own one-row tile taken straight from topk_ids (no
+ *                 permutation launch; rows and y stay in slot order).  The results equal
+ *                 the permuted path's bit for bit.
  *  workspace_bytes moe_int4_ffn_workspace_bytes(layer, t, mode).
  * Errors as moe_int4_ffn_forward's validation (the layer's device pointers are checked
  * for NULL and alignment only).
@@ -439,6 +445,7 @@ typedef struct q4_ffn_plan_t {
   int32_t prefill_addr_limited;
   int32_t rows_in_token_order;
   int32_t combine_in_down;
+  int32_t slot_tiles;
   int64_t workspace_bytes;
 } q4_ffn_plan_t;
 Q4_API int moe_int4_ffn_plan(const q4_moe_layer_t* layer, int64_t t, int mode, q4_ffn_plan_t* plan);

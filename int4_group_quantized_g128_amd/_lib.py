@@ -70,7 +70,8 @@ class Q4FfnViews(ctypes.Structure):
 class Q4FfnPlan(ctypes.Structure):
     """Mirror of q4_ffn_plan_t."""
     _fields_ = [("kernel", _i32), ("tile_rows", _i32), ("down_ksplit", _i32), ("prefill_addr_limited", _i32),
-                ("rows_in_token_order", _i32), ("combine_in_down", _i32), ("workspace_bytes", _i64)]
+                ("rows_in_token_order", _i32), ("combine_in_down", _i32), ("slot_tiles", _i32),
+                ("workspace_bytes", _i64)]
 
 
 def _sig(name, res, args):
@@ -381,7 +382,7 @@ def moe_int4_ffn_plan(layer, t, mode):
     return {"kernel": "prefill" if p.kernel == 1 else "decode", "tile_rows": p.tile_rows,
             "down_ksplit": p.down_ksplit, "prefill_addr_limited": bool(p.prefill_addr_limited),
             "rows_in_token_order": bool(p.rows_in_token_order), "combine_in_down": bool(p.combine_in_down),
-            "workspace_bytes": int(p.workspace_bytes)}
+            "slot_tiles": bool(p.slot_tiles), "workspace_bytes": int(p.workspace_bytes)}
 
 
 class MoELayer:

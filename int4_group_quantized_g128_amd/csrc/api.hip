@@ -143,6 +143,13 @@ bool one_expert_decode(const q4_moe_layer_t* L, const FwdWorkspace& w) {
          !w.prefill;
 }
 
+// One token on a layer with one weight format (and not the one-expert path): its slots
+// have distinct experts, so the permutation is one row per expert; the GEMMs take
+// one-row tiles straight from the routed ids instead (see ffn_forward).
+bool slot_tile_decode(const q4_moe_layer_t* L, int64_t t, const FwdWorkspace& w) {
+  return t == 1 && !w.prefill && !L->expert_bits && !L->expert_groups && !one_expert_decode(L, w);
+}
+
 FwdWorkspace carve(const q4_moe_layer_t* L, int64_t t, int mode, void* base) {
   FwdWorkspace w;
   const int shared = L->shared_inter > 0 ? 1 : 0;
@@ -487,6 +494,7 @@ int moe_int4_ffn_plan(const q4_moe_layer_t* L, int64_t t, int mode, q4_ffn_plan_
   plan->prefill_addr_limited = (!w.prefill && wants_prefill(L, t, mode)) ? 1 : 0;
   plan->rows_in_token_order = one_expert_decode(L, w) ? 1 : 0;
   plan->combine_in_down = (plan->rows_in_token_order && w.ksplit == 1) ? 1 : 0;
+  plan->slot_tiles = slot_tile_decode(L, t, w) ? 1 : 0;
   plan->workspace_bytes = w.bytes;
   return ok();
 }
@@ -608,9 +616,15 @@ int ffn_forward(const q4_moe_layer_t* L, const uint16_t* x_bf16, int64_t t, cons
   // debug call still runs the permutation and the separate combine, for its views.
   const bool dense = one_expert_decode(L, w);
   const bool fused_combine = dense && w.ksplit == 1 && !views;
+  // A single token on a layer with one weight format: slot i of the token is its own
+  // one-row tile (its experts are distinct, so the permutation would give the same
+  // tiles), rows stay in slot order and the combine reads them there; no permutation
+  // launch.  Each output row depends only on its own row and expert, so the results
+  // equal the permuted path's bit for bit (the debug call takes that path, for its views).
+  const bool slots = slot_tile_decode(L, t, w) && !views;
   int rc;
   stage_begin(Q4_STAGE_PERMUTE, stream);
-  if (!dense || views) {
+  if ((!dense && !slots) || views) {
     if ((rc = check_hip(launch_permute(topk_ids, t, L->top_k, L->num_experts, shared, w.counts, w.offsets, w.perm,
                                        w.inv, w.tiles, w.num_tiles, w.tile_rows, stream, L->expert_bits,
                                        L->expert_groups, w.fmt_tiles),
@@ -656,6 +670,14 @@ int ffn_forward(const q4_moe_layer_t* L, const uint16_t* x_bf16, int64_t t, cons
   if (fused_combine) {
     dn.combine_w = topk_w;
     dn.out_bf16 = out_bf16;
+  }
+  if (slots) {
+    gu.tiles = dn.tiles = nullptr;
+    gu.slot_ids = dn.slot_ids = topk_ids;
+    gu.slot_k = dn.slot_k = L->top_k;
+    gu.perm = nullptr;
+    gu.src_div = int32_t(S);   // x row = token = slot / S
+    gu.dense_rows = dn.dense_rows = t * S;
   }
   auto gemm1 = [&](const GemmArgs& g, int act, int kind) {
     return w.prefill ? launch_gemm_prefill(g, act, kind, stream) : launch_gemm(g, act, kind, rb, stream);
@@ -749,8 +771,8 @@ int ffn_forward(const q4_moe_layer_t* L, const uint16_t* x_bf16, int64_t t, cons
   }
   stage_begin(Q4_STAGE_COMBINE, stream);
   rc = fused_combine ? Q4_OK
-                     : check_hip(launch_combine(w.y, dense ? nullptr : w.inv, topk_w, t, L->top_k, shared, H, out_bf16,
-                                                stream, dn.ksplit, dn.out_slice),
+                     : check_hip(launch_combine(w.y, (dense || slots) ? nullptr : w.inv, topk_w, t, L->top_k, shared,
+                                                H, out_bf16, stream, dn.ksplit, dn.out_slice),
                                  "combine");
   stage_end(Q4_STAGE_COMBINE, stream);
   return rc;

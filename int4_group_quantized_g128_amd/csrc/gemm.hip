@@ -168,7 +168,9 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs args) {
   const int64_t nblk = N / (16 * kCBWG);
   const int64_t tile_rows = 16 * MB;
   int64_t t_first = 0;   // layers with several weight formats: this launch's tile range
-  int64_t ntiles = args.tiles ? int64_t(*args.num_tiles) : (args.dense_rows + tile_rows - 1) / tile_rows;
+  int64_t ntiles = args.tiles      ? int64_t(*args.num_tiles)
+                   : args.slot_ids ? args.dense_rows
+                                   : (args.dense_rows + tile_rows - 1) / tile_rows;
   if (args.fmt_tiles) {
     t_first = args.fmt_tiles[args.fmt];
     ntiles = args.fmt_tiles[args.fmt_end] - t_first;
@@ -213,6 +215,13 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs args) {
       expert = d.expert;
       row_start = d.row_start + sub * tile_rows;
       rows = std::min<int64_t>(tile_rows, int64_t(d.rows) - sub * tile_rows);
+    } else if (args.slot_ids) {   // one row per slot, its expert straight from the routed ids
+      const int64_t tok = tile / args.slots_per_token;
+      const int j = int(tile - tok * args.slots_per_token);
+      expert = j < args.slot_k ? min(max(args.slot_ids[tok * args.slot_k + j], 0), args.num_experts - 1)
+                               : args.num_experts;
+      row_start = tile;
+      rows = 1;
     } else {
       row_start = tile * tile_rows;
       rows = std::min<int64_t>(tile_rows, args.dense_rows - row_start);
@@ -233,7 +242,9 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs args) {
       const int64_t r = mb * 16 + col;
       ri[mb].valid = r < rows;
       ri[mb].pos = row_start + (ri[mb].valid ? r : 0);
-      ri[mb].src = args.perm ? args.perm[ri[mb].pos] / args.slots_per_token : ri[mb].pos;
+      ri[mb].src = args.perm ? args.perm[ri[mb].pos] / args.slots_per_token
+                   : args.src_div > 1 ? ri[mb].pos / args.src_div
+                                      : ri[mb].pos;
     }
 
     const int lcb = cgrp * NBW;                       // wave's first block inside the workgroup
@@ -521,7 +532,10 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs args) {
             if (r >= rows) continue;
             const int64_t pos = row_start + r;
             float sa = 1.0f;
-            if constexpr (A == Act::I8) sa = args.a_scale[args.perm ? args.perm[pos] / args.slots_per_token : pos];
+            if constexpr (A == Act::I8)
+              sa = args.a_scale[args.perm ? args.perm[pos] / args.slots_per_token
+                                : args.src_div > 1 ? pos / args.src_div
+                                                   : pos];
             if constexpr (KIND == GEMM_PLAIN) {
               if (args.combine_w) {
                 // the combine of a one-expert layer: its arithmetic exactly (fp32 w * y, then bf16)
@@ -584,7 +598,7 @@ static hipError_t launch_cfg(const GemmArgs& g, hipStream_t st) {
   constexpr int cbwg = (4 / KW) * NBW;
   const int64_t nblk = g.N / (16 * cbwg);
   const int64_t trows = 16 * MB;
-  const int64_t max_tiles = g.tiles ? g.max_tiles : (g.dense_rows + trows - 1) / trows;
+  const int64_t max_tiles = g.tiles ? g.max_tiles : g.slot_ids ? g.dense_rows : (g.dense_rows + trows - 1) / trows;
   constexpr bool can_split = KIND == GEMM_PLAIN && MB == 1 && KW == 4 && NBW == 2;
   const int64_t nsub = (g.tiles && g.built_rows > trows) ? (g.built_rows + trows - 1) / trows : 1;
   const int64_t items = max_tiles * nsub * nblk * ((can_split && g.ksplit > 1) ? g.ksplit : 1);

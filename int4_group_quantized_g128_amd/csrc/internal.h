@@ -86,7 +86,11 @@ struct GemmArgs {
   int64_t N;              // device columns (2I for gate/up)
   int64_t K;
   // tiles
-  const TileDesc* tiles;  // NULL = dense rows [0, dense_rows)
+  const TileDesc* tiles;  // NULL = dense rows [0, dense_rows), or the slot tiles below
+  const int32_t* slot_ids;  // tiles == NULL: tile i is slot i (one row) of expert slot_ids[i / S * slot_k + i % S]
+                            //   (i % S == slot_k: the shared expert), S = slots_per_token, dense_rows slots; or NULL
+  int32_t slot_k;
+  int32_t src_div;        // perm == NULL: activation row = position / src_div (0 / 1: the position)
   int32_t built_rows;     // rows per tile as the permutation built them (0: the kernel's own);
                           //   taller tiles are walked in sub-tiles (streaming kernel only)
   const int32_t* num_tiles;

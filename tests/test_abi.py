@@ -290,10 +290,13 @@ def test_plan_kernel_choice(L):
         assert not p["prefill_addr_limited"]
         one = desc is dense and kernel == "decode"
         assert p["rows_in_token_order"] == one and p["combine_in_down"] == (one and ks == 1)
+        # a single token on a one-format layer: one-row slot tiles, no permutation launch
+        assert p["slot_tiles"] == (t == 1 and desc is not dense), (t, p)
     # layers with several weight formats keep the 64-rows-per-expert rule
     mixed = _plan_desc(L, 256, 7168, 2048, 8, shared=True, expert_bits=4096, gate_up_offsets=4096,
                        down_offsets=4096)
     assert L.moe_int4_ffn_plan(mixed, 1280, W8)["kernel"] == "decode"
+    assert not L.moe_int4_ffn_plan(mixed, 1, W8)["slot_tiles"]   # formats: the permutation orders them
     assert L.moe_int4_ffn_plan(mixed, 2048, W8)["kernel"] == "prefill"
     grouped = _plan_desc(L, 256, 7168, 2048, 8, shared=True, expert_groups=4096, gate_up_offsets=4096,
                          down_offsets=4096)

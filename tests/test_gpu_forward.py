@@ -240,3 +240,30 @@ def test_wide_bf16_prefill_tiles(lib, asym):
     rows = np.sort(rng.choice(t, 40, replace=False))
     ref = ffn.moe_w4a16(_np(x)[rows], oe, ids[rows], w[rows])
     assert ffn.max_rel_l2(_np(out)[rows], ref) <= TOL_W4A16
+
+
+# ------------------------------------------------------------------ single token: slot tiles
+@pytest.mark.parametrize("mode", [0, 1], ids=["w4a16", "w4a8"])
+@pytest.mark.parametrize("which", ["small_shared", "moe8"])
+def test_single_token_slot_tiles_equal_permuted(lib, small, moe8, which, mode):
+    """At t = 1 the forward takes one-row slot tiles straight from the routed ids (no
+    permutation launch; on the 8-expert layer the down projection also splits K); the
+    debug call runs the permuted path.  Each output row depends only on its own row and
+    expert, so the two outputs agree bit for bit, and both match the oracle."""
+    layer, oe = small if which == "small_shared" else moe8
+    plan = lib.moe_int4_ffn_plan(layer, 1, mode)
+    assert plan["slot_tiles"] and plan["kernel"] == "decode"
+    for seed in range(3):
+        x = synth.normal(synth.stream_key(71, seed), (1, layer.hidden), 1.0).to(torch.bfloat16)
+        rng = np.random.default_rng(100 + seed)
+        ids = rng.permutation(layer.num_experts)[: layer.top_k][None, :].astype(np.int32)
+        w = rng.dirichlet(np.ones(layer.top_k))[None, :]
+        out = _forward(lib, layer, x, ids, w, mode)
+        dbg, _ = lib.moe_int4_ffn_debug(layer, x.cuda(), torch.as_tensor(ids).cuda(),
+                                        torch.as_tensor(w, dtype=torch.float32).cuda(), mode=mode)
+        torch.cuda.synchronize()
+        assert torch.equal(out.cpu(), dbg.cpu()), (which, mode, seed)
+        shared = oe(layer.num_experts) if layer.shared else None
+        fn = ffn.moe_w4a16 if mode == 0 else ffn.moe_w4a8
+        ref = fn(_np(x), oe, ids, w, shared=shared) if shared is not None else fn(_np(x), oe, ids, w)
+        assert ffn.max_rel_l2(_np(out), ref) <= (TOL_W4A16 if mode == 0 else TOL_W4A8)
