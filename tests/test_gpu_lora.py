@@ -152,3 +152,21 @@ def test_lora8(lib, lora8, t):
     rows = np.arange(t) if t <= 64 else np.sort(np.random.default_rng(7).choice(t, 24, replace=False))
     ref = lora.moe_lora(_np(x)[rows], ob, oa, ids[rows], w[rows])
     assert ffn.max_rel_l2(_np(out)[rows], ref) <= TOL
+
+
+def test_lora_grouped_many_experts(lib):
+    """Grouped adapter path with many experts and four choices per token (E = 64,
+    top-4, rank 16, T = 320): most tiles of the permutation hold a few slots, some
+    experts none."""
+    E, H, I, k, r, t = 64, 256, 384, 4, 16, 320
+    base = (synth.normal(synth.stream_key(68, 1), (I, H), 0.05), synth.normal(synth.stream_key(68, 2), (I, H), 0.05),
+            synth.normal(synth.stream_key(68, 3), (H, I), 0.05))
+    adapters = lambda e: synth.lora_adapters("lora8", e, rank=r, dims=(H, I))
+    layer, ob, oa = _build(lib, base, adapters, E, H, I, k, r, False)
+    x = synth.normal(synth.stream_key(69, t), (t, H), 1.0).to(torch.bfloat16)
+    rng = np.random.default_rng(5)
+    ids = np.stack([rng.choice(E // 2, k, replace=False) for _ in range(t)]).astype(np.int32)   # experts 32.. unused
+    w = rng.dirichlet(np.ones(k), size=t)
+    out = _run(lib, layer, x, ids, w)
+    ref = lora.moe_lora(_np(x), ob, oa, ids, w)
+    assert ffn.max_rel_l2(_np(out), ref) <= TOL
