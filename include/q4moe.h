@@ -216,11 +216,16 @@ Q4_API int q2_repack_device(const uint8_t* packed, const uint16_t* scales, int64
  *
  *  x_bf16    device [t][h] bf16 tokens.
  *  w_router  device [e][h] fp32 router weight; bias: device [e] fp32 or NULL.
- *  logits_out device [t][e] fp32 (required): L = x W_r^T + b, fp32 arithmetic.
+ *  logits_out device [t][e] fp32 (required): L = x W_r^T + b with exact products
+ *            and fp32 sums.  From 512 tokens and 64 experts the sums run on the bf16
+ *            matrix cores: each fp32 weight is split exactly into three bf16 parts
+ *            (hi + mid + lo), and x is bf16, so every product stays exact.
  *  topk_ids  device [t][k] int32: experts by descending L, equal L -> lower index.
  *  topk_w    device [t][k] fp32: exp(L_j - L_max) / sum over the selected k
  *            (softmax over e, then renormalised over the selected k).
- *  workspace device buffer of moe_route_workspace_bytes(t, h, e) bytes (may be 0).
+ *  workspace device buffer of moe_route_workspace_bytes(t, h, e) bytes (may be 0),
+ *            16-byte aligned (Q4_ERR_ALIGN otherwise): K-slice partial sums and, for
+ *            the large batches above, the three bf16 parts of w_router.
  *  Requires 1 <= k <= e <= 1024, h % 16 == 0, h >= 16; t == 0 is a no-op.
  *  NaN logits give unspecified ids.
  */

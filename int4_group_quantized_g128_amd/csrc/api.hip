@@ -433,7 +433,7 @@ int q2_repack_device(const uint8_t* packed, const uint16_t* scales, int64_t n, i
 
 size_t moe_route_workspace_bytes(int64_t t, int64_t h, int32_t e) {
   if (t <= 0 || h <= 0 || e <= 0) return 0;
-  return size_t(route_kslices(t, h, e)) * size_t(t) * size_t(e) * sizeof(float);
+  return route_workspace_bytes(t, h, e);
 }
 
 int moe_route_topk(const uint16_t* x_bf16, const float* w_router, const float* bias, int64_t t, int64_t h, int32_t e,
@@ -448,6 +448,7 @@ int moe_route_topk(const uint16_t* x_bf16, const float* w_router, const float* b
   Q4_REQUIRE(!misaligned(x_bf16) && !misaligned(w_router), Q4_ERR_ALIGN, "x and w_router must be 16-byte aligned");
   const size_t need = moe_route_workspace_bytes(t, h, e);
   Q4_REQUIRE(ws_bytes >= need && (need == 0 || workspace), Q4_ERR_WORKSPACE, "workspace %zu < %zu", ws_bytes, need);
+  Q4_REQUIRE(!misaligned(workspace), Q4_ERR_ALIGN, "workspace must be 16-byte aligned");
   return check_hip(launch_route(x_bf16, w_router, bias, t, h, e, k, logits_out, topk_ids, topk_w,
                                 static_cast<float*>(workspace), stream),
                    "route launch");

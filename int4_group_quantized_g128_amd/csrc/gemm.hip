@@ -715,8 +715,9 @@ hipError_t launch_gemm(const GemmArgs& g, int act, int kind, int row_blocks, hip
 // out[t][n] = bf16( sum_{j<k, ascending} w[t][j] * y[inv[t S + j]][n] (+ y[inv[t S + k]][n]) ),
 // inv == NULL: positions in slot order (a one-expert layer's rows are its tokens),
 // with y = the sum of the ksplit slices y + s * slice in slice order when the down
-// projection split K (SPLIT)
-template <bool SPLIT>
+// projection split K (SPLIT); NT reads y with non-temporal loads (each value is read
+// once; used when y is larger than the 256 MB last-level cache)
+template <bool SPLIT, bool NT>
 __global__ void __launch_bounds__(256) k_combine(const float* __restrict__ y, const int32_t* __restrict__ inv,
                                                  const float* __restrict__ w, int64_t t, int32_t k, int shared,
                                                  int64_t h, uint16_t* __restrict__ out, int ksplit, int64_t slice) {
@@ -727,7 +728,13 @@ __global__ void __launch_bounds__(256) k_combine(const float* __restrict__ y, co
   const int64_t c = (i - tok * per_tok) * 4;
   const int S = k + shared;
   auto row = [&](int64_t pos) {
-    float4 v = *reinterpret_cast<const float4*>(y + pos * h + c);
+    float4 v;
+    if constexpr (NT) {
+      const uint4 u = load16_stream(y + pos * h + c);
+      v = make_float4(__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z), __uint_as_float(u.w));
+    } else {
+      v = *reinterpret_cast<const float4*>(y + pos * h + c);
+    }
     if constexpr (SPLIT) {
       for (int s = 1; s < ksplit; ++s) {
         const float4 u = *reinterpret_cast<const float4*>(y + s * slice + pos * h + c);
@@ -782,10 +789,16 @@ hipError_t launch_combine(const float* y, const int32_t* inv, const float* w, in
   const int64_t n = t * (h / 4);
   if (n == 0) return hipSuccess;
   const dim3 grid(unsigned((n + 255) / 256));
+  const bool nt = double(t) * (k + shared) * h * 4 > 256.0 * 1024 * 1024;
   if (ksplit > 1)
-    hipLaunchKernelGGL(k_combine<true>, grid, dim3(256), 0, st, y, inv, w, t, k, shared, h, out, ksplit, slice);
+    hipLaunchKernelGGL((k_combine<true, false>), grid, dim3(256), 0, st, y, inv, w, t, k, shared, h, out, ksplit,
+                       slice);
+  else if (nt)
+    hipLaunchKernelGGL((k_combine<false, true>), grid, dim3(256), 0, st, y, inv, w, t, k, shared, h, out, 1,
+                       int64_t(0));
   else
-    hipLaunchKernelGGL(k_combine<false>, grid, dim3(256), 0, st, y, inv, w, t, k, shared, h, out, 1, int64_t(0));
+    hipLaunchKernelGGL((k_combine<false, false>), grid, dim3(256), 0, st, y, inv, w, t, k, shared, h, out, 1,
+                       int64_t(0));
   return hipGetLastError();
 }
 

@@ -38,8 +38,10 @@ hipError_t launch_quantize2(const void* w, int dtype, int64_t n, int64_t k, uint
 hipError_t launch_repack2(const uint8_t* packed, const uint16_t* scales, int64_t n, int64_t k, int gate_up, void* out,
                           hipStream_t st);
 
-// Router: fp32 logits split over kslices partial sums, then reduction + top-k.
+// Router: fp32 logits split over kslices partial sums, then reduction + top-k; the
+// workspace holds the partial sums (and for large batches the split weights).
 int route_kslices(int64_t t, int64_t h, int32_t e);
+size_t route_workspace_bytes(int64_t t, int64_t h, int32_t e);
 hipError_t launch_route(const uint16_t* x, const float* wr, const float* bias, int64_t t, int64_t h,
                         int32_t e, int32_t k, float* logits, int32_t* ids, float* w, float* partial,
                         hipStream_t st);

@@ -11,11 +11,10 @@ namespace q4 {
 // Partial logits over K slices: a (16 TB)-token x (16 EB)-expert tile per wave, fp32
 // MFMA 16x16x4.  Lane (m = lane % 16, kq = lane / 16) feeds x[t0 + 16 i + m][k] and
 // W[e0 + 16 j + m][k] for k = k0 + 4 kq + s to MFMA s of each 16-wide K step; U steps
-// of loads are issued before their MFMAs.  Small batches use 16 x 16 tiles and many K
-// slices, with RED the workgroup's waves (up to 16) on consecutive slices whose sums are
-// added in LDS (in wave order) so that one partial per workgroup is written; large
-// batches use 32 x 64 or 64 x 64 tiles (each loaded x value feeds four expert blocks,
-// each W value two or four token blocks), one wave per slice.
+// of loads are issued before their MFMAs.  Batches below 512 tokens (or with fewer than
+// 64 experts) run 16 x 16 tiles and many K slices, with RED the workgroup's waves (up to
+// 16) on consecutive slices whose sums are added in LDS (in wave order) so that one
+// partial per workgroup is written; larger batches take the split-weight kernel below.
 template <int TB, int EB, int U, bool RED>
 __global__ void __launch_bounds__(RED ? 1024 : 64) k_router_partial(const uint16_t* __restrict__ x,
                                                                    const float* __restrict__ wr, int64_t t, int64_t h,
@@ -98,6 +97,123 @@ __global__ void __launch_bounds__(RED ? 1024 : 64) k_router_partial(const uint16
         for (int j = 0; j < EB; ++j) acc[i][j] += red[w - 1][i * EB + j][lane];
   }
   // C layout: lane holds tokens t0 + 16 i + 4 kq + r, expert e0 + 16 j + m
+  const int64_t slot = blockIdx.z;
+#pragma unroll
+  for (int i = 0; i < TB; ++i)
+#pragma unroll
+    for (int j = 0; j < EB; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t tt = t0 + 16 * i + 4 * kq + r;
+        if (tt < t && ev[j]) partial[(slot * t + tt) * e + e0 + 16 * j + m] = acc[i][j][r];
+      }
+}
+
+// Large batches run the logits on the bf16 matrix cores at fp32 accuracy.  Each fp32
+// weight w is split into three bf16 parts with w = hi + mid + lo: hi is w truncated to
+// bf16, mid is (w - hi) truncated, lo is the rest truncated.  Both differences are exact
+// in fp32 and the rest has at most eight significant bits, so the sum is exact (for
+// |w| below about 2^-110 the last part can lose bits to underflow).  x is bf16 already,
+// so every product of x with a part is exact, and the matrix core adds them in fp32.
+// A non-finite w goes whole into hi (a NaN stays a NaN), with mid = lo = 0.
+// w3 holds the parts as three consecutive [n] bf16 arrays; each thread splits 8 values.
+__global__ void __launch_bounds__(256) k_router_split3(const float* __restrict__ w, int64_t n,
+                                                       uint16_t* __restrict__ w3) {
+  const int64_t i = (int64_t(blockIdx.x) * blockDim.x + threadIdx.x) * 8;
+  if (i >= n) return;
+  const float4 a = *reinterpret_cast<const float4*>(w + i);
+  const float4 b = *reinterpret_cast<const float4*>(w + i + 4);
+  const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  uint32_t part[3][4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    uint32_t hpart[3][2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const float x = v[2 * q + s];
+      const uint32_t u = __float_as_uint(x);
+      if (!__builtin_isfinite(x)) {
+        hpart[0][s] = (u >> 16) | (x != x ? 0x40u : 0u);
+        hpart[1][s] = 0;
+        hpart[2][s] = 0;
+      } else {
+        const float r = x - __uint_as_float(u & 0xffff0000u);
+        const uint32_t ru = __float_as_uint(r);
+        const float r2 = r - __uint_as_float(ru & 0xffff0000u);
+        hpart[0][s] = u >> 16;
+        hpart[1][s] = ru >> 16;
+        hpart[2][s] = __float_as_uint(r2) >> 16;
+      }
+    }
+#pragma unroll
+    for (int p = 0; p < 3; ++p) part[p][q] = hpart[p][0] | (hpart[p][1] << 16);
+  }
+#pragma unroll
+  for (int p = 0; p < 3; ++p)
+    *reinterpret_cast<uint4*>(w3 + p * n + i) = make_uint4(part[p][0], part[p][1], part[p][2], part[p][3]);
+}
+
+// Partial logits from the split weights: a (16 TB)-token x (16 EB)-expert tile per
+// wave, bf16 MFMA 16x16x32, one wave per K slice.  Lane (m = lane % 16, kq = lane / 16)
+// feeds x[t0 + 16 i + m][k .. k + 7] and part p of W[e0 + 16 j + m][k .. k + 7] with
+// k = k0 + 8 kq; each K step runs the three parts' MFMAs on one accumulator per tile
+// (hi, then mid, then lo), U steps of loads issued before their MFMAs.  Rows past t or
+// e and K past the slice load zeros for both operands.  Same partial layout as above.
+template <int TB, int EB, int U>
+__global__ void __launch_bounds__(64) k_router_x3(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w3,
+                                                  int64_t t, int64_t h, int32_t e, int64_t kslice,
+                                                  float* __restrict__ partial) {
+  const int lane = threadIdx.x;
+  const int m = lane & 15, kq = lane >> 4;
+  const int64_t e0 = int64_t(blockIdx.x) * 16 * EB, t0 = int64_t(blockIdx.y) * 16 * TB;
+  const int64_t kb = std::min<int64_t>(h, int64_t(blockIdx.z) * kslice), ke = std::min<int64_t>(h, kb + kslice);
+  const int64_t pn = int64_t(e) * h;   // elements from one part to the next
+  const uint16_t* xr[TB];
+  const uint16_t* wrow[EB];
+  bool tv[TB], ev[EB];
+#pragma unroll
+  for (int i = 0; i < TB; ++i) {
+    tv[i] = t0 + 16 * i + m < t;
+    xr[i] = x + (tv[i] ? t0 + 16 * i + m : 0) * h + 8 * kq;
+  }
+#pragma unroll
+  for (int j = 0; j < EB; ++j) {
+    ev[j] = e0 + 16 * j + m < e;
+    wrow[j] = w3 + (ev[j] ? e0 + 16 * j + m : 0) * h + 8 * kq;
+  }
+  f32x4_t acc[TB][EB];
+#pragma unroll
+  for (int i = 0; i < TB; ++i)
+#pragma unroll
+    for (int j = 0; j < EB; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const uint4 zero = make_uint4(0, 0, 0, 0);
+  for (int64_t k0 = kb; k0 < ke; k0 += 32 * U) {
+    uint4 xv[U][TB];
+    uint4 wv[U][3][EB];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t k = k0 + 32 * u;
+      const bool kv = k + 8 * kq < ke;   // ke and k are multiples of 16: all 8 or none
+#pragma unroll
+      for (int i = 0; i < TB; ++i) xv[u][i] = (tv[i] && kv) ? load16(xr[i] + k) : zero;
+#pragma unroll
+      for (int p = 0; p < 3; ++p)
+#pragma unroll
+        for (int j = 0; j < EB; ++j) wv[u][p][j] = (ev[j] && kv) ? load16(wrow[j] + p * pn + k) : zero;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int p = 0; p < 3; ++p)
+#pragma unroll
+        for (int i = 0; i < TB; ++i)
+#pragma unroll
+          for (int j = 0; j < EB; ++j) {
+            const u32x4_t av = {xv[u][i].x, xv[u][i].y, xv[u][i].z, xv[u][i].w};
+            const u32x4_t bv = {wv[u][p][j].x, wv[u][p][j].y, wv[u][p][j].z, wv[u][p][j].w};
+            acc[i][j] = mfma16x16x32<Act::BF16>(av, bv, acc[i][j]);
+          }
+  }
   const int64_t slot = blockIdx.z;
 #pragma unroll
   for (int i = 0; i < TB; ++i)
@@ -278,20 +394,39 @@ static hipError_t launch_topk(const float* partial, int nparts, const float* bia
   return hipGetLastError();
 }
 
+// Bytes of the partial sums, and with the split weights of large batches (the big
+// tiles) behind them at the next 256-byte boundary.
+static size_t route_partial_bytes(int64_t t, int64_t h, int32_t e) {
+  return size_t(route_kslices(t, h, e)) * size_t(t) * size_t(e) * sizeof(float);
+}
+size_t route_workspace_bytes(int64_t t, int64_t h, int32_t e) {
+  const size_t p = route_partial_bytes(t, h, e);
+  if (!route_big_tiles(t, e)) return p;
+  return (p + 255) / 256 * 256 + 3 * size_t(e) * size_t(h) * sizeof(uint16_t);
+}
+
 hipError_t launch_route(const uint16_t* x, const float* wr, const float* bias, int64_t t, int64_t h,
                         int32_t e, int32_t k, float* logits, int32_t* ids, float* w, float* partial,
                         hipStream_t st) {
+  const bool x3 = route_big_tiles(t, e);
   const int ks = route_kslices(t, h, e);
+  const int64_t kalign = x3 ? 32 : 16;   // the K step of the logit kernel
   int64_t kslice = (h + ks - 1) / ks;
-  kslice = (kslice + 15) / 16 * 16;
+  kslice = (kslice + kalign - 1) / kalign * kalign;
   const int kused = int((h + kslice - 1) / kslice);
   int nparts = kused;   // partial sums written (one per K slice, or per workgroup of slices)
-  if (route_huge_tiles(t, e)) {
-    dim3 grid(unsigned((e + 63) / 64), unsigned((t + 63) / 64), unsigned(kused));
-    hipLaunchKernelGGL((k_router_partial<4, 4, 2, false>), grid, dim3(64), 0, st, x, wr, t, h, e, kslice, partial);
-  } else if (route_big_tiles(t, e)) {
-    dim3 grid(unsigned((e + 63) / 64), unsigned((t + 31) / 32), unsigned(kused));
-    hipLaunchKernelGGL((k_router_partial<2, 4, 4, false>), grid, dim3(64), 0, st, x, wr, t, h, e, kslice, partial);
+  if (x3) {
+    uint16_t* w3 = reinterpret_cast<uint16_t*>(reinterpret_cast<uint8_t*>(partial) +
+                                               (route_partial_bytes(t, h, e) + 255) / 256 * 256);
+    const int64_t n = int64_t(e) * h;
+    hipLaunchKernelGGL(k_router_split3, dim3(unsigned((n / 8 + 255) / 256)), dim3(256), 0, st, wr, n, w3);
+    if (route_huge_tiles(t, e)) {
+      dim3 grid(unsigned((e + 63) / 64), unsigned((t + 63) / 64), unsigned(kused));
+      hipLaunchKernelGGL((k_router_x3<4, 4, 1>), grid, dim3(64), 0, st, x, w3, t, h, e, kslice, partial);
+    } else {
+      dim3 grid(unsigned((e + 63) / 64), unsigned((t + 31) / 32), unsigned(kused));
+      hipLaunchKernelGGL((k_router_x3<2, 4, 2>), grid, dim3(64), 0, st, x, w3, t, h, e, kslice, partial);
+    }
   } else {
     // about one workgroup per CU: the slices of a tile are shared out over
     // Q4_ROUTE_WGS / tiles workgroups (at least one), at most 16 waves each

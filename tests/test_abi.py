@@ -83,6 +83,11 @@ def test_route_validation(L):
     need = r.moe_route_workspace_bytes(4, 256, 8)
     assert need > 0
     assert r.moe_route_topk(fake, fake, None, 4, 256, 8, 2, fake, fake, fake, fake, need - 1, None) == L.Q4_ERR_WORKSPACE
+    odd = ctypes.c_void_p(4096 + 4)
+    assert r.moe_route_topk(fake, fake, None, 4, 256, 8, 2, fake, fake, fake, odd, need, None) == L.Q4_ERR_ALIGN
+    # from 512 tokens and 64 experts the workspace also holds the three bf16 parts of the weights
+    big = r.moe_route_workspace_bytes(512, 256, 64)
+    assert big >= 3 * 64 * 256 * 2 + 512 * 64 * 4
     # t == 0 is a successful no-op, even without buffers
     assert r.moe_route_topk(None, None, None, 0, 256, 8, 2, None, None, None, None, 0, None) == L.Q4_OK
 

@@ -104,12 +104,13 @@ def test_router_parity(lib, name, t):
 
 
 @pytest.mark.parametrize("t,h,e,k", [(17, 512, 100, 3), (9, 256, 1000, 70), (3, 768, 64, 64), (40, 256, 300, 8),
-                                     (600, 512, 256, 8), (517, 256, 100, 5), (2100, 256, 130, 4)])
+                                     (600, 512, 256, 8), (517, 256, 100, 5), (2100, 256, 130, 4),
+                                     (520, 272, 64, 2), (2050, 784, 72, 6)])
 def test_router_parity_shapes(lib, t, h, e, k):
     """Expert counts across the one-, two-, four-, eight- and sixteen-slot variants of
     the selection kernel, k up to e and beyond one wave's width; batches of 512 and 2048
-    tokens and more take the 32 x 64- and 64 x 64-tile logit kernels (ragged in tokens
-    and experts here)."""
+    tokens and more take the 32 x 64- and 64 x 64-tile split-weight logit kernels (ragged
+    in tokens and experts here, and with hidden sizes that end in half a 32-wide K step)."""
     x = synth.normal(synth.stream_key(70, t, e), (t, h), 1.0).to(torch.bfloat16)
     w = synth.normal(synth.stream_key(71, h, e), (e, h), 0.05)
     b = synth.normal(synth.stream_key(72, e), (e,), 0.3)
@@ -121,6 +122,29 @@ def test_router_parity_shapes(lib, t, h, e, k):
     ref_ids = router.select_topk(Lg, k)
     assert np.array_equal(_np(ids), ref_ids)
     assert np.allclose(_np(wts), router.topk_weights(Lg, ref_ids), rtol=2e-6, atol=1e-7)
+
+
+@pytest.mark.parametrize("t", [5, 600])
+def test_router_nonfinite_weight(lib, t):
+    """A non-finite router weight on both logit kernels (fp32 matrix cores below 512
+    tokens, the three-part bf16 split from 512): +inf times positive x gives a +inf logit,
+    so that expert is every token's first choice, a NaN weight a NaN logit, and the other
+    logits keep the fp32 bound."""
+    e, h, k = 64, 256, 4
+    x = synth.normal(synth.stream_key(73, t), (t, h), 1.0)
+    x[:, 5] = x[:, 5].abs() + 0.5
+    x = x.to(torch.bfloat16)
+    w = synth.normal(synth.stream_key(74, h), (e, h), 0.05)
+    w[3, 5] = float("inf")
+    w[9, 7] = float("nan")
+    logits, ids, _ = lib.moe_route_topk(x.cuda(), w.cuda(), None, k)
+    Lg = _np(logits)
+    assert np.all(np.isposinf(Lg[:, 3])) and np.all(np.isnan(Lg[:, 9]))
+    assert np.all(_np(ids)[:, 0] == 3)
+    rest = [c for c in range(e) if c not in (3, 9)]
+    xs, ws = _np(x).astype(np.float64), _np(w)[rest].astype(np.float64)
+    L64 = xs @ ws.T
+    assert np.all(np.abs(Lg[:, rest] - L64) <= 2e-6 * (np.abs(xs) @ np.abs(ws).T) + 1e-6)
 
 
 def test_router_ties_pick_lower_index(lib):
