@@ -159,14 +159,22 @@ __global__ void __launch_bounds__(256) k_router_split3(const float* __restrict__
 // k = k0 + 8 kq; each K step runs the three parts' MFMAs on one accumulator per tile
 // (hi, then mid, then lo), U steps of loads issued before their MFMAs.  Rows past t or
 // e and K past the slice load zeros for both operands.  Same partial layout as above.
+// The grid is one-dimensional, a multiple of 8 workgroups: workgroup b runs on XCD
+// b % 8 (round-robin dispatch), and each XCD takes one contiguous range of tiles in
+// (slice, token block, expert block) order, so its L2 holds the weight parts of about
+// one K slice for every expert block and each x block serves all expert blocks there.
 template <int TB, int EB, int U>
 __global__ void __launch_bounds__(64) k_router_x3(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w3,
-                                                  int64_t t, int64_t h, int32_t e, int64_t kslice,
-                                                  float* __restrict__ partial) {
+                                                  int64_t t, int64_t h, int32_t e, int64_t kslice, int32_t neb,
+                                                  int32_t ntb, int32_t nslices, float* __restrict__ partial) {
   const int lane = threadIdx.x;
   const int m = lane & 15, kq = lane >> 4;
-  const int64_t e0 = int64_t(blockIdx.x) * 16 * EB, t0 = int64_t(blockIdx.y) * 16 * TB;
-  const int64_t kb = std::min<int64_t>(h, int64_t(blockIdx.z) * kslice), ke = std::min<int64_t>(h, kb + kslice);
+  const int64_t chunk = gridDim.x / 8;
+  const int64_t tile = int64_t(blockIdx.x % 8) * chunk + blockIdx.x / 8;
+  if (tile >= int64_t(neb) * ntb * nslices) return;
+  const int64_t eb = tile % neb, tb = (tile / neb) % ntb, slot = tile / (int64_t(neb) * ntb);
+  const int64_t e0 = eb * 16 * EB, t0 = tb * 16 * TB;
+  const int64_t kb = std::min<int64_t>(h, slot * kslice), ke = std::min<int64_t>(h, kb + kslice);
   const int64_t pn = int64_t(e) * h;   // elements from one part to the next
   const uint16_t* xr[TB];
   const uint16_t* wrow[EB];
@@ -214,8 +222,7 @@ __global__ void __launch_bounds__(64) k_router_x3(const uint16_t* __restrict__ x
             acc[i][j] = mfma16x16x32<Act::BF16>(av, bv, acc[i][j]);
           }
   }
-  const int64_t slot = blockIdx.z;
-#pragma unroll
+  #pragma unroll
   for (int i = 0; i < TB; ++i)
 #pragma unroll
     for (int j = 0; j < EB; ++j)
@@ -228,8 +235,19 @@ __global__ void __launch_bounds__(64) k_router_x3(const uint16_t* __restrict__ x
 
 constexpr int kMaxSlices = 32;
 
-// workgroups of the small-batch logit kernel to aim for (one per CU); overridable at
-// build time
+// Tuning defaults, overridable at build time: token blocks of 16 per wave tile from
+// 2048 tokens, and the waves the K slices aim for there (one per SIMD measured faster
+// than two: 86 vs 87-119 us at 4096 tokens on the 256-expert router) and below it.
+#ifndef Q4_ROUTE_HUGE_TB
+#define Q4_ROUTE_HUGE_TB 8
+#endif
+#ifndef Q4_ROUTE_HUGE_WAVES
+#define Q4_ROUTE_HUGE_WAVES 1024
+#endif
+#ifndef Q4_ROUTE_WAVES
+#define Q4_ROUTE_WAVES 2048
+#endif
+// workgroups of the small-batch logit kernel to aim for (one per CU)
 #ifndef Q4_ROUTE_WGS
 #define Q4_ROUTE_WGS 256
 #endif
@@ -357,18 +375,22 @@ __global__ void __launch_bounds__(64) k_topk(const float* __restrict__ partial, 
   }
 }
 
-// Wave tile of the partial-logit kernel: 16 x 16 for small batches, 32 tokens x 64
-// experts once there are enough tiles to fill the chip without splitting K much.
+// Wave tile of the partial-logit kernel: 16 x 16 for small batches (fp32 matrix
+// cores); with enough tiles to fill the chip without splitting K much, the split-weight
+// kernel with 32 tokens x 64 experts, and from 2048 tokens 16 Q4_ROUTE_HUGE_TB tokens.
 static bool route_big_tiles(int64_t t, int32_t e) { return t >= 512 && e >= 64; }
 static bool route_huge_tiles(int64_t t, int32_t e) { return t >= 2048 && e >= 64; }
 
-// K slices: enough waves to cover the chip (about 2048), at least 256 of K per slice,
-// at most kMaxSlices partial sums.
+// K slices: enough waves to cover the chip (about 2048; 1024 from 2048 tokens), at
+// least 256 of K per slice, at most kMaxSlices partial sums.
 int route_kslices(int64_t t, int64_t h, int32_t e) {
-  const int64_t tiles = route_huge_tiles(t, e) ? ((e + 63) / 64) * ((t + 63) / 64)
-                       : route_big_tiles(t, e) ? ((e + 63) / 64) * ((t + 31) / 32)
-                                               : ((e + 15) / 16) * ((t + 15) / 16);
-  int64_t ks = (2048 + tiles - 1) / tiles;
+  constexpr int64_t hrows = 16 * Q4_ROUTE_HUGE_TB;
+  const bool huge = route_huge_tiles(t, e);
+  const int64_t tiles = huge                    ? ((e + 63) / 64) * ((t + hrows - 1) / hrows)
+                        : route_big_tiles(t, e) ? ((e + 63) / 64) * ((t + 31) / 32)
+                                                : ((e + 15) / 16) * ((t + 15) / 16);
+  const int64_t waves = huge ? Q4_ROUTE_HUGE_WAVES : Q4_ROUTE_WAVES;
+  int64_t ks = (waves + tiles - 1) / tiles;
   ks = std::max<int64_t>(1, std::min<int64_t>(std::min<int64_t>(ks, h / 256), kMaxSlices));
   return int(ks);
 }
@@ -421,11 +443,16 @@ hipError_t launch_route(const uint16_t* x, const float* wr, const float* bias, i
     const int64_t n = int64_t(e) * h;
     hipLaunchKernelGGL(k_router_split3, dim3(unsigned((n / 8 + 255) / 256)), dim3(256), 0, st, wr, n, w3);
     if (route_huge_tiles(t, e)) {
-      dim3 grid(unsigned((e + 63) / 64), unsigned((t + 63) / 64), unsigned(kused));
-      hipLaunchKernelGGL((k_router_x3<4, 4, 1>), grid, dim3(64), 0, st, x, w3, t, h, e, kslice, partial);
+      constexpr int TB = Q4_ROUTE_HUGE_TB;
+      const int neb = int((e + 63) / 64), ntb = int((t + 16 * TB - 1) / (16 * TB));
+      const dim3 grid(unsigned((int64_t(neb) * ntb * kused + 7) / 8 * 8));
+      hipLaunchKernelGGL((k_router_x3<TB, 4, 1>), grid, dim3(64), 0, st, x, w3, t, h, e, kslice, neb, ntb, kused,
+                         partial);
     } else {
-      dim3 grid(unsigned((e + 63) / 64), unsigned((t + 31) / 32), unsigned(kused));
-      hipLaunchKernelGGL((k_router_x3<2, 4, 2>), grid, dim3(64), 0, st, x, w3, t, h, e, kslice, partial);
+      const int neb = int((e + 63) / 64), ntb = int((t + 31) / 32);
+      const dim3 grid(unsigned((int64_t(neb) * ntb * kused + 7) / 8 * 8));
+      hipLaunchKernelGGL((k_router_x3<2, 4, 2>), grid, dim3(64), 0, st, x, w3, t, h, e, kslice, neb, ntb, kused,
+                         partial);
     }
   } else {
     // about one workgroup per CU: the slices of a tile are shared out over
