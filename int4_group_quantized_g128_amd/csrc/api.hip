@@ -62,6 +62,8 @@ struct FwdWorkspace {
   TileDesc* tiles = nullptr;
   int32_t* num_tiles = nullptr;
   int32_t* fmt_tiles = nullptr;   // [kNumFormats + 1] tile range of each weight format
+  int32_t* perm_scratch = nullptr;   // per-range expert counts of the many-workgroup permutation
+  int64_t perm_scratch_ints = 0;
   void* h = nullptr;
   float* y = nullptr;
   int8_t* qx = nullptr;
@@ -174,6 +176,8 @@ FwdWorkspace carve(const q4_moe_layer_t* L, int64_t t, int mode, void* base) {
   w.tiles = reinterpret_cast<TileDesc*>(take(int64_t(w.max_tiles) * sizeof(TileDesc)));
   w.num_tiles = reinterpret_cast<int32_t*>(take(4));
   w.fmt_tiles = reinterpret_cast<int32_t*>(take((kNumFormats + 1) * 4));
+  w.perm_scratch_ints = permute_scratch_ints(P, int(ee));
+  w.perm_scratch = reinterpret_cast<int32_t*>(take(w.perm_scratch_ints * 4));
   w.h = take(P * I * (int8_acts(mode) ? 4 : 2));
   // Decode down projections with few work items (narrow layers: the dense FFN, a few
   // touched experts) split K over workgroups, aiming at about 512 items; the combine sums
@@ -628,7 +632,7 @@ int ffn_forward(const q4_moe_layer_t* L, const uint16_t* x_bf16, int64_t t, cons
   if ((!dense && !slots) || views) {
     if ((rc = check_hip(launch_permute(topk_ids, t, L->top_k, L->num_experts, shared, w.counts, w.offsets, w.perm,
                                        w.inv, w.tiles, w.num_tiles, w.tile_rows, stream, L->expert_bits,
-                                       L->expert_groups, w.fmt_tiles),
+                                       L->expert_groups, w.fmt_tiles, w.perm_scratch, w.perm_scratch_ints),
                         "permute")))
       return rc;
   }

@@ -52,10 +52,14 @@ constexpr int kNumFormats = 5;
 
 // Permutation.  Slots s = t * S + j with S = k + shared; expert(s) = ids[t][j] for
 // j < k, num_experts for the shared slot.  Optionally builds the row-tile list.
+// scratch: permute_scratch_ints(t * (k + shared), e + shared) ints lets large batches use
+// many workgroups (NULL: one workgroup at every size).
+int64_t permute_scratch_ints(int64_t slots, int ee);
 hipError_t launch_permute(const int32_t* ids, int64_t t, int32_t k, int32_t e, int shared, int32_t* counts,
                           int32_t* offsets, int32_t* perm, int32_t* inv, TileDesc* tiles, int32_t* num_tiles,
                           int tile_rows, hipStream_t st, const uint8_t* ebits = nullptr,
-                          const uint8_t* egroups = nullptr, int32_t* fmt_tiles = nullptr);
+                          const uint8_t* egroups = nullptr, int32_t* fmt_tiles = nullptr, int32_t* scratch = nullptr,
+                          int64_t scratch_ints = 0);
 
 // Per-row INT8 activation quantisation (x: bf16 or fp32 rows).
 hipError_t launch_act_quant(const void* x, int x_is_f32, int64_t rows, int64_t cols, int8_t* q, float* s,

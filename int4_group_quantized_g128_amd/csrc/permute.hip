@@ -69,6 +69,89 @@ __device__ __forceinline__ int tile_format(const uint8_t* ebits, const uint8_t* 
   return 0;
 }
 
+// Tile list: ceil(count / tile_rows) tiles per expert, ordered by (weight format,
+// expert), so that a GEMM launch for one format walks one contiguous range of tiles;
+// fmt_tiles[f] .. fmt_tiles[f + 1] is format f's range.  cntl / offl: the experts'
+// counts and offsets (LDS); ntl, first, tmp: LDS scratch of ee ints each.  All threads
+// call; the caller has synchronised after writing cntl / offl.
+__device__ void build_tile_list(int ee, const int32_t* cntl, const int32_t* offl, int32_t* ntl, int32_t* first,
+                                int32_t* tmp, int32_t* wave_tot, TileDesc* __restrict__ tiles,
+                                int32_t* __restrict__ num_tiles, int tile_rows, const uint8_t* __restrict__ ebits,
+                                const uint8_t* __restrict__ egroups, int32_t* __restrict__ fmt_tiles) {
+  const int tid = threadIdx.x;
+  for (int x = tid; x < ee; x += kPermThreads) ntl[x] = (cntl[x] + tile_rows - 1) / tile_rows;
+  __syncthreads();
+  int32_t base = 0;
+  const int nfmt = (ebits || egroups) ? kNumFormats : 1;   // one format unless the layer mixes them
+  for (int f = 0; f < kNumFormats; ++f) {
+    if (f >= nfmt) {
+      if (fmt_tiles && tid == 0) fmt_tiles[f] = base;
+      continue;
+    }
+    for (int x = tid; x < ee; x += kPermThreads) tmp[x] = tile_format(ebits, egroups, x) == f ? ntl[x] : 0;
+    __syncthreads();
+    const int32_t nf = block_exclusive_scan(tmp, ee, wave_tot);
+    for (int x = tid; x < ee; x += kPermThreads)
+      if (tile_format(ebits, egroups, x) == f) first[x] = base + tmp[x];
+    if (fmt_tiles && tid == 0) fmt_tiles[f] = base;
+    base += nf;
+    __syncthreads();
+  }
+  const int32_t ntiles = base;
+  if (fmt_tiles && tid == 0) fmt_tiles[kNumFormats] = ntiles;
+  for (int x = tid; x < ee; x += kPermThreads) {
+    const int32_t c = cntl[x], o = offl[x];
+    int32_t ti = first[x];
+    for (int32_t r = 0; r < c; r += tile_rows, ++ti) {
+      TileDesc d;
+      d.expert = x;
+      d.row_start = o + r;
+      d.rows = min(tile_rows, c - r);
+      d.pad = 0;
+      tiles[ti] = d;
+    }
+  }
+  if (tid == 0) *num_tiles = ntiles;
+}
+
+// One 64-slot step of a wave's stable scatter: lanes with the same expert find their
+// rank among the step's valid lanes with ballots over the expert's nbits bits; the
+// wave's running position per expert (cntw, LDS) gives each lane's position, and the
+// step's first lane of each expert advances it.
+Q4_DEVICE void scatter_step(int64_t s, bool valid, int ex, int nbits, int32_t* cntw, int32_t* __restrict__ perm,
+                            int32_t* __restrict__ inv) {
+  const int lane = threadIdx.x & 63;
+  unsigned long long peers = __ballot(valid);
+  for (int b = 0; b < nbits; ++b) {
+    const unsigned long long m = __ballot((ex >> b) & 1);
+    peers &= ((ex >> b) & 1) ? m : ~m;
+  }
+  const unsigned long long below = peers & ((1ull << lane) - 1ull);
+  const int rank = __popcll(below);
+  int32_t pos = 0;
+  if (valid) pos = cntw[ex] + rank;
+  // make sure every lane has read the base before the leader advances it
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  if (valid) {
+    perm[pos] = int32_t(s);
+    inv[s] = pos;
+    if (below == 0) cntw[ex] += __popcll(peers);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+}
+
+// Expert of slot s (s < t * S < 2^31): the token's routed id, clamped into range, or
+// the shared expert e for j == k.
+Q4_DEVICE int slot_expert(const int32_t* __restrict__ ids, int32_t k, int32_t e, int S, int64_t s) {
+  const uint32_t tok = uint32_t(s) / uint32_t(S);
+  const int j = int(uint32_t(s) - tok * uint32_t(S));
+  if (j >= k) return e;
+  const int x = ids[tok * k + j];
+  return min(max(x, 0), e - 1);
+}
+
 __global__ void __launch_bounds__(kPermThreads) k_permute(const int32_t* __restrict__ ids, int64_t t, int32_t k,
                                                           int32_t e, int shared, int nwaves,
                                                           int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
@@ -90,13 +173,7 @@ __global__ void __launch_bounds__(kPermThreads) k_permute(const int32_t* __restr
   __syncthreads();
   const int64_t per = (P + nwaves - 1) / nwaves;
   const int64_t beg = std::min<int64_t>(P, int64_t(wid) * per), end = std::min<int64_t>(P, beg + per);
-  auto expert_of = [&](int64_t s) -> int {   // s < t * S < 2^31
-    const uint32_t tok = uint32_t(s) / uint32_t(S);
-    const int j = int(uint32_t(s) - tok * uint32_t(S));
-    if (j >= k) return e;               // the shared expert
-    int x = ids[tok * k + j];
-    return min(max(x, 0), e - 1);       // out-of-range ids are clamped
-  };
+  auto expert_of = [&](int64_t s) -> int { return slot_expert(ids, k, e, S, s); };
   // pass 1 (the experts of a lane's first kKeep slots stay in registers for pass 3)
   constexpr int kKeep = 4;
   int kept[kKeep];
@@ -172,73 +249,152 @@ __global__ void __launch_bounds__(kPermThreads) k_permute(const int32_t* __restr
       } else if (valid) {
         ex = expert_of(s);
       }
-      unsigned long long peers = __ballot(valid);
-      for (int b = 0; b < nbits; ++b) {
-        const unsigned long long m = __ballot((ex >> b) & 1);
-        peers &= ((ex >> b) & 1) ? m : ~m;
-      }
-      const unsigned long long below = peers & ((1ull << lane) - 1ull);
-      const int rank = __popcll(below);
-      int32_t pos = 0;
-      if (valid) pos = cnt[wid * ee + ex] + rank;
-      // make sure every lane has read the base before the leader advances it
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      if (valid) {
-        perm[pos] = int32_t(s);
-        inv[s] = pos;
-        if (below == 0) cnt[wid * ee + ex] += __popcll(peers);
-      }
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
+      scatter_step(s, valid, ex, nbits, cnt + wid * ee, perm, inv);
     }
   }
-  // tile list: ceil(count / tile_rows) tiles per expert, ordered by (weight format,
-  // expert), so that a GEMM launch for one format walks one contiguous range of tiles;
-  // fmt_tiles[f] .. fmt_tiles[f + 1] is format f's range
   if (tiles) {
     __syncthreads();
-    for (int x = tid; x < ee; x += kPermThreads) ntl[x] = (cntl[x] + tile_rows - 1) / tile_rows;
-    __syncthreads();
-    int32_t base = 0;
-    const int nfmt = (ebits || egroups) ? kNumFormats : 1;   // one format unless the layer mixes them
-    for (int f = 0; f < kNumFormats; ++f) {
-      if (f >= nfmt) {
-        if (fmt_tiles && tid == 0) fmt_tiles[f] = base;
-        continue;
-      }
-      for (int x = tid; x < ee; x += kPermThreads) tot[x] = tile_format(ebits, egroups, x) == f ? ntl[x] : 0;
-      __syncthreads();
-      const int32_t nf = block_exclusive_scan(tot, ee, wave_tot);
-      for (int x = tid; x < ee; x += kPermThreads)
-        if (tile_format(ebits, egroups, x) == f) first[x] = base + tot[x];
-      if (fmt_tiles && tid == 0) fmt_tiles[f] = base;
-      base += nf;
-      __syncthreads();
+    build_tile_list(ee, cntl, offl, ntl, first, tot, wave_tot, tiles, num_tiles, tile_rows, ebits, egroups,
+                    fmt_tiles);
+  }
+}
+
+// ---------------------------------------------------------------- large batches
+// From kPermMultiSlots slots (given scratch for the per-range counts) the same result
+// comes from many workgroups in three launches: (1) each workgroup counts its
+// contiguous range of kPermRangeSlots slots per expert; (2) one workgroup adds the
+// ranges' counts in range order -- counts, offsets, each range's first position per
+// expert -- and builds the tile list; (3) each workgroup scatters its range, its waves
+// on consecutive sub-ranges, so the positions of an expert stay in slot order.
+constexpr int64_t kPermRangeSlots = 2048;
+constexpr int64_t kPermMultiSlots = 4 * kPermRangeSlots;
+
+int64_t permute_scratch_ints(int64_t slots, int ee) {
+  return slots >= kPermMultiSlots ? (slots + kPermRangeSlots - 1) / kPermRangeSlots * ee : 0;
+}
+
+__global__ void __launch_bounds__(kPermThreads) k_perm_count(const int32_t* __restrict__ ids, int64_t t, int32_t k,
+                                                             int32_t e, int shared, int32_t* __restrict__ rcnt) {
+  extern __shared__ int32_t lds[];   // [ee]
+  const int ee = e + shared, S = k + shared;
+  const int64_t P = t * S;
+  const int tid = threadIdx.x;
+  for (int x = tid; x < ee; x += kPermThreads) lds[x] = 0;
+  __syncthreads();
+  const int64_t beg = int64_t(blockIdx.x) * kPermRangeSlots, end = std::min<int64_t>(P, beg + kPermRangeSlots);
+  for (int64_t s = beg + tid; s < end; s += kPermThreads) atomicAdd(&lds[slot_expert(ids, k, e, S, s)], 1);
+  __syncthreads();
+  for (int x = tid; x < ee; x += kPermThreads) rcnt[int64_t(blockIdx.x) * ee + x] = lds[x];
+}
+
+// rcnt [nr][ee]: the ranges' counts in, each range's first position per expert out.
+__global__ void __launch_bounds__(kPermThreads) k_perm_plan(int32_t* __restrict__ rcnt, int nr, int ee,
+                                                            int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                                                            TileDesc* __restrict__ tiles, int32_t* __restrict__ num_tiles,
+                                                            int tile_rows, const uint8_t* __restrict__ ebits,
+                                                            const uint8_t* __restrict__ egroups,
+                                                            int32_t* __restrict__ fmt_tiles) {
+  extern __shared__ int32_t lds[];   // cntl, offl, ntl, first, tmp: [ee] each
+  __shared__ int32_t wave_tot[kPermThreads / 64 + 1];
+  int32_t* cntl = lds;
+  int32_t* offl = cntl + ee;
+  int32_t* ntl = offl + ee;
+  int32_t* first = ntl + ee;
+  int32_t* tmp = first + ee;
+  const int tid = threadIdx.x;
+  // (eight ranges' counts of an expert in flight at a time)
+  constexpr int kU = 8;
+  for (int x = tid; x < ee; x += kPermThreads) {
+    int32_t run = 0;
+    for (int r0 = 0; r0 < nr; r0 += kU) {
+      int32_t c[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) c[u] = r0 + u < nr ? rcnt[int64_t(r0 + u) * ee + x] : 0;
+#pragma unroll
+      for (int u = 0; u < kU; ++u) run += c[u];
     }
-    const int32_t ntiles = base;
-    if (fmt_tiles && tid == 0) fmt_tiles[kNumFormats] = ntiles;
-    for (int x = tid; x < ee; x += kPermThreads) {
-      const int32_t c = cntl[x], o = offl[x];
-      int32_t ti = first[x];
-      for (int32_t r = 0; r < c; r += tile_rows, ++ti) {
-        TileDesc d;
-        d.expert = x;
-        d.row_start = o + r;
-        d.rows = min(tile_rows, c - r);
-        d.pad = 0;
-        tiles[ti] = d;
+    cntl[x] = run;
+    tmp[x] = run;
+    counts[x] = run;
+  }
+  __syncthreads();
+  const int32_t total = block_exclusive_scan(tmp, ee, wave_tot);
+  for (int x = tid; x < ee; x += kPermThreads) {
+    offsets[x] = tmp[x];
+    offl[x] = tmp[x];
+    int32_t run = tmp[x];
+    for (int r0 = 0; r0 < nr; r0 += kU) {
+      int32_t c[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) c[u] = r0 + u < nr ? rcnt[int64_t(r0 + u) * ee + x] : 0;
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        if (r0 + u < nr) rcnt[int64_t(r0 + u) * ee + x] = run;
+        run += c[u];
       }
     }
-    if (tid == 0) *num_tiles = ntiles;
+  }
+  if (tid == 0) offsets[ee] = total;
+  __syncthreads();
+  if (tiles) build_tile_list(ee, cntl, offl, ntl, first, tmp, wave_tot, tiles, num_tiles, tile_rows, ebits, egroups,
+                             fmt_tiles);
+}
+
+__global__ void __launch_bounds__(kPermThreads) k_perm_scatter(const int32_t* __restrict__ ids, int64_t t, int32_t k,
+                                                               int32_t e, int shared, int nwaves,
+                                                               const int32_t* __restrict__ rbase,
+                                                               int32_t* __restrict__ perm, int32_t* __restrict__ inv) {
+  extern __shared__ int32_t lds[];   // [nwaves][ee]: per-wave counts, then running positions
+  const int ee = e + shared, S = k + shared;
+  const int64_t P = t * S;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  for (int i = tid; i < nwaves * ee; i += kPermThreads) lds[i] = 0;
+  __syncthreads();
+  const int64_t r0 = int64_t(blockIdx.x) * kPermRangeSlots, r1 = std::min<int64_t>(P, r0 + kPermRangeSlots);
+  const int64_t per = (r1 - r0 + nwaves - 1) / nwaves;
+  const int64_t beg = std::min<int64_t>(r1, r0 + int64_t(wid) * per), end = std::min<int64_t>(r1, beg + per);
+  if (wid < nwaves)
+    for (int64_t s = beg + lane; s < end; s += 64) atomicAdd(&lds[wid * ee + slot_expert(ids, k, e, S, s)], 1);
+  __syncthreads();
+  for (int x = tid; x < ee; x += kPermThreads) {
+    int32_t run = rbase[int64_t(blockIdx.x) * ee + x];
+    for (int w = 0; w < nwaves; ++w) {
+      const int32_t c = lds[w * ee + x];
+      lds[w * ee + x] = run;
+      run += c;
+    }
+  }
+  __syncthreads();
+  int nbits = 1;
+  while ((1 << nbits) <= ee) ++nbits;
+  if (wid < nwaves) {
+    for (int64_t s0 = beg; s0 < end; s0 += 64) {
+      const int64_t s = s0 + lane;
+      const bool valid = s < end;
+      const int ex = valid ? slot_expert(ids, k, e, S, s) : 0;
+      scatter_step(s, valid, ex, nbits, lds + wid * ee, perm, inv);
+    }
   }
 }
 
 hipError_t launch_permute(const int32_t* ids, int64_t t, int32_t k, int32_t e, int shared, int32_t* counts,
                           int32_t* offsets, int32_t* perm, int32_t* inv, TileDesc* tiles, int32_t* num_tiles,
                           int tile_rows, hipStream_t st, const uint8_t* ebits, const uint8_t* egroups,
-                          int32_t* fmt_tiles) {
+                          int32_t* fmt_tiles, int32_t* scratch, int64_t scratch_ints) {
   const int ee = e + shared;
+  const int64_t slots = t * (k + shared);
+  const int64_t need = permute_scratch_ints(slots, ee);
+  if (need > 0 && scratch && scratch_ints >= need) {
+    const int nr = int((slots + kPermRangeSlots - 1) / kPermRangeSlots);
+    const int nwaves = int(std::max<int64_t>(1, std::min<int64_t>(16, (96 * 1024 / 4) / ee)));
+    hipLaunchKernelGGL(k_perm_count, dim3(unsigned(nr)), dim3(kPermThreads), size_t(ee) * 4, st, ids, t, k, e,
+                       shared, scratch);
+    hipLaunchKernelGGL(k_perm_plan, dim3(1), dim3(kPermThreads), size_t(5) * ee * 4, st, scratch, nr, ee, counts,
+                       offsets, tiles, num_tiles, tile_rows, ebits, egroups, fmt_tiles);
+    hipLaunchKernelGGL(k_perm_scatter, dim3(unsigned(nr)), dim3(kPermThreads), size_t(nwaves) * ee * 4, st, ids, t,
+                       k, e, shared, nwaves, scratch, perm, inv);
+    return hipGetLastError();
+  }
   const size_t budget = 96 * 1024;
   // one wave per 64 slots (at most 16, and as many as the LDS budget allows): the
   // per-expert loops of pass 2 walk every wave's counts, so idle waves only cost time

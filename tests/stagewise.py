@@ -18,6 +18,15 @@ def _rows_rel(y, ref):
     return ffn.max_rel_l2(y, ref)
 
 
+# Per-row bar of a bf16-activation GEMM stage (W4A16 gate/up products, y) against the
+# oracle's fp64 product on the same inputs.  The kernels widen a stored nibble d = q + 8
+# to the bf16 value 128 + d and sum a * (136 + q) in fp32, removing 136 * sum(a) with the
+# exact row sums afterwards: the fp32 rounding therefore scales with 136 * sum|a| rather
+# than with |sum a * q|, about 30x a plain fp32 dot product's (measured up to 2.1e-5 per
+# row with K = 128).  W4A8 stages accumulate in INT32, exactly, and keep 2e-5.
+W4A16_STAGE_TOL = 1e-4
+
+
 def gate_up_canonical(n2):
     """Device column c of a Q4_REPACK_GATE_UP block -> row of the stacked [gate; up]
     matrix: 16-column block 2b holds gate rows 16b.., block 2b + 1 up rows 16b.."""
@@ -56,7 +65,7 @@ def check_gate_up_core(lib, layer, e, mode, gate, up, a_rows, x32_rows, qx_rows)
         got = np.empty_like(y)
         got[:, canon] = y
         ref = np.concatenate([ffn.linear_w4a16(x32_rows, gate), ffn.linear_w4a16(x32_rows, up)], axis=1)
-        assert _rows_rel(got, ref) <= 2e-5, f"gate/up products, expert {e}"
+        assert _rows_rel(got, ref) <= W4A16_STAGE_TOL, f"gate/up products, expert {e}"
 
 
 def check_stagewise(lib, layer, oe, x, ids, w, mode, shared, expect_ksplit=None, experts=None, gate_up_rows=64):
@@ -122,6 +131,7 @@ def check_stagewise(lib, layer, oe, x, ids, w, mode, shared, expect_ksplit=None,
             assert _rows_rel(h[lo:hi], ffn.silu(g) * u) <= 5e-3, f"h, expert {e}"
             down_of = lambda qm: ffn.linear_w4a16(hk, qm)
             hk = h[lo:hi]
+        y_tol = 2e-5 if mode == 1 else W4A16_STAGE_TOL
         if nsl > 1:
             for sidx in range(nsl):
                 g0, g1 = sidx * gsl, min(G, (sidx + 1) * gsl)
@@ -130,8 +140,8 @@ def check_stagewise(lib, layer, oe, x, ids, w, mode, shared, expect_ksplit=None,
                     ref_s = ffn.linear_w4a8(qh_gpu[lo:hi, 128 * g0:128 * g1], sh_gpu[lo:hi], k_slice(down, g0, g1))
                 else:
                     ref_s = ffn.linear_w4a16(h[lo:hi, 128 * g0:128 * g1], k_slice(down, g0, g1))
-                assert _rows_rel(ys[sidx, lo:hi], ref_s) <= 2e-5, f"y slice {sidx}, expert {e}"
-        assert _rows_rel(y[lo:hi], down_of(down)) <= 2e-5, f"y, expert {e}"
+                assert _rows_rel(ys[sidx, lo:hi], ref_s) <= y_tol, f"y slice {sidx}, expert {e}"
+        assert _rows_rel(y[lo:hi], down_of(down)) <= y_tol, f"y, expert {e}"
     # combine of the GPU's per-position outputs
     ref = np.zeros((t, layer.hidden))
     for tok in range(t):

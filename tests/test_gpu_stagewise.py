@@ -9,11 +9,12 @@ inputs of that stage, so the bars can be tight:
   the oracle's fp32 quantisation of the GPU's own h; the down-projection INT32 group
   accumulators bit-exact on those codes; y within 2e-5 per row of the oracle's fp64
   rescale of them;
-* W4A16: h (bf16) within 5e-3 per row of the fp64 h; y within 2e-5 per row of the
-  oracle's down projection of the GPU's bf16 h;
+* W4A16: h (bf16) within 5e-3 per row of the fp64 h; y within 1e-4 per row of the
+  oracle's down projection of the GPU's bf16 h (the offset-widened weights are summed
+  in fp32; tests/stagewise.py derives the bar);
 * gate and up before SwiGLU, through the same GEMM core on the layer's own gate/up
   block: the INT32 group accumulators bit-exact on the GPU's x codes (W4A8), the fp32
-  products within 2e-5 per row of the fp64 ones (W4A16);
+  products within 1e-4 per row of the fp64 ones (W4A16);
 * where the forward splits the down projection's K over workgroups (narrow layers at
   small batches), every K slice of y against the oracle's down projection restricted
   to that slice's groups, and their in-order sum as above;
@@ -109,3 +110,28 @@ def test_dense_stagewise_ksplit(lib, dense, mode, t, ksplit):
     ids = np.zeros((t, 1), np.int64)
     w = np.ones((t, 1))
     check_stagewise(lib, layer, oe, x, ids, w, mode, shared=False, expect_ksplit=ksplit)
+
+
+@pytest.fixture(scope="module")
+def wide(lib):
+    """300 routed experts + a shared one on a small hidden size."""
+    make = random_expert_maker(43, 128, 128)
+    layer = build_gpu_layer(lib, make, 300, 128, 128, 8, shared=True)
+    return layer, OracleExperts(make, False)
+
+
+@pytest.mark.parametrize("mode", [0, 1], ids=["w4a16", "w4a8"])
+@pytest.mark.parametrize("t", [1100, 2300])
+def test_many_experts_large_batch_stagewise(lib, wide, mode, t):
+    """9 t slots (9900 and 20700) take the many-workgroup permutation (ranges of 2048
+    slots, the last one ragged): counts, offsets, perm and inv bit-exact through the
+    forward, and the stages of a hot expert (a quarter of the tokens, many tiles), two
+    ordinary ones and the shared expert."""
+    layer, oe = wide
+    x = synth.normal(synth.stream_key(44, t), (t, 128), 1.0).to(torch.bfloat16)
+    rng = np.random.default_rng(t + 9)
+    others = np.delete(np.arange(300), 7)
+    ids = np.stack([np.concatenate([[7], rng.permutation(others)[:7]]) if i < t // 4 else rng.permutation(300)[:8]
+                    for i in range(t)]).astype(np.int64)
+    w = rng.dirichlet(np.ones(8), size=t)
+    check_stagewise(lib, layer, oe, x, ids, w, mode, shared=True, experts=[7, 100, 299, 300])
