@@ -76,6 +76,19 @@ def test_noalloc_moe8_prefill_then_split_decode(lib, moe8):
         assert torch.equal(got, ref), (t, mode)
 
 
+def test_noalloc_many_workgroup_permutation(lib):
+    """300 routed experts + a shared one (hidden 128): T = 1100 is 9900 routed slots, so
+    the permutation runs over many workgroups with its per-range counts in the scratch
+    array; then T = 40 (one workgroup)."""
+    layer = build_gpu_layer(lib, random_expert_maker(64, 128, 128), 300, 128, 128, 8, shared=True)
+    for t, mode in ((1100, 1), (40, 1), (1100, 0)):
+        x, ids, w = _batch(t, 300, 8, 128, 65)
+        ref = lib.moe_int4_ffn_forward(layer, x, ids, w, mode=mode)
+        got = _noalloc_raw(lib, layer, x, ids, w, mode)
+        torch.cuda.synchronize()
+        assert torch.equal(got, ref), (t, mode)
+
+
 def test_noalloc_refuses_batches_beyond_the_scratch(lib, moe8):
     t = 1
     while lib.moe_int4_ffn_plan(moe8, t, 0)["workspace_bytes"] <= lib.Q4_NOALLOC_SCRATCH_BYTES:
