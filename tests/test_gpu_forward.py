@@ -153,19 +153,24 @@ def test_dense_one_expert_path(lib, dense, t, mode):
     tokens (no K slices) the down projection applies the weight and rounds to bf16 in its
     epilogue.  Weights other than 1 (the combine's multiply is exercised); the result
     equals the debug call's (which runs the permutation and the separate combine) bit for
-    bit, and the oracle within the mode's bar."""
+    bit, also on repeated calls with a workspace of nonzero bytes, and the oracle within
+    the mode's bar."""
     layer, oe = dense
     plan = lib.moe_int4_ffn_plan(layer, t, mode)
     assert plan["kernel"] == "decode" and plan["rows_in_token_order"]
-    assert plan["combine_in_down"] == (t > 16)
+    assert plan["combine_in_down"] == (t > 16) and (plan["down_ksplit"] > 1) == (t <= 16)
     x = synth.tokens("dense", t)
     ids = np.zeros((t, 1), np.int32)
     w = np.random.default_rng(t).uniform(0.25, 1.75, (t, 1))
     out = _forward(lib, layer, x, ids, w, mode)
-    dbg, _ = lib.moe_int4_ffn_debug(layer, x.cuda(), torch.as_tensor(ids).cuda(),
-                                    torch.as_tensor(w, dtype=torch.float32).cuda(), mode=mode)
+    # a workspace full of nonzero bytes, twice: no step depends on its prior contents
+    ws = torch.full((layer.workspace_bytes(t, mode),), 0x5A, dtype=torch.uint8, device="cuda")
+    args = (x.cuda(), torch.as_tensor(ids).cuda(), torch.as_tensor(w, dtype=torch.float32).cuda())
+    again = [lib.moe_int4_ffn_forward(layer, *args, mode=mode, workspace=ws) for _ in range(2)]
+    dbg, _ = lib.moe_int4_ffn_debug(layer, *args, mode=mode)
     torch.cuda.synchronize()
     assert torch.equal(out.cpu(), dbg.cpu())
+    assert all(torch.equal(a.cpu(), out.cpu()) for a in again)
     ref = (ffn.moe_w4a16 if mode == 0 else ffn.moe_w4a8)(_np(x), oe, ids, w)
     assert ffn.max_rel_l2(_np(out), ref) <= (TOL_W4A16 if mode == 0 else TOL_W4A8)
 
