@@ -103,6 +103,35 @@ def test_router_parity(lib, name, t):
     assert np.allclose(_np(wts).sum(axis=1), 1.0, atol=2e-6)
 
 
+@pytest.mark.parametrize("name,t", [("moe256", 1), ("moe256", 64), ("moe8", 37)])
+def test_router_workspace_contents_do_not_matter(lib, name, t):
+    """The router's workspace needs no initial contents: a workspace of 0xFF bytes or of
+    zeros, and the same workspace again (what the previous call left behind), give the
+    same logits, ids and weights, bit for bit."""
+    cfg = synth.CONFIGS[name]
+    x, w, b = _router_case(name, t, salt=3)
+    x, w, b = x.cuda(), w.cuda(), (b.cuda() if b is not None else None)
+    k, e, h = cfg["top_k"], w.shape[0], x.shape[1]
+    L = lib._lib
+    nbytes = int(L.raw.moe_route_workspace_bytes(t, h, e))
+    outs = []
+    for fill in (0xFF, None, 0x00, None):
+        if fill is not None:
+            ws = torch.full((max(nbytes, 1),), fill, dtype=torch.uint8, device="cuda")
+        logits = torch.empty((t, e), dtype=torch.float32, device="cuda")
+        ids = torch.empty((t, k), dtype=torch.int32, device="cuda")
+        wts = torch.empty((t, k), dtype=torch.float32, device="cuda")
+        rc = L.raw.moe_route_topk(L._ptr(x), L._ptr(w), L._ptr(b), t, h, e, k, L._ptr(logits), L._ptr(ids),
+                                  L._ptr(wts), L._ptr(ws), nbytes, L._stream())
+        assert rc == 0
+        torch.cuda.synchronize()
+        outs.append((logits.cpu(), ids.cpu(), wts.cpu()))
+    ref = lib.moe_route_topk(x, w, b, k)
+    for o in outs:
+        for a, r in zip(o, ref):
+            assert torch.equal(a, r.cpu())
+
+
 @pytest.mark.parametrize("t,h,e,k", [(17, 512, 100, 3), (9, 256, 1000, 70), (3, 768, 64, 64), (40, 256, 300, 8),
                                      (600, 512, 256, 8), (517, 256, 100, 5), (2100, 256, 130, 4),
                                      (520, 272, 64, 2), (2050, 784, 72, 6)])
