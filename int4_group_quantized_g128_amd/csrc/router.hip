@@ -12,7 +12,7 @@ namespace q4 {
 // MFMA 16x16x4.  Lane (m = lane % 16, kq = lane / 16) feeds x[t0 + 16 i + m][k] and
 // W[e0 + 16 j + m][k] for k = k0 + 4 kq + s to MFMA s of each 16-wide K step; U steps
 // of loads are issued before their MFMAs.  Batches below 512 tokens (or with fewer than
-// 64 experts) run 16 x 16 tiles and many K slices, with RED the workgroup's waves (up to
+// 64 experts) run (16, 32 or 64) x 16 tiles and many K slices, with RED the workgroup's waves (up to
 // 16) on consecutive slices whose sums are added in LDS (in wave order) so that one
 // partial per workgroup is written; larger batches take the split-weight kernel below.
 template <int TB, int EB, int U, bool RED>
@@ -383,12 +383,23 @@ static bool route_huge_tiles(int64_t t, int32_t e) { return t >= 2048 && e >= 64
 
 // K slices: enough waves to cover the chip (about 2048; 1024 from 2048 tokens), at
 // least 256 of K per slice, at most kMaxSlices partial sums.
+// Token blocks of 16 per wave tile of the small-batch kernel.  With 16-token tiles each
+// router weight row is re-read by every token tile; from 65 tokens (64 experts or more)
+// two or four token blocks per tile read it half or a quarter as often (router + top-k
+// per call, 256 experts: T = 96 / 128 23.6 / 22.8 -> 16.9 / 18.3 us with two, T = 192 /
+// 256 / 384 34.5 / 37.9 / 62.3 -> 24.0 / 26.8 / 49.1 us with four; T = 64 and the
+// 8-expert router, whose weights are 64 KB, stay fastest with one).
+static int small_tb(int64_t t, int32_t e) {
+  if (e < 64 || t <= 64) return 1;
+  return t < 160 ? 2 : 4;
+}
 int route_kslices(int64_t t, int64_t h, int32_t e) {
   constexpr int64_t hrows = 16 * Q4_ROUTE_HUGE_TB;
+  const int64_t srows = 16 * small_tb(t, e);
   const bool huge = route_huge_tiles(t, e);
   const int64_t tiles = huge                    ? ((e + 63) / 64) * ((t + hrows - 1) / hrows)
                         : route_big_tiles(t, e) ? ((e + 63) / 64) * ((t + 31) / 32)
-                                                : ((e + 15) / 16) * ((t + 15) / 16);
+                                                : ((e + 15) / 16) * ((t + srows - 1) / srows);
   const int64_t waves = huge ? Q4_ROUTE_HUGE_WAVES : Q4_ROUTE_WAVES;
   int64_t ks = (waves + tiles - 1) / tiles;
   ks = std::max<int64_t>(1, std::min<int64_t>(std::min<int64_t>(ks, h / 256), kMaxSlices));
@@ -457,13 +468,21 @@ hipError_t launch_route(const uint16_t* x, const float* wr, const float* bias, i
   } else {
     // about one workgroup per CU: the slices of a tile are shared out over
     // Q4_ROUTE_WGS / tiles workgroups (at least one), at most 16 waves each
-    const int64_t tiles = int64_t((e + 15) / 16) * ((t + 15) / 16);
+    const int tb = small_tb(t, e);
+    const int64_t tiles = int64_t((e + 15) / 16) * ((t + 16 * tb - 1) / (16 * tb));
     const int want = int(std::max<int64_t>(1, std::min<int64_t>(kused, Q4_ROUTE_WGS / tiles)));
     const int kw = std::min(16, (kused + want - 1) / want);
     nparts = (kused + kw - 1) / kw;
-    dim3 grid(unsigned((e + 15) / 16), unsigned((t + 15) / 16), unsigned(nparts));
-    hipLaunchKernelGGL((k_router_partial<1, 1, 16, true>), grid, dim3(64 * kw), 0, st, x, wr, t, h, e, kslice,
-                       partial);
+    dim3 grid(unsigned((e + 15) / 16), unsigned((t + 16 * tb - 1) / (16 * tb)), unsigned(nparts));
+    if (tb == 4)   // (fewer steps per load batch: the registers of four token blocks)
+      hipLaunchKernelGGL((k_router_partial<4, 1, 4, true>), grid, dim3(64 * kw), 0, st, x, wr, t, h, e, kslice,
+                         partial);
+    else if (tb == 2)
+      hipLaunchKernelGGL((k_router_partial<2, 1, 8, true>), grid, dim3(64 * kw), 0, st, x, wr, t, h, e, kslice,
+                         partial);
+    else
+      hipLaunchKernelGGL((k_router_partial<1, 1, 16, true>), grid, dim3(64 * kw), 0, st, x, wr, t, h, e, kslice,
+                         partial);
   }
   if (e <= 64) return launch_topk<1>(partial, nparts, bias, t, e, k, logits, ids, w, st);
   if (e <= 128) return launch_topk<2>(partial, nparts, bias, t, e, k, logits, ids, w, st);
